@@ -1,0 +1,280 @@
+"""CPU oracle for the compressed-KV decode path (ctypes binding of kvq_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` may import this package.  The HIP library never imports, links or calls it,
+and the two share no code.
+
+Parity notes: every function here is pinned by ``tests/test_oracle_pins.py`` except the
+Sinkhorn calibration's agreement with KVarN itself (the pages give no values), which is
+"parity unpinned" beyond the invariants tested there.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "kvq_oracle.c")
+LIB = os.path.join(HERE, "libkvq_oracle.so")
+
+UNIFORM, TURBO_QJL, TURBO_MSE = 0, 1, 2
+TENSOR_K, TENSOR_V = 0, 1
+D = 128
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no FMA contraction, no fast-math)."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"], cwd=HERE)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+class PlaneCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in
+                ("scheme", "bits", "rotate", "sinkhorn", "window", "tensor", "capacity")]
+
+
+class Tables(ctypes.Structure):
+    _fields_ = [(n, ctypes.POINTER(ctypes.c_float)) for n in
+                ("signs", "c", "inv_c", "S", "mu", "theta")]
+
+
+_lib = None
+_F = ctypes.POINTER(ctypes.c_float)
+_Dp = ctypes.POINTER(ctypes.c_double)
+_U8 = ctypes.POINTER(ctypes.c_uint8)
+_U16 = ctypes.POINTER(ctypes.c_uint16)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build(force=True)
+        L = ctypes.CDLL(LIB)
+        L.orc_f32_to_f16_rn.restype = ctypes.c_uint16
+        L.orc_f32_to_f16_rn.argtypes = [ctypes.c_float]
+        L.orc_f32_to_f16_rd.restype = ctypes.c_uint16
+        L.orc_f32_to_f16_rd.argtypes = [ctypes.c_float]
+        L.orc_f16_to_f32.restype = ctypes.c_float
+        L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_rotate_f32.argtypes = [_F, _F, _F]
+        L.orc_rotate_f64.argtypes = [_Dp, _F, _Dp]
+        L.orc_unrotate_f64.argtypes = [_Dp, _F, _Dp]
+        L.orc_sinkhorn.argtypes = [_F, ctypes.c_int, _F, ctypes.c_int, _F, _F, _Dp, _Dp]
+        L.orc_quant_group.argtypes = [_F, ctypes.c_int, _U8, _U16, _U16]
+        L.orc_lloyd_max.argtypes = [ctypes.c_int, _Dp, _F, _F, _Dp]
+        L.orc_turbo_encode.argtypes = [_F, ctypes.POINTER(Tables), ctypes.c_int, _F, _U8, _U16,
+                                       _U16, _U8, _F]
+        L.orc_tree_sum_sq.restype = ctypes.c_float
+        L.orc_tree_sum_sq.argtypes = [_F]
+        for f in ("orc_codes_bytes", "orc_meta_bytes", "orc_qjl_bytes", "orc_ring_floats"):
+            getattr(L, f).restype = ctypes.c_size_t
+            getattr(L, f).argtypes = [ctypes.POINTER(PlaneCfg)]
+        L.orc_plane_append.argtypes = [ctypes.POINTER(PlaneCfg), ctypes.POINTER(Tables), _F,
+                                       ctypes.c_int, ctypes.c_int, _U8, _U8, _U8, _F]
+        L.orc_plane_read.argtypes = [ctypes.POINTER(PlaneCfg), _U8, _U8, _U8, ctypes.c_int, _U8,
+                                     _U16, _U8]
+        L.orc_dequant_token.argtypes = [ctypes.POINTER(PlaneCfg), ctypes.POINTER(Tables), _U8,
+                                        _U8, ctypes.c_int, _Dp]
+        L.orc_turbo_score.restype = ctypes.c_double
+        L.orc_turbo_score.argtypes = [ctypes.POINTER(Tables), _U8, _U8, _U8, ctypes.c_int, _Dp,
+                                      _Dp]
+        L.orc_attention.argtypes = [ctypes.POINTER(PlaneCfg), ctypes.POINTER(PlaneCfg),
+                                    ctypes.POINTER(Tables), ctypes.POINTER(Tables), _U8, _U8, _U8,
+                                    _F, _U8, _U8, _F, ctypes.c_int, ctypes.c_int, _F,
+                                    ctypes.c_double, _Dp]
+        _lib = L
+    return _lib
+
+
+def _p(a, t):
+    return a.ctypes.data_as(t) if a is not None else None
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------------------------
+# scalar / vector helpers
+# ----------------------------------------------------------------------------------------------
+
+def f32_to_f16_rn(x: float) -> int:
+    return int(lib().orc_f32_to_f16_rn(float(np.float32(x))))
+
+
+def f32_to_f16_rd(x: float) -> int:
+    return int(lib().orc_f32_to_f16_rd(float(np.float32(x))))
+
+
+def f16_to_f32(h: int) -> float:
+    return float(lib().orc_f16_to_f32(int(h)))
+
+
+def rotate_f32(x, signs):
+    x, s = _f32(x), _f32(signs)
+    y = np.empty(D, np.float32)
+    lib().orc_rotate_f32(_p(x, _F), _p(s, _F), _p(y, _F))
+    return y
+
+
+def rotate_f64(x, signs):
+    x, s = np.ascontiguousarray(x, np.float64), _f32(signs)
+    y = np.empty(D, np.float64)
+    lib().orc_rotate_f64(_p(x, _Dp), _p(s, _F), _p(y, _Dp))
+    return y
+
+
+def unrotate_f64(y, signs):
+    y, s = np.ascontiguousarray(y, np.float64), _f32(signs)
+    x = np.empty(D, np.float64)
+    lib().orc_unrotate_f64(_p(y, _Dp), _p(s, _F), _p(x, _Dp))
+    return x
+
+
+def sinkhorn(X, signs=None, iters=5, want_internals=False):
+    X = _f32(X)
+    n = X.shape[0]
+    c = np.empty(D, np.float32)
+    inv_c = np.empty(D, np.float32)
+    A = np.empty((n, D), np.float64) if want_internals else None
+    C = np.empty(D, np.float64) if want_internals else None
+    s = _f32(signs) if signs is not None else None
+    lib().orc_sinkhorn(_p(X, _F), n, _p(s, _F), iters, _p(c, _F), _p(inv_c, _F), _p(A, _Dp),
+                       _p(C, _Dp))
+    if want_internals:
+        return c, inv_c, A, C
+    return c, inv_c
+
+
+def quant_group(y, bits):
+    y = _f32(y)
+    codes = np.empty(32, np.uint8)
+    s16 = np.zeros(1, np.uint16)
+    z16 = np.zeros(1, np.uint16)
+    lib().orc_quant_group(_p(y, _F), bits, _p(codes, _U8), _p(s16, _U16), _p(z16, _U16))
+    return codes, int(s16[0]), int(z16[0])
+
+
+def lloyd_max(iters=2000):
+    mu_star = np.empty(8, np.float64)
+    mu = np.empty(8, np.float32)
+    theta = np.empty(7, np.float32)
+    ch = np.zeros(1, np.float64)
+    lib().orc_lloyd_max(iters, _p(mu_star, _Dp), _p(mu, _F), _p(theta, _F), _p(ch, _Dp))
+    return mu_star, mu, theta, float(ch[0])
+
+
+LLOYD_ITERS = 2000  # fixed iteration count of the codebook (same count on the device side)
+
+
+class TableSet:
+    """Keeps numpy arrays alive behind an orc_tables struct."""
+
+    def __init__(self, signs=None, c=None, inv_c=None, S=None, mu=None, theta=None):
+        self.arrays = {}
+        self.struct = Tables()
+        for name, val in (("signs", signs), ("c", c), ("inv_c", inv_c), ("S", S), ("mu", mu),
+                          ("theta", theta)):
+            if val is not None:
+                a = _f32(val).ravel()
+                self.arrays[name] = a
+                setattr(self.struct, name, _p(a, _F))
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+
+def turbo_encode(x, tables: TableSet, with_qjl=True):
+    x = _f32(x)
+    rho = np.empty(D, np.float32)
+    resid = np.empty(D, np.float32)
+    codes = np.empty(D, np.uint8)
+    bits = np.zeros(D, np.uint8)
+    n16 = np.zeros(1, np.uint16)
+    g16 = np.zeros(1, np.uint16)
+    lib().orc_turbo_encode(_p(x, _F), tables.ref, int(with_qjl), _p(rho, _F), _p(codes, _U8),
+                           _p(n16, _U16), _p(g16, _U16), _p(bits, _U8), _p(resid, _F))
+    return dict(rho=rho, codes=codes, n16=int(n16[0]), g16=int(g16[0]), bits=bits, resid=resid)
+
+
+def tree_sum_sq(v):
+    v = _f32(v)
+    return float(lib().orc_tree_sum_sq(_p(v, _F)))
+
+
+# ----------------------------------------------------------------------------------------------
+# planes
+# ----------------------------------------------------------------------------------------------
+
+class Plane:
+    """One (layer, sequence, kv head, tensor) plane: code bytes, meta bytes, QJL bytes, ring."""
+
+    def __init__(self, scheme, bits, rotate, sinkhorn, window, tensor, capacity):
+        self.cfg = PlaneCfg(scheme, bits, int(rotate or scheme != UNIFORM), int(sinkhorn), window,
+                            tensor, capacity)
+        L = lib()
+        r = ctypes.byref(self.cfg)
+        self.codes = np.zeros(L.orc_codes_bytes(r), np.uint8)
+        self.meta = np.zeros(L.orc_meta_bytes(r), np.uint8)
+        self.qjl = np.zeros(max(1, L.orc_qjl_bytes(r)), np.uint8)
+        self.ring = np.zeros(max(1, L.orc_ring_floats(r)), np.float32)
+        self.length = 0
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.cfg)
+
+    def append(self, X, tables: TableSet):
+        X = _f32(X).reshape(-1, D)
+        n = X.shape[0]
+        if self.length + n > self.cfg.capacity:
+            raise ValueError("oracle plane capacity exceeded")
+        lib().orc_plane_append(self.ref, tables.ref, _p(X, _F), self.length, n,
+                               _p(self.codes, _U8), _p(self.meta, _U8), _p(self.qjl, _U8),
+                               _p(self.ring, _F))
+        self.length += n
+
+    def read(self, t):
+        code = np.empty(D, np.uint8)
+        meta8 = np.empty(8, np.uint16)
+        bits = np.zeros(D, np.uint8)
+        lib().orc_plane_read(self.ref, _p(self.codes, _U8), _p(self.meta, _U8), _p(self.qjl, _U8),
+                             t, _p(code, _U8), _p(meta8, _U16), _p(bits, _U8))
+        return code, meta8, bits
+
+    def dequant(self, t, tables: TableSet):
+        out = np.empty(D, np.float64)
+        lib().orc_dequant_token(self.ref, tables.ref, _p(self.codes, _U8), _p(self.meta, _U8), t,
+                                _p(out, _Dp))
+        return out
+
+    def turbo_score(self, t, tables: TableSet, rho_q, s_rho_q):
+        rq = np.ascontiguousarray(rho_q, np.float64)
+        srq = np.ascontiguousarray(s_rho_q, np.float64)
+        return float(lib().orc_turbo_score(tables.ref, _p(self.codes, _U8), _p(self.meta, _U8),
+                                           _p(self.qjl, _U8), t, _p(rq, _Dp), _p(srq, _Dp)))
+
+
+def attention(kplane: Plane, vplane: Plane, ktables: TableSet, vtables: TableSet, q, n=None,
+              scale=None):
+    """fp64 decode attention of G = q.shape[0] query heads over one kv head's planes."""
+    q = _f32(q).reshape(-1, D)
+    G = q.shape[0]
+    n = kplane.length if n is None else n
+    scale = 1.0 / np.sqrt(128.0) if scale is None or scale <= 0 else float(scale)
+    out = np.empty((G, D), np.float64)
+    lib().orc_attention(kplane.ref, vplane.ref, ktables.ref, vtables.ref,
+                        _p(kplane.codes, _U8), _p(kplane.meta, _U8), _p(kplane.qjl, _U8),
+                        _p(kplane.ring, _F), _p(vplane.codes, _U8), _p(vplane.meta, _U8),
+                        _p(vplane.ring, _F), n, G, _p(q, _F), scale, _p(out, _Dp))
+    return out

@@ -1,0 +1,677 @@
+/*
+ * kvq_oracle.c -- plain, slow, obviously-correct CPU oracle for the compressed-KV path.
+ *
+ * TEST INFRASTRUCTURE ONLY (see kvq_oracle.h).  Build:
+ *   gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fPIC -shared kvq_oracle.c -lm
+ * Binary32 rounding is the C default (round-to-nearest-even); no expression below relies on FMA
+ * contraction, and the build forbids it.
+ *
+ * Section map (pages cited by title and section):
+ *   binary16 helpers ........ format of the "fp16 scale + fp16 zero" per group (quantcpp article,
+ *                             KV compression claim of 6.4x = 32 bits / (4 + 32/32) bits).
+ *   rotation ................ KVarN post, TL;DR: Walsh-Hadamard transform before quantizing;
+ *                             TurboQuant row of the method table: random rotation.
+ *   Sinkhorn ................ KVarN post, TL;DR: Sinkhorn variance balancing.
+ *   uniform quantizer ....... quantcpp article, progressive table: 4-bit KV; groups of 32 along
+ *                             the head dimension with fp16 scale/zero (reading of "6.4x").
+ *   Lloyd-Max + turbo ....... TurboQuant row: per-coordinate optimal scalar quantizer after a
+ *                             random rotation, 1-bit QJL on the residual for an unbiased inner
+ *                             product.
+ *   window .................. quantcpp article, progressive paragraph: the most recent 128
+ *                             tokens stay FP32, everything else 4-bit.
+ *   attention ............... plain softmax(q k^T * scale) v on the dequantized cache.
+ */
+#include "kvq_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define D ORC_D
+#define ORC_PI 3.14159265358979323846
+#define GS ORC_GROUP
+#define NG ORC_NGROUPS
+
+/* ------------------------------------------------------------------------------------------ */
+/* binary16 by integer manipulation                                                            */
+/* ------------------------------------------------------------------------------------------ */
+
+float orc_f16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int ex = (h >> 10) & 0x1f;
+    int man = h & 0x3ff;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)man, -24); /* zero or subnormal: man * 2^-24 */
+    else if (ex == 31)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp((double)(man | 0x400), ex - 25); /* (1024 + man) * 2^(ex - 15 - 10) */
+    return (float)(sign ? -v : v);
+}
+
+/* Round-to-nearest-even binary32 -> binary16.  Every scaling below is by a power of two, so the
+ * only rounding is the rint() (half-even under the default rounding mode). */
+uint16_t orc_f32_to_f16_rn(float xf)
+{
+    double x = (double)xf;
+    uint16_t s = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(a)) return 0x7e00;
+    if (a >= 65520.0) return (uint16_t)(s | 0x7c00); /* halfway to 2^16 rounds to even = inf */
+    if (a < ldexp(1.0, -14)) {                        /* subnormal range: units of 2^-24 */
+        double m = rint(a * 16777216.0);               /* <= 1024; 1024 is the smallest normal */
+        return (uint16_t)(s | (uint16_t)m);
+    }
+    int e;
+    frexp(a, &e); /* a in [2^(e-1), 2^e) */
+    int E = e - 1;
+    double m = rint(ldexp(a, 10 - E)); /* in [1024, 2048] */
+    if (m == 2048.0) {
+        m = 1024.0;
+        E += 1;
+    }
+    if (E > 15) return (uint16_t)(s | 0x7c00);
+    return (uint16_t)(s | (uint16_t)(((E + 15) << 10) | ((int)m - 1024)));
+}
+
+/* Largest binary16 value <= x (x finite, |x| < 65504): round to nearest, then step down one
+ * binary16 ulp if that overshot.  This is the zero-point rounding that keeps every value of a
+ * group inside [z, z + L*s] (reading G2). */
+uint16_t orc_f32_to_f16_rd(float x)
+{
+    uint16_t h = orc_f32_to_f16_rn(x);
+    if (orc_f16_to_f32(h) > x) {
+        if (h == 0x0000 || h == 0x8000)
+            h = 0x8001; /* -(2^-24) */
+        else if (h & 0x8000)
+            h = (uint16_t)(h + 1); /* negative: larger magnitude */
+        else
+            h = (uint16_t)(h - 1); /* positive: smaller magnitude */
+    }
+    return h;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* rotation R(x) = c0 * H (d .* x), H the 128x128 Sylvester Hadamard matrix (entries +-1)      */
+/* ------------------------------------------------------------------------------------------ */
+
+/* c0 = 2^-3.5 rounded to binary32 (bits 0x3DB504F3). */
+static float c0_f32(void)
+{
+    uint32_t bits = 0x3DB504F3u;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+/* Butterfly stages with span h = 1, 2, 4, ..., 64 in that order; each maps the pair
+ * (t[i], t[i+h]), bit h of i clear, to (t[i] + t[i+h], t[i] - t[i+h]).  The final scaling by c0 is
+ * one binary32 multiply per element. */
+void orc_rotate_f32(const float* x, const float* signs, float* y)
+{
+    float t[D];
+    for (int j = 0; j < D; j++) t[j] = (signs[j] < 0.0f) ? -x[j] : x[j];
+    for (int h = 1; h < D; h <<= 1)
+        for (int i = 0; i < D; i++)
+            if (!(i & h)) {
+                float a = t[i], b = t[i + h];
+                t[i] = a + b;
+                t[i + h] = a - b;
+            }
+    float c0 = c0_f32();
+    for (int j = 0; j < D; j++) y[j] = t[j] * c0;
+}
+
+static void hadamard_f64(double* t)
+{
+    for (int h = 1; h < D; h <<= 1)
+        for (int i = 0; i < D; i++)
+            if (!(i & h)) {
+                double a = t[i], b = t[i + h];
+                t[i] = a + b;
+                t[i + h] = a - b;
+            }
+}
+
+void orc_rotate_f64(const double* x, const float* signs, double* y)
+{
+    double t[D];
+    for (int j = 0; j < D; j++) t[j] = (double)signs[j] * x[j];
+    hadamard_f64(t);
+    double r = sqrt(128.0);
+    for (int j = 0; j < D; j++) y[j] = t[j] / r;
+}
+
+/* R^-1 = R^T = d .* (H y) / sqrt(128): H is symmetric and H H = 128 I. */
+void orc_unrotate_f64(const double* y, const float* signs, double* x)
+{
+    double t[D];
+    for (int j = 0; j < D; j++) t[j] = y[j];
+    hadamard_f64(t);
+    double r = sqrt(128.0);
+    for (int j = 0; j < D; j++) x[j] = (double)signs[j] * (t[j] / r);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Sinkhorn variance balancing (reading C3)                                                    */
+/* ------------------------------------------------------------------------------------------ */
+
+/* X: n calibration tokens [n][128] in the original domain.  A = (double) R(X) (or X).  Each
+ * iteration first divides every row by its population standard deviation, then every column by
+ * its own, accumulating the column divisors in C.  Sums run sequentially in index order.  The
+ * row divisors are discarded: per-token groups carry their own scale, and a future token's row
+ * scale is unknown at append time.  Output c = fp32(C), inv_c = fp32(1 / (double) c). */
+void orc_sinkhorn(const float* X, int n, const float* signs_or_null, int iters, float* c,
+                  float* inv_c, double* A_out, double* C_out)
+{
+    double* A = (double*)malloc(sizeof(double) * (size_t)n * D);
+    double C[D];
+    float y[D];
+    for (int t = 0; t < n; t++) {
+        if (signs_or_null)
+            orc_rotate_f32(X + (size_t)t * D, signs_or_null, y);
+        else
+            memcpy(y, X + (size_t)t * D, sizeof y);
+        for (int j = 0; j < D; j++) A[(size_t)t * D + j] = (double)y[j];
+    }
+    for (int j = 0; j < D; j++) C[j] = 1.0;
+    for (int it = 0; it < iters; it++) {
+        for (int t = 0; t < n; t++) {
+            double* row = A + (size_t)t * D;
+            double s = 0.0;
+            for (int j = 0; j < D; j++) s = s + row[j];
+            double mean = s / 128.0;
+            double v = 0.0;
+            for (int j = 0; j < D; j++) {
+                double dv = row[j] - mean;
+                v = v + dv * dv;
+            }
+            double sd = sqrt(v / 128.0);
+            if (sd < 1e-30) sd = 1e-30;
+            for (int j = 0; j < D; j++) row[j] = row[j] / sd;
+        }
+        for (int j = 0; j < D; j++) {
+            double s = 0.0;
+            for (int t = 0; t < n; t++) s = s + A[(size_t)t * D + j];
+            double mean = s / (double)n;
+            double v = 0.0;
+            for (int t = 0; t < n; t++) {
+                double dv = A[(size_t)t * D + j] - mean;
+                v = v + dv * dv;
+            }
+            double sd = sqrt(v / (double)n);
+            if (sd < 1e-30) sd = 1e-30;
+            for (int t = 0; t < n; t++) A[(size_t)t * D + j] = A[(size_t)t * D + j] / sd;
+            C[j] = C[j] * sd;
+        }
+    }
+    for (int j = 0; j < D; j++) {
+        c[j] = (float)C[j];
+        inv_c[j] = (float)(1.0 / (double)c[j]);
+    }
+    if (A_out) memcpy(A_out, A, sizeof(double) * (size_t)n * D);
+    if (C_out) memcpy(C_out, C, sizeof C);
+    free(A);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* uniform asymmetric b-bit quantizer for one group of 32 (reading C4)                          */
+/* ------------------------------------------------------------------------------------------ */
+
+void orc_quant_group(const float* y, int bits, uint8_t* codes, uint16_t* s16o, uint16_t* z16o)
+{
+    const int L = (1 << bits) - 1;
+    float mn = y[0], mx = y[0];
+    for (int i = 1; i < GS; i++) {
+        if (y[i] < mn) mn = y[i];
+        if (y[i] > mx) mx = y[i];
+    }
+    mn = mn + 0.0f; /* -0 -> +0 */
+    mx = mx + 0.0f;
+    uint16_t z16 = orc_f32_to_f16_rd(mn);
+    float z = orc_f16_to_f32(z16);
+    float s32 = (mx - z) / (float)L;
+    uint16_t s16 = orc_f32_to_f16_rn(s32);
+    float s = orc_f16_to_f32(s16);
+    float inv = (s > 0.0f) ? 1.0f / s : 0.0f;
+    for (int i = 0; i < GS; i++) {
+        float d = y[i] - z;
+        float u = d * inv;
+        float r = rintf(u);
+        if (r < 0.0f) r = 0.0f;
+        if (r > (float)L) r = (float)L;
+        codes[i] = (uint8_t)r;
+    }
+    *s16o = s16;
+    *z16o = z16;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Lloyd-Max 8-level quantizer of N(0,1), scaled to N(0,1/128) (reading C5)                    */
+/* ------------------------------------------------------------------------------------------ */
+
+static double phi(double x) { return exp(-0.5 * x * x) / sqrt(2.0 * ORC_PI); }
+
+/* Probability mass of N(0,1) on [a, b], 0 <= a < b <= inf, via erfc (accurate in the tails). */
+static double mass(double a, double b)
+{
+    double eb = isinf(b) ? 0.0 : erfc(b / sqrt(2.0));
+    return 0.5 * (erfc(a / sqrt(2.0)) - eb);
+}
+
+/* Lloyd's two conditions, iterated on the positive half line (the density is even, so the
+ * optimal 8-level quantizer is odd-symmetric with a threshold at 0): thresholds are midpoints of
+ * neighbouring centroids, centroids are conditional means (phi(a) - phi(b)) / mass(a, b). */
+void orc_lloyd_max(int iters, double* mu_star, float* mu, float* theta, double* last_change)
+{
+    double m[4] = {0.5, 1.0, 1.5, 2.0};
+    double change = 0.0;
+    for (int it = 0; it < iters; it++) {
+        double b[5];
+        b[0] = 0.0;
+        for (int k = 1; k < 4; k++) b[k] = (m[k - 1] + m[k]) * 0.5;
+        b[4] = INFINITY;
+        change = 0.0;
+        for (int k = 0; k < 4; k++) {
+            double pb = isinf(b[k + 1]) ? 0.0 : phi(b[k + 1]);
+            double nm = (phi(b[k]) - pb) / mass(b[k], b[k + 1]);
+            double dlt = fabs(nm - m[k]);
+            if (dlt > change) change = dlt;
+            m[k] = nm;
+        }
+    }
+    double r = sqrt(128.0);
+    for (int k = 0; k < 4; k++) {
+        mu_star[4 + k] = m[k];
+        mu_star[3 - k] = -m[k];
+        float f = (float)(m[k] / r);
+        mu[4 + k] = f;
+        mu[3 - k] = -f;
+    }
+    theta[3] = 0.0f;
+    for (int k = 1; k < 4; k++) {
+        double t = (m[k - 1] + m[k]) * 0.5;
+        float f = (float)(t / r);
+        theta[3 + k] = f;
+        theta[3 - k] = -f;
+    }
+    if (last_change) *last_change = change;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* TurboQuant token code (reading C5 / C6)                                                      */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Pairwise sum of v[j]^2 in index order: level 1 adds (0,1), (2,3), ...; level 2 adds adjacent
+ * pair sums; and so on up to one value.  Products and sums are binary32. */
+float orc_tree_sum_sq(const float* v)
+{
+    float t[D];
+    for (int j = 0; j < D; j++) t[j] = v[j] * v[j];
+    for (int w = D / 2; w >= 1; w >>= 1)
+        for (int i = 0; i < w; i++) t[i] = t[2 * i] + t[2 * i + 1];
+    return t[0];
+}
+
+void orc_turbo_encode(const float* x, const orc_tables* tb, int with_qjl, float* rho_out,
+                      uint8_t* codes, uint16_t* n16o, uint16_t* g16o, uint8_t* bits,
+                      float* resid_out)
+{
+    float rho[D], r[D];
+    orc_rotate_f32(x, tb->signs, rho);
+    float nsq = orc_tree_sum_sq(rho);
+    uint16_t n16 = orc_f32_to_f16_rn(sqrtf(nsq));
+    float n = orc_f16_to_f32(n16);
+    float inv = (n > 0.0f) ? 1.0f / n : 0.0f;
+    for (int j = 0; j < D; j++) {
+        float u = rho[j] * inv;
+        int c = 0;
+        for (int i = 0; i < 7; i++)
+            if (u > tb->theta[i]) c++;
+        codes[j] = (uint8_t)c;
+        float p = n * tb->mu[c];
+        r[j] = rho[j] - p;
+    }
+    uint16_t g16 = 0;
+    if (with_qjl) {
+        g16 = orc_f32_to_f16_rn(sqrtf(orc_tree_sum_sq(r)));
+        for (int i = 0; i < D; i++) {
+            float acc = 0.0f;
+            for (int j = 0; j < D; j++) acc = fmaf(tb->S[i * D + j], r[j], acc);
+            bits[i] = (acc >= 0.0f) ? 1 : 0; /* sign(0) = +1 */
+        }
+    } else if (bits) {
+        memset(bits, 0, D);
+    }
+    *n16o = n16;
+    *g16o = g16;
+    if (rho_out) memcpy(rho_out, rho, sizeof rho);
+    if (resid_out) memcpy(resid_out, r, sizeof r);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* plane layouts                                                                               */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * Uniform K (token-major), blocks of 64 tokens.  Token t is stored at row
+ *     64*(t/64) + 16*((t%64)%4) + (t%64)/4
+ * of both the code plane and the meta plane.  4-bit row (64 B) = 16 little-endian u32 words;
+ * word 4*kb + g (kb, g in 0..3) holds elements 32*g + 8*kb + i, i = 0..7, element i at bit
+ * 16*(i%2) + 4*(i/2).  8-bit row (128 B) = 16 units of 8 B; unit 4*kb + g holds the same 8
+ * elements, element i at byte i.  Meta row (16 B) = u16 scale[0..3], then u16 zero[0..3].
+ *
+ * Uniform V (blocks of 32 tokens, head dimension outermost within 8-token lanes).  Token t:
+ * block b = t/32, tau = t%32, kb = tau/8, i = tau%8; element d: n = d%16, N = d/16.
+ * 4-bit block (2048 B): u32 word 8*(16*kb + n) + N, token i at bit 16*(i%2) + 4*(i/2).
+ * 8-bit block (4096 B): 8-byte unit 8*(16*kb + n) + N, token i at byte i.
+ * Meta: natural token order, 16 B per token as for K.
+ *
+ * Turbo (K or V): 48 B per token, natural order; group g at byte 12*g: u64 little-endian with
+ * bits 2e..2e+1 = code_e & 3, then u32 with bit e = code_e >> 2 (e = 0..31).
+ * Turbo-QJL meta: u16 n, u16 gamma per token; QJL plane: 16 B per token, bit i at byte i/8,
+ * bit i%8.  Turbo-MSE meta: u16 n per token.
+ * Window ring: [W][128] fp32, token t at slot t % W.
+ */
+
+static int ceil_to(int x, int m) { return (x + m - 1) / m * m; }
+
+static size_t k_row(int t) { return (size_t)(64 * (t / 64) + 16 * ((t % 64) % 4) + (t % 64) / 4); }
+
+size_t orc_codes_bytes(const orc_plane_cfg* pc)
+{
+    if (pc->scheme != ORC_UNIFORM) return (size_t)pc->capacity * 48;
+    if (pc->tensor == ORC_TENSOR_K) return (size_t)ceil_to(pc->capacity, 64) * 16 * pc->bits;
+    return (size_t)ceil_to(pc->capacity, 32) * 16 * pc->bits;
+}
+
+size_t orc_meta_bytes(const orc_plane_cfg* pc)
+{
+    if (pc->scheme == ORC_TURBO_QJL) return (size_t)pc->capacity * 4;
+    if (pc->scheme == ORC_TURBO_MSE) return (size_t)pc->capacity * 2;
+    if (pc->tensor == ORC_TENSOR_K) return (size_t)ceil_to(pc->capacity, 64) * 16;
+    return (size_t)ceil_to(pc->capacity, 32) * 16;
+}
+
+size_t orc_qjl_bytes(const orc_plane_cfg* pc)
+{
+    return pc->scheme == ORC_TURBO_QJL ? (size_t)pc->capacity * 16 : 0;
+}
+
+size_t orc_ring_floats(const orc_plane_cfg* pc) { return (size_t)pc->window * D; }
+
+static void put_u16(uint8_t* p, uint16_t v)
+{
+    p[0] = (uint8_t)(v & 0xff);
+    p[1] = (uint8_t)(v >> 8);
+}
+static uint16_t get_u16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* Set 4-bit field `code` at bit position `bit` of the little-endian u32 at p. */
+static void put_nibble(uint8_t* p, int bit, int code)
+{
+    int byte = bit / 8, sh = bit % 8;
+    p[byte] = (uint8_t)((p[byte] & ~(0xf << sh)) | ((code & 0xf) << sh));
+}
+static int get_nibble(const uint8_t* p, int bit) { return (p[bit / 8] >> (bit % 8)) & 0xf; }
+
+static void pack_token(const orc_plane_cfg* pc, int t, const uint8_t* code, const uint16_t* s16,
+                       const uint16_t* z16, uint16_t n16, uint16_t g16, const uint8_t* bits,
+                       uint8_t* codes, uint8_t* meta, uint8_t* qjl)
+{
+    if (pc->scheme == ORC_UNIFORM) {
+        if (pc->tensor == ORC_TENSOR_K) {
+            size_t row = k_row(t);
+            uint8_t* r = codes + row * (size_t)(16 * pc->bits);
+            for (int j = 0; j < D; j++) {
+                int g = j / 32, e = j % 32, kb = e / 8, i = e % 8;
+                if (pc->bits == 4)
+                    put_nibble(r + 4 * (4 * kb + g), 16 * (i % 2) + 4 * (i / 2), code[j]);
+                else
+                    r[8 * (4 * kb + g) + i] = code[j];
+            }
+            uint8_t* m = meta + row * 16;
+            for (int g = 0; g < NG; g++) {
+                put_u16(m + 2 * g, s16[g]);
+                put_u16(m + 8 + 2 * g, z16[g]);
+            }
+        } else {
+            int b = t / 32, tau = t % 32, kb = tau / 8, i = tau % 8;
+            uint8_t* blk = codes + (size_t)b * (size_t)(512 * pc->bits);
+            for (int d = 0; d < D; d++) {
+                int n = d % 16, N = d / 16;
+                int w = 8 * (16 * kb + n) + N;
+                if (pc->bits == 4)
+                    put_nibble(blk + 4 * w, 16 * (i % 2) + 4 * (i / 2), code[d]);
+                else
+                    blk[8 * w + i] = code[d];
+            }
+            uint8_t* m = meta + (size_t)t * 16;
+            for (int g = 0; g < NG; g++) {
+                put_u16(m + 2 * g, s16[g]);
+                put_u16(m + 8 + 2 * g, z16[g]);
+            }
+        }
+        return;
+    }
+    uint8_t* r = codes + (size_t)t * 48;
+    for (int g = 0; g < NG; g++) {
+        uint64_t lo = 0;
+        uint32_t hi = 0;
+        for (int e = 0; e < 32; e++) {
+            int c = code[32 * g + e];
+            lo |= (uint64_t)(c & 3) << (2 * e);
+            hi |= (uint32_t)((c >> 2) & 1) << e;
+        }
+        for (int k = 0; k < 8; k++) r[12 * g + k] = (uint8_t)(lo >> (8 * k));
+        for (int k = 0; k < 4; k++) r[12 * g + 8 + k] = (uint8_t)(hi >> (8 * k));
+    }
+    if (pc->scheme == ORC_TURBO_QJL) {
+        put_u16(meta + (size_t)t * 4, n16);
+        put_u16(meta + (size_t)t * 4 + 2, g16);
+        uint8_t* q = qjl + (size_t)t * 16;
+        memset(q, 0, 16);
+        for (int i = 0; i < D; i++) q[i / 8] |= (uint8_t)(bits[i] << (i % 8));
+    } else {
+        put_u16(meta + (size_t)t * 2, n16);
+    }
+}
+
+void orc_plane_read(const orc_plane_cfg* pc, const uint8_t* codes, const uint8_t* meta,
+                    const uint8_t* qjl, int t, uint8_t* code, uint16_t* meta8, uint8_t* bits)
+{
+    if (pc->scheme == ORC_UNIFORM) {
+        const uint8_t* m;
+        if (pc->tensor == ORC_TENSOR_K) {
+            size_t row = k_row(t);
+            const uint8_t* r = codes + row * (size_t)(16 * pc->bits);
+            for (int j = 0; j < D; j++) {
+                int g = j / 32, e = j % 32, kb = e / 8, i = e % 8;
+                if (pc->bits == 4)
+                    code[j] = (uint8_t)get_nibble(r + 4 * (4 * kb + g), 16 * (i % 2) + 4 * (i / 2));
+                else
+                    code[j] = r[8 * (4 * kb + g) + i];
+            }
+            m = meta + row * 16;
+        } else {
+            int b = t / 32, tau = t % 32, kb = tau / 8, i = tau % 8;
+            const uint8_t* blk = codes + (size_t)b * (size_t)(512 * pc->bits);
+            for (int d = 0; d < D; d++) {
+                int w = 8 * (16 * kb + d % 16) + d / 16;
+                if (pc->bits == 4)
+                    code[d] = (uint8_t)get_nibble(blk + 4 * w, 16 * (i % 2) + 4 * (i / 2));
+                else
+                    code[d] = blk[8 * w + i];
+            }
+            m = meta + (size_t)t * 16;
+        }
+        for (int k = 0; k < 8; k++) meta8[k] = get_u16(m + 2 * k);
+        return;
+    }
+    const uint8_t* r = codes + (size_t)t * 48;
+    for (int g = 0; g < NG; g++) {
+        uint64_t lo = 0;
+        uint32_t hi = 0;
+        for (int k = 0; k < 8; k++) lo |= (uint64_t)r[12 * g + k] << (8 * k);
+        for (int k = 0; k < 4; k++) hi |= (uint32_t)r[12 * g + 8 + k] << (8 * k);
+        for (int e = 0; e < 32; e++)
+            code[32 * g + e] = (uint8_t)(((lo >> (2 * e)) & 3) | (((hi >> e) & 1) << 2));
+    }
+    for (int k = 0; k < 8; k++) meta8[k] = 0;
+    if (pc->scheme == ORC_TURBO_QJL) {
+        meta8[0] = get_u16(meta + (size_t)t * 4);
+        meta8[1] = get_u16(meta + (size_t)t * 4 + 2);
+        if (bits)
+            for (int i = 0; i < D; i++) bits[i] = (qjl[(size_t)t * 16 + i / 8] >> (i % 8)) & 1;
+    } else {
+        meta8[0] = get_u16(meta + (size_t)t * 2);
+    }
+}
+
+/* Append semantics (reading C7): every token is coded when it is appended; with W > 0 the
+ * original binary32 values of token t also go to ring slot t % W, so after any sequence of
+ * appends the ring holds the originals of the last min(n, W) tokens. */
+void orc_plane_append(const orc_plane_cfg* pc, const orc_tables* tb, const float* X, int t0, int n,
+                      uint8_t* codes, uint8_t* meta, uint8_t* qjl, float* ring)
+{
+    for (int k = 0; k < n; k++) {
+        int t = t0 + k;
+        const float* x = X + (size_t)k * D;
+        uint8_t code[D], bits[D];
+        uint16_t s16[NG] = {0}, z16[NG] = {0}, n16 = 0, g16 = 0;
+        if (pc->scheme == ORC_UNIFORM) {
+            float y[D];
+            if (pc->rotate)
+                orc_rotate_f32(x, tb->signs, y);
+            else
+                memcpy(y, x, sizeof y);
+            if (pc->sinkhorn)
+                for (int j = 0; j < D; j++) y[j] = y[j] * tb->inv_c[j];
+            for (int g = 0; g < NG; g++) orc_quant_group(y + GS * g, pc->bits, code + GS * g, &s16[g], &z16[g]);
+        } else {
+            orc_turbo_encode(x, tb, pc->scheme == ORC_TURBO_QJL, NULL, code, &n16, &g16, bits, NULL);
+        }
+        pack_token(pc, t, code, s16, z16, n16, g16, bits, codes, meta, qjl);
+        if (pc->window > 0) memcpy(ring + (size_t)(t % pc->window) * D, x, sizeof(float) * D);
+    }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* dequantization and attention                                                                */
+/* ------------------------------------------------------------------------------------------ */
+
+void orc_dequant_token(const orc_plane_cfg* pc, const orc_tables* tb, const uint8_t* codes,
+                       const uint8_t* meta, int t, double* out)
+{
+    uint8_t code[D];
+    uint16_t m8[8];
+    double y[D];
+    orc_plane_read(pc, codes, meta, NULL, t, code, m8, NULL);
+    if (pc->scheme == ORC_UNIFORM) {
+        for (int j = 0; j < D; j++) {
+            int g = j / GS;
+            double s = orc_f16_to_f32(m8[g]), z = orc_f16_to_f32(m8[4 + g]);
+            y[j] = z + s * (double)code[j]; /* exact in binary64 */
+            if (pc->sinkhorn) y[j] = y[j] * (double)tb->c[j];
+        }
+        if (pc->rotate)
+            orc_unrotate_f64(y, tb->signs, out);
+        else
+            memcpy(out, y, sizeof y);
+        return;
+    }
+    double n = orc_f16_to_f32(m8[0]);
+    for (int j = 0; j < D; j++) y[j] = n * (double)tb->mu[code[j]];
+    orc_unrotate_f64(y, tb->signs, out);
+}
+
+/* <q, k_t> ~= n <rho_q, mu[code]> + gamma sqrt(pi/2)/128 sum_i sign_i (S rho_q)_i, where
+ * rho_q = R(q) and sign_i = 2 bit_i - 1.  The second term is the QJL estimate of <rho_q, r> from
+ * E[sign(s.r) (s.x)] = sqrt(2/pi) <x, r> / |r| for s ~ N(0, I). */
+double orc_turbo_score(const orc_tables* tb, const uint8_t* codes, const uint8_t* meta,
+                       const uint8_t* qjl, int t, const double* rho_q, const double* s_rho_q)
+{
+    orc_plane_cfg pc = {ORC_TURBO_QJL, 3, 1, 0, 0, ORC_TENSOR_K, t + 1};
+    uint8_t code[D], bits[D];
+    uint16_t m8[8];
+    orc_plane_read(&pc, codes, meta, qjl, t, code, m8, bits);
+    double n = orc_f16_to_f32(m8[0]), gam = orc_f16_to_f32(m8[1]);
+    double a = 0.0, b = 0.0;
+    for (int j = 0; j < D; j++) a += rho_q[j] * (double)tb->mu[code[j]];
+    for (int i = 0; i < D; i++) b += (bits[i] ? 1.0 : -1.0) * s_rho_q[i];
+    return n * a + gam * sqrt(ORC_PI / 2.0) / 128.0 * b;
+}
+
+void orc_attention(const orc_plane_cfg* kc, const orc_plane_cfg* vc, const orc_tables* ktb,
+                   const orc_tables* vtb, const uint8_t* kcodes, const uint8_t* kmeta,
+                   const uint8_t* kqjl, const float* kring, const uint8_t* vcodes,
+                   const uint8_t* vmeta, const float* vring, int n, int G, const float* q,
+                   double scale, double* out)
+{
+    if (n <= 0) {
+        for (int i = 0; i < G * D; i++) out[i] = 0.0;
+        return;
+    }
+    int W = kc->window;
+    int nq = (W > 0 && n > W) ? n - W : (W > 0 ? 0 : n); /* tokens read from the codes */
+    double* V = (double*)malloc(sizeof(double) * (size_t)n * D);
+    double* K = NULL;
+    if (kc->scheme != ORC_TURBO_QJL) K = (double*)malloc(sizeof(double) * (size_t)n * D);
+    for (int t = 0; t < n; t++) {
+        if (t >= nq) { /* FP32 window token */
+            const float* kr = kring + (size_t)(t % W) * D;
+            const float* vr = vring + (size_t)(t % W) * D;
+            for (int j = 0; j < D; j++) {
+                if (K) K[(size_t)t * D + j] = kr[j];
+                V[(size_t)t * D + j] = vr[j];
+            }
+        } else {
+            if (K) orc_dequant_token(kc, ktb, kcodes, kmeta, t, K + (size_t)t * D);
+            orc_dequant_token(vc, vtb, vcodes, vmeta, t, V + (size_t)t * D);
+        }
+    }
+    double* a = (double*)malloc(sizeof(double) * (size_t)n);
+    for (int h = 0; h < G; h++) {
+        const float* qh = q + (size_t)h * D;
+        double qd[D], rq[D], srq[D];
+        for (int j = 0; j < D; j++) qd[j] = qh[j];
+        if (!K) {
+            orc_rotate_f64(qd, ktb->signs, rq);
+            for (int i = 0; i < D; i++) {
+                double s = 0.0;
+                for (int j = 0; j < D; j++) s += (double)ktb->S[i * D + j] * rq[j];
+                srq[i] = s;
+            }
+        }
+        double mx = -INFINITY;
+        for (int t = 0; t < n; t++) {
+            double s;
+            if (K || t >= nq) {
+                s = 0.0;
+                if (t >= nq) {
+                    const float* kr = kring + (size_t)(t % W) * D;
+                    for (int j = 0; j < D; j++) s += qd[j] * (double)kr[j];
+                } else {
+                    for (int j = 0; j < D; j++) s += qd[j] * K[(size_t)t * D + j];
+                }
+            } else {
+                s = orc_turbo_score(ktb, kcodes, kmeta, kqjl, t, rq, srq);
+            }
+            a[t] = scale * s;
+            if (a[t] > mx) mx = a[t];
+        }
+        double l = 0.0;
+        double o[D];
+        for (int j = 0; j < D; j++) o[j] = 0.0;
+        for (int t = 0; t < n; t++) {
+            double p = exp(a[t] - mx);
+            l += p;
+            for (int j = 0; j < D; j++) o[j] += p * V[(size_t)t * D + j];
+        }
+        for (int j = 0; j < D; j++) out[(size_t)h * D + j] = o[j] / l;
+    }
+    free(a);
+    free(V);
+    free(K);
+}

@@ -1,0 +1,119 @@
+/*
+ * kvq_oracle.h -- plain C CPU oracle for the compressed-KV decode-attention path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of
+ * bench.py may load this library.  It shares no code, header, table or generator with the HIP
+ * library under quantized_decode_attention_kvq_amd/.
+ *
+ * What it follows (pages, by title and section):
+ *  - quantcpp article ("Beyond RAG: load whole documents on your laptop"), the progressive table
+ *    and its "how it works" paragraph: 4-bit KV with the most recent 128 tokens kept in FP32,
+ *    6.4x compression (4-bit codes + fp16 scale + fp16 zero per 32 values).
+ *  - KVarN-on-Bonsai post, TL;DR paragraph: Walsh-Hadamard transform plus Sinkhorn variance
+ *    balancing before 4-bit quantization.
+ *  - "LLM memory saving: weights vs KV-cache quantization 2026", method comparison table
+ *    (TurboQuant row "core idea"): random rotation, per-coordinate optimal scalar quantizer,
+ *    1-bit QJL on the residual for an unbiased inner product.
+ * Every step the pages leave open is fixed by a stated reading (see the .c file's comments).
+ *
+ * Arithmetic conventions: binary32 round-to-nearest-even with no FMA contraction (the library is
+ * built with -ffp-contract=off; fmaf is called only where the format says "fused"), denormals
+ * preserved, binary16 converted by integer manipulation, attention in binary64.
+ */
+#ifndef KVQ_ORACLE_H
+#define KVQ_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORC_D 128
+#define ORC_GROUP 32
+#define ORC_NGROUPS 4
+
+enum { ORC_UNIFORM = 0, ORC_TURBO_QJL = 1, ORC_TURBO_MSE = 2 };
+enum { ORC_TENSOR_K = 0, ORC_TENSOR_V = 1 };
+
+/* One (layer, sequence, kv head, tensor) plane description. */
+typedef struct {
+    int scheme;    /* ORC_UNIFORM / ORC_TURBO_QJL / ORC_TURBO_MSE */
+    int bits;      /* uniform: 4 or 8; turbo: 3 */
+    int rotate;    /* random-sign WHT before coding (always on for turbo) */
+    int sinkhorn;  /* fold 1/c before uniform coding */
+    int window;    /* FP32 window W: 0 (flat) or 128 (progressive) */
+    int tensor;    /* ORC_TENSOR_K or ORC_TENSOR_V: selects the code layout */
+    int capacity;  /* tokens the plane can hold */
+} orc_plane_cfg;
+
+/* Tables for one (layer, kv head, tensor) plus the per-cache turbo tables. */
+typedef struct {
+    const float* signs;  /* [128] +-1, used when rotate */
+    const float* c;      /* [128] Sinkhorn channel scale (NULL = all ones) */
+    const float* inv_c;  /* [128] fp32(1/c) (NULL = all ones) */
+    const float* S;      /* [128*128] QJL projection, row-major S[i][j] */
+    const float* mu;     /* [8] Lloyd-Max centroids for N(0,1/128), fp32 */
+    const float* theta;  /* [7] decision thresholds, fp32 */
+} orc_tables;
+
+/* ---- binary16 ---- */
+uint16_t orc_f32_to_f16_rn(float x);
+uint16_t orc_f32_to_f16_rd(float x);
+float orc_f16_to_f32(uint16_t h);
+
+/* ---- rotation R(x) = c0 * H (d .* x) ---- */
+void orc_rotate_f32(const float* x, const float* signs, float* y);
+void orc_rotate_f64(const double* x, const float* signs, double* y);
+void orc_unrotate_f64(const double* y, const float* signs, double* x);
+
+/* ---- Sinkhorn variance balancing (calibration) ---- */
+void orc_sinkhorn(const float* X, int n, const float* signs_or_null, int iters, float* c,
+                  float* inv_c, double* A_out /* [n*128] or NULL */, double* C_out /* [128] or NULL */);
+
+/* ---- uniform asymmetric group quantizer ---- */
+void orc_quant_group(const float* y, int bits, uint8_t* codes, uint16_t* s16, uint16_t* z16);
+
+/* ---- Lloyd-Max codebook ---- */
+void orc_lloyd_max(int iters, double* mu_star, float* mu, float* theta, double* last_change);
+
+/* ---- TurboQuant token code ---- */
+void orc_turbo_encode(const float* x, const orc_tables* tb, int with_qjl, float* rho_out,
+                      uint8_t* codes, uint16_t* n16, uint16_t* g16, uint8_t* bits,
+                      float* resid_out);
+float orc_tree_sum_sq(const float* v);
+
+/* ---- planes ---- */
+size_t orc_codes_bytes(const orc_plane_cfg* pc);
+size_t orc_meta_bytes(const orc_plane_cfg* pc);
+size_t orc_qjl_bytes(const orc_plane_cfg* pc);
+size_t orc_ring_floats(const orc_plane_cfg* pc);
+
+/* Append tokens t0..t0+n-1 (X: [n][128] fp32 originals) to one plane, one token at a time. */
+void orc_plane_append(const orc_plane_cfg* pc, const orc_tables* tb, const float* X, int t0, int n,
+                      uint8_t* codes, uint8_t* meta, uint8_t* qjl, float* ring);
+
+/* Read back token t's unpacked code fields. */
+void orc_plane_read(const orc_plane_cfg* pc, const uint8_t* codes, const uint8_t* meta,
+                    const uint8_t* qjl, int t, uint8_t* code128, uint16_t* meta8, uint8_t* bits128);
+
+/* Dequantized token in the ORIGINAL domain (uniform / turbo-MSE; fp64). */
+void orc_dequant_token(const orc_plane_cfg* pc, const orc_tables* tb, const uint8_t* codes,
+                       const uint8_t* meta, int t, double* out);
+
+/* Turbo-QJL score estimate of <q, k_t> (fp64, unscaled). */
+double orc_turbo_score(const orc_tables* tb, const uint8_t* codes, const uint8_t* meta,
+                       const uint8_t* qjl, int t, const double* rho_q, const double* s_rho_q);
+
+/* Decode attention for one kv head and its G query heads, fp64. */
+void orc_attention(const orc_plane_cfg* kc, const orc_plane_cfg* vc, const orc_tables* ktb,
+                   const orc_tables* vtb, const uint8_t* kcodes, const uint8_t* kmeta,
+                   const uint8_t* kqjl, const float* kring, const uint8_t* vcodes,
+                   const uint8_t* vmeta, const float* vring, int n, int G, const float* q,
+                   double scale, double* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

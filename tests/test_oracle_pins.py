@@ -1,0 +1,636 @@
+"""Pins of the CPU oracle against things other than itself: library routines, closed forms,
+invariants, brute force on small inputs and the numbers the pages print.
+
+Each test says what a plausible mistake in the oracle would break.  No test here needs a GPU.
+"""
+import os
+
+import numpy as np
+import pytest
+import scipy.integrate
+import scipy.linalg
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    out = {}
+    for line in open(os.path.join(GOLD, name)):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            k, v = line.split()
+            out[k] = v
+    return out
+
+
+def _f16_bits_np(x32):
+    return np.asarray(x32, np.float32).astype(np.float16).view(np.uint16)
+
+
+# ---------------------------------------------------------------------------------------------
+# binary16 conversions vs numpy (an independent, correctly rounded implementation)
+# ---------------------------------------------------------------------------------------------
+
+def test_f16_rn_matches_numpy():
+    rng = np.random.default_rng(1)
+    xs = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(10.0) ** rng.integers(-9, 5, 20000),
+        np.float32([0.0, -0.0, 65504.0, 65519.99, 65520.0, -65520.0, 6.1e-5, 5.96e-8, 2.98e-8,
+                    2.99e-8, 1e-9, 1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, 2049.0, 2051.0]),
+    ]).astype(np.float32)
+    # include exact binary16 midpoints (ties) in the normal and subnormal ranges
+    h = rng.integers(0, 0x7bff, 5000).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    mids = ((lo + hi) / 2).astype(np.float32)
+    xs = np.concatenate([xs, mids, -mids])
+    ref = _f16_bits_np(xs)
+    got = np.array([oracle.f32_to_f16_rn(x) for x in xs], np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_f16_to_f32_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([oracle.f16_to_f32(int(b)) for b in bits], np.float32)
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite].view(np.uint32), ref[finite].view(np.uint32))
+    assert np.all(np.isnan(got[np.isnan(ref)]))
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+
+
+def test_f16_round_down_is_floor():
+    rng = np.random.default_rng(2)
+    xs = (rng.standard_normal(20000) * 10.0 ** rng.integers(-8, 4, 20000)).astype(np.float32)
+    xs = np.concatenate([xs, np.float32([0.0, -0.0, 1e-9, -1e-9, -6e-8, 3.0, -3.0])])
+    for x in xs:
+        h = oracle.f32_to_f16_rd(x)
+        v = np.uint16(h).view(np.float16)
+        assert float(v) <= float(x)
+        up = np.nextafter(v, np.float16(np.inf))
+        assert float(up) > float(x)
+
+
+# ---------------------------------------------------------------------------------------------
+# rotation: Sylvester closed form, orthonormality, inverse (library: scipy.linalg.hadamard)
+# ---------------------------------------------------------------------------------------------
+
+def _signs(seed):
+    return np.where(np.random.default_rng(seed).random(128) < 0.5, -1.0, 1.0).astype(np.float32)
+
+
+def test_rotation_sylvester_closed_form_exact():
+    # R(e_i) has entries d_i * (-1)^popcount(i & j) * c0 exactly: no rounding happens before the
+    # final multiply.  A wrong butterfly index or a transposed operand changes the sign pattern.
+    d = _signs(3)
+    H = scipy.linalg.hadamard(128)
+    c0 = np.uint32(0x3DB504F3).view(np.float32)
+    for i in range(128):
+        e = np.zeros(128, np.float32)
+        e[i] = 1.0
+        y = oracle.rotate_f32(e, d)
+        ref = (H[:, i] * d[i]).astype(np.float32) * c0
+        assert np.array_equal(y, ref), i
+
+
+def test_rotation_matches_matrix_and_inverse():
+    d = _signs(4)
+    H = scipy.linalg.hadamard(128).astype(np.float64)
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        x = rng.standard_normal(128).astype(np.float32) * 3
+        ref = H @ (d.astype(np.float64) * x) / np.sqrt(128.0)
+        y32 = oracle.rotate_f32(x, d)
+        y64 = oracle.rotate_f64(x.astype(np.float64), d)
+        assert np.max(np.abs(y32 - ref)) <= 1e-6 * np.max(np.abs(ref))
+        assert np.allclose(y64, ref, rtol=0, atol=1e-12)
+        nx = np.linalg.norm(x.astype(np.float64))
+        assert abs(np.linalg.norm(y64) - nx) < 1e-12 * nx
+        back = oracle.unrotate_f64(y64, d)
+        assert np.allclose(back, x, rtol=0, atol=1e-12)
+        back32 = oracle.unrotate_f64(y32.astype(np.float64), d)
+        assert np.max(np.abs(back32 - x)) <= 1e-6 * np.max(np.abs(x))
+
+
+def test_rotation_of_sign_vector_is_scaled_e0():
+    d = _signs(6)
+    y = oracle.rotate_f64(d.astype(np.float64), d)
+    ref = np.zeros(128)
+    ref[0] = np.sqrt(128.0)
+    assert np.allclose(y, ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# uniform group quantizer
+# ---------------------------------------------------------------------------------------------
+
+def _deq(codes, s16, z16):
+    s = float(np.uint16(s16).view(np.float16))
+    z = float(np.uint16(z16).view(np.float16))
+    return z + s * codes.astype(np.float64), s, z
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quant_group_error_bound_and_range(bits):
+    L = (1 << bits) - 1
+    rng = np.random.default_rng(10 + bits)
+    for k in range(3000):
+        scale = 10.0 ** rng.uniform(-4, 2)
+        y = (rng.standard_normal(32) * scale + rng.uniform(-3, 3) * scale).astype(np.float32)
+        codes, s16, z16 = oracle.quant_group(y, bits)
+        assert codes.max() <= L
+        yh, s, z = _deq(codes, s16, z16)
+        assert z <= y.min()
+        err = np.abs(y.astype(np.float64) - yh)
+        slack = 4 * np.spacing(np.abs(y - np.float32(z)).astype(np.float32)).astype(np.float64)
+        # |y - yhat| <= s/2 + L |s32 - s16|; the fp16 rounding of the scale is at most half an
+        # fp16 ulp of s, which is negligible for normal s and 2^-25 for subnormal s.
+        ulp16 = float(np.spacing(np.float16(s))) if s > 0 else 2.0 ** -24
+        assert np.all(err <= s / 2 + L * ulp16 / 2 + slack + 1e-12), (k, err.max(), s)
+        if s >= 2.0 ** -14:
+            assert np.all(err <= s / 2 + L * s * 2.0 ** -12 + slack + 1e-12)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quant_group_brute_force_nearest_level(bits):
+    # code = argmin_c |y - (z + s c)| over all L+1 levels, except inputs within float rounding
+    # of a tie between two levels.
+    L = (1 << bits) - 1
+    rng = np.random.default_rng(20 + bits)
+    for _ in range(2000):
+        y = (rng.standard_normal(32) * rng.uniform(0.01, 5)).astype(np.float32)
+        codes, s16, z16 = oracle.quant_group(y, bits)
+        _, s, z = _deq(codes, s16, z16)
+        levels = z + s * np.arange(L + 1)
+        dist = np.abs(y.astype(np.float64)[:, None] - levels[None, :])
+        best = dist.argmin(1)
+        frac = (y.astype(np.float64) - z) / s
+        near_tie = np.abs(np.abs(frac - np.floor(frac)) - 0.5) < 1e-5
+        clipped = frac > L + 0.5
+        ok = (best == codes) | near_tie | clipped
+        assert ok.all()
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_quant_group_grid_points_recovered(bits):
+    # y = z + s*c with fp16 z, s and the extreme codes 0 and L present: lossless.
+    L = (1 << bits) - 1
+    rng = np.random.default_rng(30 + bits)
+    for _ in range(500):
+        # z on a 2^-8 grid and s on a 2^-12 grid keep z + s*c exact in binary32
+        z = np.float16(rng.integers(-1024, 256) / 256.0)
+        s = np.float16(rng.integers(40, 2000) / 4096.0)
+        c = rng.integers(0, L + 1, 32)
+        c[0], c[1] = 0, L
+        rng.shuffle(c)
+        y = (np.float64(z) + np.float64(s) * c).astype(np.float32)
+        assert np.array_equal(y.astype(np.float64), np.float64(z) + np.float64(s) * c)
+        codes, s16, z16 = oracle.quant_group(y, bits)
+        assert np.array_equal(codes, c)
+        assert s16 == int(np.float16(s).view(np.uint16))
+        assert z16 == int(np.float16(z).view(np.uint16))
+
+
+def test_quant_group_degenerate_cases():
+    codes, s16, z16 = oracle.quant_group(np.full(32, 1.25, np.float32), 4)
+    assert s16 == 0 and np.all(codes == 0) and np.uint16(z16).view(np.float16) == np.float16(1.25)
+    y = np.zeros(32, np.float32)
+    y[::2] = -0.0
+    codes, s16, z16 = oracle.quant_group(y, 4)
+    assert s16 == 0 and z16 == 0 and np.all(codes == 0)  # -0 canonicalised to +0
+
+
+def test_quant_group_monotone_in_value():
+    rng = np.random.default_rng(40)
+    y = np.sort(rng.standard_normal(32).astype(np.float32))
+    codes, _, _ = oracle.quant_group(y, 4)
+    assert np.all(np.diff(codes.astype(int)) >= 0)
+
+
+# ---------------------------------------------------------------------------------------------
+# plane layouts: hand-derived golden words, round trips, sizes printed on the pages
+# ---------------------------------------------------------------------------------------------
+
+def _word(buf, w):
+    return int(np.frombuffer(buf[4 * w:4 * w + 4].tobytes(), np.uint32)[0])
+
+
+def test_layout_golden_words():
+    g = _golden("layout_words.txt")
+    tb = oracle.TableSet()
+    # One K token whose groups are exactly on the grid: codes j % 16 with s = 1, z = 0.
+    x = (np.arange(128) % 16).astype(np.float32)
+    pk = oracle.Plane(oracle.UNIFORM, 4, False, False, 0, oracle.TENSOR_K, 128)
+    pk.append(np.zeros((5, 128), np.float32), tb)
+    pk.append(x, tb)  # token 5
+    row = int(g["k_row_of_t5"])
+    rowbytes = pk.codes[64 * row:64 * row + 64]
+    assert hex(_word(rowbytes, 0)) == g["k4_word0"]
+    assert hex(_word(rowbytes, 1)) == g["k4_word1"]
+    assert hex(_word(rowbytes, 4)) == g["k4_word4"]
+    code, meta8, _ = pk.read(5)
+    assert np.array_equal(code, np.arange(128) % 16)
+    pk2 = oracle.Plane(oracle.UNIFORM, 4, False, False, 0, oracle.TENSOR_K, 128)
+    pk2.append(np.zeros((70, 128), np.float32), tb)
+    pk2.append(x, tb)  # token 70
+    r70 = int(g["k_row_of_t70"])
+    assert hex(_word(pk2.codes[64 * r70:64 * r70 + 64], 0)) == g["k4_word0"]
+    # V: tokens 0..7 with channel 0 = token index (and channel 1 pinned to 15 so s = 1, z = 0).
+    pv = oracle.Plane(oracle.UNIFORM, 4, False, False, 0, oracle.TENSOR_V, 64)
+    X = np.zeros((16, 128), np.float32)
+    X[:, 1] = 15.0
+    X[:8, 0] = np.arange(8)
+    X[9, 17] = 7.0
+    pv.append(X, tb)
+    assert hex(_word(pv.codes, 0)) == g["v4_word0_tokens0to7"]
+    w = int(g["v4_d17_t9_word"])
+    bit = int(g["v4_d17_t9_bit"])
+    assert (_word(pv.codes, w) >> bit) & 0xF == 7
+
+
+@pytest.mark.parametrize("scheme,bits,tensor", [
+    (oracle.UNIFORM, 4, oracle.TENSOR_K), (oracle.UNIFORM, 4, oracle.TENSOR_V),
+    (oracle.UNIFORM, 8, oracle.TENSOR_K), (oracle.UNIFORM, 8, oracle.TENSOR_V),
+    (oracle.TURBO_QJL, 3, oracle.TENSOR_K), (oracle.TURBO_MSE, 3, oracle.TENSOR_V)])
+def test_layout_round_trip_and_disjoint(scheme, bits, tensor):
+    # Every token's fields read back exactly, and writing token t never disturbs another token.
+    rng = np.random.default_rng(50)
+    n = 150
+    d = _signs(7)
+    S = rng.standard_normal((128, 128)).astype(np.float32)
+    _, mu, theta, _ = oracle.lloyd_max()
+    tb = oracle.TableSet(signs=d, S=S, mu=mu, theta=theta)
+    X = rng.standard_normal((n, 128)).astype(np.float32)
+    p = oracle.Plane(scheme, bits, False, False, 0, tensor, 200)
+    p.append(X, tb)
+    for t in range(n):
+        code, meta8, qbits = p.read(t)
+        if scheme == oracle.UNIFORM:
+            y = X[t]
+            for gi in range(4):
+                c, s16, z16 = oracle.quant_group(y[32 * gi:32 * gi + 32], bits)
+                assert np.array_equal(code[32 * gi:32 * gi + 32], c)
+                assert meta8[gi] == s16 and meta8[4 + gi] == z16
+        else:
+            enc = oracle.turbo_encode(X[t], tb, scheme == oracle.TURBO_QJL)
+            assert np.array_equal(code, enc["codes"])
+            assert meta8[0] == enc["n16"]
+            if scheme == oracle.TURBO_QJL:
+                assert meta8[1] == enc["g16"] and np.array_equal(qbits, enc["bits"])
+    # tokens never written read back as zero codes and zero meta
+    code, meta8, _ = p.read(n + 3)
+    assert not code.any() and not meta8.any()
+
+
+def test_sizes_printed_on_pages():
+    g = _golden("pages_numbers.txt")
+    p = oracle.Plane(oracle.UNIFORM, 4, False, False, 0, oracle.TENSOR_K, 64)
+    per_token = (p.codes.size + p.meta.size) / 64
+    assert per_token == 80
+    assert round(512 / per_token, 1) == float(g["kv_compression_4bit"])
+    W = int(g["window_tokens"])
+    assert round(100 * W / int(g["progressive_context"]), 1) == float(g["progressive_fp32_percent"])
+    assert round(100 * W / int(g["long_context"]), 1) == float(g["long_fp32_percent"])
+
+
+def test_window_ring_holds_last_w_originals():
+    rng = np.random.default_rng(60)
+    tb = oracle.TableSet()
+    p = oracle.Plane(oracle.UNIFORM, 4, False, False, 128, oracle.TENSOR_K, 1000)
+    X = rng.standard_normal((300, 128)).astype(np.float32)
+    p.append(X[:77], tb)
+    p.append(X[77:300], tb)
+    ring = p.ring.reshape(128, 128)
+    for t in range(300 - 128, 300):
+        assert np.array_equal(ring[t % 128], X[t])
+
+
+# ---------------------------------------------------------------------------------------------
+# Sinkhorn invariants
+# ---------------------------------------------------------------------------------------------
+
+def test_sinkhorn_columns_unit_std_and_divisor_bookkeeping():
+    rng = np.random.default_rng(70)
+    sig = np.exp(rng.uniform(np.log(0.1), np.log(10), 128))
+    X = (rng.standard_normal((512, 128)) * sig).astype(np.float32)
+    d = _signs(8)
+    c, inv_c, A, C = oracle.sinkhorn(X, d, 5, want_internals=True)
+    col_std = A.std(axis=0)
+    assert np.allclose(col_std, 1.0, atol=1e-12)  # the last sweep is a column sweep
+    # A = diag(1/r) Y diag(1/C) for some row factors r: Y / (A * C) is constant along each row.
+    Y = np.stack([oracle.rotate_f32(x, d) for x in X]).astype(np.float64)
+    ratio = Y / (A * C[None, :])
+    assert np.allclose(ratio, ratio[:, :1], rtol=1e-12)
+    assert np.array_equal(c, C.astype(np.float32))
+    assert np.array_equal(inv_c, (1.0 / c.astype(np.float64)).astype(np.float32))
+
+
+def test_sinkhorn_row_scaling_invariance_exact():
+    # Power-of-two row scaling commutes exactly with the binary32 rotation and with the first
+    # row normalisation, so c must be bit-identical.
+    rng = np.random.default_rng(71)
+    X = rng.standard_normal((512, 128)).astype(np.float32)
+    X2 = X.copy()
+    X2[::3] *= np.float32(8.0)
+    X2[1::7] *= np.float32(0.25)
+    d = _signs(9)
+    c1, _ = oracle.sinkhorn(X, d, 5)
+    c2, _ = oracle.sinkhorn(X2, d, 5)
+    assert np.array_equal(c1, c2)
+
+
+def test_sinkhorn_recovers_column_scales():
+    # Rank-one variance structure Y_tj = r_t s_j z_tj: balancing returns C proportional to s.
+    rng = np.random.default_rng(72)
+    s = np.exp(rng.uniform(np.log(0.1), np.log(10), 128))
+    r = np.exp(rng.uniform(np.log(0.5), np.log(2), 512))
+    Y = (r[:, None] * s[None, :] * rng.standard_normal((512, 128))).astype(np.float32)
+    c, _ = oracle.sinkhorn(Y, None, 5)
+    ratio = c.astype(np.float64) / s
+    assert np.std(np.log(ratio)) < 0.1
+
+
+def test_sinkhorn_row_permutation_invariance():
+    rng = np.random.default_rng(73)
+    X = (rng.standard_normal((512, 128)) * rng.uniform(0.1, 3, 128)).astype(np.float32)
+    d = _signs(10)
+    c1, _ = oracle.sinkhorn(X, d, 5)
+    c2, _ = oracle.sinkhorn(X[rng.permutation(512)], d, 5)
+    assert np.allclose(c1, c2, rtol=1e-6)
+
+
+# ---------------------------------------------------------------------------------------------
+# Lloyd-Max codebook
+# ---------------------------------------------------------------------------------------------
+
+def test_lloyd_max_fixed_point_symmetry_and_conditions():
+    mu_star, mu, theta, change = oracle.lloyd_max(oracle.LLOYD_ITERS)
+    assert change == 0.0
+    assert np.array_equal(mu_star[:4], -mu_star[::-1][:4])
+    assert theta[3] == 0.0
+    assert np.array_equal(mu[:4], -mu[::-1][:4])
+    # centroid condition, by independent numerical integration (scipy.integrate.quad)
+    phi = lambda x: np.exp(-0.5 * x * x) / np.sqrt(2 * np.pi)
+    b = [-np.inf] + [(mu_star[k] + mu_star[k + 1]) / 2 for k in range(7)] + [np.inf]
+    mse = 0.0
+    for k in range(8):
+        m0 = scipy.integrate.quad(phi, b[k], b[k + 1], epsabs=1e-14)[0]
+        m1 = scipy.integrate.quad(lambda x: x * phi(x), b[k], b[k + 1], epsabs=1e-14)[0]
+        assert abs(m1 / m0 - mu_star[k]) < 1e-9
+        mse += scipy.integrate.quad(lambda x: (x - mu_star[k]) ** 2 * phi(x), b[k], b[k + 1],
+                                    epsabs=1e-14)[0]
+    # textbook distortion of the 8-level Gaussian Lloyd-Max quantizer (Max, 1960): about 0.0345
+    assert 0.0340 < mse < 0.0350
+    # fp32 tables = rounding of the fp64 fixed point scaled by 1/sqrt(128)
+    assert np.array_equal(mu, (mu_star / np.sqrt(128.0)).astype(np.float32))
+
+
+def test_lloyd_max_agrees_with_kmeans_on_samples():
+    mu_star, _, _, _ = oracle.lloyd_max()
+    x = np.sort(np.random.default_rng(80).standard_normal(2_000_000))
+    m = np.array([-2.0, -1.3, -0.7, -0.2, 0.2, 0.7, 1.3, 2.0])
+    for _ in range(200):
+        edges = (m[1:] + m[:-1]) / 2
+        idx = np.searchsorted(edges, x)
+        m = np.array([x[idx == k].mean() for k in range(8)])
+    assert np.max(np.abs(m - mu_star)) < 5e-3
+
+
+# ---------------------------------------------------------------------------------------------
+# TurboQuant token code and the QJL estimator
+# ---------------------------------------------------------------------------------------------
+
+def _turbo_tables(seed=90):
+    rng = np.random.default_rng(seed)
+    _, mu, theta, _ = oracle.lloyd_max()
+    return oracle.TableSet(signs=_signs(seed), S=rng.standard_normal((128, 128)).astype(np.float32),
+                           mu=mu, theta=theta), mu, theta
+
+
+def test_turbo_code_is_nearest_centroid_and_residual_definition():
+    tb, mu, theta = _turbo_tables()
+    rng = np.random.default_rng(91)
+    S = tb.arrays["S"].reshape(128, 128).astype(np.float64)
+    for _ in range(300):
+        x = (rng.standard_normal(128) * rng.uniform(0.1, 5)).astype(np.float32)
+        e = oracle.turbo_encode(x, tb, True)
+        n = float(np.uint16(e["n16"]).view(np.float16))
+        assert abs(n - np.linalg.norm(x.astype(np.float64))) <= 2 ** -10 * n
+        u = e["rho"].astype(np.float64) / n
+        best = np.abs(u[:, None] - mu.astype(np.float64)[None, :]).argmin(1)
+        mids = (mu[1:].astype(np.float64) + mu[:-1]) / 2
+        near = np.min(np.abs(u[:, None] - mids[None, :]), 1) < 1e-6
+        assert np.all((best == e["codes"]) | near)
+        r_ref = e["rho"].astype(np.float64) - n * mu[e["codes"]].astype(np.float64)
+        assert np.allclose(e["resid"], r_ref, rtol=0, atol=1e-6 * n)
+        g = float(np.uint16(e["g16"]).view(np.float16))
+        assert abs(g - np.linalg.norm(r_ref)) <= 2 ** -10 * g + 1e-7
+        proj = S @ e["resid"].astype(np.float64)
+        tiny = np.abs(proj) < 1e-5 * np.linalg.norm(e["resid"])
+        assert np.all((e["bits"] == (proj >= 0)) | tiny)
+
+
+def test_turbo_zero_key_and_centroid_aligned_key():
+    # (a) k = 0: n = 0, every code is the one just above 0's thresholds, r = 0, gamma = 0, every
+    #     QJL bit is sign(0) = +1 and the score estimate is exactly 0.
+    # (b) rho = a * mu[c]: the codes are c and r = (a - n) mu[c], so gamma = |a - n| |mu[c]|.
+    tb, mu, theta = _turbo_tables(92)
+    d = tb.arrays["signs"]
+    S64 = tb.arrays["S"].reshape(128, 128).astype(np.float64)
+    plane = oracle.Plane(oracle.TURBO_QJL, 3, True, False, 0, oracle.TENSOR_K, 4)
+    plane.append(np.zeros(128, np.float32), tb)
+    code, meta8, bits = plane.read(0)
+    assert meta8[0] == 0 and meta8[1] == 0 and np.all(bits == 1)
+    assert np.all(code == np.sum(0.0 > theta))
+    q = np.random.default_rng(94).standard_normal(128)
+    rq = oracle.rotate_f64(q, d)
+    assert plane.turbo_score(0, tb, rq, S64 @ rq) == 0.0
+    rng = np.random.default_rng(93)
+    for _ in range(20):
+        # codes of a Gaussian draw, so |mu[c]| is close to 1 and mu[c] / |mu[c]| keeps codes c
+        z = rng.standard_normal(128) / np.sqrt(128.0)
+        c = np.abs(z[:, None] - mu.astype(np.float64)[None, :]).argmin(1)
+        m = mu[c].astype(np.float64)
+        assert abs(np.linalg.norm(m) - 1) < 0.15
+        a = rng.uniform(0.5, 5.0)
+        x = oracle.unrotate_f64(a * m, d).astype(np.float32)
+        e = oracle.turbo_encode(x, tb, True)
+        assert np.array_equal(e["codes"], c)
+        n = float(np.uint16(e["n16"]).view(np.float16))
+        g = float(np.uint16(e["g16"]).view(np.float16))
+        expect = abs(a - n) * np.linalg.norm(m)
+        assert abs(g - expect) <= 2 ** -10 * expect + 1e-5 * a
+
+
+@pytest.mark.slow
+def test_qjl_estimator_unbiased_over_1e5_projections():
+    # For a fixed key k and query q, averaging the oracle's score estimate over 1e5 independent
+    # Gaussian projections S must give n<rho_q, mu[c]> + (gamma/|r|) <rho_q, r> within 5 standard
+    # errors; the standard error comes from the closed-form variance of sign(s.r)(s.x).
+    rng = np.random.default_rng(95)
+    _, mu, theta, _ = oracle.lloyd_max()
+    d = _signs(96)
+    k = rng.standard_normal(128).astype(np.float32)
+    q = rng.standard_normal(128)
+    rq = oracle.rotate_f64(q, d)
+    N = 100_000
+    ests = np.empty(N)
+    plane = oracle.Plane(oracle.TURBO_QJL, 3, True, False, 0, oracle.TENSOR_K, 1)
+    for s in range(N):
+        S = np.random.default_rng(1_000_000 + s).standard_normal((128, 128), dtype=np.float32)
+        tb = oracle.TableSet(signs=d, S=S, mu=mu, theta=theta)
+        plane.length = 0
+        plane.append(k, tb)
+        ests[s] = plane.turbo_score(0, tb, rq, S.astype(np.float64) @ rq)
+    e = oracle.turbo_encode(k, oracle.TableSet(signs=d, S=np.zeros((128, 128), np.float32), mu=mu,
+                                               theta=theta), True)
+    r = e["resid"].astype(np.float64)
+    n = float(np.uint16(e["n16"]).view(np.float16))
+    g = float(np.uint16(e["g16"]).view(np.float16))
+    rn = np.linalg.norm(r)
+    expect = n * float(rq @ mu[e["codes"]].astype(np.float64)) + (g / rn) * float(rq @ r)
+    var = (np.pi / 2) * g * g * (rq @ rq - (2 / np.pi) * (rq @ r) ** 2 / rn ** 2) / 128
+    se = np.sqrt(var / N)
+    assert abs(ests.mean() - expect) < 5 * se
+    assert abs(ests.var() / var - 1) < 0.05
+    # and the target is the true inner product up to the fp16 rounding of gamma
+    assert abs(expect - float(q @ k)) < 2 ** -10 * abs(float(rq @ r)) + 1e-4
+
+
+# ---------------------------------------------------------------------------------------------
+# attention: textbook special cases
+# ---------------------------------------------------------------------------------------------
+
+def _textbook(q, K, V, scale=1 / np.sqrt(128.0)):
+    a = (q.astype(np.float64) @ K.astype(np.float64).T) * scale
+    a -= a.max(axis=1, keepdims=True)
+    p = np.exp(a)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ V.astype(np.float64)
+
+
+def _grid_tokens(rng, n, bits):
+    """Tokens whose every group lies exactly on an fp16 (z, s) grid with codes 0 and L present."""
+    L = (1 << bits) - 1
+    X = np.empty((n, 128), np.float32)
+    for t in range(n):
+        for g in range(4):
+            z = np.float16(rng.uniform(-3, 0))
+            s = np.float16(rng.uniform(0.05, 0.4) * 15 / L)
+            c = rng.integers(0, L + 1, 32)
+            c[0], c[1] = 0, L
+            rng.shuffle(c)
+            X[t, 32 * g:32 * g + 32] = np.float64(z) + np.float64(s) * c
+    return X
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_attention_lossless_grid_equals_textbook(bits):
+    rng = np.random.default_rng(100 + bits)
+    n, G = 37, 3
+    K, V = _grid_tokens(rng, n, bits), _grid_tokens(rng, n, bits)
+    q = rng.standard_normal((G, 128)).astype(np.float32)
+    tb = oracle.TableSet()
+    pk = oracle.Plane(oracle.UNIFORM, bits, False, False, 0, oracle.TENSOR_K, 64)
+    pv = oracle.Plane(oracle.UNIFORM, bits, False, False, 0, oracle.TENSOR_V, 64)
+    pk.append(K, tb)
+    pv.append(V, tb)
+    out = oracle.attention(pk, pv, tb, tb, q)
+    assert np.allclose(out, _textbook(q, K, V), rtol=0, atol=1e-12)
+
+
+def test_attention_window_only_equals_textbook():
+    rng = np.random.default_rng(110)
+    n, G = 100, 3
+    K = rng.standard_normal((n, 128)).astype(np.float32) * 3
+    V = rng.standard_normal((n, 128)).astype(np.float32)
+    q = rng.standard_normal((G, 128)).astype(np.float32)
+    tb = oracle.TableSet()
+    pk = oracle.Plane(oracle.UNIFORM, 4, False, False, 128, oracle.TENSOR_K, 320)
+    pv = oracle.Plane(oracle.UNIFORM, 4, False, False, 128, oracle.TENSOR_V, 320)
+    pk.append(K, tb)
+    pv.append(V, tb)
+    assert np.allclose(oracle.attention(pk, pv, tb, tb, q), _textbook(q, K, V), atol=1e-12)
+    # beyond the window: the last 128 tokens use originals, the rest the dequantized values
+    K2 = rng.standard_normal((200, 128)).astype(np.float32)
+    V2 = rng.standard_normal((200, 128)).astype(np.float32)
+    pk.append(K2, tb)
+    pv.append(V2, tb)
+    Kall, Vall = np.concatenate([K, K2]), np.concatenate([V, V2])
+    Kd = Kall.astype(np.float64).copy()
+    Vd = Vall.astype(np.float64).copy()
+    for t in range(300 - 128):
+        Kd[t] = pk.dequant(t, tb)
+        Vd[t] = pv.dequant(t, tb)
+    assert np.allclose(oracle.attention(pk, pv, tb, tb, q), _textbook(q, Kd, Vd), atol=1e-12)
+
+
+def test_attention_single_token_and_equal_keys():
+    rng = np.random.default_rng(120)
+    tb = oracle.TableSet()
+    pk = oracle.Plane(oracle.UNIFORM, 4, False, False, 0, oracle.TENSOR_K, 64)
+    pv = oracle.Plane(oracle.UNIFORM, 4, False, False, 0, oracle.TENSOR_V, 64)
+    k = rng.standard_normal(128).astype(np.float32)
+    V = rng.standard_normal((20, 128)).astype(np.float32)
+    pk.append(k, tb)
+    pv.append(V[0], tb)
+    q = rng.standard_normal((2, 128)).astype(np.float32)
+    out = oracle.attention(pk, pv, tb, tb, q)
+    assert np.allclose(out, pv.dequant(0, tb)[None, :], atol=1e-12)
+    for t in range(1, 20):
+        pk.append(k, tb)
+        pv.append(V[t], tb)
+    out = oracle.attention(pk, pv, tb, tb, q)
+    mean_v = np.mean([pv.dequant(t, tb) for t in range(20)], axis=0)
+    assert np.allclose(out, mean_v[None, :], atol=1e-12)
+
+
+@pytest.mark.parametrize("bits,bound", [(4, 0.15), (8, 0.03)])
+def test_attention_rotated_sinkhorn_close_to_exact(bits, bound):
+    # With rotation and Sinkhorn folding the cache is lossy, but a sign, index or fold mistake
+    # gives O(1) errors; a correct one stays within the quantizer's error.
+    rng = np.random.default_rng(130 + bits)
+    sig = np.exp(rng.uniform(np.log(0.1), np.log(10), 128))
+    n = 300
+    K = (rng.standard_normal((n, 128)) * sig).astype(np.float32)
+    V = (rng.standard_normal((n, 128)) * sig).astype(np.float32)
+    q = rng.standard_normal((3, 128)).astype(np.float32)
+    dk, dv = _signs(131), _signs(132)
+    ck, ick = oracle.sinkhorn((rng.standard_normal((512, 128)) * sig).astype(np.float32), dk, 5)
+    cv, icv = oracle.sinkhorn((rng.standard_normal((512, 128)) * sig).astype(np.float32), dv, 5)
+    tk = oracle.TableSet(signs=dk, c=ck, inv_c=ick)
+    tv = oracle.TableSet(signs=dv, c=cv, inv_c=icv)
+    pk = oracle.Plane(oracle.UNIFORM, bits, True, True, 0, oracle.TENSOR_K, 320)
+    pv = oracle.Plane(oracle.UNIFORM, bits, True, True, 0, oracle.TENSOR_V, 320)
+    pk.append(K, tk)
+    pv.append(V, tv)
+    out = oracle.attention(pk, pv, tk, tv, q)
+    ref = _textbook(q, K, V)
+    assert np.linalg.norm(out - ref) / np.linalg.norm(ref) < bound
+    # dequantized tokens are within the rotated-domain error bound of the originals
+    for t in range(0, n, 37):
+        kd = pk.dequant(t, tk)
+        assert np.linalg.norm(kd - K[t]) < 0.1 * np.linalg.norm(K[t]) * (16 / (1 << bits))
+
+
+def test_attention_turbo_close_to_exact():
+    rng = np.random.default_rng(140)
+    tb, mu, theta = _turbo_tables(141)
+    _, muv, thv, _ = oracle.lloyd_max()
+    tv = oracle.TableSet(signs=_signs(142), mu=muv, theta=thv)
+    n = 400
+    K = rng.standard_normal((n, 128)).astype(np.float32)
+    V = rng.standard_normal((n, 128)).astype(np.float32)
+    q = rng.standard_normal((3, 128)).astype(np.float32)
+    pk = oracle.Plane(oracle.TURBO_QJL, 3, True, False, 0, oracle.TENSOR_K, n)
+    pv = oracle.Plane(oracle.TURBO_MSE, 3, True, False, 0, oracle.TENSOR_V, n)
+    pk.append(K, tb)
+    pv.append(V, tv)
+    out = oracle.attention(pk, pv, tb, tv, q)
+    ref = _textbook(q, K, V)
+    assert np.linalg.norm(out - ref) / np.linalg.norm(ref) < 0.35
+    # the turbo-MSE dequantization is R^-1(n mu[code]) with relative error ~ sqrt(0.0345)
+    errs = [np.linalg.norm(pv.dequant(t, tv) - V[t]) / np.linalg.norm(V[t]) for t in range(n)]
+    assert 0.15 < np.mean(errs) < 0.22
