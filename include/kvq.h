@@ -1,0 +1,185 @@
+/*
+ * kvq.h -- C ABI of the MI355X (gfx950) compressed KV cache and decode-attention library.
+ *
+ * The library keeps, per (layer, sequence, kv head), a K plane and a V plane of quantized tokens
+ * inside ONE device buffer that the caller allocates and owns.  It never allocates device memory.
+ * All device pointers are caller-owned and stream-ordered: they must stay valid until the given
+ * stream has passed the call.  Streams are hipStream_t handles passed as void* (NULL = the
+ * default stream).  Every argument check runs on the host before anything is enqueued; on any
+ * error nothing is enqueued and no length changes.  A handle is not thread-safe, and calls on one
+ * handle must be issued on one stream (they share one workspace inside the buffer).
+ *
+ * What each call computes follows these pages (cited by title and section):
+ *  [P1] quantcpp article "Beyond RAG: load whole documents on your laptop": progressive table
+ *       and "how it works" paragraph (4-bit KV, 128 most recent tokens in FP32, 6.4x
+ *       compression = 4-bit codes + fp16 scale + fp16 zero per group of 32), the Python API line
+ *       with progressive=True and context_length=131072.
+ *  [P2] KVarN-on-Bonsai post, TL;DR and caveats: Walsh-Hadamard transform plus Sinkhorn variance
+ *       balancing before 4-bit quantization; cache types chosen separately for K and V
+ *       (--cache-type-k / --cache-type-v).
+ *  [P3] "LLM memory saving: weights vs KV-cache quantization 2026", method table (TurboQuant
+ *       row: random rotation, per-coordinate optimal scalar quantizer, 1-bit QJL on the residual
+ *       for an unbiased inner product; online and training-free) and the application rules
+ *       (asymmetric K = 8-bit, V = 3/4-bit).
+ *
+ * Data conventions: head_dim = 128; groups of 32 consecutive channels; GQA maps query head h to
+ * kv head h / (n_q_heads / n_kv_heads); fp32 outputs; inputs fp32 or bf16; all input/output
+ * pointers 16-byte aligned and contiguous in the shapes stated.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_ERR_INVALID_ARG = 1,      /* null pointer, index out of range, bad count            */
+    KVQ_ERR_UNSUPPORTED = 2,      /* configuration outside what the kernels implement       */
+    KVQ_ERR_CAPACITY = 3,         /* append would exceed max_context; nothing is written    */
+    KVQ_ERR_NOT_READY = 4,        /* rotation/QJL tables not set, or layer not calibrated   */
+    KVQ_ERR_BUFFER_TOO_SMALL = 5, /* dev_buf smaller than kvq_cache_required_bytes()        */
+    KVQ_ERR_MISALIGNED = 6,       /* a pointer is not 16-byte (dev_buf: 256-byte) aligned   */
+    KVQ_ERR_HOST_ALLOC = 7,       /* host memory for the handle could not be allocated      */
+    KVQ_ERR_DEVICE = 8            /* a HIP call failed; kvq_last_hip_error() has its code   */
+} kvq_status;
+
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
+
+typedef enum {
+    KVQ_UNIFORM = 0,   /* b-bit asymmetric groups of 32, fp16 scale + fp16 zero [P1], b = 4|8 */
+    KVQ_TURBO_QJL = 1, /* K only: rotation + 3-bit Lloyd-Max code + 1-bit QJL residual [P3]  */
+    KVQ_TURBO_MSE = 2  /* rotation + 3-bit Lloyd-Max code, no residual sketch [P3]            */
+} kvq_scheme;
+
+typedef struct {
+    int n_layers, n_q_heads, n_kv_heads; /* n_q_heads % n_kv_heads == 0, group <= 8          */
+    int head_dim;                        /* must be 128                                      */
+    int max_batch, max_context;          /* sequences per call (<= 64); tokens per sequence
+                                            ("context_length" of [P1])                       */
+    int k_scheme, v_scheme;              /* kvq_scheme, chosen separately for K and V [P2]   */
+    int k_bits, v_bits;                  /* UNIFORM: 4 or 8; TURBO_*: 3                      */
+    int group_size;                      /* must be 32                                       */
+    int fp32_window;                     /* 0 = flat, 128 = progressive [P1]                 */
+    int rotate_k, rotate_v;              /* random-sign Walsh-Hadamard before coding [P2];
+                                            implied by the TURBO schemes                      */
+    int sinkhorn_iters, calib_tokens;    /* Sinkhorn balancing of UNIFORM planes [P2]; 0 = off;
+                                            calib_tokens bounds kvq_calibrate's n_tokens     */
+} kvq_config;
+
+typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
+
+/* Device view of one (layer, sequence, kv head, tensor) plane, for inspection and tests.
+ * Byte layouts:
+ *  UNIFORM K (token-major rows, blocks of 64 tokens): token t at row
+ *      64*(t/64) + 16*((t%64)%4) + (t%64)/4 of the code and meta planes.  4-bit row = 16 u32
+ *      words, word 4*kb+g holds channels 32g+8kb+i (i=0..7) with channel i at bit
+ *      16*(i%2) + 4*(i/2); 8-bit row = 16 units of 8 B, unit 4*kb+g, channel i at byte i.
+ *  UNIFORM V (blocks of 32 tokens): token t -> block t/32, kb = (t%32)/8, i = t%8; channel d
+ *      -> word (4-bit) or 8-byte unit (8-bit) index 8*(16*kb + d%16) + d/16; token i at bit
+ *      16*(i%2) + 4*(i/2) (4-bit) or byte i (8-bit).
+ *  UNIFORM meta: 16 B per token: u16 fp16 scale[4], then u16 fp16 zero[4] (K: row order,
+ *      V: token order).
+ *  TURBO codes: 48 B per token; group g at byte 12g: u64 of 2-bit low fields then u32 of high
+ *      bits.  TURBO_QJL meta: u16 fp16 norm, u16 fp16 residual norm; QJL plane: 16 B per token,
+ *      bit i at byte i/8 bit i%8.  TURBO_MSE meta: u16 fp16 norm.
+ *  Window ring: [fp32_window][128] fp32, token t at slot t % fp32_window.               */
+typedef struct {
+    void *codes, *meta, *qjl, *window;
+    size_t codes_bytes, meta_bytes, qjl_bytes, window_bytes;
+    int length;
+} kvq_layout;
+
+/* Device pointers of the cache's tables (see kvq_set_random_tables / kvq_calibrate). */
+typedef struct {
+    const float* signs;  /* [n_layers][n_kv_heads][2][128] rotation signs (+-1)          */
+    const float* c;      /* [n_layers][n_kv_heads][2][128] Sinkhorn channel scales       */
+    const float* inv_c;  /* [n_layers][n_kv_heads][2][128] fp32(1/c)                     */
+    const float* qjl_S;  /* [128][128] QJL projection, row-major                         */
+    const float* mu;     /* [8] Lloyd-Max centroids for N(0, 1/128)                      */
+    const float* theta;  /* [7] Lloyd-Max decision thresholds                            */
+} kvq_tables;
+
+enum {
+    KVQ_OPT_SPLIT_TOKENS = 1, /* tokens per decode split (multiple of 64); 0 = automatic     */
+    KVQ_OPT_DECODE_PATH = 2   /* 0 = automatic, 1 = vector-ALU kernel, 2 = matrix-core kernel */
+};
+
+/* Bytes of device memory a cache with this configuration needs (planes for every layer,
+ * sequence and kv head at max_context, tables and workspace).  Pure host computation. */
+kvq_status kvq_cache_required_bytes(const kvq_config* cfg, size_t* bytes);
+
+/* Bind a cache to the caller's device buffer (256-byte aligned, >= required bytes) on the
+ * current HIP device.  Zero-fills the buffer on `stream` and, when a TURBO scheme is used,
+ * computes the Lloyd-Max codebook on the device ([P3], TurboQuant row).  The handle is
+ * host memory owned by the library until kvq_cache_destroy. */
+kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, void* stream,
+                            kvq_cache** out);
+
+/* Free the host handle.  The device buffer stays the caller's. */
+kvq_status kvq_cache_destroy(kvq_cache* cache);
+
+/* Install the random tables the method draws ([P2] random-sign rotation, [P3] random rotation
+ * and QJL projection): signs [n_layers][n_kv_heads][2][128] of +-1.0f and S [128][128] of
+ * N(0,1) fp32, both device pointers, copied on `stream`.  Either may be NULL when no plane
+ * uses it.  Required before appending to a rotated or TURBO plane (else KVQ_ERR_NOT_READY).
+ * Entries are not checked on the device. */
+kvq_status kvq_set_random_tables(kvq_cache* cache, const float* signs, const float* qjl_S,
+                                 void* stream);
+
+/* Sinkhorn variance balancing of one layer ([P2] TL;DR): for every kv head and every UNIFORM
+ * tensor with sinkhorn_iters > 0, rotate the calibration tokens (device, [n_tokens][n_kv_heads]
+ * [128] of dtype for K and V; a tensor's pointer may be NULL when it is not balanced), then
+ * alternately divide rows and columns by their population standard deviation sinkhorn_iters
+ * times in fp64 on the device, and store c = product of the column divisors and fp32(1/c).
+ * 2 <= n_tokens <= calib_tokens.  Required once per layer before appending to it. */
+kvq_status kvq_calibrate(kvq_cache* cache, int layer, const void* Kc, const void* Vc, int dtype,
+                         int n_tokens, void* stream);
+
+/* Quantize and append n_tokens new tokens of every sequence b < batch of `layer` ([P1]
+ * progressive window, [P2] rotation + balancing, [P3] online TurboQuant code).
+ * K, V: device [batch][n_tokens][n_kv_heads][128] of dtype.  Token k of sequence b becomes
+ * token len[b] + k.  Bit-identical to n_tokens calls of kvq_append.  KVQ_ERR_CAPACITY if
+ * len[b] + n_tokens > max_context for any b. */
+kvq_status kvq_prefill_quantize(kvq_cache* cache, int layer, const void* K, const void* V,
+                                int dtype, int n_tokens, int batch, void* stream);
+
+/* kvq_prefill_quantize with n_tokens = 1; k, v: device [batch][n_kv_heads][128]. */
+kvq_status kvq_append(kvq_cache* cache, int layer, const void* k, const void* v, int dtype,
+                      int batch, void* stream);
+
+/* Decode attention of one new query token per sequence over everything cached for `layer`
+ * ([P1], [P3] method row): out[b][h] = sum_t softmax_t(scale <q[b][h], k_t>) v_t, where k_t, v_t
+ * are the FP32 originals for the last fp32_window tokens and the dequantized codes (or the
+ * TurboQuant estimate for K) before that.  q: device [batch][n_q_heads][128] of dtype;
+ * out: device [batch][n_q_heads][128] fp32.  softmax_scale <= 0 means 1/sqrt(128).  A sequence
+ * with no tokens gets zeros. */
+kvq_status kvq_attn_decode(kvq_cache* cache, int layer, const void* q, int dtype, float* out,
+                           int batch, float softmax_scale, void* stream);
+
+/* Plane pointers and sizes of (layer, seq, kv_head, tensor 0 = K / 1 = V). */
+kvq_status kvq_get_layout(const kvq_cache* cache, int layer, int seq, int kv_head, int tensor,
+                          kvq_layout* out);
+
+/* Device pointers of the tables. */
+kvq_status kvq_get_tables(const kvq_cache* cache, kvq_tables* out);
+
+/* Set a tuning option (KVQ_OPT_*). Results do not depend on it beyond float rounding order. */
+kvq_status kvq_set_option(kvq_cache* cache, int option, int value);
+
+/* Tokens cached for (layer, seq); -1 on a bad argument. */
+int kvq_get_length(const kvq_cache* cache, int layer, int seq);
+
+/* Static description of a status code. */
+const char* kvq_status_str(kvq_status status);
+
+/* hipError_t of the last failed HIP call on this handle (0 if none). */
+int kvq_last_hip_error(const kvq_cache* cache);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

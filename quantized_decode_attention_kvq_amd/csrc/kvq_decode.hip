@@ -1,0 +1,422 @@
+// Decode attention over the compressed cache: split-K partials (vector-ALU kernel for every
+// scheme) and the fixed-order log-sum-exp merge with the inverse rotation of V.
+//
+// Method sources (pages by title and section):
+//  - quantcpp article "Beyond RAG...", "how it works": the newest 128 tokens are read in FP32,
+//    everything older from the 4-bit codes.
+//  - KVarN-on-Bonsai post, TL;DR: keys and values were rotated (Walsh-Hadamard) and balanced
+//    (Sinkhorn) before coding, so scores use R(q) .* c and the output is R^-1(c .* acc).
+//  - "LLM memory saving ... 2026", TurboQuant row: the score of a TurboQuant key is
+//    n <R q, mu[code]> plus the 1-bit QJL estimate of the residual's inner product.
+//
+// Scores are kept in the log2 domain: q' = q * softmax_scale * log2(e), p = exp2(s - m).
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ float c0f() { return __uint_as_float(0x3DB504F3u); }
+__device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+__device__ __forceinline__ void hadamard_wave(float& a, float& b) {
+    const int l = lane_id();
+    const float s = a + b, d = a - b;
+    a = s;
+    b = d;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float pa = __shfl_xor(a, m), pb = __shfl_xor(b, m);
+        const bool lower = (l & m) == 0;
+        a = lower ? (a + pa) : (pa - a);
+        b = lower ? (b + pb) : (pb - b);
+    }
+}
+
+__device__ __forceinline__ int k_row(int t) { return 64 * (t / 64) + 16 * ((t % 64) % 4) + (t % 64) / 4; }
+
+__device__ __forceinline__ void load_q_pair(const DecodeParams& p, int b, int hq, float& a, float& c) {
+    const int l = lane_id();
+    const size_t off = ((size_t)b * p.Hq + hq) * kDim;
+    if (p.dtype == 0) {
+        const float2 v = reinterpret_cast<const float2*>(static_cast<const float*>(p.q) + off)[l];
+        a = v.x;
+        c = v.y;
+    } else {
+        const uint32_t v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.q) + off)[l];
+        a = bf2f((uint16_t)(v & 0xffff));
+        c = bf2f((uint16_t)(v >> 16));
+    }
+}
+
+// 3-bit TurboQuant code of channel e (0..31) of group g from a 48-byte token row.
+__device__ __forceinline__ uint32_t turbo_code(const uint8_t* row, int j) {
+    const int g = j >> 5, e = j & 31;
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(row + 12 * g);
+    const uint32_t lo = w[e >> 4];
+    const uint32_t hi = w[2];
+    return ((lo >> (2 * (e & 15))) & 3u) | (((hi >> e) & 1u) << 2);
+}
+
+__global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
+    __shared__ float qp[kMaxGroupHeads][kDim];
+    __shared__ float sp[kMaxGroupHeads][kDim];
+    __shared__ float qsum[kMaxGroupHeads][4];
+    __shared__ float spsum[kMaxGroupHeads];
+    __shared__ float pbuf[4][kMaxGroupHeads][64];
+    __shared__ float wm[4][kMaxGroupHeads], wl[4][kMaxGroupHeads];
+    __shared__ float wacc[4][kMaxGroupHeads][kDim];
+
+    const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int wave = threadIdx.x >> 6, l = lane_id();
+    const int G = p.G, W = p.window;
+    const int n = p.len[b];
+    const int nq = (W > 0) ? max(0, n - W) : n;
+    const bool wsplit = (W > 0) && (split == p.n_splits);
+    int t0, t1;
+    if (wsplit) {
+        t0 = nq;
+        t1 = n;
+    } else {
+        t0 = split * p.split_tokens;
+        t1 = min(nq, t0 + p.split_tokens);
+    }
+    const PlaneGeom& KG = p.geom[0];
+    const PlaneGeom& VG = p.geom[1];
+    const char* slot = p.layer_base + (size_t)b * p.seq_stride + (size_t)kvh * p.head_stride;
+    const uint8_t* kcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.codes_off);
+    const uint8_t* kmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.meta_off);
+    const uint8_t* kqjl = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.qjl_off);
+    const float* kring = reinterpret_cast<const float*>(slot + p.plane_off[0] + KG.ring_off);
+    const uint8_t* vcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.codes_off);
+    const uint8_t* vmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.meta_off);
+    const float* vring = reinterpret_cast<const float*>(slot + p.plane_off[1] + VG.ring_off);
+
+    // ---- query preparation: q' = (R_K q .* c_K) * scale * log2(e) (plain q for the window)
+    for (int h = wave; h < G; h += 4) {
+        float a, c;
+        load_q_pair(p, b, kvh * G + h, a, c);
+        if (!wsplit && KG.rotate) {
+            const float* sg = p.signs + (size_t)(kvh * 2 + 0) * kDim;
+            if (sg[2 * l] < 0.0f) a = -a;
+            if (sg[2 * l + 1] < 0.0f) c = -c;
+            hadamard_wave(a, c);
+            a *= c0f();
+            c *= c0f();
+        }
+        if (!wsplit && KG.sinkhorn) {
+            const float* cs = p.cs + (size_t)(kvh * 2 + 0) * kDim;
+            a *= cs[2 * l];
+            c *= cs[2 * l + 1];
+        }
+        qp[h][2 * l] = a * p.qscale;
+        qp[h][2 * l + 1] = c * p.qscale;
+    }
+    __syncthreads();
+    const bool turbo_k = !wsplit && KG.scheme == kTurboQjl;
+    if (turbo_k) {
+        for (int idx = threadIdx.x; idx < G * kDim; idx += 256) {
+            const int h = idx / kDim, i = idx % kDim;
+            float s = 0.0f;
+            for (int j = 0; j < kDim; ++j) s += p.qjl_st[j * kDim + i] * qp[h][j];
+            sp[h][i] = s;
+        }
+    }
+    if (threadIdx.x < G * 4) {
+        const int h = threadIdx.x / 4, g = threadIdx.x % 4;
+        float s = 0.0f;
+        for (int j = 0; j < 32; ++j) s += qp[h][32 * g + j];
+        qsum[h][g] = s;
+    }
+    __syncthreads();
+    if (turbo_k && threadIdx.x < G) {
+        float s = 0.0f;
+        for (int i = 0; i < kDim; ++i) s += sp[threadIdx.x][i];
+        spsum[threadIdx.x] = s;
+    }
+    __syncthreads();
+
+    float m[kMaxGroupHeads], lsum[kMaxGroupHeads], acc0[kMaxGroupHeads], acc1[kMaxGroupHeads];
+#pragma unroll
+    for (int h = 0; h < kMaxGroupHeads; ++h) {
+        m[h] = kNegInf;
+        lsum[h] = 0.0f;
+        acc0[h] = 0.0f;
+        acc1[h] = 0.0f;
+    }
+
+    const float kappa = 0.0097915166977774f; // sqrt(pi/2) / 128
+    for (int cs0 = t0 + 64 * wave; cs0 < t1; cs0 += 256) {
+        const int t = cs0 + l;
+        const bool valid = t < t1;
+        float s[kMaxGroupHeads];
+#pragma unroll
+        for (int h = 0; h < kMaxGroupHeads; ++h) s[h] = 0.0f;
+        if (valid) {
+            if (wsplit) {
+                const float* kr = kring + (size_t)(t % W) * kDim;
+                for (int j = 0; j < kDim; j += 4) {
+                    const float4 kv = *reinterpret_cast<const float4*>(kr + j);
+#pragma unroll
+                    for (int h = 0; h < kMaxGroupHeads; ++h)
+                        if (h < G)
+                            s[h] += kv.x * qp[h][j] + kv.y * qp[h][j + 1] + kv.z * qp[h][j + 2] +
+                                    kv.w * qp[h][j + 3];
+                }
+            } else if (KG.scheme == kUniform) {
+                const int row = k_row(t);
+                const uint16_t* mt = reinterpret_cast<const uint16_t*>(kmeta + (size_t)row * 16);
+                float dot[kMaxGroupHeads][4];
+#pragma unroll
+                for (int h = 0; h < kMaxGroupHeads; ++h)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) dot[h][g] = 0.0f;
+                if (KG.bits == 4) {
+                    const uint32_t* r = reinterpret_cast<const uint32_t*>(kcodes + (size_t)row * 64);
+#pragma unroll
+                    for (int w = 0; w < 16; ++w) {
+                        const uint32_t word = r[w];
+                        const int kb = w >> 2, g = w & 3;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const float cv = (float)((word >> (16 * (i & 1) + 4 * (i >> 1))) & 15u);
+                            const int j = 32 * g + 8 * kb + i;
+#pragma unroll
+                            for (int h = 0; h < kMaxGroupHeads; ++h)
+                                if (h < G) dot[h][g] += cv * qp[h][j];
+                        }
+                    }
+                } else {
+                    const uint8_t* r = kcodes + (size_t)row * 128;
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) {
+                        const int kb = u >> 2, g = u & 3;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const float cv = (float)r[8 * u + i];
+                            const int j = 32 * g + 8 * kb + i;
+#pragma unroll
+                            for (int h = 0; h < kMaxGroupHeads; ++h)
+                                if (h < G) dot[h][g] += cv * qp[h][j];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float sc = h2f(mt[g]), zc = h2f(mt[4 + g]);
+#pragma unroll
+                    for (int h = 0; h < kMaxGroupHeads; ++h)
+                        if (h < G) s[h] += sc * dot[h][g] + zc * qsum[h][g];
+                }
+            } else { // TurboQuant key
+                const uint8_t* row = kcodes + (size_t)t * 48;
+                const uint16_t* mt = reinterpret_cast<const uint16_t*>(kmeta + (size_t)t * 4);
+                const float nrm = h2f(mt[0]), gam = h2f(mt[1]);
+                float a1[kMaxGroupHeads], a2[kMaxGroupHeads];
+#pragma unroll
+                for (int h = 0; h < kMaxGroupHeads; ++h) a1[h] = a2[h] = 0.0f;
+                for (int j = 0; j < kDim; ++j) {
+                    const float mv = p.mu[turbo_code(row, j)];
+#pragma unroll
+                    for (int h = 0; h < kMaxGroupHeads; ++h)
+                        if (h < G) a1[h] += mv * qp[h][j];
+                }
+                const uint32_t* qb = reinterpret_cast<const uint32_t*>(kqjl + (size_t)t * 16);
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t bits = qb[w];
+                    for (int i = 0; i < 32; ++i)
+                        if ((bits >> i) & 1u) {
+#pragma unroll
+                            for (int h = 0; h < kMaxGroupHeads; ++h)
+                                if (h < G) a2[h] += sp[h][32 * w + i];
+                        }
+                }
+#pragma unroll
+                for (int h = 0; h < kMaxGroupHeads; ++h)
+                    if (h < G) s[h] = nrm * a1[h] + gam * kappa * (2.0f * a2[h] - spsum[h]);
+            }
+        }
+        // online softmax over this 64-token chunk
+        float alpha[kMaxGroupHeads];
+#pragma unroll
+        for (int h = 0; h < kMaxGroupHeads; ++h) {
+            if (h < G) {
+                const float cm = wave_max(valid ? s[h] : kNegInf);
+                const float mn = fmaxf(m[h], cm);
+                const float al = (mn == kNegInf) ? 1.0f : exp2f(m[h] - mn);
+                const float pr = valid ? exp2f(s[h] - mn) : 0.0f;
+                lsum[h] = lsum[h] * al + wave_sum(pr);
+                m[h] = mn;
+                alpha[h] = al;
+                pbuf[wave][h][l] = pr;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int h = 0; h < kMaxGroupHeads; ++h)
+            if (h < G) {
+                acc0[h] *= alpha[h];
+                acc1[h] *= alpha[h];
+            }
+        const int nv = min(64, t1 - cs0);
+        const int d0 = 2 * l;
+        for (int tau = 0; tau < nv; ++tau) {
+            const int tok = cs0 + tau;
+            float v0, v1;
+            if (wsplit) {
+                const float2 vv = reinterpret_cast<const float2*>(vring + (size_t)(tok % W) * kDim)[l];
+                v0 = vv.x;
+                v1 = vv.y;
+            } else if (VG.scheme == kUniform) {
+                const int blk = tok >> 5, kb = (tok & 31) >> 3, i = tok & 7;
+                const int w0 = 8 * (16 * kb + (d0 & 15)) + (d0 >> 4);
+                const uint16_t* mt = reinterpret_cast<const uint16_t*>(vmeta + (size_t)tok * 16);
+                const int g = d0 >> 5;
+                const float sc = h2f(mt[g]), zc = h2f(mt[4 + g]);
+                uint32_t q0, q1;
+                if (VG.bits == 4) {
+                    const uint32_t* bp = reinterpret_cast<const uint32_t*>(vcodes + (size_t)blk * 2048);
+                    const int sh = 16 * (i & 1) + 4 * (i >> 1);
+                    q0 = (bp[w0] >> sh) & 15u;
+                    q1 = (bp[w0 + 8] >> sh) & 15u;
+                } else {
+                    const uint8_t* bp = vcodes + (size_t)blk * 4096;
+                    q0 = bp[8 * w0 + i];
+                    q1 = bp[8 * (w0 + 8) + i];
+                }
+                v0 = zc + sc * (float)q0;
+                v1 = zc + sc * (float)q1;
+            } else { // TurboQuant-MSE value (rotated domain)
+                const uint8_t* row = vcodes + (size_t)tok * 48;
+                const float nrm = h2f(reinterpret_cast<const uint16_t*>(vmeta)[tok]);
+                v0 = nrm * p.mu[turbo_code(row, d0)];
+                v1 = nrm * p.mu[turbo_code(row, d0 + 1)];
+            }
+#pragma unroll
+            for (int h = 0; h < kMaxGroupHeads; ++h)
+                if (h < G) {
+                    const float pr = pbuf[wave][h][tau];
+                    acc0[h] += pr * v0;
+                    acc1[h] += pr * v1;
+                }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // ---- combine the four waves, then write this split's partial per query head
+#pragma unroll
+    for (int h = 0; h < kMaxGroupHeads; ++h)
+        if (h < G) {
+            if (l == 0) {
+                wm[wave][h] = m[h];
+                wl[wave][h] = lsum[h];
+            }
+            wacc[wave][h][2 * l] = acc0[h];
+            wacc[wave][h][2 * l + 1] = acc1[h];
+        }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * kDim; idx += 256) {
+        const int h = idx / kDim, d = idx % kDim;
+        float M = kNegInf;
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][h]);
+        float A = 0.0f, L = 0.0f;
+        if (M != kNegInf) {
+            for (int w = 0; w < 4; ++w) {
+                if (wm[w][h] == kNegInf) continue;
+                const float f = exp2f(wm[w][h] - M);
+                A += wacc[w][h][d] * f;
+                L += wl[w][h] * f;
+            }
+        }
+        float* part = p.partials +
+                      (((size_t)b * p.Hq + kvh * G + h) * p.n_splits_total + split) * kPartialFloats;
+        if (d == 0) {
+            part[0] = M;
+            part[1] = L;
+        }
+        part[4 + d] = A;
+    }
+}
+
+// Fixed-order merge of the splits of one (sequence, query head), then
+// out = (R_V^-1(c_V .* acc_codes) + acc_window) / l.
+__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
+    __shared__ float buf[kDim];
+    const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const int kvh = hq / p.G;
+    float* out = p.out + ((size_t)b * p.Hq + hq) * kDim;
+    if (p.len[b] == 0) {
+        out[d] = 0.0f;
+        return;
+    }
+    const float* part = p.partials + ((size_t)b * p.Hq + hq) * p.n_splits_total * kPartialFloats;
+    float M = kNegInf;
+    for (int s = 0; s < p.n_splits_total; ++s) M = fmaxf(M, part[s * kPartialFloats]);
+    float L = 0.0f, aq = 0.0f, aw = 0.0f;
+    for (int s = 0; s < p.n_splits_total; ++s) {
+        const float ms = part[s * kPartialFloats];
+        if (ms == kNegInf) continue;
+        const float f = exp2f(ms - M);
+        L += part[s * kPartialFloats + 1] * f;
+        const float a = part[s * kPartialFloats + 4 + d] * f;
+        if (p.window > 0 && s == p.n_splits)
+            aw += a;
+        else
+            aq += a;
+    }
+    const PlaneGeom& VG = p.geom[1];
+    if (VG.sinkhorn) aq *= p.cs[(size_t)(kvh * 2 + 1) * kDim + d];
+    if (VG.rotate) {
+        buf[d] = aq;
+        __syncthreads();
+        for (int h = 1; h < kDim; h <<= 1) {
+            float x = 0.0f, y = 0.0f;
+            const bool lower = !(d & h);
+            if (lower) {
+                x = buf[d];
+                y = buf[d + h];
+            }
+            __syncthreads();
+            if (lower) {
+                buf[d] = x + y;
+                buf[d + h] = x - y;
+            }
+            __syncthreads();
+        }
+        aq = buf[d] * c0f();
+        if (p.signs[(size_t)(kvh * 2 + 1) * kDim + d] < 0.0f) aq = -aq;
+    }
+    out[d] = (aq + aw) / L;
+}
+
+} // namespace
+
+hipError_t launch_decode_vec(const DecodeParams& p, hipStream_t s) {
+    dim3 grid(p.n_splits_total, p.Hkv, p.batch);
+    hipLaunchKernelGGL(decode_vec_kernel, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(p.Hq, p.batch), dim3(kDim), 0, s, p);
+    return hipGetLastError();
+}
+
+} // namespace kvq

@@ -1,0 +1,475 @@
+// Host side of libkvq: configuration checks, the device-buffer layout planner, table setup and
+// kernel launches behind the C ABI declared in include/kvq.h.  No call allocates device memory;
+// every argument is checked before anything is enqueued.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kLloydIters = 2000;
+
+size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+size_t ceil_to(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+struct Plan {
+    PlaneGeom geom[2];
+    size_t plane_bytes[2];
+    size_t slot_bytes;
+    size_t off_signs, off_c, off_inv_c, off_S, off_ST, off_mu, off_theta;
+    size_t off_work, work_bytes, off_counters;
+    size_t off_planes, total;
+};
+
+kvq_status check_config(const kvq_config* c) {
+    if (!c) return KVQ_ERR_INVALID_ARG;
+    if (c->n_layers < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->max_batch < 1 ||
+        c->max_context < 1 || c->head_dim < 1 || c->group_size < 1 || c->sinkhorn_iters < 0 ||
+        c->calib_tokens < 0 || c->fp32_window < 0)
+        return KVQ_ERR_INVALID_ARG;
+    if (c->n_q_heads % c->n_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
+    if (c->head_dim != kDim || c->group_size != kGroup) return KVQ_ERR_UNSUPPORTED;
+    if (c->n_q_heads / c->n_kv_heads > kMaxGroupHeads) return KVQ_ERR_UNSUPPORTED;
+    if (c->max_batch > kMaxBatch) return KVQ_ERR_UNSUPPORTED;
+    if (c->max_context > (1 << 26)) return KVQ_ERR_UNSUPPORTED;
+    if (c->fp32_window != 0 && c->fp32_window != kWindowMax) return KVQ_ERR_UNSUPPORTED;
+    if (c->k_scheme != KVQ_UNIFORM && c->k_scheme != KVQ_TURBO_QJL) return KVQ_ERR_UNSUPPORTED;
+    if (c->v_scheme != KVQ_UNIFORM && c->v_scheme != KVQ_TURBO_MSE) return KVQ_ERR_UNSUPPORTED;
+    if (c->k_scheme == KVQ_UNIFORM && c->k_bits != 4 && c->k_bits != 8) return KVQ_ERR_UNSUPPORTED;
+    if (c->v_scheme == KVQ_UNIFORM && c->v_bits != 4 && c->v_bits != 8) return KVQ_ERR_UNSUPPORTED;
+    if (c->k_scheme != KVQ_UNIFORM && c->k_bits != 3) return KVQ_ERR_UNSUPPORTED;
+    if (c->v_scheme != KVQ_UNIFORM && c->v_bits != 3) return KVQ_ERR_UNSUPPORTED;
+    if ((c->rotate_k != 0 && c->rotate_k != 1) || (c->rotate_v != 0 && c->rotate_v != 1))
+        return KVQ_ERR_INVALID_ARG;
+    if (c->sinkhorn_iters > 1000) return KVQ_ERR_UNSUPPORTED;
+    if (c->sinkhorn_iters > 0 && (c->calib_tokens < 2 || c->calib_tokens > 65536))
+        return KVQ_ERR_UNSUPPORTED;
+    return KVQ_OK;
+}
+
+PlaneGeom make_geom(const kvq_config* c, int tensor) {
+    PlaneGeom g{};
+    const int scheme = tensor == 0 ? c->k_scheme : c->v_scheme;
+    g.scheme = scheme;
+    g.bits = tensor == 0 ? c->k_bits : c->v_bits;
+    g.rotate = (scheme != KVQ_UNIFORM) ? 1 : (tensor == 0 ? c->rotate_k : c->rotate_v);
+    g.sinkhorn = (scheme == KVQ_UNIFORM && c->sinkhorn_iters > 0) ? 1 : 0;
+    const size_t cap = (size_t)c->max_context;
+    if (scheme == KVQ_UNIFORM) {
+        const size_t rows = tensor == 0 ? ceil_to(cap, 64) : ceil_to(cap, 32);
+        g.codes_bytes = rows * 16 * (size_t)g.bits;
+        g.meta_bytes = rows * 16;
+        g.qjl_bytes = 0;
+    } else {
+        g.codes_bytes = cap * 48;
+        g.meta_bytes = cap * (scheme == KVQ_TURBO_QJL ? 4 : 2);
+        g.qjl_bytes = scheme == KVQ_TURBO_QJL ? cap * 16 : 0;
+    }
+    g.ring_bytes = (size_t)c->fp32_window * kDim * sizeof(float);
+    size_t off = 0;
+    g.codes_off = off;
+    off = align_up(off + g.codes_bytes);
+    g.meta_off = off;
+    off = align_up(off + g.meta_bytes);
+    g.qjl_off = off;
+    off = align_up(off + g.qjl_bytes);
+    g.ring_off = off;
+    return g;
+}
+
+Plan make_plan(const kvq_config* c) {
+    Plan p{};
+    for (int t = 0; t < 2; ++t) {
+        p.geom[t] = make_geom(c, t);
+        p.plane_bytes[t] = align_up(p.geom[t].ring_off + p.geom[t].ring_bytes);
+    }
+    p.slot_bytes = p.plane_bytes[0] + p.plane_bytes[1];
+    const size_t tab = (size_t)c->n_layers * c->n_kv_heads * 2 * kDim * sizeof(float);
+    size_t off = 0;
+    p.off_signs = off;
+    off = align_up(off + tab);
+    p.off_c = off;
+    off = align_up(off + tab);
+    p.off_inv_c = off;
+    off = align_up(off + tab);
+    p.off_S = off;
+    off = align_up(off + kDim * kDim * sizeof(float));
+    p.off_ST = off;
+    off = align_up(off + kDim * kDim * sizeof(float));
+    p.off_mu = off;
+    off = align_up(off + 8 * sizeof(float));
+    p.off_theta = off;
+    off = align_up(off + 8 * sizeof(float));
+    p.off_counters = off;
+    off = align_up(off + (size_t)c->max_batch * c->n_kv_heads * sizeof(uint32_t));
+    const size_t partial = (size_t)c->max_batch * c->n_q_heads * (kMaxSplits + 1) * kPartialFloats *
+                           sizeof(float);
+    const size_t calib = c->sinkhorn_iters > 0
+                             ? (size_t)2 * c->n_kv_heads * c->calib_tokens * kDim * sizeof(double)
+                             : 0;
+    p.work_bytes = align_up(std::max(partial, calib));
+    p.off_work = off;
+    off += p.work_bytes;
+    p.off_planes = off;
+    off += (size_t)c->n_layers * c->max_batch * c->n_kv_heads * p.slot_bytes;
+    p.total = off;
+    return p;
+}
+
+} // namespace
+
+struct kvq_cache {
+    kvq_config cfg;
+    Plan plan;
+    char* base;
+    size_t bytes;
+    std::vector<int> len;              // [n_layers][max_batch]
+    std::vector<unsigned char> calibrated;
+    bool tables_set;
+    int last_hip_error;
+    int split_tokens_opt;
+    int decode_path;
+    int num_cus;
+    int device;
+
+    float* signs() const { return reinterpret_cast<float*>(base + plan.off_signs); }
+    float* cs() const { return reinterpret_cast<float*>(base + plan.off_c); }
+    float* inv_c() const { return reinterpret_cast<float*>(base + plan.off_inv_c); }
+    float* S() const { return reinterpret_cast<float*>(base + plan.off_S); }
+    float* ST() const { return reinterpret_cast<float*>(base + plan.off_ST); }
+    float* mu() const { return reinterpret_cast<float*>(base + plan.off_mu); }
+    float* theta() const { return reinterpret_cast<float*>(base + plan.off_theta); }
+    char* layer_base(int layer) const {
+        return base + plan.off_planes + (size_t)layer * cfg.max_batch * cfg.n_kv_heads * plan.slot_bytes;
+    }
+    size_t table_off(int layer) const { return (size_t)layer * cfg.n_kv_heads * 2 * kDim; }
+    bool needs_signs() const { return plan.geom[0].rotate || plan.geom[1].rotate; }
+    bool needs_S() const { return cfg.k_scheme == KVQ_TURBO_QJL; }
+    bool needs_calib() const { return plan.geom[0].sinkhorn || plan.geom[1].sinkhorn; }
+    bool turbo() const { return cfg.k_scheme != KVQ_UNIFORM || cfg.v_scheme != KVQ_UNIFORM; }
+};
+
+namespace {
+
+kvq_status dev_fail(kvq_cache* c, hipError_t e) {
+    if (c) c->last_hip_error = (int)e;
+    return KVQ_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+void fill_params_common(const kvq_cache* c, int layer, char*& lb, size_t& seq_stride,
+                        size_t& head_stride, size_t plane_off[2], PlaneGeom geom[2]) {
+    lb = c->layer_base(layer);
+    head_stride = c->plan.slot_bytes;
+    seq_stride = (size_t)c->cfg.n_kv_heads * c->plan.slot_bytes;
+    plane_off[0] = 0;
+    plane_off[1] = c->plan.plane_bytes[0];
+    geom[0] = c->plan.geom[0];
+    geom[1] = c->plan.geom[1];
+}
+
+} // namespace
+
+extern "C" {
+
+kvq_status kvq_cache_required_bytes(const kvq_config* cfg, size_t* bytes) {
+    if (!bytes) return KVQ_ERR_INVALID_ARG;
+    const kvq_status st = check_config(cfg);
+    if (st != KVQ_OK) return st;
+    *bytes = make_plan(cfg).total;
+    return KVQ_OK;
+}
+
+kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, void* stream,
+                            kvq_cache** out) {
+    if (!out) return KVQ_ERR_INVALID_ARG;
+    *out = nullptr;
+    const kvq_status st = check_config(cfg);
+    if (st != KVQ_OK) return st;
+    if (!dev_buf) return KVQ_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(dev_buf) & (kAlign - 1)) != 0) return KVQ_ERR_MISALIGNED;
+    const Plan plan = make_plan(cfg);
+    if (bytes < plan.total) return KVQ_ERR_BUFFER_TOO_SMALL;
+    kvq_cache* c = new (std::nothrow) kvq_cache();
+    if (!c) return KVQ_ERR_HOST_ALLOC;
+    try {
+        c->len.assign((size_t)cfg->n_layers * cfg->max_batch, 0);
+        c->calibrated.assign((size_t)cfg->n_layers, 0);
+    } catch (...) {
+        delete c;
+        return KVQ_ERR_HOST_ALLOC;
+    }
+    c->cfg = *cfg;
+    c->plan = plan;
+    c->base = static_cast<char*>(dev_buf);
+    c->bytes = bytes;
+    c->tables_set = false;
+    c->last_hip_error = 0;
+    c->split_tokens_opt = 0;
+    c->decode_path = 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipGetDevice(&c->device);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, c->device);
+    if (e == hipSuccess) e = hipMemsetAsync(dev_buf, 0, plan.total, s);
+    if (e == hipSuccess) {
+        const size_t n = (size_t)cfg->n_layers * cfg->n_kv_heads * 2 * kDim;
+        e = launch_fill(c->cs(), n, 1.0f, s);
+        if (e == hipSuccess) e = launch_fill(c->inv_c(), n, 1.0f, s);
+        if (e == hipSuccess) e = launch_fill(c->signs(), n, 1.0f, s);
+    }
+    if (e == hipSuccess && c->turbo()) e = launch_codebook(c->mu(), c->theta(), kLloydIters, s);
+    if (e != hipSuccess) {
+        delete c;
+        return KVQ_ERR_DEVICE;
+    }
+    *out = c;
+    return KVQ_OK;
+}
+
+kvq_status kvq_cache_destroy(kvq_cache* cache) {
+    if (!cache) return KVQ_ERR_INVALID_ARG;
+    delete cache;
+    return KVQ_OK;
+}
+
+kvq_status kvq_set_random_tables(kvq_cache* c, const float* signs, const float* qjl_S, void* stream) {
+    if (!c) return KVQ_ERR_INVALID_ARG;
+    if (c->needs_signs() && !signs) return KVQ_ERR_INVALID_ARG;
+    if (c->needs_S() && !qjl_S) return KVQ_ERR_INVALID_ARG;
+    if ((signs && !aligned16(signs)) || (qjl_S && !aligned16(qjl_S))) return KVQ_ERR_MISALIGNED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (signs)
+        e = hipMemcpyAsync(c->signs(), signs,
+                           (size_t)c->cfg.n_layers * c->cfg.n_kv_heads * 2 * kDim * sizeof(float),
+                           hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && qjl_S) {
+        e = hipMemcpyAsync(c->S(), qjl_S, kDim * kDim * sizeof(float), hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess) e = launch_transpose128(c->S(), c->ST(), s);
+    }
+    if (e != hipSuccess) return dev_fail(c, e);
+    c->tables_set = true;
+    return KVQ_OK;
+}
+
+kvq_status kvq_calibrate(kvq_cache* c, int layer, const void* Kc, const void* Vc, int dtype,
+                         int n_tokens, void* stream) {
+    if (!c) return KVQ_ERR_INVALID_ARG;
+    if (layer < 0 || layer >= c->cfg.n_layers) return KVQ_ERR_INVALID_ARG;
+    if (dtype != KVQ_F32 && dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
+    if (!c->needs_calib()) return KVQ_ERR_INVALID_ARG;
+    if (n_tokens < 2 || n_tokens > c->cfg.calib_tokens) return KVQ_ERR_INVALID_ARG;
+    CalibParams p{};
+    const void* src[2] = {Kc, Vc};
+    for (int t = 0; t < 2; ++t) {
+        p.do_tensor[t] = c->plan.geom[t].sinkhorn;
+        p.rotate[t] = c->plan.geom[t].rotate;
+        if (p.do_tensor[t] && !src[t]) return KVQ_ERR_INVALID_ARG;
+        if (src[t] && !aligned16(src[t])) return KVQ_ERR_MISALIGNED;
+        p.src[t] = src[t];
+    }
+    if (c->needs_signs() && !c->tables_set) return KVQ_ERR_NOT_READY;
+    p.work = reinterpret_cast<double*>(c->base + c->plan.off_work);
+    p.signs = c->signs() + c->table_off(layer);
+    p.cs = c->cs() + c->table_off(layer);
+    p.inv_c = c->inv_c() + c->table_off(layer);
+    p.dtype = dtype;
+    p.n = n_tokens;
+    p.Hkv = c->cfg.n_kv_heads;
+    p.iters = c->cfg.sinkhorn_iters;
+    const hipError_t e = launch_calibrate(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return dev_fail(c, e);
+    c->calibrated[(size_t)layer] = 1;
+    return KVQ_OK;
+}
+
+kvq_status kvq_prefill_quantize(kvq_cache* c, int layer, const void* K, const void* V, int dtype,
+                                int n_tokens, int batch, void* stream) {
+    if (!c) return KVQ_ERR_INVALID_ARG;
+    if (layer < 0 || layer >= c->cfg.n_layers) return KVQ_ERR_INVALID_ARG;
+    if (batch < 1 || batch > c->cfg.max_batch || n_tokens < 0) return KVQ_ERR_INVALID_ARG;
+    if (dtype != KVQ_F32 && dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
+    if (!K || !V) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(K) || !aligned16(V)) return KVQ_ERR_MISALIGNED;
+    int* len = &c->len[(size_t)layer * c->cfg.max_batch];
+    for (int b = 0; b < batch; ++b)
+        if ((long long)len[b] + n_tokens > c->cfg.max_context) return KVQ_ERR_CAPACITY;
+    if ((c->needs_signs() || c->needs_S()) && !c->tables_set) return KVQ_ERR_NOT_READY;
+    if (c->needs_calib() && !c->calibrated[(size_t)layer]) return KVQ_ERR_NOT_READY;
+    if (n_tokens == 0) return KVQ_OK;
+
+    QuantParams p{};
+    p.src[0] = K;
+    p.src[1] = V;
+    fill_params_common(c, layer, p.layer_base, p.seq_stride, p.head_stride, p.plane_off, p.geom);
+    for (int t = 0; t < 2; ++t) {
+        p.signs[t] = c->signs() + c->table_off(layer);
+        p.inv_c[t] = c->inv_c() + c->table_off(layer);
+    }
+    p.qjl_st = c->ST();
+    p.mu = c->mu();
+    p.theta = c->theta();
+    p.dtype = dtype;
+    p.T = n_tokens;
+    p.batch = batch;
+    p.Hkv = c->cfg.n_kv_heads;
+    p.window = c->cfg.fp32_window;
+    int groups = 0;
+    for (int b = 0; b < batch; ++b) {
+        p.start[b] = len[b];
+        groups = std::max(groups, (len[b] + n_tokens - 1) / 8 - len[b] / 8 + 1);
+    }
+    p.groups8 = groups;
+    const hipError_t e = launch_quantize(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return dev_fail(c, e);
+    for (int b = 0; b < batch; ++b) len[b] += n_tokens;
+    return KVQ_OK;
+}
+
+kvq_status kvq_append(kvq_cache* c, int layer, const void* k, const void* v, int dtype, int batch,
+                      void* stream) {
+    return kvq_prefill_quantize(c, layer, k, v, dtype, 1, batch, stream);
+}
+
+kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, float* out, int batch,
+                           float softmax_scale, void* stream) {
+    if (!c) return KVQ_ERR_INVALID_ARG;
+    if (layer < 0 || layer >= c->cfg.n_layers) return KVQ_ERR_INVALID_ARG;
+    if (batch < 1 || batch > c->cfg.max_batch) return KVQ_ERR_INVALID_ARG;
+    if (dtype != KVQ_F32 && dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
+    if (!q || !out) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_MISALIGNED;
+    if (!std::isfinite(softmax_scale)) return KVQ_ERR_INVALID_ARG;
+    if ((c->needs_signs() || c->needs_S()) && !c->tables_set) return KVQ_ERR_NOT_READY;
+
+    DecodeParams p{};
+    p.q = q;
+    p.out = out;
+    fill_params_common(c, layer, p.layer_base, p.seq_stride, p.head_stride, p.plane_off, p.geom);
+    p.signs = c->signs() + c->table_off(layer);
+    p.cs = c->cs() + c->table_off(layer);
+    p.qjl_st = c->ST();
+    p.mu = c->mu();
+    p.partials = reinterpret_cast<float*>(c->base + c->plan.off_work);
+    p.dtype = dtype;
+    p.batch = batch;
+    p.Hq = c->cfg.n_q_heads;
+    p.Hkv = c->cfg.n_kv_heads;
+    p.G = p.Hq / p.Hkv;
+    p.window = c->cfg.fp32_window;
+    const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(128.0f);
+    p.qscale = scale * 1.4426950408889634f;
+    const int* len = &c->len[(size_t)layer * c->cfg.max_batch];
+    int nq_max = 0;
+    for (int b = 0; b < batch; ++b) {
+        p.len[b] = len[b];
+        const int nq = p.window > 0 ? std::max(0, len[b] - p.window) : len[b];
+        nq_max = std::max(nq_max, nq);
+    }
+    int st;
+    if (c->split_tokens_opt > 0) {
+        st = c->split_tokens_opt;
+    } else {
+        const int target = std::max(1, (2 * c->num_cus + p.Hkv * batch - 1) / (p.Hkv * batch));
+        st = (int)ceil_to((size_t)std::max(1, (nq_max + target - 1) / target), 64);
+        st = std::max(st, 256);
+    }
+    int ns = std::max(1, (nq_max + st - 1) / st);
+    if (ns > kMaxSplits) {
+        st = (int)ceil_to((size_t)((nq_max + kMaxSplits - 1) / kMaxSplits), 64);
+        ns = std::max(1, (nq_max + st - 1) / st);
+    }
+    p.split_tokens = st;
+    p.n_splits = ns;
+    p.n_splits_total = ns + (p.window > 0 ? 1 : 0);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_decode_vec(p, s);
+    if (e == hipSuccess) e = launch_decode_merge(p, s);
+    if (e != hipSuccess) return dev_fail(c, e);
+    return KVQ_OK;
+}
+
+kvq_status kvq_get_layout(const kvq_cache* c, int layer, int seq, int kv_head, int tensor,
+                          kvq_layout* out) {
+    if (!c || !out) return KVQ_ERR_INVALID_ARG;
+    if (layer < 0 || layer >= c->cfg.n_layers || seq < 0 || seq >= c->cfg.max_batch ||
+        kv_head < 0 || kv_head >= c->cfg.n_kv_heads || (tensor != 0 && tensor != 1))
+        return KVQ_ERR_INVALID_ARG;
+    char* slot = c->layer_base(layer) + (size_t)seq * c->cfg.n_kv_heads * c->plan.slot_bytes +
+                 (size_t)kv_head * c->plan.slot_bytes + (tensor ? c->plan.plane_bytes[0] : 0);
+    const PlaneGeom& g = c->plan.geom[tensor];
+    out->codes = slot + g.codes_off;
+    out->meta = slot + g.meta_off;
+    out->qjl = g.qjl_bytes ? slot + g.qjl_off : nullptr;
+    out->window = g.ring_bytes ? slot + g.ring_off : nullptr;
+    out->codes_bytes = g.codes_bytes;
+    out->meta_bytes = g.meta_bytes;
+    out->qjl_bytes = g.qjl_bytes;
+    out->window_bytes = g.ring_bytes;
+    out->length = c->len[(size_t)layer * c->cfg.max_batch + seq];
+    return KVQ_OK;
+}
+
+kvq_status kvq_get_tables(const kvq_cache* c, kvq_tables* out) {
+    if (!c || !out) return KVQ_ERR_INVALID_ARG;
+    out->signs = c->signs();
+    out->c = c->cs();
+    out->inv_c = c->inv_c();
+    out->qjl_S = c->S();
+    out->mu = c->mu();
+    out->theta = c->theta();
+    return KVQ_OK;
+}
+
+kvq_status kvq_set_option(kvq_cache* c, int option, int value) {
+    if (!c) return KVQ_ERR_INVALID_ARG;
+    switch (option) {
+    case KVQ_OPT_SPLIT_TOKENS:
+        if (value < 0 || value % 64 != 0) return KVQ_ERR_INVALID_ARG;
+        c->split_tokens_opt = value;
+        return KVQ_OK;
+    case KVQ_OPT_DECODE_PATH:
+        if (value < 0 || value > 2) return KVQ_ERR_INVALID_ARG;
+        c->decode_path = value;
+        return KVQ_OK;
+    default:
+        return KVQ_ERR_INVALID_ARG;
+    }
+}
+
+int kvq_get_length(const kvq_cache* c, int layer, int seq) {
+    if (!c || layer < 0 || layer >= c->cfg.n_layers || seq < 0 || seq >= c->cfg.max_batch) return -1;
+    return c->len[(size_t)layer * c->cfg.max_batch + seq];
+}
+
+const char* kvq_status_str(kvq_status s) {
+    switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_CAPACITY: return "context capacity exceeded";
+    case KVQ_ERR_NOT_READY: return "tables not set or layer not calibrated";
+    case KVQ_ERR_BUFFER_TOO_SMALL: return "device buffer too small";
+    case KVQ_ERR_MISALIGNED: return "misaligned pointer";
+    case KVQ_ERR_HOST_ALLOC: return "host allocation failed";
+    case KVQ_ERR_DEVICE: return "HIP error";
+    }
+    return "unknown status";
+}
+
+int kvq_last_hip_error(const kvq_cache* c) { return c ? c->last_hip_error : 0; }
+
+} // extern "C"

@@ -1,0 +1,84 @@
+// Internal declarations shared by the host code and the HIP kernels of libkvq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace kvq {
+
+constexpr int kDim = 128;
+constexpr int kGroup = 32;
+constexpr int kMaxBatch = 64;
+constexpr int kMaxGroupHeads = 8;   // query heads per kv head
+constexpr int kMaxSplits = 256;     // quantized-token splits per (sequence, kv head)
+constexpr int kPartialFloats = 132; // m, l, pad, pad, acc[128] per (sequence, q head, split)
+constexpr int kWindowMax = 128;
+
+enum Scheme { kUniform = 0, kTurboQjl = 1, kTurboMse = 2 };
+
+// Geometry of one tensor's plane inside a (layer, seq, head) slot.
+struct PlaneGeom {
+    int scheme, bits, rotate, sinkhorn;
+    size_t codes_off, meta_off, qjl_off, ring_off; // byte offsets from the slot base
+    size_t codes_bytes, meta_bytes, qjl_bytes, ring_bytes;
+};
+
+// Parameters of the quantize-on-append kernel (K and V in one launch).
+struct QuantParams {
+    const void* src[2];       // [batch][T][Hkv][128] of dtype
+    char* layer_base;         // slot of (layer, seq 0, head 0)
+    size_t seq_stride;        // bytes between sequences
+    size_t head_stride;       // bytes between kv heads (= slot bytes)
+    size_t plane_off[2];      // offset of the K / V plane inside a slot
+    PlaneGeom geom[2];
+    const float* signs[2];    // layer base of [Hkv][2][128]; index (head*2 + tensor)*128
+    const float* inv_c[2];    // same indexing
+    const float* qjl_st;      // [128 j][128 i] = S[i][j]
+    const float* mu;          // [8]
+    const float* theta;       // [8], 7 used
+    int dtype, T, batch, Hkv, window;
+    int groups8;              // 8-token groups per (sequence) unit range (max over sequences)
+    int start[kMaxBatch];     // length before this append, per sequence
+};
+
+// Parameters of the decode kernels.
+struct DecodeParams {
+    const void* q;            // [batch][Hq][128] of dtype
+    float* out;               // [batch][Hq][128]
+    char* layer_base;
+    size_t seq_stride, head_stride;
+    size_t plane_off[2];
+    PlaneGeom geom[2];
+    const float* signs;       // layer base [Hkv][2][128]
+    const float* cs;          // layer base [Hkv][2][128] Sinkhorn c
+    const float* qjl_st;      // [128 j][128 i]
+    const float* mu;
+    float* partials;          // [batch][Hq][n_splits_total][kPartialFloats]
+    int dtype, batch, Hq, Hkv, G, window;
+    float qscale;             // softmax scale * log2(e)
+    int split_tokens, n_splits, n_splits_total;
+    int len[kMaxBatch];
+};
+
+struct CalibParams {
+    const void* src[2];       // [n][Hkv][128] of dtype
+    double* work;             // [2][Hkv][n][128]
+    const float* signs;       // layer base [Hkv][2][128]
+    float* cs;                // layer base
+    float* inv_c;             // layer base
+    int do_tensor[2], rotate[2];
+    int dtype, n, Hkv, iters;
+};
+
+// Launchers (defined in the .hip files); return the launch's hipError_t.
+hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+hipError_t launch_calibrate(const CalibParams& p, hipStream_t s);
+hipError_t launch_codebook(float* mu, float* theta, int iters, hipStream_t s);
+hipError_t launch_transpose128(const float* in, float* out, hipStream_t s);
+hipError_t launch_fill(float* p, size_t n, float v, hipStream_t s);
+hipError_t launch_decode_vec(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t s);
+
+} // namespace kvq

@@ -1,0 +1,94 @@
+"""Host-only checks of libkvq: it loads, exports every symbol include/kvq.h declares, plans the
+buffer layout with the byte counts the format implies, and rejects bad arguments before touching
+the device.  No compute call is made (no GPU here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+K = pytest.importorskip("quantized_decode_attention_kvq_amd._kvq")
+
+
+def _header_symbols():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = K.load()
+    syms = _header_symbols()
+    assert len(syms) >= 14
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert sorted(K.EXPORTS) == syms
+
+
+def _cfg(wl, **over):
+    d = wl.kvq_config()
+    d.update(over)
+    return K.make_config(**d)
+
+
+def test_required_bytes_match_format():
+    # 4-bit K and V: 64 B codes + 16 B meta per token-head (the "6.4x" of the quantcpp article);
+    # the 32K KVarN workload is 28 layers x 8 heads x 32768 tokens x 160 B plus small tables.
+    wl = W.LLAMA3B_32K_KVARN
+    n = K.kvq_cache_required_bytes(_cfg(wl))
+    planes = 28 * 8 * 32768 * 160
+    assert planes <= n <= planes + 16 * 2 ** 20
+    # 8-bit: 128 + 16 B per token-head
+    wl8 = W.DENSE27B_120K_U8
+    n8 = K.kvq_cache_required_bytes(_cfg(wl8))
+    p8 = 64 * 4 * 8 * 122880 * 144 * 2
+    assert p8 <= n8 <= p8 + 64 * 2 ** 20
+    # TurboQuant K: 48 B codes + 4 B norms + 16 B QJL bits = 68 B; uniform 4-bit V: 80 B
+    wlt = W.LLAMA3B_32K_TURBO
+    nt = K.kvq_cache_required_bytes(_cfg(wlt))
+    pt = 28 * 8 * 32768 * (68 + 80)
+    assert pt <= nt <= pt + 16 * 2 ** 20
+    # progressive window: 128 x 128 fp32 per (layer, seq, head, tensor) on top of the codes
+    wlp = W.LLAMA3B_128K_PROGRESSIVE
+    npg = K.kvq_cache_required_bytes(_cfg(wlp))
+    pp = 28 * 8 * (131072 * 160 + 2 * 128 * 512)
+    assert pp <= npg <= pp + 16 * 2 ** 20
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=64), 2), (dict(group_size=64), 2), (dict(k_bits=3), 2), (dict(v_bits=2), 2),
+    (dict(fp32_window=64), 2), (dict(n_q_heads=25), 1), (dict(n_q_heads=8 * 9), 2),
+    (dict(max_batch=65), 2), (dict(max_batch=0), 1), (dict(k_scheme=2), 2), (dict(v_scheme=1), 2),
+    (dict(rotate_k=2), 1), (dict(n_layers=0), 1), (dict(sinkhorn_iters=5, calib_tokens=1), 2),
+])
+def test_invalid_configs_rejected(over, status):
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_cache_required_bytes(_cfg(W.LLAMA3B_3970_PROGRESSIVE, **over))
+    assert e.value.status == status
+
+
+def test_create_argument_checks_before_device():
+    lib = K.load()
+    cfg = _cfg(W.LLAMA3B_3970_PROGRESSIVE)
+    need = K.kvq_cache_required_bytes(cfg)
+    h = ctypes.c_void_p()
+    assert lib.kvq_cache_create(ctypes.byref(cfg), None, need, None, ctypes.byref(h)) == 1
+    assert lib.kvq_cache_create(ctypes.byref(cfg), ctypes.c_void_p(0x10010), need, None,
+                                ctypes.byref(h)) == 6
+    assert lib.kvq_cache_create(ctypes.byref(cfg), ctypes.c_void_p(0x10000), need - 1, None,
+                                ctypes.byref(h)) == 5
+    assert lib.kvq_cache_create(ctypes.byref(cfg), ctypes.c_void_p(0x10000), need, None, None) == 1
+    assert not h.value
+
+
+def test_null_handle_calls_rejected():
+    lib = K.load()
+    assert lib.kvq_append(None, 0, None, None, 0, 1, None) == 1
+    assert lib.kvq_attn_decode(None, 0, None, 0, None, 1, 0.0, None) == 1
+    assert lib.kvq_calibrate(None, 0, None, None, 0, 512, None) == 1
+    assert lib.kvq_get_length(None, 0, 0) == -1
+    assert lib.kvq_cache_destroy(None) == 1
+    assert K.kvq_status_str(0) == "ok" and K.kvq_status_str(3) == "context capacity exceeded"

@@ -1,0 +1,210 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: packed codes, fp16 scales/zeros, norms, QJL bits, window bytes and tables are bit-exact;
+attention outputs are within 2e-3 relative L2 and 1e-2 max-abs of the oracle's fp64 attention on
+the same dequantized cache.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from kvq_testlib import (MAX_ABS_TOL, REL_L2_TOL, Case, compare_plane, max_abs,
+                         oracle_attention_case, rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _check_all_planes(case, li, heads=None, seqs=None):
+    _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS)
+    planes = {}
+    for b in (seqs if seqs is not None else range(case.batch)):
+        for h in (heads if heads is not None else range(case.wl.n_kv_heads)):
+            row = []
+            for tensor in (0, 1):
+                tb = case.oracle_tables(li, h, tensor, mu, theta)
+                p, _ = case.oracle_plane(li, b, h, tensor, tb)
+                compare_plane(case.device_plane(li, b, h, tensor), p, f"layer {li} seq {b} head {h} tensor {tensor}")
+                row += [p, tb]
+            planes[(b, h)] = row
+    return planes
+
+
+def _decode_and_compare(case, li, planes=None, step=0, seqs=None):
+    wl = case.wl
+    q = W.gen_q(wl, case.layers[li], step, batch=case.batch).to(case.device)
+    out = torch.empty((case.batch, wl.n_q_heads, 128), dtype=torch.float32, device=case.device)
+    case.cache.attn_decode(li, q, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    qn = q.float().cpu().numpy()
+    worst = (0.0, 0.0)
+    for b in (seqs if seqs is not None else range(case.batch)):
+        pl = None
+        if planes is not None:
+            pl = {h: planes[(b, h)] for h in range(wl.n_kv_heads)}
+        ref = oracle_attention_case(case, li, b, qn[b], planes=pl)
+        r, m = rel_l2(got[b], ref), max_abs(got[b], ref)
+        worst = (max(worst[0], r), max(worst[1], m))
+        assert r <= REL_L2_TOL and m <= MAX_ABS_TOL, (b, r, m)
+    _say(f"  attention rel_l2={worst[0]:.2e} max_abs={worst[1]:.2e}")
+    return got
+
+
+def test_progressive_3970_full():
+    wl = W.LLAMA3B_3970_PROGRESSIVE
+    _say("case:", wl.name)
+    case = Case(wl, wl.context)
+    case.prefill(0)
+    torch.cuda.synchronize()
+    planes = _check_all_planes(case, 0)
+    _decode_and_compare(case, 0, planes)
+
+
+def test_prefill_equals_appends_bytewise():
+    wl = W.LLAMA3B_3970_PROGRESSIVE
+    _say("case: prefill == appends,", wl.name, "n=300")
+    a = Case(wl, 300)
+    b = Case(wl, 300)
+    a.prefill(0, chunks=[1, 63, 100, 7, 129])
+    b.append_all(0)
+    torch.cuda.synchronize()
+    for h in range(wl.n_kv_heads):
+        for t in (0, 1):
+            da, db = a.device_plane(0, 0, h, t), b.device_plane(0, 0, h, t)
+            for x, y in zip(da, db):
+                if x is not None:
+                    assert np.array_equal(x, y), (h, t)
+    _check_all_planes(a, 0, heads=[0, 5])
+
+
+def test_kvarn_rotation_sinkhorn_small():
+    wl = W.LLAMA3B_32K_KVARN
+    _say("case:", wl.name, "2 layers, 1000 tokens")
+    case = Case(wl, 1000, layers=[0, 13])
+    for li in range(2):
+        case.prefill(li)
+    torch.cuda.synchronize()
+    # Sinkhorn tables bit-exact
+    for li, layer in enumerate(case.layers):
+        c_dev = case.cache.table("c", 2 * 8 * 2 * 128).cpu().numpy().reshape(2, 8, 2, 128)
+        ic_dev = case.cache.table("inv_c", 2 * 8 * 2 * 128).cpu().numpy().reshape(2, 8, 2, 128)
+        for h in range(8):
+            for t in (0, 1):
+                tb = case.oracle_tables(li, h, t)
+                assert np.array_equal(c_dev[li, h, t].view(np.uint32), tb.arrays["c"].view(np.uint32)), (li, h, t)
+                assert np.array_equal(ic_dev[li, h, t].view(np.uint32), tb.arrays["inv_c"].view(np.uint32))
+    for li in range(2):
+        planes = _check_all_planes(case, li)
+        _decode_and_compare(case, li, planes)
+
+
+def test_turbo_qjl_small():
+    wl = W.LLAMA3B_32K_TURBO
+    _say("case:", wl.name, "1 layer, 700 tokens")
+    case = Case(wl, 700, layers=[3])
+    case.prefill(0)
+    torch.cuda.synchronize()
+    _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS)
+    mu_dev = case.cache.table("mu", 8).cpu().numpy()
+    th_dev = case.cache.table("theta", 7).cpu().numpy()
+    assert np.array_equal(mu_dev.view(np.uint32), mu.view(np.uint32))
+    assert np.array_equal(th_dev.view(np.uint32), theta.view(np.uint32))
+    planes = _check_all_planes(case, 0)
+    _decode_and_compare(case, 0, planes)
+
+
+def test_turbo_asym_u8k_msev_small():
+    wl = W.LLAMA3B_32K_TURBO_ASYM
+    _say("case:", wl.name, "1 layer, 777 tokens")
+    case = Case(wl, 777, layers=[5])
+    case.prefill(0)
+    torch.cuda.synchronize()
+    planes = _check_all_planes(case, 0)
+    _decode_and_compare(case, 0, planes)
+
+
+@pytest.mark.parametrize("wl", [W.DENSE27B_120K_U8, W.DENSE27B_120K_KVARN], ids=lambda w: w.name)
+def test_dense27b_bf16_gqa5_small(wl):
+    _say("case:", wl.name, "1 layer, 2 seqs, 650 tokens")
+    case = Case(wl, 650, layers=[63], batch=2)
+    case.prefill(0)
+    torch.cuda.synchronize()
+    planes = _check_all_planes(case, 0, heads=[0, 3, 7])
+    _decode_and_compare(case, 0, None)
+
+
+def test_progressive_batch_ragged_lengths():
+    # two sequences of different lengths: append to seq 0 only (batch=1 calls) after a shared prefill
+    wl = W.LLAMA3B_128K_PROGRESSIVE
+    _say("case:", wl.name, "batch 2, ragged")
+    case = Case(wl, 500, layers=[0], batch=2, extra_tokens=64)
+    case.prefill(0)
+    k, v = W.gen_step_kv(wl, 0, 0, batch=1)
+    case.cache.append(0, k.to("cuda"), v.to("cuda"))
+    torch.cuda.synchronize()
+    assert case.cache.length(0, 0) == 501 and case.cache.length(0, 1) == 500
+    q = W.gen_q(wl, 0, 0, batch=2).to("cuda")
+    out = torch.empty((2, 24, 128), device="cuda")
+    case.cache.attn_decode(0, q, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    qn = q.float().cpu().numpy()
+    _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS)
+    for b in (0, 1):
+        ref = np.zeros((24, 128))
+        for h in range(8):
+            pk, tk = case.oracle_plane(0, b, h, 0, case.oracle_tables(0, h, 0))
+            pv, tv = case.oracle_plane(0, b, h, 1, case.oracle_tables(0, h, 1))
+            if b == 0:
+                pk.append(k[0, h].float().numpy(), tk)
+                pv.append(v[0, h].float().numpy(), tv)
+                compare_plane(case.device_plane(0, 0, h, 0), pk, f"seq0 head {h} K")
+                compare_plane(case.device_plane(0, 0, h, 1), pv, f"seq0 head {h} V")
+            ref[h * 3:h * 3 + 3] = oracle.attention(pk, pv, tk, tv, qn[b, h * 3:h * 3 + 3])
+        assert rel_l2(got[b], ref) <= REL_L2_TOL and max_abs(got[b], ref) <= MAX_ABS_TOL
+
+
+def test_split_count_invariance_and_determinism():
+    wl = W.LLAMA3B_3970_PROGRESSIVE
+    _say("case: split invariance", wl.name)
+    case = Case(wl, 3970)
+    case.prefill(0)
+    q = W.gen_q(wl, 0, 0).to("cuda")
+    outs = {}
+    for st in (0, 64, 256, 1024, 4096):
+        case.cache.set_option(1, st)
+        o1 = torch.empty((1, 24, 128), device="cuda")
+        o2 = torch.empty((1, 24, 128), device="cuda")
+        case.cache.attn_decode(0, q, o1)
+        case.cache.attn_decode(0, q, o2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), st  # run-to-run bit identity at a fixed split count
+        outs[st] = o1.cpu().numpy()
+    for st, o in outs.items():
+        assert rel_l2(o, outs[0]) < 1e-5, st
+
+
+def test_empty_and_single_token():
+    wl = W.LLAMA3B_32K_KVARN
+    _say("case: empty / single token")
+    case = Case(wl, 1, layers=[0], extra_tokens=10)
+    q = W.gen_q(wl, 0, 0).to("cuda")
+    out = torch.full((1, 24, 128), 7.0, device="cuda")
+    case.cache.attn_decode(0, q, out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+    case.prefill(0)
+    case.cache.attn_decode(0, q, out)
+    torch.cuda.synchronize()
+    _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS)
+    for h in range(8):
+        pv, tv = case.oracle_plane(0, 0, h, 1, case.oracle_tables(0, h, 1))
+        ref = pv.dequant(0, tv)
+        for g in range(3):
+            assert rel_l2(out[0, 3 * h + g].cpu().numpy(), ref) < 1e-5
