@@ -78,6 +78,7 @@ typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
  *      64*(t/64) + 16*((t%64)%4) + (t%64)/4 of the code and meta planes.  4-bit row = 16 u32
  *      words, word 4*kb+g holds channels 32g+8kb+i (i=0..7) with channel i at bit
  *      16*(i%2) + 4*(i/2); 8-bit row = 16 units of 8 B, unit 4*kb+g, channel i at byte i.
+ *  UNIFORM planes of both tensors hold whole 64-token blocks.
  *  UNIFORM V (blocks of 32 tokens): token t -> block t/32, kb = (t%32)/8, i = t%8; channel d
  *      -> word (4-bit) or 8-byte unit (8-bit) index 8*(16*kb + d%16) + d/16; token i at bit
  *      16*(i%2) + 4*(i/2) (4-bit) or byte i (8-bit).

@@ -362,6 +362,8 @@ void orc_turbo_encode(const float* x, const orc_tables* tb, int with_qjl, float*
  * 16*(i%2) + 4*(i/2).  8-bit row (128 B) = 16 units of 8 B; unit 4*kb + g holds the same 8
  * elements, element i at byte i.  Meta row (16 B) = u16 scale[0..3], then u16 zero[0..3].
  *
+ * Uniform planes of either tensor hold a whole number of 64-token blocks.
+ *
  * Uniform V (blocks of 32 tokens, head dimension outermost within 8-token lanes).  Token t:
  * block b = t/32, tau = t%32, kb = tau/8, i = tau%8; element d: n = d%16, N = d/16.
  * 4-bit block (2048 B): u32 word 8*(16*kb + n) + N, token i at bit 16*(i%2) + 4*(i/2).
@@ -382,16 +384,14 @@ static size_t k_row(int t) { return (size_t)(64 * (t / 64) + 16 * ((t % 64) % 4)
 size_t orc_codes_bytes(const orc_plane_cfg* pc)
 {
     if (pc->scheme != ORC_UNIFORM) return (size_t)pc->capacity * 48;
-    if (pc->tensor == ORC_TENSOR_K) return (size_t)ceil_to(pc->capacity, 64) * 16 * pc->bits;
-    return (size_t)ceil_to(pc->capacity, 32) * 16 * pc->bits;
+    return (size_t)ceil_to(pc->capacity, 64) * 16 * pc->bits;
 }
 
 size_t orc_meta_bytes(const orc_plane_cfg* pc)
 {
     if (pc->scheme == ORC_TURBO_QJL) return (size_t)pc->capacity * 4;
     if (pc->scheme == ORC_TURBO_MSE) return (size_t)pc->capacity * 2;
-    if (pc->tensor == ORC_TENSOR_K) return (size_t)ceil_to(pc->capacity, 64) * 16;
-    return (size_t)ceil_to(pc->capacity, 32) * 16;
+    return (size_t)ceil_to(pc->capacity, 64) * 16;
 }
 
 size_t orc_qjl_bytes(const orc_plane_cfg* pc)

@@ -18,13 +18,16 @@ LIB = os.path.join(HERE, "libkvq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function"]
+ROOT = os.path.dirname(HERE)
+INCLUDE = os.environ.get("KVQ_INCLUDE", os.path.join(ROOT, "include"))
+COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-rdc"]
 UNITS = [
     ("kvq_quant.hip", DEVICE + ["-ffp-contract=off"]),
     ("kvq_decode.hip", DEVICE),
-    ("kvq_host.cpp", []),
+    ("kvq_decode_mfma.hip", DEVICE),
+    ("kvq_host.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]),  # host only
 ]
 
 

@@ -10,7 +10,7 @@
 #include <new>
 #include <vector>
 
-#include "../../include/kvq.h"
+#include "kvq.h"
 #include "kvq_internal.h"
 
 using namespace kvq;
@@ -67,7 +67,7 @@ PlaneGeom make_geom(const kvq_config* c, int tensor) {
     g.sinkhorn = (scheme == KVQ_UNIFORM && c->sinkhorn_iters > 0) ? 1 : 0;
     const size_t cap = (size_t)c->max_context;
     if (scheme == KVQ_UNIFORM) {
-        const size_t rows = tensor == 0 ? ceil_to(cap, 64) : ceil_to(cap, 32);
+        const size_t rows = ceil_to(cap, 64); // whole 64-token blocks: decode reads 64 at a time
         g.codes_bytes = rows * 16 * (size_t)g.bits;
         g.meta_bytes = rows * 16;
         g.qjl_bytes = 0;
@@ -364,6 +364,7 @@ kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, fl
     p.qjl_st = c->ST();
     p.mu = c->mu();
     p.partials = reinterpret_cast<float*>(c->base + c->plan.off_work);
+    p.counters = reinterpret_cast<unsigned*>(c->base + c->plan.off_counters);
     p.dtype = dtype;
     p.batch = batch;
     p.Hq = c->cfg.n_q_heads;
@@ -379,9 +380,16 @@ kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, fl
         const int nq = p.window > 0 ? std::max(0, len[b] - p.window) : len[b];
         nq_max = std::max(nq_max, nq);
     }
+    const bool matrix = c->decode_path != 1 && mfma_path_supported(p);
+    if (c->decode_path == 2 && !matrix) return KVQ_ERR_UNSUPPORTED;
     int st;
     if (c->split_tokens_opt > 0) {
         st = c->split_tokens_opt;
+    } else if (matrix) {
+        // one 8-wave workgroup per compute unit across all (sequence, kv head) pairs
+        const int target = std::max(1, (c->num_cus + p.Hkv * batch - 1) / (p.Hkv * batch));
+        st = (int)ceil_to((size_t)std::max(1, (nq_max + target - 1) / target), 64);
+        st = std::max(st, 128);
     } else {
         const int target = std::max(1, (2 * c->num_cus + p.Hkv * batch - 1) / (p.Hkv * batch));
         st = (int)ceil_to((size_t)std::max(1, (nq_max + target - 1) / target), 64);
@@ -396,8 +404,13 @@ kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, fl
     p.n_splits = ns;
     p.n_splits_total = ns + (p.window > 0 ? 1 : 0);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_decode_vec(p, s);
-    if (e == hipSuccess) e = launch_decode_merge(p, s);
+    hipError_t e;
+    if (matrix) {
+        e = launch_decode_mfma(p, s);
+    } else {
+        e = launch_decode_vec(p, s);
+        if (e == hipSuccess) e = launch_decode_merge(p, s);
+    }
     if (e != hipSuccess) return dev_fail(c, e);
     return KVQ_OK;
 }

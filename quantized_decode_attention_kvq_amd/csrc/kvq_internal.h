@@ -1,7 +1,7 @@
 // Internal declarations shared by the host code and the HIP kernels of libkvq.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cstddef>
 #include <cstdint>
@@ -55,7 +55,9 @@ struct DecodeParams {
     const float* cs;          // layer base [Hkv][2][128] Sinkhorn c
     const float* qjl_st;      // [128 j][128 i]
     const float* mu;
-    float* partials;          // [batch][Hq][n_splits_total][kPartialFloats]
+    float* partials;          // vector path: [batch][Hq][n_splits_total][kPartialFloats];
+                              // matrix path: [batch][Hkv][n_splits_total][G][kPartialFloats]
+    unsigned* counters;       // [batch][Hkv] arrival counters of the matrix path (zero between calls)
     int dtype, batch, Hq, Hkv, G, window;
     float qscale;             // softmax scale * log2(e)
     int split_tokens, n_splits, n_splits_total;
@@ -80,5 +82,7 @@ hipError_t launch_transpose128(const float* in, float* out, hipStream_t s);
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t s);
 hipError_t launch_decode_vec(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t s);
+bool mfma_path_supported(const DecodeParams& p);
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s);
 
 } // namespace kvq
