@@ -356,54 +356,89 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
 }
 
 // Fixed-order merge of the splits of one (sequence, query head), then
-// out = (R_V^-1(c_V .* acc_codes) + acc_window) / l.
-__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeParams p) {
-    __shared__ float buf[kDim];
-    const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+// out = (R_V^-1(c_V .* acc_codes) + acc_window) / l.  256 threads: thread t owns channels
+// 4(t%32)..4(t%32)+3 of splits t/32, t/32 + 8, ...; the 8 split classes are then combined in
+// LDS in ascending order, so the result depends only on the split count.
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
+    __shared__ float s_m[8], s_l[8];
+    __shared__ float4 s_q[8][32], s_w[8][32];
+    const int hq = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+    const int c4 = t & 31, part = t >> 5;
     const int kvh = hq / p.G;
-    float* out = p.out + ((size_t)b * p.Hq + hq) * kDim;
+    float4* out = reinterpret_cast<float4*>(p.out + ((size_t)b * p.Hq + hq) * kDim) + c4;
     if (p.len[b] == 0) {
-        out[d] = 0.0f;
+        if (part == 0) *out = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         return;
     }
-    const float* part = p.partials + ((size_t)b * p.Hq + hq) * p.n_splits_total * kPartialFloats;
-    float M = kNegInf;
-    for (int s = 0; s < p.n_splits_total; ++s) M = fmaxf(M, part[s * kPartialFloats]);
-    float L = 0.0f, aq = 0.0f, aw = 0.0f;
-    for (int s = 0; s < p.n_splits_total; ++s) {
-        const float ms = part[s * kPartialFloats];
+    const float* base = p.partials + ((size_t)b * p.Hq + hq) * p.n_splits_total * kPartialFloats;
+    float m = kNegInf, l = 0.0f;
+    float4 aq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), aw = aq;
+#pragma unroll 4
+    for (int s = part; s < p.n_splits_total; s += 8) {
+        const float* ps = base + (size_t)s * kPartialFloats;
+        const float ms = ps[0], ls = ps[1];
+        const float4 a = *reinterpret_cast<const float4*>(ps + 4 + 4 * c4);
         if (ms == kNegInf) continue;
-        const float f = exp2f(ms - M);
-        L += part[s * kPartialFloats + 1] * f;
-        const float a = part[s * kPartialFloats + 4 + d] * f;
-        if (p.window > 0 && s == p.n_splits)
-            aw += a;
-        else
-            aq += a;
+        const float mn = fmaxf(m, ms);
+        const float fo = exp2f(m - mn), fn = exp2f(ms - mn);
+        m = mn;
+        l = fmaf(ls, fn, l * fo);
+        aq.x *= fo; aq.y *= fo; aq.z *= fo; aq.w *= fo;
+        aw.x *= fo; aw.y *= fo; aw.z *= fo; aw.w *= fo;
+        float4& dst = s >= p.n_splits ? aw : aq;
+        dst.x = fmaf(a.x, fn, dst.x);
+        dst.y = fmaf(a.y, fn, dst.y);
+        dst.z = fmaf(a.z, fn, dst.z);
+        dst.w = fmaf(a.w, fn, dst.w);
+    }
+    if (c4 == 0) {
+        s_m[part] = m;
+        s_l[part] = l;
+    }
+    s_q[part][c4] = aq;
+    s_w[part][c4] = aw;
+    __syncthreads();
+    if (part != 0) return;
+    float M = kNegInf;
+    for (int i = 0; i < 8; ++i) M = fmaxf(M, s_m[i]);
+    float L = 0.0f, q[4] = {0.0f, 0.0f, 0.0f, 0.0f}, w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < 8; ++i) {
+        if (s_m[i] == kNegInf) continue;
+        const float f = exp2f(s_m[i] - M);
+        L = fmaf(s_l[i], f, L);
+        const float4 a = s_q[i][c4], c = s_w[i][c4];
+        q[0] = fmaf(a.x, f, q[0]); q[1] = fmaf(a.y, f, q[1]);
+        q[2] = fmaf(a.z, f, q[2]); q[3] = fmaf(a.w, f, q[3]);
+        w[0] = fmaf(c.x, f, w[0]); w[1] = fmaf(c.y, f, w[1]);
+        w[2] = fmaf(c.z, f, w[2]); w[3] = fmaf(c.w, f, w[3]);
     }
     const PlaneGeom& VG = p.geom[1];
-    if (VG.sinkhorn) aq *= p.cs[(size_t)(kvh * 2 + 1) * kDim + d];
+    const size_t tab = (size_t)(kvh * 2 + 1) * kDim + 4 * c4;
+    if (VG.sinkhorn)
+        for (int j = 0; j < 4; ++j) q[j] *= p.cs[tab + j];
     if (VG.rotate) {
-        buf[d] = aq;
-        __syncthreads();
-        for (int h = 1; h < kDim; h <<= 1) {
-            float x = 0.0f, y = 0.0f;
-            const bool lower = !(d & h);
-            if (lower) {
-                x = buf[d];
-                y = buf[d + h];
+        // Walsh-Hadamard butterflies over the 128 channels: strides 1 and 2 inside a thread,
+        // strides 4..64 between the 32 lanes (channel 4*lane + j) by xor shuffles.
+        for (int h = 1; h < 4; h <<= 1)
+            for (int j = 0; j < 4; ++j)
+                if (!(j & h)) {
+                    const float x = q[j], y = q[j + h];
+                    q[j] = x + y;
+                    q[j + h] = x - y;
+                }
+        for (int h = 1; h < 32; h <<= 1) {
+            const bool upper = (c4 & h) != 0;
+            for (int j = 0; j < 4; ++j) {
+                const float o = __shfl_xor(q[j], h, 64);
+                q[j] = upper ? o - q[j] : q[j] + o;
             }
-            __syncthreads();
-            if (lower) {
-                buf[d] = x + y;
-                buf[d + h] = x - y;
-            }
-            __syncthreads();
         }
-        aq = buf[d] * c0f();
-        if (p.signs[(size_t)(kvh * 2 + 1) * kDim + d] < 0.0f) aq = -aq;
+        for (int j = 0; j < 4; ++j) {
+            q[j] *= c0f();
+            if (p.signs[tab + j] < 0.0f) q[j] = -q[j];
+        }
     }
-    out[d] = (aq + aw) / L;
+    *out = make_float4((q[0] + w[0]) / L, (q[1] + w[1]) / L, (q[2] + w[2]) / L, (q[3] + w[3]) / L);
 }
 
 } // namespace
@@ -415,7 +450,7 @@ hipError_t launch_decode_vec(const DecodeParams& p, hipStream_t s) {
 }
 
 hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(p.Hq, p.batch), dim3(kDim), 0, s, p);
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(p.Hq, p.batch), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

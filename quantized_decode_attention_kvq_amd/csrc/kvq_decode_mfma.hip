@@ -19,9 +19,8 @@
 //  * PV: A = p * scale_g (fp16 hi + lo) staged through LDS into matrix-operand order, B = raw V
 //    codes from the token-blocked V plane (dense over tokens), plus a vector-ALU sum of
 //    p * zero_g.
-//  * Split partials are merged by the last workgroup to finish for each (sequence, kv head)
-//    (device-scope arrival counter, fixed merge order), which also applies R_V^-1 and c_V.
-//    Partials travel through write-through stores/loads, so no cache flush is needed.
+//  * Each split writes one partial (running max, sum, acc[128]) per query head; the separate
+//    merge kernel combines them in a fixed order and applies c_V and R_V^-1.
 //  * The FP32 window (progressive mode) is one extra split computed on the vector ALU.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
@@ -153,16 +152,6 @@ __device__ __forceinline__ void load_v(VRegs<VB>& r, const uint8_t* vc, const ui
     for (int j = 0; j < 4; ++j) r.vm[j] = *reinterpret_cast<const u4*>(vm + 16 * j);
 }
 
-// Write-through (agent-scope) accesses for the split partials and the arrival counter: they
-// reach the device-coherent level directly, so no L2 writeback/invalidate is needed to hand
-// data between workgroups on different dies.
-__device__ __forceinline__ void st_agent(float* p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 template <int KB, int VB, int MB, int kNW>
 __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     __shared__ float s_q[kMaxGroupHeads][kDim];   // q' in the rotated/balanced domain, scaled
@@ -172,15 +161,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     __shared__ __align__(16) _Float16 s_p[kNW * kPWave];
     __shared__ float s_wm[kNW][kMaxGroupHeads], s_wl[kNW][kMaxGroupHeads];
     __shared__ float s_wz[kNW][kMaxGroupHeads][4];
-    __shared__ float s_M[kMaxGroupHeads], s_L[kMaxGroupHeads];
-    __shared__ int s_last;
 
     const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
     const int G = p.G, W = p.window;
     const int n = p.len[b];
     const int nq = (W > 0) ? max(0, n - W) : n;
-    const bool wsplit = (W > 0) && (split == p.n_splits);
+    const bool wsplit = (W > 0) && (split >= p.n_splits); // FP32-window workgroups come last
     const PlaneGeom& KG = p.geom[0];
     const PlaneGeom& VG = p.geom[1];
     const char* slot = p.layer_base + (size_t)b * p.seq_stride + (size_t)kvh * p.head_stride;
@@ -193,33 +180,67 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     const float UK = (KB == 4) ? 1048576.0f : 16777216.0f; // 2^20 / 2^24: unit of a code product
     const float UV = (VB == 4) ? 1048576.0f : 16777216.0f;
 
-    // ---------------- query preparation (once per workgroup) ----------------
-    for (int h = wave; h < G; h += kNW) {
-        const size_t off = ((size_t)b * p.Hq + kvh * G + h) * kDim;
-        float a, c;
-        if (p.dtype == 0) {
-            const float2 v = reinterpret_cast<const float2*>(static_cast<const float*>(p.q) + off)[l];
-            a = v.x;
-            c = v.y;
-        } else {
-            const uint32_t v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.q) + off)[l];
-            a = bf2f((uint16_t)(v & 0xffff));
-            c = bf2f((uint16_t)(v >> 16));
+    // ---------------- the query-side loads go out first (they are small and the preparation
+    // waits on them), then this wave's first chunk, so the memory pipe starts immediately
+    constexpr int kHPW = (kMaxGroupHeads + kNW - 1) / kNW; // heads prepared per wave
+    float qa[kHPW], qc[kHPW];
+#pragma unroll
+    for (int i = 0; i < kHPW; ++i) {
+        const int h = wave + i * kNW;
+        qa[i] = qc[i] = 0.0f;
+        if (h < G) {
+            const size_t off = ((size_t)b * p.Hq + kvh * G + h) * kDim;
+            if (p.dtype == 0) {
+                const float2 v = reinterpret_cast<const float2*>(static_cast<const float*>(p.q) + off)[l];
+                qa[i] = v.x;
+                qc[i] = v.y;
+            } else {
+                const uint32_t v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.q) + off)[l];
+                qa[i] = bf2f((uint16_t)(v & 0xffff));
+                qc[i] = bf2f((uint16_t)(v >> 16));
+            }
         }
+    }
+    const float2 sgn = reinterpret_cast<const float2*>(p.signs + (size_t)(kvh * 2 + 0) * kDim)[l];
+    const float2 csk = reinterpret_cast<const float2*>(p.cs + (size_t)(kvh * 2 + 0) * kDim)[l];
+    const int lr = l & 15, lq = l >> 4; // column / quarter of the 16x16 tiles
+    const int tok_begin = split * p.split_tokens;
+    const int tok_end = wsplit ? tok_begin : min(nq, tok_begin + p.split_tokens);
+    const int nch = (tok_end > tok_begin) ? (tok_end - tok_begin + 63) / 64 : 0;
+    // chunk ci of this split starts at token tok_begin + 64 ci; a lane's addresses in it:
+    auto kc_at = [&](int ci) { return kcodes + ((size_t)tok_begin + 64 * ci + lr) * (16 * KB) + (16 * KB / 4) * lq; };
+    auto km_at = [&](int ci) { return kmeta + ((size_t)tok_begin + 64 * ci + lr) * 16; };
+    auto vc_at = [&](int ci) {
+        return vcodes + (size_t)((tok_begin + 64 * ci) / 32) * (512 * VB) + (size_t)(32 * VB / 4) * l;
+    };
+    auto vm_at = [&](int ci) { return vmeta + ((size_t)tok_begin + 64 * ci + 4 * lr) * 16; };
+    // The wave's first chunk is requested right away; each later chunk is requested as soon as
+    // the registers it goes into have been consumed (K after the scores, V after PV).
+    KRegs<KB> kr;
+    VRegs<VB> vr;
+    if (wave < nch) {
+        load_k(kr, kc_at(wave), km_at(wave));
+        load_v(vr, vc_at(wave), vm_at(wave));
+    }
+
+    // ---------------- query preparation (once per workgroup) ----------------
+#pragma unroll
+    for (int i = 0; i < kHPW; ++i) {
+        const int h = wave + i * kNW;
+        if (h >= G) break;
+        float a = qa[i], c = qc[i];
         s_qw[h][2 * l] = a * p.qscale;
         s_qw[h][2 * l + 1] = c * p.qscale;
         if (KG.rotate) {
-            const float* sg = p.signs + (size_t)(kvh * 2 + 0) * kDim;
-            if (sg[2 * l] < 0.0f) a = -a;
-            if (sg[2 * l + 1] < 0.0f) c = -c;
+            if (sgn.x < 0.0f) a = -a;
+            if (sgn.y < 0.0f) c = -c;
             hadamard_wave(a, c, l);
             a *= c0f();
             c *= c0f();
         }
         if (KG.sinkhorn) {
-            const float* cs = p.cs + (size_t)(kvh * 2 + 0) * kDim;
-            a *= cs[2 * l];
-            c *= cs[2 * l + 1];
+            a *= csk.x;
+            c *= csk.y;
         }
         a *= p.qscale;
         c *= p.qscale;
@@ -238,8 +259,6 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
         if (l == 0) s_qfac[h] = ldexpf(1.0f, -e);
     }
     __syncthreads();
-
-    const int lr = l & 15, lq = l >> 4; // column / quarter of the 16x16 tiles
 
     // per-wave softmax state, in the score layout (lane: head 4*mb + lq, column lr)
     float m_run[MB], l_run[MB], z_run[MB][4];
@@ -293,26 +312,10 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             F[mb] = UK * s_qfac[hs];
         }
 
-        const int tok_begin = split * p.split_tokens;
-        const int tok_end = min(nq, tok_begin + p.split_tokens);
-        const int nch = (tok_end > tok_begin) ? (tok_end - tok_begin + 63) / 64 : 0;
-        // per-wave streams (advanced by kNW chunks per iteration)
-        const int t0w = tok_begin + 64 * wave;
-        const uint8_t* kc_p = kcodes + ((size_t)t0w + lr) * (16 * KB) + (16 * KB / 4) * lq;
-        const uint8_t* km_p = kmeta + ((size_t)t0w + lr) * 16;
-        const uint8_t* vc_p = vcodes + (size_t)(t0w / 32) * (512 * VB) + (size_t)(32 * VB / 4) * l;
-        const uint8_t* vm_p = vmeta + ((size_t)t0w + 4 * lr) * 16;
-        constexpr size_t kc_step = (size_t)64 * kNW * 16 * KB, km_step = (size_t)64 * kNW * 16;
-        constexpr size_t vc_step = (size_t)2 * kNW * 512 * VB, vm_step = (size_t)64 * kNW * 16;
-        KRegs<KB> kr;
-        VRegs<VB> vr;
-        if (wave < nch) {
-            load_k(kr, kc_p, km_p);
-            load_v(vr, vc_p, vm_p);
-        }
         for (int ci = wave; ci < nch; ci += kNW) {
             const int c0 = tok_begin + 64 * ci;
-            const bool more = ci + kNW < nch;
+            const int nci = ci + kNW; // the chunk the registers are refilled with
+            const bool more = nci < nch;
             const auto& kc = kr.kc;
             const auto& km = kr.km;
             const auto& vc = vr.vc;
@@ -352,11 +355,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             }
 
             // the next chunk's K is requested as soon as this chunk's scores are formed
-            if (more) {
-                kc_p += kc_step;
-                km_p += km_step;
-                load_k(kr, kc_p, km_p);
-            }
+            if (more) load_k(kr, kc_at(nci), km_at(nci));
 
             // ---- online softmax
             float pj[MB][4], alpha[MB];
@@ -449,11 +448,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             }
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            if (more) {
-                vc_p += vc_step;
-                vm_p += vm_step;
-                load_v(vr, vc_p, vm_p);
-            }
+            if (more) load_v(vr, vc_at(nci), vm_at(nci));
         }
         // reduce the per-lane softmax sums over each row of 16 lanes
 #pragma unroll
@@ -463,59 +458,45 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             for (int g = 0; g < 4; ++g) z_run[mb][g] = row_sum16(z_run[mb][g]);
         }
     } else {
-        // ---------------- FP32 window split (vector ALU): tokens nq .. n-1 ----------------
-        // kWinPW tokens per wave: lanes 0..kWinPW-1 score one token each, then every lane
-        // accumulates two channels over those tokens.
-        constexpr int kWinPW = kWindowMax / kNW;
-        float* pb = reinterpret_cast<float*>(my_p); // [8 heads][kWinPW] probabilities
-        const int base = nq + kWinPW * wave;
-        if (base < n) {
-            const int t = base + l;
-            const bool valid = (l < kWinPW) && (t < n);
-            float sc[kMaxGroupHeads];
+        // ---------------- FP32 window (vector ALU): tokens nq .. n-1 ----------------
+        // The window is spread over p.n_win_splits workgroups.  A wave takes 4 tokens at a time:
+        // 16 lanes per token form its G scores (8 channels per lane, then a row reduction), the
+        // four tokens update the running softmax, and every lane accumulates two channels of V.
+        const int per_wg = (kWindowMax + p.n_win_splits - 1) / p.n_win_splits;
+        const int wb = nq + (split - p.n_splits) * per_wg;
+        const int we = min(n, wb + per_wg);
+        for (int t4 = wb + 4 * wave; t4 < we; t4 += 4 * kNW) {
+            const int tok = t4 + lq;
+            const bool valid = tok < we;
+            const float* krow = kring + (size_t)((valid ? tok : t4) % W) * kDim + 8 * lr;
+            const float4 k0 = *reinterpret_cast<const float4*>(krow);
+            const float4 k1 = *reinterpret_cast<const float4*>(krow + 4);
+            float2 vv[4];
 #pragma unroll
-            for (int h = 0; h < kMaxGroupHeads; ++h) sc[h] = 0.0f;
-            if (valid) {
-                const float* kr = kring + (size_t)(t % W) * kDim;
-#pragma unroll 4
-                for (int j = 0; j < kDim; j += 4) {
-                    const float4 kv = *reinterpret_cast<const float4*>(kr + j);
-#pragma unroll
-                    for (int h = 0; h < kMaxGroupHeads; ++h)
-                        if (h < G)
-                            sc[h] += kv.x * s_qw[h][j] + kv.y * s_qw[h][j + 1] + kv.z * s_qw[h][j + 2] +
-                                     kv.w * s_qw[h][j + 3];
-                }
-            }
-#pragma unroll
-            for (int h = 0; h < kMaxGroupHeads; ++h) {
-                if (h < G) {
-                    const float mh = wave_max(valid ? sc[h] : kNegInf);
-                    const float pr = valid ? exp2f(sc[h] - mh) : 0.0f;
-                    wm[h] = mh;
-                    wl[h] = wave_sum(pr);
-                    if (l < kWinPW) pb[h * kWinPW + l] = pr;
-                }
-            }
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            float2 vv[kWinPW];
-#pragma unroll
-            for (int tau = 0; tau < kWinPW; ++tau) {
-                const int tt = min(base + tau, n - 1);
+            for (int tau = 0; tau < 4; ++tau) {
+                const int tt = min(t4 + tau, we - 1);
                 vv[tau] = reinterpret_cast<const float2*>(vring + (size_t)(tt % W) * kDim)[l];
             }
 #pragma unroll
-            for (int tau = 0; tau < kWinPW; ++tau) {
-                if (base + tau < n) {
-#pragma unroll
-                    for (int h = 0; h < kMaxGroupHeads; ++h)
-                        if (h < G) {
-                            const float pr = pb[h * kWinPW + tau];
-                            wacc0[h] = fmaf(pr, vv[tau].x, wacc0[h]);
-                            wacc1[h] = fmaf(pr, vv[tau].y, wacc1[h]);
-                        }
-                }
+            for (int h = 0; h < kMaxGroupHeads; ++h) {
+                if (h >= G) continue;
+                const float* qh = &s_qw[h][8 * lr];
+                float d = k0.x * qh[0] + k0.y * qh[1] + k0.z * qh[2] + k0.w * qh[3] +
+                          k1.x * qh[4] + k1.y * qh[5] + k1.z * qh[6] + k1.w * qh[7];
+                d = row_sum16(d);
+                const float sv = valid ? d : kNegInf;
+                const float s0 = readlane_f(sv, 0), s1 = readlane_f(sv, 16), s2 = readlane_f(sv, 32),
+                            s3 = readlane_f(sv, 48);
+                const float mnew = fmaxf(wm[h], fmaxf(fmaxf(s0, s1), fmaxf(s2, s3)));
+                const float al = (mnew == kNegInf) ? 1.0f : exp2f(wm[h] - mnew);
+                const float p0 = (s0 == kNegInf) ? 0.0f : exp2f(s0 - mnew);
+                const float p1 = (s1 == kNegInf) ? 0.0f : exp2f(s1 - mnew);
+                const float p2 = (s2 == kNegInf) ? 0.0f : exp2f(s2 - mnew);
+                const float p3 = (s3 == kNegInf) ? 0.0f : exp2f(s3 - mnew);
+                wl[h] = wl[h] * al + ((p0 + p1) + (p2 + p3));
+                wm[h] = mnew;
+                wacc0[h] = fmaf(p3, vv[3].x, fmaf(p2, vv[2].x, fmaf(p1, vv[1].x, fmaf(p0, vv[0].x, wacc0[h] * al))));
+                wacc1[h] = fmaf(p3, vv[3].y, fmaf(p2, vv[2].y, fmaf(p1, vv[1].y, fmaf(p0, vv[0].y, wacc1[h] * al))));
             }
         }
     }
@@ -557,8 +538,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
         }
     }
     __syncthreads();
-    const int S_total = p.n_splits_total;
-    float* part_kvh = p.partials + (((size_t)b * p.Hkv + kvh) * S_total) * G * kPartialFloats;
+    // partial of this split for each of its query heads: [b][hq][split][m, l, -, -, acc[128]]
     for (int idx = tid; idx < G * kDim; idx += kNW * 64) {
         const int h = idx >> 7, d = idx & 127;
         float M = kNegInf;
@@ -572,140 +552,15 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                 L = fmaf(f, s_wl[w][h], L);
             }
         }
-        float* part = part_kvh + ((size_t)split * G + h) * kPartialFloats;
-        st_agent(part + 4 + d, A);
+        float* part = p.partials + (((size_t)b * p.Hq + kvh * G + h) * p.n_splits_total + split) * kPartialFloats;
+        part[4 + d] = A;
         if (d == 0) {
-            st_agent(part + 0, M);
-            st_agent(part + 1, L);
+            part[0] = M;
+            part[1] = L;
         }
     }
-
-    // ---------------- the last workgroup of this (sequence, kv head) merges ----------------
-    // Every partial store above is write-through and has completed once the barrier's wait on
-    // outstanding memory operations returns; only then is the arrival counted.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(&p.counters[b * p.Hkv + kvh], 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == (unsigned)(S_total - 1)) ? 1 : 0;
-    }
-    __syncthreads();
-    if (!s_last) return;
-
-    float* s_wgt = s_acc;                         // [8][S_total] split weights
-    float* s_fin = s_acc + kMaxGroupHeads * (kMaxSplits + 1);  // [8][128] code-domain sums
-    float* s_finw = s_fin + kMaxGroupHeads * kDim;             // [8][128] window sums
-    for (int h = wave; h < G; h += kNW) {
-        float M = kNegInf;
-        for (int s = l; s < S_total; s += 64) M = fmaxf(M, ld_agent(part_kvh + ((size_t)s * G + h) * kPartialFloats));
-        M = wave_max(M);
-        float L = 0.0f;
-        for (int s = l; s < S_total; s += 64) {
-            const float* ps = part_kvh + ((size_t)s * G + h) * kPartialFloats;
-            const float ms = ld_agent(ps);
-            const float w = (ms == kNegInf) ? 0.0f : exp2f(ms - M);
-            s_wgt[h * (kMaxSplits + 1) + s] = w;
-            L = fmaf(w, ld_agent(ps + 1), L);
-        }
-        L = wave_sum(L);
-        if (l == 0) {
-            s_M[h] = M;
-            s_L[h] = L;
-        }
-    }
-    __syncthreads();
-    {
-        // code-domain splits: every thread sums a strided subset of splits for one (head, 4
-        // channels); loads are issued in batches of 4 so their latencies overlap.  The subsets
-        // and their final sum run in a fixed order.
-        const int items = G * 32;
-        const int nparts = max(1, (kNW * 64) / items);
-        const int nqs = p.n_splits;
-        float4* s_red = reinterpret_cast<float4*>(s_finw + kMaxGroupHeads * kDim); // [nparts][items]
-        if (tid < items * nparts) {
-            const int item = tid % items, part = tid / items;
-            const int h = item >> 5, d4 = item & 31;
-            float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            for (int s0 = part; s0 < nqs; s0 += 4 * nparts) {
-                float4 v[4];
-                float w[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int s = s0 + u * nparts;
-                    if (s < nqs) {
-                        w[u] = s_wgt[h * (kMaxSplits + 1) + s];
-                        const float* ps = part_kvh + ((size_t)s * G + h) * kPartialFloats + 4 + 4 * d4;
-                        v[u] = make_float4(ld_agent(ps), ld_agent(ps + 1), ld_agent(ps + 2), ld_agent(ps + 3));
-                    } else {
-                        w[u] = 0.0f;
-                        v[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    a.x = fmaf(w[u], v[u].x, a.x);
-                    a.y = fmaf(w[u], v[u].y, a.y);
-                    a.z = fmaf(w[u], v[u].z, a.z);
-                    a.w = fmaf(w[u], v[u].w, a.w);
-                }
-            }
-            s_red[part * items + item] = a;
-        }
-        // the FP32 window split
-        if (tid < items) {
-            const int h = tid >> 5, d4 = tid & 31;
-            float4 aw = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (W > 0) {
-                const float w = s_wgt[h * (kMaxSplits + 1) + nqs];
-                const float* ps = part_kvh + ((size_t)nqs * G + h) * kPartialFloats + 4 + 4 * d4;
-                const float4 v = make_float4(ld_agent(ps), ld_agent(ps + 1), ld_agent(ps + 2), ld_agent(ps + 3));
-                aw = make_float4(w * v.x, w * v.y, w * v.z, w * v.w);
-            }
-            *reinterpret_cast<float4*>(s_finw + h * kDim + 4 * d4) = aw;
-        }
-        __syncthreads();
-        if (tid < items) {
-            float4 a = s_red[tid];
-            for (int q = 1; q < nparts; ++q) {
-                const float4 b2 = s_red[q * items + tid];
-                a.x += b2.x;
-                a.y += b2.y;
-                a.z += b2.z;
-                a.w += b2.w;
-            }
-            const int h = tid >> 5, d4 = tid & 31;
-            *reinterpret_cast<float4*>(s_fin + h * kDim + 4 * d4) = a;
-        }
-    }
-    __syncthreads();
-    for (int h = wave; h < G; h += kNW) {
-        float a = s_fin[h * kDim + 2 * l], c = s_fin[h * kDim + 2 * l + 1];
-        if (VG.sinkhorn) {
-            const float* cs = p.cs + (size_t)(kvh * 2 + 1) * kDim;
-            a *= cs[2 * l];
-            c *= cs[2 * l + 1];
-        }
-        if (VG.rotate) {
-            hadamard_wave(a, c, l);
-            a *= c0f();
-            c *= c0f();
-            const float* sg = p.signs + (size_t)(kvh * 2 + 1) * kDim;
-            if (sg[2 * l] < 0.0f) a = -a;
-            if (sg[2 * l + 1] < 0.0f) c = -c;
-        }
-        const float L = s_L[h];
-        const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
-        float2 o;
-        o.x = (a + s_finw[h * kDim + 2 * l]) * inv;
-        o.y = (c + s_finw[h * kDim + 2 * l + 1]) * inv;
-        reinterpret_cast<float2*>(p.out + ((size_t)b * p.Hq + kvh * G + h) * kDim)[l] = o;
-    }
-    if (tid == 0) __hip_atomic_store(&p.counters[b * p.Hkv + kvh], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// 8 waves (2 per SIMD, <= 256 registers each) for the 4-bit / 4-bit, <= 4 heads-per-group
-// variant; 4 waves (1 per SIMD, up to 512 registers) for the variants with more operand state.
 template <int KB, int VB, int MB>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
     constexpr int NW = (KB == 4 && VB == 4 && MB == 1) ? 8 : 4;

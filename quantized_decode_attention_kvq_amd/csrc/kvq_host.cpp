@@ -28,7 +28,7 @@ struct Plan {
     size_t plane_bytes[2];
     size_t slot_bytes;
     size_t off_signs, off_c, off_inv_c, off_S, off_ST, off_mu, off_theta;
-    size_t off_work, work_bytes, off_counters;
+    size_t off_work, work_bytes;
     size_t off_planes, total;
 };
 
@@ -111,9 +111,7 @@ Plan make_plan(const kvq_config* c) {
     off = align_up(off + 8 * sizeof(float));
     p.off_theta = off;
     off = align_up(off + 8 * sizeof(float));
-    p.off_counters = off;
-    off = align_up(off + (size_t)c->max_batch * c->n_kv_heads * sizeof(uint32_t));
-    const size_t partial = (size_t)c->max_batch * c->n_q_heads * (kMaxSplits + 1) * kPartialFloats *
+    const size_t partial = (size_t)c->max_batch * c->n_q_heads * kMaxSplits * kPartialFloats *
                            sizeof(float);
     const size_t calib = c->sinkhorn_iters > 0
                              ? (size_t)2 * c->n_kv_heads * c->calib_tokens * kDim * sizeof(double)
@@ -364,7 +362,6 @@ kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, fl
     p.qjl_st = c->ST();
     p.mu = c->mu();
     p.partials = reinterpret_cast<float*>(c->base + c->plan.off_work);
-    p.counters = reinterpret_cast<unsigned*>(c->base + c->plan.off_counters);
     p.dtype = dtype;
     p.batch = batch;
     p.Hq = c->cfg.n_q_heads;
@@ -386,8 +383,10 @@ kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, fl
     if (c->split_tokens_opt > 0) {
         st = c->split_tokens_opt;
     } else if (matrix) {
-        // one 8-wave workgroup per compute unit across all (sequence, kv head) pairs
-        const int target = std::max(1, (c->num_cus + p.Hkv * batch - 1) / (p.Hkv * batch));
+        // one workgroup per compute unit across all (sequence, kv head) pairs, the FP32-window
+        // workgroup included, so that no workgroup waits for a free compute unit
+        const int per = std::max(1, c->num_cus / (p.Hkv * batch));
+        const int target = std::max(1, per - (p.window > 0 ? kWinSplitsMatrix : 0));
         st = (int)ceil_to((size_t)std::max(1, (nq_max + target - 1) / target), 64);
         st = std::max(st, 128);
     } else {
@@ -395,22 +394,21 @@ kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, fl
         st = (int)ceil_to((size_t)std::max(1, (nq_max + target - 1) / target), 64);
         st = std::max(st, 256);
     }
+    const int nwin = p.window > 0 ? (matrix ? kWinSplitsMatrix : 1) : 0;
+    const int max_code_splits = kMaxSplits - nwin;
     int ns = std::max(1, (nq_max + st - 1) / st);
-    if (ns > kMaxSplits) {
-        st = (int)ceil_to((size_t)((nq_max + kMaxSplits - 1) / kMaxSplits), 64);
+    if (ns > max_code_splits) {
+        st = (int)ceil_to((size_t)((nq_max + max_code_splits - 1) / max_code_splits), 64);
         ns = std::max(1, (nq_max + st - 1) / st);
     }
     p.split_tokens = st;
     p.n_splits = ns;
-    p.n_splits_total = ns + (p.window > 0 ? 1 : 0);
+    p.n_win_splits = nwin;
+    p.n_splits_total = ns + nwin;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (matrix) {
-        e = launch_decode_mfma(p, s);
-    } else {
-        e = launch_decode_vec(p, s);
-        if (e == hipSuccess) e = launch_decode_merge(p, s);
-    }
+    e = matrix ? launch_decode_mfma(p, s) : launch_decode_vec(p, s);
+    if (e == hipSuccess) e = launch_decode_merge(p, s);
     if (e != hipSuccess) return dev_fail(c, e);
     return KVQ_OK;
 }

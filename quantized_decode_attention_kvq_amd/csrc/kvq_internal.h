@@ -12,9 +12,10 @@ constexpr int kDim = 128;
 constexpr int kGroup = 32;
 constexpr int kMaxBatch = 64;
 constexpr int kMaxGroupHeads = 8;   // query heads per kv head
-constexpr int kMaxSplits = 256;     // quantized-token splits per (sequence, kv head)
+constexpr int kMaxSplits = 256;     // splits per (sequence, kv head), window splits included
 constexpr int kPartialFloats = 132; // m, l, pad, pad, acc[128] per (sequence, q head, split)
 constexpr int kWindowMax = 128;
+constexpr int kWinSplitsMatrix = 1; // FP32-window workgroups per (sequence, kv head), matrix path
 
 enum Scheme { kUniform = 0, kTurboQjl = 1, kTurboMse = 2 };
 
@@ -55,12 +56,10 @@ struct DecodeParams {
     const float* cs;          // layer base [Hkv][2][128] Sinkhorn c
     const float* qjl_st;      // [128 j][128 i]
     const float* mu;
-    float* partials;          // vector path: [batch][Hq][n_splits_total][kPartialFloats];
-                              // matrix path: [batch][Hkv][n_splits_total][G][kPartialFloats]
-    unsigned* counters;       // [batch][Hkv] arrival counters of the matrix path (zero between calls)
+    float* partials;          // [batch][Hq][n_splits_total][kPartialFloats]
     int dtype, batch, Hq, Hkv, G, window;
     float qscale;             // softmax scale * log2(e)
-    int split_tokens, n_splits, n_splits_total;
+    int split_tokens, n_splits, n_win_splits, n_splits_total; // window splits come last
     int len[kMaxBatch];
 };
 
