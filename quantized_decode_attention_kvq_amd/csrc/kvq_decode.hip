@@ -373,23 +373,38 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     const float* base = p.partials + ((size_t)b * p.Hq + hq) * p.n_splits_total * kPartialFloats;
     float m = kNegInf, l = 0.0f;
     float4 aq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), aw = aq;
-#pragma unroll 4
-    for (int s = part; s < p.n_splits_total; s += 8) {
-        const float* ps = base + (size_t)s * kPartialFloats;
-        const float ms = ps[0], ls = ps[1];
-        const float4 a = *reinterpret_cast<const float4*>(ps + 4 + 4 * c4);
-        if (ms == kNegInf) continue;
-        const float mn = fmaxf(m, ms);
-        const float fo = exp2f(m - mn), fn = exp2f(ms - mn);
-        m = mn;
-        l = fmaf(ls, fn, l * fo);
-        aq.x *= fo; aq.y *= fo; aq.z *= fo; aq.w *= fo;
-        aw.x *= fo; aw.y *= fo; aw.z *= fo; aw.w *= fo;
-        float4& dst = s >= p.n_splits ? aw : aq;
-        dst.x = fmaf(a.x, fn, dst.x);
-        dst.y = fmaf(a.y, fn, dst.y);
-        dst.z = fmaf(a.z, fn, dst.z);
-        dst.w = fmaf(a.w, fn, dst.w);
+    // four splits per thread per round, all loads issued before any is used
+    for (int s0 = part; s0 < p.n_splits_total; s0 += 32) {
+        float ms[4], ls[4];
+        float4 a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = s0 + 8 * i;
+            ms[i] = kNegInf;
+            ls[i] = 0.0f;
+            a[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (s < p.n_splits_total) {
+                const float* ps = base + (size_t)s * kPartialFloats;
+                ms[i] = ps[0];
+                ls[i] = ps[1];
+                a[i] = *reinterpret_cast<const float4*>(ps + 4 + 4 * c4);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (ms[i] == kNegInf) continue;
+            const float mn = fmaxf(m, ms[i]);
+            const float fo = exp2f(m - mn), fn = exp2f(ms[i] - mn);
+            m = mn;
+            l = fmaf(ls[i], fn, l * fo);
+            aq.x *= fo; aq.y *= fo; aq.z *= fo; aq.w *= fo;
+            aw.x *= fo; aw.y *= fo; aw.z *= fo; aw.w *= fo;
+            float4& dst = s0 + 8 * i >= p.n_splits ? aw : aq;
+            dst.x = fmaf(a[i].x, fn, dst.x);
+            dst.y = fmaf(a[i].y, fn, dst.y);
+            dst.z = fmaf(a[i].z, fn, dst.z);
+            dst.w = fmaf(a[i].w, fn, dst.w);
+        }
     }
     if (c4 == 0) {
         s_m[part] = m;
