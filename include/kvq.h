@@ -84,9 +84,16 @@ typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
  *      16*(i%2) + 4*(i/2) (4-bit) or byte i (8-bit).
  *  UNIFORM meta: 16 B per token: u16 fp16 scale[4], then u16 fp16 zero[4] (K: row order,
  *      V: token order).
- *  TURBO codes: 48 B per token; group g at byte 12g: u64 of 2-bit low fields then u32 of high
- *      bits.  TURBO_QJL meta: u16 fp16 norm, u16 fp16 residual norm; QJL plane: 16 B per token,
- *      bit i at byte i/8 bit i%8.  TURBO_MSE meta: u16 fp16 norm.
+ *  TURBO planes keep the three bits of each 3-bit code in three bit planes of "half-interleaved"
+ *      u32 words: value e (0..31) of a word at bit 16*(e%2) + e/2.  Every plane holds whole
+ *      64-token blocks.
+ *  TURBO_QJL K: rows in the UNIFORM K order; 48 B per row, group g at byte 12g = words P0, P1,
+ *      P2 with value e of Pk = bit k of the code of channel 32g+e.  QJL plane: 16 B per row,
+ *      word w value e = sign bit of projection 32w+e.  Meta per row: u16 fp16 norm, u16 fp16
+ *      residual norm.
+ *  TURBO_MSE V: blocks of 32 tokens, 1536 B each; token t (tau = t%32, o = tau/8, i = tau%8),
+ *      channel d (n = d%16, N = d/16): bit k of its code is in u32 word 6*(16o + n) + 2k + N/4
+ *      of block t/32, at bit 16*(i%2) + 4*(N%4) + i/2.  Meta: u16 fp16 norm per token.
  *  Window ring: [fp32_window][128] fp32, token t at slot t % fp32_window.               */
 typedef struct {
     void *codes, *meta, *qjl, *window;

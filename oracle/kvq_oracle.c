@@ -370,10 +370,19 @@ void orc_turbo_encode(const float* x, const orc_tables* tb, int with_qjl, float*
  * 8-bit block (4096 B): 8-byte unit 8*(16*kb + n) + N, token i at byte i.
  * Meta: natural token order, 16 B per token as for K.
  *
- * Turbo (K or V): 48 B per token, natural order; group g at byte 12*g: u64 little-endian with
- * bits 2e..2e+1 = code_e & 3, then u32 with bit e = code_e >> 2 (e = 0..31).
- * Turbo-QJL meta: u16 n, u16 gamma per token; QJL plane: 16 B per token, bit i at byte i/8,
- * bit i%8.  Turbo-MSE meta: u16 n per token.
+ * Turbo planes store the 3-bit codes as three bit planes (bit k of every code) in
+ * "half-interleaved" u32 words: value e (0..31) of a word sits at bit 16*(e%2) + e/2, so the
+ * even-indexed values fill the low half and the odd-indexed values the high half.
+ * Turbo K (TURBO_QJL or TURBO_MSE): rows in the same 64-token-block order as uniform K; a row is
+ * 48 B: group g at byte 12*g holds words P0, P1, P2, where value e of Pk = bit k of the code of
+ * channel 32g + e.  QJL plane (TURBO_QJL): 16 B per row, word w holds the sign bits of
+ * projections 32w + e as values e.  Meta per row: u16 n, u16 gamma (TURBO_QJL) or u16 n
+ * (TURBO_MSE).
+ * Turbo V (TURBO_MSE): blocks of 32 tokens, 1536 B each.  Token t: tau = t%32, octet o = tau/8,
+ * i = tau%8; channel d: n = d%16, N = d/16.  Bit k of the code of (t, d) is in u32 word
+ * 6*(16*o + n) + 2*k + N/4 of block t/32, at bit 16*(i%2) + 4*(N%4) + i/2.  Meta: u16 n per
+ * token, natural order.
+ * Every turbo plane holds a whole number of 64-token blocks.
  * Window ring: [W][128] fp32, token t at slot t % W.
  */
 
@@ -383,20 +392,20 @@ static size_t k_row(int t) { return (size_t)(64 * (t / 64) + 16 * ((t % 64) % 4)
 
 size_t orc_codes_bytes(const orc_plane_cfg* pc)
 {
-    if (pc->scheme != ORC_UNIFORM) return (size_t)pc->capacity * 48;
+    if (pc->scheme != ORC_UNIFORM) return (size_t)ceil_to(pc->capacity, 64) * 48;
     return (size_t)ceil_to(pc->capacity, 64) * 16 * pc->bits;
 }
 
 size_t orc_meta_bytes(const orc_plane_cfg* pc)
 {
-    if (pc->scheme == ORC_TURBO_QJL) return (size_t)pc->capacity * 4;
-    if (pc->scheme == ORC_TURBO_MSE) return (size_t)pc->capacity * 2;
+    if (pc->scheme == ORC_TURBO_QJL) return (size_t)ceil_to(pc->capacity, 64) * 4;
+    if (pc->scheme == ORC_TURBO_MSE) return (size_t)ceil_to(pc->capacity, 64) * 2;
     return (size_t)ceil_to(pc->capacity, 64) * 16;
 }
 
 size_t orc_qjl_bytes(const orc_plane_cfg* pc)
 {
-    return pc->scheme == ORC_TURBO_QJL ? (size_t)pc->capacity * 16 : 0;
+    return pc->scheme == ORC_TURBO_QJL ? (size_t)ceil_to(pc->capacity, 64) * 16 : 0;
 }
 
 size_t orc_ring_floats(const orc_plane_cfg* pc) { return (size_t)pc->window * D; }
@@ -415,6 +424,29 @@ static void put_nibble(uint8_t* p, int bit, int code)
     p[byte] = (uint8_t)((p[byte] & ~(0xf << sh)) | ((code & 0xf) << sh));
 }
 static int get_nibble(const uint8_t* p, int bit) { return (p[bit / 8] >> (bit % 8)) & 0xf; }
+
+/* Single bits of the little-endian u32 at p. */
+static void put_bit(uint8_t* p, int bit, int v)
+{
+    int byte = bit / 8, sh = bit % 8;
+    p[byte] = (uint8_t)((p[byte] & ~(1 << sh)) | ((v & 1) << sh));
+}
+static int get_bit(const uint8_t* p, int bit) { return (p[bit / 8] >> (bit % 8)) & 1; }
+
+/* Position of value e (0..31) inside a half-interleaved u32 word. */
+static int ibit(int e) { return 16 * (e % 2) + e / 2; }
+
+/* Turbo V: byte offset of the u32 word and bit position of bit k of (token t, channel d). */
+static size_t tv_word(int t, int d, int k)
+{
+    int tau = t % 32, o = tau / 8, n = d % 16, N = d / 16;
+    return (size_t)(t / 32) * 1536 + 4 * (size_t)(6 * (16 * o + n) + 2 * k + N / 4);
+}
+static int tv_bit(int t, int d)
+{
+    int i = t % 8, N = d / 16;
+    return 16 * (i % 2) + 4 * (N % 4) + i / 2;
+}
 
 static void pack_token(const orc_plane_cfg* pc, int t, const uint8_t* code, const uint16_t* s16,
                        const uint16_t* z16, uint16_t n16, uint16_t g16, const uint8_t* bits,
@@ -455,26 +487,25 @@ static void pack_token(const orc_plane_cfg* pc, int t, const uint8_t* code, cons
         }
         return;
     }
-    uint8_t* r = codes + (size_t)t * 48;
-    for (int g = 0; g < NG; g++) {
-        uint64_t lo = 0;
-        uint32_t hi = 0;
-        for (int e = 0; e < 32; e++) {
-            int c = code[32 * g + e];
-            lo |= (uint64_t)(c & 3) << (2 * e);
-            hi |= (uint32_t)((c >> 2) & 1) << e;
-        }
-        for (int k = 0; k < 8; k++) r[12 * g + k] = (uint8_t)(lo >> (8 * k));
-        for (int k = 0; k < 4; k++) r[12 * g + 8 + k] = (uint8_t)(hi >> (8 * k));
+    if (pc->tensor == ORC_TENSOR_V) {
+        for (int d = 0; d < D; d++)
+            for (int k = 0; k < 3; k++) put_bit(codes + tv_word(t, d, k), tv_bit(t, d), code[d] >> k);
+        put_u16(meta + (size_t)t * 2, n16);
+        return;
+    }
+    size_t row = k_row(t);
+    uint8_t* r = codes + row * 48;
+    for (int j = 0; j < D; j++) {
+        int g = j / 32, e = j % 32;
+        for (int k = 0; k < 3; k++) put_bit(r + 12 * g + 4 * k, ibit(e), code[j] >> k);
     }
     if (pc->scheme == ORC_TURBO_QJL) {
-        put_u16(meta + (size_t)t * 4, n16);
-        put_u16(meta + (size_t)t * 4 + 2, g16);
-        uint8_t* q = qjl + (size_t)t * 16;
-        memset(q, 0, 16);
-        for (int i = 0; i < D; i++) q[i / 8] |= (uint8_t)(bits[i] << (i % 8));
+        put_u16(meta + row * 4, n16);
+        put_u16(meta + row * 4 + 2, g16);
+        uint8_t* q = qjl + row * 16;
+        for (int i = 0; i < D; i++) put_bit(q + 4 * (i / 32), ibit(i % 32), bits[i]);
     } else {
-        put_u16(meta + (size_t)t * 2, n16);
+        put_u16(meta + row * 2, n16);
     }
 }
 
@@ -509,23 +540,30 @@ void orc_plane_read(const orc_plane_cfg* pc, const uint8_t* codes, const uint8_t
         for (int k = 0; k < 8; k++) meta8[k] = get_u16(m + 2 * k);
         return;
     }
-    const uint8_t* r = codes + (size_t)t * 48;
-    for (int g = 0; g < NG; g++) {
-        uint64_t lo = 0;
-        uint32_t hi = 0;
-        for (int k = 0; k < 8; k++) lo |= (uint64_t)r[12 * g + k] << (8 * k);
-        for (int k = 0; k < 4; k++) hi |= (uint32_t)r[12 * g + 8 + k] << (8 * k);
-        for (int e = 0; e < 32; e++)
-            code[32 * g + e] = (uint8_t)(((lo >> (2 * e)) & 3) | (((hi >> e) & 1) << 2));
-    }
     for (int k = 0; k < 8; k++) meta8[k] = 0;
-    if (pc->scheme == ORC_TURBO_QJL) {
-        meta8[0] = get_u16(meta + (size_t)t * 4);
-        meta8[1] = get_u16(meta + (size_t)t * 4 + 2);
-        if (bits)
-            for (int i = 0; i < D; i++) bits[i] = (qjl[(size_t)t * 16 + i / 8] >> (i % 8)) & 1;
-    } else {
+    if (pc->tensor == ORC_TENSOR_V) {
+        for (int d = 0; d < D; d++) {
+            int c = 0;
+            for (int k = 0; k < 3; k++) c |= get_bit(codes + tv_word(t, d, k), tv_bit(t, d)) << k;
+            code[d] = (uint8_t)c;
+        }
         meta8[0] = get_u16(meta + (size_t)t * 2);
+        return;
+    }
+    size_t row = k_row(t);
+    const uint8_t* r = codes + row * 48;
+    for (int j = 0; j < D; j++) {
+        int g = j / 32, e = j % 32, c = 0;
+        for (int k = 0; k < 3; k++) c |= get_bit(r + 12 * g + 4 * k, ibit(e)) << k;
+        code[j] = (uint8_t)c;
+    }
+    if (pc->scheme == ORC_TURBO_QJL) {
+        meta8[0] = get_u16(meta + row * 4);
+        meta8[1] = get_u16(meta + row * 4 + 2);
+        if (bits)
+            for (int i = 0; i < D; i++) bits[i] = (uint8_t)get_bit(qjl + row * 16 + 4 * (i / 32), ibit(i % 32));
+    } else {
+        meta8[0] = get_u16(meta + row * 2);
     }
 }
 

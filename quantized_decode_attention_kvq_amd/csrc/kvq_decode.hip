@@ -66,13 +66,22 @@ __device__ __forceinline__ void load_q_pair(const DecodeParams& p, int b, int hq
     }
 }
 
-// 3-bit TurboQuant code of channel e (0..31) of group g from a 48-byte token row.
-__device__ __forceinline__ uint32_t turbo_code(const uint8_t* row, int j) {
+// 3-bit TurboQuant code of channel j from a 48-byte K row: group j/32 holds three bit-plane
+// words, value e of a word at bit 16*(e%2) + e/2.
+__device__ __forceinline__ uint32_t turbo_k_code(const uint8_t* row, int j) {
     const int g = j >> 5, e = j & 31;
     const uint32_t* w = reinterpret_cast<const uint32_t*>(row + 12 * g);
-    const uint32_t lo = w[e >> 4];
-    const uint32_t hi = w[2];
-    return ((lo >> (2 * (e & 15))) & 3u) | (((hi >> e) & 1u) << 2);
+    const int b = 16 * (e & 1) + (e >> 1);
+    return ((w[0] >> b) & 1u) | (((w[1] >> b) & 1u) << 1) | (((w[2] >> b) & 1u) << 2);
+}
+
+// 3-bit TurboQuant code of (token t, channel d) from the V plane's 32-token blocks.
+__device__ __forceinline__ uint32_t turbo_v_code(const uint8_t* codes, int t, int d) {
+    const int o = (t & 31) >> 3, i = t & 7, n = d & 15, N = d >> 4;
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(codes + (size_t)(t >> 5) * 1536) +
+                        6 * (16 * o + n) + (N >> 2);
+    const int b = 16 * (i & 1) + 4 * (N & 3) + (i >> 1);
+    return ((w[0] >> b) & 1u) | (((w[2] >> b) & 1u) << 1) | (((w[4] >> b) & 1u) << 2);
 }
 
 __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
@@ -226,26 +235,28 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
                         if (h < G) s[h] += sc * dot[h][g] + zc * qsum[h][g];
                 }
             } else { // TurboQuant key
-                const uint8_t* row = kcodes + (size_t)t * 48;
-                const uint16_t* mt = reinterpret_cast<const uint16_t*>(kmeta + (size_t)t * 4);
+                const int krow = k_row(t);
+                const uint8_t* row = kcodes + (size_t)krow * 48;
+                const uint16_t* mt = reinterpret_cast<const uint16_t*>(kmeta + (size_t)krow * 4);
                 const float nrm = h2f(mt[0]), gam = h2f(mt[1]);
                 float a1[kMaxGroupHeads], a2[kMaxGroupHeads];
 #pragma unroll
                 for (int h = 0; h < kMaxGroupHeads; ++h) a1[h] = a2[h] = 0.0f;
                 for (int j = 0; j < kDim; ++j) {
-                    const float mv = p.mu[turbo_code(row, j)];
+                    const float mv = p.mu[turbo_k_code(row, j)];
 #pragma unroll
                     for (int h = 0; h < kMaxGroupHeads; ++h)
                         if (h < G) a1[h] += mv * qp[h][j];
                 }
-                const uint32_t* qb = reinterpret_cast<const uint32_t*>(kqjl + (size_t)t * 16);
+                const uint32_t* qb = reinterpret_cast<const uint32_t*>(kqjl + (size_t)krow * 16);
                 for (int w = 0; w < 4; ++w) {
                     const uint32_t bits = qb[w];
                     for (int i = 0; i < 32; ++i)
                         if ((bits >> i) & 1u) {
+                            const int idx = 32 * w + 2 * (i & 15) + (i >> 4);
 #pragma unroll
                             for (int h = 0; h < kMaxGroupHeads; ++h)
-                                if (h < G) a2[h] += sp[h][32 * w + i];
+                                if (h < G) a2[h] += sp[h][idx];
                         }
                 }
 #pragma unroll
@@ -304,10 +315,9 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
                 v0 = zc + sc * (float)q0;
                 v1 = zc + sc * (float)q1;
             } else { // TurboQuant-MSE value (rotated domain)
-                const uint8_t* row = vcodes + (size_t)tok * 48;
                 const float nrm = h2f(reinterpret_cast<const uint16_t*>(vmeta)[tok]);
-                v0 = nrm * p.mu[turbo_code(row, d0)];
-                v1 = nrm * p.mu[turbo_code(row, d0 + 1)];
+                v0 = nrm * p.mu[turbo_v_code(vcodes, tok, d0)];
+                v1 = nrm * p.mu[turbo_v_code(vcodes, tok, d0 + 1)];
             }
 #pragma unroll
             for (int h = 0; h < kMaxGroupHeads; ++h)

@@ -65,16 +65,16 @@ PlaneGeom make_geom(const kvq_config* c, int tensor) {
     g.bits = tensor == 0 ? c->k_bits : c->v_bits;
     g.rotate = (scheme != KVQ_UNIFORM) ? 1 : (tensor == 0 ? c->rotate_k : c->rotate_v);
     g.sinkhorn = (scheme == KVQ_UNIFORM && c->sinkhorn_iters > 0) ? 1 : 0;
-    const size_t cap = (size_t)c->max_context;
+    // whole 64-token blocks for every plane: decode reads 64 tokens at a time
+    const size_t rows = ceil_to((size_t)c->max_context, 64);
     if (scheme == KVQ_UNIFORM) {
-        const size_t rows = ceil_to(cap, 64); // whole 64-token blocks: decode reads 64 at a time
         g.codes_bytes = rows * 16 * (size_t)g.bits;
         g.meta_bytes = rows * 16;
         g.qjl_bytes = 0;
     } else {
-        g.codes_bytes = cap * 48;
-        g.meta_bytes = cap * (scheme == KVQ_TURBO_QJL ? 4 : 2);
-        g.qjl_bytes = scheme == KVQ_TURBO_QJL ? cap * 16 : 0;
+        g.codes_bytes = rows * 48;
+        g.meta_bytes = rows * (scheme == KVQ_TURBO_QJL ? 4 : 2);
+        g.qjl_bytes = scheme == KVQ_TURBO_QJL ? rows * 16 : 0;
     }
     g.ring_bytes = (size_t)c->fp32_window * kDim * sizeof(float);
     size_t off = 0;

@@ -104,6 +104,16 @@ __device__ __forceinline__ uint32_t or_reduce(uint32_t v, int width) {
     return v;
 }
 
+// Half-interleave: bit e of x moves to bit 16*(e%2) + e/2 (even bits to the low half, odd bits
+// to the high half, order kept), by four swaps of bit fields.
+__device__ __forceinline__ uint32_t unshuffle32(uint32_t x) {
+    x = ((x & 0x22222222u) << 1) | ((x >> 1) & 0x22222222u) | (x & 0x99999999u);
+    x = ((x & 0x0C0C0C0Cu) << 2) | ((x >> 2) & 0x0C0C0C0Cu) | (x & 0xC3C3C3C3u);
+    x = ((x & 0x00F000F0u) << 4) | ((x >> 4) & 0x00F000F0u) | (x & 0xF00FF00Fu);
+    x = ((x & 0x0000FF00u) << 8) | ((x >> 8) & 0x0000FF00u) | (x & 0xFF0000FFu);
+    return x;
+}
+
 __device__ __forceinline__ int k_row(int t) { return 64 * (t / 64) + 16 * ((t % 64) % 4) + (t % 64) / 4; }
 
 // Uniform quantizer of the two elements a lane holds; the lane's group is lanes 16g..16g+15.
@@ -162,6 +172,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
 
     // V uniform accumulators for the group's packed words (channels 2l and 2l+1).
     uint64_t vacc0 = 0, vacc1 = 0, vmask = 0;
+    // V turbo bit-plane words of channels 2l and 2l+1 for this octet, and the bits written.
+    uint32_t tv_a[3] = {0u, 0u, 0u}, tv_c[3] = {0u, 0u, 0u}, tv_mask = 0u;
 
     for (int t = t_lo; t < t_hi; ++t) {
         const size_t elem = (((size_t)b * p.T + (t - start)) * p.Hkv + head) * kDim;
@@ -229,45 +241,86 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
             }
             const float pa = n * p.mu[qa], pc = n * p.mu[qc];
             const float ra = a - pa, rc = c - pc;
-            // pack the 3-bit codes of group g (lanes 16g..16g+15)
-            const int lg = l & 15, g = l >> 4;
-            uint32_t lo = ((qa & 3u) | ((qc & 3u) << 2)) << (4 * (lg & 7));
-            uint32_t hi = ((qa >> 2) | ((qc >> 2) << 1)) << (2 * lg);
-            lo = or_reduce(lo, 8);
-            hi = or_reduce(hi, 16);
-            uint8_t* row = codes + (size_t)t * 48 + 12 * g;
-            if (lg == 0) {
-                reinterpret_cast<uint32_t*>(row)[0] = lo;
-                reinterpret_cast<uint32_t*>(row)[2] = hi;
-            } else if (lg == 8) {
-                reinterpret_cast<uint32_t*>(row)[1] = lo;
+            if (tensor == 0) {
+                // K row: bit planes of group g (lanes 16g..16g+15 hold its channels 2lg, 2lg+1,
+                // i.e. half-interleaved values lg and 16 + lg)
+                const int lg = l & 15, g = l >> 4;
+                const int row = k_row(t);
+                uint32_t pw[3];
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    pw[k] = or_reduce((((qa >> k) & 1u) << lg) | (((qc >> k) & 1u) << (16 + lg)), 16);
+                if (lg == 0) {
+                    uint32_t* w = reinterpret_cast<uint32_t*>(codes + (size_t)row * 48 + 12 * g);
+                    w[0] = pw[0];
+                    w[1] = pw[1];
+                    w[2] = pw[2];
+                }
+                if (G.scheme == kTurboQjl) {
+                    const uint16_t g16 = f16_rn(sqrtf(tree_sum_sq(ra, rc)));
+                    rbuf[wave][2 * l] = ra;
+                    rbuf[wave][2 * l + 1] = rc;
+                    __builtin_amdgcn_wave_barrier();
+                    float acc0 = 0.0f, acc1 = 0.0f;
+                    for (int j = 0; j < kDim; ++j) {
+                        const float rj = rbuf[wave][j];
+                        acc0 = fmaf(p.qjl_st[j * kDim + l], rj, acc0);
+                        acc1 = fmaf(p.qjl_st[j * kDim + 64 + l], rj, acc1);
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                    const uint64_t b0 = __ballot(acc0 >= 0.0f);
+                    const uint64_t b1 = __ballot(acc1 >= 0.0f);
+                    if (l == 0) {
+                        uint32_t* qj = reinterpret_cast<uint32_t*>(slot + G.qjl_off + (size_t)row * 16);
+                        qj[0] = unshuffle32((uint32_t)b0);
+                        qj[1] = unshuffle32((uint32_t)(b0 >> 32));
+                        qj[2] = unshuffle32((uint32_t)b1);
+                        qj[3] = unshuffle32((uint32_t)(b1 >> 32));
+                        uint16_t* m = reinterpret_cast<uint16_t*>(meta + (size_t)row * 4);
+                        m[0] = n16;
+                        m[1] = g16;
+                    }
+                } else if (l == 0) {
+                    reinterpret_cast<uint16_t*>(meta)[row] = n16;
+                }
+            } else {
+                // V block: bit k of channel 2l (2l+1) goes to word 6(16 o + n) + 2k + N/4 with
+                // n = 2(l%8) (+1), N = l/8; token i of the octet at bit 16(i%2) + 4(N%4) + i/2
+                const int i = t % 8, N = l >> 3;
+                const uint32_t pos = 1u << (16 * (i & 1) + 4 * (N & 3) + (i >> 1));
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    tv_a[k] |= ((qa >> k) & 1u) ? pos : 0u;
+                    tv_c[k] |= ((qc >> k) & 1u) ? pos : 0u;
+                }
+                tv_mask |= pos;
+                if (l == 0) reinterpret_cast<uint16_t*>(meta)[t] = n16;
             }
-            if (G.scheme == kTurboQjl) {
-                const uint16_t g16 = f16_rn(sqrtf(tree_sum_sq(ra, rc)));
-                rbuf[wave][2 * l] = ra;
-                rbuf[wave][2 * l + 1] = rc;
-                __builtin_amdgcn_wave_barrier();
-                float acc0 = 0.0f, acc1 = 0.0f;
-                for (int j = 0; j < kDim; ++j) {
-                    const float rj = rbuf[wave][j];
-                    acc0 = fmaf(p.qjl_st[j * kDim + l], rj, acc0);
-                    acc1 = fmaf(p.qjl_st[j * kDim + 64 + l], rj, acc1);
-                }
-                __builtin_amdgcn_wave_barrier();
-                const uint64_t b0 = __ballot(acc0 >= 0.0f);
-                const uint64_t b1 = __ballot(acc1 >= 0.0f);
-                if (l == 0) {
-                    uint32_t* qj = reinterpret_cast<uint32_t*>(slot + G.qjl_off + (size_t)t * 16);
-                    qj[0] = (uint32_t)b0;
-                    qj[1] = (uint32_t)(b0 >> 32);
-                    qj[2] = (uint32_t)b1;
-                    qj[3] = (uint32_t)(b1 >> 32);
-                    uint16_t* m = reinterpret_cast<uint16_t*>(meta + (size_t)t * 4);
-                    m[0] = n16;
-                    m[1] = g16;
-                }
-            } else if (l == 0) {
-                reinterpret_cast<uint16_t*>(meta)[t] = n16;
+        }
+    }
+
+    if (tensor == 1 && G.scheme != kUniform) {
+        // merge the four lanes (l ^ 8, l ^ 16) whose channels share each word, then
+        // read-modify-write this octet's words
+        uint32_t m = tv_mask;
+        m |= (uint32_t)__shfl_xor((int)m, 8);
+        m |= (uint32_t)__shfl_xor((int)m, 16);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            tv_a[k] |= (uint32_t)__shfl_xor((int)tv_a[k], 8);
+            tv_a[k] |= (uint32_t)__shfl_xor((int)tv_a[k], 16);
+            tv_c[k] |= (uint32_t)__shfl_xor((int)tv_c[k], 8);
+            tv_c[k] |= (uint32_t)__shfl_xor((int)tv_c[k], 16);
+        }
+        if (((l >> 3) & 3) == 0) {
+            const int o = (t_lo % 32) / 8, n0 = 2 * (l & 7), N = l >> 3;
+            uint32_t* blk = reinterpret_cast<uint32_t*>(codes + (size_t)(t_lo / 32) * 1536);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                uint32_t* wa = blk + 6 * (16 * o + n0) + 2 * k + (N >> 2);
+                uint32_t* wc = wa + 6;
+                *wa = (*wa & ~m) | tv_a[k];
+                *wc = (*wc & ~m) | tv_c[k];
             }
         }
     }

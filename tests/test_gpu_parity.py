@@ -80,11 +80,12 @@ def test_progressive_3970_full():
     _decode_and_compare(case, 0, planes)
 
 
-def test_prefill_equals_appends_bytewise():
-    wl = W.LLAMA3B_3970_PROGRESSIVE
+@pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_TURBO, W.LLAMA3B_32K_TURBO_ASYM],
+                         ids=lambda w: w.name)
+def test_prefill_equals_appends_bytewise(wl):
     _say("case: prefill == appends,", wl.name, "n=300")
-    a = Case(wl, 300)
-    b = Case(wl, 300)
+    a = Case(wl, 300, layers=[0])
+    b = Case(wl, 300, layers=[0])
     a.prefill(0, chunks=[1, 63, 100, 7, 129])
     b.append_all(0)
     torch.cuda.synchronize()

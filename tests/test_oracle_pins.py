@@ -250,6 +250,36 @@ def test_layout_golden_words():
     assert (_word(pv.codes, w) >> bit) & 0xF == 7
 
 
+def test_layout_golden_turbo_bits():
+    # Bit positions of turbo codes and QJL signs against hand-derived word/bit numbers; the codes
+    # themselves come from turbo_encode, which is pinned separately.
+    g = _golden("layout_words.txt")
+    rng = np.random.default_rng(71)
+    S = rng.standard_normal((128, 128)).astype(np.float32)
+    _, mu, theta, _ = oracle.lloyd_max()
+    tb = oracle.TableSet(signs=_signs(3), S=S, mu=mu, theta=theta)
+    X = rng.standard_normal((48, 128)).astype(np.float32)
+    pk = oracle.Plane(oracle.TURBO_QJL, 3, True, False, 0, oracle.TENSOR_K, 64)
+    pk.append(X, tb)
+    enc = oracle.turbo_encode(X[5], tb, True)
+    row = int(g["k_row_of_t5"])
+    rb = pk.codes[48 * row:48 * row + 48]
+    qb = pk.qjl[16 * row:16 * row + 16]
+    for k in range(3):
+        w33 = _word(rb, int(g["tk_ch33_word0"]) + k)
+        assert (w33 >> int(g["tk_ch33_bit"])) & 1 == (enc["codes"][33] >> k) & 1
+        assert (_word(rb, k) >> int(g["tk_ch2_bit"])) & 1 == (enc["codes"][2] >> k) & 1
+    assert (_word(qb, int(g["qjl_idx70_word"])) >> int(g["qjl_idx70_bit"])) & 1 == enc["bits"][70]
+    pv = oracle.Plane(oracle.TURBO_MSE, 3, True, False, 0, oracle.TENSOR_V, 64)
+    pv.append(X, tb)
+    for t, d, key in ((41, 37, "tv_t41_d37"), (3, 100, "tv_t3_d100")):
+        ev = oracle.turbo_encode(X[t], tb, False)
+        blk = pv.codes[1536 * (t // 32):1536 * (t // 32 + 1)]
+        for k in range(3):
+            w = _word(blk, int(g[key + "_word0"]) + 2 * k)
+            assert (w >> int(g[key + "_bit"])) & 1 == (ev["codes"][d] >> k) & 1, (t, d, k)
+
+
 @pytest.mark.parametrize("scheme,bits,tensor", [
     (oracle.UNIFORM, 4, oracle.TENSOR_K), (oracle.UNIFORM, 4, oracle.TENSOR_V),
     (oracle.UNIFORM, 8, oracle.TENSOR_K), (oracle.UNIFORM, 8, oracle.TENSOR_V),
