@@ -1,26 +1,33 @@
-// Matrix-core (MFMA) split-K decode attention over uniform 4/8-bit caches, gfx950.
+// Matrix-core (MFMA) split-K decode attention over the compressed cache, gfx950.
 //
-// What it computes (pages by title and section): the quantcpp article's progressive cache
-// (4-bit codes with fp16 scale/zero per 32 channels, newest 128 tokens read in FP32) and the
-// KVarN post's Walsh-Hadamard + Sinkhorn-balanced 4-bit cache: out = softmax(q k^T * scale) v,
-// with k, v the dequantized tokens, scores in the rotated/balanced domain via q' = R(q) .* c and
-// the output un-rotated at the end: R^-1(c .* sum_t p_t yhat_t).
+// What it computes (pages by title and section):
+//  * the quantcpp article's progressive cache (4-bit codes with fp16 scale/zero per 32 channels,
+//    newest 128 tokens read in FP32) and the KVarN post's Walsh-Hadamard + Sinkhorn-balanced
+//    4-bit cache: out = softmax(q k^T * scale) v with k, v the dequantized tokens, scores in the
+//    rotated/balanced domain via q' = R(q) .* c, output un-rotated at the end (merge kernel);
+//  * the TurboQuant row of "LLM memory saving ... 2026": a key scores
+//    n <R q, mu[code]> + gamma * sqrt(pi/2)/128 * sum_i (2 b_i - 1) (S R q)_i, a TurboQuant-MSE
+//    value is n mu[code] in the rotated domain.
 //
 // How (one workgroup = NW waves per (sequence, kv head, token split); each wave streams 64-token
-// chunks):
-//  * Scores: v_mfma_f32_16x16x32_f16 with A = the G query rows split into fp16 hi + lo parts and
-//    laid out as (head, group) rows, B = the raw 4-bit / 8-bit codes.  4-bit codes enter the
-//    B operand as fp16 subnormal bit patterns (code * 2^-24, or 16 * code * 2^-24 for the odd
-//    nibbles, compensated in A), 8-bit codes as zero-extended bytes (code * 2^-24): no
-//    int->float conversion, and products are exact.  The per-group fp16 scale and zero fold in
-//    afterwards: s_t = sum_g scale_g,t * dot_g + zero_g,t * sum_{j in g} q'_j.
+// chunks; all products on v_mfma_f32_16x16x32_f16, every code operand exact):
+//  * Uniform K: A = (head, group) rows of q' as fp16 hi + scaled lo, B = raw codes: 4-bit codes as fp16
+//    subnormal bit patterns (code * 2^-24, odd nibbles x16 compensated in A), 8-bit codes as
+//    zero-extended bytes.  The fp16 scale and zero fold in afterwards:
+//    s_t = sum_g scale_g,t dot_g + zero_g,t sum_{j in g} q'_j.
+//  * TurboQuant K: the 8 Lloyd-Max centroids are odd-symmetric, so with code bits c0, c1, c2 and
+//    b = 2c - 1, mu[code] = a0 b0 + a1 b1 + a2 b2 + a3 b0 b1 b2, and b0 b1 b2 = 2 (c0^c1^c2) - 1.
+//    <q', mu[code]> is then four dot products of q' with 0/1 bit planes (plus a constant), and
+//    the QJL term a fifth.  A bit plane enters B as a masked word (bit * 2^(k-24) for a bit at
+//    position k < 10, compensated in A); A rows are (head; q' hi, q' lo, Sq' hi, Sq' lo).
 //  * Online softmax in the log2 domain (q' carries softmax_scale * log2(e) and a per-head power
 //    of two that keeps 16 q' inside fp16 range).
-//  * PV: A = p * scale_g (fp16 hi + lo) staged through LDS into matrix-operand order, B = raw V
-//    codes from the token-blocked V plane (dense over tokens), plus a vector-ALU sum of
-//    p * zero_g.
-//  * Each split writes one partial (running max, sum, acc[128]) per query head; the separate
-//    merge kernel combines them in a fixed order and applies c_V and R_V^-1.
+//  * PV: A = p * (scale_g | -n * a_p) as fp16 hi (rows 0-7) + scaled lo (rows 8-15), staged
+//    through LDS in operand order; B = centred V codes c - 8 (c - 128) as exact fp16 integers,
+//    or the TurboQuant-MSE bit planes as -+1, plus a vector-ALU sum of p (zero + 8 scale).
+//    Centring keeps every accumulator of the order of the output itself.
+//  * Each split writes one partial (running max, sum, acc[128]) per query head; the merge
+//    kernel combines them in a fixed order and applies c_V and R_V^-1.
 //  * The FP32 window (progressive mode) is one extra split computed on the vector ALU.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
@@ -37,8 +44,16 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kPRow = 72;                       // halves per staged P row: 64 tokens + 8 pad
-constexpr int kPWave = 4 * 2 * 8 * kPRow;       // halves per wave: [group][hi/lo][row][token]
+constexpr int kPRow = 72;                 // halves per staged P row: 64 tokens + 8 pad
+constexpr int kPWave = 4 * 16 * kPRow;    // halves per wave: [group | plane][16 rows][token]
+constexpr float kKappa = 0.0097915166977774f; // sqrt(pi/2) / 128
+// An operand x goes in as fp16 hi = fp16(x) plus lo = fp16((x - hi) * 2^11): the scaled low part
+// stays a normal fp16 number whenever hi is, so the pair keeps about 22 significant bits; the
+// products of the lo parts are scaled back by 2^-11.
+constexpr float kLoScale = 2048.0f, kLoInv = 1.0f / 2048.0f;
+
+// cache kinds (template parameters)
+constexpr int kU4 = 0, kU8 = 1, kTb = 2; // uniform 4-bit, uniform 8-bit, TurboQuant 3-bit
 
 __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -68,6 +83,56 @@ __device__ __forceinline__ u4 unpack8(uint32_t x0, uint32_t x1) {
     r.y = __builtin_amdgcn_perm(0u, x0, 0x0c030c02u);
     r.z = __builtin_amdgcn_perm(0u, x1, 0x0c010c00u);
     r.w = __builtin_amdgcn_perm(0u, x1, 0x0c030c02u);
+    return r;
+}
+
+// Eight one-bit operands from a half-interleaved word: quarter q (0..3) of each half, i.e. bits
+// 4q + v and 16 + 4q + v (v = 0..3).  Operand 2v + h is that bit times 2^(4(q%2) + v - 24).
+__device__ __forceinline__ u4 bits8(uint32_t w, int q) {
+    const uint32_t x = (q & 2) ? (w >> 8) : w;
+    const uint32_t m = 0x00010001u << (4 * (q & 1));
+    u4 r;
+    r.x = x & m;
+    r.y = x & (m << 1);
+    r.z = x & (m << 2);
+    r.w = x & (m << 3);
+    return r;
+}
+
+// V operands are centred so that no large one-signed sum has to cancel against the zero-point
+// term: a code c enters as the exact fp16 integer c - 8 (4-bit) or c - 128 (8-bit), made by
+// placing c in the mantissa of 1024 (bit pattern 0x6400 | c) and subtracting 1024 + 8 (or the
+// x16 slots' 1024 + 128, or 1024 + 128 for 8-bit codes) with one packed fp16 add.
+__device__ __forceinline__ uint32_t h2sub(uint32_t x, _Float16 c) {
+    const h2v r = __builtin_bit_cast(h2v, x) - h2v{c, c};
+    return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ u4 centred4(uint32_t x) {
+    u4 r;
+    r.x = h2sub((x & 0x000F000Fu) | 0x64006400u, (_Float16)1032.0f);
+    r.y = h2sub((x & 0x00F000F0u) | 0x64006400u, (_Float16)1152.0f);
+    const uint32_t y = x >> 8;
+    r.z = h2sub((y & 0x000F000Fu) | 0x64006400u, (_Float16)1032.0f);
+    r.w = h2sub((y & 0x00F000F0u) | 0x64006400u, (_Float16)1152.0f);
+    return r;
+}
+__device__ __forceinline__ u4 centred8(uint32_t x0, uint32_t x1) {
+    const u4 b = unpack8(x0, x1);
+    u4 r;
+    r.x = h2sub(b.x | 0x64006400u, (_Float16)1152.0f);
+    r.y = h2sub(b.y | 0x64006400u, (_Float16)1152.0f);
+    r.z = h2sub(b.z | 0x64006400u, (_Float16)1152.0f);
+    r.w = h2sub(b.w | 0x64006400u, (_Float16)1152.0f);
+    return r;
+}
+// TurboQuant-MSE V bits as fp16 -1 (bit set) / +1 (bit clear), quarter q of a half-interleaved
+// word: operand 2v + h comes from bit 16h + 4q + v.
+__device__ __forceinline__ u4 pm1x8(uint32_t w, int q) {
+    u4 r;
+    r.x = ((w << (15 - 4 * q)) & 0x80008000u) | 0x3C003C00u;
+    r.y = ((w << (14 - 4 * q)) & 0x80008000u) | 0x3C003C00u;
+    r.z = ((w << (13 - 4 * q)) & 0x80008000u) | 0x3C003C00u;
+    r.w = ((w << (12 - 4 * q)) & 0x80008000u) | 0x3C003C00u;
     return r;
 }
 
@@ -119,44 +184,41 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// Loads of one 64-token chunk, split so that the next chunk's K can be requested as soon as the
-// scores are done and its V as soon as PV is done.  Per lane: K codes and meta of rows
-// 16j + (lane % 16) of the 64-token block; V codes of the two 32-token blocks (32 * VB / 4 bytes
-// at lane * 32 * VB / 4); V meta of tokens 4 * (lane % 16) + 0..3.
-template <int KB>
+// Per-lane registers of one 64-token chunk.  K: sub-tile j = rows 16j + (lane % 16) of the
+// 64-token block (tokens 4 (lane % 16) + j).  Uniform: the lane's quarter of the code row and the
+// row's 16-byte meta.  TurboQuant: the three plane words of group lane / 16, QJL word lane / 16,
+// and (n, gamma).  V: uniform = 32*VB/4 bytes of each 32-token block at lane * 32*VB/4 plus the
+// 16-byte meta of tokens 4 (lane % 16) + 0..3; TurboQuant-MSE = the lane's six words of each
+// 32-token block plus the norms of tokens 4 (lane % 16) + 0..3.
+template <int KT>
 struct KRegs {
+    static constexpr int KB = KT == kU4 ? 4 : 8;
     u4 kc[4][KB / 4], km[4];
 };
-template <int VB>
+template <>
+struct KRegs<kTb> {
+    uint32_t pw[4][3], qw[4], nm[4];
+};
+template <int VT>
 struct VRegs {
+    static constexpr int VB = VT == kU4 ? 4 : 8;
     u4 vc[2][VB / 2], vm[4];
 };
+template <>
+struct VRegs<kTb> {
+    uint2 w[2][3];
+    uint2 nm;
+};
 
-template <int KB>
-__device__ __forceinline__ void load_k(KRegs<KB>& r, const uint8_t* kc, const uint8_t* km) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int u = 0; u < KB / 4; ++u)
-            r.kc[j][u] = *reinterpret_cast<const u4*>(kc + j * 16 * 16 * KB + 16 * u);
-        r.km[j] = *reinterpret_cast<const u4*>(km + j * 16 * 16);
-    }
-}
-template <int VB>
-__device__ __forceinline__ void load_v(VRegs<VB>& r, const uint8_t* vc, const uint8_t* vm) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-#pragma unroll
-        for (int u = 0; u < VB / 2; ++u) r.vc[k][u] = *reinterpret_cast<const u4*>(vc + k * 512 * VB + 16 * u);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r.vm[j] = *reinterpret_cast<const u4*>(vm + 16 * j);
-}
-
-template <int KB, int VB, int MB, int kNW>
+template <int KT, int VT, int MB, int kNW>
 __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
+    constexpr bool KU = KT != kTb, VU = VT != kTb;
+    constexpr int KB = KT == kU4 ? 4 : 8, VB = VT == kU4 ? 4 : 8;
     __shared__ float s_q[kMaxGroupHeads][kDim];   // q' in the rotated/balanced domain, scaled
     __shared__ float s_qw[kMaxGroupHeads][kDim];  // plain q * scale * log2e (FP32 window)
+    __shared__ float s_sp[KU ? 1 : kMaxGroupHeads][kDim]; // S q' (TurboQuant K)
     __shared__ float s_qsum[kMaxGroupHeads][4];
+    __shared__ float s_spsum[kMaxGroupHeads];
     __shared__ float s_qfac[kMaxGroupHeads];
     __shared__ __align__(16) _Float16 s_p[kNW * kPWave];
     __shared__ float s_wm[kNW][kMaxGroupHeads], s_wl[kNW][kMaxGroupHeads];
@@ -173,12 +235,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     const char* slot = p.layer_base + (size_t)b * p.seq_stride + (size_t)kvh * p.head_stride;
     const uint8_t* kcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.codes_off);
     const uint8_t* kmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.meta_off);
+    const uint8_t* kqjl = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.qjl_off);
     const float* kring = reinterpret_cast<const float*>(slot + p.plane_off[0] + KG.ring_off);
     const uint8_t* vcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.codes_off);
     const uint8_t* vmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.meta_off);
     const float* vring = reinterpret_cast<const float*>(slot + p.plane_off[1] + VG.ring_off);
     const float UK = (KB == 4) ? 1048576.0f : 16777216.0f; // 2^20 / 2^24: unit of a code product
-    const float UV = (VB == 4) ? 1048576.0f : 16777216.0f;
+    const float UV = (VB == 4) ? 0.0625f : 1.0f; // 4-bit: half the weights carry x16
 
     // ---------------- the query-side loads go out first (they are small and the preparation
     // waits on them), then this wave's first chunk, so the memory pipe starts immediately
@@ -207,20 +270,56 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     const int tok_begin = split * p.split_tokens;
     const int tok_end = wsplit ? tok_begin : min(nq, tok_begin + p.split_tokens);
     const int nch = (tok_end > tok_begin) ? (tok_end - tok_begin + 63) / 64 : 0;
-    // chunk ci of this split starts at token tok_begin + 64 ci; a lane's addresses in it:
-    auto kc_at = [&](int ci) { return kcodes + ((size_t)tok_begin + 64 * ci + lr) * (16 * KB) + (16 * KB / 4) * lq; };
-    auto km_at = [&](int ci) { return kmeta + ((size_t)tok_begin + 64 * ci + lr) * 16; };
-    auto vc_at = [&](int ci) {
-        return vcodes + (size_t)((tok_begin + 64 * ci) / 32) * (512 * VB) + (size_t)(32 * VB / 4) * l;
+
+    KRegs<KT> kr;
+    VRegs<VT> vr;
+    auto load_k = [&](int ci) {
+        const size_t r0 = (size_t)tok_begin + 64 * ci + lr; // row of sub-tile 0
+        if constexpr (KU) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint8_t* c = kcodes + (r0 + 16 * j) * (16 * KB) + (16 * KB / 4) * lq;
+#pragma unroll
+                for (int u = 0; u < KB / 4; ++u) kr.kc[j][u] = *reinterpret_cast<const u4*>(c + 16 * u);
+                kr.km[j] = *reinterpret_cast<const u4*>(kmeta + (r0 + 16 * j) * 16);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t* c = reinterpret_cast<const uint32_t*>(kcodes + (r0 + 16 * j) * 48 + 12 * lq);
+                kr.pw[j][0] = c[0];
+                kr.pw[j][1] = c[1];
+                kr.pw[j][2] = c[2];
+                kr.qw[j] = *reinterpret_cast<const uint32_t*>(kqjl + (r0 + 16 * j) * 16 + 4 * lq);
+                kr.nm[j] = *reinterpret_cast<const uint32_t*>(kmeta + (r0 + 16 * j) * 4);
+            }
+        }
     };
-    auto vm_at = [&](int ci) { return vmeta + ((size_t)tok_begin + 64 * ci + 4 * lr) * 16; };
+    auto load_v = [&](int ci) {
+        const size_t t0 = (size_t)tok_begin + 64 * ci;
+        if constexpr (VU) {
+            const uint8_t* c = vcodes + (t0 / 32) * (512 * VB) + (size_t)(32 * VB / 4) * l;
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int u = 0; u < VB / 2; ++u)
+                    vr.vc[k][u] = *reinterpret_cast<const u4*>(c + k * 512 * VB + 16 * u);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vr.vm[j] = *reinterpret_cast<const u4*>(vmeta + (t0 + 4 * lr + j) * 16);
+        } else {
+            const uint8_t* c = vcodes + (t0 / 32) * 1536 + 24 * l;
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int u = 0; u < 3; ++u) vr.w[k][u] = *reinterpret_cast<const uint2*>(c + k * 1536 + 8 * u);
+            vr.nm = *reinterpret_cast<const uint2*>(vmeta + (t0 + 4 * lr) * 2);
+        }
+    };
     // The wave's first chunk is requested right away; each later chunk is requested as soon as
     // the registers it goes into have been consumed (K after the scores, V after PV).
-    KRegs<KB> kr;
-    VRegs<VB> vr;
     if (wave < nch) {
-        load_k(kr, kc_at(wave), km_at(wave));
-        load_v(vr, vc_at(wave), vm_at(wave));
+        load_k(wave);
+        load_v(wave);
     }
 
     // ---------------- query preparation (once per workgroup) ----------------
@@ -259,6 +358,35 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
         if (l == 0) s_qfac[h] = ldexpf(1.0f, -e);
     }
     __syncthreads();
+    if constexpr (!KU) {
+        // S q' for the QJL term (S^T is stored [j][i]), then its sum per head
+        if (!wsplit) {
+            for (int idx = tid; idx < G * kDim; idx += kNW * 64) {
+                const int h = idx >> 7, i = idx & 127;
+                float s = 0.0f;
+#pragma unroll 8
+                for (int j = 0; j < kDim; ++j) s = fmaf(p.qjl_st[j * kDim + i], s_q[h][j], s);
+                s_sp[h][i] = s;
+            }
+        }
+        __syncthreads();
+        for (int h = wave; h < G; h += kNW) {
+            const float v = wave_sum(s_sp[h][2 * l] + s_sp[h][2 * l + 1]);
+            if (l == 0) s_spsum[h] = v;
+        }
+        __syncthreads();
+    }
+
+    // TurboQuant centroids as odd bit functions: mu[c] = a0 b0 + a1 b1 + a2 b2 + a3 b0 b1 b2
+    float al[4] = {0.0f, 0.0f, 0.0f, 0.0f}, asum = 0.0f;
+    if constexpr (!KU || !VU) {
+        const float m4 = p.mu[4], m5 = p.mu[5], m6 = p.mu[6], m7 = p.mu[7];
+        al[0] = 0.25f * ((m5 - m4) + (m7 - m6));
+        al[1] = 0.25f * ((m6 - m4) + (m7 - m5));
+        al[2] = 0.25f * ((m4 + m5) + (m6 + m7));
+        al[3] = 0.25f * ((m4 - m5) + (m7 - m6));
+        asum = (al[0] + al[1]) + (al[2] + al[3]);
+    }
 
     // per-wave softmax state, in the score layout (lane: head 4*mb + lq, column lr)
     float m_run[MB], l_run[MB], z_run[MB][4];
@@ -269,6 +397,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) z_run[mb][g] = 0.0f;
     }
+    // PV accumulators: tile N = channels 16N..16N+15; rows 4*lq + v: lq 0,1 = fp16-hi part of
+    // heads 4*lq + v, lq 2,3 = fp16-lo part of heads 4*(lq-2) + v
     f4 acc[8];
 #pragma unroll
     for (int N = 0; N < 8; ++N) acc[N] = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -284,78 +414,138 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     _Float16* my_p = s_p + wave * kPWave;
 
     if (!wsplit) {
-        // ---------------- A operands: (head, group) rows of q' split into fp16 hi + lo -------
-        h8 Ahi[MB][4], Alo[MB][4];
-        float qs_l[MB][4], F[MB];
+        // ---------------- A operands ----------------
+        // uniform K: Ahi/Alo[mb][g] = (head, group) rows of q' (fp16 hi / lo), zero outside g.
+        // TurboQuant K: At[mb][s] rows (head 4mb + lr/4; q' hi, q' lo, Sq' hi, Sq' lo), k-slice s
+        // = channels 32*lq + 8s + 0..7, pre-scaled by 2^-(4(s%2) + i/2) for the bit operands.
+        constexpr int NA = KU ? 4 : 1;
+        h8 Ahi[MB][NA], Alo[MB][NA], At[MB][KU ? 1 : 4];
+        float qs_l[MB][4], F[MB], cQ[MB], cS[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const int h = 4 * mb + (lr >> 2), gq = lr & 3;
-            const int hc = min(h, G - 1);
-            h8 hi, lo;
+            const int hs = min(4 * mb + lq, G - 1); // score-layout head of this lane
+            if constexpr (KU) {
+                const int h = 4 * mb + (lr >> 2), gq = lr & 3;
+                const int hc = min(h, G - 1);
+                h8 hi, lo;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float w = (KB == 4 && (i == 0 || i == 1 || i == 4 || i == 5)) ? 16.0f : 1.0f;
-                const float x = (h < G) ? s_q[hc][32 * gq + 8 * lq + i] * w : 0.0f;
-                const _Float16 xh = (_Float16)x;
-                hi[i] = xh;
-                lo[i] = (_Float16)(x - (float)xh);
+                for (int i = 0; i < 8; ++i) {
+                    const float w = (KB == 4 && (i == 0 || i == 1 || i == 4 || i == 5)) ? 16.0f : 1.0f;
+                    const float x = (h < G) ? s_q[hc][32 * gq + 8 * lq + i] * w : 0.0f;
+                    const _Float16 xh = (_Float16)x;
+                    hi[i] = xh;
+                    lo[i] = (_Float16)((x - (float)xh) * kLoScale);
+                }
+                const h8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    Ahi[mb][g] = (g == gq) ? hi : zero;
+                    Alo[mb][g] = (g == gq) ? lo : zero;
+                }
+#pragma unroll
+                for (int g = 0; g < 4; ++g) qs_l[mb][g] = s_qsum[hs][g] * (1.0f / UK);
+                F[mb] = UK * s_qfac[hs];
+            } else {
+                const int h = 4 * mb + (lr >> 2), v = lr & 3;
+                const int hc = min(h, G - 1);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    h8 a;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int c = 32 * lq + 8 * s + i;
+                        const float sc = __uint_as_float((uint32_t)(127 - 4 * (s & 1) - (i >> 1)) << 23);
+                        const float x = (h < G) ? ((v < 2) ? s_q[hc][c] : s_sp[hc][c]) * sc : 0.0f;
+                        const _Float16 xh = (_Float16)x;
+                        a[i] = (v & 1) ? (_Float16)((x - (float)xh) * kLoScale) : xh;
+                    }
+                    At[mb][s] = a;
+                }
+                const float qtot = (s_qsum[hs][0] + s_qsum[hs][1]) + (s_qsum[hs][2] + s_qsum[hs][3]);
+                cQ[mb] = asum * qtot * 5.9604644775390625e-8f; // 2^-24
+                cS[mb] = s_spsum[hs] * 5.9604644775390625e-8f;
+                F[mb] = 16777216.0f * s_qfac[hs];
             }
-            const h8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                Ahi[mb][g] = (g == gq) ? hi : zero;
-                Alo[mb][g] = (g == gq) ? lo : zero;
-            }
-            const int hs = min(4 * mb + lq, G - 1);
-#pragma unroll
-            for (int g = 0; g < 4; ++g) qs_l[mb][g] = s_qsum[hs][g] * (1.0f / UK);
-            F[mb] = UK * s_qfac[hs];
         }
 
         for (int ci = wave; ci < nch; ci += kNW) {
             const int c0 = tok_begin + 64 * ci;
             const int nci = ci + kNW; // the chunk the registers are refilled with
             const bool more = nci < nch;
-            const auto& kc = kr.kc;
-            const auto& km = kr.km;
-            const auto& vc = vr.vc;
-            const auto& vm = vr.vm;
 
             // ---- scores
             float raw[MB][4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                h8 B[4];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    if (KB == 4)
-                        B[g] = as_h8(unpack4(kc[j][0][g]));
-                    else
-                        B[g] = as_h8(unpack8(kc[j][g >> 1][2 * (g & 1)], kc[j][g >> 1][2 * (g & 1) + 1]));
-                }
                 const bool valid = (c0 + 4 * lr + j) < tok_end;
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    f4 D = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (KU) {
+                    const auto& kc = kr.kc;
+                    const auto& km = kr.km;
+                    h8 B[4];
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        D = mfma16(Ahi[mb][g], B[g], D);
-                        D = mfma16(Alo[mb][g], B[g], D);
+                        if (KB == 4)
+                            B[g] = as_h8(unpack4(kc[j][0][g]));
+                        else
+                            B[g] = as_h8(unpack8(kc[j][g >> 1][2 * (g & 1)], kc[j][g >> 1][2 * (g & 1) + 1]));
                     }
-                    float r = lo_h(km[j].x) * D[0];
-                    r = fmaf(hi_h(km[j].x), D[1], r);
-                    r = fmaf(lo_h(km[j].y), D[2], r);
-                    r = fmaf(hi_h(km[j].y), D[3], r);
-                    r = fmaf(lo_h(km[j].z), qs_l[mb][0], r);
-                    r = fmaf(hi_h(km[j].z), qs_l[mb][1], r);
-                    r = fmaf(lo_h(km[j].w), qs_l[mb][2], r);
-                    r = fmaf(hi_h(km[j].w), qs_l[mb][3], r);
-                    raw[mb][j] = valid ? r : kNegInf;
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        f4 D = {0.0f, 0.0f, 0.0f, 0.0f}, E = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            D = mfma16(Ahi[mb][g], B[g], D);
+                            E = mfma16(Alo[mb][g], B[g], E);
+                        }
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) D[v] = fmaf(E[v], kLoInv, D[v]);
+                        float r = lo_h(km[j].x) * D[0];
+                        r = fmaf(hi_h(km[j].x), D[1], r);
+                        r = fmaf(lo_h(km[j].y), D[2], r);
+                        r = fmaf(hi_h(km[j].y), D[3], r);
+                        r = fmaf(lo_h(km[j].z), qs_l[mb][0], r);
+                        r = fmaf(hi_h(km[j].z), qs_l[mb][1], r);
+                        r = fmaf(lo_h(km[j].w), qs_l[mb][2], r);
+                        r = fmaf(hi_h(km[j].w), qs_l[mb][3], r);
+                        raw[mb][j] = valid ? r : kNegInf;
+                    }
+                } else {
+                    const uint32_t P0 = kr.pw[j][0], P1 = kr.pw[j][1], P2 = kr.pw[j][2];
+                    const uint32_t X = P0 ^ P1 ^ P2, Q = kr.qw[j];
+                    f4 D[MB][5];
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int k = 0; k < 5; ++k) D[mb][k] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const h8 B0 = as_h8(bits8(P0, s)), B1 = as_h8(bits8(P1, s)), B2 = as_h8(bits8(P2, s));
+                        const h8 B3 = as_h8(bits8(X, s)), BQ = as_h8(bits8(Q, s));
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) {
+                            D[mb][0] = mfma16(At[mb][s], B0, D[mb][0]);
+                            D[mb][1] = mfma16(At[mb][s], B1, D[mb][1]);
+                            D[mb][2] = mfma16(At[mb][s], B2, D[mb][2]);
+                            D[mb][3] = mfma16(At[mb][s], B3, D[mb][3]);
+                            D[mb][4] = mfma16(At[mb][s], BQ, D[mb][4]);
+                        }
+                    }
+                    const float nrm = lo_h(kr.nm[j]), gam = hi_h(kr.nm[j]);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        float mse = al[0] * fmaf(D[mb][0][1], kLoInv, D[mb][0][0]);
+                        mse = fmaf(al[1], fmaf(D[mb][1][1], kLoInv, D[mb][1][0]), mse);
+                        mse = fmaf(al[2], fmaf(D[mb][2][1], kLoInv, D[mb][2][0]), mse);
+                        mse = fmaf(al[3], fmaf(D[mb][3][1], kLoInv, D[mb][3][0]), mse);
+                        const float qj = fmaf(D[mb][4][3], kLoInv, D[mb][4][2]);
+                        const float r = fmaf(nrm, fmaf(2.0f, mse, -cQ[mb]), gam * kKappa * fmaf(2.0f, qj, -cS[mb]));
+                        raw[mb][j] = valid ? r : kNegInf;
+                    }
                 }
             }
 
             // the next chunk's K is requested as soon as this chunk's scores are formed
-            if (more) load_k(kr, kc_at(nci), km_at(nci));
+            if (more) load_k(nci);
 
             // ---- online softmax
             float pj[MB][4], alpha[MB];
@@ -380,14 +570,14 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                 for (int g = 0; g < 4; ++g) z_run[mb][g] *= alpha[mb];
             }
             if (__ballot(grew) != 0) {
-                // rescale the PV accumulators: row 4*lq + v of the 16x16 tiles is head 4*lq + v
+                // rescale the PV accumulators: rows 4*lq + v hold head 4*(lq % 2) + v
                 float av[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const float a0 = readlane_f(alpha[0], 16 * v);
                     float a1 = 1.0f;
                     if (MB == 2) a1 = readlane_f(alpha[MB - 1], 16 * v);
-                    av[v] = (lq == 0) ? a0 : ((lq == 1) ? a1 : 1.0f);
+                    av[v] = (lq & 1) ? a1 : a0;
                 }
 #pragma unroll
                 for (int N = 0; N < 8; ++N)
@@ -395,32 +585,50 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                     for (int v = 0; v < 4; ++v) acc[N][v] *= av[v];
             }
 
-            // ---- zero-point term, and P * scale staged into matrix-operand order
+            // ---- zero-point / centroid-constant term, and the PV A operand staged in LDS:
+            // [g][row][token], row = head (fp16 hi) or 8 + head (fp16 lo)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    z_run[mb][0] = fmaf(pj[mb][j], lo_h(vm[j].z), z_run[mb][0]);
-                    z_run[mb][1] = fmaf(pj[mb][j], hi_h(vm[j].z), z_run[mb][1]);
-                    z_run[mb][2] = fmaf(pj[mb][j], lo_h(vm[j].w), z_run[mb][2]);
-                    z_run[mb][3] = fmaf(pj[mb][j], hi_h(vm[j].w), z_run[mb][3]);
-                }
                 const int row = 4 * mb + lq;
+                float P[4][4]; // [g][j]
+                if constexpr (VU) {
+                    const auto& vm = vr.vm;
+                    constexpr float mid = (VB == 4) ? 8.0f : 128.0f; // codes enter as c - mid
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        z_run[mb][0] = fmaf(pj[mb][j], fmaf(mid, lo_h(vm[j].x), lo_h(vm[j].z)), z_run[mb][0]);
+                        z_run[mb][1] = fmaf(pj[mb][j], fmaf(mid, hi_h(vm[j].x), hi_h(vm[j].z)), z_run[mb][1]);
+                        z_run[mb][2] = fmaf(pj[mb][j], fmaf(mid, lo_h(vm[j].y), lo_h(vm[j].w)), z_run[mb][2]);
+                        z_run[mb][3] = fmaf(pj[mb][j], fmaf(mid, hi_h(vm[j].y), hi_h(vm[j].w)), z_run[mb][3]);
+                        const float w = (VB == 4 && j < 2) ? 16.0f : 1.0f;
+                        const float pw = pj[mb][j] * w;
+                        P[0][j] = pw * lo_h(vm[j].x);
+                        P[1][j] = pw * hi_h(vm[j].x);
+                        P[2][j] = pw * lo_h(vm[j].y);
+                        P[3][j] = pw * hi_h(vm[j].y);
+                    }
+                } else {
+                    // weight of plane p = -p n a_p: the bit operands are -b = -(2 bit - 1)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t nw = (j < 2) ? vr.nm.x : vr.nm.y;
+                        const float nt = (j & 1) ? hi_h(nw) : lo_h(nw);
+                        const float pn = pj[mb][j] * nt;
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) P[g][j] = -pn * al[g];
+                    }
+                }
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     h4 hv, lv;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float w = (VB == 4 && j < 2) ? 16.0f : 1.0f;
-                        const uint32_t sw = (g < 2) ? vm[j].x : vm[j].y;
-                        const float sc = (g & 1) ? hi_h(sw) : lo_h(sw);
-                        const float P = (pj[mb][j] * w) * sc;
-                        const _Float16 ph = (_Float16)P;
+                        const _Float16 ph = (_Float16)P[g][j];
                         hv[j] = ph;
-                        lv[j] = (_Float16)(P - (float)ph);
+                        lv[j] = (_Float16)((P[g][j] - (float)ph) * kLoScale);
                     }
-                    *reinterpret_cast<h4*>(my_p + ((g * 2 + 0) * 8 + row) * kPRow + 4 * lr) = hv;
-                    *reinterpret_cast<h4*>(my_p + ((g * 2 + 1) * 8 + row) * kPRow + 4 * lr) = lv;
+                    *reinterpret_cast<h4*>(my_p + (g * 16 + row) * kPRow + 4 * lr) = hv;
+                    *reinterpret_cast<h4*>(my_p + (g * 16 + 8 + row) * kPRow + 4 * lr) = lv;
                 }
             }
             __builtin_amdgcn_wave_barrier();
@@ -429,26 +637,39 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             // ---- PV over the two 32-token blocks of the chunk
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                h8 Ph[4], Pl[4];
+                h8 Pg[4];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    Ph[g] = *reinterpret_cast<const h8*>(my_p + ((g * 2 + 0) * 8 + (lr & 7)) * kPRow + 32 * k + 8 * lq);
-                    Pl[g] = *reinterpret_cast<const h8*>(my_p + ((g * 2 + 1) * 8 + (lr & 7)) * kPRow + 32 * k + 8 * lq);
-                }
+                for (int g = 0; g < 4; ++g)
+                    Pg[g] = *reinterpret_cast<const h8*>(my_p + (g * 16 + lr) * kPRow + 32 * k + 8 * lq);
+                if constexpr (VU) {
+                    const auto& vc = vr.vc;
 #pragma unroll
-                for (int N = 0; N < 8; ++N) {
-                    h8 Bv;
-                    if (VB == 4)
-                        Bv = as_h8(unpack4(vc[k][N >> 2][N & 3]));
-                    else
-                        Bv = as_h8(unpack8(vc[k][N >> 1][2 * (N & 1)], vc[k][N >> 1][2 * (N & 1) + 1]));
-                    acc[N] = mfma16(Ph[N >> 1], Bv, acc[N]);
-                    acc[N] = mfma16(Pl[N >> 1], Bv, acc[N]);
+                    for (int N = 0; N < 8; ++N) {
+                        h8 Bv;
+                        if (VB == 4)
+                            Bv = as_h8(centred4(vc[k][N >> 2][N & 3]));
+                        else
+                            Bv = as_h8(centred8(vc[k][N >> 1][2 * (N & 1)], vc[k][N >> 1][2 * (N & 1) + 1]));
+                        acc[N] = mfma16(Pg[N >> 1], Bv, acc[N]);
+                    }
+                } else {
+                    // words: [plane 0, N<4], [plane 0, N>=4], [plane 1, ...], [plane 2, ...]
+                    const uint32_t w0[2] = {vr.w[k][0].x, vr.w[k][0].y};
+                    const uint32_t w1[2] = {vr.w[k][1].x, vr.w[k][1].y};
+                    const uint32_t w2[2] = {vr.w[k][2].x, vr.w[k][2].y};
+#pragma unroll
+                    for (int N = 0; N < 8; ++N) {
+                        const int hN = N >> 2, q = N & 3;
+                        acc[N] = mfma16(Pg[0], as_h8(pm1x8(w0[hN], q)), acc[N]);
+                        acc[N] = mfma16(Pg[1], as_h8(pm1x8(w1[hN], q)), acc[N]);
+                        acc[N] = mfma16(Pg[2], as_h8(pm1x8(w2[hN], q)), acc[N]);
+                        acc[N] = mfma16(Pg[3], as_h8(pm1x8(w0[hN] ^ w1[hN] ^ w2[hN], q)), acc[N]);
+                    }
                 }
             }
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            if (more) load_v(vr, vc_at(nci), vm_at(nci));
+            if (more) load_v(nci);
         }
         // reduce the per-lane softmax sums over each row of 16 lanes
 #pragma unroll
@@ -488,15 +709,15 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                 const float s0 = readlane_f(sv, 0), s1 = readlane_f(sv, 16), s2 = readlane_f(sv, 32),
                             s3 = readlane_f(sv, 48);
                 const float mnew = fmaxf(wm[h], fmaxf(fmaxf(s0, s1), fmaxf(s2, s3)));
-                const float al = (mnew == kNegInf) ? 1.0f : exp2f(wm[h] - mnew);
+                const float a = (mnew == kNegInf) ? 1.0f : exp2f(wm[h] - mnew);
                 const float p0 = (s0 == kNegInf) ? 0.0f : exp2f(s0 - mnew);
                 const float p1 = (s1 == kNegInf) ? 0.0f : exp2f(s1 - mnew);
                 const float p2 = (s2 == kNegInf) ? 0.0f : exp2f(s2 - mnew);
                 const float p3 = (s3 == kNegInf) ? 0.0f : exp2f(s3 - mnew);
-                wl[h] = wl[h] * al + ((p0 + p1) + (p2 + p3));
+                wl[h] = wl[h] * a + ((p0 + p1) + (p2 + p3));
                 wm[h] = mnew;
-                wacc0[h] = fmaf(p3, vv[3].x, fmaf(p2, vv[2].x, fmaf(p1, vv[1].x, fmaf(p0, vv[0].x, wacc0[h] * al))));
-                wacc1[h] = fmaf(p3, vv[3].y, fmaf(p2, vv[2].y, fmaf(p1, vv[1].y, fmaf(p0, vv[0].y, wacc1[h] * al))));
+                wacc0[h] = fmaf(p3, vv[3].x, fmaf(p2, vv[2].x, fmaf(p1, vv[1].x, fmaf(p0, vv[0].x, wacc0[h] * a))));
+                wacc1[h] = fmaf(p3, vv[3].y, fmaf(p2, vv[2].y, fmaf(p1, vv[1].y, fmaf(p0, vv[0].y, wacc1[h] * a))));
             }
         }
     }
@@ -510,7 +731,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                 s_wm[wave][h] = m_run[mb];
                 s_wl[wave][h] = l_run[mb];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) s_wz[wave][h][g] = z_run[mb][g];
+                for (int g = 0; g < 4; ++g) s_wz[wave][h][g] = VU ? z_run[mb][g] : 0.0f;
             }
         }
     } else if (l == 0) {
@@ -522,19 +743,29 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
         }
     }
     __syncthreads(); // every wave is done with its staging area: reuse it for the accumulators
-    float* s_acc = reinterpret_cast<float*>(s_p); // [kNW][8][128]
+    float* s_acc = reinterpret_cast<float*>(s_p);  // [kNW][8][128], fp16-hi rows / window
+    float* s_acc2 = s_acc + kNW * 8 * kDim;         // [kNW][8][128], fp16-lo rows
     if (!wsplit) {
 #pragma unroll
-        for (int N = 0; N < 8; ++N)
+        for (int N = 0; N < 8; ++N) {
+            const float u = VU ? UV : 1.0f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int h = 4 * lq + v;
-                if (h < G) s_acc[(wave * 8 + h) * kDim + 16 * N + lr] = acc[N][v] * UV;
+                const int h = 4 * (lq & 1) + v;
+                if (h < G) {
+                    if (lq < 2)
+                        s_acc[(wave * 8 + h) * kDim + 16 * N + lr] = acc[N][v] * u;
+                    else
+                        s_acc2[(wave * 8 + h) * kDim + 16 * N + lr] = acc[N][v] * (u * kLoInv);
+                }
             }
+        }
     } else {
         for (int h = 0; h < G; ++h) {
             s_acc[(wave * 8 + h) * kDim + 2 * l] = wacc0[h];
             s_acc[(wave * 8 + h) * kDim + 2 * l + 1] = wacc1[h];
+            s_acc2[(wave * 8 + h) * kDim + 2 * l] = 0.0f;
+            s_acc2[(wave * 8 + h) * kDim + 2 * l + 1] = 0.0f;
         }
     }
     __syncthreads();
@@ -548,7 +779,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             for (int w = 0; w < kNW; ++w) {
                 if (s_wm[w][h] == kNegInf) continue;
                 const float f = exp2f(s_wm[w][h] - M);
-                A = fmaf(f, s_acc[(w * 8 + h) * kDim + d] + s_wz[w][h][d >> 5], A);
+                const int o = (w * 8 + h) * kDim + d;
+                A = fmaf(f, (s_acc[o] + s_acc2[o]) + s_wz[w][h][d >> 5], A);
                 L = fmaf(f, s_wl[w][h], L);
             }
         }
@@ -561,29 +793,40 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     }
 }
 
-template <int KB, int VB, int MB>
+template <int KT, int VT, int MB>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
-    constexpr int NW = (KB == 4 && VB == 4 && MB == 1) ? 8 : 4;
+    constexpr int NW = (KT == kU4 && VT == kU4 && MB == 1) ? 8 : 4;
     dim3 grid(p.n_splits_total, p.Hkv, p.batch);
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, MB, NW>), grid, dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<KT, VT, MB, NW>), grid, dim3(NW * 64), 0, s, p);
     return hipGetLastError();
+}
+
+template <int KT, int VT>
+hipError_t launch_mb(const DecodeParams& p, hipStream_t s) {
+    return p.G > 4 ? launch_t<KT, VT, 2>(p, s) : launch_t<KT, VT, 1>(p, s);
+}
+
+template <int KT>
+hipError_t launch_v(const DecodeParams& p, hipStream_t s) {
+    const PlaneGeom& V = p.geom[1];
+    if (V.scheme != kUniform) return launch_mb<KT, kTb>(p, s);
+    return V.bits == 4 ? launch_mb<KT, kU4>(p, s) : launch_mb<KT, kU8>(p, s);
 }
 
 } // namespace
 
 bool mfma_path_supported(const DecodeParams& p) {
-    return p.geom[0].scheme == kUniform && p.geom[1].scheme == kUniform &&
-           (p.geom[0].bits == 4 || p.geom[0].bits == 8) && (p.geom[1].bits == 4 || p.geom[1].bits == 8) &&
-           p.G <= kMaxGroupHeads;
+    const PlaneGeom& K = p.geom[0];
+    const PlaneGeom& V = p.geom[1];
+    const bool k_ok = (K.scheme == kUniform && (K.bits == 4 || K.bits == 8)) || K.scheme == kTurboQjl;
+    const bool v_ok = (V.scheme == kUniform && (V.bits == 4 || V.bits == 8)) || V.scheme == kTurboMse;
+    return k_ok && v_ok && p.G <= kMaxGroupHeads;
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
-    const int kb = p.geom[0].bits, vb = p.geom[1].bits;
-    const bool two = p.G > 4;
-    if (kb == 4 && vb == 4) return two ? launch_t<4, 4, 2>(p, s) : launch_t<4, 4, 1>(p, s);
-    if (kb == 4 && vb == 8) return two ? launch_t<4, 8, 2>(p, s) : launch_t<4, 8, 1>(p, s);
-    if (kb == 8 && vb == 4) return two ? launch_t<8, 4, 2>(p, s) : launch_t<8, 4, 1>(p, s);
-    return two ? launch_t<8, 8, 2>(p, s) : launch_t<8, 8, 1>(p, s);
+    const PlaneGeom& K = p.geom[0];
+    if (K.scheme != kUniform) return launch_v<kTb>(p, s);
+    return K.bits == 4 ? launch_v<kU4>(p, s) : launch_v<kU8>(p, s);
 }
 
 } // namespace kvq

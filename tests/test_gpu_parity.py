@@ -36,8 +36,7 @@ def _check_all_planes(case, li, heads=None, seqs=None):
 
 
 def _paths(wl):
-    uniform = wl.k_scheme == W.UNIFORM and wl.v_scheme == W.UNIFORM
-    return (1, 2) if uniform else (1,)
+    return (1, 2)  # vector-ALU kernel, matrix-core kernel
 
 
 def _decode_and_compare(case, li, planes=None, step=0, seqs=None):
@@ -190,10 +189,11 @@ def test_progressive_batch_ragged_lengths():
 
 
 @pytest.mark.parametrize("path", [1, 2])
-def test_split_count_invariance_and_determinism(path):
-    wl = W.LLAMA3B_3970_PROGRESSIVE
+@pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_TURBO, W.LLAMA3B_32K_TURBO_ASYM],
+                         ids=lambda w: w.name)
+def test_split_count_invariance_and_determinism(wl, path):
     _say("case: split invariance", wl.name, "path", path)
-    case = Case(wl, 3970)
+    case = Case(wl, 3970, layers=[0])
     case.prefill(0)
     case.cache.set_option(2, path)
     q = W.gen_q(wl, 0, 0).to("cuda")
