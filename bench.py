@@ -5,9 +5,10 @@ One step = for every layer: kvq_append of the new token's K and V (rotation, Sin
 seeded synthetic tensors of the workload's shape, generated on the device before timing.
 
 Prints one JSON line: queries/s (one query = one (sequence, layer) decode attention over all
-query heads), ms per step, the decode kernel's achieved HBM bandwidth against the 8 TB/s MI355X
-peak (algorithmic compressed bytes / average decode-call duration from HIP events recorded on
-the launch stream inside the timed region), and the CPU oracle timed on a bounded sample.
+query heads), ms per step, the split-K decode kernel's achieved HBM bandwidth against the 8 TB/s
+MI355X peak (algorithmic compressed bytes / the kernel's average duration, from HIP events bound
+to that kernel's dispatch on the launch stream inside the timed region; the time of one layer's
+append + decode + merge is reported beside it), and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -45,6 +46,47 @@ def query_bytes(wl: W.Workload, n: int) -> int:
     nw = n - nq
     per = token_head_bytes(wl.k_scheme, wl.k_bits) + token_head_bytes(wl.v_scheme, wl.v_bits)
     return wl.n_kv_heads * (nq * per + nw * 2 * 512)
+
+
+def step_driver(cache, wl: W.Workload, step_in, qs, out, stream):
+    """run(n, events=None): n decode steps (append + decode for every layer) issued by the native
+    loop in libkvq_bench.so through the C ABI; inputs cycle through the pool."""
+    import ctypes
+
+    import quantized_decode_attention_kvq_amd as K
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(K.__file__), "libkvq_bench.so"))
+    fn = lib.kvq_bench_steps
+    vp = ctypes.c_void_p
+    fn.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, ctypes.c_int,
+                   ctypes.c_int, vp, vp, vp, ctypes.POINTER(ctypes.c_int)]
+    fn.restype = ctypes.c_int
+    L, pool = wl.n_layers, len(step_in)
+    arr = lambda xs: (vp * len(xs))(*[vp(x) for x in xs])  # noqa: E731
+    kp = arr([step_in[s][l][0].data_ptr() for s in range(pool) for l in range(L)])
+    vptr = arr([step_in[s][l][1].data_ptr() for s in range(pool) for l in range(L)])
+    qp = arr([qs[s][l].data_ptr() for s in range(pool) for l in range(L)])
+    op = arr([out[l].data_ptr() for l in range(L)])
+    dtype = 1 if qs[0][0].dtype == torch.bfloat16 else 0
+
+    def run(n, events=None):
+        e0 = e1 = None
+        if events is not None:
+            e0 = arr([pair[0].cuda_event for pair in events])
+            e1 = arr([pair[1].cuda_event for pair in events])
+        where = ctypes.c_int(-1)
+        st = fn(cache.handle, L, n, pool, kp, vptr, qp, op, dtype, wl.batch, vp(stream.cuda_stream),
+                e0, e1, ctypes.byref(where))
+        if st != 0:
+            raise RuntimeError(f"kvq_bench_steps failed with status {st} at call {where.value}")
+
+    return run
+
+
+def split_kernel_name(wl: W.Workload) -> str:
+    """The split-K decode kernel the library launches for this cache (matrix-core path)."""
+    kind = lambda scheme, bits: "Tb" if scheme != W.UNIFORM else f"U{bits}"  # noqa: E731
+    return (f"decode_mfma_kernel (K {kind(wl.k_scheme, wl.k_bits)}, V {kind(wl.v_scheme, wl.v_bits)}, "
+            f"{wl.group} query heads per kv head)")
 
 
 def build_cache(wl: W.Workload, extra: int, log):
@@ -137,10 +179,9 @@ def main():
     if args.batch:
         wl = wl.with_(batch=args.batch)
     torch.cuda.init()
-    total_steps = args.warmup + args.steps
     log(f"workload {wl.name}: building cache")
     t_build = time.perf_counter()
-    cache, kv0 = build_cache(wl, total_steps, log)
+    cache, kv0 = build_cache(wl, args.warmup + 2 * args.steps, log)
     log(f"cache built in {time.perf_counter() - t_build:.1f} s")
 
     L, B = wl.n_layers, wl.batch
@@ -149,43 +190,40 @@ def main():
     qs = [[W.gen_q(wl, layer, s, device="cuda") for layer in range(L)] for s in range(pool)]
     out = torch.empty((L, B, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    run = step_driver(cache, wl, step_in, qs, out, stream)
 
-    def step(s, evs=None):
-        for layer in range(L):
-            k, v = step_in[s % pool][layer]
-            cache.append(layer, k, v)
-            if evs is not None:
-                evs[2 * layer].record(stream)
-            cache.attn_decode(layer, qs[s % pool][layer], out[layer])
-            if evs is not None:
-                evs[2 * layer + 1].record(stream)
-
-    for s in range(args.warmup):
-        step(s)
+    run(args.warmup)
     torch.cuda.synchronize()
     n_start = cache.length(0)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * L)] for _ in range(args.steps)]
+    # timed region: `steps` decode steps, nothing but the library's own launches inside
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t0.record(stream)
-    for s in range(args.steps):
-        step(args.warmup + s, evs[s])
+    run(args.steps)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     elapsed = t0.elapsed_time(t1) / 1e3
-    dec = np.array([[e[2 * i].elapsed_time(e[2 * i + 1]) for i in range(L)] for e in evs]) / 1e3
-    n_end = cache.length(0)
+    # kernel pass: the same steps again with start / stop events bound by the library to each
+    # split-K kernel's own dispatch on the launch stream (each recorded once here so it exists)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps * L)]
+    for pair in evs:
+        for e in pair:
+            e.record(stream)
+    torch.cuda.synchronize()
+    run(args.steps, evs)
+    torch.cuda.synchronize()
+    split = np.array([pair[0].elapsed_time(pair[1]) for pair in evs]) / 1e3
     assert torch.isfinite(out).all()
 
     queries = L * B * args.steps
     qps = queries / elapsed
-    n_mean = 0.5 * (n_start + 1 + n_end)
+    n_mean = 0.5 * (n_start + 1 + cache.length(0))  # mean context over both passes
     bytes_per_launch = B * query_bytes(wl, int(round(n_mean)))
-    dec_mean = float(dec.mean())
-    achieved = bytes_per_launch / dec_mean / 1e9
+    split_mean = float(split.mean())
+    achieved = bytes_per_launch / split_mean / 1e9
     res = {
         "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": 1e3 * elapsed / args.steps,
@@ -199,10 +237,11 @@ def main():
                    "step": "append + decode per layer"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "kvq_attn_decode (split-K + merge)",
-                     "bytes_per_launch": bytes_per_launch, "avg_launch_us": 1e6 * dec_mean,
-                     "p10_us": 1e6 * float(np.percentile(dec, 10)),
-                     "p90_us": 1e6 * float(np.percentile(dec, 90))},
+                     "kernel": split_kernel_name(wl),
+                     "bytes_per_launch": bytes_per_launch, "avg_launch_us": 1e6 * split_mean,
+                     "p10_us": 1e6 * float(np.percentile(split, 10)),
+                     "p90_us": 1e6 * float(np.percentile(split, 90)),
+                     "layer_step_us": 1e6 * elapsed / (args.steps * L)},
         "wall_s": wall,
     }
     if not args.no_cpu_baseline:

@@ -178,6 +178,13 @@ kvq_status kvq_get_tables(const kvq_cache* cache, kvq_tables* out);
 /* Set a tuning option (KVQ_OPT_*). Results do not depend on it beyond float rounding order. */
 kvq_status kvq_set_option(kvq_cache* cache, int option, int value);
 
+/* Measurement hook: while set, every kvq_attn_decode launches its split-K decode kernel with
+ * ev_start / ev_stop attached to the kernel's own dispatch (hipExtLaunchKernelGGL), so the pair
+ * times exactly that kernel on the call's stream.  hipEvent_t handles passed as void*, created
+ * (with timing) and owned by the caller, who keeps them alive while set.  Both NULL clears the
+ * hook; exactly one NULL is KVQ_ERR_INVALID_ARG.  Results do not depend on it. */
+kvq_status kvq_set_timing_events(kvq_cache* cache, void* ev_start, void* ev_stop);
+
 /* Tokens cached for (layer, seq); -1 on a bad argument. */
 int kvq_get_length(const kvq_cache* cache, int layer, int seq);
 

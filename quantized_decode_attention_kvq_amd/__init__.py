@@ -56,6 +56,10 @@ class KvCache:
     def set_option(self, option, value):
         _kvq.kvq_set_option(self.handle, option, value)
 
+    def set_timing_events(self, ev_start=None, ev_stop=None):
+        """torch.cuda.Event objects that already exist on the device (record each once first)."""
+        _kvq.kvq_set_timing_events(self.handle, ev_start, ev_stop)
+
     def length(self, layer, seq=0):
         return _kvq.kvq_get_length(self.handle, layer, seq)
 

@@ -21,7 +21,7 @@ STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_INVALID_ARG", 2: "KVQ_ERR_UNSUPPORTED", 3: "K
 EXPORTS = ["kvq_cache_required_bytes", "kvq_cache_create", "kvq_cache_destroy",
            "kvq_set_random_tables", "kvq_calibrate", "kvq_prefill_quantize", "kvq_append",
            "kvq_attn_decode", "kvq_get_layout", "kvq_get_tables", "kvq_set_option",
-           "kvq_get_length", "kvq_status_str", "kvq_last_hip_error"]
+           "kvq_set_timing_events", "kvq_get_length", "kvq_status_str", "kvq_last_hip_error"]
 
 
 class KvqError(RuntimeError):
@@ -59,7 +59,7 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m quantized_decode_attention_kvq_amd.build`")
+                          "`python quantized_decode_attention_kvq_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
     vp, i, f, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int
     sig = {
@@ -75,6 +75,7 @@ def load():
         "kvq_get_layout": [vp, i, i, i, i, ctypes.POINTER(kvq_layout)],
         "kvq_get_tables": [vp, ctypes.POINTER(kvq_tables)],
         "kvq_set_option": [vp, i, i],
+        "kvq_set_timing_events": [vp, vp, vp],
         "kvq_get_length": [vp, i, i],
         "kvq_status_str": [i],
         "kvq_last_hip_error": [vp],
@@ -184,6 +185,12 @@ def kvq_get_tables(h) -> kvq_tables:
 
 def kvq_set_option(h, option, value):
     _check(load().kvq_set_option(h, option, value), "kvq_set_option")
+
+
+def kvq_set_timing_events(h, ev_start=None, ev_stop=None):
+    """Events are torch.cuda.Event objects (their raw handles are passed) or None."""
+    raw = [None if e is None else ctypes.c_void_p(e.cuda_event) for e in (ev_start, ev_stop)]
+    _check(load().kvq_set_timing_events(h, *raw), "kvq_set_timing_events")
 
 
 def kvq_get_length(h, layer, seq) -> int:

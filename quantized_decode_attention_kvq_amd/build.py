@@ -1,6 +1,7 @@
 """Build libkvq.so (HIP kernels for gfx950 + the C-ABI host code) in-tree with hipcc.
 
-Run as ``python -m quantized_decode_attention_kvq_amd.build``.  The quantize/calibration unit is
+Run as ``python quantized_decode_attention_kvq_amd/build.py`` (by path: importing the package
+loads the library, which may be missing or stale before a build).  The quantize/calibration unit is
 compiled with -ffp-contract=off so its binary32 operations round in the order written; every HIP
 unit is compiled with packed-fp32 instructions disabled.
 """
@@ -15,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
+BENCH_LIB = os.path.join(HERE, "libkvq_bench.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -50,6 +52,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the measurement loop driver (calls the C ABI of libkvq.so; not part of that ABI)
+    bobj = os.path.join(BUILD, "kvq_bench.o")
+    for cmd in ([HIPCC, *COMMON, "-x", "c++", "-c", os.path.join(CSRC, "kvq_bench.cpp"), "-o", bobj],
+                [HIPCC, "-shared", "-fPIC", "-o", BENCH_LIB + ".tmp", bobj, f"-L{HERE}", "-lkvq",
+                 "-Wl,-rpath,$ORIGIN"]):
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"bench driver build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(BENCH_LIB + ".tmp", BENCH_LIB)
     if verbose:
         print(f"built {LIB}")
     return LIB

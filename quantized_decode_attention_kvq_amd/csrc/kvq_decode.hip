@@ -11,6 +11,7 @@
 //
 // Scores are kept in the log2 domain: q' = q * softmax_scale * log2(e), p = exp2(s - m).
 #include <hip/hip_fp16.h>
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "kvq_internal.h"
@@ -468,9 +469,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
 
 } // namespace
 
-hipError_t launch_decode_vec(const DecodeParams& p, hipStream_t s) {
+hipError_t launch_decode_vec(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     dim3 grid(p.n_splits_total, p.Hkv, p.batch);
-    hipLaunchKernelGGL(decode_vec_kernel, grid, dim3(256), 0, s, p);
+    hipExtLaunchKernelGGL(decode_vec_kernel, grid, dim3(256), 0, s, ev0, ev1, 0, p);
     return hipGetLastError();
 }
 

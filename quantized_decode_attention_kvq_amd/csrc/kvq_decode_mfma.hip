@@ -29,6 +29,7 @@
 //  * Each split writes one partial (running max, sum, acc[128]) per query head; the merge
 //    kernel combines them in a fixed order and applies c_V and R_V^-1.
 //  * The FP32 window (progressive mode) is one extra split computed on the vector ALU.
+#include <hip/hip_ext.h>
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -266,6 +267,20 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     }
     const float2 sgn = reinterpret_cast<const float2*>(p.signs + (size_t)(kvh * 2 + 0) * kDim)[l];
     const float2 csk = reinterpret_cast<const float2*>(p.cs + (size_t)(kvh * 2 + 0) * kDim)[l];
+    // TurboQuant tables: centroids 4..7, and this thread's slice of S^T (stored [j][i]) for S q'
+    constexpr int kParts = kNW * 64 / kDim, kJ = kDim / kParts;
+    float mu4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float st[KU ? 1 : kJ];
+    if constexpr (!KU || !VU) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mu4[c] = p.mu[4 + c];
+    }
+    if constexpr (!KU) {
+        if (!wsplit) {
+#pragma unroll
+            for (int jj = 0; jj < kJ; ++jj) st[jj] = p.qjl_st[((tid >> 7) * kJ + jj) * kDim + (tid & 127)];
+        }
+    }
     const int lr = l & 15, lq = l >> 4; // column / quarter of the 16x16 tiles
     const int tok_begin = split * p.split_tokens;
     const int tok_end = wsplit ? tok_begin : min(nq, tok_begin + p.split_tokens);
@@ -359,14 +374,28 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     }
     __syncthreads();
     if constexpr (!KU) {
-        // S q' for the QJL term (S^T is stored [j][i]), then its sum per head
+        // S q' for the QJL term: thread (i, part) sums 128/kParts values of j for every head, then
+        // the parts are added in order
+        float* s_spp = reinterpret_cast<float*>(s_p); // [kParts][8][128] scratch
+        if (!wsplit) {
+            const int i = tid & 127, part = tid >> 7;
+#pragma unroll
+            for (int h = 0; h < kMaxGroupHeads; ++h) {
+                if (h >= G) break;
+                float a = 0.0f;
+#pragma unroll
+                for (int jj = 0; jj < kJ; ++jj) a = fmaf(st[jj], s_q[h][part * kJ + jj], a);
+                s_spp[(part * 8 + h) * kDim + i] = a;
+            }
+        }
+        __syncthreads();
         if (!wsplit) {
             for (int idx = tid; idx < G * kDim; idx += kNW * 64) {
                 const int h = idx >> 7, i = idx & 127;
-                float s = 0.0f;
-#pragma unroll 8
-                for (int j = 0; j < kDim; ++j) s = fmaf(p.qjl_st[j * kDim + i], s_q[h][j], s);
-                s_sp[h][i] = s;
+                float a = 0.0f;
+#pragma unroll
+                for (int q = 0; q < kParts; ++q) a += s_spp[(q * 8 + h) * kDim + i];
+                s_sp[h][i] = a;
             }
         }
         __syncthreads();
@@ -380,7 +409,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     // TurboQuant centroids as odd bit functions: mu[c] = a0 b0 + a1 b1 + a2 b2 + a3 b0 b1 b2
     float al[4] = {0.0f, 0.0f, 0.0f, 0.0f}, asum = 0.0f;
     if constexpr (!KU || !VU) {
-        const float m4 = p.mu[4], m5 = p.mu[5], m6 = p.mu[6], m7 = p.mu[7];
+        const float m4 = mu4[0], m5 = mu4[1], m6 = mu4[2], m7 = mu4[3];
         al[0] = 0.25f * ((m5 - m4) + (m7 - m6));
         al[1] = 0.25f * ((m6 - m4) + (m7 - m5));
         al[2] = 0.25f * ((m4 + m5) + (m6 + m7));
@@ -794,23 +823,23 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 }
 
 template <int KT, int VT, int MB>
-hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
-    constexpr int NW = (KT == kU4 && VT == kU4 && MB == 1) ? 8 : 4;
+hipError_t launch_t(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    constexpr int NW = (MB == 1 && !(KT == kU8 && VT == kU8)) ? 8 : 4; // 8 waves where registers allow
     dim3 grid(p.n_splits_total, p.Hkv, p.batch);
-    hipLaunchKernelGGL((decode_mfma_kernel<KT, VT, MB, NW>), grid, dim3(NW * 64), 0, s, p);
+    hipExtLaunchKernelGGL((decode_mfma_kernel<KT, VT, MB, NW>), grid, dim3(NW * 64), 0, s, ev0, ev1, 0, p);
     return hipGetLastError();
 }
 
 template <int KT, int VT>
-hipError_t launch_mb(const DecodeParams& p, hipStream_t s) {
-    return p.G > 4 ? launch_t<KT, VT, 2>(p, s) : launch_t<KT, VT, 1>(p, s);
+hipError_t launch_mb(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    return p.G > 4 ? launch_t<KT, VT, 2>(p, s, ev0, ev1) : launch_t<KT, VT, 1>(p, s, ev0, ev1);
 }
 
 template <int KT>
-hipError_t launch_v(const DecodeParams& p, hipStream_t s) {
+hipError_t launch_v(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const PlaneGeom& V = p.geom[1];
-    if (V.scheme != kUniform) return launch_mb<KT, kTb>(p, s);
-    return V.bits == 4 ? launch_mb<KT, kU4>(p, s) : launch_mb<KT, kU8>(p, s);
+    if (V.scheme != kUniform) return launch_mb<KT, kTb>(p, s, ev0, ev1);
+    return V.bits == 4 ? launch_mb<KT, kU4>(p, s, ev0, ev1) : launch_mb<KT, kU8>(p, s, ev0, ev1);
 }
 
 } // namespace
@@ -823,10 +852,10 @@ bool mfma_path_supported(const DecodeParams& p) {
     return k_ok && v_ok && p.G <= kMaxGroupHeads;
 }
 
-hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s) {
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const PlaneGeom& K = p.geom[0];
-    if (K.scheme != kUniform) return launch_v<kTb>(p, s);
-    return K.bits == 4 ? launch_v<kU4>(p, s) : launch_v<kU8>(p, s);
+    if (K.scheme != kUniform) return launch_v<kTb>(p, s, ev0, ev1);
+    return K.bits == 4 ? launch_v<kU4>(p, s, ev0, ev1) : launch_v<kU8>(p, s, ev0, ev1);
 }
 
 } // namespace kvq

@@ -140,6 +140,7 @@ struct kvq_cache {
     int decode_path;
     int num_cus;
     int device;
+    hipEvent_t ev[2]; // measurement hook of kvq_set_timing_events (caller-owned), or both null
 
     float* signs() const { return reinterpret_cast<float*>(base + plan.off_signs); }
     float* cs() const { return reinterpret_cast<float*>(base + plan.off_c); }
@@ -217,6 +218,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, 
     c->last_hip_error = 0;
     c->split_tokens_opt = 0;
     c->decode_path = 0;
+    c->ev[0] = c->ev[1] = nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipGetDevice(&c->device);
     if (e == hipSuccess)
@@ -407,7 +409,7 @@ kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, fl
     p.n_splits_total = ns + nwin;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    e = matrix ? launch_decode_mfma(p, s) : launch_decode_vec(p, s);
+    e = matrix ? launch_decode_mfma(p, s, c->ev[0], c->ev[1]) : launch_decode_vec(p, s, c->ev[0], c->ev[1]);
     if (e == hipSuccess) e = launch_decode_merge(p, s);
     if (e != hipSuccess) return dev_fail(c, e);
     return KVQ_OK;
@@ -459,6 +461,13 @@ kvq_status kvq_set_option(kvq_cache* c, int option, int value) {
     default:
         return KVQ_ERR_INVALID_ARG;
     }
+}
+
+kvq_status kvq_set_timing_events(kvq_cache* c, void* ev_start, void* ev_stop) {
+    if (!c || (!ev_start) != (!ev_stop)) return KVQ_ERR_INVALID_ARG;
+    c->ev[0] = static_cast<hipEvent_t>(ev_start);
+    c->ev[1] = static_cast<hipEvent_t>(ev_stop);
+    return KVQ_OK;
 }
 
 int kvq_get_length(const kvq_cache* c, int layer, int seq) {

@@ -79,9 +79,10 @@ hipError_t launch_calibrate(const CalibParams& p, hipStream_t s);
 hipError_t launch_codebook(float* mu, float* theta, int iters, hipStream_t s);
 hipError_t launch_transpose128(const float* in, float* out, hipStream_t s);
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t s);
-hipError_t launch_decode_vec(const DecodeParams& p, hipStream_t s);
+// The split-K launchers take optional events bound to the kernel's dispatch (measurement).
+hipError_t launch_decode_vec(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t s);
 bool mfma_path_supported(const DecodeParams& p);
-hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
 } // namespace kvq

@@ -91,4 +91,6 @@ def test_null_handle_calls_rejected():
     assert lib.kvq_calibrate(None, 0, None, None, 0, 512, None) == 1
     assert lib.kvq_get_length(None, 0, 0) == -1
     assert lib.kvq_cache_destroy(None) == 1
+    assert lib.kvq_set_timing_events(None, None, None) == 1
+    assert lib.kvq_set_option(None, 1, 0) == 1
     assert K.kvq_status_str(0) == "ok" and K.kvq_status_str(3) == "context capacity exceeded"
