@@ -82,6 +82,23 @@ def step_driver(cache, wl: W.Workload, step_in, qs, out, stream):
     return run
 
 
+def traffic_record(wl: W.Workload):
+    """HBM bytes per launch of the split-K kernel measured with rocprofv3 --pmc (FETCH_SIZE and
+    WRITE_SIZE, scaled by the copy-probe factors) and recorded under profiles/, valid only while
+    the kernel source has the recorded sha256; None otherwise."""
+    import glob
+    import hashlib
+    src = os.path.join(ROOT, "quantized_decode_attention_kvq_amd", "csrc", "kvq_decode_mfma.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            if line.startswith("traffic_record "):
+                rec = json.loads(line[len("traffic_record "):])
+                if rec["workload"] == wl.name and rec["kernel_sha256"] == sha:
+                    return rec
+    return None
+
+
 def split_kernel_name(wl: W.Workload) -> str:
     """The split-K decode kernel the library launches for this cache (matrix-core path)."""
     kind = lambda scheme, bits: "Tb" if scheme != W.UNIFORM else f"U{bits}"  # noqa: E731
@@ -158,6 +175,20 @@ def cpu_baseline(wl: W.Workload, kv0, budget_s: float):
                       f"(fp64 attention over the oracle's own planes; plane building not timed)"}
 
 
+def copy_probe():
+    """Three plain device copies of exactly 1 GiB: the reference for scaling rocprofv3's
+    FETCH_SIZE / WRITE_SIZE counters to HBM bytes."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe": "torch copy_", "bytes_read": 4 * n, "bytes_written": 4 * n,
+                      "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +198,8 @@ def main():
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy 1 GiB device-to-device (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path has no cross-GPU step in this build "
@@ -174,6 +207,9 @@ def main():
         sys.exit(2)
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
 
+    if args.copy_probe:
+        copy_probe()
+        return
     import quantized_decode_attention_kvq_amd  # noqa: F401  (fails loudly without libkvq.so)
     wl = W.BY_NAME[args.workload]
     if args.batch:
@@ -224,6 +260,8 @@ def main():
     bytes_per_launch = B * query_bytes(wl, int(round(n_mean)))
     split_mean = float(split.mean())
     achieved = bytes_per_launch / split_mean / 1e9
+    rec = traffic_record(wl)
+    traffic = None if rec is None else rec["fetch_bytes"] + rec["write_bytes"]
     res = {
         "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": 1e3 * elapsed / args.steps,
@@ -236,7 +274,9 @@ def main():
                    "fp32_window": wl.window, "sinkhorn_iters": wl.sinkhorn_iters,
                    "step": "append + decode per layer"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_unit": "bytes/launch",
+                     "traffic_vs_algorithmic": None if traffic is None else traffic / bytes_per_launch,
                      "kernel": split_kernel_name(wl),
                      "bytes_per_launch": bytes_per_launch, "avg_launch_us": 1e6 * split_mean,
                      "p10_us": 1e6 * float(np.percentile(split, 10)),
