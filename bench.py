@@ -48,9 +48,10 @@ def query_bytes(wl: W.Workload, n: int) -> int:
     return wl.n_kv_heads * (nq * per + nw * 2 * 512)
 
 
-def step_driver(cache, wl: W.Workload, step_in, qs, out, stream):
+def step_driver(cache, wl: W.Workload, step_in, qs, out, stream, fused=True):
     """run(n, events=None): n decode steps (append + decode for every layer) issued by the native
-    loop in libkvq_bench.so through the C ABI; inputs cycle through the pool."""
+    loop in libkvq_bench.so through the C ABI (kvq_append_attn_decode per layer when fused, else
+    kvq_append then kvq_attn_decode); inputs cycle through the pool."""
     import ctypes
 
     import quantized_decode_attention_kvq_amd as K
@@ -58,7 +59,7 @@ def step_driver(cache, wl: W.Workload, step_in, qs, out, stream):
     fn = lib.kvq_bench_steps
     vp = ctypes.c_void_p
     fn.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, ctypes.c_int,
-                   ctypes.c_int, vp, vp, vp, ctypes.POINTER(ctypes.c_int)]
+                   ctypes.c_int, vp, vp, vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     fn.restype = ctypes.c_int
     L, pool = wl.n_layers, len(step_in)
     arr = lambda xs: (vp * len(xs))(*[vp(x) for x in xs])  # noqa: E731
@@ -75,7 +76,7 @@ def step_driver(cache, wl: W.Workload, step_in, qs, out, stream):
             e1 = arr([pair[1].cuda_event for pair in events])
         where = ctypes.c_int(-1)
         st = fn(cache.handle, L, n, pool, kp, vptr, qp, op, dtype, wl.batch, vp(stream.cuda_stream),
-                e0, e1, ctypes.byref(where))
+                e0, e1, int(fused), ctypes.byref(where))
         if st != 0:
             raise RuntimeError(f"kvq_bench_steps failed with status {st} at call {where.value}")
 
@@ -198,6 +199,8 @@ def main():
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="kvq_append + kvq_attn_decode per layer instead of kvq_append_attn_decode")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device-to-device (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -226,7 +229,7 @@ def main():
     qs = [[W.gen_q(wl, layer, s, device="cuda") for layer in range(L)] for s in range(pool)]
     out = torch.empty((L, B, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    run = step_driver(cache, wl, step_in, qs, out, stream)
+    run = step_driver(cache, wl, step_in, qs, out, stream, fused=not args.separate)
 
     run(args.warmup)
     torch.cuda.synchronize()
@@ -272,7 +275,8 @@ def main():
                    "k_cache": [wl.k_scheme, wl.k_bits, bool(wl.rotate_k)],
                    "v_cache": [wl.v_scheme, wl.v_bits, bool(wl.rotate_v)],
                    "fp32_window": wl.window, "sinkhorn_iters": wl.sinkhorn_iters,
-                   "step": "append + decode per layer"},
+                   "step": ("kvq_append + kvq_attn_decode" if args.separate
+                            else "kvq_append_attn_decode") + " per layer"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_unit": "bytes/launch",

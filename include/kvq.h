@@ -168,6 +168,16 @@ kvq_status kvq_append(kvq_cache* cache, int layer, const void* k, const void* v,
 kvq_status kvq_attn_decode(kvq_cache* cache, int layer, const void* q, int dtype, float* out,
                            int batch, float softmax_scale, void* stream);
 
+/* One decode step of one layer: kvq_append(k, v) followed by kvq_attn_decode(q) over the cache
+ * that now includes the new token, in one call ([P1], [P2], [P3] as for those two calls).  Same
+ * arguments, layouts, checks and results: the packed planes are bit-identical to the two calls,
+ * and so is the output.  On the matrix-core path the append runs inside the decode kernel: the
+ * workgroup whose token range holds the new token quantizes it before reading.  The lengths grow
+ * by one only when the call is accepted. */
+kvq_status kvq_append_attn_decode(kvq_cache* cache, int layer, const void* k, const void* v,
+                                  const void* q, int dtype, float* out, int batch,
+                                  float softmax_scale, void* stream);
+
 /* Plane pointers and sizes of (layer, seq, kv_head, tensor 0 = K / 1 = V). */
 kvq_status kvq_get_layout(const kvq_cache* cache, int layer, int seq, int kv_head, int tensor,
                           kvq_layout* out);

@@ -28,7 +28,7 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 UNITS = [
     ("kvq_quant.hip", DEVICE + ["-ffp-contract=off"]),
     ("kvq_decode.hip", DEVICE),
-    ("kvq_decode_mfma.hip", DEVICE),
+    ("kvq_decode_mfma.hip", DEVICE + ["-ffp-contract=off"]),  # holds the fused append
     ("kvq_host.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]),  # host only
 ]
 

@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kvq_internal.h"
+#include "kvq_quant_dev.h"
 
 namespace kvq {
 namespace {
@@ -241,6 +242,17 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     const uint8_t* vcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.codes_off);
     const uint8_t* vmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.meta_off);
     const float* vring = reinterpret_cast<const float*>(slot + p.plane_off[1] + VG.ring_off);
+    // Fused append: the workgroup whose split holds the newest token (the window split in
+    // progressive mode, else the code split of token n - 1) quantizes it first, K on wave 0 and
+    // V on wave 1; the barrier makes its stores visible to the workgroup's own loads below.
+    if (p.fuse) {
+        const int owner = (W > 0) ? p.n_splits + min(p.n_win_splits - 1, (n - 1 - nq) / ((kWindowMax + p.n_win_splits - 1) / p.n_win_splits))
+                                  : (n - 1) / p.split_tokens;
+        if (split == owner && n > 0) {
+            if (wave < 2) qdev::quantize_wave(p.append, wave, b, kvh, 0, reinterpret_cast<float*>(s_p) + wave * kDim);
+            __syncthreads();
+        }
+    }
     const float UK = (KB == 4) ? 1048576.0f : 16777216.0f; // 2^20 / 2^24: unit of a code product
     const float UV = (VB == 4) ? 0.0625f : 1.0f; // 4-bit: half the weights carry x16
 

@@ -296,22 +296,25 @@ kvq_status kvq_calibrate(kvq_cache* c, int layer, const void* Kc, const void* Vc
     return KVQ_OK;
 }
 
-kvq_status kvq_prefill_quantize(kvq_cache* c, int layer, const void* K, const void* V, int dtype,
-                                int n_tokens, int batch, void* stream) {
+namespace {
+
+// Checks of an append / prefill of n_tokens and its kernel parameters (nothing is enqueued and
+// no length changes here).
+kvq_status make_quant(kvq_cache* c, int layer, const void* K, const void* V, int dtype, int n_tokens,
+                      int batch, QuantParams& p) {
     if (!c) return KVQ_ERR_INVALID_ARG;
     if (layer < 0 || layer >= c->cfg.n_layers) return KVQ_ERR_INVALID_ARG;
     if (batch < 1 || batch > c->cfg.max_batch || n_tokens < 0) return KVQ_ERR_INVALID_ARG;
     if (dtype != KVQ_F32 && dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
     if (!K || !V) return KVQ_ERR_INVALID_ARG;
     if (!aligned16(K) || !aligned16(V)) return KVQ_ERR_MISALIGNED;
-    int* len = &c->len[(size_t)layer * c->cfg.max_batch];
+    const int* len = &c->len[(size_t)layer * c->cfg.max_batch];
     for (int b = 0; b < batch; ++b)
         if ((long long)len[b] + n_tokens > c->cfg.max_context) return KVQ_ERR_CAPACITY;
     if ((c->needs_signs() || c->needs_S()) && !c->tables_set) return KVQ_ERR_NOT_READY;
     if (c->needs_calib() && !c->calibrated[(size_t)layer]) return KVQ_ERR_NOT_READY;
-    if (n_tokens == 0) return KVQ_OK;
 
-    QuantParams p{};
+    p = QuantParams{};
     p.src[0] = K;
     p.src[1] = V;
     fill_params_common(c, layer, p.layer_base, p.seq_stride, p.head_stride, p.plane_off, p.geom);
@@ -333,19 +336,12 @@ kvq_status kvq_prefill_quantize(kvq_cache* c, int layer, const void* K, const vo
         groups = std::max(groups, (len[b] + n_tokens - 1) / 8 - len[b] / 8 + 1);
     }
     p.groups8 = groups;
-    const hipError_t e = launch_quantize(p, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return dev_fail(c, e);
-    for (int b = 0; b < batch; ++b) len[b] += n_tokens;
     return KVQ_OK;
 }
 
-kvq_status kvq_append(kvq_cache* c, int layer, const void* k, const void* v, int dtype, int batch,
-                      void* stream) {
-    return kvq_prefill_quantize(c, layer, k, v, dtype, 1, batch, stream);
-}
-
-kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, float* out, int batch,
-                           float softmax_scale, void* stream) {
+// Argument checks of a decode call.
+kvq_status check_decode(const kvq_cache* c, int layer, const void* q, int dtype, const float* out,
+                        int batch, float softmax_scale) {
     if (!c) return KVQ_ERR_INVALID_ARG;
     if (layer < 0 || layer >= c->cfg.n_layers) return KVQ_ERR_INVALID_ARG;
     if (batch < 1 || batch > c->cfg.max_batch) return KVQ_ERR_INVALID_ARG;
@@ -354,8 +350,13 @@ kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, fl
     if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_MISALIGNED;
     if (!std::isfinite(softmax_scale)) return KVQ_ERR_INVALID_ARG;
     if ((c->needs_signs() || c->needs_S()) && !c->tables_set) return KVQ_ERR_NOT_READY;
+    return KVQ_OK;
+}
 
-    DecodeParams p{};
+// Decode parameters and split plan over the current lengths; `matrix` = matrix-core path.
+kvq_status make_decode(const kvq_cache* c, int layer, const void* q, int dtype, float* out, int batch,
+                       float softmax_scale, DecodeParams& p, bool& matrix) {
+    p = DecodeParams{};
     p.q = q;
     p.out = out;
     fill_params_common(c, layer, p.layer_base, p.seq_stride, p.head_stride, p.plane_off, p.geom);
@@ -379,7 +380,7 @@ kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, fl
         const int nq = p.window > 0 ? std::max(0, len[b] - p.window) : len[b];
         nq_max = std::max(nq_max, nq);
     }
-    const bool matrix = c->decode_path != 1 && mfma_path_supported(p);
+    matrix = c->decode_path != 1 && mfma_path_supported(p);
     if (c->decode_path == 2 && !matrix) return KVQ_ERR_UNSUPPORTED;
     int st;
     if (c->split_tokens_opt > 0) {
@@ -407,10 +408,80 @@ kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, fl
     p.n_splits = ns;
     p.n_win_splits = nwin;
     p.n_splits_total = ns + nwin;
+    return KVQ_OK;
+}
+
+hipError_t launch_decode(const kvq_cache* c, const DecodeParams& p, bool matrix, hipStream_t s) {
+    hipError_t e = matrix ? launch_decode_mfma(p, s, c->ev[0], c->ev[1])
+                          : launch_decode_vec(p, s, c->ev[0], c->ev[1]);
+    if (e == hipSuccess) e = launch_decode_merge(p, s);
+    return e;
+}
+
+} // namespace
+
+kvq_status kvq_prefill_quantize(kvq_cache* c, int layer, const void* K, const void* V, int dtype,
+                                int n_tokens, int batch, void* stream) {
+    QuantParams p;
+    const kvq_status st = make_quant(c, layer, K, V, dtype, n_tokens, batch, p);
+    if (st != KVQ_OK || n_tokens == 0) return st;
+    const hipError_t e = launch_quantize(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return dev_fail(c, e);
+    int* len = &c->len[(size_t)layer * c->cfg.max_batch];
+    for (int b = 0; b < batch; ++b) len[b] += n_tokens;
+    return KVQ_OK;
+}
+
+kvq_status kvq_append(kvq_cache* c, int layer, const void* k, const void* v, int dtype, int batch,
+                      void* stream) {
+    return kvq_prefill_quantize(c, layer, k, v, dtype, 1, batch, stream);
+}
+
+kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, float* out, int batch,
+                           float softmax_scale, void* stream) {
+    kvq_status st = check_decode(c, layer, q, dtype, out, batch, softmax_scale);
+    if (st != KVQ_OK) return st;
+    DecodeParams p;
+    bool matrix = false;
+    st = make_decode(c, layer, q, dtype, out, batch, softmax_scale, p, matrix);
+    if (st != KVQ_OK) return st;
+    const hipError_t e = launch_decode(c, p, matrix, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return dev_fail(c, e);
+    return KVQ_OK;
+}
+
+kvq_status kvq_append_attn_decode(kvq_cache* c, int layer, const void* k, const void* v, const void* q,
+                                  int dtype, float* out, int batch, float softmax_scale, void* stream) {
+    QuantParams qp;
+    kvq_status st = make_quant(c, layer, k, v, dtype, 1, batch, qp);
+    if (st != KVQ_OK) return st;
+    st = check_decode(c, layer, q, dtype, out, batch, softmax_scale);
+    if (st != KVQ_OK) return st;
+    // plan the decode over the lengths after the append; undone if the plan is refused
+    int* len = &c->len[(size_t)layer * c->cfg.max_batch];
+    for (int b = 0; b < batch; ++b) len[b] += 1;
+    DecodeParams p;
+    bool matrix = false;
+    st = make_decode(c, layer, q, dtype, out, batch, softmax_scale, p, matrix);
+    if (st != KVQ_OK) {
+        for (int b = 0; b < batch; ++b) len[b] -= 1;
+        return st;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    e = matrix ? launch_decode_mfma(p, s, c->ev[0], c->ev[1]) : launch_decode_vec(p, s, c->ev[0], c->ev[1]);
-    if (e == hipSuccess) e = launch_decode_merge(p, s);
+    if (matrix) {
+        p.fuse = 1;
+        p.append = qp;
+        e = launch_decode_mfma(p, s, c->ev[0], c->ev[1]);
+        if (e != hipSuccess) { // nothing was enqueued: the append did not happen
+            for (int b = 0; b < batch; ++b) len[b] -= 1;
+            return dev_fail(c, e);
+        }
+        e = launch_decode_merge(p, s);
+    } else {
+        e = launch_quantize(qp, s);
+        if (e == hipSuccess) e = launch_decode(c, p, false, s);
+    }
     if (e != hipSuccess) return dev_fail(c, e);
     return KVQ_OK;
 }

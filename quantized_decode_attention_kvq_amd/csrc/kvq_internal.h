@@ -61,6 +61,10 @@ struct DecodeParams {
     float qscale;             // softmax scale * log2(e)
     int split_tokens, n_splits, n_win_splits, n_splits_total; // window splits come last
     int len[kMaxBatch];
+    // Fused append (kvq_append_attn_decode, matrix path): when set, the workgroup whose split
+    // holds token len[b] - 1 of (b, kv head) first appends that token with `append` (T = 1).
+    int fuse;
+    QuantParams append;
 };
 
 struct CalibParams {

@@ -1,0 +1,347 @@
+// Device code of quantize-on-append, shared by the append kernel and the fused append + decode
+// kernel.  Every translation unit that includes it is compiled with -ffp-contract=off, so each
+// binary32 operation rounds separately, in the order written, and the packed codes and fp16
+// scales are bit-identical to any other implementation of the same format; fmaf() is used only
+// where the format fuses (the QJL projection).
+//
+// Method sources (pages by title and section):
+//  - quantcpp article "Beyond RAG...", progressive table + "how it works": 4-bit codes with fp16
+//    scale and zero per 32 channels (6.4x), newest 128 tokens kept in FP32.
+//  - KVarN-on-Bonsai post, TL;DR: Walsh-Hadamard transform and Sinkhorn variance balancing
+//    before 4-bit quantization.
+//  - "LLM memory saving ... 2026", TurboQuant row of the method table: random rotation,
+//    per-coordinate optimal scalar quantizer, 1-bit QJL of the residual.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace qdev {
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ float c0f() { return __uint_as_float(0x3DB504F3u); } // 2^-3.5
+
+__device__ __forceinline__ uint16_t f16_rn(float x) { return __half_as_ushort(__float2half_rn(x)); }
+__device__ __forceinline__ float f16_val(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+
+// Largest binary16 <= x: round to nearest, step down one binary16 ulp if that overshot.
+__device__ __forceinline__ uint16_t f16_rd(float x) {
+    uint16_t h = f16_rn(x);
+    if (f16_val(h) > x) {
+        if ((h & 0x7fff) == 0)
+            h = 0x8001;
+        else if (h & 0x8000)
+            h = (uint16_t)(h + 1);
+        else
+            h = (uint16_t)(h - 1);
+    }
+    return h;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Lane l loads channels 2l and 2l+1 of one 128-vector.
+__device__ __forceinline__ void load_pair(const void* base, size_t elem_off, int dtype, float& a,
+                                          float& b) {
+    const int l = lane_id();
+    if (dtype == 0) {
+        const float2 v = reinterpret_cast<const float2*>(
+            static_cast<const float*>(base) + elem_off)[l];
+        a = v.x;
+        b = v.y;
+    } else {
+        const uint32_t v = reinterpret_cast<const uint32_t*>(
+            static_cast<const uint16_t*>(base) + elem_off)[l];
+        a = bf16_to_f32((uint16_t)(v & 0xffff));
+        b = bf16_to_f32((uint16_t)(v >> 16));
+    }
+}
+
+// Sylvester-Hadamard butterflies over a wave (lane l holds elements 2l, 2l+1), spans
+// h = 1, 2, ..., 64 in ascending order; pair (i, i+h) with bit h of i clear maps to
+// (t_i + t_{i+h}, t_i - t_{i+h}).  The lane holding the upper element forms partner - own,
+// which is the same binary32 value as t_i - t_{i+h}.
+__device__ __forceinline__ void hadamard_wave(float& a, float& b) {
+    const int l = lane_id();
+    const float s = a + b, d = a - b;
+    a = s;
+    b = d;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float pa = __shfl_xor(a, m), pb = __shfl_xor(b, m);
+        const bool lower = (l & m) == 0;
+        a = lower ? (a + pa) : (pa - a);
+        b = lower ? (b + pb) : (pb - b);
+    }
+}
+
+// R(x) = c0 * H (d .* x).
+__device__ __forceinline__ void rotate_wave(float& a, float& b, const float* signs) {
+    const int l = lane_id();
+    if (signs[2 * l] < 0.0f) a = -a;
+    if (signs[2 * l + 1] < 0.0f) b = -b;
+    hadamard_wave(a, b);
+    a = a * c0f();
+    b = b * c0f();
+}
+
+// Index-order pairwise sum of v^2 over the 128 elements (level 1 inside the lane, then lane
+// pairs at distance 1, 2, ..., 32); every lane returns the total.
+__device__ __forceinline__ float tree_sum_sq(float a, float b) {
+    float t = a * a + b * b;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float o = __shfl_xor(t, m);
+        t = t + o;
+    }
+    return t;
+}
+
+__device__ __forceinline__ uint32_t or_reduce(uint32_t v, int width) {
+    for (int m = 1; m < width; m <<= 1) v |= (uint32_t)__shfl_xor((int)v, m);
+    return v;
+}
+
+// Half-interleave: bit e of x moves to bit 16*(e%2) + e/2 (even bits to the low half, odd bits
+// to the high half, order kept), by four swaps of bit fields.
+__device__ __forceinline__ uint32_t unshuffle32(uint32_t x) {
+    x = ((x & 0x22222222u) << 1) | ((x >> 1) & 0x22222222u) | (x & 0x99999999u);
+    x = ((x & 0x0C0C0C0Cu) << 2) | ((x >> 2) & 0x0C0C0C0Cu) | (x & 0xC3C3C3C3u);
+    x = ((x & 0x00F000F0u) << 4) | ((x >> 4) & 0x00F000F0u) | (x & 0xF00FF00Fu);
+    x = ((x & 0x0000FF00u) << 8) | ((x >> 8) & 0x0000FF00u) | (x & 0xFF0000FFu);
+    return x;
+}
+
+__device__ __forceinline__ int k_row(int t) { return 64 * (t / 64) + 16 * ((t % 64) % 4) + (t % 64) / 4; }
+
+// Uniform quantizer of the two elements a lane holds; the lane's group is lanes 16g..16g+15.
+__device__ __forceinline__ void quant_uniform(float a, float b, int bits, uint32_t& c0, uint32_t& c1,
+                                              uint16_t& s16, uint16_t& z16) {
+    float mn = fminf(a, b), mx = fmaxf(a, b);
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, m));
+        mx = fmaxf(mx, __shfl_xor(mx, m));
+    }
+    mn = mn + 0.0f;
+    mx = mx + 0.0f;
+    const float L = (float)((1 << bits) - 1);
+    z16 = f16_rd(mn);
+    const float z = f16_val(z16);
+    const float s32 = (mx - z) / L;
+    s16 = f16_rn(s32);
+    const float s = f16_val(s16);
+    const float inv = (s > 0.0f) ? 1.0f / s : 0.0f;
+    float u0 = (a - z) * inv, u1 = (b - z) * inv;
+    u0 = fminf(fmaxf(rintf(u0), 0.0f), L);
+    u1 = fminf(fmaxf(rintf(u1), 0.0f), L);
+    c0 = (uint32_t)u0;
+    c1 = (uint32_t)u1;
+}
+
+struct Unit {
+    int tensor, b, head, grp;
+};
+
+// Quantize-on-append of one wave's unit: the tokens of (tensor, sequence b, kv head, 8-token
+// octet `unit` counted from the octet of p.start[b]) that this call appends.  rbuf: 128 floats of
+// LDS owned by the wave (QJL residual staging).  Owning whole octets makes the V
+// read-modify-write race free.
+__device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, int b, int head,
+                                              int unit, float* rbuf) {
+    const int l = lane_id();
+    if (unit >= p.groups8) return;
+    const int start = p.start[b];
+    const int end = start + p.T;
+    const int g0 = start / 8 + unit;
+    const int t_lo = max(start, 8 * g0), t_hi = min(end, 8 * g0 + 8);
+    if (t_lo >= t_hi) return;
+
+    const PlaneGeom& G = p.geom[tensor];
+    char* slot = p.layer_base + (size_t)b * p.seq_stride + (size_t)head * p.head_stride +
+                 p.plane_off[tensor];
+    uint8_t* codes = reinterpret_cast<uint8_t*>(slot + G.codes_off);
+    uint8_t* meta = reinterpret_cast<uint8_t*>(slot + G.meta_off);
+    const float* signs = p.signs[tensor] ? p.signs[tensor] + (size_t)(head * 2 + tensor) * kDim : nullptr;
+    const float* inv_c = p.inv_c[tensor] ? p.inv_c[tensor] + (size_t)(head * 2 + tensor) * kDim : nullptr;
+
+    // V uniform accumulators for the group's packed words (channels 2l and 2l+1).
+    uint64_t vacc0 = 0, vacc1 = 0, vmask = 0;
+    // V turbo bit-plane words of channels 2l and 2l+1 for this octet, and the bits written.
+    uint32_t tv_a[3] = {0u, 0u, 0u}, tv_c[3] = {0u, 0u, 0u}, tv_mask = 0u;
+
+    for (int t = t_lo; t < t_hi; ++t) {
+        const size_t elem = (((size_t)b * p.T + (t - start)) * p.Hkv + head) * kDim;
+        float a, c;
+        load_pair(p.src[tensor], elem, p.dtype, a, c);
+
+        if (p.window > 0 && t >= end - p.window) {
+            float* ring = reinterpret_cast<float*>(slot + G.ring_off) + (size_t)(t % p.window) * kDim;
+            reinterpret_cast<float2*>(ring)[l] = make_float2(a, c);
+        }
+
+        if (G.scheme == kUniform) {
+            if (G.rotate) rotate_wave(a, c, signs);
+            if (G.sinkhorn) {
+                a = a * inv_c[2 * l];
+                c = c * inv_c[2 * l + 1];
+            }
+            uint32_t q0, q1;
+            uint16_t s16, z16;
+            quant_uniform(a, c, G.bits, q0, q1, s16, z16);
+            const int g = l >> 4;
+            if (tensor == 0) {
+                const int row = k_row(t);
+                uint8_t* r = codes + (size_t)row * (16 * G.bits);
+                const int kb = (l & 15) >> 2, i = 2 * (l & 3);
+                if (G.bits == 4) {
+                    uint32_t w = (q0 << (4 * (l & 3))) | (q1 << (16 + 4 * (l & 3)));
+                    w = or_reduce(w, 4);
+                    if ((l & 3) == 0) reinterpret_cast<uint32_t*>(r)[4 * kb + g] = w;
+                } else {
+                    *reinterpret_cast<uint16_t*>(r + 8 * (4 * kb + g) + i) = (uint16_t)(q0 | (q1 << 8));
+                }
+                if ((l & 15) == 0) {
+                    uint16_t* m = reinterpret_cast<uint16_t*>(meta + (size_t)row * 16);
+                    m[g] = s16;
+                    m[4 + g] = z16;
+                }
+            } else {
+                const int i = t % 8;
+                const int sh = (G.bits == 4) ? 16 * (i % 2) + 4 * (i / 2) : 8 * i;
+                vacc0 |= (uint64_t)q0 << sh;
+                vacc1 |= (uint64_t)q1 << sh;
+                vmask |= (uint64_t)((1u << G.bits) - 1) << sh;
+                if ((l & 15) == 0) {
+                    uint16_t* m = reinterpret_cast<uint16_t*>(meta + (size_t)t * 16);
+                    m[g] = s16;
+                    m[4 + g] = z16;
+                }
+            }
+        } else {
+            // TurboQuant code: rho = R(x); n = fp16(|rho|); codes = #thresholds below rho/n;
+            // residual r = rho - n mu[code]; QJL bits = sign(S r) with a sequential fma chain.
+            rotate_wave(a, c, signs);
+            const float nsq = tree_sum_sq(a, c);
+            const uint16_t n16 = f16_rn(sqrtf(nsq));
+            const float n = f16_val(n16);
+            const float inv = (n > 0.0f) ? 1.0f / n : 0.0f;
+            const float ua = a * inv, uc = c * inv;
+            uint32_t qa = 0, qc = 0;
+#pragma unroll
+            for (int k = 0; k < 7; ++k) {
+                const float th = p.theta[k];
+                qa += (ua > th) ? 1u : 0u;
+                qc += (uc > th) ? 1u : 0u;
+            }
+            const float pa = n * p.mu[qa], pc = n * p.mu[qc];
+            const float ra = a - pa, rc = c - pc;
+            if (tensor == 0) {
+                // K row: bit planes of group g (lanes 16g..16g+15 hold its channels 2lg, 2lg+1,
+                // i.e. half-interleaved values lg and 16 + lg)
+                const int lg = l & 15, g = l >> 4;
+                const int row = k_row(t);
+                uint32_t pw[3];
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    pw[k] = or_reduce((((qa >> k) & 1u) << lg) | (((qc >> k) & 1u) << (16 + lg)), 16);
+                if (lg == 0) {
+                    uint32_t* w = reinterpret_cast<uint32_t*>(codes + (size_t)row * 48 + 12 * g);
+                    w[0] = pw[0];
+                    w[1] = pw[1];
+                    w[2] = pw[2];
+                }
+                if (G.scheme == kTurboQjl) {
+                    const uint16_t g16 = f16_rn(sqrtf(tree_sum_sq(ra, rc)));
+                    rbuf[2 * l] = ra;
+                    rbuf[2 * l + 1] = rc;
+                    __builtin_amdgcn_wave_barrier();
+                    float acc0 = 0.0f, acc1 = 0.0f;
+                    for (int j = 0; j < kDim; ++j) {
+                        const float rj = rbuf[j];
+                        acc0 = fmaf(p.qjl_st[j * kDim + l], rj, acc0);
+                        acc1 = fmaf(p.qjl_st[j * kDim + 64 + l], rj, acc1);
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                    const uint64_t b0 = __ballot(acc0 >= 0.0f);
+                    const uint64_t b1 = __ballot(acc1 >= 0.0f);
+                    if (l == 0) {
+                        uint32_t* qj = reinterpret_cast<uint32_t*>(slot + G.qjl_off + (size_t)row * 16);
+                        qj[0] = unshuffle32((uint32_t)b0);
+                        qj[1] = unshuffle32((uint32_t)(b0 >> 32));
+                        qj[2] = unshuffle32((uint32_t)b1);
+                        qj[3] = unshuffle32((uint32_t)(b1 >> 32));
+                        uint16_t* m = reinterpret_cast<uint16_t*>(meta + (size_t)row * 4);
+                        m[0] = n16;
+                        m[1] = g16;
+                    }
+                } else if (l == 0) {
+                    reinterpret_cast<uint16_t*>(meta)[row] = n16;
+                }
+            } else {
+                // V block: bit k of channel 2l (2l+1) goes to word 6(16 o + n) + 2k + N/4 with
+                // n = 2(l%8) (+1), N = l/8; token i of the octet at bit 16(i%2) + 4(N%4) + i/2
+                const int i = t % 8, N = l >> 3;
+                const uint32_t pos = 1u << (16 * (i & 1) + 4 * (N & 3) + (i >> 1));
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    tv_a[k] |= ((qa >> k) & 1u) ? pos : 0u;
+                    tv_c[k] |= ((qc >> k) & 1u) ? pos : 0u;
+                }
+                tv_mask |= pos;
+                if (l == 0) reinterpret_cast<uint16_t*>(meta)[t] = n16;
+            }
+        }
+    }
+
+    if (tensor == 1 && G.scheme != kUniform) {
+        // merge the four lanes (l ^ 8, l ^ 16) whose channels share each word, then
+        // read-modify-write this octet's words
+        uint32_t m = tv_mask;
+        m |= (uint32_t)__shfl_xor((int)m, 8);
+        m |= (uint32_t)__shfl_xor((int)m, 16);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            tv_a[k] |= (uint32_t)__shfl_xor((int)tv_a[k], 8);
+            tv_a[k] |= (uint32_t)__shfl_xor((int)tv_a[k], 16);
+            tv_c[k] |= (uint32_t)__shfl_xor((int)tv_c[k], 8);
+            tv_c[k] |= (uint32_t)__shfl_xor((int)tv_c[k], 16);
+        }
+        if (((l >> 3) & 3) == 0) {
+            const int o = (t_lo % 32) / 8, n0 = 2 * (l & 7), N = l >> 3;
+            uint32_t* blk = reinterpret_cast<uint32_t*>(codes + (size_t)(t_lo / 32) * 1536);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                uint32_t* wa = blk + 6 * (16 * o + n0) + 2 * k + (N >> 2);
+                uint32_t* wc = wa + 6;
+                *wa = (*wa & ~m) | tv_a[k];
+                *wc = (*wc & ~m) | tv_c[k];
+            }
+        }
+    }
+
+    if (tensor == 1 && G.scheme == kUniform) {
+        // read-modify-write the packed words of channels 2l, 2l+1 for this 8-token group
+        const int blk = t_lo / 32, kb = (t_lo % 32) / 8;
+        const int d0 = 2 * l, n0 = d0 % 16, N = d0 / 16;
+        const int w0 = 8 * (16 * kb + n0) + N, w1 = w0 + 8;
+        if (G.bits == 4) {
+            uint32_t* bp = reinterpret_cast<uint32_t*>(codes + (size_t)blk * 2048);
+            const uint32_t m = (uint32_t)vmask;
+            bp[w0] = (bp[w0] & ~m) | (uint32_t)vacc0;
+            bp[w1] = (bp[w1] & ~m) | (uint32_t)vacc1;
+        } else {
+            uint64_t* bp = reinterpret_cast<uint64_t*>(codes + (size_t)blk * 4096);
+            bp[w0] = (bp[w0] & ~vmask) | vacc0;
+            bp[w1] = (bp[w1] & ~vmask) | vacc1;
+        }
+    }
+}
+
+
+} // namespace qdev
+} // namespace kvq

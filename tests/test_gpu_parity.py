@@ -231,3 +231,64 @@ def test_empty_and_single_token(path):
         ref = pv.dequant(0, tv)
         for g in range(3):
             assert rel_l2(out[0, 3 * h + g].cpu().numpy(), ref) < 1e-5
+
+
+def _planes_equal(a, b, li, batch, n_heads):
+    for s in range(batch):
+        for h in range(n_heads):
+            for t in (0, 1):
+                for x, y in zip(a.device_plane(li, s, h, t), b.device_plane(li, s, h, t)):
+                    if x is not None:
+                        assert np.array_equal(x, y), (s, h, t)
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("wl,n", [(W.LLAMA3B_3970_PROGRESSIVE, 1000), (W.LLAMA3B_3970_PROGRESSIVE, 0),
+                                  (W.LLAMA3B_32K_KVARN, 1023), (W.LLAMA3B_32K_TURBO, 700),
+                                  (W.LLAMA3B_32K_TURBO_ASYM, 64), (W.DENSE27B_120K_KVARN, 500)],
+                         ids=lambda x: x.name if hasattr(x, "name") else str(x))
+def test_fused_append_decode_equals_separate_calls(wl, n, path):
+    # kvq_append_attn_decode == kvq_append + kvq_attn_decode: byte-identical planes and
+    # bit-identical outputs over consecutive steps, with ragged lengths in the batch
+    _say("case: fused append+decode", wl.name, "n", n, "path", path)
+    B = 2
+    a = Case(wl, max(n, 1), layers=[0], batch=B, extra_tokens=8)
+    b = Case(wl, max(n, 1), layers=[0], batch=B, extra_tokens=8)
+    for c in (a, b):
+        c.cache.set_option(2, path)
+        if n > 0:
+            c.prefill(0)
+    k0, v0 = W.gen_step_kv(wl, 0, 99, batch=1)
+    for c in (a, b):  # sequence 0 one token longer than sequence 1
+        c.cache.append(0, k0.to("cuda"), v0.to("cuda"))
+    for step in range(3):
+        k, v = W.gen_step_kv(wl, 0, step, batch=B)
+        q = W.gen_q(wl, 0, step, batch=B).to("cuda")
+        k, v = k.to("cuda"), v.to("cuda")
+        oa = torch.full((B, wl.n_q_heads, 128), float("nan"), device="cuda")
+        ob = torch.full_like(oa, float("nan"))
+        a.cache.append(0, k, v)
+        a.cache.attn_decode(0, q, oa)
+        b.cache.append_attn_decode(0, k, v, q, ob)
+        torch.cuda.synchronize()
+        assert a.cache.length(0, 0) == b.cache.length(0, 0) == n + 2 + step
+        assert torch.equal(oa, ob), step
+        _planes_equal(a, b, 0, B, wl.n_kv_heads)
+
+
+def test_fused_append_decode_matches_oracle():
+    wl = W.LLAMA3B_3970_PROGRESSIVE
+    _say("case: fused append+decode vs oracle", wl.name)
+    n = 777
+    case = Case(wl, n + 1, layers=[0])
+    k_all, v_all = case.kv(0)
+    case.cache.prefill_quantize(0, k_all[:, :n].contiguous(), v_all[:, :n].contiguous())
+    q = W.gen_q(wl, 0, 5).to("cuda")
+    out = torch.empty((1, wl.n_q_heads, 128), device="cuda")
+    case.cache.append_attn_decode(0, k_all[:, n].contiguous(), v_all[:, n].contiguous(), q, out)
+    torch.cuda.synchronize()
+    planes = _check_all_planes(case, 0)
+    ref = oracle_attention_case(case, 0, 0, q.float().cpu().numpy()[0],
+                                planes={h: planes[(0, h)] for h in range(wl.n_kv_heads)})
+    got = out.cpu().numpy()[0]
+    assert rel_l2(got, ref) <= REL_L2_TOL and max_abs(got, ref) <= MAX_ABS_TOL
