@@ -298,9 +298,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     const int tok_end = wsplit ? tok_begin : min(nq, tok_begin + p.split_tokens);
     const int nch = (tok_end > tok_begin) ? (tok_end - tok_begin + 63) / 64 : 0;
 
-    KRegs<KT> kr;
-    VRegs<VT> vr;
-    auto load_k = [&](int ci) {
+    // kBuf register sets per wave: with 4 waves (one per SIMD) each wave keeps two chunks in
+    // flight (uniform K; TurboQuant K has no registers to spare); with 8 waves, two waves share
+    // a SIMD and each keeps one
+    constexpr int kBuf = (kNW == 4 && KU) ? 2 : 1;
+    KRegs<KT> krs[kBuf];
+    VRegs<VT> vrs[kBuf];
+    auto load_k = [&](KRegs<KT>& kr, int ci) {
         const size_t r0 = (size_t)tok_begin + 64 * ci + lr; // row of sub-tile 0
         if constexpr (KU) {
 #pragma unroll
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             }
         }
     };
-    auto load_v = [&](int ci) {
+    auto load_v = [&](VRegs<VT>& vr, int ci) {
         const size_t t0 = (size_t)tok_begin + 64 * ci;
         if constexpr (VU) {
             const uint8_t* c = vcodes + (t0 / 32) * (512 * VB) + (size_t)(32 * VB / 4) * l;
@@ -345,8 +349,12 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     // The wave's first chunk is requested right away; each later chunk is requested as soon as
     // the registers it goes into have been consumed (K after the scores, V after PV).
     if (wave < nch) {
-        load_k(wave);
-        load_v(wave);
+        load_k(krs[0], wave);
+        load_v(vrs[0], wave);
+    }
+    if (kBuf == 2 && wave + kNW < nch) {
+        load_k(krs[kBuf - 1], wave + kNW);
+        load_v(vrs[kBuf - 1], wave + kNW);
     }
 
     // ---------------- query preparation (once per workgroup) ----------------
@@ -509,9 +517,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             }
         }
 
-        for (int ci = wave; ci < nch; ci += kNW) {
+        auto chunk = [&](KRegs<KT>& kr, VRegs<VT>& vr, int ci) __attribute__((always_inline)) {
             const int c0 = tok_begin + 64 * ci;
-            const int nci = ci + kNW; // the chunk the registers are refilled with
+            const int nci = ci + kBuf * kNW; // the chunk these registers are refilled with
             const bool more = nci < nch;
 
             // ---- scores
@@ -586,7 +594,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             }
 
             // the next chunk's K is requested as soon as this chunk's scores are formed
-            if (more) load_k(nci);
+            if (more) load_k(kr, nci);
 
             // ---- online softmax
             float pj[MB][4], alpha[MB];
@@ -710,7 +718,11 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             }
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            if (more) load_v(nci);
+            if (more) load_v(vr, nci);
+        };
+        for (int ci = wave; ci < nch; ci += kBuf * kNW) {
+            chunk(krs[0], vrs[0], ci);
+            if (kBuf == 2 && ci + kNW < nch) chunk(krs[kBuf - 1], vrs[kBuf - 1], ci + kNW);
         }
         // reduce the per-lane softmax sums over each row of 16 lanes
 #pragma unroll
