@@ -100,6 +100,19 @@ def traffic_record(wl: W.Workload):
     return None
 
 
+def prefill_report(wl: W.Workload, prefill_s):
+    """Bulk kvq_prefill_quantize of the whole context, one call per layer (HIP events around
+    each call on the launch stream): source bytes read + packed bytes written per second."""
+    n, B = wl.context, wl.batch
+    src = B * n * wl.n_kv_heads * 128 * 2 * (2 if wl.dtype == "bf16" else 4)
+    per = token_head_bytes(wl.k_scheme, wl.k_bits) + token_head_bytes(wl.v_scheme, wl.v_bits)
+    packed = B * wl.n_kv_heads * (n * per + min(n, wl.window) * 2 * 512)
+    t = float(np.mean(prefill_s))
+    return {"tokens_per_call": B * n, "calls": len(prefill_s), "us_per_call": 1e6 * t,
+            "tokens_per_s": B * n / t, "bytes_per_call": src + packed,
+            "achieved_GBps": (src + packed) / t / 1e9}
+
+
 def split_kernel_name(wl: W.Workload) -> str:
     """The split-K decode kernel the library launches for this cache (matrix-core path)."""
     kind = lambda scheme, bits: "Tb" if scheme != W.UNIFORM else f"U{bits}"  # noqa: E731
@@ -115,20 +128,27 @@ def build_cache(wl: W.Workload, extra: int, log):
     S = torch.from_numpy(W.qjl_projection(wl)).cuda()
     cache.set_random_tables(signs, S)
     keep = None
+    stream = torch.cuda.current_stream()
+    pre = []  # (start, end) events around each layer's bulk prefill on the launch stream
     for layer in range(wl.n_layers):
         if wl.sinkhorn_iters > 0:
             cache.calibrate(layer, W.gen_calib(wl, layer, 0, device="cuda"),
                             W.gen_calib(wl, layer, 1, device="cuda"))
         k = W.gen_kv(wl, layer, 0, device="cuda")
         v = W.gen_kv(wl, layer, 1, device="cuda")
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        ev[0].record(stream)
         cache.prefill_quantize(layer, k, v)
+        ev[1].record(stream)
+        pre.append(ev)
         if layer == 0:
             keep = (k[:1].cpu(), v[:1].cpu())
         del k, v
         if layer % 8 == 7:
             log(f"prefilled {layer + 1}/{wl.n_layers} layers")
     torch.cuda.synchronize()
-    return cache, keep
+    prefill_s = np.array([a.elapsed_time(b) for a, b in pre]) / 1e3
+    return cache, keep, prefill_s
 
 
 def cpu_baseline(wl: W.Workload, kv0, budget_s: float):
@@ -220,7 +240,7 @@ def main():
     torch.cuda.init()
     log(f"workload {wl.name}: building cache")
     t_build = time.perf_counter()
-    cache, kv0 = build_cache(wl, args.warmup + 2 * args.steps, log)
+    cache, kv0, prefill_s = build_cache(wl, args.warmup + 2 * args.steps, log)
     log(f"cache built in {time.perf_counter() - t_build:.1f} s")
 
     L, B = wl.n_layers, wl.batch
@@ -287,6 +307,7 @@ def main():
                      "p90_us": 1e6 * float(np.percentile(split, 90)),
                      "layer_step_us": 1e6 * elapsed / (args.steps * L)},
         "wall_s": wall,
+        "prefill": prefill_report(wl, prefill_s),
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")

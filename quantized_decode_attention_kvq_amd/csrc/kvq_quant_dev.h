@@ -89,6 +89,15 @@ __device__ __forceinline__ void rotate_wave(float& a, float& b, const float* sig
     b = b * c0f();
 }
 
+// R(x) = c0 * H (d .* x) with the lane's two signs already loaded.
+__device__ __forceinline__ void rotate_signed(float& a, float& b, float s0, float s1) {
+    if (s0 < 0.0f) a = -a;
+    if (s1 < 0.0f) b = -b;
+    hadamard_wave(a, b);
+    a = a * c0f();
+    b = b * c0f();
+}
+
 // Index-order pairwise sum of v^2 over the 128 elements (level 1 inside the lane, then lane
 // pairs at distance 1, 2, ..., 32); every lane returns the total.
 __device__ __forceinline__ float tree_sum_sq(float a, float b) {
@@ -174,10 +183,34 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
     // V turbo bit-plane words of channels 2l and 2l+1 for this octet, and the bits written.
     uint32_t tv_a[3] = {0u, 0u, 0u}, tv_c[3] = {0u, 0u, 0u}, tv_mask = 0u;
 
-    for (int t = t_lo; t < t_hi; ++t) {
-        const size_t elem = (((size_t)b * p.T + (t - start)) * p.Hkv + head) * kDim;
-        float a, c;
-        load_pair(p.src[tensor], elem, p.dtype, a, c);
+    // all of the octet's source values are requested before the first is used, so a wave pays
+    // one memory round trip instead of one per token
+    float pa[8], pc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        pa[i] = pc[i] = 0.0f;
+        if (t_lo + i < t_hi) {
+            const size_t elem = (((size_t)b * p.T + (t_lo + i - start)) * p.Hkv + head) * kDim;
+            load_pair(p.src[tensor], elem, p.dtype, pa[i], pc[i]);
+        }
+    }
+    const float* sg_l = signs ? signs + 2 * l : nullptr;
+    const float* ic_l = inv_c ? inv_c + 2 * l : nullptr;
+    float sg0 = 1.0f, sg1 = 1.0f, ic0 = 1.0f, ic1 = 1.0f;
+    if (sg_l) {
+        sg0 = sg_l[0];
+        sg1 = sg_l[1];
+    }
+    if (G.scheme == kUniform && G.sinkhorn) {
+        ic0 = ic_l[0];
+        ic1 = ic_l[1];
+    }
+
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = t_lo + i;
+        if (t >= t_hi) break;
+        float a = pa[i], c = pc[i];
 
         if (p.window > 0 && t >= end - p.window) {
             float* ring = reinterpret_cast<float*>(slot + G.ring_off) + (size_t)(t % p.window) * kDim;
@@ -185,10 +218,10 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
         }
 
         if (G.scheme == kUniform) {
-            if (G.rotate) rotate_wave(a, c, signs);
+            if (G.rotate) rotate_signed(a, c, sg0, sg1);
             if (G.sinkhorn) {
-                a = a * inv_c[2 * l];
-                c = c * inv_c[2 * l + 1];
+                a = a * ic0;
+                c = c * ic1;
             }
             uint32_t q0, q1;
             uint16_t s16, z16;
@@ -225,7 +258,7 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
         } else {
             // TurboQuant code: rho = R(x); n = fp16(|rho|); codes = #thresholds below rho/n;
             // residual r = rho - n mu[code]; QJL bits = sign(S r) with a sequential fma chain.
-            rotate_wave(a, c, signs);
+            rotate_signed(a, c, sg0, sg1);
             const float nsq = tree_sum_sq(a, c);
             const uint16_t n16 = f16_rn(sqrtf(nsq));
             const float n = f16_val(n16);
