@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kvq_internal.h"
+#include "kvq_lanes.h"
 
 namespace kvq {
 namespace {
@@ -27,28 +28,30 @@ __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
+    return xor_reduce<64>(v, [](float x, float y) { return fmaxf(x, y); });
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
-    return v;
+    return xor_reduce<64>(v, [](float x, float y) { return x + y; });
 }
 
+template <int M>
+__device__ __forceinline__ void hadamard_step(float& a, float& b, int l) {
+    const float pa = xor_lane<M>(a), pb = xor_lane<M>(b);
+    const bool lower = (l & M) == 0;
+    a = lower ? (a + pa) : (pa - a);
+    b = lower ? (b + pb) : (pb - b);
+}
 __device__ __forceinline__ void hadamard_wave(float& a, float& b) {
     const int l = lane_id();
     const float s = a + b, d = a - b;
     a = s;
     b = d;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const float pa = __shfl_xor(a, m), pb = __shfl_xor(b, m);
-        const bool lower = (l & m) == 0;
-        a = lower ? (a + pa) : (pa - a);
-        b = lower ? (b + pb) : (pb - b);
-    }
+    hadamard_step<1>(a, b, l);
+    hadamard_step<2>(a, b, l);
+    hadamard_step<4>(a, b, l);
+    hadamard_step<8>(a, b, l);
+    hadamard_step<16>(a, b, l);
+    hadamard_step<32>(a, b, l);
 }
 
 __device__ __forceinline__ int k_row(int t) { return 64 * (t / 64) + 16 * ((t % 64) % 4) + (t % 64) / 4; }
@@ -452,13 +455,19 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
                     q[j] = x + y;
                     q[j + h] = x - y;
                 }
-        for (int h = 1; h < 32; h <<= 1) {
+        auto stage = [&](auto hc) {
+            constexpr int h = decltype(hc)::value;
             const bool upper = (c4 & h) != 0;
             for (int j = 0; j < 4; ++j) {
-                const float o = __shfl_xor(q[j], h, 64);
+                const float o = xor_lane<h>(q[j]);
                 q[j] = upper ? o - q[j] : q[j] + o;
             }
-        }
+        };
+        stage(std::integral_constant<int, 1>{});
+        stage(std::integral_constant<int, 2>{});
+        stage(std::integral_constant<int, 4>{});
+        stage(std::integral_constant<int, 8>{});
+        stage(std::integral_constant<int, 16>{});
         for (int j = 0; j < 4; ++j) {
             q[j] *= c0f();
             if (p.signs[tab + j] < 0.0f) q[j] = -q[j];

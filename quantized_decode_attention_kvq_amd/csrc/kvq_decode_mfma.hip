@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kvq_internal.h"
+#include "kvq_lanes.h"
 #include "kvq_quant_dev.h"
 
 namespace kvq {
@@ -159,28 +160,13 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
+    return xor_reduce<64>(v, [](float x, float y) { return fmaxf(x, y); });
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
-    return v;
+    return xor_reduce<64>(v, [](float x, float y) { return x + y; });
 }
 
-__device__ __forceinline__ void hadamard_wave(float& a, float& b, int l) {
-    const float s = a + b, d = a - b;
-    a = s;
-    b = d;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const float pa = __shfl_xor(a, m), pb = __shfl_xor(b, m);
-        const bool lower = (l & m) == 0;
-        a = lower ? (a + pa) : (pa - a);
-        b = lower ? (b + pb) : (pb - b);
-    }
-}
+__device__ __forceinline__ void hadamard_wave(float& a, float& b, int) { qdev::hadamard_wave(a, b); }
 
 __device__ __forceinline__ float readlane_f(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));

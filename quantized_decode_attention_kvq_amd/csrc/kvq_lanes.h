@@ -1,0 +1,50 @@
+// Cross-lane exchange within a 64-lane wavefront on gfx950: lane l receives the value of lane
+// l ^ M.  Same result as __shfl_xor(v, M), but without the LDS address round trip for M = 1, 2, 8
+// (DPP quad_perm [1,0,3,2] / [2,3,0,1], row_ror:8 over rows of 16 lanes) and M = 32
+// (v_permlane32_swap), and as a single ds_swizzle (xor mask inside 32 lanes) for M = 4, 16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace kvq {
+
+template <int M>
+__device__ __forceinline__ int xor_lane_i(int x) {
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "xor distance");
+    if constexpr (M == 1) {
+        return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false);
+    } else if constexpr (M == 2) {
+        return __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false);
+    } else if constexpr (M == 8) {
+        return __builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false);
+    } else if constexpr (M == 4 || M == 16) {
+        return __builtin_amdgcn_ds_swizzle(x, 0x1F | (M << 10));
+    } else {
+        const auto pr = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (__lane_id() < 32) ? (int)pr[1] : (int)pr[0];
+    }
+}
+
+template <int M>
+__device__ __forceinline__ float xor_lane(float v) {
+    return __int_as_float(xor_lane_i<M>(__float_as_int(v)));
+}
+
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+    return (uint32_t)xor_lane_i<M>((int)v);
+}
+
+// Butterfly over the xor distances 1, 2, ..., W/2 (ascending): v = op(v, partner) each step.
+template <int W, typename T, typename Op>
+__device__ __forceinline__ T xor_reduce(T v, Op op) {
+    if constexpr (W > 1) v = op(v, xor_lane<1>(v));
+    if constexpr (W > 2) v = op(v, xor_lane<2>(v));
+    if constexpr (W > 4) v = op(v, xor_lane<4>(v));
+    if constexpr (W > 8) v = op(v, xor_lane<8>(v));
+    if constexpr (W > 16) v = op(v, xor_lane<16>(v));
+    if constexpr (W > 32) v = op(v, xor_lane<32>(v));
+    return v;
+}
+
+} // namespace kvq

@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kvq_internal.h"
+#include "kvq_lanes.h"
 
 namespace kvq {
 namespace qdev {
@@ -65,18 +66,24 @@ __device__ __forceinline__ void load_pair(const void* base, size_t elem_off, int
 // h = 1, 2, ..., 64 in ascending order; pair (i, i+h) with bit h of i clear maps to
 // (t_i + t_{i+h}, t_i - t_{i+h}).  The lane holding the upper element forms partner - own,
 // which is the same binary32 value as t_i - t_{i+h}.
+template <int M>
+__device__ __forceinline__ void hadamard_step(float& a, float& b, int l) {
+    const float pa = xor_lane<M>(a), pb = xor_lane<M>(b);
+    const bool lower = (l & M) == 0;
+    a = lower ? (a + pa) : (pa - a);
+    b = lower ? (b + pb) : (pb - b);
+}
 __device__ __forceinline__ void hadamard_wave(float& a, float& b) {
     const int l = lane_id();
     const float s = a + b, d = a - b;
     a = s;
     b = d;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const float pa = __shfl_xor(a, m), pb = __shfl_xor(b, m);
-        const bool lower = (l & m) == 0;
-        a = lower ? (a + pa) : (pa - a);
-        b = lower ? (b + pb) : (pb - b);
-    }
+    hadamard_step<1>(a, b, l);
+    hadamard_step<2>(a, b, l);
+    hadamard_step<4>(a, b, l);
+    hadamard_step<8>(a, b, l);
+    hadamard_step<16>(a, b, l);
+    hadamard_step<32>(a, b, l);
 }
 
 // R(x) = c0 * H (d .* x).
@@ -101,18 +108,13 @@ __device__ __forceinline__ void rotate_signed(float& a, float& b, float s0, floa
 // Index-order pairwise sum of v^2 over the 128 elements (level 1 inside the lane, then lane
 // pairs at distance 1, 2, ..., 32); every lane returns the total.
 __device__ __forceinline__ float tree_sum_sq(float a, float b) {
-    float t = a * a + b * b;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const float o = __shfl_xor(t, m);
-        t = t + o;
-    }
-    return t;
+    const float t = a * a + b * b;
+    return xor_reduce<64>(t, [](float x, float y) { return x + y; });
 }
 
-__device__ __forceinline__ uint32_t or_reduce(uint32_t v, int width) {
-    for (int m = 1; m < width; m <<= 1) v |= (uint32_t)__shfl_xor((int)v, m);
-    return v;
+template <int W>
+__device__ __forceinline__ uint32_t or_reduce(uint32_t v) {
+    return xor_reduce<W>(v, [](uint32_t x, uint32_t y) { return x | y; });
 }
 
 // Half-interleave: bit e of x moves to bit 16*(e%2) + e/2 (even bits to the low half, odd bits
@@ -131,11 +133,8 @@ __device__ __forceinline__ int k_row(int t) { return 64 * (t / 64) + 16 * ((t % 
 __device__ __forceinline__ void quant_uniform(float a, float b, int bits, uint32_t& c0, uint32_t& c1,
                                               uint16_t& s16, uint16_t& z16) {
     float mn = fminf(a, b), mx = fmaxf(a, b);
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, m));
-        mx = fmaxf(mx, __shfl_xor(mx, m));
-    }
+    mn = xor_reduce<16>(mn, [](float x, float y) { return fminf(x, y); });
+    mx = xor_reduce<16>(mx, [](float x, float y) { return fmaxf(x, y); });
     mn = mn + 0.0f;
     mx = mx + 0.0f;
     const float L = (float)((1 << bits) - 1);
@@ -233,7 +232,7 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
                 const int kb = (l & 15) >> 2, i = 2 * (l & 3);
                 if (G.bits == 4) {
                     uint32_t w = (q0 << (4 * (l & 3))) | (q1 << (16 + 4 * (l & 3)));
-                    w = or_reduce(w, 4);
+                    w = or_reduce<4>(w);
                     if ((l & 3) == 0) reinterpret_cast<uint32_t*>(r)[4 * kb + g] = w;
                 } else {
                     *reinterpret_cast<uint16_t*>(r + 8 * (4 * kb + g) + i) = (uint16_t)(q0 | (q1 << 8));
@@ -281,7 +280,7 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
                 uint32_t pw[3];
 #pragma unroll
                 for (int k = 0; k < 3; ++k)
-                    pw[k] = or_reduce((((qa >> k) & 1u) << lg) | (((qc >> k) & 1u) << (16 + lg)), 16);
+                    pw[k] = or_reduce<16>((((qa >> k) & 1u) << lg) | (((qc >> k) & 1u) << (16 + lg)));
                 if (lg == 0) {
                     uint32_t* w = reinterpret_cast<uint32_t*>(codes + (size_t)row * 48 + 12 * g);
                     w[0] = pw[0];
@@ -335,14 +334,14 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
         // merge the four lanes (l ^ 8, l ^ 16) whose channels share each word, then
         // read-modify-write this octet's words
         uint32_t m = tv_mask;
-        m |= (uint32_t)__shfl_xor((int)m, 8);
-        m |= (uint32_t)__shfl_xor((int)m, 16);
+        m |= xor_lane<8>(m);
+        m |= xor_lane<16>(m);
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-            tv_a[k] |= (uint32_t)__shfl_xor((int)tv_a[k], 8);
-            tv_a[k] |= (uint32_t)__shfl_xor((int)tv_a[k], 16);
-            tv_c[k] |= (uint32_t)__shfl_xor((int)tv_c[k], 8);
-            tv_c[k] |= (uint32_t)__shfl_xor((int)tv_c[k], 16);
+            tv_a[k] |= xor_lane<8>(tv_a[k]);
+            tv_a[k] |= xor_lane<16>(tv_a[k]);
+            tv_c[k] |= xor_lane<8>(tv_c[k]);
+            tv_c[k] |= xor_lane<16>(tv_c[k]);
         }
         if (((l >> 3) & 3) == 0) {
             const int o = (t_lo % 32) / 8, n0 = 2 * (l & 7), N = l >> 3;
