@@ -425,7 +425,8 @@ kvq_status kvq_prefill_quantize(kvq_cache* c, int layer, const void* K, const vo
     QuantParams p;
     const kvq_status st = make_quant(c, layer, K, V, dtype, n_tokens, batch, p);
     if (st != KVQ_OK || n_tokens == 0) return st;
-    const hipError_t e = launch_quantize(p, static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = n_tokens >= kQuantBulkMinTokens ? launch_quantize_bulk(p, s) : launch_quantize(p, s);
     if (e != hipSuccess) return dev_fail(c, e);
     int* len = &c->len[(size_t)layer * c->cfg.max_batch];
     for (int b = 0; b < batch; ++b) len[b] += n_tokens;

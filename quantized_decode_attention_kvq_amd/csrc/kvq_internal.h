@@ -79,6 +79,12 @@ struct CalibParams {
 
 // Launchers (defined in the .hip files); return the launch's hipError_t.
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
+// Lane-dense quantizer for many tokens per call (same bytes as launch_quantize).
+hipError_t launch_quantize_bulk(const QuantParams& p, hipStream_t s);
+// Workgroups the bulk quantizer spreads TurboQuant-QJL K planes over (about two per CU).
+constexpr int kQuantBulkQjlBlocks = 512;
+// Smallest append the bulk quantizer takes.
+constexpr int kQuantBulkMinTokens = 16;
 hipError_t launch_calibrate(const CalibParams& p, hipStream_t s);
 hipError_t launch_codebook(float* mu, float* theta, int iters, hipStream_t s);
 hipError_t launch_transpose128(const float* in, float* out, hipStream_t s);

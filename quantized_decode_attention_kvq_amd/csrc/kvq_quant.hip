@@ -11,6 +11,8 @@
 //    before 4-bit quantization.
 //  - "LLM memory saving ... 2026", TurboQuant row of the method table: random rotation,
 //    per-coordinate optimal scalar quantizer, 1-bit QJL of the residual.
+#include <algorithm>
+
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -32,6 +34,26 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
     __shared__ float rbuf[4][kDim];
     const int wave = threadIdx.x >> 6;
     qdev::quantize_wave(p, blockIdx.z & 1, blockIdx.z >> 1, blockIdx.y, blockIdx.x * 4 + wave, rbuf[wave]);
+}
+
+// Bulk quantizer: wave w of workgroup x takes octets 4x + w, then every 4 * gridDim.x-th after
+// it, of one (tensor, sequence, kv head).  kQjl: the tensor is a TurboQuant-QJL K plane, and the
+// workgroup first stages S^T (64 KiB) in LDS for all of its octets.
+template <bool kQjl>
+__global__ __launch_bounds__(256) void quantize_bulk_kernel(QuantParams p, int tensor0, int n_tensors) {
+    constexpr int kWaveFloats = kQjl ? qdev::kBulkWaveLds / 4 : 8 * kDim / 4;
+    __shared__ __align__(16) float wl[4][kWaveFloats];
+    __shared__ __align__(16) float st[kQjl ? kDim * kDim : 4];
+    const int tensor = tensor0 + (int)blockIdx.z % n_tensors, b = (int)blockIdx.z / n_tensors;
+    if constexpr (kQjl) {
+        const float4* src = reinterpret_cast<const float4*>(p.qjl_st);
+        float4* dst = reinterpret_cast<float4*>(st);
+        for (int i = threadIdx.x; i < kDim * kDim / 4; i += blockDim.x) dst[i] = src[i];
+        __syncthreads();
+    }
+    const int wave = threadIdx.x >> 6;
+    for (int u = blockIdx.x * 4 + wave; u < p.groups8; u += gridDim.x * 4)
+        qdev::quantize_octet_dense(p, tensor, b, blockIdx.y, u, wl[wave], st);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -173,6 +195,24 @@ __global__ void transpose128_kernel(const float* in, float* out) {
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
     dim3 grid((p.groups8 + 3) / 4, p.Hkv, 2 * p.batch);
     hipLaunchKernelGGL(quantize_kernel, grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_bulk(const QuantParams& p, hipStream_t s) {
+    const int gx = (p.groups8 + 3) / 4;
+    if (p.geom[0].scheme != kTurboQjl) {
+        hipLaunchKernelGGL(quantize_bulk_kernel<false>, dim3(gx, p.Hkv, 2 * p.batch), dim3(256), 0, s,
+                           p, 0, 2);
+        return hipGetLastError();
+    }
+    // QJL K planes: about two workgroups per compute unit (LDS holds two), each staging S^T once
+    // and looping over its share of the octets
+    const int planes = p.Hkv * p.batch;
+    const int gq = std::max(1, std::min(gx, (kQuantBulkQjlBlocks + planes - 1) / planes));
+    hipLaunchKernelGGL(quantize_bulk_kernel<true>, dim3(gq, p.Hkv, p.batch), dim3(256), 0, s, p, 0, 1);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(quantize_bulk_kernel<false>, dim3(gx, p.Hkv, p.batch), dim3(256), 0, s, p, 1, 1);
     return hipGetLastError();
 }
 
