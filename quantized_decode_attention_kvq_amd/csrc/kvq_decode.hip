@@ -387,12 +387,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     const float* base = p.partials + ((size_t)b * p.Hq + hq) * p.n_splits_total * kPartialFloats;
     float m = kNegInf, l = 0.0f;
     float4 aq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), aw = aq;
-    // four splits per thread per round, all loads issued before any is used
-    for (int s0 = part; s0 < p.n_splits_total; s0 += 32) {
-        float ms[4], ls[4];
-        float4 a[4];
+    // eight splits per thread per round (one round up to 64 splits), all loads issued before
+    // any is used; each thread combines its splits in ascending order
+    for (int s0 = part; s0 < p.n_splits_total; s0 += 64) {
+        float ms[8], ls[8];
+        float4 a[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             const int s = s0 + 8 * i;
             ms[i] = kNegInf;
             ls[i] = 0.0f;
@@ -405,7 +406,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             if (ms[i] == kNegInf) continue;
             const float mn = fmaxf(m, ms[i]);
             const float fo = exp2f(m - mn), fn = exp2f(ms[i] - mn);

@@ -81,7 +81,9 @@ struct CalibParams {
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 // Lane-dense quantizer for many tokens per call (same bytes as launch_quantize).
 hipError_t launch_quantize_bulk(const QuantParams& p, hipStream_t s);
-// Workgroups the bulk quantizer spreads TurboQuant-QJL K planes over (about two per CU).
+// Workgroups a bulk-quantizer launch aims for (its waves loop over octets beyond that), and the
+// same for TurboQuant-QJL K planes (two per CU: each holds S^T in 64 KiB of LDS).
+constexpr int kQuantBulkBlocks = 4096;
 constexpr int kQuantBulkQjlBlocks = 512;
 // Smallest append the bulk quantizer takes.
 constexpr int kQuantBulkMinTokens = 16;

@@ -18,6 +18,7 @@
 
 #include "kvq_internal.h"
 #include "kvq_quant_dev.h"
+#include "kvq_quant_bulk.h"
 
 namespace kvq {
 namespace {
@@ -37,23 +38,74 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
 }
 
 // Bulk quantizer: wave w of workgroup x takes octets 4x + w, then every 4 * gridDim.x-th after
-// it, of one (tensor, sequence, kv head).  kQjl: the tensor is a TurboQuant-QJL K plane, and the
-// workgroup first stages S^T (64 KiB) in LDS for all of its octets.
-template <bool kQjl>
+// it, of one (tensor, sequence, kv head); the next octet's source values are requested before the
+// current one is quantized.  SCH: the scheme of the tensors the launch covers.  TurboQuant-QJL K
+// planes first stage S^T (64 KiB) in LDS for all of the workgroup's octets.
+template <int SCH>
 __global__ __launch_bounds__(256) void quantize_bulk_kernel(QuantParams p, int tensor0, int n_tensors) {
-    constexpr int kWaveFloats = kQjl ? qdev::kBulkWaveLds / 4 : 8 * kDim / 4;
+    constexpr bool kStage = SCH == kTurboQjl;
+    constexpr int kWaveFloats = kStage ? qdev::kBulkWaveLds / 4 : 8 * kDim / 4;
     __shared__ __align__(16) float wl[4][kWaveFloats];
-    __shared__ __align__(16) float st[kQjl ? kDim * kDim : 4];
+    __shared__ __align__(16) float st[kStage ? kDim * kDim : 4];
     const int tensor = tensor0 + (int)blockIdx.z % n_tensors, b = (int)blockIdx.z / n_tensors;
-    if constexpr (kQjl) {
+    const int head = blockIdx.y;
+    if constexpr (kStage) {
         const float4* src = reinterpret_cast<const float4*>(p.qjl_st);
         float4* dst = reinterpret_cast<float4*>(st);
         for (int i = threadIdx.x; i < kDim * kDim / 4; i += blockDim.x) dst[i] = src[i];
         __syncthreads();
     }
-    const int wave = threadIdx.x >> 6;
-    for (int u = blockIdx.x * 4 + wave; u < p.groups8; u += gridDim.x * 4)
-        qdev::quantize_octet_dense(p, tensor, b, blockIdx.y, u, wl[wave], st);
+    const int wave = threadIdx.x >> 6, step = gridDim.x * 4;
+    int u = blockIdx.x * 4 + wave;
+    qdev::OctetSrc cur;
+    qdev::load_octet(p, tensor, b, head, u, cur);
+    for (; u < p.groups8; u += step) {
+        qdev::OctetSrc nxt;
+        qdev::load_octet(p, tensor, b, head, u + step, nxt);
+        qdev::quantize_octet_dense<SCH>(p, tensor, b, head, u, cur, wl[wave], st);
+        cur = nxt;
+    }
+}
+
+// Bulk quantizer of uniform planes (BITS-bit codes, ROT: rotated, SINK: Sinkhorn-balanced); the
+// launch covers tensors tensor0 .. tensor0 + n_tensors - 1, which share that format.  Wave w of
+// workgroup x takes octets 4x + w, then every 4 * gridDim.x-th after it, of one (tensor,
+// sequence, kv head), requesting the next octet's source before quantizing the current one.
+template <int BITS, bool ROT, bool SINK>
+__global__ __launch_bounds__(256) void quantize_uniform_bulk_kernel(QuantParams p, int tensor0,
+                                                                    int n_tensors) {
+    __shared__ __align__(16) uint8_t wv[4][8 * kDim];
+    const int tensor = tensor0 + (int)blockIdx.z % n_tensors, b = (int)blockIdx.z / n_tensors;
+    const int head = blockIdx.y, wave = threadIdx.x >> 6, j = threadIdx.x & 15;
+    const qbulk::WavePlane w = qbulk::wave_plane(p, tensor, b, head);
+    uint32_t sgm[8];
+    float ic[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        sgm[i] = 0u;
+        ic[i] = 1.0f;
+    }
+    if (ROT) {
+        const float* sg = p.signs[tensor] + (size_t)(head * 2 + tensor) * kDim + 8 * j;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sgm[i] = sg[i] < 0.0f ? 0x80000000u : 0u;
+    }
+    if (SINK) {
+        const float* c = p.inv_c[tensor] + (size_t)(head * 2 + tensor) * kDim + 8 * j;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ic[i] = c[i];
+    }
+    const bool is_v = tensor == 1;
+    const int g_first = w.start / 8, step = gridDim.x * 4;
+    int u = blockIdx.x * 4 + wave;
+    qbulk::OctetIn cur;
+    qbulk::load_octet(w, g_first + u, cur);
+    for (; u < p.groups8; u += step) {
+        qbulk::OctetIn nxt;
+        qbulk::load_octet(w, g_first + u + step, nxt);
+        qbulk::uniform_octet<BITS, ROT, SINK>(w, is_v, g_first + u, cur, sgm, ic, wv[wave]);
+        cur = nxt;
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -198,22 +250,64 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_bulk(const QuantParams& p, hipStream_t s) {
-    const int gx = (p.groups8 + 3) / 4;
-    if (p.geom[0].scheme != kTurboQjl) {
-        hipLaunchKernelGGL(quantize_bulk_kernel<false>, dim3(gx, p.Hkv, 2 * p.batch), dim3(256), 0, s,
-                           p, 0, 2);
-        return hipGetLastError();
-    }
-    // QJL K planes: about two workgroups per compute unit (LDS holds two), each staging S^T once
-    // and looping over its share of the octets
-    const int planes = p.Hkv * p.batch;
-    const int gq = std::max(1, std::min(gx, (kQuantBulkQjlBlocks + planes - 1) / planes));
-    hipLaunchKernelGGL(quantize_bulk_kernel<true>, dim3(gq, p.Hkv, p.batch), dim3(256), 0, s, p, 0, 1);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(quantize_bulk_kernel<false>, dim3(gx, p.Hkv, p.batch), dim3(256), 0, s, p, 1, 1);
+namespace {
+
+template <int SCH>
+hipError_t launch_bulk_one(const QuantParams& p, hipStream_t s, int tensor0, int n_tensors) {
+    // workgroups per (tensor, sequence, kv head): enough for about kQuantBulkBlocks in all (two
+    // per compute unit for QJL K planes, whose LDS holds two), each wave looping over octets
+    const int planes = p.Hkv * p.batch * n_tensors;
+    const int target = SCH == kTurboQjl ? kQuantBulkQjlBlocks : kQuantBulkBlocks;
+    const int gx = std::max(1, std::min((p.groups8 + 3) / 4, (target + planes - 1) / planes));
+    hipLaunchKernelGGL(quantize_bulk_kernel<SCH>, dim3(gx, p.Hkv, n_tensors * p.batch), dim3(256), 0,
+                       s, p, tensor0, n_tensors);
     return hipGetLastError();
+}
+
+template <int BITS, bool ROT, bool SINK>
+hipError_t launch_uniform_bulk(const QuantParams& p, hipStream_t s, int tensor0, int n_tensors) {
+    const int planes = p.Hkv * p.batch * n_tensors;
+    const int gx = std::max(1, std::min((p.groups8 + 3) / 4, (kQuantBulkBlocks + planes - 1) / planes));
+    hipLaunchKernelGGL((quantize_uniform_bulk_kernel<BITS, ROT, SINK>), dim3(gx, p.Hkv, n_tensors * p.batch),
+                       dim3(256), 0, s, p, tensor0, n_tensors);
+    return hipGetLastError();
+}
+
+hipError_t launch_uniform_bulk_for(const PlaneGeom& G, const QuantParams& p, hipStream_t s,
+                                   int tensor0, int n_tensors) {
+    const int key = (G.bits == 8 ? 4 : 0) | (G.rotate ? 2 : 0) | (G.sinkhorn ? 1 : 0);
+    switch (key) {
+    case 0: return launch_uniform_bulk<4, false, false>(p, s, tensor0, n_tensors);
+    case 1: return launch_uniform_bulk<4, false, true>(p, s, tensor0, n_tensors);
+    case 2: return launch_uniform_bulk<4, true, false>(p, s, tensor0, n_tensors);
+    case 3: return launch_uniform_bulk<4, true, true>(p, s, tensor0, n_tensors);
+    case 4: return launch_uniform_bulk<8, false, false>(p, s, tensor0, n_tensors);
+    case 5: return launch_uniform_bulk<8, false, true>(p, s, tensor0, n_tensors);
+    case 6: return launch_uniform_bulk<8, true, false>(p, s, tensor0, n_tensors);
+    default: return launch_uniform_bulk<8, true, true>(p, s, tensor0, n_tensors);
+    }
+}
+
+hipError_t launch_bulk_scheme(int scheme, const QuantParams& p, hipStream_t s, int tensor0,
+                              int n_tensors) {
+    switch (scheme) {
+    case kUniform: return launch_uniform_bulk_for(p.geom[tensor0], p, s, tensor0, n_tensors);
+    case kTurboQjl: return launch_bulk_one<kTurboQjl>(p, s, tensor0, n_tensors);
+    default: return launch_bulk_one<kTurboMse>(p, s, tensor0, n_tensors);
+    }
+}
+
+} // namespace
+
+hipError_t launch_quantize_bulk(const QuantParams& p, hipStream_t s) {
+    const PlaneGeom &g0 = p.geom[0], &g1 = p.geom[1];
+    const int s0 = g0.scheme, s1 = g1.scheme;
+    const bool same = s0 == s1 && (s0 != kUniform || (g0.bits == g1.bits && g0.rotate == g1.rotate &&
+                                                      g0.sinkhorn == g1.sinkhorn));
+    if (same) return launch_bulk_scheme(s0, p, s, 0, 2);
+    const hipError_t e = launch_bulk_scheme(s0, p, s, 0, 1);
+    if (e != hipSuccess) return e;
+    return launch_bulk_scheme(s1, p, s, 1, 1);
 }
 
 hipError_t launch_calibrate(const CalibParams& p, hipStream_t s) {

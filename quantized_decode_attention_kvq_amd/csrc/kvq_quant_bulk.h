@@ -1,0 +1,287 @@
+// Bulk (prefill) quantizer for uniform planes, lane-dense.  A wave owns one (tensor, sequence,
+// kv head) and loops over its 8-token octets; an octet is quantized in two rounds of four tokens,
+// lane L holding channels 8j .. 8j+7 (j = L % 16) of octet token 4r + L / 16.  The binary32
+// operations that decide a code are the same, in the same order, as in quantize_wave (spans
+// 1, 2, 4 of the Walsh-Hadamard butterflies inside the lane, spans 8 .. 64 across lanes
+// j ^ 1, 2, 4, 8; the same group min / max, fp16 zero and scale, and rounding), so the bytes
+// are identical; only the integer packing differs in how it is done.
+//
+// Method sources (pages by title and section):
+//  - quantcpp article "Beyond RAG...", progressive table + "how it works": 4-bit codes with fp16
+//    scale and zero per 32 channels, newest 128 tokens kept in FP32.
+//  - KVarN-on-Bonsai post, TL;DR: Walsh-Hadamard transform and Sinkhorn variance balancing
+//    before 4-bit quantization.
+#pragma once
+
+#include "kvq_quant_dev.h"
+
+namespace kvq {
+namespace qbulk {
+
+using qdev::bf16_to_f32;
+using qdev::c0f;
+using qdev::f16_rd;
+using qdev::f16_rn;
+using qdev::f16_val;
+using qdev::k_row;
+using qdev::lane_id;
+
+// 2^23: adding it to a value u in [0, 2^23) rounds u to an integer (ties to even) and leaves
+// that integer in the low mantissa bits.
+__device__ __forceinline__ float magic23() { return __uint_as_float(0x4B000000u); }
+
+// Source values of one octet: v[r][i] = channel 8j + i of octet token 4r + L / 16 (zero for
+// tokens outside the append).
+struct OctetIn {
+    float v[2][8];
+};
+
+// What a wave keeps for its (tensor, sequence, kv head) across octets.
+struct WavePlane {
+    const char* src;  // source of channel 8j of append token 0
+    size_t tok_bytes; // bytes between consecutive tokens of the source
+    int dtype, start, end, window;
+    uint8_t* codes;
+    uint8_t* meta;
+    float* ring;
+};
+
+__device__ __forceinline__ WavePlane wave_plane(const QuantParams& p, int tensor, int b, int head) {
+    const int j = lane_id() & 15;
+    const PlaneGeom& G = p.geom[tensor];
+    char* slot = p.layer_base + (size_t)b * p.seq_stride + (size_t)head * p.head_stride +
+                 p.plane_off[tensor];
+    WavePlane w;
+    const size_t esz = p.dtype == 0 ? 4 : 2;
+    w.tok_bytes = (size_t)p.Hkv * kDim * esz;
+    w.src = static_cast<const char*>(p.src[tensor]) + ((size_t)b * p.T * p.Hkv + head) * kDim * esz +
+            8 * j * esz;
+    w.dtype = p.dtype;
+    w.start = p.start[b];
+    w.end = w.start + p.T;
+    w.window = p.window;
+    w.codes = reinterpret_cast<uint8_t*>(slot + G.codes_off);
+    w.meta = reinterpret_cast<uint8_t*>(slot + G.meta_off);
+    w.ring = reinterpret_cast<float*>(slot + G.ring_off);
+    return w;
+}
+
+__device__ __forceinline__ void load_octet(const WavePlane& w, int g, OctetIn& in) {
+    const int tk = lane_id() >> 4;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int t = 8 * g + 4 * r + tk;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) in.v[r][i] = 0.0f;
+        if (t >= w.start && t < w.end) {
+            const char* s = w.src + (size_t)(t - w.start) * w.tok_bytes;
+            if (w.dtype == 0) {
+                const float4 a = reinterpret_cast<const float4*>(s)[0];
+                const float4 c = reinterpret_cast<const float4*>(s)[1];
+                in.v[r][0] = a.x; in.v[r][1] = a.y; in.v[r][2] = a.z; in.v[r][3] = a.w;
+                in.v[r][4] = c.x; in.v[r][5] = c.y; in.v[r][6] = c.z; in.v[r][7] = c.w;
+            } else {
+                const uint4 a = *reinterpret_cast<const uint4*>(s);
+                const uint32_t x[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    in.v[r][2 * i] = bf16_to_f32((uint16_t)(x[i] & 0xffff));
+                    in.v[r][2 * i + 1] = bf16_to_f32((uint16_t)(x[i] >> 16));
+                }
+            }
+        }
+    }
+}
+
+// Span 8 D of the butterflies across lanes j and j ^ D: the lower lane forms own + partner, the
+// upper lane partner + (-own), the same binary32 value as partner - own.
+template <int D>
+__device__ __forceinline__ void cross8(float* e, int j) {
+    const uint32_t neg = (j & D) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float pv = xor_lane<D>(e[i]);
+        e[i] = pv + __uint_as_float(__float_as_uint(e[i]) ^ neg);
+    }
+}
+
+// R(x) = c0 H (d .* x) of the lane's 8 values; sgm[i] is the sign bit of d for channel 8j + i.
+__device__ __forceinline__ void rotate(float* e, const uint32_t* sgm, int j) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = __uint_as_float(__float_as_uint(e[i]) ^ sgm[i]);
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (!(i & h)) {
+                const float x = e[i], y = e[i + h];
+                e[i] = x + y;
+                e[i + h] = x - y;
+            }
+    cross8<1>(e, j);
+    cross8<2>(e, j);
+    cross8<4>(e, j);
+    cross8<8>(e, j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = e[i] * c0f();
+}
+
+// Group code of the lane's 8 values (group = lanes 4g .. 4g+3 of the token): fp16 zero = the
+// largest fp16 <= min, fp16 scale = fp16((max - zero) / L), code = min(rint((x - zero) / scale), L)
+// (x - zero >= 0, so the lower clamp never acts).  r[i] holds 2^23 + code as binary32 bits, so its
+// low byte is the code.
+template <int BITS>
+__device__ __forceinline__ void group_codes(const float* e, uint32_t* r, uint16_t& s16, uint16_t& z16) {
+    float mn = e[0], mx = e[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+        mn = fminf(mn, e[i]);
+        mx = fmaxf(mx, e[i]);
+    }
+    mn = xor_reduce<4>(mn, [](float x, float y) { return fminf(x, y); });
+    mx = xor_reduce<4>(mx, [](float x, float y) { return fmaxf(x, y); });
+    mn = mn + 0.0f;
+    mx = mx + 0.0f;
+    constexpr float L = (float)((1 << BITS) - 1);
+    z16 = f16_rd(mn);
+    const float z = f16_val(z16);
+    const float s32 = (mx - z) / L;
+    s16 = f16_rn(s32);
+    const float s = f16_val(s16);
+    const float inv = (s > 0.0f) ? 1.0f / s : 0.0f;
+    const float top = magic23() + L;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float u = (e[i] - z) * inv;
+        r[i] = __float_as_uint(fminf(u + magic23(), top));
+    }
+}
+
+// Low bytes of a and b at bytes 0 and 2: a | b << 16 for codes below 256.
+__device__ __forceinline__ uint32_t pair16(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_perm(b, a, 0x0C040C00u);
+}
+
+// K row word of 8 4-bit codes: element i at bit 16 (i % 2) + 4 (i / 2).
+__device__ __forceinline__ uint32_t pack_k4(const uint32_t* r) {
+    const uint32_t a = pair16(r[0], r[1]), b = pair16(r[2], r[3]);
+    const uint32_t c = pair16(r[4], r[5]), d = pair16(r[6], r[7]);
+    return (d << 12) | (c << 8) | (b << 4) | a;
+}
+
+// Low bytes of r[0..3] in byte order.
+__device__ __forceinline__ uint32_t pack_bytes(const uint32_t* r) {
+    const uint32_t lo = __builtin_amdgcn_perm(r[1], r[0], 0x0C0C0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(r[3], r[2], 0x04000C0Cu);
+    return lo | hi;
+}
+
+// V word of one channel from its 8 token codes in byte order (lo = tokens 0..3, hi = 4..7):
+// token i at bit 16 (i % 2) + 4 (i / 2).
+__device__ __forceinline__ uint32_t pack_v4(uint32_t lo, uint32_t hi) {
+    uint32_t ev = __builtin_amdgcn_perm(hi, lo, 0x06040200u); // tokens 0, 2, 4, 6
+    uint32_t od = __builtin_amdgcn_perm(hi, lo, 0x07050301u); // tokens 1, 3, 5, 7
+    ev = ev | (ev >> 4);
+    od = od | (od >> 4);
+    return __builtin_amdgcn_perm(od, ev, 0x06040200u);
+}
+
+// Bits of the V word that belong to tokens i of the octet with lo <= i < hi.
+template <int BITS>
+__device__ __forceinline__ uint64_t v_token_mask(int lo, int hi) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int sh = BITS == 4 ? 16 * (i % 2) + 4 * (i / 2) : 8 * i;
+        if (i >= lo && i < hi) m |= (uint64_t)((1u << BITS) - 1) << sh;
+    }
+    return m;
+}
+
+// One octet g of a uniform plane.  wv: 1 KiB of the wave's LDS (V planes: codes staged as
+// [channel][token] bytes).
+template <int BITS, bool ROT, bool SINK>
+__device__ __forceinline__ void uniform_octet(const WavePlane& w, bool IS_V, int g, const OctetIn& in,
+                                              const uint32_t* sgm, const float* ic, uint8_t* wv) {
+    const int L = lane_id(), tk = L >> 4, j = L & 15;
+    const int t_lo = max(w.start, 8 * g), t_hi = min(w.end, 8 * g + 8);
+    if (t_lo >= t_hi) return;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int i_tok = 4 * r + tk, t = 8 * g + i_tok;
+        const bool valid = t >= t_lo && t < t_hi;
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = in.v[r][i];
+        if (w.window > 0 && valid && t >= w.end - w.window) {
+            float4* ring = reinterpret_cast<float4*>(w.ring + (size_t)(t % w.window) * kDim + 8 * j);
+            ring[0] = make_float4(e[0], e[1], e[2], e[3]);
+            ring[1] = make_float4(e[4], e[5], e[6], e[7]);
+        }
+        if (ROT) rotate(e, sgm, j);
+        if (SINK) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) e[i] = e[i] * ic[i];
+        }
+        uint32_t c[8];
+        uint16_t s16, z16;
+        group_codes<BITS>(e, c, s16, z16);
+        const int g4 = j >> 2, kb = j & 3;
+        const int row = IS_V ? t : k_row(t);
+        if (!IS_V && valid) {
+            uint8_t* rp = w.codes + (size_t)row * (16 * BITS);
+            if (BITS == 4) {
+                reinterpret_cast<uint32_t*>(rp)[4 * kb + g4] = pack_k4(c);
+            } else {
+                *reinterpret_cast<uint2*>(rp + 8 * (4 * kb + g4)) = make_uint2(pack_bytes(c), pack_bytes(c + 4));
+            }
+        }
+        if (IS_V) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wv[(8 * j + i) * 8 + i_tok] = (uint8_t)c[i];
+        }
+        if (valid && kb == 0) {
+            uint16_t* m = reinterpret_cast<uint16_t*>(w.meta + (size_t)row * 16);
+            m[g4] = s16;
+            m[4 + g4] = z16;
+        }
+    }
+    if (IS_V) {
+        // lane L forms V words w = 2L and 2L + 1 of the octet's 128 (word w holds channel
+        // 16 (w % 8) + w / 8): channels 32 (L % 4) + L / 4 and that + 16
+        __builtin_amdgcn_wave_barrier();
+        const int da = 32 * (L & 3) + (L >> 2);
+        const uint2 ca = *reinterpret_cast<const uint2*>(wv + da * 8);
+        const uint2 cb = *reinterpret_cast<const uint2*>(wv + (da + 16) * 8);
+        __builtin_amdgcn_wave_barrier();
+        const int blk = g >> 2, kb = g & 3;
+        const bool full = t_hi - t_lo == 8;
+        if (BITS == 4) {
+            uint2 v = make_uint2(pack_v4(ca.x, ca.y), pack_v4(cb.x, cb.y));
+            uint2* dst = reinterpret_cast<uint2*>(w.codes + (size_t)blk * 2048 + 4 * (128 * kb + 2 * L));
+            if (!full) {
+                const uint32_t m = (uint32_t)v_token_mask<4>(t_lo - 8 * g, t_hi - 8 * g);
+                const uint2 old = *dst;
+                v.x = (old.x & ~m) | (v.x & m);
+                v.y = (old.y & ~m) | (v.y & m);
+            }
+            *dst = v;
+        } else {
+            uint4 v = make_uint4(ca.x, ca.y, cb.x, cb.y);
+            uint4* dst = reinterpret_cast<uint4*>(w.codes + (size_t)blk * 4096 + 8 * (128 * kb + 2 * L));
+            if (!full) {
+                const uint64_t m = v_token_mask<8>(t_lo - 8 * g, t_hi - 8 * g);
+                const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
+                const uint4 old = *dst;
+                v.x = (old.x & ~ml) | (v.x & ml);
+                v.y = (old.y & ~mh) | (v.y & mh);
+                v.z = (old.z & ~ml) | (v.z & ml);
+                v.w = (old.w & ~mh) | (v.w & mh);
+            }
+            *dst = v;
+        }
+    }
+}
+
+} // namespace qbulk
+} // namespace kvq

@@ -393,13 +393,15 @@ __device__ __forceinline__ float tree_sum_sq16(const float* e) {
     return xor_reduce<16>(t, [](float x, float y) { return x + y; });
 }
 
+// Butterfly span 8 D across lanes j and j ^ D: the lower lane forms own + partner, the upper lane
+// partner + (-own), which is the same binary32 value as partner - own.
 template <int D>
 __device__ __forceinline__ void hadamard_cross8(float* e, int j) {
-    const bool lower = (j & D) == 0;
+    const uint32_t neg = (j & D) ? 0x80000000u : 0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float pv = xor_lane<D>(e[i]);
-        e[i] = lower ? (e[i] + pv) : (pv - e[i]);
+        e[i] = pv + __uint_as_float(__float_as_uint(e[i]) ^ neg);
     }
 }
 
@@ -465,19 +467,69 @@ __device__ __forceinline__ float select8(uint32_t c, const float* mu) {
 // QJL projection, or 8 tokens x 128 codes (one byte each) for the V words.
 constexpr int kBulkWaveLds = 8 * kDim * 4;
 
-// One octet of the bulk quantizer.  wl: kBulkWaveLds bytes of LDS owned by the wave.  st: the
-// 128 x 128 QJL matrix S^T ([j][i] = S[i][j]) in LDS when the tensor is a TurboQuant-QJL K
-// plane, else unused.
-__device__ __forceinline__ void quantize_octet_dense(const QuantParams& p, int tensor, int b,
-                                                     int head, int unit, float* wl,
-                                                     const float* st) {
+// Source values of one octet as the bulk quantizer holds them: v[r][i] = channel 8j + i of octet
+// token 4r + L / 16 (zero for tokens outside the append).
+struct OctetSrc {
+    float v[2][8];
+};
+
+struct OctetSpan {
+    int start, end, g0, t_lo, t_hi;
+};
+
+__device__ __forceinline__ bool octet_span(const QuantParams& p, int b, int unit, OctetSpan& o) {
+    if (unit >= p.groups8) return false;
+    o.start = p.start[b];
+    o.end = o.start + p.T;
+    o.g0 = o.start / 8 + unit;
+    o.t_lo = max(o.start, 8 * o.g0);
+    o.t_hi = min(o.end, 8 * o.g0 + 8);
+    return o.t_lo < o.t_hi;
+}
+
+__device__ __forceinline__ void load_octet(const QuantParams& p, int tensor, int b, int head,
+                                           int unit, OctetSrc& src) {
     const int L = lane_id(), tk = L >> 4, j = L & 15;
-    if (unit >= p.groups8) return;
-    const int start = p.start[b];
-    const int end = start + p.T;
-    const int g0 = start / 8 + unit;
-    const int t_lo = max(start, 8 * g0), t_hi = min(end, 8 * g0 + 8);
-    if (t_lo >= t_hi) return;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) src.v[r][i] = 0.0f;
+    OctetSpan o;
+    if (!octet_span(p, b, unit, o)) return;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int t = 8 * o.g0 + 4 * r + tk;
+        if (t >= o.t_lo && t < o.t_hi) {
+            const size_t elem = (((size_t)b * p.T + (t - o.start)) * p.Hkv + head) * kDim + 8 * j;
+            if (p.dtype == 0) {
+                const float4* s4 = reinterpret_cast<const float4*>(static_cast<const float*>(p.src[tensor]) + elem);
+                const float4 v0 = s4[0], v1 = s4[1];
+                src.v[r][0] = v0.x; src.v[r][1] = v0.y; src.v[r][2] = v0.z; src.v[r][3] = v0.w;
+                src.v[r][4] = v1.x; src.v[r][5] = v1.y; src.v[r][6] = v1.z; src.v[r][7] = v1.w;
+            } else {
+                const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.src[tensor]) + elem);
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    src.v[r][2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xffff));
+                    src.v[r][2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+                }
+            }
+        }
+    }
+}
+
+// One octet of the bulk quantizer, tensor scheme SCH, from its loaded source values.  wl:
+// kBulkWaveLds bytes of LDS owned by the wave.  st: the 128 x 128 QJL matrix S^T ([j][i] =
+// S[i][j]) in LDS when SCH is TurboQuant-QJL (a K plane), else unused.
+template <int SCH>
+__device__ __forceinline__ void quantize_octet_dense(const QuantParams& p, int tensor, int b,
+                                                     int head, int unit, const OctetSrc& src,
+                                                     float* wl, const float* st) {
+    const int L = lane_id(), tk = L >> 4, j = L & 15;
+    OctetSpan o;
+    if (!octet_span(p, b, unit, o)) return;
+    const int end = o.end, g0 = o.g0, t_lo = o.t_lo, t_hi = o.t_hi;
 
     const PlaneGeom& G = p.geom[tensor];
     char* slot = p.layer_base + (size_t)b * p.seq_stride + (size_t)head * p.head_stride +
@@ -485,33 +537,8 @@ __device__ __forceinline__ void quantize_octet_dense(const QuantParams& p, int t
     uint8_t* codes = reinterpret_cast<uint8_t*>(slot + G.codes_off);
     uint8_t* meta = reinterpret_cast<uint8_t*>(slot + G.meta_off);
     uint8_t* wcodes = reinterpret_cast<uint8_t*>(wl);
-    const bool qjl = tensor == 0 && G.scheme == kTurboQjl;
+    constexpr bool qjl = SCH == kTurboQjl;
 
-    // all source values of the octet are requested before the first is used
-    float src[2][8];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int t = 8 * g0 + 4 * r + tk;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) src[r][i] = 0.0f;
-        if (t >= t_lo && t < t_hi) {
-            const size_t elem = (((size_t)b * p.T + (t - start)) * p.Hkv + head) * kDim + 8 * j;
-            if (p.dtype == 0) {
-                const float4* s4 = reinterpret_cast<const float4*>(static_cast<const float*>(p.src[tensor]) + elem);
-                const float4 v0 = s4[0], v1 = s4[1];
-                src[r][0] = v0.x; src[r][1] = v0.y; src[r][2] = v0.z; src[r][3] = v0.w;
-                src[r][4] = v1.x; src[r][5] = v1.y; src[r][6] = v1.z; src[r][7] = v1.w;
-            } else {
-                const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.src[tensor]) + elem);
-                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    src[r][2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xffff));
-                    src[r][2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
-                }
-            }
-        }
-    }
     float sg[8], ic[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) sg[i] = ic[i] = 1.0f;
@@ -521,7 +548,7 @@ __device__ __forceinline__ void quantize_octet_dense(const QuantParams& p, int t
         sg[0] = a.x; sg[1] = a.y; sg[2] = a.z; sg[3] = a.w;
         sg[4] = c.x; sg[5] = c.y; sg[6] = c.z; sg[7] = c.w;
     }
-    if (G.scheme == kUniform && G.sinkhorn) {
+    if (SCH == kUniform && G.sinkhorn) {
         const float4* c4 = reinterpret_cast<const float4*>(p.inv_c[tensor] + (size_t)(head * 2 + tensor) * kDim + 8 * j);
         const float4 a = c4[0], c = c4[1];
         ic[0] = a.x; ic[1] = a.y; ic[2] = a.z; ic[3] = a.w;
@@ -534,14 +561,14 @@ __device__ __forceinline__ void quantize_octet_dense(const QuantParams& p, int t
         const bool valid = t >= t_lo && t < t_hi;
         float e[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = src[r][i];
+        for (int i = 0; i < 8; ++i) e[i] = src.v[r][i];
         if (valid && p.window > 0 && t >= end - p.window) {
             float4* ring = reinterpret_cast<float4*>(reinterpret_cast<float*>(slot + G.ring_off) +
                                                      (size_t)(t % p.window) * kDim + 8 * j);
             ring[0] = make_float4(e[0], e[1], e[2], e[3]);
             ring[1] = make_float4(e[4], e[5], e[6], e[7]);
         }
-        if (G.scheme == kUniform) {
+        if constexpr (SCH == kUniform) {
             if (G.rotate) rotate8(e, sg, j);
             if (G.sinkhorn) {
 #pragma unroll
@@ -622,7 +649,7 @@ __device__ __forceinline__ void quantize_octet_dense(const QuantParams& p, int t
                     w[1] = pw[1];
                     w[2] = pw[2];
                 }
-                if (qjl) {
+                if constexpr (qjl) {
                     const uint16_t g16 = f16_rn(sqrtf(tree_sum_sq16(rr)));
                     // residual of channel 8j + i, token i_tok at wl[(8j + i) * 8 + i_tok]
 #pragma unroll
@@ -646,7 +673,7 @@ __device__ __forceinline__ void quantize_octet_dense(const QuantParams& p, int t
     }
     __builtin_amdgcn_wave_barrier();
 
-    if (qjl) {
+    if constexpr (qjl) {
         // sign(S r) for the octet's 8 tokens: lane L forms projections L and 64 + L, each a
         // sequential fma chain over j = 0 .. 127; S^T rows are shared by the 8 tokens
         float acc0[8], acc1[8];
@@ -685,7 +712,7 @@ __device__ __forceinline__ void quantize_octet_dense(const QuantParams& p, int t
         // V words of channels 2L, 2L+1 for this octet from the staged codes, then a
         // read-modify-write of the octet's bits (tokens outside [t_lo, t_hi) keep theirs)
         const int d0 = 2 * L;
-        if (G.scheme == kUniform) {
+        if constexpr (SCH == kUniform) {
             uint64_t vacc0 = 0, vacc1 = 0, vmask = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
