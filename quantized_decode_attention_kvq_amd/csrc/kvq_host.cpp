@@ -113,8 +113,9 @@ Plan make_plan(const kvq_config* c) {
     off = align_up(off + 8 * sizeof(float));
     const size_t partial = (size_t)c->max_batch * c->n_q_heads * kMaxSplits * kPartialFloats *
                            sizeof(float);
+    // Sinkhorn work: the calibration block [2][Hkv][n][128], then two [2][Hkv][128] scale rows
     const size_t calib = c->sinkhorn_iters > 0
-                             ? (size_t)2 * c->n_kv_heads * c->calib_tokens * kDim * sizeof(double)
+                             ? (size_t)2 * c->n_kv_heads * (c->calib_tokens + 2) * kDim * sizeof(double)
                              : 0;
     p.work_bytes = align_up(std::max(partial, calib));
     p.off_work = off;

@@ -69,7 +69,7 @@ struct DecodeParams {
 
 struct CalibParams {
     const void* src[2];       // [n][Hkv][128] of dtype
-    double* work;             // [2][Hkv][n][128]
+    double* work;             // [2][Hkv][n][128], then [2][Hkv][128] twice (column scales)
     const float* signs;       // layer base [Hkv][2][128]
     float* cs;                // layer base
     float* inv_c;             // layer base

@@ -37,32 +37,47 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
     qdev::quantize_wave(p, blockIdx.z & 1, blockIdx.z >> 1, blockIdx.y, blockIdx.x * 4 + wave, rbuf[wave]);
 }
 
-// Bulk quantizer: wave w of workgroup x takes octets 4x + w, then every 4 * gridDim.x-th after
-// it, of one (tensor, sequence, kv head); the next octet's source values are requested before the
-// current one is quantized.  SCH: the scheme of the tensors the launch covers.  TurboQuant-QJL K
-// planes first stage S^T (64 KiB) in LDS for all of the workgroup's octets.
-template <int SCH>
-__global__ __launch_bounds__(256) void quantize_bulk_kernel(QuantParams p, int tensor0, int n_tensors) {
-    constexpr bool kStage = SCH == kTurboQjl;
-    constexpr int kWaveFloats = kStage ? qdev::kBulkWaveLds / 4 : 8 * kDim / 4;
-    __shared__ __align__(16) float wl[4][kWaveFloats];
-    __shared__ __align__(16) float st[kStage ? kDim * kDim : 4];
-    const int tensor = tensor0 + (int)blockIdx.z % n_tensors, b = (int)blockIdx.z / n_tensors;
-    const int head = blockIdx.y;
-    if constexpr (kStage) {
+// Bulk quantizer of one TurboQuant tensor (QJL: TurboQuant-QJL K, else TurboQuant-MSE).  Wave
+// w of workgroup x takes octets 4x + w, then every 4 * gridDim.x-th after it, of one (sequence,
+// kv head), requesting the next octet's source before quantizing the current one.  QJL
+// workgroups first stage S^T (64 KiB) in LDS for all of their octets.
+template <bool QJL>
+__global__ __launch_bounds__(256) void quantize_turbo_bulk_kernel(QuantParams p, int tensor) {
+    __shared__ __align__(16) float wl[4][qbulk::kTurboWaveLds / 4];
+    __shared__ __align__(16) float st[QJL ? kDim * kDim : 4];
+    const int b = blockIdx.z, head = blockIdx.y, wave = threadIdx.x >> 6, j = threadIdx.x & 15;
+    if constexpr (QJL) {
         const float4* src = reinterpret_cast<const float4*>(p.qjl_st);
         float4* dst = reinterpret_cast<float4*>(st);
         for (int i = threadIdx.x; i < kDim * kDim / 4; i += blockDim.x) dst[i] = src[i];
         __syncthreads();
     }
-    const int wave = threadIdx.x >> 6, step = gridDim.x * 4;
+    const qbulk::WavePlane w = qbulk::wave_plane(p, tensor, b, head);
+    uint8_t* qjl_base = reinterpret_cast<uint8_t*>(p.layer_base + (size_t)b * p.seq_stride +
+                                                   (size_t)head * p.head_stride + p.plane_off[tensor] +
+                                                   p.geom[tensor].qjl_off);
+    uint32_t sgm[8], kbit[8];
+    const float* sg = p.signs[tensor] + (size_t)(head * 2 + tensor) * kDim + 8 * j;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        sgm[i] = sg[i] < 0.0f ? 0x80000000u : 0u;
+        const int v = 8 * (j & 3) + i; // value index of channel 8j + i in its 32-channel group
+        kbit[i] = 1u << (16 * (v & 1) + (v >> 1));
+    }
+    qbulk::TurboTabs T;
+#pragma unroll
+    for (int k = 0; k < 7; ++k) T.th[k] = p.theta[k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) T.mu[k] = p.mu[k];
+    const bool is_v = tensor == 1;
+    const int g_first = w.start / 8, step = gridDim.x * 4;
     int u = blockIdx.x * 4 + wave;
-    qdev::OctetSrc cur;
-    qdev::load_octet(p, tensor, b, head, u, cur);
+    qbulk::OctetIn cur;
+    qbulk::load_octet(w, g_first + u, cur);
     for (; u < p.groups8; u += step) {
-        qdev::OctetSrc nxt;
-        qdev::load_octet(p, tensor, b, head, u + step, nxt);
-        qdev::quantize_octet_dense<SCH>(p, tensor, b, head, u, cur, wl[wave], st);
+        qbulk::OctetIn nxt;
+        qbulk::load_octet(w, g_first + u + step, nxt);
+        qbulk::turbo_octet<QJL>(w, is_v, g_first + u, cur, sgm, T, kbit, wl[wave], st, qjl_base);
         cur = nxt;
     }
 }
@@ -112,81 +127,126 @@ __global__ __launch_bounds__(256) void quantize_uniform_bulk_kernel(QuantParams 
 // Sinkhorn calibration (fp64, sequential sums in index order)
 // ---------------------------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void calibrate_kernel(CalibParams p) {
-    const int head = blockIdx.x, tensor = blockIdx.y;
+// Work layout: A [2][Hkv][n][128], then the current sweep's column scales sdc [2][Hkv][128],
+// then the accumulated column scales C [2][Hkv][128] (all binary64).
+__device__ __forceinline__ double* calib_A(const CalibParams& p, int tensor, int head) {
+    return p.work + ((size_t)tensor * p.Hkv + head) * (size_t)p.n * kDim;
+}
+__device__ __forceinline__ double* calib_sdc(const CalibParams& p, int tensor, int head) {
+    return p.work + (size_t)2 * p.Hkv * p.n * kDim + ((size_t)tensor * p.Hkv + head) * kDim;
+}
+__device__ __forceinline__ double* calib_C(const CalibParams& p, int tensor, int head) {
+    return calib_sdc(p, tensor, head) + (size_t)2 * p.Hkv * kDim;
+}
+
+// A = R(x) (binary32 butterflies, as the quantizer rotates) widened to binary64, or x; C = 1.
+// One thread per (token, kv head, tensor).
+__global__ __launch_bounds__(64) void calib_init_kernel(CalibParams p) {
+    const int t = blockIdx.x * 64 + threadIdx.x, head = blockIdx.y, tensor = blockIdx.z;
+    if (!p.do_tensor[tensor]) return;
+    if (blockIdx.x == 0)
+        for (int j = threadIdx.x; j < kDim; j += 64) calib_C(p, tensor, head)[j] = 1.0;
+    if (t >= p.n) return;
+    const float* signs = p.signs + (size_t)(head * 2 + tensor) * kDim;
+    float y[kDim];
+    const size_t off = ((size_t)t * p.Hkv + head) * kDim;
+#pragma unroll
+    for (int j = 0; j < kDim; ++j) {
+        float v = (p.dtype == 0) ? static_cast<const float*>(p.src[tensor])[off + j]
+                                 : bf16_to_f32(static_cast<const uint16_t*>(p.src[tensor])[off + j]);
+        if (p.rotate[tensor] && signs[j] < 0.0f) v = -v;
+        y[j] = v;
+    }
+    if (p.rotate[tensor]) {
+#pragma unroll
+        for (int h = 1; h < kDim; h <<= 1)
+#pragma unroll
+            for (int i = 0; i < kDim; ++i)
+                if (!(i & h)) {
+                    const float u = y[i], w = y[i + h];
+                    y[i] = u + w;
+                    y[i + h] = u - w;
+                }
+#pragma unroll
+        for (int j = 0; j < kDim; ++j) y[j] = y[j] * c0f();
+    }
+    double* A = calib_A(p, tensor, head) + (size_t)t * kDim;
+#pragma unroll
+    for (int j = 0; j < kDim; ++j) A[j] = (double)y[j];
+}
+
+// Row sweep, one wave per row: (when `divide`) the previous sweep's column scales are applied
+// first, A[t][j] / sdc[j]; then mean and variance of the row, each a sum in index order taken by
+// lane 0 from LDS, and A[t][j] / sd_row by every lane.
+__global__ __launch_bounds__(256) void calib_rows_kernel(CalibParams p, int divide) {
+    __shared__ double s_row[4][kDim];
+    __shared__ double s_sd[4];
+    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave, head = blockIdx.y, tensor = blockIdx.z;
+    if (!p.do_tensor[tensor] || t >= p.n) return;
+    double* A = calib_A(p, tensor, head) + (size_t)t * kDim;
+    const double* sdc = calib_sdc(p, tensor, head);
+    double2 a = reinterpret_cast<const double2*>(A)[l];
+    if (divide) {
+        a.x = a.x / sdc[2 * l];
+        a.y = a.y / sdc[2 * l + 1];
+    }
+    s_row[wave][2 * l] = a.x;
+    s_row[wave][2 * l + 1] = a.y;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (l == 0) {
+        const double* r = s_row[wave];
+        double s = 0.0;
+#pragma unroll 16
+        for (int j = 0; j < kDim; ++j) s = s + r[j];
+        const double mean = s / 128.0;
+        double v = 0.0;
+#pragma unroll 16
+        for (int j = 0; j < kDim; ++j) {
+            const double dv = r[j] - mean;
+            v = v + dv * dv;
+        }
+        double sd = sqrt(v / 128.0);
+        if (sd < 1e-30) sd = 1e-30;
+        s_sd[wave] = sd;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const double sd = s_sd[wave];
+    reinterpret_cast<double2*>(A)[l] = make_double2(a.x / sd, a.y / sd);
+}
+
+// Column sweep: lane l of wave w of (kv head, tensor) takes column 64 w + l; mean and variance
+// over the n rows, each a sum in index order; sdc = sd, C *= sd.  `last`: also write c = C and
+// 1 / c as binary32.
+__global__ __launch_bounds__(128) void calib_cols_kernel(CalibParams p, int last) {
+    const int head = blockIdx.x, tensor = blockIdx.y, j = threadIdx.x;
     if (!p.do_tensor[tensor]) return;
     const int n = p.n;
-    double* A = p.work + ((size_t)tensor * p.Hkv + head) * (size_t)n * kDim;
-    __shared__ double C[kDim];
-    const float* signs = p.signs + (size_t)(head * 2 + tensor) * kDim;
-
-    for (int t = threadIdx.x; t < n; t += blockDim.x) {
-        float y[kDim];
-        const size_t off = ((size_t)t * p.Hkv + head) * kDim;
-#pragma unroll
-        for (int j = 0; j < kDim; ++j) {
-            float v = (p.dtype == 0)
-                          ? static_cast<const float*>(p.src[tensor])[off + j]
-                          : bf16_to_f32(static_cast<const uint16_t*>(p.src[tensor])[off + j]);
-            if (p.rotate[tensor] && signs[j] < 0.0f) v = -v;
-            y[j] = v;
-        }
-        if (p.rotate[tensor]) {
-#pragma unroll
-            for (int h = 1; h < kDim; h <<= 1)
-#pragma unroll
-                for (int i = 0; i < kDim; ++i)
-                    if (!(i & h)) {
-                        const float u = y[i], w = y[i + h];
-                        y[i] = u + w;
-                        y[i + h] = u - w;
-                    }
-#pragma unroll
-            for (int j = 0; j < kDim; ++j) y[j] = y[j] * c0f();
-        }
-        for (int j = 0; j < kDim; ++j) A[(size_t)t * kDim + j] = (double)y[j];
+    const double* A = calib_A(p, tensor, head) + j;
+    double s = 0.0;
+#pragma unroll 16
+    for (int t = 0; t < n; ++t) s = s + A[(size_t)t * kDim];
+    const double mean = s / (double)n;
+    double v = 0.0;
+#pragma unroll 16
+    for (int t = 0; t < n; ++t) {
+        const double dv = A[(size_t)t * kDim] - mean;
+        v = v + dv * dv;
     }
-    if (threadIdx.x < kDim) C[threadIdx.x] = 1.0;
-    __syncthreads();
-
-    for (int it = 0; it < p.iters; ++it) {
-        for (int t = threadIdx.x; t < n; t += blockDim.x) {
-            double* row = A + (size_t)t * kDim;
-            double s = 0.0;
-            for (int j = 0; j < kDim; ++j) s = s + row[j];
-            const double mean = s / 128.0;
-            double v = 0.0;
-            for (int j = 0; j < kDim; ++j) {
-                const double dv = row[j] - mean;
-                v = v + dv * dv;
-            }
-            double sd = sqrt(v / 128.0);
-            if (sd < 1e-30) sd = 1e-30;
-            for (int j = 0; j < kDim; ++j) row[j] = row[j] / sd;
-        }
-        __syncthreads();
-        if (threadIdx.x < kDim) {
-            const int j = threadIdx.x;
-            double s = 0.0;
-            for (int t = 0; t < n; ++t) s = s + A[(size_t)t * kDim + j];
-            const double mean = s / (double)n;
-            double v = 0.0;
-            for (int t = 0; t < n; ++t) {
-                const double dv = A[(size_t)t * kDim + j] - mean;
-                v = v + dv * dv;
-            }
-            double sd = sqrt(v / (double)n);
-            if (sd < 1e-30) sd = 1e-30;
-            for (int t = 0; t < n; ++t) A[(size_t)t * kDim + j] = A[(size_t)t * kDim + j] / sd;
-            C[j] = C[j] * sd;
-        }
-        __syncthreads();
-    }
-    if (threadIdx.x < kDim) {
-        const int j = threadIdx.x;
-        const float c = (float)C[j];
-        p.cs[(size_t)(head * 2 + tensor) * kDim + j] = c;
-        p.inv_c[(size_t)(head * 2 + tensor) * kDim + j] = (float)(1.0 / (double)c);
+    double sd = sqrt(v / (double)n);
+    if (sd < 1e-30) sd = 1e-30;
+    calib_sdc(p, tensor, head)[j] = sd;
+    double* C = calib_C(p, tensor, head);
+    const double c = C[j] * sd;
+    C[j] = c;
+    if (last) {
+        const float cf = (float)c;
+        p.cs[(size_t)(head * 2 + tensor) * kDim + j] = cf;
+        p.inv_c[(size_t)(head * 2 + tensor) * kDim + j] = (float)(1.0 / (double)cf);
     }
 }
 
@@ -252,15 +312,13 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t s) {
 
 namespace {
 
-template <int SCH>
-hipError_t launch_bulk_one(const QuantParams& p, hipStream_t s, int tensor0, int n_tensors) {
-    // workgroups per (tensor, sequence, kv head): enough for about kQuantBulkBlocks in all (two
-    // per compute unit for QJL K planes, whose LDS holds two), each wave looping over octets
-    const int planes = p.Hkv * p.batch * n_tensors;
-    const int target = SCH == kTurboQjl ? kQuantBulkQjlBlocks : kQuantBulkBlocks;
+template <bool QJL>
+hipError_t launch_turbo_bulk(const QuantParams& p, hipStream_t s, int tensor) {
+    // QJL K planes: about two workgroups per compute unit (LDS holds two), each staging S^T once
+    const int planes = p.Hkv * p.batch;
+    const int target = QJL ? kQuantBulkQjlBlocks : kQuantBulkBlocks;
     const int gx = std::max(1, std::min((p.groups8 + 3) / 4, (target + planes - 1) / planes));
-    hipLaunchKernelGGL(quantize_bulk_kernel<SCH>, dim3(gx, p.Hkv, n_tensors * p.batch), dim3(256), 0,
-                       s, p, tensor0, n_tensors);
+    hipLaunchKernelGGL(quantize_turbo_bulk_kernel<QJL>, dim3(gx, p.Hkv, p.batch), dim3(256), 0, s, p, tensor);
     return hipGetLastError();
 }
 
@@ -288,12 +346,13 @@ hipError_t launch_uniform_bulk_for(const PlaneGeom& G, const QuantParams& p, hip
     }
 }
 
+// One launch for tensors tensor0 .. tensor0 + n_tensors - 1 (TurboQuant: one tensor).
 hipError_t launch_bulk_scheme(int scheme, const QuantParams& p, hipStream_t s, int tensor0,
                               int n_tensors) {
     switch (scheme) {
     case kUniform: return launch_uniform_bulk_for(p.geom[tensor0], p, s, tensor0, n_tensors);
-    case kTurboQjl: return launch_bulk_one<kTurboQjl>(p, s, tensor0, n_tensors);
-    default: return launch_bulk_one<kTurboMse>(p, s, tensor0, n_tensors);
+    case kTurboQjl: return launch_turbo_bulk<true>(p, s, tensor0);
+    default: return launch_turbo_bulk<false>(p, s, tensor0);
     }
 }
 
@@ -302,8 +361,8 @@ hipError_t launch_bulk_scheme(int scheme, const QuantParams& p, hipStream_t s, i
 hipError_t launch_quantize_bulk(const QuantParams& p, hipStream_t s) {
     const PlaneGeom &g0 = p.geom[0], &g1 = p.geom[1];
     const int s0 = g0.scheme, s1 = g1.scheme;
-    const bool same = s0 == s1 && (s0 != kUniform || (g0.bits == g1.bits && g0.rotate == g1.rotate &&
-                                                      g0.sinkhorn == g1.sinkhorn));
+    const bool same = s0 == kUniform && s1 == kUniform && g0.bits == g1.bits &&
+                      g0.rotate == g1.rotate && g0.sinkhorn == g1.sinkhorn;
     if (same) return launch_bulk_scheme(s0, p, s, 0, 2);
     const hipError_t e = launch_bulk_scheme(s0, p, s, 0, 1);
     if (e != hipSuccess) return e;
@@ -311,8 +370,16 @@ hipError_t launch_quantize_bulk(const QuantParams& p, hipStream_t s) {
 }
 
 hipError_t launch_calibrate(const CalibParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(calibrate_kernel, dim3(p.Hkv, 2), dim3(256), 0, s, p);
-    return hipGetLastError();
+    hipLaunchKernelGGL(calib_init_kernel, dim3((p.n + 63) / 64, p.Hkv, 2), dim3(64), 0, s, p);
+    hipError_t e = hipGetLastError();
+    for (int it = 0; it < p.iters && e == hipSuccess; ++it) {
+        hipLaunchKernelGGL(calib_rows_kernel, dim3((p.n + 3) / 4, p.Hkv, 2), dim3(256), 0, s, p, it > 0 ? 1 : 0);
+        e = hipGetLastError();
+        if (e != hipSuccess) break;
+        hipLaunchKernelGGL(calib_cols_kernel, dim3(p.Hkv, 2), dim3(kDim), 0, s, p, it == p.iters - 1 ? 1 : 0);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 hipError_t launch_codebook(float* mu, float* theta, int iters, hipStream_t s) {

@@ -1,16 +1,19 @@
-// Bulk (prefill) quantizer for uniform planes, lane-dense.  A wave owns one (tensor, sequence,
-// kv head) and loops over its 8-token octets; an octet is quantized in two rounds of four tokens,
-// lane L holding channels 8j .. 8j+7 (j = L % 16) of octet token 4r + L / 16.  The binary32
-// operations that decide a code are the same, in the same order, as in quantize_wave (spans
-// 1, 2, 4 of the Walsh-Hadamard butterflies inside the lane, spans 8 .. 64 across lanes
-// j ^ 1, 2, 4, 8; the same group min / max, fp16 zero and scale, and rounding), so the bytes
-// are identical; only the integer packing differs in how it is done.
+// Bulk (prefill) quantizer, lane-dense.  A wave owns one (tensor, sequence, kv head) and loops
+// over its 8-token octets; an octet is quantized in two rounds of four tokens, lane L holding
+// channels 8j .. 8j+7 (j = L % 16) of octet token 4r + L / 16.  The binary32 operations that
+// decide a code are the same, in the same order, as in quantize_wave (spans 1, 2, 4 of the
+// Walsh-Hadamard butterflies inside the lane, spans 8 .. 64 across lanes j ^ 1, 2, 4, 8; the same
+// group min / max, fp16 zero and scale, and rounding; the same pairwise norm tree; the same
+// sequential QJL fma chain), so the bytes are identical; only the integer packing differs in how
+// it is done.
 //
 // Method sources (pages by title and section):
 //  - quantcpp article "Beyond RAG...", progressive table + "how it works": 4-bit codes with fp16
 //    scale and zero per 32 channels, newest 128 tokens kept in FP32.
 //  - KVarN-on-Bonsai post, TL;DR: Walsh-Hadamard transform and Sinkhorn variance balancing
 //    before 4-bit quantization.
+//  - "LLM memory saving ... 2026", TurboQuant row of the method table: random rotation,
+//    per-coordinate optimal scalar quantizer, 1-bit QJL of the residual.
 #pragma once
 
 #include "kvq_quant_dev.h"
@@ -281,6 +284,207 @@ __device__ __forceinline__ void uniform_octet(const WavePlane& w, bool IS_V, int
             *dst = v;
         }
     }
+}
+
+// ---------------------------------------------------------------------------------------------
+// TurboQuant planes
+// ---------------------------------------------------------------------------------------------
+
+// Pairwise tree sum of the squares of the 128 values a 16-lane group holds, 8 per lane: three
+// levels inside the lane, then lane partners at distances 1, 2, 4, 8 (the index-order tree).
+__device__ __forceinline__ float tree_sum_sq16(const float* e) {
+    const float l0 = e[0] * e[0] + e[1] * e[1], l1 = e[2] * e[2] + e[3] * e[3];
+    const float l2 = e[4] * e[4] + e[5] * e[5], l3 = e[6] * e[6] + e[7] * e[7];
+    const float t = (l0 + l1) + (l2 + l3);
+    return xor_reduce<16>(t, [](float x, float y) { return x + y; });
+}
+
+// Bytes of LDS per wave of the TurboQuant bulk kernels: 128 channels x 8 tokens of binary32
+// residuals (QJL K planes) or of one-byte codes (V planes).
+constexpr int kTurboWaveLds = 8 * kDim * 4;
+
+// Per-wave constants of a TurboQuant plane.  th: the 7 ascending thresholds; mu: the 8 levels.
+struct TurboTabs {
+    float th[7], mu[8];
+};
+
+// Lloyd-Max code of u: the number of thresholds below u, found by a binary search over the
+// ascending thresholds (the same count as comparing u with each of them).  b0, b1, b2: its bits.
+__device__ __forceinline__ void turbo_code(float u, const TurboTabs& T, bool& b0, bool& b1, bool& b2) {
+    b2 = u > T.th[3];
+    b1 = u > (b2 ? T.th[5] : T.th[1]);
+    b0 = u > (b2 ? (b1 ? T.th[6] : T.th[4]) : (b1 ? T.th[2] : T.th[0]));
+}
+
+__device__ __forceinline__ float turbo_level(bool b0, bool b1, bool b2, const TurboTabs& T) {
+    const float hi = b1 ? (b0 ? T.mu[7] : T.mu[6]) : (b0 ? T.mu[5] : T.mu[4]);
+    const float lo = b1 ? (b0 ? T.mu[3] : T.mu[2]) : (b0 ? T.mu[1] : T.mu[0]);
+    return b2 ? hi : lo;
+}
+
+// Nibble of bit k of the four bytes of x (byte 0 -> bit 0).
+__device__ __forceinline__ uint32_t byte_bits(uint32_t x, int k) {
+    x = (x >> k) & 0x01010101u;
+    x = x | (x >> 7);
+    x = x | (x >> 14);
+    return x & 0xFu;
+}
+
+// One octet g of a TurboQuant plane (QJL: TurboQuant-QJL K plane; else TurboQuant-MSE, K or V).
+// wl: kTurboWaveLds bytes of the wave's LDS.  st: S^T ([j][i] = S[i][j], 128 x 128) in LDS (QJL).
+// kbit[i]: 1 << (the bit of channel 8j + i in its K plane words).
+template <bool QJL>
+__device__ __forceinline__ void turbo_octet(const WavePlane& w, bool IS_V, int g, const OctetIn& in,
+                                            const uint32_t* sgm, const TurboTabs& T,
+                                            const uint32_t* kbit, float* wl, const float* st,
+                                            uint8_t* qjl_base) {
+    const int L = lane_id(), tk = L >> 4, j = L & 15;
+    const int t_lo = max(w.start, 8 * g), t_hi = min(w.end, 8 * g + 8);
+    if (t_lo >= t_hi) return;
+    uint8_t* wv = reinterpret_cast<uint8_t*>(wl);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int i_tok = 4 * r + tk, t = 8 * g + i_tok;
+        const bool valid = t >= t_lo && t < t_hi;
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = in.v[r][i];
+        if (w.window > 0 && valid && t >= w.end - w.window) {
+            float4* ring = reinterpret_cast<float4*>(w.ring + (size_t)(t % w.window) * kDim + 8 * j);
+            ring[0] = make_float4(e[0], e[1], e[2], e[3]);
+            ring[1] = make_float4(e[4], e[5], e[6], e[7]);
+        }
+        rotate(e, sgm, j);
+        const uint16_t n16 = f16_rn(sqrtf(tree_sum_sq16(e)));
+        const float n = f16_val(n16);
+        const float inv = (n > 0.0f) ? 1.0f / n : 0.0f;
+        uint32_t pw0 = 0u, pw1 = 0u, pw2 = 0u, codes_lo = 0u, codes_hi = 0u;
+        float rr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            bool b0, b1, b2;
+            turbo_code(e[i] * inv, T, b0, b1, b2);
+            if (IS_V) {
+                const uint32_t q = (b0 ? 1u : 0u) | (b1 ? 2u : 0u) | (b2 ? 4u : 0u);
+                if (i < 4) codes_lo |= q << (8 * i);
+                else codes_hi |= q << (8 * (i - 4));
+            } else {
+                pw0 |= b0 ? kbit[i] : 0u;
+                pw1 |= b1 ? kbit[i] : 0u;
+                pw2 |= b2 ? kbit[i] : 0u;
+            }
+            if (QJL) rr[i] = e[i] - n * turbo_level(b0, b1, b2, T);
+        }
+        if (IS_V) {
+            *reinterpret_cast<uint2*>(wv + (size_t)i_tok * kDim + 8 * j) = make_uint2(codes_lo, codes_hi);
+            if (valid && j == 0) reinterpret_cast<uint16_t*>(w.meta)[t] = n16;
+            continue;
+        }
+        // K row of token t: plane words of group j / 4, merged over its 4 lanes
+        pw0 = qdev::or_reduce<4>(pw0);
+        pw1 = qdev::or_reduce<4>(pw1);
+        pw2 = qdev::or_reduce<4>(pw2);
+        const int row = k_row(t);
+        if (valid && (j & 3) == 0) {
+            uint32_t* kw = reinterpret_cast<uint32_t*>(w.codes + (size_t)row * 48 + 12 * (j >> 2));
+            kw[0] = pw0;
+            kw[1] = pw1;
+            kw[2] = pw2;
+        }
+        if (QJL) {
+            const uint16_t g16 = f16_rn(sqrtf(tree_sum_sq16(rr)));
+            // residual of channel 8j + i of octet token i_tok at wl[(8j + i) * 8 + i_tok]
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wl[(8 * j + i) * 8 + i_tok] = rr[i];
+            if (valid && j == 0) {
+                uint16_t* m = reinterpret_cast<uint16_t*>(w.meta + (size_t)row * 4);
+                m[0] = n16;
+                m[1] = g16;
+            }
+        } else if (valid && j == 0) {
+            reinterpret_cast<uint16_t*>(w.meta)[row] = n16;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (QJL && !IS_V) {
+        // sign(S r) of the octet's 8 tokens: lane L forms projections L and 64 + L, each a
+        // sequential fma chain over j = 0 .. 127; the rows of S^T are shared by the 8 tokens
+        float acc0[8], acc1[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc0[i] = acc1[i] = 0.0f;
+#pragma unroll 4
+        for (int jj = 0; jj < kDim; ++jj) {
+            const float s0 = st[jj * kDim + L], s1 = st[jj * kDim + 64 + L];
+            const float4 ra = *reinterpret_cast<const float4*>(wl + jj * 8);
+            const float4 rb = *reinterpret_cast<const float4*>(wl + jj * 8 + 4);
+            const float rj[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                acc0[i] = fmaf(s0, rj[i], acc0[i]);
+                acc1[i] = fmaf(s1, rj[i], acc1[i]);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint64_t m0 = __ballot(acc0[i] >= 0.0f);
+            const uint64_t m1 = __ballot(acc1[i] >= 0.0f);
+            const int t = 8 * g + i;
+            if (L == i && t >= t_lo && t < t_hi) {
+                uint4 qw;
+                qw.x = qdev::unshuffle32((uint32_t)m0);
+                qw.y = qdev::unshuffle32((uint32_t)(m0 >> 32));
+                qw.z = qdev::unshuffle32((uint32_t)m1);
+                qw.w = qdev::unshuffle32((uint32_t)(m1 >> 32));
+                *reinterpret_cast<uint4*>(qjl_base + (size_t)k_row(t) * 16) = qw;
+            }
+        }
+    }
+    if (IS_V) {
+        // TurboQuant-MSE V block words: bit k of channel d -> word 6 (16 o + d % 16) + 2k + (d / 16) / 4,
+        // token i at bit 16 (i % 2) + 4 ((d / 16) % 4) + i / 2.  Lane L (< 32) forms the three words of
+        // n = L % 16, h = L / 16 (channels 16 N + n, N = 4h .. 4h + 3); lanes 32 + L take channels
+        // N = 4h + 2, 4h + 3 of the same words, merged by the lane 32 apart.
+        const int n = L & 15, h = (L >> 4) & 1, half = L >> 5;
+        uint32_t wk0 = 0u, wk1 = 0u, wk2 = 0u;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int Nl = 2 * half + c; // N % 4
+            const int d = 16 * (4 * h + Nl) + n;
+            uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo |= (uint32_t)wv[i * kDim + d] << (8 * i);
+                hi |= (uint32_t)wv[(i + 4) * kDim + d] << (8 * i);
+            }
+            const uint32_t ev = __builtin_amdgcn_perm(hi, lo, 0x06040200u); // tokens 0, 2, 4, 6
+            const uint32_t od = __builtin_amdgcn_perm(hi, lo, 0x07050301u); // tokens 1, 3, 5, 7
+            wk0 |= (byte_bits(ev, 0) | (byte_bits(od, 0) << 16)) << (4 * Nl);
+            wk1 |= (byte_bits(ev, 1) | (byte_bits(od, 1) << 16)) << (4 * Nl);
+            wk2 |= (byte_bits(ev, 2) | (byte_bits(od, 2) << 16)) << (4 * Nl);
+        }
+        wk0 |= xor_lane<32>(wk0);
+        wk1 |= xor_lane<32>(wk1);
+        wk2 |= xor_lane<32>(wk2);
+        __builtin_amdgcn_wave_barrier();
+        if (half == 0) {
+            const int o = g & 3;
+            uint32_t* blk = reinterpret_cast<uint32_t*>(w.codes + (size_t)(g >> 2) * 1536) + 6 * (16 * o + n) + h;
+            if (t_hi - t_lo == 8) {
+                blk[0] = wk0;
+                blk[2] = wk1;
+                blk[4] = wk2;
+            } else {
+                // token bits of the octet present in this append
+                uint32_t m = 0u;
+                for (int i = t_lo - 8 * g; i < t_hi - 8 * g; ++i) m |= 0x1111u << (16 * (i & 1) + (i >> 1));
+                blk[0] = (blk[0] & ~m) | (wk0 & m);
+                blk[2] = (blk[2] & ~m) | (wk1 & m);
+                blk[4] = (blk[4] & ~m) | (wk2 & m);
+            }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
 }
 
 } // namespace qbulk

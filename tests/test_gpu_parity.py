@@ -97,6 +97,47 @@ def test_prefill_equals_appends_bytewise(wl):
     _check_all_planes(a, 0, heads=[0, 5])
 
 
+# (sequences, tokens) of successive prefill calls: ragged starts per sequence, partial octets at
+# both ends of the bulk calls (>= 16 tokens) and single-octet calls below that
+RAGGED_CALLS = [(3, 21), (1, 5), (2, 3), (3, 37), (1, 16), (3, 130)]
+
+
+@pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_KVARN, W.LLAMA3B_32K_TURBO,
+                                W.LLAMA3B_32K_TURBO_ASYM, W.DENSE27B_120K_U8],
+                         ids=lambda w: w.name)
+def test_prefill_ragged_batch_bytewise(wl):
+    """Prefill calls over a batch whose sequences start at different lengths leave exactly the
+    bytes the oracle builds from each sequence's own token stream."""
+    n_max = sum(t for _, t in RAGGED_CALLS)
+    _say("case: ragged-batch prefill,", wl.name, RAGGED_CALLS)
+    case = Case(wl, n_max, layers=[0], batch=3)
+    streams = {b: ([], []) for b in range(3)}
+    for ci, (nb, nt) in enumerate(RAGGED_CALLS):
+        k = W.gen_kv(wl, 1000 + ci, 0, nt, batch=nb)
+        v = W.gen_kv(wl, 1000 + ci, 1, nt, batch=nb)
+        case.cache.prefill_quantize(0, k.to("cuda"), v.to("cuda"))
+        for b in range(nb):
+            streams[b][0].append(k[b].float().numpy())
+            streams[b][1].append(v[b].float().numpy())
+    torch.cuda.synchronize()
+    _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS)
+    cap = case.cache.cfg.max_context
+    for b in range(3):
+        assert case.cache.length(0, b) == sum(x.shape[0] for x in streams[b][0])
+        for h in range(wl.n_kv_heads):
+            for tensor in (0, 1):
+                X = np.concatenate(streams[b][tensor])[:, h]
+                scheme = wl.k_scheme if tensor == 0 else wl.v_scheme
+                bits = wl.k_bits if tensor == 0 else wl.v_bits
+                rot = (wl.rotate_k if tensor == 0 else wl.rotate_v) or scheme != W.UNIFORM
+                sink = wl.sinkhorn_iters > 0 and scheme == W.UNIFORM
+                tb = case.oracle_tables(0, h, tensor, mu, theta)
+                pl = oracle.Plane(scheme, bits, rot, sink, wl.window, tensor, cap)
+                pl.append(X, tb)
+                compare_plane(case.device_plane(0, b, h, tensor), pl, f"seq {b} head {h} tensor {tensor}")
+    _say("  planes bit-exact for 3 sequences x", wl.n_kv_heads, "heads")
+
+
 def test_kvarn_rotation_sinkhorn_small():
     wl = W.LLAMA3B_32K_KVARN
     _say("case:", wl.name, "2 layers, 1000 tokens")
