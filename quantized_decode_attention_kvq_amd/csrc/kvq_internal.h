@@ -82,9 +82,9 @@ hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 // Lane-dense quantizer for many tokens per call (same bytes as launch_quantize).
 hipError_t launch_quantize_bulk(const QuantParams& p, hipStream_t s);
 // Workgroups a bulk-quantizer launch aims for (its waves loop over octets beyond that), and the
-// same for TurboQuant-QJL K planes (two per CU: each holds S^T in 64 KiB of LDS).
+// same for TurboQuant-QJL K planes (one 16-wave workgroup per CU, holding S^T in 64 KiB of LDS).
 constexpr int kQuantBulkBlocks = 4096;
-constexpr int kQuantBulkQjlBlocks = 512;
+constexpr int kQuantBulkQjlBlocks = 256;
 // Smallest append the bulk quantizer takes.
 constexpr int kQuantBulkMinTokens = 16;
 hipError_t launch_calibrate(const CalibParams& p, hipStream_t s);

@@ -42,8 +42,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
 // kv head), requesting the next octet's source before quantizing the current one.  QJL
 // workgroups first stage S^T (64 KiB) in LDS for all of their octets.
 template <bool QJL>
-__global__ __launch_bounds__(256) void quantize_turbo_bulk_kernel(QuantParams p, int tensor) {
-    __shared__ __align__(16) float wl[4][qbulk::kTurboWaveLds / 4];
+__global__ __launch_bounds__(QJL ? 1024 : 256) void quantize_turbo_bulk_kernel(QuantParams p, int tensor) {
+    constexpr int kW = QJL ? 16 : 4; // waves per workgroup: QJL workgroups share one copy of S^T
+    __shared__ __align__(16) float wl[kW][qbulk::kTurboWaveLds / 4];
     __shared__ __align__(16) float st[QJL ? kDim * kDim : 4];
     const int b = blockIdx.z, head = blockIdx.y, wave = threadIdx.x >> 6, j = threadIdx.x & 15;
     if constexpr (QJL) {
@@ -70,8 +71,8 @@ __global__ __launch_bounds__(256) void quantize_turbo_bulk_kernel(QuantParams p,
 #pragma unroll
     for (int k = 0; k < 8; ++k) T.mu[k] = p.mu[k];
     const bool is_v = tensor == 1;
-    const int g_first = w.start / 8, step = gridDim.x * 4;
-    int u = blockIdx.x * 4 + wave;
+    const int g_first = w.start / 8, step = gridDim.x * kW;
+    int u = blockIdx.x * kW + wave;
     qbulk::OctetIn cur;
     qbulk::load_octet(w, g_first + u, cur);
     for (; u < p.groups8; u += step) {
@@ -315,10 +316,11 @@ namespace {
 template <bool QJL>
 hipError_t launch_turbo_bulk(const QuantParams& p, hipStream_t s, int tensor) {
     // QJL K planes: about two workgroups per compute unit (LDS holds two), each staging S^T once
+    constexpr int kW = QJL ? 16 : 4;
     const int planes = p.Hkv * p.batch;
     const int target = QJL ? kQuantBulkQjlBlocks : kQuantBulkBlocks;
-    const int gx = std::max(1, std::min((p.groups8 + 3) / 4, (target + planes - 1) / planes));
-    hipLaunchKernelGGL(quantize_turbo_bulk_kernel<QJL>, dim3(gx, p.Hkv, p.batch), dim3(256), 0, s, p, tensor);
+    const int gx = std::max(1, std::min((p.groups8 + kW - 1) / kW, (target + planes - 1) / planes));
+    hipLaunchKernelGGL(quantize_turbo_bulk_kernel<QJL>, dim3(gx, p.Hkv, p.batch), dim3(kW * 64), 0, s, p, tensor);
     return hipGetLastError();
 }
 

@@ -16,6 +16,8 @@
 //    per-coordinate optimal scalar quantizer, 1-bit QJL of the residual.
 #pragma once
 
+#include <utility>
+
 #include "kvq_quant_dev.h"
 
 namespace kvq {
@@ -299,9 +301,9 @@ __device__ __forceinline__ float tree_sum_sq16(const float* e) {
     return xor_reduce<16>(t, [](float x, float y) { return x + y; });
 }
 
-// Bytes of LDS per wave of the TurboQuant bulk kernels: 128 channels x 8 tokens of binary32
-// residuals (QJL K planes) or of one-byte codes (V planes).
-constexpr int kTurboWaveLds = 8 * kDim * 4;
+// Bytes of LDS per wave of the TurboQuant bulk kernels: 128 channels x 4 tokens of binary32
+// residuals (QJL K planes, one round) or 128 channels x 8 tokens of one-byte codes (V planes).
+constexpr int kTurboWaveLds = 4 * kDim * 4;
 
 // Per-wave constants of a TurboQuant plane.  th: the 7 ascending thresholds; mu: the 8 levels.
 struct TurboTabs {
@@ -328,6 +330,35 @@ __device__ __forceinline__ uint32_t byte_bits(uint32_t x, int k) {
     x = x | (x >> 7);
     x = x | (x >> 14);
     return x & 0xFu;
+}
+
+// acc = (r of lane LN of this 16-lane row) * s + acc with one rounding: v_fmac_f32 with a
+// row_newbcast DPP source, the same binary32 result as fmaf(s, r_LN, acc).
+template <int LN>
+__device__ __forceinline__ void fmac_row_bcast(float& acc, float r, float s) {
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc)
+        : "v"(r), "v"(s), "n"(LN));
+}
+
+// Step j = JJ of the QJL chains of a round's 4 tokens (residual (JJ, token) is value 4 JJ + token,
+// held by lane JJ % 16 of every row in register (JJ / 16, token)).
+template <int JJ>
+__device__ __forceinline__ void qjl_step(const float (&rv)[8][4], const float* st, int L, float* acc0,
+                                         float* acc1) {
+    constexpr int lane = JJ % 16, m = JJ / 16;
+    const float s0 = st[JJ * kDim + L], s1 = st[JJ * kDim + 64 + L];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        fmac_row_bcast<lane>(acc0[c], rv[m][c], s0);
+        fmac_row_bcast<lane>(acc1[c], rv[m][c], s1);
+    }
+}
+
+template <int... JJ>
+__device__ __forceinline__ void qjl_chain(const float (&rv)[8][4], const float* st, int L, float* acc0,
+                                          float* acc1, std::integer_sequence<int, JJ...>) {
+    (qjl_step<JJ>(rv, st, L, acc0, acc1), ...);
 }
 
 // One octet g of a TurboQuant plane (QJL: TurboQuant-QJL K plane; else TurboQuant-MSE, K or V).
@@ -393,53 +424,52 @@ __device__ __forceinline__ void turbo_octet(const WavePlane& w, bool IS_V, int g
         }
         if (QJL) {
             const uint16_t g16 = f16_rn(sqrtf(tree_sum_sq16(rr)));
-            // residual of channel 8j + i of octet token i_tok at wl[(8j + i) * 8 + i_tok]
-#pragma unroll
-            for (int i = 0; i < 8; ++i) wl[(8 * j + i) * 8 + i_tok] = rr[i];
             if (valid && j == 0) {
                 uint16_t* m = reinterpret_cast<uint16_t*>(w.meta + (size_t)row * 4);
                 m[0] = n16;
                 m[1] = g16;
+            }
+            // sign(S r) of this round's 4 tokens: lane L forms projections L and 64 + L, each a
+            // sequential fma chain over j = 0 .. 127.  The residual of channel 8j + i of token
+            // tk goes to wl[(8j + i) * 4 + tk]; then every 16-lane row holds all 512 of them
+            // (value v at lane (v % 64) / 4, register (v / 64, v % 4)) and each fma takes its
+            // residual by a row broadcast; only the rows of S^T come from LDS.
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wl[(8 * j + i) * 4 + tk] = rr[i];
+            __builtin_amdgcn_wave_barrier();
+            float rv[8][4];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float4 x = *reinterpret_cast<const float4*>(wl + 64 * m + 4 * j);
+                rv[m][0] = x.x;
+                rv[m][1] = x.y;
+                rv[m][2] = x.z;
+                rv[m][3] = x.w;
+            }
+            __builtin_amdgcn_wave_barrier();
+            float acc0[4], acc1[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc0[c] = acc1[c] = 0.0f;
+            qjl_chain(rv, st, L, acc0, acc1, std::make_integer_sequence<int, kDim>{});
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint64_t m0 = __ballot(acc0[c] >= 0.0f);
+                const uint64_t m1 = __ballot(acc1[c] >= 0.0f);
+                const int tc = 8 * g + 4 * r + c;
+                if (L == c && tc >= t_lo && tc < t_hi) {
+                    uint4 qw;
+                    qw.x = qdev::unshuffle32((uint32_t)m0);
+                    qw.y = qdev::unshuffle32((uint32_t)(m0 >> 32));
+                    qw.z = qdev::unshuffle32((uint32_t)m1);
+                    qw.w = qdev::unshuffle32((uint32_t)(m1 >> 32));
+                    *reinterpret_cast<uint4*>(qjl_base + (size_t)k_row(tc) * 16) = qw;
+                }
             }
         } else if (valid && j == 0) {
             reinterpret_cast<uint16_t*>(w.meta)[row] = n16;
         }
     }
     __builtin_amdgcn_wave_barrier();
-    if (QJL && !IS_V) {
-        // sign(S r) of the octet's 8 tokens: lane L forms projections L and 64 + L, each a
-        // sequential fma chain over j = 0 .. 127; the rows of S^T are shared by the 8 tokens
-        float acc0[8], acc1[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc0[i] = acc1[i] = 0.0f;
-#pragma unroll 4
-        for (int jj = 0; jj < kDim; ++jj) {
-            const float s0 = st[jj * kDim + L], s1 = st[jj * kDim + 64 + L];
-            const float4 ra = *reinterpret_cast<const float4*>(wl + jj * 8);
-            const float4 rb = *reinterpret_cast<const float4*>(wl + jj * 8 + 4);
-            const float rj[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                acc0[i] = fmaf(s0, rj[i], acc0[i]);
-                acc1[i] = fmaf(s1, rj[i], acc1[i]);
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint64_t m0 = __ballot(acc0[i] >= 0.0f);
-            const uint64_t m1 = __ballot(acc1[i] >= 0.0f);
-            const int t = 8 * g + i;
-            if (L == i && t >= t_lo && t < t_hi) {
-                uint4 qw;
-                qw.x = qdev::unshuffle32((uint32_t)m0);
-                qw.y = qdev::unshuffle32((uint32_t)(m0 >> 32));
-                qw.z = qdev::unshuffle32((uint32_t)m1);
-                qw.w = qdev::unshuffle32((uint32_t)(m1 >> 32));
-                *reinterpret_cast<uint4*>(qjl_base + (size_t)k_row(t) * 16) = qw;
-            }
-        }
-    }
     if (IS_V) {
         // TurboQuant-MSE V block words: bit k of channel d -> word 6 (16 o + d % 16) + 2k + (d / 16) / 4,
         // token i at bit 16 (i % 2) + 4 ((d / 16) % 4) + i / 2.  Lane L (< 32) forms the three words of
