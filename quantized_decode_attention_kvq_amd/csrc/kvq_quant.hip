@@ -65,11 +65,10 @@ __global__ __launch_bounds__(QJL ? 1024 : 256) void quantize_turbo_bulk_kernel(Q
         const int v = 8 * (j & 3) + i; // value index of channel 8j + i in its 32-channel group
         kbit[i] = 1u << (16 * (v & 1) + (v >> 1));
     }
-    qbulk::TurboTabs T;
-#pragma unroll
-    for (int k = 0; k < 7; ++k) T.th[k] = p.theta[k];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) T.mu[k] = p.mu[k];
+    const float* th = p.theta;
+    const float* mu = p.mu;
+    const qbulk::TurboTabs T{th[0], th[1], th[2], th[3], th[4], th[5], th[6],
+                             mu[0], mu[1], mu[2], mu[3], mu[4], mu[5], mu[6], mu[7]};
     const bool is_v = tensor == 1;
     const int g_first = w.start / 8, step = gridDim.x * kW;
     int u = blockIdx.x * kW + wave;

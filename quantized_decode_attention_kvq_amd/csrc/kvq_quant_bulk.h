@@ -305,22 +305,25 @@ __device__ __forceinline__ float tree_sum_sq16(const float* e) {
 // residuals (QJL K planes, one round) or 128 channels x 8 tokens of one-byte codes (V planes).
 constexpr int kTurboWaveLds = 4 * kDim * 4;
 
-// Per-wave constants of a TurboQuant plane.  th: the 7 ascending thresholds; mu: the 8 levels.
+// Per-wave constants of a TurboQuant plane: the 7 ascending thresholds and the 8 levels, as
+// separate values (kept in registers; selects between them never become indexed loads).
 struct TurboTabs {
-    float th[7], mu[8];
+    float t0, t1, t2, t3, t4, t5, t6;
+    float m0, m1, m2, m3, m4, m5, m6, m7;
 };
 
 // Lloyd-Max code of u: the number of thresholds below u, found by a binary search over the
 // ascending thresholds (the same count as comparing u with each of them).  b0, b1, b2: its bits.
-__device__ __forceinline__ void turbo_code(float u, const TurboTabs& T, bool& b0, bool& b1, bool& b2) {
-    b2 = u > T.th[3];
-    b1 = u > (b2 ? T.th[5] : T.th[1]);
-    b0 = u > (b2 ? (b1 ? T.th[6] : T.th[4]) : (b1 ? T.th[2] : T.th[0]));
+__device__ __forceinline__ void turbo_code(float u, const TurboTabs T, bool& b0, bool& b1, bool& b2) {
+    const float t0 = T.t0, t1 = T.t1, t2 = T.t2, t3 = T.t3, t4 = T.t4, t5 = T.t5, t6 = T.t6;
+    b2 = u > t3;
+    b1 = u > (b2 ? t5 : t1);
+    b0 = u > (b2 ? (b1 ? t6 : t4) : (b1 ? t2 : t0));
 }
 
-__device__ __forceinline__ float turbo_level(bool b0, bool b1, bool b2, const TurboTabs& T) {
-    const float hi = b1 ? (b0 ? T.mu[7] : T.mu[6]) : (b0 ? T.mu[5] : T.mu[4]);
-    const float lo = b1 ? (b0 ? T.mu[3] : T.mu[2]) : (b0 ? T.mu[1] : T.mu[0]);
+__device__ __forceinline__ float turbo_level(bool b0, bool b1, bool b2, const TurboTabs T) {
+    const float hi = b1 ? (b0 ? T.m7 : T.m6) : (b0 ? T.m5 : T.m4);
+    const float lo = b1 ? (b0 ? T.m3 : T.m2) : (b0 ? T.m1 : T.m0);
     return b2 ? hi : lo;
 }
 
@@ -366,7 +369,7 @@ __device__ __forceinline__ void qjl_chain(const float (&rv)[8][4], const float* 
 // kbit[i]: 1 << (the bit of channel 8j + i in its K plane words).
 template <bool QJL>
 __device__ __forceinline__ void turbo_octet(const WavePlane& w, bool IS_V, int g, const OctetIn& in,
-                                            const uint32_t* sgm, const TurboTabs& T,
+                                            const uint32_t* sgm, const TurboTabs T,
                                             const uint32_t* kbit, float* wl, const float* st,
                                             uint8_t* qjl_base) {
     const int L = lane_id(), tk = L >> 4, j = L & 15;
