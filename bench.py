@@ -210,6 +210,35 @@ def copy_probe():
                       "launches": 3}), flush=True)
 
 
+def copy_bandwidth():
+    """Device-to-device copy rate on this machine (read + written bytes / time, three 1 GiB copies
+    after one warm-up): what a plain streaming kernel reaches here, beside the 8 TB/s peak."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 3 * 2 * 4 * n / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
+
+
+def gpu_info():
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "compute_units": p.multi_processor_count,
+            "hbm_GiB": round(p.total_memory / 2**30, 1)}
+    arch = getattr(p, "gcnArchName", None)
+    if arch:
+        info["arch"] = arch
+    return info
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,6 +338,8 @@ def main():
         "wall_s": wall,
         "prefill": prefill_report(wl, prefill_s),
     }
+    res["gpu"] = gpu_info()
+    res["gpu"]["copy_GBps"] = copy_bandwidth()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(wl, kv0, args.cpu_budget)

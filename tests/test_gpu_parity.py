@@ -274,6 +274,88 @@ def test_empty_and_single_token(path):
             assert rel_l2(out[0, 3 * h + g].cpu().numpy(), ref) < 1e-5
 
 
+def test_capacity_and_batch_limits_leave_state_unchanged():
+    """A call past max_context or max_batch fails with its status before anything is enqueued:
+    lengths, planes and the output buffer are left as they were."""
+    wl = W.LLAMA3B_3970_PROGRESSIVE
+    case = Case(wl, 90, layers=[0], batch=2, max_context=100)
+    K = case.K
+    case.prefill(0)
+    torch.cuda.synchronize()
+    before = [case.device_plane(0, b, 0, 0) for b in (0, 1)]
+    k = W.gen_kv(wl, 7, 0, 11, batch=2).to("cuda")
+    v = W.gen_kv(wl, 7, 1, 11, batch=2).to("cuda")
+    with pytest.raises(K.KvqError) as e:
+        case.cache.prefill_quantize(0, k, v)  # 90 + 11 > 100
+    assert e.value.name == "KVQ_ERR_CAPACITY"
+    k3 = W.gen_kv(wl, 7, 0, 1, batch=3).to("cuda")
+    v3 = W.gen_kv(wl, 7, 1, 1, batch=3).to("cuda")
+    with pytest.raises(K.KvqError) as e:
+        case.cache.prefill_quantize(0, k3, v3)  # batch 3 > max_batch 2
+    assert e.value.name == "KVQ_ERR_INVALID_ARG"
+    q3 = W.gen_q(wl, 0, 0, batch=3).to("cuda")
+    out3 = torch.full((3, 24, 128), 3.0, device="cuda")
+    with pytest.raises(K.KvqError):
+        case.cache.attn_decode(0, q3, out3)
+    torch.cuda.synchronize()
+    assert case.cache.length(0, 0) == 90 and case.cache.length(0, 1) == 90
+    assert bool((out3 == 3.0).all())
+    for b in (0, 1):
+        for x, y in zip(before[b], case.device_plane(0, b, 0, 0)):
+            if x is not None:
+                assert np.array_equal(x, y)
+    # filling the cache exactly to max_context is allowed
+    k10 = W.gen_kv(wl, 8, 0, 10, batch=2).to("cuda")
+    v10 = W.gen_kv(wl, 8, 1, 10, batch=2).to("cuda")
+    case.cache.prefill_quantize(0, k10, v10)
+    torch.cuda.synchronize()
+    assert case.cache.length(0, 0) == 100
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_max_batch_64_sequences(path):
+    """The largest batch a call takes (64 sequences, ragged lengths): planes of sampled
+    sequences are bit-exact and their attention matches the oracle."""
+    wl = W.LLAMA3B_32K_KVARN
+    B = 64
+    _say("case: batch 64, path", path)
+    case = Case(wl, 160, layers=[0], batch=B, extra_tokens=40)
+    case.prefill(0)
+    # ragged: the first 17 sequences get 23 more tokens
+    k = W.gen_kv(wl, 500, 0, 23, batch=17).to("cuda")
+    v = W.gen_kv(wl, 500, 1, 23, batch=17).to("cuda")
+    case.cache.prefill_quantize(0, k, v)
+    case.cache.set_option(2, path)
+    q = W.gen_q(wl, 0, 0, batch=B).to("cuda")
+    out = torch.full((B, 24, 128), float("nan"), device="cuda")
+    case.cache.attn_decode(0, q, out)
+    torch.cuda.synchronize()
+    assert case.cache.length(0, 0) == 183 and case.cache.length(0, 63) == 160
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    qn = q.float().cpu().numpy()
+    _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS)
+    cap = case.cache.cfg.max_context
+    base_k, base_v = case.kv(0)
+    for b in (0, 16, 17, 63):
+        ref = np.zeros((24, 128))
+        for h in range(8):
+            pl = []
+            for tensor, base, extra in ((0, base_k, k), (1, base_v, v)):
+                X = base[b, :, h].float().cpu().numpy()
+                if b < 17:
+                    X = np.concatenate([X, extra[b, :, h].float().cpu().numpy()])
+                tb = case.oracle_tables(0, h, tensor, mu, theta)
+                p = oracle.Plane(W.UNIFORM, 4, True, True, 0, tensor, cap)
+                p.append(X, tb)
+                if h in (0, 7):
+                    compare_plane(case.device_plane(0, b, h, tensor), p, f"seq {b} head {h} tensor {tensor}")
+                pl += [p, tb]
+            ref[h * 3:h * 3 + 3] = oracle.attention(pl[0], pl[2], pl[1], pl[3], qn[b, h * 3:h * 3 + 3])
+        r, m = rel_l2(got[b], ref), max_abs(got[b], ref)
+        assert r <= REL_L2_TOL and m <= MAX_ABS_TOL, (b, r, m)
+
+
 def _planes_equal(a, b, li, batch, n_heads):
     for s in range(batch):
         for h in range(n_heads):
