@@ -91,6 +91,10 @@ def lib():
                                     ctypes.POINTER(Tables), ctypes.POINTER(Tables), _U8, _U8, _U8,
                                     _F, _U8, _U8, _F, ctypes.c_int, ctypes.c_int, _F,
                                     ctypes.c_double, _Dp]
+        L.orc_attention_prefix.argtypes = [ctypes.POINTER(PlaneCfg), ctypes.POINTER(PlaneCfg),
+                                           ctypes.POINTER(Tables), ctypes.POINTER(Tables), _U8,
+                                           _U8, _U8, _F, _U8, _U8, _F, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, _F, ctypes.c_double, _Dp]
         _lib = L
     return _lib
 
@@ -277,4 +281,20 @@ def attention(kplane: Plane, vplane: Plane, ktables: TableSet, vtables: TableSet
                         _p(kplane.codes, _U8), _p(kplane.meta, _U8), _p(kplane.qjl, _U8),
                         _p(kplane.ring, _F), _p(vplane.codes, _U8), _p(vplane.meta, _U8),
                         _p(vplane.ring, _F), n, G, _p(q, _F), scale, _p(out, _Dp))
+    return out
+
+
+def attention_prefix(kplane: Plane, vplane: Plane, ktables: TableSet, vtables: TableSet, q,
+                     n_vis, scale=None):
+    """fp64 attention of G = q.shape[0] query heads over tokens 0 .. n_vis - 1 of the cache as it
+    stands (the FP32 window is chosen by the cache length): one query of a prefill chunk."""
+    q = _f32(q).reshape(-1, D)
+    G = q.shape[0]
+    scale = 1.0 / np.sqrt(128.0) if scale is None or scale <= 0 else float(scale)
+    out = np.empty((G, D), np.float64)
+    lib().orc_attention_prefix(kplane.ref, vplane.ref, ktables.ref, vtables.ref,
+                               _p(kplane.codes, _U8), _p(kplane.meta, _U8), _p(kplane.qjl, _U8),
+                               _p(kplane.ring, _F), _p(vplane.codes, _U8), _p(vplane.meta, _U8),
+                               _p(vplane.ring, _F), kplane.length, int(n_vis), G, _p(q, _F), scale,
+                               _p(out, _Dp))
     return out

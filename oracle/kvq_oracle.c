@@ -19,7 +19,10 @@
  *                             product.
  *   window .................. quantcpp article, progressive paragraph: the most recent 128
  *                             tokens stay FP32, everything else 4-bit.
- *   attention ............... plain softmax(q k^T * scale) v on the dequantized cache.
+ *   attention ............... plain softmax(q k^T * scale) v on the dequantized cache; the
+ *                             prefix form serves the queries of a prefill chunk, each seeing
+ *                             the tokens up to its own position (quantcpp article, v3.2 batched
+ *                             prefill: the prompt is processed as whole chunks).
  */
 #include "kvq_oracle.h"
 
@@ -641,16 +644,21 @@ double orc_turbo_score(const orc_tables* tb, const uint8_t* codes, const uint8_t
     return n * a + gam * sqrt(ORC_PI / 2.0) / 128.0 * b;
 }
 
-void orc_attention(const orc_plane_cfg* kc, const orc_plane_cfg* vc, const orc_tables* ktb,
-                   const orc_tables* vtb, const uint8_t* kcodes, const uint8_t* kmeta,
-                   const uint8_t* kqjl, const float* kring, const uint8_t* vcodes,
-                   const uint8_t* vmeta, const float* vring, int n, int G, const float* q,
-                   double scale, double* out)
+/* Attention of G query heads over the first n_vis tokens of a cache holding n tokens
+ * (1 <= n_vis <= n).  Which tokens are read from the FP32 window depends on n (the cache as it
+ * stands), not on n_vis: a query of a prefill chunk at position n_vis - 1 sees the same token
+ * values as a decode query would, cut off at its own position (causal). */
+void orc_attention_prefix(const orc_plane_cfg* kc, const orc_plane_cfg* vc,
+                          const orc_tables* ktb, const orc_tables* vtb, const uint8_t* kcodes,
+                          const uint8_t* kmeta, const uint8_t* kqjl, const float* kring,
+                          const uint8_t* vcodes, const uint8_t* vmeta, const float* vring, int n,
+                          int n_vis, int G, const float* q, double scale, double* out)
 {
-    if (n <= 0) {
+    if (n <= 0 || n_vis <= 0) {
         for (int i = 0; i < G * D; i++) out[i] = 0.0;
         return;
     }
+    if (n_vis > n) n_vis = n;
     int W = kc->window;
     int nq = (W > 0 && n > W) ? n - W : (W > 0 ? 0 : n); /* tokens read from the codes */
     double* V = (double*)malloc(sizeof(double) * (size_t)n * D);
@@ -683,7 +691,7 @@ void orc_attention(const orc_plane_cfg* kc, const orc_plane_cfg* vc, const orc_t
             }
         }
         double mx = -INFINITY;
-        for (int t = 0; t < n; t++) {
+        for (int t = 0; t < n_vis; t++) {
             double s;
             if (K || t >= nq) {
                 s = 0.0;
@@ -702,7 +710,7 @@ void orc_attention(const orc_plane_cfg* kc, const orc_plane_cfg* vc, const orc_t
         double l = 0.0;
         double o[D];
         for (int j = 0; j < D; j++) o[j] = 0.0;
-        for (int t = 0; t < n; t++) {
+        for (int t = 0; t < n_vis; t++) {
             double p = exp(a[t] - mx);
             l += p;
             for (int j = 0; j < D; j++) o[j] += p * V[(size_t)t * D + j];
@@ -712,4 +720,15 @@ void orc_attention(const orc_plane_cfg* kc, const orc_plane_cfg* vc, const orc_t
     free(a);
     free(V);
     free(K);
+}
+
+/* Decode attention: every token of the cache is visible. */
+void orc_attention(const orc_plane_cfg* kc, const orc_plane_cfg* vc, const orc_tables* ktb,
+                   const orc_tables* vtb, const uint8_t* kcodes, const uint8_t* kmeta,
+                   const uint8_t* kqjl, const float* kring, const uint8_t* vcodes,
+                   const uint8_t* vmeta, const float* vring, int n, int G, const float* q,
+                   double scale, double* out)
+{
+    orc_attention_prefix(kc, vc, ktb, vtb, kcodes, kmeta, kqjl, kring, vcodes, vmeta, vring, n, n,
+                         G, q, scale, out);
 }

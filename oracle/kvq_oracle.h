@@ -106,6 +106,14 @@ void orc_dequant_token(const orc_plane_cfg* pc, const orc_tables* tb, const uint
 double orc_turbo_score(const orc_tables* tb, const uint8_t* codes, const uint8_t* meta,
                        const uint8_t* qjl, int t, const double* rho_q, const double* s_rho_q);
 
+/* Attention of one kv head's G query heads over tokens 0 .. n_vis - 1 of a cache of n tokens
+ * (window tokens chosen by n), fp64. */
+void orc_attention_prefix(const orc_plane_cfg* kc, const orc_plane_cfg* vc,
+                          const orc_tables* ktb, const orc_tables* vtb, const uint8_t* kcodes,
+                          const uint8_t* kmeta, const uint8_t* kqjl, const float* kring,
+                          const uint8_t* vcodes, const uint8_t* vmeta, const float* vring, int n,
+                          int n_vis, int G, const float* q, double scale, double* out);
+
 /* Decode attention for one kv head and its G query heads, fp64. */
 void orc_attention(const orc_plane_cfg* kc, const orc_plane_cfg* vc, const orc_tables* ktb,
                    const orc_tables* vtb, const uint8_t* kcodes, const uint8_t* kmeta,

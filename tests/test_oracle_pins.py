@@ -597,6 +597,69 @@ def test_attention_window_only_equals_textbook():
     assert np.allclose(oracle.attention(pk, pv, tb, tb, q), _textbook(q, Kd, Vd), atol=1e-12)
 
 
+def test_attention_prefix_full_equals_decode_and_first_token():
+    """The prefix form with every token visible is the decode attention; with one visible token
+    every head returns that token's value."""
+    rng = np.random.default_rng(130)
+    n, G = 70, 3
+    K = rng.standard_normal((n, 128)).astype(np.float32)
+    V = rng.standard_normal((n, 128)).astype(np.float32)
+    q = rng.standard_normal((G, 128)).astype(np.float32)
+    tb = oracle.TableSet()
+    pk = oracle.Plane(oracle.UNIFORM, 4, False, False, 0, oracle.TENSOR_K, 128)
+    pv = oracle.Plane(oracle.UNIFORM, 4, False, False, 0, oracle.TENSOR_V, 128)
+    pk.append(K, tb)
+    pv.append(V, tb)
+    assert np.array_equal(oracle.attention_prefix(pk, pv, tb, tb, q, n), oracle.attention(pk, pv, tb, tb, q))
+    first = oracle.attention_prefix(pk, pv, tb, tb, q, 1)
+    v0 = pv.dequant(0, tb)
+    for h in range(G):
+        assert np.allclose(first[h], v0, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_attention_prefix_causal_equals_textbook(bits):
+    """On tokens the quantizer reproduces exactly, the query at position p is the textbook
+    softmax attention over tokens 0 .. p."""
+    rng = np.random.default_rng(140 + bits)
+    n, G = 37, 3
+    K, V = _grid_tokens(rng, n, bits), _grid_tokens(rng, n, bits)
+    q = rng.standard_normal((G, 128)).astype(np.float32)
+    tb = oracle.TableSet()
+    pk = oracle.Plane(oracle.UNIFORM, bits, False, False, 0, oracle.TENSOR_K, 64)
+    pv = oracle.Plane(oracle.UNIFORM, bits, False, False, 0, oracle.TENSOR_V, 64)
+    pk.append(K, tb)
+    pv.append(V, tb)
+    for pos in (0, 5, 17, 36):
+        got = oracle.attention_prefix(pk, pv, tb, tb, q, pos + 1)
+        assert np.allclose(got, _textbook(q, K[:pos + 1], V[:pos + 1]), rtol=0, atol=1e-12), pos
+
+
+def test_attention_prefix_window_follows_cache_length():
+    """With an FP32 window the tokens read as originals are the newest W of the cache as it
+    stands, whatever the query's position."""
+    rng = np.random.default_rng(150)
+    n, W, G, vis = 300, 128, 3, 250
+    K = rng.standard_normal((n, 128)).astype(np.float32)
+    V = rng.standard_normal((n, 128)).astype(np.float32)
+    q = rng.standard_normal((G, 128)).astype(np.float32)
+    tb = oracle.TableSet()
+    pk = oracle.Plane(oracle.UNIFORM, 4, False, False, W, oracle.TENSOR_K, 320)
+    pv = oracle.Plane(oracle.UNIFORM, 4, False, False, W, oracle.TENSOR_V, 320)
+    pk.append(K, tb)
+    pv.append(V, tb)
+    Kd, Vd = K.astype(np.float64).copy(), V.astype(np.float64).copy()
+    for t in range(n - W):
+        Kd[t] = pk.dequant(t, tb)
+        Vd[t] = pv.dequant(t, tb)
+    got = oracle.attention_prefix(pk, pv, tb, tb, q, vis)
+    assert np.allclose(got, _textbook(q, Kd[:vis], Vd[:vis]), rtol=0, atol=1e-12)
+    # not the reading where the window would trail the query (tokens vis - W .. vis - 1)
+    Kt, Vt = Kd[:vis].copy(), Vd[:vis].copy()
+    Kt[vis - W:], Vt[vis - W:] = K[vis - W:vis], V[vis - W:vis]
+    assert not np.allclose(got, _textbook(q, Kt, Vt), rtol=0, atol=1e-6)
+
+
 def test_attention_single_token_and_equal_keys():
     rng = np.random.default_rng(120)
     tb = oracle.TableSet()
