@@ -178,6 +178,20 @@ kvq_status kvq_append_attn_decode(kvq_cache* cache, int layer, const void* k, co
                                   const void* q, int dtype, float* out, int batch,
                                   float softmax_scale, void* stream);
 
+/* Attention of a prefill chunk ([P1] v3.2 batched prefill: the prompt goes through in whole
+ * chunks; keys and values as for kvq_attn_decode).  The n_q newest tokens of each of the first
+ * `batch` sequences are the queries: they must already be in the cache (kvq_prefill_quantize),
+ * and query i of sequence b, at position pos = len[b] - n_q + i, attends to tokens 0 .. pos of
+ * the cache as it stands: out[b][i][h] = sum_{t <= pos} softmax_t(scale <q[b][i][h], k_t>) v_t.
+ * q: device [batch][n_q][n_q_heads][128] of dtype; out: device [batch][n_q][n_q_heads][128]
+ * fp32 (row-major, 16-byte aligned).  softmax_scale <= 0 means 1/sqrt(128).
+ * Errors (nothing enqueued): KVQ_ERR_INVALID_ARG for a bad handle, layer, pointer, dtype, batch
+ * outside 1 .. max_batch, n_q < 1, or n_q above some sequence's length; KVQ_ERR_MISALIGNED;
+ * KVQ_ERR_NOT_READY before the layer's tables / calibration are set; KVQ_ERR_UNSUPPORTED for
+ * TurboQuant planes and for caches with an FP32 window (this kernel reads uniform codes only). */
+kvq_status kvq_attn_prefill(kvq_cache* cache, int layer, const void* q, int dtype, float* out,
+                            int n_q, int batch, float softmax_scale, void* stream);
+
 /* Plane pointers and sizes of (layer, seq, kv_head, tensor 0 = K / 1 = V). */
 kvq_status kvq_get_layout(const kvq_cache* cache, int layer, int seq, int kv_head, int tensor,
                           kvq_layout* out);

@@ -56,6 +56,9 @@ class KvCache:
     def append_attn_decode(self, layer, k, v, q, out, softmax_scale=0.0, stream=None):
         _kvq.kvq_append_attn_decode(self.handle, layer, k, v, q, out, softmax_scale, stream)
 
+    def attn_prefill(self, layer, q, out, softmax_scale=0.0, stream=None):
+        _kvq.kvq_attn_prefill(self.handle, layer, q, out, softmax_scale, stream)
+
     def set_option(self, option, value):
         _kvq.kvq_set_option(self.handle, option, value)
 

@@ -21,8 +21,8 @@ STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_INVALID_ARG", 2: "KVQ_ERR_UNSUPPORTED", 3: "K
 EXPORTS = ["kvq_cache_required_bytes", "kvq_cache_create", "kvq_cache_destroy",
            "kvq_set_random_tables", "kvq_calibrate", "kvq_prefill_quantize", "kvq_append",
            "kvq_attn_decode", "kvq_get_layout", "kvq_get_tables", "kvq_set_option",
-           "kvq_set_timing_events", "kvq_append_attn_decode", "kvq_get_length", "kvq_status_str",
-           "kvq_last_hip_error"]
+           "kvq_set_timing_events", "kvq_append_attn_decode", "kvq_attn_prefill",
+           "kvq_get_length", "kvq_status_str", "kvq_last_hip_error"]
 
 
 class KvqError(RuntimeError):
@@ -74,6 +74,7 @@ def load():
         "kvq_append": [vp, i, vp, vp, i, i, vp],
         "kvq_attn_decode": [vp, i, vp, i, vp, i, f, vp],
         "kvq_append_attn_decode": [vp, i, vp, vp, vp, i, vp, i, f, vp],
+        "kvq_attn_prefill": [vp, i, vp, i, vp, i, i, f, vp],
         "kvq_get_layout": [vp, i, i, i, i, ctypes.POINTER(kvq_layout)],
         "kvq_get_tables": [vp, ctypes.POINTER(kvq_tables)],
         "kvq_set_option": [vp, i, i],
@@ -170,6 +171,12 @@ def kvq_attn_decode(h, layer, q, out, softmax_scale=0.0, stream=None):
     """q: [batch][n_q_heads][128]; out: [batch][n_q_heads][128] fp32."""
     _check(load().kvq_attn_decode(h, layer, _ptr(q), _dtype(q), _ptr(out), q.shape[0],
                                   float(softmax_scale), _stream(stream)), "kvq_attn_decode")
+
+
+def kvq_attn_prefill(h, layer, q, out, softmax_scale=0.0, stream=None):
+    """q: [batch][n_q][Hq][128] (f32 or bf16), out: [batch][n_q][Hq][128] f32."""
+    _check(load().kvq_attn_prefill(h, layer, _ptr(q), _dtype(q), _ptr(out), q.shape[1], q.shape[0],
+                                   float(softmax_scale), _stream(stream)), "kvq_attn_prefill")
 
 
 def kvq_append_attn_decode(h, layer, k, v, q, out, softmax_scale=0.0, stream=None):

@@ -29,6 +29,7 @@ UNITS = [
     ("kvq_quant.hip", DEVICE + ["-ffp-contract=off"]),
     ("kvq_decode.hip", DEVICE),
     ("kvq_decode_mfma.hip", DEVICE + ["-ffp-contract=off"]),  # holds the fused append
+    ("kvq_prefill_attn.hip", DEVICE),
     ("kvq_host.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]),  # host only
 ]
 

@@ -488,6 +488,37 @@ kvq_status kvq_append_attn_decode(kvq_cache* c, int layer, const void* k, const 
     return KVQ_OK;
 }
 
+kvq_status kvq_attn_prefill(kvq_cache* c, int layer, const void* q, int dtype, float* out, int n_q,
+                            int batch, float softmax_scale, void* stream) {
+    kvq_status st = check_decode(c, layer, q, dtype, out, batch, softmax_scale);
+    if (st != KVQ_OK) return st;
+    if (n_q < 1) return KVQ_ERR_INVALID_ARG;
+    PrefillParams p{};
+    p.q = q;
+    p.out = out;
+    fill_params_common(c, layer, p.layer_base, p.seq_stride, p.head_stride, p.plane_off, p.geom);
+    p.signs = c->signs() + c->table_off(layer);
+    p.cs = c->cs() + c->table_off(layer);
+    p.dtype = dtype;
+    p.batch = batch;
+    p.n_q = n_q;
+    p.Hq = c->cfg.n_q_heads;
+    p.Hkv = c->cfg.n_kv_heads;
+    p.G = p.Hq / p.Hkv;
+    p.window = c->cfg.fp32_window;
+    const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(128.0f);
+    p.qscale = scale * 1.4426950408889634f;
+    const int* len = &c->len[(size_t)layer * c->cfg.max_batch];
+    for (int b = 0; b < batch; ++b) {
+        if (n_q > len[b]) return KVQ_ERR_INVALID_ARG;
+        p.len[b] = len[b];
+    }
+    if (!prefill_attn_supported(p)) return KVQ_ERR_UNSUPPORTED;
+    const hipError_t e = launch_prefill_attn(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return dev_fail(c, e);
+    return KVQ_OK;
+}
+
 kvq_status kvq_get_layout(const kvq_cache* c, int layer, int seq, int kv_head, int tensor,
                           kvq_layout* out) {
     if (!c || !out) return KVQ_ERR_INVALID_ARG;

@@ -67,6 +67,22 @@ struct DecodeParams {
     QuantParams append;
 };
 
+// Parameters of the prefill-chunk attention kernel: the n_q newest tokens of each sequence are
+// the queries, each attending to the cache up to its own position.
+struct PrefillParams {
+    const void* q;            // [batch][n_q][Hq][128] of dtype
+    float* out;               // [batch][n_q][Hq][128]
+    char* layer_base;
+    size_t seq_stride, head_stride;
+    size_t plane_off[2];
+    PlaneGeom geom[2];
+    const float* signs;       // layer base [Hkv][2][128]
+    const float* cs;          // layer base [Hkv][2][128] Sinkhorn c
+    int dtype, batch, n_q, Hq, Hkv, G, window;
+    float qscale;             // softmax scale * log2(e)
+    int len[kMaxBatch];
+};
+
 struct CalibParams {
     const void* src[2];       // [n][Hkv][128] of dtype
     double* work;             // [2][Hkv][n][128], then [2][Hkv][128] twice (column scales)
@@ -96,5 +112,7 @@ hipError_t launch_decode_vec(const DecodeParams& p, hipStream_t s, hipEvent_t ev
 hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t s);
 bool mfma_path_supported(const DecodeParams& p);
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+bool prefill_attn_supported(const PrefillParams& p);
+hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
 
 } // namespace kvq

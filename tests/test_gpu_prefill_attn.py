@@ -1,0 +1,120 @@
+"""GPU parity of the prefill-chunk attention (kvq_attn_prefill) against the oracle's prefix
+attention: the n_q newest tokens of each sequence are the queries, query i at position
+len - n_q + i sees tokens 0 .. len - n_q + i of the cache as it stands.
+
+Bar: 2e-3 relative L2 and 1e-2 max-abs per (sequence, query token) output [Hq x 128].
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from kvq_testlib import MAX_ABS_TOL, REL_L2_TOL, Case, max_abs, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _run(wl, n0, B, nb, ne, n_q, seed=0):
+    """Every sequence gets n0 tokens; the first nb of them ne more in a second call (ragged
+    lengths); then n_q queries per sequence over the cache as it stands."""
+    case = Case(wl, n0, layers=[0], batch=B, max_context=n0 + ne)
+    case.prefill(0)
+    streams = {b: [x[b].float().cpu().numpy() for x in case.kv(0)] for b in range(B)}
+    if nb:
+        k = W.gen_kv(wl, 900 + seed, 0, ne, batch=nb)
+        v = W.gen_kv(wl, 900 + seed, 1, ne, batch=nb)
+        case.cache.prefill_quantize(0, k.to("cuda"), v.to("cuda"))
+        for b in range(nb):
+            streams[b][0] = np.concatenate([streams[b][0], k[b].float().numpy()])
+            streams[b][1] = np.concatenate([streams[b][1], v[b].float().numpy()])
+    g = torch.Generator().manual_seed(1234 + seed)
+    q = torch.randn((B, n_q, wl.n_q_heads, 128), generator=g)
+    if wl.dtype == "bf16":
+        q = q.to(torch.bfloat16)
+    out = torch.full((B, n_q, wl.n_q_heads, 128), float("nan"), device="cuda")
+    case.cache.attn_prefill(0, q.to("cuda"), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    qn = q.float().numpy()
+    _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS)
+    cap = case.cache.cfg.max_context
+    G = wl.group
+    worst = (0.0, 0.0)
+    for b in range(B):
+        n = streams[b][0].shape[0]
+        assert case.cache.length(0, b) == n
+        planes = []
+        for h in range(wl.n_kv_heads):
+            row = []
+            for tensor in (0, 1):
+                scheme = wl.k_scheme if tensor == 0 else wl.v_scheme
+                bits = wl.k_bits if tensor == 0 else wl.v_bits
+                rot = (wl.rotate_k if tensor == 0 else wl.rotate_v) or scheme != W.UNIFORM
+                sink = wl.sinkhorn_iters > 0 and scheme == W.UNIFORM
+                tb = case.oracle_tables(0, h, tensor, mu, theta)
+                pl = oracle.Plane(scheme, bits, rot, sink, wl.window, tensor, cap)
+                pl.append(streams[b][tensor][:, h], tb)
+                row += [pl, tb]
+            planes.append(row)
+        for i in range(n_q):
+            pos = n - n_q + i
+            ref = np.zeros((wl.n_q_heads, 128))
+            for h in range(wl.n_kv_heads):
+                pk, tk, pv, tv = planes[h]
+                ref[h * G:(h + 1) * G] = oracle.attention_prefix(pk, pv, tk, tv, qn[b, i, h * G:(h + 1) * G], pos + 1)
+            r, m = rel_l2(got[b, i], ref), max_abs(got[b, i], ref)
+            worst = (max(worst[0], r), max(worst[1], m))
+            assert r <= REL_L2_TOL and m <= MAX_ABS_TOL, (b, i, pos, r, m)
+    _say(f"  {wl.name} batch {B} n_q {n_q}: rel_l2 <= {worst[0]:.2e}, max_abs <= {worst[1]:.2e}")
+    return case, got, q
+
+
+@pytest.mark.parametrize("n_q", [1, 37, 130])
+def test_prefill_attention_kvarn(n_q):
+    _say("case: prefill attention, KVarN U4, n_q", n_q)
+    _run(W.LLAMA3B_32K_KVARN, n0=220, B=2, nb=1, ne=40, n_q=n_q)
+
+
+@pytest.mark.parametrize("wl", [W.DENSE27B_120K_U8, W.DENSE27B_120K_KVARN], ids=lambda w: w.name)
+def test_prefill_attention_dense27b_gqa5_bf16(wl):
+    _say("case: prefill attention,", wl.name)
+    _run(wl, n0=150, B=3, nb=2, ne=33, n_q=70, seed=1)
+
+
+def test_prefill_attention_asym_bits_and_long_chunk():
+    # 8-bit K with 4-bit V (uniform, no rotation), a chunk longer than the two-tile boundary
+    wl = W.LLAMA3B_3970_PROGRESSIVE.with_(window=0, k_bits=8)
+    _say("case: prefill attention, U8 K / U4 V, n_q 200")
+    _run(wl, n0=520, B=1, nb=0, ne=0, n_q=200, seed=2)
+
+
+def test_prefill_attention_last_token_equals_decode():
+    wl = W.LLAMA3B_32K_KVARN
+    case, got, q = _run(wl, n0=333, B=1, nb=0, ne=0, n_q=1, seed=3)
+    out = torch.empty((1, wl.n_q_heads, 128), device="cuda")
+    case.cache.attn_decode(0, q[:, 0].contiguous().to("cuda"), out)
+    torch.cuda.synchronize()
+    assert rel_l2(got[0, 0], out.cpu().numpy()[0]) <= REL_L2_TOL
+
+
+def test_prefill_attention_refusals():
+    import quantized_decode_attention_kvq_amd as K
+    # FP32 window and TurboQuant planes are not read by this kernel; n_q beyond a length
+    for wl, n, nq, name in ((W.LLAMA3B_3970_PROGRESSIVE, 200, 10, "KVQ_ERR_UNSUPPORTED"),
+                            (W.LLAMA3B_32K_TURBO, 200, 10, "KVQ_ERR_UNSUPPORTED"),
+                            (W.LLAMA3B_32K_KVARN, 200, 201, "KVQ_ERR_INVALID_ARG")):
+        case = Case(wl, n, layers=[0], batch=1)
+        case.prefill(0)
+        q = torch.zeros((1, nq, wl.n_q_heads, 128), device="cuda")
+        out = torch.full((1, nq, wl.n_q_heads, 128), 5.0, device="cuda")
+        with pytest.raises(K.KvqError) as e:
+            case.cache.attn_prefill(0, q, out)
+        assert e.value.name == name
+        torch.cuda.synchronize()
+        assert bool((out == 5.0).all())
