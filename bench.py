@@ -28,6 +28,7 @@ import workloads as W  # noqa: E402
 
 METRIC = "decode-attn queries/s + achieved HBM GB/s (% peak) at 32K/128K, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak (no sparsity)
 
 
 def token_head_bytes(scheme, bits):
@@ -229,6 +230,44 @@ def copy_bandwidth():
     return gbps
 
 
+def prefill_attention_report(cache, wl: W.Workload, n_q: int = 512, reps: int = 5):
+    """kvq_attn_prefill of an n_q-token chunk at the end of layer 0's cache (the chunk's queries
+    see the cache up to their own positions), timed with events on the launch stream.  Bound:
+    the fp16 matrix cores; algorithmic flops = 4 * 128 * Hq * sum_i (visible tokens of query i)
+    per sequence (QK^T and PV, multiply-adds counted as two)."""
+    import quantized_decode_attention_kvq_amd as K
+    B = wl.batch
+    n = cache.length(0)
+    if n < n_q:
+        return None
+    g = torch.Generator(device="cuda").manual_seed(7)
+    q = torch.randn((B, n_q, wl.n_q_heads, 128), generator=g, device="cuda")
+    if wl.dtype == "bf16":
+        q = q.to(torch.bfloat16)
+    out = torch.empty((B, n_q, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
+    try:
+        cache.attn_prefill(0, q, out)
+    except K.KvqError as e:
+        return {"supported": False, "status": e.name}
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        cache.attn_prefill(0, q, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    visible = sum(n - n_q + i + 1 for i in range(n_q))
+    flops = 4.0 * 128 * wl.n_q_heads * visible * B
+    tflops = flops / sec / 1e12
+    return {"supported": True, "n_q": n_q, "context": n, "us_per_call": 1e6 * sec,
+            "query_tokens_per_s": B * n_q / sec,
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tflops / MFMA_F16_PEAK_TFLOPS,
+                         "flops_per_call": flops}}
+
+
 def gpu_info():
     p = torch.cuda.get_device_properties(0)
     info = {"name": p.name, "compute_units": p.multi_processor_count,
@@ -338,6 +377,7 @@ def main():
         "wall_s": wall,
         "prefill": prefill_report(wl, prefill_s),
     }
+    res["prefill_attention"] = prefill_attention_report(cache, wl)
     res["gpu"] = gpu_info()
     res["gpu"]["copy_GBps"] = copy_bandwidth()
     if not args.no_cpu_baseline:

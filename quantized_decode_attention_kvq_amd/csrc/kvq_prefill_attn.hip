@@ -18,9 +18,9 @@
 //    operands (the decode kernel's operand forms).  The token's fp16 scale and zero fold in
 //    afterwards: s = sum_g scale_g D_g + zero_g sum_{j in g} q'_j.
 //  * Online softmax per query row in the log2 domain; tokens after a row's position are masked.
-//  * PV: A = p * scale_g (fp16 hi and lo as two operands) staged through LDS, B = centred V codes
-//    c - 8 (c - 128) as exact fp16 integers; the zero-point term sum p (zero + 8 scale) on the
-//    vector ALU.
+//  * PV: A = p * scale_g in fp16 (p in [0, 1]: a relative rounding of 2^-12 per weight, which
+//    averages out over the tokens) staged through LDS, B = centred V codes c - 8 (c - 128) as
+//    exact fp16 integers; the zero-point term sum p (zero + 8 scale) on the vector ALU in fp32.
 //  * Each row's output is divided by its softmax sum and mapped back with c_V and R_V^-1.
 // Planes with an FP32 window, or TurboQuant planes, are refused by the host (not supported by
 // this kernel).
@@ -39,7 +39,9 @@ using namespace mops;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kWaves = 4;              // waves per workgroup (16 query rows each)
 constexpr int kPR = 72;                // halves per staged P row: 64 tokens + 8 pad
-constexpr int kStage = 2 * 4 * 16 * kPR; // halves per wave: [hi | lo][group][16 rows][token]
+constexpr int kStage = 4 * 16 * kPR;   // halves per wave: [group][16 rows][token], and the
+                                       // [16][128] float rows before and after the loop
+static_assert(kStage * 2 >= 16 * kDim * 4, "row scratch fits the staging area");
 
 __device__ __forceinline__ float wave_max(float v) {
     return xor_reduce<64>(v, [](float x, float y) { return fmaxf(x, y); });
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams
     __builtin_amdgcn_wave_barrier();
 
     float m_run[4], l_run[4], z_run[4][4];
-    f4 accH[8], accL[8];
+    f4 acc[8];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         m_run[v] = kNegInf;
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams
         for (int g = 0; g < 4; ++g) z_run[v][g] = 0.0f;
     }
 #pragma unroll
-    for (int n = 0; n < 8; ++n) accH[n] = accL[n] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int n = 0; n < 8; ++n) acc[n] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int kend = min(N, P0 + i0 + rows); // keys this wave needs: 0 .. kend - 1
     const int nch = (kend + 63) / 64;
@@ -221,7 +223,8 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams
 
         // ---- online softmax per row (state per lane: its 4 tokens; the row max over the
         // row's 16 lanes)
-        float pj[4][4];
+        float pj[4][4], al[4];
+        bool grew = false;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             float t = fmaxf(fmaxf(raw[0][v], raw[1][v]), fmaxf(raw[2][v], raw[3][v]));
@@ -236,17 +239,21 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams
                 s += pj[j][v];
             }
             l_run[v] = l_run[v] * alpha + s;
+            grew |= mnew > m_run[v];
             m_run[v] = mnew;
+            al[v] = alpha;
+        }
+        if (__ballot(grew) != 0) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) z_run[v][g] *= alpha;
+            for (int v = 0; v < 4; ++v) {
 #pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                accH[n][v] *= alpha;
-                accL[n][v] *= alpha;
+                for (int g = 0; g < 4; ++g) z_run[v][g] *= al[v];
+#pragma unroll
+                for (int n = 0; n < 8; ++n) acc[n][v] *= al[v];
             }
         }
 
-        // ---- zero-point term and the PV A operands: [hi | lo][g][row][token 4 lr + j]
+        // ---- zero-point term and the PV A operands: p * scale_g in fp16, [g][row][token 4 lr + j]
         constexpr float mid = (VB == 4) ? 8.0f : 128.0f; // codes enter as c - mid
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -261,20 +268,16 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams
         for (int g = 0; g < 4; ++g) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                h4 hv, lv;
+                h4 hv;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t w = (g < 2) ? vm[j].x : vm[j].y;
                     const float sg = (g & 1) ? hi_h(w) : lo_h(w);
                     const float wt = (VB == 4 && j < 2) ? 16.0f : 1.0f;
-                    const float x = pj[j][v] * sg * wt;
-                    const _Float16 xh = (_Float16)x;
-                    hv[j] = xh;
-                    lv[j] = (_Float16)((x - (float)xh) * kLoScale);
+                    hv[j] = (_Float16)(pj[j][v] * sg * wt);
                 }
                 const int row = 4 * lq + v;
-                *reinterpret_cast<h4*>(my_stage + (0 * 4 + g) * 16 * kPR + row * kPR + 4 * lr) = hv;
-                *reinterpret_cast<h4*>(my_stage + (1 * 4 + g) * 16 * kPR + row * kPR + 4 * lr) = lv;
+                *reinterpret_cast<h4*>(my_stage + g * 16 * kPR + row * kPR + 4 * lr) = hv;
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -284,12 +287,10 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams
         // ---- PV over the chunk's two 32-token blocks
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            h8 Ph[4], Pl[4];
+            h8 Ph[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                Ph[g] = *reinterpret_cast<const h8*>(my_stage + (0 * 4 + g) * 16 * kPR + lr * kPR + 32 * k + 8 * lq);
-                Pl[g] = *reinterpret_cast<const h8*>(my_stage + (1 * 4 + g) * 16 * kPR + lr * kPR + 32 * k + 8 * lq);
-            }
+            for (int g = 0; g < 4; ++g)
+                Ph[g] = *reinterpret_cast<const h8*>(my_stage + g * 16 * kPR + lr * kPR + 32 * k + 8 * lq);
 #pragma unroll
             for (int n = 0; n < 8; ++n) {
                 h8 Bv;
@@ -297,8 +298,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams
                     Bv = as_h8(centred4(vc[k][n >> 2][n & 3]));
                 else
                     Bv = as_h8(centred8(vc[k][n >> 1][2 * (n & 1)], vc[k][n >> 1][2 * (n & 1) + 1]));
-                accH[n] = mfma16(Ph[n >> 1], Bv, accH[n]);
-                accL[n] = mfma16(Pl[n >> 1], Bv, accL[n]);
+                acc[n] = mfma16(Ph[n >> 1], Bv, acc[n]);
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams
     for (int n = 0; n < 8; ++n)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const float a = fmaf(accL[n][v], kLoInv, accH[n][v]) * UV + zt[v][n >> 1];
+            const float a = acc[n][v] * UV + zt[v][n >> 1];
             s_row[(4 * lq + v) * kDim + 16 * n + lr] = (lt[v] > 0.0f) ? a / lt[v] : 0.0f;
         }
     __builtin_amdgcn_wave_barrier();
