@@ -246,6 +246,7 @@ def prefill_attention_report(cache, wl: W.Workload, n_q: int = 512, reps: int = 
         q = q.to(torch.bfloat16)
     out = torch.empty((B, n_q, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
     try:
+        ws_bytes = cache.attn_prefill_workspace(0, n_q, B)
         cache.attn_prefill(0, q, out)
     except K.KvqError as e:
         return {"supported": False, "status": e.name}
@@ -262,6 +263,7 @@ def prefill_attention_report(cache, wl: W.Workload, n_q: int = 512, reps: int = 
     flops = 4.0 * 128 * wl.n_q_heads * visible * B
     tflops = flops / sec / 1e12
     return {"supported": True, "n_q": n_q, "context": n, "us_per_call": 1e6 * sec,
+            "workspace_bytes": ws_bytes,
             "query_tokens_per_s": B * n_q / sec,
             "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": tflops / MFMA_F16_PEAK_TFLOPS,

@@ -56,8 +56,21 @@ class KvCache:
     def append_attn_decode(self, layer, k, v, q, out, softmax_scale=0.0, stream=None):
         _kvq.kvq_append_attn_decode(self.handle, layer, k, v, q, out, softmax_scale, stream)
 
-    def attn_prefill(self, layer, q, out, softmax_scale=0.0, stream=None):
-        _kvq.kvq_attn_prefill(self.handle, layer, q, out, softmax_scale, stream)
+    def attn_prefill(self, layer, q, out, softmax_scale=0.0, stream=None, workspace="auto"):
+        """workspace: "auto" (a device buffer of kvq_attn_prefill_workspace bytes, kept on this
+        object and grown when a call needs more), None (the cache's own), or a device tensor."""
+        if isinstance(workspace, str):
+            need = _kvq.kvq_attn_prefill_workspace(self.handle, layer, q.shape[1], q.shape[0])
+            ws = getattr(self, "_prefill_ws", None)
+            if need and (ws is None or ws.numel() < need):
+                import torch
+                ws = torch.empty(need, dtype=torch.uint8, device=self.buf.device)
+                self._prefill_ws = ws
+            workspace = ws if need else None
+        _kvq.kvq_attn_prefill(self.handle, layer, q, out, softmax_scale, workspace, stream)
+
+    def attn_prefill_workspace(self, layer, n_q, batch):
+        return _kvq.kvq_attn_prefill_workspace(self.handle, layer, n_q, batch)
 
     def set_option(self, option, value):
         _kvq.kvq_set_option(self.handle, option, value)

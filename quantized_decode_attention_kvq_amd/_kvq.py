@@ -22,6 +22,7 @@ EXPORTS = ["kvq_cache_required_bytes", "kvq_cache_create", "kvq_cache_destroy",
            "kvq_set_random_tables", "kvq_calibrate", "kvq_prefill_quantize", "kvq_append",
            "kvq_attn_decode", "kvq_get_layout", "kvq_get_tables", "kvq_set_option",
            "kvq_set_timing_events", "kvq_append_attn_decode", "kvq_attn_prefill",
+           "kvq_attn_prefill_workspace",
            "kvq_get_length", "kvq_status_str", "kvq_last_hip_error"]
 
 
@@ -74,7 +75,8 @@ def load():
         "kvq_append": [vp, i, vp, vp, i, i, vp],
         "kvq_attn_decode": [vp, i, vp, i, vp, i, f, vp],
         "kvq_append_attn_decode": [vp, i, vp, vp, vp, i, vp, i, f, vp],
-        "kvq_attn_prefill": [vp, i, vp, i, vp, i, i, f, vp],
+        "kvq_attn_prefill": [vp, i, vp, i, vp, i, i, f, vp, ctypes.c_size_t, vp],
+        "kvq_attn_prefill_workspace": [vp, i, i, i, ctypes.POINTER(ctypes.c_size_t)],
         "kvq_get_layout": [vp, i, i, i, i, ctypes.POINTER(kvq_layout)],
         "kvq_get_tables": [vp, ctypes.POINTER(kvq_tables)],
         "kvq_set_option": [vp, i, i],
@@ -173,10 +175,20 @@ def kvq_attn_decode(h, layer, q, out, softmax_scale=0.0, stream=None):
                                   float(softmax_scale), _stream(stream)), "kvq_attn_decode")
 
 
-def kvq_attn_prefill(h, layer, q, out, softmax_scale=0.0, stream=None):
-    """q: [batch][n_q][Hq][128] (f32 or bf16), out: [batch][n_q][Hq][128] f32."""
+def kvq_attn_prefill(h, layer, q, out, softmax_scale=0.0, workspace=None, stream=None):
+    """q: [batch][n_q][Hq][128] (f32 or bf16), out: [batch][n_q][Hq][128] f32; workspace: a
+    device tensor (any dtype, contiguous) or None for the cache's own."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().kvq_attn_prefill(h, layer, _ptr(q), _dtype(q), _ptr(out), q.shape[1], q.shape[0],
-                                   float(softmax_scale), _stream(stream)), "kvq_attn_prefill")
+                                   float(softmax_scale), _ptr(workspace), ws_bytes, _stream(stream)),
+           "kvq_attn_prefill")
+
+
+def kvq_attn_prefill_workspace(h, layer, n_q, batch) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().kvq_attn_prefill_workspace(h, layer, n_q, batch, ctypes.byref(n)),
+           "kvq_attn_prefill_workspace")
+    return n.value
 
 
 def kvq_append_attn_decode(h, layer, k, v, q, out, softmax_scale=0.0, stream=None):

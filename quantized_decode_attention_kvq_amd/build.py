@@ -29,7 +29,9 @@ UNITS = [
     ("kvq_quant.hip", DEVICE + ["-ffp-contract=off"]),
     ("kvq_decode.hip", DEVICE),
     ("kvq_decode_mfma.hip", DEVICE + ["-ffp-contract=off"]),  # holds the fused append
-    ("kvq_prefill_attn.hip", DEVICE),
+    # matrix-core accumulators in VGPRs: the softmax rescales them with vector ALU instructions,
+    # and AGPR-homed accumulators cost a copy each way per chunk
+    ("kvq_prefill_attn.hip", DEVICE + ["-mllvm", "--amdgpu-mfma-vgpr-form"]),
     ("kvq_host.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]),  # host only
 ]
 

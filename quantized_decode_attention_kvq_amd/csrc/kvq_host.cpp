@@ -488,11 +488,72 @@ kvq_status kvq_append_attn_decode(kvq_cache* c, int layer, const void* k, const 
     return KVQ_OK;
 }
 
+namespace {
+
+// Key splits per (query, head) row for a prefill-attention call.  A workgroup owns
+// kPrefillRowsPerBlock rows of one (sequence, kv head) and streams its keys in 64-token chunks;
+// with `base` workgroups per split, S splits take ceil(base S / CUs) rounds of ceil(chunks / S)
+// chunks each, and every split adds one partial row (kPartialFloats floats) per row, written and
+// read once by the merge.  The plan minimises that modelled time over S (at most `cap_bytes` of
+// partials).
+int prefill_splits(const kvq_cache* c, int n_q, int batch, int max_len, size_t cap_bytes) {
+    const int G = c->cfg.n_q_heads / c->cfg.n_kv_heads;
+    const long tiles = (static_cast<long>(n_q) * G + kPrefillRowsPerBlock - 1) / kPrefillRowsPerBlock;
+    const long base = tiles * c->cfg.n_kv_heads * batch;
+    const long chunks = (max_len + 63) / 64;
+    const double rows = static_cast<double>(batch) * n_q * c->cfg.n_q_heads;
+    const double chunk_s = 0.9e-6, merge_launch_s = 4e-6, hbm_Bps = 4e12;
+    const long cus = std::max(1, c->num_cus);
+    int best = 1;
+    double best_t = 0.0;
+    for (int S = 1; S <= 64 && S <= chunks; ++S) {
+        const double bytes = rows * S * kPartialFloats * sizeof(float);
+        if (S > 1 && bytes > static_cast<double>(cap_bytes)) break;
+        const long rounds = (base * S + cus - 1) / cus;
+        double t = static_cast<double>(rounds) * ((chunks + S - 1) / S) * chunk_s;
+        if (S > 1) t += merge_launch_s + 2.0 * bytes / hbm_Bps;
+        if (S == 1 || t < 0.97 * best_t) {
+            best = S;
+            best_t = t;
+        }
+    }
+    return best;
+}
+
+kvq_status check_prefill(const kvq_cache* c, int layer, int n_q, int batch, int* max_len) {
+    if (!c || layer < 0 || layer >= c->cfg.n_layers || batch < 1 || batch > c->cfg.max_batch || n_q < 1)
+        return KVQ_ERR_INVALID_ARG;
+    const int* len = &c->len[(size_t)layer * c->cfg.max_batch];
+    int mx = 0;
+    for (int b = 0; b < batch; ++b) {
+        if (n_q > len[b]) return KVQ_ERR_INVALID_ARG;
+        mx = std::max(mx, len[b]);
+    }
+    *max_len = mx;
+    return KVQ_OK;
+}
+
+} // namespace
+
+kvq_status kvq_attn_prefill_workspace(const kvq_cache* c, int layer, int n_q, int batch, size_t* bytes) {
+    int max_len = 0;
+    const kvq_status st = check_prefill(c, layer, n_q, batch, &max_len);
+    if (st != KVQ_OK) return st;
+    if (!bytes) return KVQ_ERR_INVALID_ARG;
+    const int S = prefill_splits(c, n_q, batch, max_len, static_cast<size_t>(-1));
+    *bytes = S > 1 ? (size_t)batch * n_q * c->cfg.n_q_heads * S * kPartialFloats * sizeof(float) : 0;
+    return KVQ_OK;
+}
+
 kvq_status kvq_attn_prefill(kvq_cache* c, int layer, const void* q, int dtype, float* out, int n_q,
-                            int batch, float softmax_scale, void* stream) {
+                            int batch, float softmax_scale, void* workspace, size_t workspace_bytes,
+                            void* stream) {
     kvq_status st = check_decode(c, layer, q, dtype, out, batch, softmax_scale);
     if (st != KVQ_OK) return st;
-    if (n_q < 1) return KVQ_ERR_INVALID_ARG;
+    int max_len = 0;
+    st = check_prefill(c, layer, n_q, batch, &max_len);
+    if (st != KVQ_OK) return st;
+    if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return KVQ_ERR_MISALIGNED;
     PrefillParams p{};
     p.q = q;
     p.out = out;
@@ -509,11 +570,11 @@ kvq_status kvq_attn_prefill(kvq_cache* c, int layer, const void* q, int dtype, f
     const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt(128.0f);
     p.qscale = scale * 1.4426950408889634f;
     const int* len = &c->len[(size_t)layer * c->cfg.max_batch];
-    for (int b = 0; b < batch; ++b) {
-        if (n_q > len[b]) return KVQ_ERR_INVALID_ARG;
-        p.len[b] = len[b];
-    }
+    for (int b = 0; b < batch; ++b) p.len[b] = len[b];
     if (!prefill_attn_supported(p)) return KVQ_ERR_UNSUPPORTED;
+    const size_t cap = workspace ? workspace_bytes : c->plan.work_bytes;
+    p.partials = workspace ? static_cast<float*>(workspace) : reinterpret_cast<float*>(c->base + c->plan.off_work);
+    p.n_splits = prefill_splits(c, n_q, batch, max_len, cap);
     const hipError_t e = launch_prefill_attn(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return dev_fail(c, e);
     return KVQ_OK;

@@ -69,9 +69,12 @@ struct DecodeParams {
 
 // Parameters of the prefill-chunk attention kernel: the n_q newest tokens of each sequence are
 // the queries, each attending to the cache up to its own position.
+constexpr int kPrefillRowsPerBlock = 128; // (query, head) rows per prefill-attention workgroup
+
 struct PrefillParams {
     const void* q;            // [batch][n_q][Hq][128] of dtype
     float* out;               // [batch][n_q][Hq][128]
+    float* partials;          // [batch][n_q][Hq][n_splits][kPartialFloats] when n_splits > 1
     char* layer_base;
     size_t seq_stride, head_stride;
     size_t plane_off[2];
@@ -79,6 +82,7 @@ struct PrefillParams {
     const float* signs;       // layer base [Hkv][2][128]
     const float* cs;          // layer base [Hkv][2][128] Sinkhorn c
     int dtype, batch, n_q, Hq, Hkv, G, window;
+    int n_splits;             // key splits per row (1: the attention kernel writes out itself)
     float qscale;             // softmax scale * log2(e)
     int len[kMaxBatch];
 };

@@ -11,19 +11,24 @@
 //    rotated / balanced domain with q' = R(q) .* c, and the output is mapped back with c_V and
 //    R_V^-1.
 //
-// How: one workgroup per (sequence, query head, 64-query tile), one wave per 16 queries; each
-// wave walks the cache in 64-token chunks up to its last query's position.
-//  * Scores: per 32-channel group g, D_g = Q'_g C_g on v_mfma_f32_16x16x32_f16 with A = the 16
-//    query rows of q' (fp16 hi and a 2^11-scaled lo part) and B = the raw codes as exact fp16
-//    operands (the decode kernel's operand forms).  The token's fp16 scale and zero fold in
-//    afterwards: s = sum_g scale_g D_g + zero_g sum_{j in g} q'_j.
-//  * Online softmax per query row in the log2 domain; tokens after a row's position are masked.
-//  * PV: A = p * scale_g in fp16 (p in [0, 1]: a relative rounding of 2^-12 per weight, which
-//    averages out over the tokens) staged through LDS, B = centred V codes c - 8 (c - 128) as
-//    exact fp16 integers; the zero-point term sum p (zero + 8 scale) on the vector ALU in fp32.
-//  * Each row's output is divided by its softmax sum and mapped back with c_V and R_V^-1.
-// Planes with an FP32 window, or TurboQuant planes, are refused by the host (not supported by
-// this kernel).
+// How.  The (query, head) pairs of one (sequence, kv head) are rows r = G * i + h (query i,
+// query head h of the kv head's group).  A workgroup of 8 waves owns 256 consecutive rows (32 per
+// wave, two 16-row MFMA column blocks) and one share of the key chunks up to its last row's
+// position ("split"; the host picks the number of splits that fills the chip).  Per 64-token
+// chunk:
+//  * the workgroup dequantizes the chunk's keys and values (z + s * code in fp32) into LDS as
+//    fp16 pairs (hi = the value rounded, lo = the remainder rounded), once for its 256 rows,
+//    while the waves work on the previous chunk (two LDS buffers, global loads one chunk ahead);
+//  * each wave forms the transposed scores S^T = K q'^T on v_mfma_f32_16x16x32_f16 with three
+//    products per slice (K_hi q_hi, K_hi q_lo, K_lo q_hi: close to fp32 accuracy);
+//    key rows are ordered in LDS so that each lane's score values are exactly the P^T operand
+//    of the PV product, which therefore never leaves the registers;
+//  * an online softmax per row in the log2 domain (tokens after the row's position are masked),
+//    then O^T += V_hi^T P^T + V_lo^T P^T (values as the A operand, fp16 probabilities as B).
+// With one split, each row's output is divided by its softmax sum and mapped back with c_V and
+// R_V^-1 in the same kernel; with several, each split writes (m, l, acc) and a merge kernel
+// combines them in a fixed order.  Planes with an FP32 window, or TurboQuant planes, are refused
+// by the host (not supported by this kernel).
 #include <hip/hip_runtime.h>
 
 #include "kvq_internal.h"
@@ -37,318 +42,492 @@ namespace {
 using namespace mops;
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kWaves = 4;              // waves per workgroup (16 query rows each)
-constexpr int kPR = 72;                // halves per staged P row: 64 tokens + 8 pad
-constexpr int kStage = 4 * 16 * kPR;   // halves per wave: [group][16 rows][token], and the
-                                       // [16][128] float rows before and after the loop
-static_assert(kStage * 2 >= 16 * kDim * 4, "row scratch fits the staging area");
+constexpr float kLazy = 8.0f; // log2 headroom of the running softmax maximum
+constexpr int kQB = 1;                            // 16-row column blocks per wave
+constexpr int kWaveRows = 16 * kQB;
+constexpr int kWaves = kPrefillRowsPerBlock / kWaveRows;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKS = 136;                          // halves per dequantized key row (128 + pad)
+constexpr int kVS = 72;                           // halves per dequantized value row (64 + pad)
+constexpr int kKBuf = 2 * 64 * kKS;               // one chunk's keys: 64 hi rows, then 64 lo rows
+constexpr int kVBuf = 2 * 128 * kVS;              // one chunk's values [channel][token]: hi, lo
+constexpr int kLdsHalves = 2 * (kKBuf + kVBuf);   // two buffers of each
+constexpr int kVmRow = 68;                        // value meta row (64 tokens + pad: groups on
+                                                  // different banks)
+constexpr int kUnits = 64 * 16 / kThreads;        // 8-code units of a chunk per thread (K; V alike)
+static_assert(kWaves == 8, "two waves per SIMD");
+static_assert(kUnits * kThreads == 1024, "a chunk is 1024 key units and 1024 value units");
+static_assert(kLdsHalves * 2 >= kWaves * 16 * kDim * 4, "the q' rows fit in the chunk buffers");
 
-__device__ __forceinline__ float wave_max(float v) {
-    return xor_reduce<64>(v, [](float x, float y) { return fmaxf(x, y); });
+// LDS row of chunk token t (0..63) in the key buffer.  Score tile b (16 key rows) holds at row
+// 4u + v the token 32 (b / 2) + 8u + 4 (b % 2) + v, so that a lane's four score values of tile
+// 2k and its four of tile 2k + 1 are tokens 32k + 8u .. 32k + 8u + 7: the lane's B operand of the
+// PV product over the chunk's k-th 32 tokens.
+__device__ __forceinline__ int key_lds_row(int t) {
+    return 16 * (2 * (t >> 5) + ((t >> 2) & 1)) + 4 * ((t >> 3) & 3) + (t & 3);
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// Code i (0..7) of an 8-code unit: 4-bit at bit 16 (i % 2) + 4 (i / 2) of w.x, 8-bit at byte i.
+template <int BITS>
+__device__ __forceinline__ float code_at(uint2 w, int i) {
+    if constexpr (BITS == 4) return (float)((w.x >> (16 * (i & 1) + 4 * (i >> 1))) & 15u);
+    else return (float)(((i < 4 ? w.x : w.y) >> (8 * (i & 3))) & 255u);
+}
+
+// Prefetched global words of one chunk: kUnits key units (8 codes + their group's scale and
+// zero), kUnits value units (8 codes), and one token's value meta (threads 0..63).
+struct ChunkRegs {
+    uint2 kc[kUnits], vc[kUnits];
+    uint32_t ks[kUnits], kz[kUnits]; // fp16 bits of the key unit's scale and zero
+    u4 vm;
+};
+
+struct Planes {
+    const uint8_t *kcodes, *kmeta, *vcodes, *vmeta;
+};
+
+template <int KB, int VB>
+__device__ __forceinline__ void load_codes(const Planes& P, int ci, int tid, ChunkRegs& R) {
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+        const int u = tid + kThreads * j, g = (u >> 2) & 3, word = 4 * (u & 3) + g;
+        const size_t row = (size_t)64 * ci + (u >> 4);
+        if constexpr (KB == 4) R.kc[j].x = reinterpret_cast<const uint32_t*>(P.kcodes + row * 64)[word];
+        else R.kc[j] = reinterpret_cast<const uint2*>(P.kcodes + row * 128)[word];
+        const uint16_t* m = reinterpret_cast<const uint16_t*>(P.kmeta + row * 16);
+        R.ks[j] = m[g]; // kept apart until the dequantization: no wait on the load here
+        R.kz[j] = m[4 + g];
+    }
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+        const int u = tid + kThreads * j;
+        const size_t blk = (size_t)2 * ci + (u >> 9);
+        if constexpr (VB == 4) R.vc[j].x = reinterpret_cast<const uint32_t*>(P.vcodes + blk * 2048)[u & 511];
+        else R.vc[j] = reinterpret_cast<const uint2*>(P.vcodes + blk * 4096)[u & 511];
+    }
+}
+
+__device__ __forceinline__ void load_vmeta(const Planes& P, int ci, int tid, ChunkRegs& R) {
+    if (tid < 64) R.vm = *reinterpret_cast<const u4*>(P.vmeta + ((size_t)64 * ci + tid) * 16);
+}
+
+// value meta of one chunk -> sm[scale | zero][group][token]
+__device__ __forceinline__ void store_vmeta(float (*sm)[4][kVmRow], int tid, const ChunkRegs& R) {
+    if (tid < 64) {
+        sm[0][0][tid] = lo_h(R.vm.x);
+        sm[0][1][tid] = hi_h(R.vm.x);
+        sm[0][2][tid] = lo_h(R.vm.y);
+        sm[0][3][tid] = hi_h(R.vm.y);
+        sm[1][0][tid] = lo_h(R.vm.z);
+        sm[1][1][tid] = hi_h(R.vm.z);
+        sm[1][2][tid] = lo_h(R.vm.w);
+        sm[1][3][tid] = hi_h(R.vm.w);
+    }
+}
+
+// Dequantize the prefetched chunk into one key buffer and one value buffer.
+//  key unit u: physical row p = u / 16 (token 4 (p % 16) + p / 16 of the chunk), w = u % 16 =
+//    4 g + kb: code word 4 kb + g, channels 32 g + 8 kb + i (so consecutive lanes fill
+//    consecutive 16 B of the LDS row);
+//  value unit u: 32-token block u / 512, word w = u % 512 = 8 (16 kb + n) + N (channel
+//    d = 16 N + n, tokens 8 kb + i of the block).  Value rows [channel][token] store the 8-token
+//    slot s at slot s ^ (d / 16), which keeps both these writes and the operand reads free of
+//    bank conflicts.
+template <int KB, int VB>
+__device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const float (*sm)[4][kVmRow], int tid,
+                                              const ChunkRegs& R) {
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+        const int u = tid + kThreads * j, p = u >> 4, w = u & 15;
+        const int t = 4 * (p & 15) + (p >> 4);
+        const float sc = h2f(R.ks[j]), zr = h2f(R.kz[j]);
+        h8 hi, lo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float y = fmaf(sc, code_at<KB>(R.kc[j], i), zr);
+            const _Float16 h = (_Float16)y;
+            hi[i] = h;
+            lo[i] = (_Float16)(y - (float)h);
+        }
+        _Float16* dst = sk + key_lds_row(t) * kKS + 8 * w; // channels 32 (w / 4) + 8 (w % 4) + i
+        *reinterpret_cast<h8*>(dst) = hi;
+        *reinterpret_cast<h8*>(dst + 64 * kKS) = lo;
+    }
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+        const int u = tid + kThreads * j, half = u >> 9, w = u & 511;
+        const int kb = w >> 7, n = (w >> 3) & 15, N = w & 7, d = 16 * N + n, g = N >> 1;
+        const int t0 = 32 * half + 8 * kb;
+        const float4 s0 = *reinterpret_cast<const float4*>(&sm[0][g][t0]);
+        const float4 s1 = *reinterpret_cast<const float4*>(&sm[0][g][t0 + 4]);
+        const float4 z0 = *reinterpret_cast<const float4*>(&sm[1][g][t0]);
+        const float4 z1 = *reinterpret_cast<const float4*>(&sm[1][g][t0 + 4]);
+        const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+        h8 hv, lv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float y = fmaf(ss[i], code_at<VB>(R.vc[j], i), zz[i]);
+            const _Float16 h = (_Float16)y;
+            hv[i] = h;
+            lv[i] = (_Float16)(y - (float)h);
+        }
+        _Float16* dst = sv + d * kVS + 8 * ((4 * half + kb) ^ N);
+        *reinterpret_cast<h8*>(dst) = hv;
+        *reinterpret_cast<h8*>(dst + 128 * kVS) = lv;
+    }
+}
+
+// out row = R_V^-1(c_V .* x) for a row held as two channels per lane (2l, 2l + 1).
+__device__ __forceinline__ void store_out_row(float a, float c, const PlaneGeom& VG, float2 csv, float2 sgv,
+                                              float* out_row, int l) {
+    if (VG.sinkhorn) {
+        a *= csv.x;
+        c *= csv.y;
+    }
+    if (VG.rotate) {
+        qdev::hadamard_wave(a, c);
+        a *= c0f();
+        c *= c0f();
+        if (sgv.x < 0.0f) a = -a;
+        if (sgv.y < 0.0f) c = -c;
+    }
+    reinterpret_cast<float2*>(out_row)[l] = make_float2(a, c);
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int KB, int VB>
-__global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(PrefillParams p) {
-    __shared__ __align__(16) _Float16 s_stage[kWaves * kStage];
-    __shared__ float s_qsum[kWaves][16][4];
-    __shared__ float s_qfac[kWaves][16];
+__global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p) {
+    __shared__ __align__(16) _Float16 s_lds[kLdsHalves];
+    __shared__ __align__(16) float s_vm[2][2][4][kVmRow]; // [buffer][scale | zero][group][token]
+    __shared__ float s_qf[kWaves][kWaveRows];          // 2^-e of each row's q' scaling
 
-    const int tile = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
-    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, lr = l & 15, lq = l >> 4;
-    const int G = p.G, kvh = hq / G;
+    const int S = p.n_splits;
+    const int kvh = blockIdx.x % p.Hkv, rest = blockIdx.x / p.Hkv;
+    const int split = rest % S, tile = rest / S, b = blockIdx.y;
+    const int G = p.G, nrows = p.n_q * G;
+    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, lr = l & 15, lq = l >> 4;
     const int N = p.len[b], P0 = N - p.n_q;
-    const int i0 = tile * 64 + wave * 16; // first query row of this wave
-    if (i0 >= p.n_q) return;              // the waves share no barrier
-    const int rows = min(16, p.n_q - i0);
+    const int row0 = tile * kPrefillRowsPerBlock + kWaveRows * wave; // this wave's first row
     const PlaneGeom& KG = p.geom[0];
     const PlaneGeom& VG = p.geom[1];
     const char* slot = p.layer_base + (size_t)b * p.seq_stride + (size_t)kvh * p.head_stride;
-    const uint8_t* kcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.codes_off);
-    const uint8_t* kmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.meta_off);
-    const uint8_t* vcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.codes_off);
-    const uint8_t* vmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.meta_off);
-    _Float16* my_stage = s_stage + wave * kStage;
-    float* s_row = reinterpret_cast<float*>(my_stage); // [16][128] floats, before and after the loop
+    Planes P;
+    P.kcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.codes_off);
+    P.kmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.meta_off);
+    P.vcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.codes_off);
+    P.vmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.meta_off);
 
-    // ---------------- q' of the 16 rows: R_K(q) .* c_K * scale * log2(e), a power of two per
-    // row keeping 16 max|q'| in [2^10, 2^11), and the row's four group sums
-    const float2 sgn = reinterpret_cast<const float2*>(p.signs + (size_t)(kvh * 2 + 0) * kDim)[l];
-    const float2 csk = reinterpret_cast<const float2*>(p.cs + (size_t)(kvh * 2 + 0) * kDim)[l];
-    for (int r = 0; r < 16; ++r) {
-        float a = 0.0f, c = 0.0f;
-        if (r < rows) {
-            const size_t off = (((size_t)b * p.n_q + i0 + r) * p.Hq + hq) * kDim;
-            if (p.dtype == 0) {
-                const float2 v = reinterpret_cast<const float2*>(static_cast<const float*>(p.q) + off)[l];
-                a = v.x;
-                c = v.y;
-            } else {
-                const uint32_t v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.q) + off)[l];
-                a = bf2f((uint16_t)(v & 0xffff));
-                c = bf2f((uint16_t)(v >> 16));
-            }
-        }
-        if (KG.rotate) {
-            if (sgn.x < 0.0f) a = -a;
-            if (sgn.y < 0.0f) c = -c;
-            qdev::hadamard_wave(a, c);
-            a *= c0f();
-            c *= c0f();
-        }
-        if (KG.sinkhorn) {
-            a *= csk.x;
-            c *= csk.y;
-        }
-        a *= p.qscale;
-        c *= p.qscale;
-        const float mx = wave_max(fmaxf(fabsf(a), fabsf(c)));
-        int e2 = 0;
-        if (mx > 0.0f) frexpf(mx, &e2);
-        const int e = (mx > 0.0f) ? min(max(7 - e2, -100), 100) : 0;
-        const float f = ldexpf(1.0f, e);
-        a *= f;
-        c *= f;
-        s_row[r * kDim + 2 * l] = a;
-        s_row[r * kDim + 2 * l + 1] = c;
-        const float gs = row_sum16(a + c);
-        if (lr == 0) s_qsum[wave][r][lq] = gs;
-        if (l == 0) s_qfac[wave][r] = ldexpf(1.0f, -e);
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---------------- A operands: row lr = query, k-slice = channels 32g + 8 lq + 0..7
-    const float UK = (KB == 4) ? 1048576.0f : 16777216.0f; // unit of a code product
-    const float UV = (VB == 4) ? 0.0625f : 1.0f;
-    h8 Ahi[4], Alo[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float w = (KB == 4 && (i == 0 || i == 1 || i == 4 || i == 5)) ? 16.0f : 1.0f;
-            const float x = s_row[lr * kDim + 32 * g + 8 * lq + i] * w;
-            const _Float16 xh = (_Float16)x;
-            Ahi[g][i] = xh;
-            Alo[g][i] = (_Float16)((x - (float)xh) * kLoScale);
-        }
-    }
-    // score layout: lane holds rows 4 lq + v, token column lr
-    float qs_l[4][4], F[4];
-    int pos[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int r = 4 * lq + v;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) qs_l[v][g] = s_qsum[wave][r][g] * (1.0f / UK);
-        F[v] = UK * s_qfac[wave][r];
-        pos[v] = (r < rows) ? P0 + i0 + r : -1; // -1: no token is visible to an absent row
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    float m_run[4], l_run[4], z_run[4][4];
-    f4 acc[8];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        m_run[v] = kNegInf;
-        l_run[v] = 0.0f;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) z_run[v][g] = 0.0f;
-    }
-#pragma unroll
-    for (int n = 0; n < 8; ++n) acc[n] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const int kend = min(N, P0 + i0 + rows); // keys this wave needs: 0 .. kend - 1
-    const int nch = (kend + 63) / 64;
-    u4 kc[4][KB / 4], km[4], vc[2][VB / 2], vm[4];
-    auto load_k = [&](int ci) {
-        const size_t r0 = (size_t)64 * ci + lr; // row of sub-tile 0: token 4 lr + j in row 16 j + lr
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint8_t* c = kcodes + (r0 + 16 * j) * (16 * KB) + (16 * KB / 4) * lq;
-#pragma unroll
-            for (int u = 0; u < KB / 4; ++u) kc[j][u] = *reinterpret_cast<const u4*>(c + 16 * u);
-            km[j] = *reinterpret_cast<const u4*>(kmeta + (r0 + 16 * j) * 16);
-        }
-    };
-    auto load_v = [&](int ci) {
-        const size_t t0 = (size_t)64 * ci;
-        const uint8_t* c = vcodes + (t0 / 32) * (512 * VB) + (size_t)(32 * VB / 4) * l;
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-            for (int u = 0; u < VB / 2; ++u) vc[k][u] = *reinterpret_cast<const u4*>(c + k * 512 * VB + 16 * u);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vm[j] = *reinterpret_cast<const u4*>(vmeta + (t0 + 4 * lr + j) * 16);
-    };
-    if (nch > 0) {
-        load_k(0);
-        load_v(0);
-    }
-
-    for (int ci = 0; ci < nch; ++ci) {
-        // ---- scores of sub-tile j: token t = 64 ci + 4 lr + j
-        float raw[4][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = 64 * ci + 4 * lr + j;
-            h8 B[4];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                if (KB == 4)
-                    B[g] = as_h8(unpack4(kc[j][0][g]));
-                else
-                    B[g] = as_h8(unpack8(kc[j][g >> 1][2 * (g & 1)], kc[j][g >> 1][2 * (g & 1) + 1]));
-            }
-            const float sc[4] = {lo_h(km[j].x), hi_h(km[j].x), lo_h(km[j].y), hi_h(km[j].y)};
-            const float zr[4] = {lo_h(km[j].z), hi_h(km[j].z), lo_h(km[j].w), hi_h(km[j].w)};
-            float r[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-                const f4 D = mfma16(Ahi[g], B[g], zero4);
-                const f4 E = mfma16(Alo[g], B[g], zero4);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) r[v] = fmaf(sc[g], fmaf(E[v], kLoInv, D[v]), r[v]);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                float s = r[v];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) s = fmaf(zr[g], qs_l[v][g], s);
-                raw[j][v] = (t <= pos[v] && t < N) ? s : kNegInf;
-            }
-        }
-        if (ci + 1 < nch) load_k(ci + 1);
-
-        // ---- online softmax per row (state per lane: its 4 tokens; the row max over the
-        // row's 16 lanes)
-        float pj[4][4], al[4];
-        bool grew = false;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float t = fmaxf(fmaxf(raw[0][v], raw[1][v]), fmaxf(raw[2][v], raw[3][v]));
-            t = row_max16(t);
-            const float mnew = fmaxf(m_run[v], t * F[v]);
-            const bool inf = (mnew == kNegInf);
-            const float alpha = inf ? 1.0f : exp2f(m_run[v] - mnew);
-            float s = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pj[j][v] = inf ? 0.0f : exp2f(fmaf(raw[j][v], F[v], -mnew));
-                s += pj[j][v];
-            }
-            l_run[v] = l_run[v] * alpha + s;
-            grew |= mnew > m_run[v];
-            m_run[v] = mnew;
-            al[v] = alpha;
-        }
-        if (__ballot(grew) != 0) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) z_run[v][g] *= al[v];
-#pragma unroll
-                for (int n = 0; n < 8; ++n) acc[n][v] *= al[v];
-            }
-        }
-
-        // ---- zero-point term and the PV A operands: p * scale_g in fp16, [g][row][token 4 lr + j]
-        constexpr float mid = (VB == 4) ? 8.0f : 128.0f; // codes enter as c - mid
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float vs[4] = {lo_h(vm[j].x), hi_h(vm[j].x), lo_h(vm[j].y), hi_h(vm[j].y)};
-            const float vz[4] = {lo_h(vm[j].z), hi_h(vm[j].z), lo_h(vm[j].w), hi_h(vm[j].w)};
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) z_run[v][g] = fmaf(pj[j][v], fmaf(mid, vs[g], vz[g]), z_run[v][g]);
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                h4 hv;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t w = (g < 2) ? vm[j].x : vm[j].y;
-                    const float sg = (g & 1) ? hi_h(w) : lo_h(w);
-                    const float wt = (VB == 4 && j < 2) ? 16.0f : 1.0f;
-                    hv[j] = (_Float16)(pj[j][v] * sg * wt);
+    // ---------------- q' = R_K(q) .* c_K * scale * log2(e) * 2^e per row (2^e keeps max|q'| in
+    // [64, 128)), then the B operands of the score product (column = row lr of the block,
+    // k = channel 32 ks + 8 lq + i): hi = fp16(q'), lo = fp16(q' - hi)
+    h8 Bh[4][kQB], Bl[4][kQB];
+    {
+        const float2 sgn = reinterpret_cast<const float2*>(p.signs + (size_t)(kvh * 2 + 0) * kDim)[l];
+        const float2 csk = reinterpret_cast<const float2*>(p.cs + (size_t)(kvh * 2 + 0) * kDim)[l];
+        float* s_rows = reinterpret_cast<float*>(s_lds) + wave * 16 * kDim;
+        for (int qb = 0; qb < kQB; ++qb) {
+            for (int rr = 0; rr < 16; ++rr) {
+                const int r = 16 * qb + rr, gr = row0 + r;
+                float a = 0.0f, c = 0.0f;
+                if (gr < nrows) {
+                    const int i = gr / G, hq = kvh * G + (gr - i * G);
+                    const size_t off = (((size_t)b * p.n_q + i) * p.Hq + hq) * kDim;
+                    if (p.dtype == 0) {
+                        const float2 v = reinterpret_cast<const float2*>(static_cast<const float*>(p.q) + off)[l];
+                        a = v.x;
+                        c = v.y;
+                    } else {
+                        const uint32_t v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.q) + off)[l];
+                        a = bf2f((uint16_t)(v & 0xffff));
+                        c = bf2f((uint16_t)(v >> 16));
+                    }
                 }
-                const int row = 4 * lq + v;
-                *reinterpret_cast<h4*>(my_stage + g * 16 * kPR + row * kPR + 4 * lr) = hv;
+                if (KG.rotate) {
+                    if (sgn.x < 0.0f) a = -a;
+                    if (sgn.y < 0.0f) c = -c;
+                    qdev::hadamard_wave(a, c);
+                    a *= c0f();
+                    c *= c0f();
+                }
+                if (KG.sinkhorn) {
+                    a *= csk.x;
+                    c *= csk.y;
+                }
+                a *= p.qscale;
+                c *= p.qscale;
+                const float mx = xor_reduce<64>(fmaxf(fabsf(a), fabsf(c)), [](float x, float y) { return fmaxf(x, y); });
+                int e2 = 0;
+                if (mx > 0.0f) frexpf(mx, &e2);
+                const int e = (mx > 0.0f) ? min(max(7 - e2, -100), 100) : 0;
+                const float f = ldexpf(1.0f, e);
+                reinterpret_cast<float2*>(s_rows + rr * kDim)[l] = make_float2(a * f, c * f);
+                if (l == 0) s_qf[wave][r] = ldexpf(1.0f, -e);
             }
-        }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // ---- PV over the chunk's two 32-token blocks
+            wave_lds_sync();
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            h8 Ph[4];
+            for (int ks = 0; ks < 4; ++ks) {
+                const float4 x0 = *reinterpret_cast<const float4*>(s_rows + lr * kDim + 32 * ks + 8 * lq);
+                const float4 x1 = *reinterpret_cast<const float4*>(s_rows + lr * kDim + 32 * ks + 8 * lq + 4);
+                const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                Ph[g] = *reinterpret_cast<const h8*>(my_stage + g * 16 * kPR + lr * kPR + 32 * k + 8 * lq);
-#pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                h8 Bv;
-                if (VB == 4)
-                    Bv = as_h8(centred4(vc[k][n >> 2][n & 3]));
-                else
-                    Bv = as_h8(centred8(vc[k][n >> 1][2 * (n & 1)], vc[k][n >> 1][2 * (n & 1) + 1]));
-                acc[n] = mfma16(Ph[n >> 1], Bv, acc[n]);
+                for (int i = 0; i < 8; ++i) {
+                    const _Float16 h = (_Float16)xs[i];
+                    Bh[ks][qb][i] = h;
+                    Bl[ks][qb][i] = (_Float16)(xs[i] - (float)h);
+                }
             }
+            wave_lds_sync();
         }
-        __builtin_amdgcn_wave_barrier();
-        if (ci + 1 < nch) load_v(ci + 1);
     }
-
-    // ---------------- rows: softmax sum and zero-point term over the row's 16 lanes, then
-    // out = R_V^-1(c_V .* acc) / l
-    float lt[4], zt[4][4];
+    // the lane's column (query row lr of each block): scale back, position (-1: an absent row
+    // sees no token)
+    float F[kQB], m_run[kQB], l_run[kQB];
+    int pos[kQB];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        lt[v] = row_sum16(l_run[v]);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) zt[v][g] = row_sum16(z_run[v][g]);
+    for (int qb = 0; qb < kQB; ++qb) {
+        const int gr = row0 + 16 * qb + lr;
+        F[qb] = s_qf[wave][16 * qb + lr];
+        pos[qb] = (gr < nrows) ? P0 + gr / G : -1;
+        m_run[qb] = kNegInf;
+        l_run[qb] = 0.0f;
     }
-    __builtin_amdgcn_wave_barrier();
+    int pmin = pos[0];
+#pragma unroll
+    for (int qb = 1; qb < kQB; ++qb) pmin = min(pmin, pos[qb]);
+    const float pos_min = xor_reduce<64>((float)pmin, [](float x, float y) { return fminf(x, y); });
+    f4 O[8][kQB];
 #pragma unroll
     for (int n = 0; n < 8; ++n)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const float a = acc[n][v] * UV + zt[v][n >> 1];
-            s_row[(4 * lq + v) * kDim + 16 * n + lr] = (lt[v] > 0.0f) ? a / lt[v] : 0.0f;
+        for (int qb = 0; qb < kQB; ++qb) O[n][qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // ---------------- this split's chunks of the keys the workgroup's rows can see
+    const int last_row = min(tile * kPrefillRowsPerBlock + kPrefillRowsPerBlock, nrows) - 1;
+    const int nch = (P0 + last_row / G + 1 + 63) / 64;
+    const int cps = (nch + S - 1) / S;
+    const int c0 = split * cps, c1 = min(nch, c0 + cps);
+    __syncthreads(); // the q' rows are consumed; the LDS becomes the chunk buffers
+
+    ChunkRegs R;
+    const bool late = wave >= kWaves / 2; // dequantizes before its matrix products
+    if (c0 < c1) {
+        load_vmeta(P, c0, tid, R);
+        store_vmeta(s_vm[0], tid, R);
+        load_codes<KB, VB>(P, c0, tid, R);
+        if (c0 + 1 < c1) load_vmeta(P, c0 + 1, tid, R);
+        __syncthreads();
+        dequant_chunk<KB, VB>(s_lds, s_lds + 2 * kKBuf, s_vm[0], tid, R);
+        if (c0 + 1 < c1) store_vmeta(s_vm[1], tid, R);
+        if (late && c0 + 1 < c1) load_codes<KB, VB>(P, c0 + 1, tid, R);
+        __syncthreads();
+    }
+    for (int ci = c0; ci < c1; ++ci) {
+        const int buf = (ci - c0) & 1;
+        const bool more = ci + 1 < c1;
+        // The two waves sharing a SIMD (w and w + 4) take the iteration in opposite order: one
+        // dequantizes the next chunk (vector ALU) while the other multiplies (matrix cores).  The
+        // waves that dequantize first hold their global words one chunk further ahead.
+        auto dequant_next = [&]() {
+            if (more) {
+                dequant_chunk<KB, VB>(s_lds + (buf ^ 1) * kKBuf, s_lds + 2 * kKBuf + (buf ^ 1) * kVBuf,
+                                      s_vm[buf ^ 1], tid, R);
+                if (ci + 2 < c1) store_vmeta(s_vm[buf], tid, R);
+            }
+        };
+        if (!late) {
+            if (ci + 2 < c1) load_vmeta(P, ci + 2, tid, R); // first: it may wait on its register
+            if (more) load_codes<KB, VB>(P, ci + 1, tid, R);
+        } else {
+            dequant_next();
+            if (ci + 2 < c1) load_codes<KB, VB>(P, ci + 2, tid, R);
         }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const _Float16* sk = s_lds + buf * kKBuf;
+        const _Float16* sv = s_lds + 2 * kKBuf + buf * kVBuf;
+        const bool masked = 64 * ci + 63 > (int)pos_min;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            // ---- S^T tiles 2 hh + tb of this 32-token half against both column blocks
+            f4 Sc[2][kQB];
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int qb = 0; qb < kQB; ++qb) Sc[tb][qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    const _Float16* kr = sk + (16 * (2 * hh + tb) + lr) * kKS + 32 * ks + 8 * lq;
+                    const h8 Ah = *reinterpret_cast<const h8*>(kr);
+                    const h8 Al = *reinterpret_cast<const h8*>(kr + 64 * kKS);
+#pragma unroll
+                    for (int qb = 0; qb < kQB; ++qb) {
+                        Sc[tb][qb] = mfma16(Ah, Bh[ks][qb], Sc[tb][qb]);
+                        Sc[tb][qb] = mfma16(Ah, Bl[ks][qb], Sc[tb][qb]);
+                        Sc[tb][qb] = mfma16(Al, Bh[ks][qb], Sc[tb][qb]);
+                    }
+                }
+            }
+            // ---- online softmax of each column (token 64 ci + 32 hh + 8 lq + 4 tb + v).  The
+            // running maximum m moves only when a score exceeds it by more than kLazy (log2
+            // units), so the accumulator is rescaled rarely; weights stay below 2^kLazy.
+            h8 Pb[kQB];
+            float al[kQB];
+            bool need = false;
+#pragma unroll
+            for (int qb = 0; qb < kQB; ++qb) {
+                float raw[8];
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) raw[4 * tb + v] = Sc[tb][qb][v];
+                if (__builtin_expect(masked, 0)) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int t = 64 * ci + 32 * hh + 8 * lq + i;
+                        if (t > pos[qb]) raw[i] = kNegInf;
+                    }
+                }
+                float mx = fmaxf(fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])),
+                                 fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7])));
+                mx = fmaxf(mx, xor_lane<16>(mx));
+                mx = fmaxf(mx, xor_lane<32>(mx)) * F[qb];
+                const bool up = mx > m_run[qb] + kLazy;
+                al[qb] = up ? __builtin_amdgcn_exp2f(m_run[qb] - mx) : 1.0f;
+                if (up) m_run[qb] = mx;
+                need |= up;
+                const float m = m_run[qb];
+                float sum = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float pv = (m == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(fmaf(raw[i], F[qb], -m));
+                    sum += pv;
+                    Pb[qb][i] = (_Float16)pv;
+                }
+                l_run[qb] = fmaf(l_run[qb], al[qb], sum);
+            }
+            if (__ballot(need) != 0) {
+#pragma unroll
+                for (int n = 0; n < 8; ++n)
+#pragma unroll
+                    for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) O[n][qb][v] *= al[qb];
+            }
+            // ---- O^T += V^T P^T over this half (A = values [channel 16 n + lr][token 8 lq + i])
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                const _Float16* vr = sv + (16 * n + lr) * kVS + 8 * ((4 * hh + lq) ^ n);
+                const h8 Vh = *reinterpret_cast<const h8*>(vr);
+                const h8 Vl = *reinterpret_cast<const h8*>(vr + 128 * kVS);
+#pragma unroll
+                for (int qb = 0; qb < kQB; ++qb) {
+                    O[n][qb] = mfma16(Vh, Pb[qb], O[n][qb]);
+                    O[n][qb] = mfma16(Vl, Pb[qb], O[n][qb]);
+                }
+            }
+        }
+        if (!late) dequant_next();
+        __syncthreads();
+    }
+
+    // ---------------- rows out: softmax sum over the column's four lanes; O^T lane (lr, lq) holds
+    // channels 16 n + 4 lq + v of row lr
+    float lt[kQB];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+        lt[qb] = l_run[qb] + xor_lane<16>(l_run[qb]);
+        lt[qb] += xor_lane<32>(lt[qb]);
+    }
+    if (S > 1) {
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            const int gr = row0 + 16 * qb + lr;
+            if (gr < nrows) {
+                const int i = gr / G, hq = kvh * G + (gr - i * G);
+                float* P_ = p.partials + ((((size_t)b * p.n_q + i) * p.Hq + hq) * S + split) * kPartialFloats;
+                if (lq == 0) {
+                    P_[0] = m_run[qb];
+                    P_[1] = lt[qb];
+                }
+#pragma unroll
+                for (int n = 0; n < 8; ++n) *reinterpret_cast<f4*>(P_ + 4 + 16 * n + 4 * lq) = O[n][qb];
+            }
+        }
+        return;
+    }
+    __syncthreads(); // c0 >= c1 workgroups skipped the loop's barriers
     const float2 csv = reinterpret_cast<const float2*>(p.cs + (size_t)(kvh * 2 + 1) * kDim)[l];
     const float2 sgv = reinterpret_cast<const float2*>(p.signs + (size_t)(kvh * 2 + 1) * kDim)[l];
-    for (int r = 0; r < rows; ++r) {
-        float a = s_row[r * kDim + 2 * l], c = s_row[r * kDim + 2 * l + 1];
-        if (VG.sinkhorn) {
-            a *= csv.x;
-            c *= csv.y;
+    float* s_rows = reinterpret_cast<float*>(s_lds) + wave * 8 * kDim;
+#pragma unroll
+    for (int ps = 0; ps < 2 * kQB; ++ps) { // register indexes must stay compile-time: unrolled
+        const int qb = ps >> 1, h8r = ps & 1;
+        if ((lr >> 3) == h8r) {
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+                f4 o = O[n][qb];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) o[v] = (lt[qb] > 0.0f) ? o[v] / lt[qb] : 0.0f;
+                *reinterpret_cast<f4*>(s_rows + (lr & 7) * kDim + 16 * n + 4 * lq) = o;
+            }
         }
-        if (VG.rotate) {
-            qdev::hadamard_wave(a, c);
-            a *= c0f();
-            c *= c0f();
-            if (sgv.x < 0.0f) a = -a;
-            if (sgv.y < 0.0f) c = -c;
+        wave_lds_sync();
+        for (int rr = 0; rr < 8; ++rr) {
+            const int gr = row0 + 16 * qb + 8 * h8r + rr;
+            if (gr >= nrows) break;
+            const int i = gr / G, hq = kvh * G + (gr - i * G);
+            const float2 x = reinterpret_cast<const float2*>(s_rows + rr * kDim)[l];
+            store_out_row(x.x, x.y, VG, csv, sgv, p.out + (((size_t)b * p.n_q + i) * p.Hq + hq) * kDim, l);
         }
-        float2* o = reinterpret_cast<float2*>(p.out + (((size_t)b * p.n_q + i0 + r) * p.Hq + hq) * kDim);
-        o[l] = make_float2(a, c);
+        wave_lds_sync();
     }
+}
+
+// One wave per output row: combine the splits' (m, l, acc) in split order, divide, map back.
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
+    const int l = threadIdx.x & 63;
+    const int rr = blockIdx.x * 4 + (threadIdx.x >> 6); // (b * n_q + i) * Hq + hq
+    if (rr >= p.batch * p.n_q * p.Hq) return;
+    const int hq = rr % p.Hq, kvh = hq / p.G;
+    const int S = p.n_splits;
+    const float* P_ = p.partials + (size_t)rr * S * kPartialFloats;
+    float M = kNegInf;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, P_[s * kPartialFloats]);
+    float a = 0.0f, c = 0.0f, L = 0.0f;
+    for (int s = 0; s < S; ++s) {
+        const float m = P_[s * kPartialFloats];
+        const float w = (m == kNegInf) ? 0.0f : exp2f(m - M);
+        L = fmaf(w, P_[s * kPartialFloats + 1], L);
+        const float2 v = reinterpret_cast<const float2*>(P_ + s * kPartialFloats + 4)[l];
+        a = fmaf(w, v.x, a);
+        c = fmaf(w, v.y, c);
+    }
+    a = (L > 0.0f) ? a / L : 0.0f;
+    c = (L > 0.0f) ? c / L : 0.0f;
+    const float2 csv = reinterpret_cast<const float2*>(p.cs + (size_t)(kvh * 2 + 1) * kDim)[l];
+    const float2 sgv = reinterpret_cast<const float2*>(p.signs + (size_t)(kvh * 2 + 1) * kDim)[l];
+    store_out_row(a, c, p.geom[1], csv, sgv, p.out + (size_t)rr * kDim, l);
 }
 
 template <int KB, int VB>
 hipError_t launch_t(const PrefillParams& p, hipStream_t s) {
-    const dim3 grid((p.n_q + 63) / 64, p.Hq, p.batch);
-    hipLaunchKernelGGL((prefill_attn_kernel<KB, VB>), grid, dim3(kWaves * 64), 0, s, p);
+    const int tiles = (p.n_q * p.G + kPrefillRowsPerBlock - 1) / kPrefillRowsPerBlock;
+    const dim3 grid(p.Hkv * p.n_splits * tiles, p.batch);
+    hipLaunchKernelGGL((prefill_attn_kernel<KB, VB>), grid, dim3(kThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.n_splits == 1) return e;
+    const int rows = p.batch * p.n_q * p.Hq;
+    hipLaunchKernelGGL(prefill_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -358,7 +537,7 @@ bool prefill_attn_supported(const PrefillParams& p) {
     const PlaneGeom& K = p.geom[0];
     const PlaneGeom& V = p.geom[1];
     auto ok = [](const PlaneGeom& g) { return g.scheme == kUniform && (g.bits == 4 || g.bits == 8); };
-    return ok(K) && ok(V) && p.window == 0;
+    return ok(K) && ok(V) && p.window == 0 && p.G >= 1 && p.G <= kMaxGroupHeads;
 }
 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {

@@ -19,7 +19,7 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def _run(wl, n0, B, nb, ne, n_q, seed=0):
+def _run(wl, n0, B, nb, ne, n_q, seed=0, workspace="auto"):
     """Every sequence gets n0 tokens; the first nb of them ne more in a second call (ragged
     lengths); then n_q queries per sequence over the cache as it stands."""
     case = Case(wl, n0, layers=[0], batch=B, max_context=n0 + ne)
@@ -37,7 +37,10 @@ def _run(wl, n0, B, nb, ne, n_q, seed=0):
     if wl.dtype == "bf16":
         q = q.to(torch.bfloat16)
     out = torch.full((B, n_q, wl.n_q_heads, 128), float("nan"), device="cuda")
-    case.cache.attn_prefill(0, q.to("cuda"), out)
+    ws = workspace
+    if isinstance(ws, int):
+        ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
+    case.cache.attn_prefill(0, q.to("cuda"), out, workspace=ws)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert np.isfinite(got).all()
@@ -92,6 +95,18 @@ def test_prefill_attention_asym_bits_and_long_chunk():
     wl = W.LLAMA3B_3970_PROGRESSIVE.with_(window=0, k_bits=8)
     _say("case: prefill attention, U8 K / U4 V, n_q 200")
     _run(wl, n0=520, B=1, nb=0, ne=0, n_q=200, seed=2)
+
+
+@pytest.mark.parametrize("ws", ["auto", None, 16], ids=["auto", "cache-workspace", "one-split"])
+def test_prefill_attention_split_plans(ws):
+    # the caller's workspace (several key splits + merge), the cache's own, and one too small for
+    # any partials (the attention kernel finishes the rows itself) all meet the oracle
+    wl = W.LLAMA3B_32K_KVARN
+    _say("case: prefill attention split plan", ws)
+    case, got, q = _run(wl, n0=4000, B=1, nb=0, ne=0, n_q=64, seed=4, workspace=ws)
+    need = case.cache.attn_prefill_workspace(0, 64, 1)
+    _say("  workspace bytes for the fastest plan:", need)
+    assert need > 0  # 192 rows per kv head over 63 key chunks: key splits fill the chip
 
 
 def test_prefill_attention_last_token_equals_decode():
