@@ -502,7 +502,7 @@ int prefill_splits(const kvq_cache* c, int n_q, int batch, int max_len, size_t c
     const long base = tiles * c->cfg.n_kv_heads * batch;
     const long chunks = (max_len + 63) / 64;
     const double rows = static_cast<double>(batch) * n_q * c->cfg.n_q_heads;
-    const double chunk_s = 0.9e-6, merge_launch_s = 4e-6, hbm_Bps = 4e12;
+    const double chunk_s = 3.4e-6, merge_launch_s = 4e-6, hbm_Bps = 4e12; // measured on MI355X
     const long cus = std::max(1, c->num_cus);
     int best = 1;
     double best_t = 0.0;

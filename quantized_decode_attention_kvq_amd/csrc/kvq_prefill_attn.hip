@@ -47,13 +47,16 @@ constexpr int kQB = 1;                            // 16-row column blocks per wa
 constexpr int kWaveRows = 16 * kQB;
 constexpr int kWaves = kPrefillRowsPerBlock / kWaveRows;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kKS = 136;                          // halves per dequantized key row (128 + pad)
-constexpr int kVS = 72;                           // halves per dequantized value row (64 + pad)
+// Row pitches (halves) of the dequantized chunk: 144 and 80 halves put the rows that one
+// ds_read_b128 gathers (16 rows, 16 B each, four column offsets) on disjoint banks; measured on
+// gfx950, pitches of 136 / 72 halves cost about 3 conflict cycles per read.
+constexpr int kKS = 144; // key row: 128 channels + pad
+constexpr int kVS = 80;  // value row: 64 tokens + pad
 constexpr int kKBuf = 2 * 64 * kKS;               // one chunk's keys: 64 hi rows, then 64 lo rows
 constexpr int kVBuf = 2 * 128 * kVS;              // one chunk's values [channel][token]: hi, lo
 constexpr int kLdsHalves = 2 * (kKBuf + kVBuf);   // two buffers of each
-constexpr int kVmRow = 68;                        // value meta row (64 tokens + pad: groups on
-                                                  // different banks)
+constexpr int kVmRow = 80;                        // value meta row, fp16 (64 tokens + pad: the
+                                                  // groups on different banks)
 constexpr int kUnits = 64 * 16 / kThreads;        // 8-code units of a chunk per thread (K; V alike)
 static_assert(kWaves == 8, "two waves per SIMD");
 static_assert(kUnits * kThreads == 1024, "a chunk is 1024 key units and 1024 value units");
@@ -65,17 +68,6 @@ static_assert(kLdsHalves * 2 >= kWaves * 16 * kDim * 4, "the q' rows fit in the 
 // PV product over the chunk's k-th 32 tokens.
 __device__ __forceinline__ int key_lds_row(int t) {
     return 16 * (2 * (t >> 5) + ((t >> 2) & 1)) + 4 * ((t >> 3) & 3) + (t & 3);
-}
-
-__device__ __forceinline__ float h2f(uint32_t bits16) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
-}
-
-// Code i (0..7) of an 8-code unit: 4-bit at bit 16 (i % 2) + 4 (i / 2) of w.x, 8-bit at byte i.
-template <int BITS>
-__device__ __forceinline__ float code_at(uint2 w, int i) {
-    if constexpr (BITS == 4) return (float)((w.x >> (16 * (i & 1) + 4 * (i >> 1))) & 15u);
-    else return (float)(((i < 4 ? w.x : w.y) >> (8 * (i & 3))) & 255u);
 }
 
 // Prefetched global words of one chunk: kUnits key units (8 codes + their group's scale and
@@ -115,18 +107,47 @@ __device__ __forceinline__ void load_vmeta(const Planes& P, int ci, int tid, Chu
     if (tid < 64) R.vm = *reinterpret_cast<const u4*>(P.vmeta + ((size_t)64 * ci + tid) * 16);
 }
 
-// value meta of one chunk -> sm[scale | zero][group][token]
-__device__ __forceinline__ void store_vmeta(float (*sm)[4][kVmRow], int tid, const ChunkRegs& R) {
+// value meta of one chunk -> sm[scale | zero][group][token] (fp16)
+__device__ __forceinline__ void store_vmeta(_Float16 (*sm)[4][kVmRow], int tid, const ChunkRegs& R) {
     if (tid < 64) {
-        sm[0][0][tid] = lo_h(R.vm.x);
-        sm[0][1][tid] = hi_h(R.vm.x);
-        sm[0][2][tid] = lo_h(R.vm.y);
-        sm[0][3][tid] = hi_h(R.vm.y);
-        sm[1][0][tid] = lo_h(R.vm.z);
-        sm[1][1][tid] = hi_h(R.vm.z);
-        sm[1][2][tid] = lo_h(R.vm.w);
-        sm[1][3][tid] = hi_h(R.vm.w);
+        const uint32_t w[4] = {R.vm.x, R.vm.y, R.vm.z, R.vm.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const h2v v = __builtin_bit_cast(h2v, w[k]);
+            sm[k >> 1][2 * (k & 1)][tid] = v[0];
+            sm[k >> 1][2 * (k & 1) + 1][tid] = v[1];
+        }
     }
+}
+
+// Codes 2k and 2k + 1 of an 8-code unit as exact fp16 integers: each code is placed in the
+// mantissa of 1024 (bits 0x6400 | c) and 1024 is subtracted with one packed fp16 add.
+template <int BITS>
+__device__ __forceinline__ h2v code_pair(uint2 w, int k) {
+    uint32_t b;
+    if constexpr (BITS == 4) {
+        b = ((w.x >> (4 * k)) & 0x000F000Fu) | 0x64006400u; // codes at bits 4k and 16 + 4k
+    } else {
+        const uint32_t src = (k < 2) ? w.x : w.y;          // codes at bytes 2k and 2k + 1
+        b = __builtin_amdgcn_perm(0x64646464u, src, (k & 1) ? 0x04030402u : 0x04010400u);
+    }
+    return __builtin_bit_cast(h2v, b) - h2v{(_Float16)1024.0f, (_Float16)1024.0f};
+}
+
+// y = s c + z for a pair: hi = fp16 of y in one rounding (packed fp16 fma), lo = fp16(y - hi)
+// with y - hi formed in fp32.
+struct Pair {
+    uint32_t hi, lo;
+};
+__device__ __forceinline__ Pair dequant_pair(h2v s, h2v c, h2v z, float mone) {
+    const h2v h = __builtin_elementwise_fma(s, c, z);
+    h2v r;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const float y = fmaf((float)s[e], (float)c[e], (float)z[e]);
+        r[e] = (_Float16)fmaf((float)h[e], mone, y); // mixed fp16 / fp32 fma, rounded once to fp16
+    }
+    return Pair{__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, r)};
 }
 
 // Dequantize the prefetched chunk into one key buffer and one value buffer.
@@ -138,47 +159,49 @@ __device__ __forceinline__ void store_vmeta(float (*sm)[4][kVmRow], int tid, con
 //    slot s at slot s ^ (d / 16), which keeps both these writes and the operand reads free of
 //    bank conflicts.
 template <int KB, int VB>
-__device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const float (*sm)[4][kVmRow], int tid,
+__device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const _Float16 (*sm)[4][kVmRow], int tid,
                                               const ChunkRegs& R) {
+    // -1 in a register the compiler cannot see through: hi * (-1) + y stays one mixed-precision
+    // fma (v_fma_mix*) instead of being rewritten as a conversion and a subtraction
+    float mone = -1.0f;
+    asm volatile("" : "+v"(mone));
 #pragma unroll
     for (int j = 0; j < kUnits; ++j) {
         const int u = tid + kThreads * j, p = u >> 4, w = u & 15;
         const int t = 4 * (p & 15) + (p >> 4);
-        const float sc = h2f(R.ks[j]), zr = h2f(R.kz[j]);
-        h8 hi, lo;
+        const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)R.ks[j]);
+        const _Float16 zr = __builtin_bit_cast(_Float16, (uint16_t)R.kz[j]);
+        u4 hi, lo;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float y = fmaf(sc, code_at<KB>(R.kc[j], i), zr);
-            const _Float16 h = (_Float16)y;
-            hi[i] = h;
-            lo[i] = (_Float16)(y - (float)h);
+        for (int k = 0; k < 4; ++k) {
+            const Pair q = dequant_pair(h2v{sc, sc}, code_pair<KB>(R.kc[j], k), h2v{zr, zr}, mone);
+            hi[k] = q.hi;
+            lo[k] = q.lo;
         }
         _Float16* dst = sk + key_lds_row(t) * kKS + 8 * w; // channels 32 (w / 4) + 8 (w % 4) + i
-        *reinterpret_cast<h8*>(dst) = hi;
-        *reinterpret_cast<h8*>(dst + 64 * kKS) = lo;
+        *reinterpret_cast<u4*>(dst) = hi;
+        *reinterpret_cast<u4*>(dst + 64 * kKS) = lo;
     }
 #pragma unroll
     for (int j = 0; j < kUnits; ++j) {
         const int u = tid + kThreads * j, half = u >> 9, w = u & 511;
         const int kb = w >> 7, n = (w >> 3) & 15, N = w & 7, d = 16 * N + n, g = N >> 1;
         const int t0 = 32 * half + 8 * kb;
-        const float4 s0 = *reinterpret_cast<const float4*>(&sm[0][g][t0]);
-        const float4 s1 = *reinterpret_cast<const float4*>(&sm[0][g][t0 + 4]);
-        const float4 z0 = *reinterpret_cast<const float4*>(&sm[1][g][t0]);
-        const float4 z1 = *reinterpret_cast<const float4*>(&sm[1][g][t0 + 4]);
-        const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-        const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-        h8 hv, lv;
+        const u4 sw = *reinterpret_cast<const u4*>(&sm[0][g][t0]);
+        const u4 zw = *reinterpret_cast<const u4*>(&sm[1][g][t0]);
+        u4 hi, lo;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float y = fmaf(ss[i], code_at<VB>(R.vc[j], i), zz[i]);
-            const _Float16 h = (_Float16)y;
-            hv[i] = h;
-            lv[i] = (_Float16)(y - (float)h);
+        for (int k = 0; k < 4; ++k) {
+            // bit_cast a named scalar: clang's bit_cast of an ext_vector element reads element 0
+            const uint32_t s2 = sw[k], z2 = zw[k];
+            const Pair q = dequant_pair(__builtin_bit_cast(h2v, s2), code_pair<VB>(R.vc[j], k),
+                                        __builtin_bit_cast(h2v, z2), mone);
+            hi[k] = q.hi;
+            lo[k] = q.lo;
         }
         _Float16* dst = sv + d * kVS + 8 * ((4 * half + kb) ^ N);
-        *reinterpret_cast<h8*>(dst) = hv;
-        *reinterpret_cast<h8*>(dst + 128 * kVS) = lv;
+        *reinterpret_cast<u4*>(dst) = hi;
+        *reinterpret_cast<u4*>(dst + 128 * kVS) = lo;
     }
 }
 
@@ -208,7 +231,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <int KB, int VB>
 __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p) {
     __shared__ __align__(16) _Float16 s_lds[kLdsHalves];
-    __shared__ __align__(16) float s_vm[2][2][4][kVmRow]; // [buffer][scale | zero][group][token]
+    __shared__ __align__(16) _Float16 s_vm[2][2][4][kVmRow]; // [buffer][scale | zero][group][token]
     __shared__ float s_qf[kWaves][kWaveRows];          // 2^-e of each row's q' scaling
 
     const int S = p.n_splits;
@@ -354,76 +377,80 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
         const _Float16* sk = s_lds + buf * kKBuf;
         const _Float16* sv = s_lds + 2 * kKBuf + buf * kVBuf;
         const bool masked = 64 * ci + 63 > (int)pos_min;
+        // ---- S^T for the chunk's four 16-token tiles (tile b, row 4 lq + v = token
+        // 32 (b / 2) + 8 lq + 4 (b % 2) + v); three accumulators per tile (K_hi q_hi, K_hi q_lo,
+        // K_lo q_hi) keep the matrix-core dependency chains four products long
+        f4 Sa[4][kQB], Sb[4][kQB], Sd[4][kQB];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int qb = 0; qb < kQB; ++qb) Sa[b][qb] = Sb[b][qb] = Sd[b][qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const _Float16* kr = sk + (16 * b + lr) * kKS + 32 * ks + 8 * lq;
+                const h8 Ah = *reinterpret_cast<const h8*>(kr);
+                const h8 Al = *reinterpret_cast<const h8*>(kr + 64 * kKS);
+#pragma unroll
+                for (int qb = 0; qb < kQB; ++qb) {
+                    Sa[b][qb] = mfma16(Ah, Bh[ks][qb], Sa[b][qb]);
+                    Sb[b][qb] = mfma16(Ah, Bl[ks][qb], Sb[b][qb]);
+                    Sd[b][qb] = mfma16(Al, Bh[ks][qb], Sd[b][qb]);
+                }
+            }
+        }
+        // ---- online softmax of each column over the chunk's 64 tokens.  The running maximum m
+        // moves only when a score exceeds it by more than kLazy (log2 units), so the accumulator
+        // is rescaled rarely; weights stay below 2^kLazy.
+        h8 Pb[2][kQB]; // [k-slice hh][column block]: element i = token 32 hh + 8 lq + i
+        float al[kQB];
+        bool need = false;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+            float raw[16]; // raw[8 hh + 4 tb + v]: token 32 hh + 8 lq + 4 tb + v
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) raw[4 * b + v] = Sa[b][qb][v] + (Sb[b][qb][v] + Sd[b][qb][v]);
+            if (__builtin_expect(masked, 0)) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int t = 64 * ci + 32 * (i >> 3) + 8 * lq + (i & 7);
+                    if (t > pos[qb]) raw[i] = kNegInf;
+                }
+            }
+            float mx = raw[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, raw[i]);
+            mx = fmaxf(mx, xor_lane<16>(mx));
+            mx = fmaxf(mx, xor_lane<32>(mx)) * F[qb];
+            const bool up = mx > m_run[qb] + kLazy;
+            al[qb] = up ? __builtin_amdgcn_exp2f(m_run[qb] - mx) : 1.0f;
+            if (up) m_run[qb] = mx;
+            need |= up;
+            const float m = m_run[qb];
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float pv = (m == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(fmaf(raw[i], F[qb], -m));
+                sum += pv;
+                Pb[i >> 3][qb][i & 7] = (_Float16)pv;
+            }
+            l_run[qb] = fmaf(l_run[qb], al[qb], sum);
+        }
+        if (__ballot(need) != 0) {
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+#pragma unroll
+                for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) O[n][qb][v] *= al[qb];
+        }
+        // ---- O^T += V^T P^T over the chunk's two 32-token k-slices (A = values [channel
+        // 16 n + lr][token 32 hh + 8 lq + i])
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            // ---- S^T tiles 2 hh + tb of this 32-token half against both column blocks
-            f4 Sc[2][kQB];
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                for (int qb = 0; qb < kQB; ++qb) Sc[tb][qb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb) {
-                    const _Float16* kr = sk + (16 * (2 * hh + tb) + lr) * kKS + 32 * ks + 8 * lq;
-                    const h8 Ah = *reinterpret_cast<const h8*>(kr);
-                    const h8 Al = *reinterpret_cast<const h8*>(kr + 64 * kKS);
-#pragma unroll
-                    for (int qb = 0; qb < kQB; ++qb) {
-                        Sc[tb][qb] = mfma16(Ah, Bh[ks][qb], Sc[tb][qb]);
-                        Sc[tb][qb] = mfma16(Ah, Bl[ks][qb], Sc[tb][qb]);
-                        Sc[tb][qb] = mfma16(Al, Bh[ks][qb], Sc[tb][qb]);
-                    }
-                }
-            }
-            // ---- online softmax of each column (token 64 ci + 32 hh + 8 lq + 4 tb + v).  The
-            // running maximum m moves only when a score exceeds it by more than kLazy (log2
-            // units), so the accumulator is rescaled rarely; weights stay below 2^kLazy.
-            h8 Pb[kQB];
-            float al[kQB];
-            bool need = false;
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) {
-                float raw[8];
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) raw[4 * tb + v] = Sc[tb][qb][v];
-                if (__builtin_expect(masked, 0)) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int t = 64 * ci + 32 * hh + 8 * lq + i;
-                        if (t > pos[qb]) raw[i] = kNegInf;
-                    }
-                }
-                float mx = fmaxf(fmaxf(fmaxf(raw[0], raw[1]), fmaxf(raw[2], raw[3])),
-                                 fmaxf(fmaxf(raw[4], raw[5]), fmaxf(raw[6], raw[7])));
-                mx = fmaxf(mx, xor_lane<16>(mx));
-                mx = fmaxf(mx, xor_lane<32>(mx)) * F[qb];
-                const bool up = mx > m_run[qb] + kLazy;
-                al[qb] = up ? __builtin_amdgcn_exp2f(m_run[qb] - mx) : 1.0f;
-                if (up) m_run[qb] = mx;
-                need |= up;
-                const float m = m_run[qb];
-                float sum = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float pv = (m == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(fmaf(raw[i], F[qb], -m));
-                    sum += pv;
-                    Pb[qb][i] = (_Float16)pv;
-                }
-                l_run[qb] = fmaf(l_run[qb], al[qb], sum);
-            }
-            if (__ballot(need) != 0) {
-#pragma unroll
-                for (int n = 0; n < 8; ++n)
-#pragma unroll
-                    for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) O[n][qb][v] *= al[qb];
-            }
-            // ---- O^T += V^T P^T over this half (A = values [channel 16 n + lr][token 8 lq + i])
 #pragma unroll
             for (int n = 0; n < 8; ++n) {
                 const _Float16* vr = sv + (16 * n + lr) * kVS + 8 * ((4 * hh + lq) ^ n);
@@ -431,8 +458,8 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
                 const h8 Vl = *reinterpret_cast<const h8*>(vr + 128 * kVS);
 #pragma unroll
                 for (int qb = 0; qb < kQB; ++qb) {
-                    O[n][qb] = mfma16(Vh, Pb[qb], O[n][qb]);
-                    O[n][qb] = mfma16(Vl, Pb[qb], O[n][qb]);
+                    O[n][qb] = mfma16(Vh, Pb[hh][qb], O[n][qb]);
+                    O[n][qb] = mfma16(Vl, Pb[hh][qb], O[n][qb]);
                 }
             }
         }
