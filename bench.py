@@ -33,7 +33,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak (no sparsity)
 
 def token_head_bytes(scheme, bits):
     """Compressed bytes per token-head read by decode (codes + scale/zero or norms + QJL bits)."""
-    if scheme == W.UNIFORM:
+    if not W.is_turbo(scheme):
         return 16 * bits + 16
     if scheme == W.TURBO_QJL:
         return 48 + 4 + 16
@@ -116,7 +116,7 @@ def prefill_report(wl: W.Workload, prefill_s):
 
 def split_kernel_name(wl: W.Workload) -> str:
     """The split-K decode kernel the library launches for this cache (matrix-core path)."""
-    kind = lambda scheme, bits: "Tb" if scheme != W.UNIFORM else f"U{bits}"  # noqa: E731
+    kind = lambda scheme, bits: "Tb" if W.is_turbo(scheme) else f"U{bits}"  # noqa: E731
     return (f"decode_mfma_kernel (K {kind(wl.k_scheme, wl.k_bits)}, V {kind(wl.v_scheme, wl.v_bits)}, "
             f"{wl.group} query heads per kv head)")
 
@@ -166,8 +166,8 @@ def cpu_baseline(wl: W.Workload, kv0, budget_s: float):
         for tensor, X in ((0, k0), (1, v0)):
             scheme = wl.k_scheme if tensor == 0 else wl.v_scheme
             bits = wl.k_bits if tensor == 0 else wl.v_bits
-            rot = (wl.rotate_k if tensor == 0 else wl.rotate_v) or scheme != W.UNIFORM
-            sink = wl.sinkhorn_iters > 0 and scheme == W.UNIFORM
+            rot = (wl.rotate_k if tensor == 0 else wl.rotate_v) or W.is_turbo(scheme)
+            sink = wl.sinkhorn_iters > 0 and not W.is_turbo(scheme)
             kw = dict(mu=mu, theta=theta, S=S)
             if rot:
                 kw["signs"] = signs[h, tensor]

@@ -52,7 +52,11 @@ typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 typedef enum {
     KVQ_UNIFORM = 0,   /* b-bit asymmetric groups of 32, fp16 scale + fp16 zero [P1], b = 4|8 */
     KVQ_TURBO_QJL = 1, /* K only: rotation + 3-bit Lloyd-Max code + 1-bit QJL residual [P3]  */
-    KVQ_TURBO_MSE = 2  /* rotation + 3-bit Lloyd-Max code, no residual sketch [P3]            */
+    KVQ_TURBO_MSE = 2, /* rotation + 3-bit Lloyd-Max code, no residual sketch [P3]            */
+    KVQ_Q8_0 = 3       /* symmetric 8-bit groups of 32, one fp16 scale d ("q8_0", [P2]'s
+                          baseline; K = Q8 of [P3]'s application rules): q = rint(y / d) in
+                          [-127, 127] with d = fp16(max|y| / 127); stored in the UNIFORM 8-bit
+                          layout as code q + 128 with zero = -128 d, so y = d q exactly       */
 } kvq_scheme;
 
 typedef struct {
@@ -61,7 +65,7 @@ typedef struct {
     int max_batch, max_context;          /* sequences per call (<= 64); tokens per sequence
                                             ("context_length" of [P1])                       */
     int k_scheme, v_scheme;              /* kvq_scheme, chosen separately for K and V [P2]   */
-    int k_bits, v_bits;                  /* UNIFORM: 4 or 8; TURBO_*: 3                      */
+    int k_bits, v_bits;                  /* UNIFORM: 4 or 8; TURBO_*: 3; Q8_0: 8             */
     int group_size;                      /* must be 32                                       */
     int fp32_window;                     /* 0 = flat, 128 = progressive [P1]                 */
     int rotate_k, rotate_v;              /* random-sign Walsh-Hadamard before coding [P2];

@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "kvq_oracle.c")
 LIB = os.path.join(HERE, "libkvq_oracle.so")
 
-UNIFORM, TURBO_QJL, TURBO_MSE = 0, 1, 2
+UNIFORM, TURBO_QJL, TURBO_MSE, Q8_0 = 0, 1, 2, 3
 TENSOR_K, TENSOR_V = 0, 1
 D = 128
 
@@ -70,6 +70,7 @@ def lib():
         L.orc_unrotate_f64.argtypes = [_Dp, _F, _Dp]
         L.orc_sinkhorn.argtypes = [_F, ctypes.c_int, _F, ctypes.c_int, _F, _F, _Dp, _Dp]
         L.orc_quant_group.argtypes = [_F, ctypes.c_int, _U8, _U16, _U16]
+        L.orc_quant_group_sym8.argtypes = [_F, _U8, _U16, _U16]
         L.orc_lloyd_max.argtypes = [ctypes.c_int, _Dp, _F, _F, _Dp]
         L.orc_turbo_encode.argtypes = [_F, ctypes.POINTER(Tables), ctypes.c_int, _F, _U8, _U16,
                                        _U16, _U8, _F]
@@ -168,6 +169,16 @@ def quant_group(y, bits):
     return codes, int(s16[0]), int(z16[0])
 
 
+def quant_group_sym8(y):
+    """Symmetric 8-bit ("q8_0") group quantizer: (codes q + 128, fp16 bits of d, of -128 d)."""
+    y = _f32(y)
+    codes = np.empty(32, np.uint8)
+    d16 = np.zeros(1, np.uint16)
+    z16 = np.zeros(1, np.uint16)
+    lib().orc_quant_group_sym8(_p(y, _F), _p(codes, _U8), _p(d16, _U16), _p(z16, _U16))
+    return codes, int(d16[0]), int(z16[0])
+
+
 def lloyd_max(iters=2000):
     mu_star = np.empty(8, np.float64)
     mu = np.empty(8, np.float32)
@@ -224,7 +235,7 @@ class Plane:
     """One (layer, sequence, kv head, tensor) plane: code bytes, meta bytes, QJL bytes, ring."""
 
     def __init__(self, scheme, bits, rotate, sinkhorn, window, tensor, capacity):
-        self.cfg = PlaneCfg(scheme, bits, int(rotate or scheme != UNIFORM), int(sinkhorn), window,
+        self.cfg = PlaneCfg(scheme, bits, int(rotate or scheme in (TURBO_QJL, TURBO_MSE)), int(sinkhorn), window,
                             tensor, capacity)
         L = lib()
         r = ctypes.byref(self.cfg)

@@ -14,6 +14,9 @@
  *   Sinkhorn ................ KVarN post, TL;DR: Sinkhorn variance balancing.
  *   uniform quantizer ....... quantcpp article, progressive table: 4-bit KV; groups of 32 along
  *                             the head dimension with fp16 scale/zero (reading of "6.4x").
+ *   symmetric 8-bit ......... "q8_0": the 8-bit cache type of the KVarN post's comparison and the
+ *                             "K = Q8" of the 2026 survey page's application rules (named, not
+ *                             defined there: one fp16 scale per 32, codes in [-127, 127]).
  *   Lloyd-Max + turbo ....... TurboQuant row: per-coordinate optimal scalar quantizer after a
  *                             random rotation, 1-bit QJL on the residual for an unbiased inner
  *                             product.
@@ -252,6 +255,30 @@ void orc_quant_group(const float* y, int bits, uint8_t* codes, uint16_t* s16o, u
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* symmetric 8-bit quantizer for one group of 32 ("q8_0"; see the header)                      */
+/* ------------------------------------------------------------------------------------------ */
+
+void orc_quant_group_sym8(const float* y, uint8_t* codes, uint16_t* d16o, uint16_t* z16o)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < GS; i++) {
+        float a = fabsf(y[i]);
+        if (a > amax) amax = a;
+    }
+    uint16_t d16 = orc_f32_to_f16_rn(amax / 127.0f);
+    float d = orc_f16_to_f32(d16);
+    float inv = (d > 0.0f) ? 1.0f / d : 0.0f;
+    for (int i = 0; i < GS; i++) {
+        float q = rintf(y[i] * inv);
+        if (q < -127.0f) q = -127.0f;
+        if (q > 127.0f) q = 127.0f;
+        codes[i] = (uint8_t)((int)q + 128);
+    }
+    *d16o = d16;
+    *z16o = orc_f32_to_f16_rn(-128.0f * d);
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* Lloyd-Max 8-level quantizer of N(0,1), scaled to N(0,1/128) (reading C5)                    */
 /* ------------------------------------------------------------------------------------------ */
 
@@ -393,9 +420,12 @@ static int ceil_to(int x, int m) { return (x + m - 1) / m * m; }
 
 static size_t k_row(int t) { return (size_t)(64 * (t / 64) + 16 * ((t % 64) % 4) + (t % 64) / 4); }
 
+/* q8_0 planes use the 8-bit uniform byte layout */
+static int uniform_layout(const orc_plane_cfg* pc) { return pc->scheme == ORC_UNIFORM || pc->scheme == ORC_Q8_0; }
+
 size_t orc_codes_bytes(const orc_plane_cfg* pc)
 {
-    if (pc->scheme != ORC_UNIFORM) return (size_t)ceil_to(pc->capacity, 64) * 48;
+    if (!uniform_layout(pc)) return (size_t)ceil_to(pc->capacity, 64) * 48;
     return (size_t)ceil_to(pc->capacity, 64) * 16 * pc->bits;
 }
 
@@ -455,7 +485,7 @@ static void pack_token(const orc_plane_cfg* pc, int t, const uint8_t* code, cons
                        const uint16_t* z16, uint16_t n16, uint16_t g16, const uint8_t* bits,
                        uint8_t* codes, uint8_t* meta, uint8_t* qjl)
 {
-    if (pc->scheme == ORC_UNIFORM) {
+    if (uniform_layout(pc)) {
         if (pc->tensor == ORC_TENSOR_K) {
             size_t row = k_row(t);
             uint8_t* r = codes + row * (size_t)(16 * pc->bits);
@@ -515,7 +545,7 @@ static void pack_token(const orc_plane_cfg* pc, int t, const uint8_t* code, cons
 void orc_plane_read(const orc_plane_cfg* pc, const uint8_t* codes, const uint8_t* meta,
                     const uint8_t* qjl, int t, uint8_t* code, uint16_t* meta8, uint8_t* bits)
 {
-    if (pc->scheme == ORC_UNIFORM) {
+    if (uniform_layout(pc)) {
         const uint8_t* m;
         if (pc->tensor == ORC_TENSOR_K) {
             size_t row = k_row(t);
@@ -581,7 +611,7 @@ void orc_plane_append(const orc_plane_cfg* pc, const orc_tables* tb, const float
         const float* x = X + (size_t)k * D;
         uint8_t code[D], bits[D];
         uint16_t s16[NG] = {0}, z16[NG] = {0}, n16 = 0, g16 = 0;
-        if (pc->scheme == ORC_UNIFORM) {
+        if (uniform_layout(pc)) {
             float y[D];
             if (pc->rotate)
                 orc_rotate_f32(x, tb->signs, y);
@@ -589,7 +619,12 @@ void orc_plane_append(const orc_plane_cfg* pc, const orc_tables* tb, const float
                 memcpy(y, x, sizeof y);
             if (pc->sinkhorn)
                 for (int j = 0; j < D; j++) y[j] = y[j] * tb->inv_c[j];
-            for (int g = 0; g < NG; g++) orc_quant_group(y + GS * g, pc->bits, code + GS * g, &s16[g], &z16[g]);
+            for (int g = 0; g < NG; g++) {
+                if (pc->scheme == ORC_Q8_0)
+                    orc_quant_group_sym8(y + GS * g, code + GS * g, &s16[g], &z16[g]);
+                else
+                    orc_quant_group(y + GS * g, pc->bits, code + GS * g, &s16[g], &z16[g]);
+            }
         } else {
             orc_turbo_encode(x, tb, pc->scheme == ORC_TURBO_QJL, NULL, code, &n16, &g16, bits, NULL);
         }
@@ -609,11 +644,14 @@ void orc_dequant_token(const orc_plane_cfg* pc, const orc_tables* tb, const uint
     uint16_t m8[8];
     double y[D];
     orc_plane_read(pc, codes, meta, NULL, t, code, m8, NULL);
-    if (pc->scheme == ORC_UNIFORM) {
+    if (uniform_layout(pc)) {
         for (int j = 0; j < D; j++) {
             int g = j / GS;
             double s = orc_f16_to_f32(m8[g]), z = orc_f16_to_f32(m8[4 + g]);
-            y[j] = z + s * (double)code[j]; /* exact in binary64 */
+            if (pc->scheme == ORC_Q8_0)
+                y[j] = s * ((double)code[j] - 128.0); /* d q */
+            else
+                y[j] = z + s * (double)code[j]; /* exact in binary64 */
             if (pc->sinkhorn) y[j] = y[j] * (double)tb->c[j];
         }
         if (pc->rotate)

@@ -34,12 +34,12 @@ extern "C" {
 #define ORC_GROUP 32
 #define ORC_NGROUPS 4
 
-enum { ORC_UNIFORM = 0, ORC_TURBO_QJL = 1, ORC_TURBO_MSE = 2 };
+enum { ORC_UNIFORM = 0, ORC_TURBO_QJL = 1, ORC_TURBO_MSE = 2, ORC_Q8_0 = 3 };
 enum { ORC_TENSOR_K = 0, ORC_TENSOR_V = 1 };
 
 /* One (layer, sequence, kv head, tensor) plane description. */
 typedef struct {
-    int scheme;    /* ORC_UNIFORM / ORC_TURBO_QJL / ORC_TURBO_MSE */
+    int scheme;    /* ORC_UNIFORM / ORC_TURBO_QJL / ORC_TURBO_MSE / ORC_Q8_0 */
     int bits;      /* uniform: 4 or 8; turbo: 3 */
     int rotate;    /* random-sign WHT before coding (always on for turbo) */
     int sinkhorn;  /* fold 1/c before uniform coding */
@@ -74,6 +74,13 @@ void orc_sinkhorn(const float* X, int n, const float* signs_or_null, int iters, 
 
 /* ---- uniform asymmetric group quantizer ---- */
 void orc_quant_group(const float* y, int bits, uint8_t* codes, uint16_t* s16, uint16_t* z16);
+
+/* ---- symmetric 8-bit group quantizer (reading of "q8_0", named as a cache type by the KVarN
+ * post's comparison and as "K = Q8" by the application rules of the 2026 survey page; neither
+ * page defines it): d = fp16 round-to-nearest of max|y| / 127, q = rint(y * fp32(1/d)) clamped
+ * to [-127, 127] (d = 0: q = 0).  Stored in the 8-bit uniform layout as code q + 128 with scale
+ * field d and zero field fp16(-128 d), so that zero + scale * code = d q. ---- */
+void orc_quant_group_sym8(const float* y, uint8_t* codes, uint16_t* d16, uint16_t* z16);
 
 /* ---- Lloyd-Max codebook ---- */
 void orc_lloyd_max(int iters, double* mu_star, float* mu, float* theta, double* last_change);

@@ -44,12 +44,16 @@ kvq_status check_config(const kvq_config* c) {
     if (c->max_batch > kMaxBatch) return KVQ_ERR_UNSUPPORTED;
     if (c->max_context > (1 << 26)) return KVQ_ERR_UNSUPPORTED;
     if (c->fp32_window != 0 && c->fp32_window != kWindowMax) return KVQ_ERR_UNSUPPORTED;
-    if (c->k_scheme != KVQ_UNIFORM && c->k_scheme != KVQ_TURBO_QJL) return KVQ_ERR_UNSUPPORTED;
-    if (c->v_scheme != KVQ_UNIFORM && c->v_scheme != KVQ_TURBO_MSE) return KVQ_ERR_UNSUPPORTED;
-    if (c->k_scheme == KVQ_UNIFORM && c->k_bits != 4 && c->k_bits != 8) return KVQ_ERR_UNSUPPORTED;
-    if (c->v_scheme == KVQ_UNIFORM && c->v_bits != 4 && c->v_bits != 8) return KVQ_ERR_UNSUPPORTED;
-    if (c->k_scheme != KVQ_UNIFORM && c->k_bits != 3) return KVQ_ERR_UNSUPPORTED;
-    if (c->v_scheme != KVQ_UNIFORM && c->v_bits != 3) return KVQ_ERR_UNSUPPORTED;
+    if (c->k_scheme != KVQ_UNIFORM && c->k_scheme != KVQ_TURBO_QJL && c->k_scheme != KVQ_Q8_0)
+        return KVQ_ERR_UNSUPPORTED;
+    if (c->v_scheme != KVQ_UNIFORM && c->v_scheme != KVQ_TURBO_MSE && c->v_scheme != KVQ_Q8_0)
+        return KVQ_ERR_UNSUPPORTED;
+    for (int t = 0; t < 2; ++t) {
+        const int scheme = t == 0 ? c->k_scheme : c->v_scheme, bits = t == 0 ? c->k_bits : c->v_bits;
+        if (scheme == KVQ_UNIFORM && bits != 4 && bits != 8) return KVQ_ERR_UNSUPPORTED;
+        if (scheme == KVQ_Q8_0 && bits != 8) return KVQ_ERR_UNSUPPORTED;
+        if ((scheme == KVQ_TURBO_QJL || scheme == KVQ_TURBO_MSE) && bits != 3) return KVQ_ERR_UNSUPPORTED;
+    }
     if ((c->rotate_k != 0 && c->rotate_k != 1) || (c->rotate_v != 0 && c->rotate_v != 1))
         return KVQ_ERR_INVALID_ARG;
     if (c->sinkhorn_iters > 1000) return KVQ_ERR_UNSUPPORTED;
@@ -60,8 +64,12 @@ kvq_status check_config(const kvq_config* c) {
 
 PlaneGeom make_geom(const kvq_config* c, int tensor) {
     PlaneGeom g{};
-    const int scheme = tensor == 0 ? c->k_scheme : c->v_scheme;
+    const int cfg_scheme = tensor == 0 ? c->k_scheme : c->v_scheme;
+    // a q8_0 plane is an 8-bit uniform plane to every kernel that reads it; only its quantizer
+    // differs (symmetric codes, zero field = -128 * scale)
+    const int scheme = cfg_scheme == KVQ_Q8_0 ? KVQ_UNIFORM : cfg_scheme;
     g.scheme = scheme;
+    g.symmetric = cfg_scheme == KVQ_Q8_0 ? 1 : 0;
     g.bits = tensor == 0 ? c->k_bits : c->v_bits;
     g.rotate = (scheme != KVQ_UNIFORM) ? 1 : (tensor == 0 ? c->rotate_k : c->rotate_v);
     g.sinkhorn = (scheme == KVQ_UNIFORM && c->sinkhorn_iters > 0) ? 1 : 0;
@@ -157,7 +165,7 @@ struct kvq_cache {
     bool needs_signs() const { return plan.geom[0].rotate || plan.geom[1].rotate; }
     bool needs_S() const { return cfg.k_scheme == KVQ_TURBO_QJL; }
     bool needs_calib() const { return plan.geom[0].sinkhorn || plan.geom[1].sinkhorn; }
-    bool turbo() const { return cfg.k_scheme != KVQ_UNIFORM || cfg.v_scheme != KVQ_UNIFORM; }
+    bool turbo() const { return cfg.k_scheme == KVQ_TURBO_QJL || cfg.v_scheme == KVQ_TURBO_MSE; }
 };
 
 namespace {

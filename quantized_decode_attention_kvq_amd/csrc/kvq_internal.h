@@ -22,6 +22,7 @@ enum Scheme { kUniform = 0, kTurboQjl = 1, kTurboMse = 2 };
 // Geometry of one tensor's plane inside a (layer, seq, head) slot.
 struct PlaneGeom {
     int scheme, bits, rotate, sinkhorn;
+    int symmetric; // uniform 8-bit plane written by the symmetric (q8_0-style) quantizer
     size_t codes_off, meta_off, qjl_off, ring_off; // byte offsets from the slot base
     size_t codes_bytes, meta_bytes, qjl_bytes, ring_bytes;
 };

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(QJL ? 1024 : 256) void quantize_turbo_bulk_kernel(Q
 // launch covers tensors tensor0 .. tensor0 + n_tensors - 1, which share that format.  Wave w of
 // workgroup x takes octets 4x + w, then every 4 * gridDim.x-th after it, of one (tensor,
 // sequence, kv head), requesting the next octet's source before quantizing the current one.
-template <int BITS, bool ROT, bool SINK>
+template <int BITS, bool ROT, bool SINK, bool SYM>
 __global__ __launch_bounds__(256) void quantize_uniform_bulk_kernel(QuantParams p, int tensor0,
                                                                     int n_tensors) {
     __shared__ __align__(16) uint8_t wv[4][8 * kDim];
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void quantize_uniform_bulk_kernel(QuantParams 
     for (; u < p.groups8; u += step) {
         qbulk::OctetIn nxt;
         qbulk::load_octet(w, g_first + u + step, nxt);
-        qbulk::uniform_octet<BITS, ROT, SINK>(w, is_v, g_first + u, cur, sgm, ic, wv[wave]);
+        qbulk::uniform_octet<BITS, ROT, SINK, SYM>(w, is_v, g_first + u, cur, sgm, ic, wv[wave]);
         cur = nxt;
     }
 }
@@ -323,19 +323,23 @@ hipError_t launch_turbo_bulk(const QuantParams& p, hipStream_t s, int tensor) {
     return hipGetLastError();
 }
 
-template <int BITS, bool ROT, bool SINK>
+template <int BITS, bool ROT, bool SINK, bool SYM = false>
 hipError_t launch_uniform_bulk(const QuantParams& p, hipStream_t s, int tensor0, int n_tensors) {
     const int planes = p.Hkv * p.batch * n_tensors;
     const int gx = std::max(1, std::min((p.groups8 + 3) / 4, (kQuantBulkBlocks + planes - 1) / planes));
-    hipLaunchKernelGGL((quantize_uniform_bulk_kernel<BITS, ROT, SINK>), dim3(gx, p.Hkv, n_tensors * p.batch),
+    hipLaunchKernelGGL((quantize_uniform_bulk_kernel<BITS, ROT, SINK, SYM>), dim3(gx, p.Hkv, n_tensors * p.batch),
                        dim3(256), 0, s, p, tensor0, n_tensors);
     return hipGetLastError();
 }
 
 hipError_t launch_uniform_bulk_for(const PlaneGeom& G, const QuantParams& p, hipStream_t s,
                                    int tensor0, int n_tensors) {
-    const int key = (G.bits == 8 ? 4 : 0) | (G.rotate ? 2 : 0) | (G.sinkhorn ? 1 : 0);
+    const int key = (G.symmetric ? 8 : 0) | (G.bits == 8 ? 4 : 0) | (G.rotate ? 2 : 0) | (G.sinkhorn ? 1 : 0);
     switch (key) {
+    case 12: return launch_uniform_bulk<8, false, false, true>(p, s, tensor0, n_tensors);
+    case 13: return launch_uniform_bulk<8, false, true, true>(p, s, tensor0, n_tensors);
+    case 14: return launch_uniform_bulk<8, true, false, true>(p, s, tensor0, n_tensors);
+    case 15: return launch_uniform_bulk<8, true, true, true>(p, s, tensor0, n_tensors);
     case 0: return launch_uniform_bulk<4, false, false>(p, s, tensor0, n_tensors);
     case 1: return launch_uniform_bulk<4, false, true>(p, s, tensor0, n_tensors);
     case 2: return launch_uniform_bulk<4, true, false>(p, s, tensor0, n_tensors);
@@ -363,7 +367,7 @@ hipError_t launch_quantize_bulk(const QuantParams& p, hipStream_t s) {
     const PlaneGeom &g0 = p.geom[0], &g1 = p.geom[1];
     const int s0 = g0.scheme, s1 = g1.scheme;
     const bool same = s0 == kUniform && s1 == kUniform && g0.bits == g1.bits &&
-                      g0.rotate == g1.rotate && g0.sinkhorn == g1.sinkhorn;
+                      g0.rotate == g1.rotate && g0.sinkhorn == g1.sinkhorn && g0.symmetric == g1.symmetric;
     if (same) return launch_bulk_scheme(s0, p, s, 0, 2);
     const hipError_t e = launch_bulk_scheme(s0, p, s, 0, 1);
     if (e != hipSuccess) return e;

@@ -162,6 +162,25 @@ __device__ __forceinline__ void group_codes(const float* e, uint32_t* r, uint16_
     }
 }
 
+// Symmetric 8-bit (q8_0-style) code of the lane's 8 values (group = lanes 4g .. 4g+3 of the
+// token): d = fp16(max|x| / 127), q = rint(x * fp32(1/d)) clamped to [-127, 127], code q + 128
+// (r[i] = 2^23 + code as binary32 bits), zero field fp16(-128 d).
+__device__ __forceinline__ void group_codes_sym8(const float* e, uint32_t* r, uint16_t& s16, uint16_t& z16) {
+    float amax = fabsf(e[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) amax = fmaxf(amax, fabsf(e[i]));
+    amax = xor_reduce<4>(amax, [](float x, float y) { return fmaxf(x, y); });
+    s16 = f16_rn(amax / 127.0f);
+    const float d = f16_val(s16);
+    z16 = f16_rn(-128.0f * d);
+    const float inv = (d > 0.0f) ? 1.0f / d : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float q = fminf(fmaxf(rintf(e[i] * inv), -127.0f), 127.0f);
+        r[i] = __float_as_uint((magic23() + 128.0f) + q);
+    }
+}
+
 // Low bytes of a and b at bytes 0 and 2: a | b << 16 for codes below 256.
 __device__ __forceinline__ uint32_t pair16(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_perm(b, a, 0x0C040C00u);
@@ -205,9 +224,10 @@ __device__ __forceinline__ uint64_t v_token_mask(int lo, int hi) {
 
 // One octet g of a uniform plane.  wv: 1 KiB of the wave's LDS (V planes: codes staged as
 // [channel][token] bytes).
-template <int BITS, bool ROT, bool SINK>
+template <int BITS, bool ROT, bool SINK, bool SYM = false>
 __device__ __forceinline__ void uniform_octet(const WavePlane& w, bool IS_V, int g, const OctetIn& in,
                                               const uint32_t* sgm, const float* ic, uint8_t* wv) {
+    static_assert(!SYM || BITS == 8, "the symmetric quantizer is 8-bit");
     const int L = lane_id(), tk = L >> 4, j = L & 15;
     const int t_lo = max(w.start, 8 * g), t_hi = min(w.end, 8 * g + 8);
     if (t_lo >= t_hi) return;
@@ -230,7 +250,10 @@ __device__ __forceinline__ void uniform_octet(const WavePlane& w, bool IS_V, int
         }
         uint32_t c[8];
         uint16_t s16, z16;
-        group_codes<BITS>(e, c, s16, z16);
+        if constexpr (SYM)
+            group_codes_sym8(e, c, s16, z16);
+        else
+            group_codes<BITS>(e, c, s16, z16);
         const int g4 = j >> 2, kb = j & 3;
         const int row = IS_V ? t : k_row(t);
         if (!IS_V && valid) {

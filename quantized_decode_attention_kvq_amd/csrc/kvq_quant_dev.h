@@ -129,6 +129,22 @@ __device__ __forceinline__ uint32_t unshuffle32(uint32_t x) {
 
 __device__ __forceinline__ int k_row(int t) { return 64 * (t / 64) + 16 * ((t % 64) % 4) + (t % 64) / 4; }
 
+// Symmetric 8-bit (q8_0-style) quantizer of the two elements a lane holds: d = fp16(max|y| / 127),
+// q = rint(y * fp32(1/d)) clamped to [-127, 127], code q + 128, zero field fp16(-128 d).
+__device__ __forceinline__ void quant_sym8(float a, float b, uint32_t& c0, uint32_t& c1, uint16_t& s16,
+                                           uint16_t& z16) {
+    float amax = fmaxf(fabsf(a), fabsf(b));
+    amax = xor_reduce<16>(amax, [](float x, float y) { return fmaxf(x, y); });
+    s16 = f16_rn(amax / 127.0f);
+    const float d = f16_val(s16);
+    z16 = f16_rn(-128.0f * d);
+    const float inv = (d > 0.0f) ? 1.0f / d : 0.0f;
+    const float u0 = fminf(fmaxf(rintf(a * inv), -127.0f), 127.0f);
+    const float u1 = fminf(fmaxf(rintf(b * inv), -127.0f), 127.0f);
+    c0 = (uint32_t)(int)(u0 + 128.0f);
+    c1 = (uint32_t)(int)(u1 + 128.0f);
+}
+
 // Uniform quantizer of the two elements a lane holds; the lane's group is lanes 16g..16g+15.
 __device__ __forceinline__ void quant_uniform(float a, float b, int bits, uint32_t& c0, uint32_t& c1,
                                               uint16_t& s16, uint16_t& z16) {
@@ -224,7 +240,10 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
             }
             uint32_t q0, q1;
             uint16_t s16, z16;
-            quant_uniform(a, c, G.bits, q0, q1, s16, z16);
+            if (G.symmetric)
+                quant_sym8(a, c, q0, q1, s16, z16);
+            else
+                quant_uniform(a, c, G.bits, q0, q1, s16, z16);
             const int g = l >> 4;
             if (tensor == 0) {
                 const int row = k_row(t);

@@ -44,7 +44,7 @@ class Case:
         self.cache = K.KvCache(device=device, **cfg)
         self.signs = W.rotation_signs(wl)[self.layers]  # [L][Hkv][2][128]
         self.S = W.qjl_projection(wl)
-        needs_signs = wl.rotate_k or wl.rotate_v or wl.k_scheme != W.UNIFORM or wl.v_scheme != W.UNIFORM
+        needs_signs = wl.rotate_k or wl.rotate_v or W.is_turbo(wl.k_scheme) or W.is_turbo(wl.v_scheme)
         if needs_signs or wl.k_scheme == W.TURBO_QJL:
             self.cache.set_random_tables(
                 torch.from_numpy(np.ascontiguousarray(self.signs)).to(device),
@@ -89,15 +89,15 @@ class Case:
         wl = self.wl
         layer = self.layers[li]
         scheme = wl.k_scheme if tensor == 0 else wl.v_scheme
-        rotate = (wl.rotate_k if tensor == 0 else wl.rotate_v) or scheme != W.UNIFORM
+        rotate = (wl.rotate_k if tensor == 0 else wl.rotate_v) or W.is_turbo(scheme)
         kw = {}
         if rotate:
             kw["signs"] = self.signs[li, head, tensor]
-        if wl.sinkhorn_iters > 0 and scheme == W.UNIFORM:
+        if wl.sinkhorn_iters > 0 and not W.is_turbo(scheme):
             X = self.calib[layer][tensor][:, head, :]
             c, inv_c = oracle.sinkhorn(X, kw.get("signs"), wl.sinkhorn_iters)
             kw["c"], kw["inv_c"] = c, inv_c
-        if scheme != W.UNIFORM:
+        if W.is_turbo(scheme):
             if mu is None:
                 _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS)
             kw["mu"], kw["theta"] = mu, theta
@@ -108,8 +108,8 @@ class Case:
         wl = self.wl
         scheme = wl.k_scheme if tensor == 0 else wl.v_scheme
         bits = wl.k_bits if tensor == 0 else wl.v_bits
-        rotate = (wl.rotate_k if tensor == 0 else wl.rotate_v) or scheme != W.UNIFORM
-        sink = wl.sinkhorn_iters > 0 and scheme == W.UNIFORM
+        rotate = (wl.rotate_k if tensor == 0 else wl.rotate_v) or W.is_turbo(scheme)
+        sink = wl.sinkhorn_iters > 0 and not W.is_turbo(scheme)
         cap = self.cache.cfg.max_context
         p = oracle.Plane(scheme, bits, rotate, sink, wl.window, tensor, cap)
         tb = tables or self.oracle_tables(li, head, tensor)

@@ -79,7 +79,8 @@ def test_progressive_3970_full():
     _decode_and_compare(case, 0, planes)
 
 
-@pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_TURBO, W.LLAMA3B_32K_TURBO_ASYM],
+@pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_TURBO, W.LLAMA3B_32K_TURBO_ASYM,
+                                W.LLAMA3B_32K_Q8_0_TURBO_V, W.DENSE27B_120K_Q8_0],
                          ids=lambda w: w.name)
 def test_prefill_equals_appends_bytewise(wl):
     _say("case: prefill == appends,", wl.name, "n=300")
@@ -103,7 +104,8 @@ RAGGED_CALLS = [(3, 21), (1, 5), (2, 3), (3, 37), (1, 16), (3, 130)]
 
 
 @pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_KVARN, W.LLAMA3B_32K_TURBO,
-                                W.LLAMA3B_32K_TURBO_ASYM, W.DENSE27B_120K_U8],
+                                W.LLAMA3B_32K_TURBO_ASYM, W.DENSE27B_120K_U8, W.DENSE27B_120K_Q8_0,
+                                W.LLAMA3B_32K_Q8_0_TURBO_V],
                          ids=lambda w: w.name)
 def test_prefill_ragged_batch_bytewise(wl):
     """Prefill calls over a batch whose sequences start at different lengths leave exactly the
@@ -129,8 +131,8 @@ def test_prefill_ragged_batch_bytewise(wl):
                 X = np.concatenate(streams[b][tensor])[:, h]
                 scheme = wl.k_scheme if tensor == 0 else wl.v_scheme
                 bits = wl.k_bits if tensor == 0 else wl.v_bits
-                rot = (wl.rotate_k if tensor == 0 else wl.rotate_v) or scheme != W.UNIFORM
-                sink = wl.sinkhorn_iters > 0 and scheme == W.UNIFORM
+                rot = (wl.rotate_k if tensor == 0 else wl.rotate_v) or W.is_turbo(scheme)
+                sink = wl.sinkhorn_iters > 0 and not W.is_turbo(scheme)
                 tb = case.oracle_tables(0, h, tensor, mu, theta)
                 pl = oracle.Plane(scheme, bits, rot, sink, wl.window, tensor, cap)
                 pl.append(X, tb)
@@ -184,7 +186,19 @@ def test_turbo_asym_u8k_msev_small():
     _decode_and_compare(case, 0, planes)
 
 
-@pytest.mark.parametrize("wl", [W.DENSE27B_120K_U8, W.DENSE27B_120K_KVARN], ids=lambda w: w.name)
+def test_q8_0_k_turbo_mse_v_small():
+    # the application rule K = Q8 (symmetric q8_0), V = TurboQuant 3-bit, appended token by token
+    wl = W.LLAMA3B_32K_Q8_0_TURBO_V
+    _say("case:", wl.name, "1 layer, 401 appends")
+    case = Case(wl, 401, layers=[2])
+    case.append_all(0)
+    torch.cuda.synchronize()
+    planes = _check_all_planes(case, 0)
+    _decode_and_compare(case, 0, planes)
+
+
+@pytest.mark.parametrize("wl", [W.DENSE27B_120K_U8, W.DENSE27B_120K_KVARN, W.DENSE27B_120K_Q8_0],
+                         ids=lambda w: w.name)
 def test_dense27b_bf16_gqa5_small(wl):
     _say("case:", wl.name, "1 layer, 2 seqs, 650 tokens")
     case = Case(wl, 650, layers=[63], batch=2)
@@ -368,7 +382,8 @@ def _planes_equal(a, b, li, batch, n_heads):
 @pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("wl,n", [(W.LLAMA3B_3970_PROGRESSIVE, 1000), (W.LLAMA3B_3970_PROGRESSIVE, 0),
                                   (W.LLAMA3B_32K_KVARN, 1023), (W.LLAMA3B_32K_TURBO, 700),
-                                  (W.LLAMA3B_32K_TURBO_ASYM, 64), (W.DENSE27B_120K_KVARN, 500)],
+                                  (W.LLAMA3B_32K_TURBO_ASYM, 64), (W.DENSE27B_120K_KVARN, 500),
+                                  (W.LLAMA3B_32K_Q8_0_TURBO_V, 130), (W.DENSE27B_120K_Q8_0, 65)],
                          ids=lambda x: x.name if hasattr(x, "name") else str(x))
 def test_fused_append_decode_equals_separate_calls(wl, n, path):
     # kvq_append_attn_decode == kvq_append + kvq_attn_decode: byte-identical planes and

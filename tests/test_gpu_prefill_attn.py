@@ -58,8 +58,8 @@ def _run(wl, n0, B, nb, ne, n_q, seed=0, workspace="auto"):
             for tensor in (0, 1):
                 scheme = wl.k_scheme if tensor == 0 else wl.v_scheme
                 bits = wl.k_bits if tensor == 0 else wl.v_bits
-                rot = (wl.rotate_k if tensor == 0 else wl.rotate_v) or scheme != W.UNIFORM
-                sink = wl.sinkhorn_iters > 0 and scheme == W.UNIFORM
+                rot = (wl.rotate_k if tensor == 0 else wl.rotate_v) or W.is_turbo(scheme)
+                sink = wl.sinkhorn_iters > 0 and not W.is_turbo(scheme)
                 tb = case.oracle_tables(0, h, tensor, mu, theta)
                 pl = oracle.Plane(scheme, bits, rot, sink, wl.window, tensor, cap)
                 pl.append(streams[b][tensor][:, h], tb)
@@ -84,7 +84,8 @@ def test_prefill_attention_kvarn(n_q):
     _run(W.LLAMA3B_32K_KVARN, n0=220, B=2, nb=1, ne=40, n_q=n_q)
 
 
-@pytest.mark.parametrize("wl", [W.DENSE27B_120K_U8, W.DENSE27B_120K_KVARN], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [W.DENSE27B_120K_U8, W.DENSE27B_120K_KVARN, W.DENSE27B_120K_Q8_0],
+                         ids=lambda w: w.name)
 def test_prefill_attention_dense27b_gqa5_bf16(wl):
     _say("case: prefill attention,", wl.name)
     _run(wl, n0=150, B=3, nb=2, ne=33, n_q=70, seed=1)

@@ -210,6 +210,87 @@ def test_quant_group_monotone_in_value():
 
 
 # ---------------------------------------------------------------------------------------------
+# symmetric 8-bit ("q8_0") group quantizer: y ~ d q, q in [-127, 127], stored as q + 128
+# ---------------------------------------------------------------------------------------------
+
+def _deq_sym(codes, d16, z16):
+    d = float(np.uint16(d16).view(np.float16))
+    z = float(np.uint16(z16).view(np.float16))
+    q = codes.astype(np.float64) - 128.0
+    return d * q, d, z
+
+
+def test_sym8_grid_points_recovered():
+    # y = d q with an fp16 d and integers q that reach |q| = 127: d and every q come back exactly,
+    # and the stored zero field makes zero + d * code equal d q
+    rng = np.random.default_rng(60)
+    for _ in range(500):
+        d = np.float16(rng.integers(1, 2000) / 1024.0) * np.float16(2.0 ** rng.integers(-6, 6))
+        q = rng.integers(-127, 128, 32)
+        q[rng.integers(32)] = 127 * rng.choice([-1, 1])
+        y = (np.float64(d) * q).astype(np.float32)
+        assert np.array_equal(y.astype(np.float64), np.float64(d) * q)
+        codes, d16, z16 = oracle.quant_group_sym8(y)
+        assert d16 == int(np.float16(d).view(np.uint16))
+        assert np.array_equal(codes.astype(np.int64) - 128, q)
+        yh, dd, z = _deq_sym(codes, d16, z16)
+        assert z == -128.0 * dd
+        assert np.array_equal(z + dd * codes.astype(np.float64), yh)
+
+
+def test_sym8_error_bound_range_and_nearest_level():
+    rng = np.random.default_rng(61)
+    for k in range(3000):
+        scale = 10.0 ** rng.uniform(-4, 3)
+        y = (rng.standard_t(4, 32) * scale).astype(np.float32)
+        codes, d16, z16 = oracle.quant_group_sym8(y)
+        assert codes.min() >= 1 and codes.max() <= 255
+        yh, d, _ = _deq_sym(codes, d16, z16)
+        # |y| <= 127 d up to the fp16 rounding of d, so every value lies within d/2 of its level
+        # (plus 127 times half an fp16 ulp of d, for the rounding of the scale)
+        ulp16 = float(np.spacing(np.float16(d)))
+        err = np.abs(y.astype(np.float64) - yh)
+        assert np.all(err <= d / 2 + 127 * ulp16 / 2 + 1e-12), (k, err.max(), d)
+        # brute force over the 255 levels, except within float rounding of a tie
+        levels = d * np.arange(-127, 128)
+        best = np.abs(y.astype(np.float64)[:, None] - levels[None, :]).argmin(1) - 127
+        frac = y.astype(np.float64) / d
+        near_tie = np.abs(np.abs(frac - np.floor(frac)) - 0.5) < 1e-5
+        clipped = np.abs(frac) > 127.5
+        assert np.all((best == codes.astype(np.int64) - 128) | near_tie | clipped)
+
+
+def test_sym8_odd_symmetry_and_zero_group():
+    rng = np.random.default_rng(62)
+    for _ in range(500):
+        y = (rng.standard_normal(32) * rng.uniform(0.01, 50)).astype(np.float32)
+        c1, d1, _ = oracle.quant_group_sym8(y)
+        c2, d2, _ = oracle.quant_group_sym8(-y)
+        assert d1 == d2
+        assert np.array_equal(c2.astype(np.int64) - 128, -(c1.astype(np.int64) - 128))
+    codes, d16, z16 = oracle.quant_group_sym8(np.zeros(32, np.float32))
+    assert d16 == 0 and np.all(codes == 128) and float(np.uint16(z16).view(np.float16)) == 0.0
+
+
+def test_q8_0_plane_dequant_and_uniform_layout():
+    # a q8_0 plane reads back through the 8-bit uniform layout: code q + 128, scale d, zero -128 d
+    rng = np.random.default_rng(63)
+    X = (rng.standard_normal((70, 128)) * 3).astype(np.float32)
+    for tensor in (oracle.TENSOR_K, oracle.TENSOR_V):
+        p = oracle.Plane(oracle.Q8_0, 8, False, False, 0, tensor, 128)
+        p.append(X, oracle.TableSet())
+        for t in range(70):
+            code, meta8, _ = p.read(t)
+            for gi in range(4):
+                c, d16, z16 = oracle.quant_group_sym8(X[t, 32 * gi:32 * gi + 32])
+                assert np.array_equal(code[32 * gi:32 * gi + 32], c)
+                assert meta8[gi] == d16 and meta8[4 + gi] == z16
+            y = p.dequant(t, oracle.TableSet())
+            d = np.array([float(np.uint16(meta8[g]).view(np.float16)) for g in range(4)]).repeat(32)
+            assert np.all(np.abs(y - X[t]) <= d / 2 + 127 * d * 2.0 ** -12 + 1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
 # plane layouts: hand-derived golden words, round trips, sizes printed on the pages
 # ---------------------------------------------------------------------------------------------
 

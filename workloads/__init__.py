@@ -19,8 +19,13 @@ from typing import Optional
 import numpy as np
 import torch
 
-UNIFORM, TURBO_QJL, TURBO_MSE = 0, 1, 2
+UNIFORM, TURBO_QJL, TURBO_MSE, Q8_0 = 0, 1, 2, 3
 D = 128
+
+
+def is_turbo(scheme: int) -> bool:
+    """TurboQuant planes (rotation implied, Lloyd-Max codes); the others use the uniform layout."""
+    return scheme in (TURBO_QJL, TURBO_MSE)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -84,9 +89,18 @@ DENSE27B_120K_KVARN = Workload(
 DENSE27B_120K_U8 = Workload(
     "dense27b-64layer-120k-b4-u8", 64, 40, 8, 4, 122880, UNIFORM, UNIFORM, 8, 8, 0,
     False, False, 0, 0, "bf16", "student_t4", 1005)
+# the KVarN post's q8_0 cache baseline on the 27B shape, and the survey page's application rule
+# (K kept at Q8, only V cut to TurboQuant 3-bit)
+DENSE27B_120K_Q8_0 = Workload(
+    "dense27b-64layer-120k-b4-q8_0", 64, 40, 8, 4, 122880, Q8_0, Q8_0, 8, 8, 0,
+    False, False, 0, 0, "bf16", "student_t4", 1005)
+LLAMA3B_32K_Q8_0_TURBO_V = Workload(
+    "llama3b-28layer-32k-q8_0-k-turbomse-v", 28, 24, 8, 1, 32768, Q8_0, TURBO_MSE, 8, 3, 0,
+    False, True, 0, 0, "f32", "outliers8x8", 1003)
 
 ALL = [LLAMA3B_3970_PROGRESSIVE, LLAMA3B_32K_KVARN, LLAMA3B_32K_TURBO, LLAMA3B_32K_TURBO_ASYM,
-       LLAMA3B_128K_PROGRESSIVE, DENSE27B_120K_KVARN, DENSE27B_120K_U8]
+       LLAMA3B_128K_PROGRESSIVE, DENSE27B_120K_KVARN, DENSE27B_120K_U8, DENSE27B_120K_Q8_0,
+       LLAMA3B_32K_Q8_0_TURBO_V]
 BY_NAME = {w.name: w for w in ALL}
 
 TAGS = {"kv": 1, "calib": 2, "q": 3, "signs": 4, "qjl": 5, "chan": 6, "step": 7}
