@@ -72,8 +72,11 @@ def lib():
         L.orc_quant_group.argtypes = [_F, ctypes.c_int, _U8, _U16, _U16]
         L.orc_quant_group_sym8.argtypes = [_F, _U8, _U16, _U16]
         L.orc_lloyd_max.argtypes = [ctypes.c_int, _Dp, _F, _F, _Dp]
+        L.orc_lloyd_max_levels.argtypes = [ctypes.c_int, ctypes.c_int, _Dp, _F, _F, _Dp]
         L.orc_turbo_encode.argtypes = [_F, ctypes.POINTER(Tables), ctypes.c_int, _F, _U8, _U16,
                                        _U16, _U8, _F]
+        L.orc_turbo_encode_bits.argtypes = [_F, ctypes.POINTER(Tables), ctypes.c_int, ctypes.c_int,
+                                            _F, _U8, _U16, _U16, _U8, _F]
         L.orc_tree_sum_sq.restype = ctypes.c_float
         L.orc_tree_sum_sq.argtypes = [_F]
         for f in ("orc_codes_bytes", "orc_meta_bytes", "orc_qjl_bytes", "orc_ring_floats"):
@@ -179,12 +182,14 @@ def quant_group_sym8(y):
     return codes, int(d16[0]), int(z16[0])
 
 
-def lloyd_max(iters=2000):
-    mu_star = np.empty(8, np.float64)
-    mu = np.empty(8, np.float32)
-    theta = np.empty(7, np.float32)
+def lloyd_max(iters=2000, levels=8):
+    """Lloyd-Max codebook of N(0,1) with `levels` (8 or 16) levels: (mu*, mu = mu*/sqrt(128) in
+    fp32, thresholds in fp32, last change of the iteration)."""
+    mu_star = np.empty(levels, np.float64)
+    mu = np.empty(levels, np.float32)
+    theta = np.empty(levels - 1, np.float32)
     ch = np.zeros(1, np.float64)
-    lib().orc_lloyd_max(iters, _p(mu_star, _Dp), _p(mu, _F), _p(theta, _F), _p(ch, _Dp))
+    lib().orc_lloyd_max_levels(levels, iters, _p(mu_star, _Dp), _p(mu, _F), _p(theta, _F), _p(ch, _Dp))
     return mu_star, mu, theta, float(ch[0])
 
 
@@ -209,17 +214,18 @@ class TableSet:
         return ctypes.byref(self.struct)
 
 
-def turbo_encode(x, tables: TableSet, with_qjl=True):
+def turbo_encode(x, tables: TableSet, with_qjl=True, bits=3):
     x = _f32(x)
     rho = np.empty(D, np.float32)
     resid = np.empty(D, np.float32)
     codes = np.empty(D, np.uint8)
-    bits = np.zeros(D, np.uint8)
+    qbits = np.zeros(D, np.uint8)
     n16 = np.zeros(1, np.uint16)
     g16 = np.zeros(1, np.uint16)
-    lib().orc_turbo_encode(_p(x, _F), tables.ref, int(with_qjl), _p(rho, _F), _p(codes, _U8),
-                           _p(n16, _U16), _p(g16, _U16), _p(bits, _U8), _p(resid, _F))
-    return dict(rho=rho, codes=codes, n16=int(n16[0]), g16=int(g16[0]), bits=bits, resid=resid)
+    lib().orc_turbo_encode_bits(_p(x, _F), tables.ref, int(bits), int(with_qjl), _p(rho, _F),
+                                _p(codes, _U8), _p(n16, _U16), _p(g16, _U16), _p(qbits, _U8),
+                                _p(resid, _F))
+    return dict(rho=rho, codes=codes, n16=int(n16[0]), g16=int(g16[0]), bits=qbits, resid=resid)
 
 
 def tree_sum_sq(v):

@@ -292,19 +292,24 @@ static double mass(double a, double b)
 }
 
 /* Lloyd's two conditions, iterated on the positive half line (the density is even, so the
- * optimal 8-level quantizer is odd-symmetric with a threshold at 0): thresholds are midpoints of
- * neighbouring centroids, centroids are conditional means (phi(a) - phi(b)) / mass(a, b). */
-void orc_lloyd_max(int iters, double* mu_star, float* mu, float* theta, double* last_change)
+ * optimal quantizer with an even number of levels is odd-symmetric with a threshold at 0):
+ * thresholds are midpoints of neighbouring centroids, centroids are conditional means
+ * (phi(a) - phi(b)) / mass(a, b).  `levels` = 8 (3-bit codes) or 16 (4-bit codes); the start is
+ * the evenly spaced half line 2 (k + 1) / (levels / 2), k = 0 .. levels/2 - 1. */
+void orc_lloyd_max_levels(int levels, int iters, double* mu_star, float* mu, float* theta,
+                          double* last_change)
 {
-    double m[4] = {0.5, 1.0, 1.5, 2.0};
+    const int h = levels / 2;
+    double m[8];
+    for (int k = 0; k < h; k++) m[k] = 2.0 * (double)(k + 1) / (double)h;
     double change = 0.0;
     for (int it = 0; it < iters; it++) {
-        double b[5];
+        double b[9];
         b[0] = 0.0;
-        for (int k = 1; k < 4; k++) b[k] = (m[k - 1] + m[k]) * 0.5;
-        b[4] = INFINITY;
+        for (int k = 1; k < h; k++) b[k] = (m[k - 1] + m[k]) * 0.5;
+        b[h] = INFINITY;
         change = 0.0;
-        for (int k = 0; k < 4; k++) {
+        for (int k = 0; k < h; k++) {
             double pb = isinf(b[k + 1]) ? 0.0 : phi(b[k + 1]);
             double nm = (phi(b[k]) - pb) / mass(b[k], b[k + 1]);
             double dlt = fabs(nm - m[k]);
@@ -313,21 +318,26 @@ void orc_lloyd_max(int iters, double* mu_star, float* mu, float* theta, double* 
         }
     }
     double r = sqrt(128.0);
-    for (int k = 0; k < 4; k++) {
-        mu_star[4 + k] = m[k];
-        mu_star[3 - k] = -m[k];
+    for (int k = 0; k < h; k++) {
+        mu_star[h + k] = m[k];
+        mu_star[h - 1 - k] = -m[k];
         float f = (float)(m[k] / r);
-        mu[4 + k] = f;
-        mu[3 - k] = -f;
+        mu[h + k] = f;
+        mu[h - 1 - k] = -f;
     }
-    theta[3] = 0.0f;
-    for (int k = 1; k < 4; k++) {
+    theta[h - 1] = 0.0f;
+    for (int k = 1; k < h; k++) {
         double t = (m[k - 1] + m[k]) * 0.5;
         float f = (float)(t / r);
-        theta[3 + k] = f;
-        theta[3 - k] = -f;
+        theta[h - 1 + k] = f;
+        theta[h - 1 - k] = -f;
     }
     if (last_change) *last_change = change;
+}
+
+void orc_lloyd_max(int iters, double* mu_star, float* mu, float* theta, double* last_change)
+{
+    orc_lloyd_max_levels(8, iters, mu_star, mu, theta, last_change);
 }
 
 /* ------------------------------------------------------------------------------------------ */
@@ -349,6 +359,14 @@ void orc_turbo_encode(const float* x, const orc_tables* tb, int with_qjl, float*
                       uint8_t* codes, uint16_t* n16o, uint16_t* g16o, uint8_t* bits,
                       float* resid_out)
 {
+    orc_turbo_encode_bits(x, tb, 3, with_qjl, rho_out, codes, n16o, g16o, bits, resid_out);
+}
+
+void orc_turbo_encode_bits(const float* x, const orc_tables* tb, int code_bits, int with_qjl,
+                           float* rho_out, uint8_t* codes, uint16_t* n16o, uint16_t* g16o,
+                           uint8_t* bits, float* resid_out)
+{
+    const int n_thr = (1 << code_bits) - 1;
     float rho[D], r[D];
     orc_rotate_f32(x, tb->signs, rho);
     float nsq = orc_tree_sum_sq(rho);
@@ -358,7 +376,7 @@ void orc_turbo_encode(const float* x, const orc_tables* tb, int with_qjl, float*
     for (int j = 0; j < D; j++) {
         float u = rho[j] * inv;
         int c = 0;
-        for (int i = 0; i < 7; i++)
+        for (int i = 0; i < n_thr; i++)
             if (u > tb->theta[i]) c++;
         codes[j] = (uint8_t)c;
         float p = n * tb->mu[c];
@@ -408,10 +426,10 @@ void orc_turbo_encode(const float* x, const orc_tables* tb, int with_qjl, float*
  * channel 32g + e.  QJL plane (TURBO_QJL): 16 B per row, word w holds the sign bits of
  * projections 32w + e as values e.  Meta per row: u16 n, u16 gamma (TURBO_QJL) or u16 n
  * (TURBO_MSE).
- * Turbo V (TURBO_MSE): blocks of 32 tokens, 1536 B each.  Token t: tau = t%32, octet o = tau/8,
- * i = tau%8; channel d: n = d%16, N = d/16.  Bit k of the code of (t, d) is in u32 word
- * 6*(16*o + n) + 2*k + N/4 of block t/32, at bit 16*(i%2) + 4*(N%4) + i/2.  Meta: u16 n per
- * token, natural order.
+ * Turbo V (TURBO_MSE, b = 3 or 4 bit planes): blocks of 32 tokens, 512*b B each.  Token t:
+ * tau = t%32, octet o = tau/8, i = tau%8; channel d: n = d%16, N = d/16.  Bit k of the code of
+ * (t, d) is in u32 word 2b*(16*o + n) + 2*k + N/4 of block t/32, at bit
+ * 16*(i%2) + 4*(N%4) + i/2.  Meta: u16 n per token, natural order.
  * Every turbo plane holds a whole number of 64-token blocks.
  * Window ring: [W][128] fp32, token t at slot t % W.
  */
@@ -425,7 +443,7 @@ static int uniform_layout(const orc_plane_cfg* pc) { return pc->scheme == ORC_UN
 
 size_t orc_codes_bytes(const orc_plane_cfg* pc)
 {
-    if (!uniform_layout(pc)) return (size_t)ceil_to(pc->capacity, 64) * 48;
+    if (!uniform_layout(pc)) return (size_t)ceil_to(pc->capacity, 64) * 16 * pc->bits; /* b bit planes */
     return (size_t)ceil_to(pc->capacity, 64) * 16 * pc->bits;
 }
 
@@ -470,10 +488,10 @@ static int get_bit(const uint8_t* p, int bit) { return (p[bit / 8] >> (bit % 8))
 static int ibit(int e) { return 16 * (e % 2) + e / 2; }
 
 /* Turbo V: byte offset of the u32 word and bit position of bit k of (token t, channel d). */
-static size_t tv_word(int t, int d, int k)
+static size_t tv_word(int t, int d, int k, int b)
 {
     int tau = t % 32, o = tau / 8, n = d % 16, N = d / 16;
-    return (size_t)(t / 32) * 1536 + 4 * (size_t)(6 * (16 * o + n) + 2 * k + N / 4);
+    return (size_t)(t / 32) * (size_t)(512 * b) + 4 * (size_t)(2 * b * (16 * o + n) + 2 * k + N / 4);
 }
 static int tv_bit(int t, int d)
 {
@@ -522,7 +540,8 @@ static void pack_token(const orc_plane_cfg* pc, int t, const uint8_t* code, cons
     }
     if (pc->tensor == ORC_TENSOR_V) {
         for (int d = 0; d < D; d++)
-            for (int k = 0; k < 3; k++) put_bit(codes + tv_word(t, d, k), tv_bit(t, d), code[d] >> k);
+            for (int k = 0; k < pc->bits; k++)
+                put_bit(codes + tv_word(t, d, k, pc->bits), tv_bit(t, d), code[d] >> k);
         put_u16(meta + (size_t)t * 2, n16);
         return;
     }
@@ -577,7 +596,7 @@ void orc_plane_read(const orc_plane_cfg* pc, const uint8_t* codes, const uint8_t
     if (pc->tensor == ORC_TENSOR_V) {
         for (int d = 0; d < D; d++) {
             int c = 0;
-            for (int k = 0; k < 3; k++) c |= get_bit(codes + tv_word(t, d, k), tv_bit(t, d)) << k;
+            for (int k = 0; k < pc->bits; k++) c |= get_bit(codes + tv_word(t, d, k, pc->bits), tv_bit(t, d)) << k;
             code[d] = (uint8_t)c;
         }
         meta8[0] = get_u16(meta + (size_t)t * 2);
@@ -626,7 +645,8 @@ void orc_plane_append(const orc_plane_cfg* pc, const orc_tables* tb, const float
                     orc_quant_group(y + GS * g, pc->bits, code + GS * g, &s16[g], &z16[g]);
             }
         } else {
-            orc_turbo_encode(x, tb, pc->scheme == ORC_TURBO_QJL, NULL, code, &n16, &g16, bits, NULL);
+            orc_turbo_encode_bits(x, tb, pc->bits, pc->scheme == ORC_TURBO_QJL, NULL, code, &n16, &g16, bits,
+                                  NULL);
         }
         pack_token(pc, t, code, s16, z16, n16, g16, bits, codes, meta, qjl);
         if (pc->window > 0) memcpy(ring + (size_t)(t % pc->window) * D, x, sizeof(float) * D);

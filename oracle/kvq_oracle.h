@@ -84,11 +84,18 @@ void orc_quant_group_sym8(const float* y, uint8_t* codes, uint16_t* d16, uint16_
 
 /* ---- Lloyd-Max codebook ---- */
 void orc_lloyd_max(int iters, double* mu_star, float* mu, float* theta, double* last_change);
+/* The same for `levels` = 8 or 16 (4-bit codes): mu[levels], theta[levels - 1]. */
+void orc_lloyd_max_levels(int levels, int iters, double* mu_star, float* mu, float* theta,
+                          double* last_change);
 
 /* ---- TurboQuant token code ---- */
 void orc_turbo_encode(const float* x, const orc_tables* tb, int with_qjl, float* rho_out,
                       uint8_t* codes, uint16_t* n16, uint16_t* g16, uint8_t* bits,
                       float* resid_out);
+/* The same with b-bit codes (b = 3: theta[7]; b = 4: theta[15] of the 16-level codebook). */
+void orc_turbo_encode_bits(const float* x, const orc_tables* tb, int code_bits, int with_qjl,
+                           float* rho_out, uint8_t* codes, uint16_t* n16o, uint16_t* g16o,
+                           uint8_t* bits, float* resid_out);
 float orc_tree_sum_sq(const float* v);
 
 /* ---- planes ---- */

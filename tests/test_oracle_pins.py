@@ -364,14 +364,15 @@ def test_layout_golden_turbo_bits():
 @pytest.mark.parametrize("scheme,bits,tensor", [
     (oracle.UNIFORM, 4, oracle.TENSOR_K), (oracle.UNIFORM, 4, oracle.TENSOR_V),
     (oracle.UNIFORM, 8, oracle.TENSOR_K), (oracle.UNIFORM, 8, oracle.TENSOR_V),
-    (oracle.TURBO_QJL, 3, oracle.TENSOR_K), (oracle.TURBO_MSE, 3, oracle.TENSOR_V)])
+    (oracle.TURBO_QJL, 3, oracle.TENSOR_K), (oracle.TURBO_MSE, 3, oracle.TENSOR_V),
+    (oracle.TURBO_MSE, 4, oracle.TENSOR_V)])
 def test_layout_round_trip_and_disjoint(scheme, bits, tensor):
     # Every token's fields read back exactly, and writing token t never disturbs another token.
     rng = np.random.default_rng(50)
     n = 150
     d = _signs(7)
     S = rng.standard_normal((128, 128)).astype(np.float32)
-    _, mu, theta, _ = oracle.lloyd_max()
+    _, mu, theta, _ = oracle.lloyd_max(levels=16 if (scheme == oracle.TURBO_MSE and bits == 4) else 8)
     tb = oracle.TableSet(signs=d, S=S, mu=mu, theta=theta)
     X = rng.standard_normal((n, 128)).astype(np.float32)
     p = oracle.Plane(scheme, bits, False, False, 0, tensor, 200)
@@ -385,7 +386,7 @@ def test_layout_round_trip_and_disjoint(scheme, bits, tensor):
                 assert np.array_equal(code[32 * gi:32 * gi + 32], c)
                 assert meta8[gi] == s16 and meta8[4 + gi] == z16
         else:
-            enc = oracle.turbo_encode(X[t], tb, scheme == oracle.TURBO_QJL)
+            enc = oracle.turbo_encode(X[t], tb, scheme == oracle.TURBO_QJL, bits=bits)
             assert np.array_equal(code, enc["codes"])
             assert meta8[0] == enc["n16"]
             if scheme == oracle.TURBO_QJL:
@@ -496,6 +497,59 @@ def test_lloyd_max_fixed_point_symmetry_and_conditions():
     assert 0.0340 < mse < 0.0350
     # fp32 tables = rounding of the fp64 fixed point scaled by 1/sqrt(128)
     assert np.array_equal(mu, (mu_star / np.sqrt(128.0)).astype(np.float32))
+
+
+def test_lloyd_max_16_levels_fixed_point_and_textbook_values():
+    # the 16-level codebook of the 4-bit TurboQuant-MSE values: converged, odd-symmetric, the
+    # centroid condition by independent integration, and the classical table (Max, 1960) of
+    # the 16-level Gaussian quantizer: outputs 0.1284 ... 2.733, distortion about 0.00950
+    mu_star, mu, theta, change = oracle.lloyd_max(oracle.LLOYD_ITERS, 16)
+    assert change < 1e-12
+    assert np.array_equal(mu_star[:8], -mu_star[::-1][:8]) and np.array_equal(mu[:8], -mu[::-1][:8])
+    assert theta[7] == 0.0 and np.array_equal(theta[:7], -theta[::-1][:7])
+    table = [0.1284, 0.3881, 0.6568, 0.9424, 1.2562, 1.6180, 2.0690, 2.7326]
+    assert np.max(np.abs(mu_star[8:] - table)) < 1.5e-4
+    phi = lambda x: np.exp(-0.5 * x * x) / np.sqrt(2 * np.pi)
+    b = [-np.inf] + [(mu_star[k] + mu_star[k + 1]) / 2 for k in range(15)] + [np.inf]
+    mse = 0.0
+    for k in range(16):
+        m0 = scipy.integrate.quad(phi, b[k], b[k + 1], epsabs=1e-14)[0]
+        m1 = scipy.integrate.quad(lambda x: x * phi(x), b[k], b[k + 1], epsabs=1e-14)[0]
+        assert abs(m1 / m0 - mu_star[k]) < 1e-9
+        mse += scipy.integrate.quad(lambda x: (x - mu_star[k]) ** 2 * phi(x), b[k], b[k + 1],
+                                    epsabs=1e-14)[0]
+    assert 0.0094 < mse < 0.0096
+    assert np.array_equal(mu, (mu_star / np.sqrt(128.0)).astype(np.float32))
+    assert np.array_equal(theta, (((mu_star[1:] + mu_star[:-1]) / 2) / np.sqrt(128.0)).astype(np.float32))
+
+
+def test_turbo_mse_4bit_nearest_centroid_and_layout():
+    # 4-bit codes are the nearest of the 16 centroids of the unit vector; the 4-plane V layout puts
+    # bit k of (token 37, channel 83) in word 8 (16 o + n) + 2 k + N / 4 = 25 + 2 k (hand-derived:
+    # tau = 5, o = 0, n = 3, N = 5) of block 1, at bit 16 (i % 2) + 4 (N % 4) + i / 2 = 22 (i = 5)
+    rng = np.random.default_rng(92)
+    _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS, 16)
+    tb = oracle.TableSet(signs=_signs(5), mu=mu, theta=theta)
+    X = rng.standard_normal((64, 128)).astype(np.float32)
+    for t in range(64):
+        e = oracle.turbo_encode(X[t], tb, False, bits=4)
+        n = float(np.uint16(e["n16"]).view(np.float16))
+        u = e["rho"].astype(np.float64) / n
+        best = np.abs(u[:, None] - mu.astype(np.float64)[None, :]).argmin(1)
+        mid = (mu[1:].astype(np.float64) + mu[:-1]) / 2
+        near = np.min(np.abs(u[:, None] - mid[None, :]), axis=1) < 1e-6
+        assert np.all((best == e["codes"]) | near)
+    pv = oracle.Plane(oracle.TURBO_MSE, 4, True, False, 0, oracle.TENSOR_V, 64)
+    pv.append(X, tb)
+    ev = oracle.turbo_encode(X[37], tb, False, bits=4)
+    blk = pv.codes[2048:4096]
+    for k in range(4):
+        assert (_word(blk, 25 + 2 * k) >> 22) & 1 == (ev["codes"][83] >> k) & 1
+    for t in (0, 37, 63):
+        code, meta8, _ = pv.read(t)
+        assert np.array_equal(code, oracle.turbo_encode(X[t], tb, False, bits=4)["codes"])
+        y = pv.dequant(t, tb)
+        assert np.linalg.norm(y - X[t]) < 0.15 * np.linalg.norm(X[t])  # 4-bit MSE quantizer
 
 
 def test_lloyd_max_agrees_with_kmeans_on_samples():
