@@ -52,7 +52,8 @@ typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 typedef enum {
     KVQ_UNIFORM = 0,   /* b-bit asymmetric groups of 32, fp16 scale + fp16 zero [P1], b = 4|8 */
     KVQ_TURBO_QJL = 1, /* K only: rotation + 3-bit Lloyd-Max code + 1-bit QJL residual [P3]  */
-    KVQ_TURBO_MSE = 2, /* rotation + 3-bit Lloyd-Max code, no residual sketch [P3]            */
+    KVQ_TURBO_MSE = 2, /* rotation + 3-bit (or, for V, 4-bit) Lloyd-Max code, no residual
+                          sketch [P3]                                                      */
     KVQ_Q8_0 = 3       /* symmetric 8-bit groups of 32, one fp16 scale d ("q8_0", [P2]'s
                           baseline; K = Q8 of [P3]'s application rules): q = rint(y / d) in
                           [-127, 127] with d = fp16(max|y| / 127); stored in the UNIFORM 8-bit
@@ -65,7 +66,8 @@ typedef struct {
     int max_batch, max_context;          /* sequences per call (<= 64); tokens per sequence
                                             ("context_length" of [P1])                       */
     int k_scheme, v_scheme;              /* kvq_scheme, chosen separately for K and V [P2]   */
-    int k_bits, v_bits;                  /* UNIFORM: 4 or 8; TURBO_*: 3; Q8_0: 8             */
+    int k_bits, v_bits;                  /* UNIFORM: 4 or 8; TURBO_QJL: 3; TURBO_MSE: 3, or 4
+                                            for V ("Turbo4", [P3] rules); Q8_0: 8           */
     int group_size;                      /* must be 32                                       */
     int fp32_window;                     /* 0 = flat, 128 = progressive [P1]                 */
     int rotate_k, rotate_v;              /* random-sign Walsh-Hadamard before coding [P2];
@@ -95,9 +97,10 @@ typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
  *      P2 with value e of Pk = bit k of the code of channel 32g+e.  QJL plane: 16 B per row,
  *      word w value e = sign bit of projection 32w+e.  Meta per row: u16 fp16 norm, u16 fp16
  *      residual norm.
- *  TURBO_MSE V: blocks of 32 tokens, 1536 B each; token t (tau = t%32, o = tau/8, i = tau%8),
- *      channel d (n = d%16, N = d/16): bit k of its code is in u32 word 6*(16o + n) + 2k + N/4
- *      of block t/32, at bit 16*(i%2) + 4*(N%4) + i/2.  Meta: u16 fp16 norm per token.
+ *  TURBO_MSE V (b = v_bits = 3 or 4 bit planes): blocks of 32 tokens, 512*b B each; token t
+ *      (tau = t%32, o = tau/8, i = tau%8), channel d (n = d%16, N = d/16): bit k of its code is
+ *      in u32 word 2b*(16o + n) + 2k + N/4 of block t/32, at bit 16*(i%2) + 4*(N%4) + i/2.
+ *      Meta: u16 fp16 norm per token.  4-bit codes index the 16-level Lloyd-Max codebook.
  *  Window ring: [fp32_window][128] fp32, token t at slot t % fp32_window.               */
 typedef struct {
     void *codes, *meta, *qjl, *window;
@@ -113,11 +116,15 @@ typedef struct {
     const float* qjl_S;  /* [128][128] QJL projection, row-major                         */
     const float* mu;     /* [8] Lloyd-Max centroids for N(0, 1/128)                      */
     const float* theta;  /* [7] Lloyd-Max decision thresholds                            */
+    const float* mu16;   /* [16] 16-level centroids (4-bit TurboQuant-MSE V), if present */
+    const float* theta16; /* [15] their thresholds                                       */
 } kvq_tables;
 
 enum {
     KVQ_OPT_SPLIT_TOKENS = 1, /* tokens per decode split (multiple of 64); 0 = automatic     */
-    KVQ_OPT_DECODE_PATH = 2   /* 0 = automatic, 1 = vector-ALU kernel, 2 = matrix-core kernel */
+    KVQ_OPT_DECODE_PATH = 2   /* 0 = automatic, 1 = vector-ALU kernel, 2 = matrix-core kernel;
+                                 4-bit TurboQuant V has the matrix-core kernel only (1 gives
+                                 KVQ_ERR_UNSUPPORTED at decode time)                      */
 };
 
 /* Bytes of device memory a cache with this configuration needs (planes for every layer,

@@ -97,6 +97,6 @@ class KvCache:
         return codes, meta, qjl, win
 
     def table(self, name, count):
-        """fp32 device view of one table (signs, c, inv_c, qjl_S, mu, theta)."""
+        """fp32 device view of one table (signs, c, inv_c, qjl_S, mu, theta, mu16, theta16)."""
         t = _kvq.kvq_get_tables(self.handle)
         return self._slice(getattr(t, name), 4 * count).view(torch.float32)

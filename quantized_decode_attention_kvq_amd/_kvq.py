@@ -48,7 +48,8 @@ class kvq_layout(ctypes.Structure):
 
 
 class kvq_tables(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("signs", "c", "inv_c", "qjl_S", "mu", "theta")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("signs", "c", "inv_c", "qjl_S", "mu", "theta", "mu16",
+                                              "theta16")]
 
 
 _lib = None

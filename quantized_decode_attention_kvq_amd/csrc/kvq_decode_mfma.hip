@@ -48,7 +48,8 @@ constexpr int kPRow = 72;                 // halves per staged P row: 64 tokens 
 constexpr int kPWave = 4 * 16 * kPRow;    // halves per wave: [group | plane][16 rows][token]
 constexpr float kKappa = 0.0097915166977774f; // sqrt(pi/2) / 128
 // cache kinds (template parameters)
-constexpr int kU4 = 0, kU8 = 1, kTb = 2; // uniform 4-bit, uniform 8-bit, TurboQuant 3-bit
+// uniform 4-bit, uniform 8-bit, TurboQuant 3-bit, TurboQuant-MSE 4-bit (V only)
+constexpr int kU4 = 0, kU8 = 1, kTb = 2, kTb4 = 3;
 
 // Eight one-bit operands from a half-interleaved word: quarter q (0..3) of each half, i.e. bits
 // 4q + v and 16 + 4q + v (v = 0..3).  Operand 2v + h is that bit times 2^(4(q%2) + v - 24).
@@ -108,18 +109,25 @@ struct VRegs<kTb> {
     uint2 w[2][3];
     uint2 nm;
 };
+template <>
+struct VRegs<kTb4> {
+    uint2 w[2][4];
+    uint2 nm;
+};
 
 template <int KT, int VT, int MB, int kNW>
 __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
-    constexpr bool KU = KT != kTb, VU = VT != kTb;
+    constexpr bool KU = KT != kTb, VU = VT == kU4 || VT == kU8, VT4 = VT == kTb4;
     constexpr int KB = KT == kU4 ? 4 : 8, VB = VT == kU4 ? 4 : 8;
+    // P staging slots per wave: 4 (uniform groups, or the 3-bit planes), 8 (the 4-bit monomials)
+    constexpr int kSlots = VT4 ? 8 : 4, kPW = kSlots * 16 * kPRow;
     __shared__ float s_q[kMaxGroupHeads][kDim];   // q' in the rotated/balanced domain, scaled
     __shared__ float s_qw[kMaxGroupHeads][kDim];  // plain q * scale * log2e (FP32 window)
     __shared__ float s_sp[KU ? 1 : kMaxGroupHeads][kDim]; // S q' (TurboQuant K)
     __shared__ float s_qsum[kMaxGroupHeads][4];
     __shared__ float s_spsum[kMaxGroupHeads];
     __shared__ float s_qfac[kMaxGroupHeads];
-    __shared__ __align__(16) _Float16 s_p[kNW * kPWave];
+    __shared__ __align__(16) _Float16 s_p[kNW * kPW];
     __shared__ float s_wm[kNW][kMaxGroupHeads], s_wl[kNW][kMaxGroupHeads];
     __shared__ float s_wz[kNW][kMaxGroupHeads][4];
 
@@ -180,7 +188,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     constexpr int kParts = kNW * 64 / kDim, kJ = kDim / kParts;
     float mu4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float st[KU ? 1 : kJ];
-    if constexpr (!KU || !VU) {
+    if constexpr (!KU || VT == kTb) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) mu4[c] = p.mu[4 + c];
     }
@@ -234,6 +242,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                     vr.vc[k][u] = *reinterpret_cast<const u4*>(c + k * 512 * VB + 16 * u);
 #pragma unroll
             for (int j = 0; j < 4; ++j) vr.vm[j] = *reinterpret_cast<const u4*>(vmeta + (t0 + 4 * lr + j) * 16);
+        } else if constexpr (VT4) {
+            const uint8_t* c = vcodes + (t0 / 32) * 2048 + 32 * l;
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) vr.w[k][u] = *reinterpret_cast<const uint2*>(c + k * 2048 + 8 * u);
+            vr.nm = *reinterpret_cast<const uint2*>(vmeta + (t0 + 4 * lr) * 2);
         } else {
             const uint8_t* c = vcodes + (t0 / 32) * 1536 + 24 * l;
 #pragma unroll
@@ -325,7 +340,28 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 
     // TurboQuant centroids as odd bit functions: mu[c] = a0 b0 + a1 b1 + a2 b2 + a3 b0 b1 b2
     float al[4] = {0.0f, 0.0f, 0.0f, 0.0f}, asum = 0.0f;
-    if constexpr (!KU || !VU) {
+    // 16-level (4-bit V) centroids: mu[c] = sum over the odd monomials of b0..b3 (b0, b1, b2, b3,
+    // b0b1b2, b0b1b3, b0b2b3, b1b2b3) of a_S prod b; the codebook's odd symmetry makes each a_S
+    // the mean of mu[c] prod_S b over the upper half c = 8 .. 15 (where b3 = 1)
+    float a16[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (VT4) {
+#pragma unroll
+        for (int c = 8; c < 16; ++c) {
+            const float m = p.mu16[c];
+            const float b0 = (c & 1) ? 1.0f : -1.0f, b1 = (c & 2) ? 1.0f : -1.0f, b2 = (c & 4) ? 1.0f : -1.0f;
+            a16[0] += m * b0;
+            a16[1] += m * b1;
+            a16[2] += m * b2;
+            a16[3] += m;
+            a16[4] += m * (b0 * b1 * b2);
+            a16[5] += m * (b0 * b1);
+            a16[6] += m * (b0 * b2);
+            a16[7] += m * (b1 * b2);
+        }
+#pragma unroll
+        for (int g = 0; g < 8; ++g) a16[g] *= 0.125f;
+    }
+    if constexpr (!KU || !(VU || VT4)) {
         const float m4 = mu4[0], m5 = mu4[1], m6 = mu4[2], m7 = mu4[3];
         al[0] = 0.25f * ((m5 - m4) + (m7 - m6));
         al[1] = 0.25f * ((m6 - m4) + (m7 - m5));
@@ -357,7 +393,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
         wl[h] = 0.0f;
     }
 
-    _Float16* my_p = s_p + wave * kPWave;
+    _Float16* my_p = s_p + wave * kPW;
 
     if (!wsplit) {
         // ---------------- A operands ----------------
@@ -536,7 +572,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = 4 * mb + lq;
-                float P[4][4]; // [g][j]
+                float P[kSlots][4]; // [g][j]
                 if constexpr (VU) {
                     const auto& vm = vr.vm;
                     constexpr float mid = (VB == 4) ? 8.0f : 128.0f; // codes enter as c - mid
@@ -561,11 +597,11 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                         const float nt = (j & 1) ? hi_h(nw) : lo_h(nw);
                         const float pn = pj[mb][j] * nt;
 #pragma unroll
-                        for (int g = 0; g < 4; ++g) P[g][j] = -pn * al[g];
+                        for (int g = 0; g < kSlots; ++g) P[g][j] = -pn * (VT4 ? a16[g] : al[g & 3]);
                     }
                 }
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
+                for (int g = 0; g < kSlots; ++g) {
                     h4 hv, lv;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -583,9 +619,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             // ---- PV over the two 32-token blocks of the chunk
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                h8 Pg[4];
+                h8 Pg[kSlots];
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
+                for (int g = 0; g < kSlots; ++g)
                     Pg[g] = *reinterpret_cast<const h8*>(my_p + (g * 16 + lr) * kPRow + 32 * k + 8 * lq);
                 if constexpr (VU) {
                     const auto& vc = vr.vc;
@@ -597,6 +633,26 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                         else
                             Bv = as_h8(centred8(vc[k][N >> 1][2 * (N & 1)], vc[k][N >> 1][2 * (N & 1) + 1]));
                         acc[N] = mfma16(Pg[N >> 1], Bv, acc[N]);
+                    }
+                } else if constexpr (VT4) {
+                    // four planes; the cubic monomials are XORs of three (b_i b_j b_k = 2 (c_i ^
+                    // c_j ^ c_k) - 1, an operand -b like the linear ones)
+                    const uint32_t w0[2] = {vr.w[k][0].x, vr.w[k][0].y};
+                    const uint32_t w1[2] = {vr.w[k][1].x, vr.w[k][1].y};
+                    const uint32_t w2[2] = {vr.w[k][2].x, vr.w[k][2].y};
+                    const uint32_t w3[2] = {vr.w[k][3].x, vr.w[k][3].y};
+#pragma unroll
+                    for (int N = 0; N < 8; ++N) {
+                        const int hN = N >> 2, q = N & 3;
+                        const uint32_t x01 = w0[hN] ^ w1[hN];
+                        acc[N] = mfma16(Pg[0], as_h8(pm1x8(w0[hN], q)), acc[N]);
+                        acc[N] = mfma16(Pg[1], as_h8(pm1x8(w1[hN], q)), acc[N]);
+                        acc[N] = mfma16(Pg[2], as_h8(pm1x8(w2[hN], q)), acc[N]);
+                        acc[N] = mfma16(Pg[3], as_h8(pm1x8(w3[hN], q)), acc[N]);
+                        acc[N] = mfma16(Pg[4], as_h8(pm1x8(x01 ^ w2[hN], q)), acc[N]);
+                        acc[N] = mfma16(Pg[5], as_h8(pm1x8(x01 ^ w3[hN], q)), acc[N]);
+                        acc[N] = mfma16(Pg[6], as_h8(pm1x8(w0[hN] ^ w2[hN] ^ w3[hN], q)), acc[N]);
+                        acc[N] = mfma16(Pg[7], as_h8(pm1x8(w1[hN] ^ w2[hN] ^ w3[hN], q)), acc[N]);
                     }
                 } else {
                     // words: [plane 0, N<4], [plane 0, N>=4], [plane 1, ...], [plane 2, ...]
@@ -745,7 +801,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 
 template <int KT, int VT, int MB>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    constexpr int NW = (MB == 1 && !(KT == kU8 && VT == kU8)) ? 8 : 4; // 8 waves where registers allow
+    // 8 waves where registers allow; the 4-bit TurboQuant V stages twice the P slots in LDS
+    constexpr int NW = (MB == 1 && !(KT == kU8 && VT == kU8) && VT != kTb4) ? 8 : 4;
     dim3 grid(p.n_splits_total, p.Hkv, p.batch);
     hipExtLaunchKernelGGL((decode_mfma_kernel<KT, VT, MB, NW>), grid, dim3(NW * 64), 0, s, ev0, ev1, 0, p);
     return hipGetLastError();
@@ -759,7 +816,7 @@ hipError_t launch_mb(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEv
 template <int KT>
 hipError_t launch_v(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const PlaneGeom& V = p.geom[1];
-    if (V.scheme != kUniform) return launch_mb<KT, kTb>(p, s, ev0, ev1);
+    if (V.scheme != kUniform) return V.bits == 4 ? launch_mb<KT, kTb4>(p, s, ev0, ev1) : launch_mb<KT, kTb>(p, s, ev0, ev1);
     return V.bits == 4 ? launch_mb<KT, kU4>(p, s, ev0, ev1) : launch_mb<KT, kU8>(p, s, ev0, ev1);
 }
 

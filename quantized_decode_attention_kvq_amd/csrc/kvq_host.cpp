@@ -27,7 +27,7 @@ struct Plan {
     PlaneGeom geom[2];
     size_t plane_bytes[2];
     size_t slot_bytes;
-    size_t off_signs, off_c, off_inv_c, off_S, off_ST, off_mu, off_theta;
+    size_t off_signs, off_c, off_inv_c, off_S, off_ST, off_mu, off_theta, off_mu16, off_theta16;
     size_t off_work, work_bytes;
     size_t off_planes, total;
 };
@@ -52,7 +52,9 @@ kvq_status check_config(const kvq_config* c) {
         const int scheme = t == 0 ? c->k_scheme : c->v_scheme, bits = t == 0 ? c->k_bits : c->v_bits;
         if (scheme == KVQ_UNIFORM && bits != 4 && bits != 8) return KVQ_ERR_UNSUPPORTED;
         if (scheme == KVQ_Q8_0 && bits != 8) return KVQ_ERR_UNSUPPORTED;
-        if ((scheme == KVQ_TURBO_QJL || scheme == KVQ_TURBO_MSE) && bits != 3) return KVQ_ERR_UNSUPPORTED;
+        if (scheme == KVQ_TURBO_QJL && bits != 3) return KVQ_ERR_UNSUPPORTED;
+        // TurboQuant-MSE: 3-bit codes, or 4-bit codes for V ("Turbo4")
+        if (scheme == KVQ_TURBO_MSE && bits != 3 && !(bits == 4 && t == 1)) return KVQ_ERR_UNSUPPORTED;
     }
     if ((c->rotate_k != 0 && c->rotate_k != 1) || (c->rotate_v != 0 && c->rotate_v != 1))
         return KVQ_ERR_INVALID_ARG;
@@ -80,7 +82,7 @@ PlaneGeom make_geom(const kvq_config* c, int tensor) {
         g.meta_bytes = rows * 16;
         g.qjl_bytes = 0;
     } else {
-        g.codes_bytes = rows * 48;
+        g.codes_bytes = rows * 16 * (size_t)g.bits; // b bit planes of 16 B per token-head
         g.meta_bytes = rows * (scheme == KVQ_TURBO_QJL ? 4 : 2);
         g.qjl_bytes = scheme == KVQ_TURBO_QJL ? rows * 16 : 0;
     }
@@ -119,6 +121,10 @@ Plan make_plan(const kvq_config* c) {
     off = align_up(off + 8 * sizeof(float));
     p.off_theta = off;
     off = align_up(off + 8 * sizeof(float));
+    p.off_mu16 = off;
+    off = align_up(off + 16 * sizeof(float));
+    p.off_theta16 = off;
+    off = align_up(off + 16 * sizeof(float));
     const size_t partial = (size_t)c->max_batch * c->n_q_heads * kMaxSplits * kPartialFloats *
                            sizeof(float);
     // Sinkhorn work: the calibration block [2][Hkv][n][128], then two [2][Hkv][128] scale rows
@@ -158,6 +164,9 @@ struct kvq_cache {
     float* ST() const { return reinterpret_cast<float*>(base + plan.off_ST); }
     float* mu() const { return reinterpret_cast<float*>(base + plan.off_mu); }
     float* theta() const { return reinterpret_cast<float*>(base + plan.off_theta); }
+    float* mu16() const { return reinterpret_cast<float*>(base + plan.off_mu16); }
+    float* theta16() const { return reinterpret_cast<float*>(base + plan.off_theta16); }
+    bool turbo4() const { return cfg.v_scheme == KVQ_TURBO_MSE && cfg.v_bits == 4; }
     char* layer_base(int layer) const {
         return base + plan.off_planes + (size_t)layer * cfg.max_batch * cfg.n_kv_heads * plan.slot_bytes;
     }
@@ -239,7 +248,8 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, 
         if (e == hipSuccess) e = launch_fill(c->inv_c(), n, 1.0f, s);
         if (e == hipSuccess) e = launch_fill(c->signs(), n, 1.0f, s);
     }
-    if (e == hipSuccess && c->turbo()) e = launch_codebook(c->mu(), c->theta(), kLloydIters, s);
+    if (e == hipSuccess && c->turbo()) e = launch_codebook(c->mu(), c->theta(), kLloydIters, 8, s);
+    if (e == hipSuccess && c->turbo4()) e = launch_codebook(c->mu16(), c->theta16(), kLloydIters, 16, s);
     if (e != hipSuccess) {
         delete c;
         return KVQ_ERR_DEVICE;
@@ -334,6 +344,8 @@ kvq_status make_quant(kvq_cache* c, int layer, const void* K, const void* V, int
     p.qjl_st = c->ST();
     p.mu = c->mu();
     p.theta = c->theta();
+    p.mu16 = c->mu16();
+    p.theta16 = c->theta16();
     p.dtype = dtype;
     p.T = n_tokens;
     p.batch = batch;
@@ -373,6 +385,7 @@ kvq_status make_decode(const kvq_cache* c, int layer, const void* q, int dtype, 
     p.cs = c->cs() + c->table_off(layer);
     p.qjl_st = c->ST();
     p.mu = c->mu();
+    p.mu16 = c->mu16();
     p.partials = reinterpret_cast<float*>(c->base + c->plan.off_work);
     p.dtype = dtype;
     p.batch = batch;
@@ -391,6 +404,7 @@ kvq_status make_decode(const kvq_cache* c, int layer, const void* q, int dtype, 
     }
     matrix = c->decode_path != 1 && mfma_path_supported(p);
     if (c->decode_path == 2 && !matrix) return KVQ_ERR_UNSUPPORTED;
+    if (!matrix && c->turbo4()) return KVQ_ERR_UNSUPPORTED; // 4-bit TurboQuant V: matrix path only
     int st;
     if (c->split_tokens_opt > 0) {
         st = c->split_tokens_opt;
@@ -617,6 +631,8 @@ kvq_status kvq_get_tables(const kvq_cache* c, kvq_tables* out) {
     out->qjl_S = c->S();
     out->mu = c->mu();
     out->theta = c->theta();
+    out->mu16 = c->mu16();
+    out->theta16 = c->theta16();
     return KVQ_OK;
 }
 

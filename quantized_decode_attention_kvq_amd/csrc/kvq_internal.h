@@ -40,6 +40,8 @@ struct QuantParams {
     const float* qjl_st;      // [128 j][128 i] = S[i][j]
     const float* mu;          // [8]
     const float* theta;       // [8], 7 used
+    const float* mu16;        // [16]: 4-bit TurboQuant-MSE V codebook
+    const float* theta16;     // [16], 15 used
     int dtype, T, batch, Hkv, window;
     int groups8;              // 8-token groups per (sequence) unit range (max over sequences)
     int start[kMaxBatch];     // length before this append, per sequence
@@ -57,6 +59,7 @@ struct DecodeParams {
     const float* cs;          // layer base [Hkv][2][128] Sinkhorn c
     const float* qjl_st;      // [128 j][128 i]
     const float* mu;
+    const float* mu16;        // [16]: 4-bit TurboQuant-MSE V codebook
     float* partials;          // [batch][Hq][n_splits_total][kPartialFloats]
     int dtype, batch, Hq, Hkv, G, window;
     float qscale;             // softmax scale * log2(e)
@@ -109,7 +112,7 @@ constexpr int kQuantBulkQjlBlocks = 256;
 // Smallest append the bulk quantizer takes.
 constexpr int kQuantBulkMinTokens = 16;
 hipError_t launch_calibrate(const CalibParams& p, hipStream_t s);
-hipError_t launch_codebook(float* mu, float* theta, int iters, hipStream_t s);
+hipError_t launch_codebook(float* mu, float* theta, int iters, int levels, hipStream_t s);
 hipError_t launch_transpose128(const float* in, float* out, hipStream_t s);
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t s);
 // The split-K launchers take optional events bound to the kernel's dispatch (measurement).

@@ -86,6 +86,31 @@ __global__ __launch_bounds__(QJL ? 1024 : 256) void quantize_turbo_bulk_kernel(Q
 // launch covers tensors tensor0 .. tensor0 + n_tensors - 1, which share that format.  Wave w of
 // workgroup x takes octets 4x + w, then every 4 * gridDim.x-th after it, of one (tensor,
 // sequence, kv head), requesting the next octet's source before quantizing the current one.
+// Bulk quantizer of a 4-bit TurboQuant-MSE V plane: the same schedule as the MSE kernel above.
+__global__ __launch_bounds__(256) void quantize_turbo4v_bulk_kernel(QuantParams p) {
+    constexpr int kW = 4, tensor = 1;
+    __shared__ __align__(16) float wl[kW][qbulk::kTurboWaveLds / 4];
+    const int b = blockIdx.z, head = blockIdx.y, wave = threadIdx.x >> 6, j = threadIdx.x & 15;
+    const qbulk::WavePlane w = qbulk::wave_plane(p, tensor, b, head);
+    uint32_t sgm[8];
+    const float* sg = p.signs[tensor] + (size_t)(head * 2 + tensor) * kDim + 8 * j;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sgm[i] = sg[i] < 0.0f ? 0x80000000u : 0u;
+    const float* th = p.theta16;
+    const qbulk::TurboTabs4 T{th[0], th[1], th[2], th[3], th[4], th[5], th[6], th[7],
+                              th[8], th[9], th[10], th[11], th[12], th[13], th[14]};
+    const int g_first = w.start / 8, step = gridDim.x * kW;
+    int u = blockIdx.x * kW + wave;
+    qbulk::OctetIn cur;
+    qbulk::load_octet(w, g_first + u, cur);
+    for (; u < p.groups8; u += step) {
+        qbulk::OctetIn nxt;
+        qbulk::load_octet(w, g_first + u + step, nxt);
+        qbulk::turbo4_v_octet(w, g_first + u, cur, sgm, T, wl[wave]);
+        cur = nxt;
+    }
+}
+
 template <int BITS, bool ROT, bool SINK, bool SYM>
 __global__ __launch_bounds__(256) void quantize_uniform_bulk_kernel(QuantParams p, int tensor0,
                                                                     int n_tensors) {
@@ -251,7 +276,8 @@ __global__ __launch_bounds__(128) void calib_cols_kernel(CalibParams p, int last
 }
 
 // ---------------------------------------------------------------------------------------------
-// Lloyd-Max 8-level quantizer of N(0,1) (positive half line, mirrored), scaled by 1/sqrt(128)
+// Lloyd-Max quantizer of N(0,1) with `levels` = 8 or 16 levels (positive half line, mirrored),
+// scaled by 1/sqrt(128); the half line starts evenly spaced at 2 (k + 1) / (levels / 2)
 // ---------------------------------------------------------------------------------------------
 
 __device__ double phi_d(double x) { return exp(-0.5 * x * x) / sqrt(2.0 * 3.14159265358979323846); }
@@ -261,35 +287,37 @@ __device__ double mass_d(double a, double b, bool b_inf) {
     return 0.5 * (erfc(a / sqrt(2.0)) - eb);
 }
 
-__global__ void codebook_kernel(float* mu, float* theta, int iters) {
+__global__ void codebook_kernel(float* mu, float* theta, int iters, int levels) {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    double m[4] = {0.5, 1.0, 1.5, 2.0};
+    const int h = levels / 2;
+    double m[8];
+    for (int k = 0; k < h; ++k) m[k] = 2.0 * (double)(k + 1) / (double)h;
     for (int it = 0; it < iters; ++it) {
-        double bnd[4];
+        double bnd[8];
         bnd[0] = 0.0;
-        for (int k = 1; k < 4; ++k) bnd[k] = (m[k - 1] + m[k]) * 0.5;
-        double nm[4];
-        for (int k = 0; k < 4; ++k) {
-            const bool last = (k == 3);
+        for (int k = 1; k < h; ++k) bnd[k] = (m[k - 1] + m[k]) * 0.5;
+        double nm[8];
+        for (int k = 0; k < h; ++k) {
+            const bool last = (k == h - 1);
             const double pb = last ? 0.0 : phi_d(bnd[k + 1]);
             nm[k] = (phi_d(bnd[k]) - pb) / mass_d(bnd[k], last ? 0.0 : bnd[k + 1], last);
         }
-        for (int k = 0; k < 4; ++k) m[k] = nm[k];
+        for (int k = 0; k < h; ++k) m[k] = nm[k];
     }
     const double r = sqrt(128.0);
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < h; ++k) {
         const float f = (float)(m[k] / r);
-        mu[4 + k] = f;
-        mu[3 - k] = -f;
+        mu[h + k] = f;
+        mu[h - 1 - k] = -f;
     }
-    theta[3] = 0.0f;
-    for (int k = 1; k < 4; ++k) {
+    theta[h - 1] = 0.0f;
+    for (int k = 1; k < h; ++k) {
         const double t = (m[k - 1] + m[k]) * 0.5;
         const float f = (float)(t / r);
-        theta[3 + k] = f;
-        theta[3 - k] = -f;
+        theta[h - 1 + k] = f;
+        theta[h - 1 - k] = -f;
     }
-    theta[7] = 0.0f;
+    theta[levels - 1] = 0.0f;
 }
 
 __global__ void fill_kernel(float* p, size_t n, float v) {
@@ -351,13 +379,23 @@ hipError_t launch_uniform_bulk_for(const PlaneGeom& G, const QuantParams& p, hip
     }
 }
 
+hipError_t launch_turbo4v_bulk(const QuantParams& p, hipStream_t s) {
+    constexpr int kW = 4;
+    const int planes = p.Hkv * p.batch;
+    const int gx = std::max(1, std::min((p.groups8 + kW - 1) / kW, (kQuantBulkBlocks + planes - 1) / planes));
+    hipLaunchKernelGGL(quantize_turbo4v_bulk_kernel, dim3(gx, p.Hkv, p.batch), dim3(kW * 64), 0, s, p);
+    return hipGetLastError();
+}
+
 // One launch for tensors tensor0 .. tensor0 + n_tensors - 1 (TurboQuant: one tensor).
 hipError_t launch_bulk_scheme(int scheme, const QuantParams& p, hipStream_t s, int tensor0,
                               int n_tensors) {
     switch (scheme) {
     case kUniform: return launch_uniform_bulk_for(p.geom[tensor0], p, s, tensor0, n_tensors);
     case kTurboQjl: return launch_turbo_bulk<true>(p, s, tensor0);
-    default: return launch_turbo_bulk<false>(p, s, tensor0);
+    default:
+        if (p.geom[tensor0].bits == 4) return launch_turbo4v_bulk(p, s); // V only
+        return launch_turbo_bulk<false>(p, s, tensor0);
     }
 }
 
@@ -387,8 +425,8 @@ hipError_t launch_calibrate(const CalibParams& p, hipStream_t s) {
     return e;
 }
 
-hipError_t launch_codebook(float* mu, float* theta, int iters, hipStream_t s) {
-    hipLaunchKernelGGL(codebook_kernel, dim3(1), dim3(64), 0, s, mu, theta, iters);
+hipError_t launch_codebook(float* mu, float* theta, int iters, int levels, hipStream_t s) {
+    hipLaunchKernelGGL(codebook_kernel, dim3(1), dim3(64), 0, s, mu, theta, iters, levels);
     return hipGetLastError();
 }
 

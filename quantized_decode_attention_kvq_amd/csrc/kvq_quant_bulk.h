@@ -543,5 +543,108 @@ __device__ __forceinline__ void turbo_octet(const WavePlane& w, bool IS_V, int g
     __builtin_amdgcn_wave_barrier();
 }
 
+// 15 thresholds of the 16-level codebook, by value (a select-of-array would index scratch).
+struct TurboTabs4 {
+    float t0, t1, t2, t3, t4, t5, t6, t7, t8, t9, t10, t11, t12, t13, t14;
+};
+
+// 4-bit Lloyd-Max code of u: the number of thresholds below u, by a binary search over the
+// ascending thresholds (bit 3 against t7, bit 2 against t3 / t11, bit 1 against t(4q + 1), bit 0
+// against t(2q), q = the code's bits found so far).
+__device__ __forceinline__ uint32_t turbo_code4(float u, const TurboTabs4 T) {
+    const bool b3 = u > T.t7;
+    const bool b2 = u > (b3 ? T.t11 : T.t3);
+    const float x1 = b3 ? (b2 ? T.t13 : T.t9) : (b2 ? T.t5 : T.t1);
+    const bool b1 = u > x1;
+    const float x0 = b3 ? (b2 ? (b1 ? T.t14 : T.t12) : (b1 ? T.t10 : T.t8))
+                        : (b2 ? (b1 ? T.t6 : T.t4) : (b1 ? T.t2 : T.t0));
+    const bool b0 = u > x0;
+    return (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+}
+
+// One octet g of a 4-bit TurboQuant-MSE V plane (four bit planes).  wl: kTurboWaveLds bytes of
+// the wave's LDS (codes staged as [token][channel] bytes).
+__device__ __forceinline__ void turbo4_v_octet(const WavePlane& w, int g, const OctetIn& in, const uint32_t* sgm,
+                                               const TurboTabs4 T, float* wl) {
+    const int L = lane_id(), tk = L >> 4, j = L & 15;
+    const int t_lo = max(w.start, 8 * g), t_hi = min(w.end, 8 * g + 8);
+    if (t_lo >= t_hi) return;
+    uint8_t* wv = reinterpret_cast<uint8_t*>(wl);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int i_tok = 4 * r + tk, t = 8 * g + i_tok;
+        const bool valid = t >= t_lo && t < t_hi;
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = in.v[r][i];
+        if (w.window > 0 && valid && t >= w.end - w.window) {
+            float4* ring = reinterpret_cast<float4*>(w.ring + (size_t)(t % w.window) * kDim + 8 * j);
+            ring[0] = make_float4(e[0], e[1], e[2], e[3]);
+            ring[1] = make_float4(e[4], e[5], e[6], e[7]);
+        }
+        rotate(e, sgm, j);
+        const uint16_t n16 = f16_rn(sqrtf(tree_sum_sq16(e)));
+        const float n = f16_val(n16);
+        const float inv = (n > 0.0f) ? 1.0f / n : 0.0f;
+        uint32_t codes_lo = 0u, codes_hi = 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t q = turbo_code4(e[i] * inv, T);
+            if (i < 4) codes_lo |= q << (8 * i);
+            else codes_hi |= q << (8 * (i - 4));
+        }
+        *reinterpret_cast<uint2*>(wv + (size_t)i_tok * kDim + 8 * j) = make_uint2(codes_lo, codes_hi);
+        if (valid && j == 0) reinterpret_cast<uint16_t*>(w.meta)[t] = n16;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // block words: bit k of channel d -> word 8 (16 o + d % 16) + 2k + (d / 16) / 4, token i at bit
+    // 16 (i % 2) + 4 ((d / 16) % 4) + i / 2.  Lane L (< 32) forms the four words of n = L % 16,
+    // h = L / 16 (channels 16 N + n, N = 4h .. 4h + 3); lanes 32 + L take channels N = 4h + 2,
+    // 4h + 3 of the same words, merged by the lane 32 apart.
+    const int n = L & 15, h = (L >> 4) & 1, half = L >> 5;
+    uint32_t wk0 = 0u, wk1 = 0u, wk2 = 0u, wk3 = 0u;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int Nl = 2 * half + c; // N % 4
+        const int d = 16 * (4 * h + Nl) + n;
+        uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo |= (uint32_t)wv[i * kDim + d] << (8 * i);
+            hi |= (uint32_t)wv[(i + 4) * kDim + d] << (8 * i);
+        }
+        const uint32_t ev = __builtin_amdgcn_perm(hi, lo, 0x06040200u); // tokens 0, 2, 4, 6
+        const uint32_t od = __builtin_amdgcn_perm(hi, lo, 0x07050301u); // tokens 1, 3, 5, 7
+        wk0 |= (byte_bits(ev, 0) | (byte_bits(od, 0) << 16)) << (4 * Nl);
+        wk1 |= (byte_bits(ev, 1) | (byte_bits(od, 1) << 16)) << (4 * Nl);
+        wk2 |= (byte_bits(ev, 2) | (byte_bits(od, 2) << 16)) << (4 * Nl);
+        wk3 |= (byte_bits(ev, 3) | (byte_bits(od, 3) << 16)) << (4 * Nl);
+    }
+    wk0 |= xor_lane<32>(wk0);
+    wk1 |= xor_lane<32>(wk1);
+    wk2 |= xor_lane<32>(wk2);
+    wk3 |= xor_lane<32>(wk3);
+    __builtin_amdgcn_wave_barrier();
+    if (half == 0) {
+        const int o = g & 3;
+        uint32_t* blk = reinterpret_cast<uint32_t*>(w.codes + (size_t)(g >> 2) * 2048) + 8 * (16 * o + n) + h;
+        if (t_hi - t_lo == 8) {
+            blk[0] = wk0;
+            blk[2] = wk1;
+            blk[4] = wk2;
+            blk[6] = wk3;
+        } else {
+            // token bits of the octet present in this append
+            uint32_t m = 0u;
+            for (int i = t_lo - 8 * g; i < t_hi - 8 * g; ++i) m |= 0x1111u << (16 * (i & 1) + (i >> 1));
+            blk[0] = (blk[0] & ~m) | (wk0 & m);
+            blk[2] = (blk[2] & ~m) | (wk1 & m);
+            blk[4] = (blk[4] & ~m) | (wk2 & m);
+            blk[6] = (blk[6] & ~m) | (wk3 & m);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
 } // namespace qbulk
 } // namespace kvq

@@ -195,8 +195,9 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
 
     // V uniform accumulators for the group's packed words (channels 2l and 2l+1).
     uint64_t vacc0 = 0, vacc1 = 0, vmask = 0;
-    // V turbo bit-plane words of channels 2l and 2l+1 for this octet, and the bits written.
-    uint32_t tv_a[3] = {0u, 0u, 0u}, tv_c[3] = {0u, 0u, 0u}, tv_mask = 0u;
+    // V turbo bit-plane words (3 or 4 planes) of channels 2l and 2l+1 for this octet, and the
+    // bits written.
+    uint32_t tv_a[4] = {0u, 0u, 0u, 0u}, tv_c[4] = {0u, 0u, 0u, 0u}, tv_mask = 0u;
 
     // all of the octet's source values are requested before the first is used, so a wave pays
     // one memory round trip instead of one per token
@@ -283,13 +284,24 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
             const float inv = (n > 0.0f) ? 1.0f / n : 0.0f;
             const float ua = a * inv, uc = c * inv;
             uint32_t qa = 0, qc = 0;
+            if (G.bits == 4) {
+                // 4-bit TurboQuant-MSE V: the 16-level codebook
 #pragma unroll
-            for (int k = 0; k < 7; ++k) {
-                const float th = p.theta[k];
-                qa += (ua > th) ? 1u : 0u;
-                qc += (uc > th) ? 1u : 0u;
+                for (int k = 0; k < 15; ++k) {
+                    const float th = p.theta16[k];
+                    qa += (ua > th) ? 1u : 0u;
+                    qc += (uc > th) ? 1u : 0u;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 7; ++k) {
+                    const float th = p.theta[k];
+                    qa += (ua > th) ? 1u : 0u;
+                    qc += (uc > th) ? 1u : 0u;
+                }
             }
-            const float pa = n * p.mu[qa], pc = n * p.mu[qc];
+            const float* mu = (G.bits == 4) ? p.mu16 : p.mu;
+            const float pa = n * mu[qa], pc = n * mu[qc];
             const float ra = a - pa, rc = c - pc;
             if (tensor == 0) {
                 // K row: bit planes of group g (lanes 16g..16g+15 hold its channels 2lg, 2lg+1,
@@ -334,12 +346,13 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
                     reinterpret_cast<uint16_t*>(meta)[row] = n16;
                 }
             } else {
-                // V block: bit k of channel 2l (2l+1) goes to word 6(16 o + n) + 2k + N/4 with
-                // n = 2(l%8) (+1), N = l/8; token i of the octet at bit 16(i%2) + 4(N%4) + i/2
+                // V block (b = G.bits planes): bit k of channel 2l (2l+1) goes to word
+                // 2b(16 o + n) + 2k + N/4 with n = 2(l%8) (+1), N = l/8; token i of the octet at
+                // bit 16(i%2) + 4(N%4) + i/2
                 const int i = t % 8, N = l >> 3;
                 const uint32_t pos = 1u << (16 * (i & 1) + 4 * (N & 3) + (i >> 1));
 #pragma unroll
-                for (int k = 0; k < 3; ++k) {
+                for (int k = 0; k < 4; ++k) {
                     tv_a[k] |= ((qa >> k) & 1u) ? pos : 0u;
                     tv_c[k] |= ((qc >> k) & 1u) ? pos : 0u;
                 }
@@ -356,19 +369,21 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
         m |= xor_lane<8>(m);
         m |= xor_lane<16>(m);
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
+        for (int k = 0; k < 4; ++k) {
             tv_a[k] |= xor_lane<8>(tv_a[k]);
             tv_a[k] |= xor_lane<16>(tv_a[k]);
             tv_c[k] |= xor_lane<8>(tv_c[k]);
             tv_c[k] |= xor_lane<16>(tv_c[k]);
         }
         if (((l >> 3) & 3) == 0) {
+            const int b = G.bits; // bit planes
             const int o = (t_lo % 32) / 8, n0 = 2 * (l & 7), N = l >> 3;
-            uint32_t* blk = reinterpret_cast<uint32_t*>(codes + (size_t)(t_lo / 32) * 1536);
+            uint32_t* blk = reinterpret_cast<uint32_t*>(codes + (size_t)(t_lo / 32) * (512 * b));
 #pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                uint32_t* wa = blk + 6 * (16 * o + n0) + 2 * k + (N >> 2);
-                uint32_t* wc = wa + 6;
+            for (int k = 0; k < 4; ++k) { // register indexes stay compile-time; planes k < b
+                if (k >= b) break;
+                uint32_t* wa = blk + 2 * b * (16 * o + n0) + 2 * k + (N >> 2);
+                uint32_t* wc = wa + 2 * b;
                 *wa = (*wa & ~m) | tv_a[k];
                 *wc = (*wc & ~m) | tv_c[k];
             }

@@ -98,7 +98,10 @@ class Case:
             c, inv_c = oracle.sinkhorn(X, kw.get("signs"), wl.sinkhorn_iters)
             kw["c"], kw["inv_c"] = c, inv_c
         if W.is_turbo(scheme):
-            if mu is None:
+            bits = wl.k_bits if tensor == 0 else wl.v_bits
+            if bits == 4:  # 4-bit TurboQuant-MSE V: the 16-level codebook
+                _, mu, theta, _ = _codebook16()
+            elif mu is None:
                 _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS)
             kw["mu"], kw["theta"] = mu, theta
             kw["S"] = self.S
@@ -131,6 +134,16 @@ def compare_plane(dev, orc: oracle.Plane, label=""):
     if win is not None:
         w = win.view(np.float32)
         assert np.array_equal(w.view(np.uint32), orc.ring.view(np.uint32)), f"{label}: window differs"
+
+
+_CB16 = None
+
+
+def _codebook16():
+    global _CB16
+    if _CB16 is None:
+        _CB16 = oracle.lloyd_max(oracle.LLOYD_ITERS, 16)
+    return _CB16
 
 
 def oracle_attention_case(case: Case, li, b, q_np, n=None, planes=None):

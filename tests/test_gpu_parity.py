@@ -36,6 +36,8 @@ def _check_all_planes(case, li, heads=None, seqs=None):
 
 
 def _paths(wl):
+    if wl.v_scheme == W.TURBO_MSE and wl.v_bits == 4:
+        return (2,)  # 4-bit TurboQuant V: matrix-core kernel only
     return (1, 2)  # vector-ALU kernel, matrix-core kernel
 
 
@@ -80,7 +82,7 @@ def test_progressive_3970_full():
 
 
 @pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_TURBO, W.LLAMA3B_32K_TURBO_ASYM,
-                                W.LLAMA3B_32K_Q8_0_TURBO_V, W.DENSE27B_120K_Q8_0],
+                                W.LLAMA3B_32K_Q8_0_TURBO_V, W.DENSE27B_120K_Q8_0, W.LLAMA3B_32K_Q8_0_TURBO4_V],
                          ids=lambda w: w.name)
 def test_prefill_equals_appends_bytewise(wl):
     _say("case: prefill == appends,", wl.name, "n=300")
@@ -105,7 +107,7 @@ RAGGED_CALLS = [(3, 21), (1, 5), (2, 3), (3, 37), (1, 16), (3, 130)]
 
 @pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_KVARN, W.LLAMA3B_32K_TURBO,
                                 W.LLAMA3B_32K_TURBO_ASYM, W.DENSE27B_120K_U8, W.DENSE27B_120K_Q8_0,
-                                W.LLAMA3B_32K_Q8_0_TURBO_V],
+                                W.LLAMA3B_32K_Q8_0_TURBO_V, W.LLAMA3B_32K_Q8_0_TURBO4_V],
                          ids=lambda w: w.name)
 def test_prefill_ragged_batch_bytewise(wl):
     """Prefill calls over a batch whose sequences start at different lengths leave exactly the
@@ -184,6 +186,31 @@ def test_turbo_asym_u8k_msev_small():
     torch.cuda.synchronize()
     planes = _check_all_planes(case, 0)
     _decode_and_compare(case, 0, planes)
+
+
+def test_q8_0_k_turbo4_mse_v_small():
+    # the application rule K = Q8, V = TurboQuant 4-bit: the device's 16-level codebook equals the
+    # oracle's bit for bit, the planes byte for byte (appends and a bulk prefill), and attention
+    wl = W.LLAMA3B_32K_Q8_0_TURBO4_V
+    _say("case:", wl.name, "1 layer, 300 prefill + 40 appends")
+    case = Case(wl, 340, layers=[1])
+    k, v = case.kv(1)
+    case.cache.prefill_quantize(0, k[:, :300].contiguous(), v[:, :300].contiguous())
+    for t in range(300, 340):
+        case.cache.append(0, k[:, t].contiguous(), v[:, t].contiguous())
+    torch.cuda.synchronize()
+    _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS, 16)
+    assert np.array_equal(case.cache.table("mu16", 16).cpu().numpy().view(np.uint32), mu.view(np.uint32))
+    assert np.array_equal(case.cache.table("theta16", 15).cpu().numpy().view(np.uint32), theta.view(np.uint32))
+    planes = _check_all_planes(case, 0)
+    _decode_and_compare(case, 0, planes)
+    case.cache.set_option(2, 1)
+    q = W.gen_q(wl, 1, 0).to("cuda")
+    out = torch.zeros((1, wl.n_q_heads, 128), device="cuda")
+    with pytest.raises(case.K.KvqError) as e:
+        case.cache.attn_decode(0, q, out)
+    assert e.value.name == "KVQ_ERR_UNSUPPORTED"
+    case.cache.set_option(2, 0)
 
 
 def test_q8_0_k_turbo_mse_v_small():
@@ -383,11 +410,14 @@ def _planes_equal(a, b, li, batch, n_heads):
 @pytest.mark.parametrize("wl,n", [(W.LLAMA3B_3970_PROGRESSIVE, 1000), (W.LLAMA3B_3970_PROGRESSIVE, 0),
                                   (W.LLAMA3B_32K_KVARN, 1023), (W.LLAMA3B_32K_TURBO, 700),
                                   (W.LLAMA3B_32K_TURBO_ASYM, 64), (W.DENSE27B_120K_KVARN, 500),
-                                  (W.LLAMA3B_32K_Q8_0_TURBO_V, 130), (W.DENSE27B_120K_Q8_0, 65)],
+                                  (W.LLAMA3B_32K_Q8_0_TURBO_V, 130), (W.DENSE27B_120K_Q8_0, 65),
+                                  (W.LLAMA3B_32K_Q8_0_TURBO4_V, 200)],
                          ids=lambda x: x.name if hasattr(x, "name") else str(x))
 def test_fused_append_decode_equals_separate_calls(wl, n, path):
     # kvq_append_attn_decode == kvq_append + kvq_attn_decode: byte-identical planes and
     # bit-identical outputs over consecutive steps, with ragged lengths in the batch
+    if path not in _paths(wl):
+        pytest.skip("this cache has the matrix-core decode kernel only")
     _say("case: fused append+decode", wl.name, "n", n, "path", path)
     B = 2
     a = Case(wl, max(n, 1), layers=[0], batch=B, extra_tokens=8)

@@ -97,10 +97,13 @@ DENSE27B_120K_Q8_0 = Workload(
 LLAMA3B_32K_Q8_0_TURBO_V = Workload(
     "llama3b-28layer-32k-q8_0-k-turbomse-v", 28, 24, 8, 1, 32768, Q8_0, TURBO_MSE, 8, 3, 0,
     False, True, 0, 0, "f32", "outliers8x8", 1003)
+LLAMA3B_32K_Q8_0_TURBO4_V = Workload(
+    "llama3b-28layer-32k-q8_0-k-turbo4mse-v", 28, 24, 8, 1, 32768, Q8_0, TURBO_MSE, 8, 4, 0,
+    False, True, 0, 0, "f32", "outliers8x8", 1003)
 
 ALL = [LLAMA3B_3970_PROGRESSIVE, LLAMA3B_32K_KVARN, LLAMA3B_32K_TURBO, LLAMA3B_32K_TURBO_ASYM,
        LLAMA3B_128K_PROGRESSIVE, DENSE27B_120K_KVARN, DENSE27B_120K_U8, DENSE27B_120K_Q8_0,
-       LLAMA3B_32K_Q8_0_TURBO_V]
+       LLAMA3B_32K_Q8_0_TURBO_V, LLAMA3B_32K_Q8_0_TURBO4_V]
 BY_NAME = {w.name: w for w in ALL}
 
 TAGS = {"kv": 1, "calib": 2, "q": 3, "signs": 4, "qjl": 5, "chan": 6, "step": 7}
