@@ -37,7 +37,7 @@ def token_head_bytes(scheme, bits):
         return 16 * bits + 16
     if scheme == W.TURBO_QJL:
         return 48 + 4 + 16
-    return 48 + 2
+    return 16 * bits + 2  # TurboQuant-MSE: b bit planes + fp16 norm
 
 
 def query_bytes(wl: W.Workload, n: int) -> int:
@@ -116,7 +116,7 @@ def prefill_report(wl: W.Workload, prefill_s):
 
 def split_kernel_name(wl: W.Workload) -> str:
     """The split-K decode kernel the library launches for this cache (matrix-core path)."""
-    kind = lambda scheme, bits: "Tb" if W.is_turbo(scheme) else f"U{bits}"  # noqa: E731
+    kind = lambda scheme, bits: ("Tb4" if bits == 4 else "Tb") if W.is_turbo(scheme) else f"U{bits}"  # noqa: E731
     return (f"decode_mfma_kernel (K {kind(wl.k_scheme, wl.k_bits)}, V {kind(wl.v_scheme, wl.v_bits)}, "
             f"{wl.group} query heads per kv head)")
 
