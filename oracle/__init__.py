@@ -6,7 +6,9 @@ and the two share no code.
 
 Parity notes: every function here is pinned by ``tests/test_oracle_pins.py`` except the
 Sinkhorn calibration's agreement with KVarN itself (the pages give no values), which is
-"parity unpinned" beyond the invariants tested there.
+"parity unpinned" beyond the invariants tested there.  The outlier split (TURBO_SPLIT) is pinned
+by the 64-point Sylvester matrix, brute-force outlier ranking with ties, nearest-centroid codes,
+the textbook 4-level codebook and distortions, and hand-derived layout words.
 """
 from __future__ import annotations
 
@@ -20,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "kvq_oracle.c")
 LIB = os.path.join(HERE, "libkvq_oracle.so")
 
-UNIFORM, TURBO_QJL, TURBO_MSE, Q8_0 = 0, 1, 2, 3
+UNIFORM, TURBO_QJL, TURBO_MSE, Q8_0, TURBO_SPLIT = 0, 1, 2, 3, 4
 TENSOR_K, TENSOR_V = 0, 1
 D = 128
 
@@ -43,7 +45,8 @@ class PlaneCfg(ctypes.Structure):
 
 class Tables(ctypes.Structure):
     _fields_ = [(n, ctypes.POINTER(ctypes.c_float)) for n in
-                ("signs", "c", "inv_c", "S", "mu", "theta")]
+                ("signs", "c", "inv_c", "S", "mu", "theta", "mu2", "theta2")] + \
+               [("perm", ctypes.POINTER(ctypes.c_int))]
 
 
 _lib = None
@@ -51,6 +54,7 @@ _F = ctypes.POINTER(ctypes.c_float)
 _Dp = ctypes.POINTER(ctypes.c_double)
 _U8 = ctypes.POINTER(ctypes.c_uint8)
 _U16 = ctypes.POINTER(ctypes.c_uint16)
+_I32 = ctypes.POINTER(ctypes.c_int)
 
 
 def lib():
@@ -79,6 +83,13 @@ def lib():
                                             _F, _U8, _U16, _U16, _U8, _F]
         L.orc_tree_sum_sq.restype = ctypes.c_float
         L.orc_tree_sum_sq.argtypes = [_F]
+        L.orc_lloyd_max_dim.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _Dp, _F, _F, _Dp]
+        L.orc_rotate64_f32.argtypes = [_F, _F, _F]
+        L.orc_unrotate64_f64.argtypes = [_Dp, _F, _Dp]
+        L.orc_tree_sum_sq64.restype = ctypes.c_float
+        L.orc_tree_sum_sq64.argtypes = [_F]
+        L.orc_select_outliers.argtypes = [_F, ctypes.c_int, _I32]
+        L.orc_split_encode.argtypes = [_F, ctypes.POINTER(Tables), ctypes.c_int, _U8, _U16]
         for f in ("orc_codes_bytes", "orc_meta_bytes", "orc_qjl_bytes", "orc_ring_floats"):
             getattr(L, f).restype = ctypes.c_size_t
             getattr(L, f).argtypes = [ctypes.POINTER(PlaneCfg)]
@@ -182,15 +193,52 @@ def quant_group_sym8(y):
     return codes, int(d16[0]), int(z16[0])
 
 
-def lloyd_max(iters=2000, levels=8):
-    """Lloyd-Max codebook of N(0,1) with `levels` (8 or 16) levels: (mu*, mu = mu*/sqrt(128) in
+def lloyd_max(iters=2000, levels=8, dim=128):
+    """Lloyd-Max codebook of N(0,1) with `levels` (4, 8 or 16) levels: (mu*, mu = mu*/sqrt(dim) in
     fp32, thresholds in fp32, last change of the iteration)."""
     mu_star = np.empty(levels, np.float64)
     mu = np.empty(levels, np.float32)
     theta = np.empty(levels - 1, np.float32)
     ch = np.zeros(1, np.float64)
-    lib().orc_lloyd_max_levels(levels, iters, _p(mu_star, _Dp), _p(mu, _F), _p(theta, _F), _p(ch, _Dp))
+    lib().orc_lloyd_max_dim(levels, dim, iters, _p(mu_star, _Dp), _p(mu, _F), _p(theta, _F), _p(ch, _Dp))
     return mu_star, mu, theta, float(ch[0])
+
+
+def rotate64_f32(x, signs):
+    x, s = _f32(x), _f32(signs)
+    y = np.empty(64, np.float32)
+    lib().orc_rotate64_f32(_p(x, _F), _p(s, _F), _p(y, _F))
+    return y
+
+
+def unrotate64_f64(y, signs):
+    y, s = np.ascontiguousarray(y, np.float64), _f32(signs)
+    x = np.empty(64, np.float64)
+    lib().orc_unrotate64_f64(_p(y, _Dp), _p(s, _F), _p(x, _Dp))
+    return x
+
+
+def tree_sum_sq64(v):
+    v = _f32(v)
+    return float(lib().orc_tree_sum_sq64(_p(v, _F)))
+
+
+def select_outliers(X):
+    """Outlier split permutation of calibration tokens X [n][128]: the 64 channels of largest
+    energy ascending, then the other 64 ascending (int32 [128])."""
+    X = _f32(X).reshape(-1, D)
+    perm = np.empty(D, np.int32)
+    lib().orc_select_outliers(_p(X, _F), X.shape[0], _p(perm, _I32))
+    return perm
+
+
+def split_encode(x, tables: "TableSet", bits_o):
+    """Split token code: (codes by position [128], (n_outlier, n_rest) fp16 bits)."""
+    x = _f32(x)
+    codes = np.empty(D, np.uint8)
+    n16 = np.zeros(2, np.uint16)
+    lib().orc_split_encode(_p(x, _F), tables.ref, int(bits_o), _p(codes, _U8), _p(n16, _U16))
+    return codes, (int(n16[0]), int(n16[1]))
 
 
 LLOYD_ITERS = 2000  # fixed iteration count of the codebook (same count on the device side)
@@ -199,15 +247,21 @@ LLOYD_ITERS = 2000  # fixed iteration count of the codebook (same count on the d
 class TableSet:
     """Keeps numpy arrays alive behind an orc_tables struct."""
 
-    def __init__(self, signs=None, c=None, inv_c=None, S=None, mu=None, theta=None):
+    def __init__(self, signs=None, c=None, inv_c=None, S=None, mu=None, theta=None, mu2=None,
+                 theta2=None, perm=None):
         self.arrays = {}
         self.struct = Tables()
         for name, val in (("signs", signs), ("c", c), ("inv_c", inv_c), ("S", S), ("mu", mu),
-                          ("theta", theta)):
+                          ("theta", theta), ("mu2", mu2), ("theta2", theta2)):
             if val is not None:
                 a = _f32(val).ravel()
                 self.arrays[name] = a
                 setattr(self.struct, name, _p(a, _F))
+        if perm is not None:
+            a = np.ascontiguousarray(perm, np.int32).ravel()
+            assert a.size == D and np.array_equal(np.sort(a), np.arange(D)), "perm must permute 0..127"
+            self.arrays["perm"] = a
+            self.struct.perm = _p(a, _I32)
 
     @property
     def ref(self):
@@ -241,7 +295,7 @@ class Plane:
     """One (layer, sequence, kv head, tensor) plane: code bytes, meta bytes, QJL bytes, ring."""
 
     def __init__(self, scheme, bits, rotate, sinkhorn, window, tensor, capacity):
-        self.cfg = PlaneCfg(scheme, bits, int(rotate or scheme in (TURBO_QJL, TURBO_MSE)), int(sinkhorn), window,
+        self.cfg = PlaneCfg(scheme, bits, int(rotate or scheme in (TURBO_QJL, TURBO_MSE, TURBO_SPLIT)), int(sinkhorn), window,
                             tensor, capacity)
         L = lib()
         r = ctypes.byref(self.cfg)

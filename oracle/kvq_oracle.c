@@ -294,10 +294,12 @@ static double mass(double a, double b)
 /* Lloyd's two conditions, iterated on the positive half line (the density is even, so the
  * optimal quantizer with an even number of levels is odd-symmetric with a threshold at 0):
  * thresholds are midpoints of neighbouring centroids, centroids are conditional means
- * (phi(a) - phi(b)) / mass(a, b).  `levels` = 8 (3-bit codes) or 16 (4-bit codes); the start is
- * the evenly spaced half line 2 (k + 1) / (levels / 2), k = 0 .. levels/2 - 1. */
-void orc_lloyd_max_levels(int levels, int iters, double* mu_star, float* mu, float* theta,
-                          double* last_change)
+ * (phi(a) - phi(b)) / mass(a, b).  `levels` = 4, 8 or 16 (2-, 3-, 4-bit codes); the start is
+ * the evenly spaced half line 2 (k + 1) / (levels / 2), k = 0 .. levels/2 - 1.  A coordinate of a
+ * random rotation of a unit vector in `dim` dimensions is close to N(0, 1/dim), so the stored
+ * centroids and thresholds are the N(0,1) ones divided by sqrt(dim). */
+void orc_lloyd_max_dim(int levels, int dim, int iters, double* mu_star, float* mu, float* theta,
+                       double* last_change)
 {
     const int h = levels / 2;
     double m[8];
@@ -317,7 +319,7 @@ void orc_lloyd_max_levels(int levels, int iters, double* mu_star, float* mu, flo
             m[k] = nm;
         }
     }
-    double r = sqrt(128.0);
+    double r = sqrt((double)dim);
     for (int k = 0; k < h; k++) {
         mu_star[h + k] = m[k];
         mu_star[h - 1 - k] = -m[k];
@@ -333,6 +335,12 @@ void orc_lloyd_max_levels(int levels, int iters, double* mu_star, float* mu, flo
         theta[h - 1 - k] = -f;
     }
     if (last_change) *last_change = change;
+}
+
+void orc_lloyd_max_levels(int levels, int iters, double* mu_star, float* mu, float* theta,
+                          double* last_change)
+{
+    orc_lloyd_max_dim(levels, 128, iters, mu_star, mu, theta, last_change);
 }
 
 void orc_lloyd_max(int iters, double* mu_star, float* mu, float* theta, double* last_change)
@@ -400,6 +408,112 @@ void orc_turbo_encode_bits(const float* x, const orc_tables* tb, int code_bits, 
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* outlier-channel split: fractional bit widths (reading R19)                                  */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * TurboQuant reaches 2.5 and 3.5 bits per channel by splitting the channels into an outlier set
+ * and the rest and running two independent instances of its quantizer, the outliers with one bit
+ * more.  Reading R19 fixes the open parts: 64 outlier channels (the split that gives exactly
+ * 2.5 = (64*3 + 64*2)/128 and 3.5 = (64*4 + 64*3)/128), chosen per (layer, kv head) from the
+ * calibration tokens by energy; each subset is rotated by its own 64-point random-sign
+ * Walsh-Hadamard transform, carries its own fp16 norm and is coded with the Lloyd-Max codebook
+ * of N(0, 1/64).
+ */
+
+/* Butterflies of span h = 1, 2, ..., 32 in that order, then one binary32 multiply by 1/8. */
+void orc_rotate64_f32(const float* x, const float* signs, float* y)
+{
+    float t[64];
+    for (int j = 0; j < 64; j++) t[j] = (signs[j] < 0.0f) ? -x[j] : x[j];
+    for (int h = 1; h < 64; h <<= 1)
+        for (int i = 0; i < 64; i++)
+            if (!(i & h)) {
+                float a = t[i], b = t[i + h];
+                t[i] = a + b;
+                t[i + h] = a - b;
+            }
+    for (int j = 0; j < 64; j++) y[j] = t[j] * 0.125f;
+}
+
+/* Inverse: H64 H64 = 64 I, so R^-1 y = d .* (H64 y) / 8. */
+void orc_unrotate64_f64(const double* y, const float* signs, double* x)
+{
+    double t[64];
+    for (int j = 0; j < 64; j++) t[j] = y[j];
+    for (int h = 1; h < 64; h <<= 1)
+        for (int i = 0; i < 64; i++)
+            if (!(i & h)) {
+                double a = t[i], b = t[i + h];
+                t[i] = a + b;
+                t[i + h] = a - b;
+            }
+    for (int j = 0; j < 64; j++) x[j] = (double)signs[j] * (t[j] / 8.0);
+}
+
+/* Pairwise index-order sum of squares over 64 values (the 128-value tree cut to one half). */
+float orc_tree_sum_sq64(const float* v)
+{
+    float t[64];
+    for (int j = 0; j < 64; j++) t[j] = v[j] * v[j];
+    for (int w = 32; w >= 1; w >>= 1)
+        for (int i = 0; i < w; i++) t[i] = t[2 * i] + t[2 * i + 1];
+    return t[0];
+}
+
+/* Energy of channel d = sum over the n tokens, in token order, of x[t][d]^2; a binary32 square
+ * is exact in binary64, so only the running sum rounds.  The 64 channels of largest energy are
+ * the outliers; of two channels with equal energy the one with the smaller index ranks first. */
+void orc_select_outliers(const float* X, int n, int* perm)
+{
+    double e[D];
+    int out[D];
+    for (int d = 0; d < D; d++) {
+        double acc = 0.0;
+        for (int t = 0; t < n; t++) {
+            double v = (double)X[(size_t)t * D + d];
+            acc += v * v;
+        }
+        e[d] = acc;
+    }
+    for (int d = 0; d < D; d++) {
+        int rank = 0;
+        for (int i = 0; i < D; i++)
+            if (e[i] > e[d] || (e[i] == e[d] && i < d)) rank++;
+        out[d] = rank < D / 2;
+    }
+    int k = 0;
+    for (int d = 0; d < D; d++)
+        if (out[d]) perm[k++] = d;
+    for (int d = 0; d < D; d++)
+        if (!out[d]) perm[k++] = d;
+}
+
+/* Each subset h (positions 64h .. 64h+63, channels perm[.]): rho = R64(x_h) with signs
+ * 64h .. 64h+63 of the tensor's sign vector; n_h = fp16(|rho|); code = number of thresholds of
+ * the subset's codebook below rho / n_h (outliers: bits_o bits, the rest bits_o - 1). */
+void orc_split_encode(const float* x, const orc_tables* tb, int bits_o, uint8_t* codes, uint16_t* n16)
+{
+    for (int h = 0; h < 2; h++) {
+        float z[64], rho[64];
+        for (int j = 0; j < 64; j++) z[j] = x[tb->perm[64 * h + j]];
+        orc_rotate64_f32(z, tb->signs + 64 * h, rho);
+        uint16_t nh = orc_f32_to_f16_rn(sqrtf(orc_tree_sum_sq64(rho)));
+        float n = orc_f16_to_f32(nh);
+        float inv = (n > 0.0f) ? 1.0f / n : 0.0f;
+        const float* th = h ? tb->theta2 : tb->theta;
+        const int n_thr = (1 << (h ? bits_o - 1 : bits_o)) - 1;
+        for (int j = 0; j < 64; j++) {
+            float u = rho[j] * inv;
+            int c = 0;
+            for (int i = 0; i < n_thr; i++)
+                if (u > th[i]) c++;
+            codes[64 * h + j] = (uint8_t)c;
+        }
+        n16[h] = nh;
+    }
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* plane layouts                                                                               */
 /* ------------------------------------------------------------------------------------------ */
 /*
@@ -430,6 +544,10 @@ void orc_turbo_encode_bits(const float* x, const orc_tables* tb, int code_bits, 
  * tau = t%32, octet o = tau/8, i = tau%8; channel d: n = d%16, N = d/16.  Bit k of the code of
  * (t, d) is in u32 word 2b*(16*o + n) + 2*k + N/4 of block t/32, at bit
  * 16*(i%2) + 4*(N%4) + i/2.  Meta: u16 n per token, natural order.
+ * Split V (TURBO_SPLIT, outlier bits bo, the rest bo - 1, W = 2 bo - 1 words per (o, n)): blocks
+ * of 32 tokens, 256 W B each; position j (channel perm[j]): n = j%16, N = j/16.  Bit k of the
+ * code of (t, j) is in u32 word W*(16*o + n) + k (j < 64) or W*(16*o + n) + bo + k (j >= 64) of
+ * block t/32, at bit 16*(i%2) + 4*(N%4) + i/2.  Meta: u16 n_outlier, u16 n_rest per token.
  * Every turbo plane holds a whole number of 64-token blocks.
  * Window ring: [W][128] fp32, token t at slot t % W.
  */
@@ -443,6 +561,7 @@ static int uniform_layout(const orc_plane_cfg* pc) { return pc->scheme == ORC_UN
 
 size_t orc_codes_bytes(const orc_plane_cfg* pc)
 {
+    if (pc->scheme == ORC_TURBO_SPLIT) return (size_t)ceil_to(pc->capacity, 64) * 8 * (2 * pc->bits - 1);
     if (!uniform_layout(pc)) return (size_t)ceil_to(pc->capacity, 64) * 16 * pc->bits; /* b bit planes */
     return (size_t)ceil_to(pc->capacity, 64) * 16 * pc->bits;
 }
@@ -451,6 +570,7 @@ size_t orc_meta_bytes(const orc_plane_cfg* pc)
 {
     if (pc->scheme == ORC_TURBO_QJL) return (size_t)ceil_to(pc->capacity, 64) * 4;
     if (pc->scheme == ORC_TURBO_MSE) return (size_t)ceil_to(pc->capacity, 64) * 2;
+    if (pc->scheme == ORC_TURBO_SPLIT) return (size_t)ceil_to(pc->capacity, 64) * 4;
     return (size_t)ceil_to(pc->capacity, 64) * 16;
 }
 
@@ -492,6 +612,12 @@ static size_t tv_word(int t, int d, int k, int b)
 {
     int tau = t % 32, o = tau / 8, n = d % 16, N = d / 16;
     return (size_t)(t / 32) * (size_t)(512 * b) + 4 * (size_t)(2 * b * (16 * o + n) + 2 * k + N / 4);
+}
+/* Split V: byte offset of the word holding bit k of (token t, position j); bo = outlier bits. */
+static size_t ts_word(int t, int j, int k, int bo)
+{
+    int W = 2 * bo - 1, o = (t % 32) / 8, n = j % 16;
+    return (size_t)(t / 32) * (size_t)(256 * W) + 4 * (size_t)(W * (16 * o + n) + (j < 64 ? k : bo + k));
 }
 static int tv_bit(int t, int d)
 {
@@ -536,6 +662,15 @@ static void pack_token(const orc_plane_cfg* pc, int t, const uint8_t* code, cons
                 put_u16(m + 8 + 2 * g, z16[g]);
             }
         }
+        return;
+    }
+    if (pc->scheme == ORC_TURBO_SPLIT) {
+        for (int j = 0; j < D; j++) {
+            int nb = (j < 64) ? pc->bits : pc->bits - 1;
+            for (int k = 0; k < nb; k++) put_bit(codes + ts_word(t, j, k, pc->bits), tv_bit(t, j), code[j] >> k);
+        }
+        put_u16(meta + (size_t)t * 4, n16);
+        put_u16(meta + (size_t)t * 4 + 2, g16);
         return;
     }
     if (pc->tensor == ORC_TENSOR_V) {
@@ -593,6 +728,16 @@ void orc_plane_read(const orc_plane_cfg* pc, const uint8_t* codes, const uint8_t
         return;
     }
     for (int k = 0; k < 8; k++) meta8[k] = 0;
+    if (pc->scheme == ORC_TURBO_SPLIT) {
+        for (int j = 0; j < D; j++) {
+            int nb = (j < 64) ? pc->bits : pc->bits - 1, c = 0;
+            for (int k = 0; k < nb; k++) c |= get_bit(codes + ts_word(t, j, k, pc->bits), tv_bit(t, j)) << k;
+            code[j] = (uint8_t)c;
+        }
+        meta8[0] = get_u16(meta + (size_t)t * 4);
+        meta8[1] = get_u16(meta + (size_t)t * 4 + 2);
+        return;
+    }
     if (pc->tensor == ORC_TENSOR_V) {
         for (int d = 0; d < D; d++) {
             int c = 0;
@@ -644,6 +789,11 @@ void orc_plane_append(const orc_plane_cfg* pc, const orc_tables* tb, const float
                 else
                     orc_quant_group(y + GS * g, pc->bits, code + GS * g, &s16[g], &z16[g]);
             }
+        } else if (pc->scheme == ORC_TURBO_SPLIT) {
+            uint16_t nn[2];
+            orc_split_encode(x, tb, pc->bits, code, nn);
+            n16 = nn[0]; /* outlier subset */
+            g16 = nn[1]; /* the rest */
         } else {
             orc_turbo_encode_bits(x, tb, pc->bits, pc->scheme == ORC_TURBO_QJL, NULL, code, &n16, &g16, bits,
                                   NULL);
@@ -678,6 +828,16 @@ void orc_dequant_token(const orc_plane_cfg* pc, const orc_tables* tb, const uint
             orc_unrotate_f64(y, tb->signs, out);
         else
             memcpy(out, y, sizeof y);
+        return;
+    }
+    if (pc->scheme == ORC_TURBO_SPLIT) {
+        for (int h = 0; h < 2; h++) {
+            double nh = orc_f16_to_f32(m8[h]), z[64];
+            const float* mu = h ? tb->mu2 : tb->mu;
+            for (int j = 0; j < 64; j++) y[64 * h + j] = nh * (double)mu[code[64 * h + j]];
+            orc_unrotate64_f64(y + 64 * h, tb->signs + 64 * h, z);
+            for (int j = 0; j < 64; j++) out[tb->perm[64 * h + j]] = z[j];
+        }
         return;
     }
     double n = orc_f16_to_f32(m8[0]);

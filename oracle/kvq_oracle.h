@@ -14,6 +14,9 @@
  *  - "LLM memory saving: weights vs KV-cache quantization 2026", method comparison table
  *    (TurboQuant row "core idea"): random rotation, per-coordinate optimal scalar quantizer,
  *    1-bit QJL on the residual for an unbiased inner product.
+ *  - the same page, method comparison table (the row of re-checked figures: 2.5 and 3.5 bits) and
+ *    its verification notes (non-integer bit widths come from splitting off outlier channels;
+ *    the printed example is garbled): the outlier-channel split of the value coder.
  * Every step the pages leave open is fixed by a stated reading (see the .c file's comments).
  *
  * Arithmetic conventions: binary32 round-to-nearest-even with no FMA contraction (the library is
@@ -34,13 +37,13 @@ extern "C" {
 #define ORC_GROUP 32
 #define ORC_NGROUPS 4
 
-enum { ORC_UNIFORM = 0, ORC_TURBO_QJL = 1, ORC_TURBO_MSE = 2, ORC_Q8_0 = 3 };
+enum { ORC_UNIFORM = 0, ORC_TURBO_QJL = 1, ORC_TURBO_MSE = 2, ORC_Q8_0 = 3, ORC_TURBO_SPLIT = 4 };
 enum { ORC_TENSOR_K = 0, ORC_TENSOR_V = 1 };
 
 /* One (layer, sequence, kv head, tensor) plane description. */
 typedef struct {
-    int scheme;    /* ORC_UNIFORM / ORC_TURBO_QJL / ORC_TURBO_MSE / ORC_Q8_0 */
-    int bits;      /* uniform: 4 or 8; turbo: 3 */
+    int scheme;    /* ORC_UNIFORM / ORC_TURBO_QJL / ORC_TURBO_MSE / ORC_Q8_0 / ORC_TURBO_SPLIT */
+    int bits;      /* uniform: 4 or 8; turbo: 3 (MSE V also 4); split: outlier bits 3 or 4 */
     int rotate;    /* random-sign WHT before coding (always on for turbo) */
     int sinkhorn;  /* fold 1/c before uniform coding */
     int window;    /* FP32 window W: 0 (flat) or 128 (progressive) */
@@ -56,6 +59,11 @@ typedef struct {
     const float* S;      /* [128*128] QJL projection, row-major S[i][j] */
     const float* mu;     /* [8] Lloyd-Max centroids for N(0,1/128), fp32 */
     const float* theta;  /* [7] decision thresholds, fp32 */
+    /* outlier split (ORC_TURBO_SPLIT): mu / theta above are the outlier subset's codebook, these
+     * the other subset's (one bit fewer), both for N(0, 1/64); perm[j] = channel at position j */
+    const float* mu2;
+    const float* theta2;
+    const int* perm;
 } orc_tables;
 
 /* ---- binary16 ---- */
@@ -88,6 +96,10 @@ void orc_lloyd_max(int iters, double* mu_star, float* mu, float* theta, double* 
 void orc_lloyd_max_levels(int levels, int iters, double* mu_star, float* mu, float* theta,
                           double* last_change);
 
+/* The same for coordinates of a unit vector in `dim` dimensions: centroids mu* / sqrt(dim). */
+void orc_lloyd_max_dim(int levels, int dim, int iters, double* mu_star, float* mu, float* theta,
+                       double* last_change);
+
 /* ---- TurboQuant token code ---- */
 void orc_turbo_encode(const float* x, const orc_tables* tb, int with_qjl, float* rho_out,
                       uint8_t* codes, uint16_t* n16, uint16_t* g16, uint8_t* bits,
@@ -97,6 +109,17 @@ void orc_turbo_encode_bits(const float* x, const orc_tables* tb, int code_bits, 
                            float* rho_out, uint8_t* codes, uint16_t* n16o, uint16_t* g16o,
                            uint8_t* bits, float* resid_out);
 float orc_tree_sum_sq(const float* v);
+
+/* ---- outlier-channel split (fractional bit widths) ---- */
+/* 64-point random-sign rotation (1/8) H64 (d .* x), and its inverse in binary64. */
+void orc_rotate64_f32(const float* x, const float* signs, float* y);
+void orc_unrotate64_f64(const double* y, const float* signs, double* x);
+float orc_tree_sum_sq64(const float* v);
+/* perm[128]: the 64 outlier channels of the calibration tokens X [n][128] ascending, then the
+ * other 64 ascending. */
+void orc_select_outliers(const float* X, int n, int* perm);
+/* Token code of the split: codes[j] for position j (channel perm[j]), n16[2] = subset norms. */
+void orc_split_encode(const float* x, const orc_tables* tb, int bits_o, uint8_t* codes, uint16_t* n16);
 
 /* ---- planes ---- */
 size_t orc_codes_bytes(const orc_plane_cfg* pc);

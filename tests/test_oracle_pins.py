@@ -862,3 +862,192 @@ def test_attention_turbo_close_to_exact():
     # the turbo-MSE dequantization is R^-1(n mu[code]) with relative error ~ sqrt(0.0345)
     errs = [np.linalg.norm(pv.dequant(t, tv) - V[t]) / np.linalg.norm(V[t]) for t in range(n)]
     assert 0.15 < np.mean(errs) < 0.22
+
+
+# ---------------------------------------------------------------------------------------------
+# TurboQuant outlier-channel split (fractional bit widths 2.5 / 3.5)
+# ---------------------------------------------------------------------------------------------
+
+def _split_tables(bits_o, signs_seed, perm=None):
+    _, mu_o, th_o, _ = oracle.lloyd_max(oracle.LLOYD_ITERS, 1 << bits_o, 64)
+    _, mu_r, th_r, _ = oracle.lloyd_max(oracle.LLOYD_ITERS, 1 << (bits_o - 1), 64)
+    perm = np.arange(128) if perm is None else perm
+    return oracle.TableSet(signs=_signs(signs_seed), mu=mu_o, theta=th_o, mu2=mu_r, theta2=th_r, perm=perm)
+
+
+def test_lloyd_max_4_levels_textbook_and_64_dim_scaling():
+    # the 2-bit codebook of the split's lower subset: Max's 4-level Gaussian quantizer has outputs
+    # +-0.4528, +-1.510, thresholds 0, +-0.9816 and distortion about 0.1175; the centroid condition
+    # by independent integration; every split codebook is the N(0,1) one divided by sqrt(64) = 8
+    mu_star, mu, theta, change = oracle.lloyd_max(oracle.LLOYD_ITERS, 4, 64)
+    assert change < 1e-12
+    assert np.max(np.abs(mu_star[2:] - [0.4528, 1.5104])) < 1e-4
+    assert theta[1] == 0.0 and abs(float(theta[2]) * 8 - 0.9816) < 1e-4
+    phi = lambda x: np.exp(-0.5 * x * x) / np.sqrt(2 * np.pi)
+    b = [-np.inf] + [(mu_star[k] + mu_star[k + 1]) / 2 for k in range(3)] + [np.inf]
+    mse = 0.0
+    for k in range(4):
+        m0 = scipy.integrate.quad(phi, b[k], b[k + 1], epsabs=1e-14)[0]
+        m1 = scipy.integrate.quad(lambda x: x * phi(x), b[k], b[k + 1], epsabs=1e-14)[0]
+        assert abs(m1 / m0 - mu_star[k]) < 1e-9
+        mse += scipy.integrate.quad(lambda x: (x - mu_star[k]) ** 2 * phi(x), b[k], b[k + 1],
+                                    epsabs=1e-14)[0]
+    assert 0.1170 < mse < 0.1180
+    for levels in (4, 8, 16):
+        ms, m64, t64, _ = oracle.lloyd_max(oracle.LLOYD_ITERS, levels, 64)
+        assert np.array_equal(m64, (ms / 8.0).astype(np.float32))
+        assert np.array_equal(t64, (((ms[1:] + ms[:-1]) / 2) / 8.0).astype(np.float32))
+
+
+def test_rotation64_matches_sylvester_matrix_and_inverse():
+    # (1/8) H64 (d .* x) against scipy's Sylvester matrix; the inverse restores x; the sign vector
+    # itself maps to 8 e0 exactly (H64 applied to all ones is 64 e0)
+    rng = np.random.default_rng(300)
+    H = scipy.linalg.hadamard(64).astype(np.float64)
+    for seed in range(4):
+        d = _signs(310 + seed)[:64]
+        x = rng.standard_normal(64).astype(np.float32)
+        y = oracle.rotate64_f32(x, d)
+        ref = H @ (d.astype(np.float64) * x) / 8.0
+        assert np.max(np.abs(y - ref)) < 1e-5 * np.max(np.abs(ref)) * 8
+        assert np.allclose(oracle.unrotate64_f64(ref, d), x, rtol=0, atol=1e-12)
+        assert abs(np.linalg.norm(y) - np.linalg.norm(x)) < 1e-5 * np.linalg.norm(x)
+        e = oracle.rotate64_f32(d, d)
+        assert e[0] == 8.0 and not e[1:].any()
+    v = rng.standard_normal(64).astype(np.float32)
+    assert abs(oracle.tree_sum_sq64(v) - float(np.sum(v.astype(np.float64) ** 2))) < 1e-5 * 64
+
+
+def test_select_outliers_brute_force_and_ties():
+    # planted energies far apart, plus three identical columns competing for the last two outlier
+    # places: the two with the smaller indices win; brute force sorts by (-energy, channel)
+    rng = np.random.default_rng(320)
+    n = 300
+    base = rng.standard_normal((n, 128)).astype(np.float32)
+    scale = np.ones(128, np.float32)
+    top = rng.permutation([d for d in range(128) if d not in (20, 70, 110)])[:62]
+    scale[top] = 10.0 + 0.05 * np.arange(62, dtype=np.float32)
+    X = base * scale
+    X[:, 70] = X[:, 20] = X[:, 110] = 5.0 * base[:, 0]
+    perm = oracle.select_outliers(X)
+    e = np.sum(X.astype(np.float64) ** 2, axis=0)
+    order = sorted(range(128), key=lambda d: (-e[d], d))
+    outl = sorted(order[:64])
+    assert 20 in outl and 70 in outl and 110 not in outl
+    assert list(perm[:64]) == outl and list(perm[64:]) == sorted(set(range(128)) - set(outl))
+    # one calibration token; all-zero tokens (every energy equal: channels 0..63 are the outliers)
+    perm1 = oracle.select_outliers(X[:1])
+    e1 = X[0].astype(np.float64) ** 2
+    assert list(perm1[:64]) == sorted(sorted(range(128), key=lambda d: (-e1[d], d))[:64])
+    assert np.array_equal(oracle.select_outliers(np.zeros((4, 128), np.float32)), np.arange(128))
+
+
+@pytest.mark.parametrize("bits_o", [3, 4])
+def test_split_encode_nearest_centroid_and_norms(bits_o):
+    rng = np.random.default_rng(330 + bits_o)
+    perm = rng.permutation(128).astype(np.int32)
+    tb = _split_tables(bits_o, 331, perm)
+    d = _signs(331)
+    mus = [tb.arrays["mu"].astype(np.float64), tb.arrays["mu2"].astype(np.float64)]
+    for t in range(40):
+        x = (rng.standard_normal(128) * (1.0 + 3.0 * (np.arange(128) < 20))).astype(np.float32)
+        codes, n16 = oracle.split_encode(x, tb, bits_o)
+        for h in range(2):
+            z = x[perm[64 * h:64 * h + 64]]
+            rho = scipy.linalg.hadamard(64) @ (d[64 * h:64 * h + 64].astype(np.float64) * z) / 8.0
+            n = float(np.uint16(n16[h]).view(np.float16))
+            assert abs(n - np.linalg.norm(rho)) <= 2.0 ** -10 * np.linalg.norm(rho)
+            u = rho / n
+            mu = mus[h]
+            assert mu.size == 1 << (bits_o - h)
+            best = np.abs(u[:, None] - mu[None, :]).argmin(1)
+            mid = (mu[1:] + mu[:-1]) / 2
+            near = np.min(np.abs(u[:, None] - mid[None, :]), axis=1) < 1e-5
+            assert np.all((best == codes[64 * h:64 * h + 64]) | near)
+
+
+def test_split_layout_golden_words_and_sizes():
+    # hand-derived: outlier bits 3, so W = 2*3 - 1 = 5 words per (octet, lane column), 1280 B per
+    # 32-token block.  Token 45: block 1, tau = 13, o = 1, i = 5 -> bit 16 + 4 (N % 4) + 2.
+    # Position 83 (rest subset, n = 3, N = 5): word 5 (16 + 3) + 3 + k = 98 + k, bit 22, k < 2.
+    # Position 37 (outlier subset, n = 5, N = 2): word 5 (16 + 5) + k = 105 + k, bit 26, k < 3.
+    rng = np.random.default_rng(340)
+    tb = _split_tables(3, 341, rng.permutation(128).astype(np.int32))
+    X = rng.standard_normal((64, 128)).astype(np.float32)
+    p = oracle.Plane(oracle.TURBO_SPLIT, 3, True, False, 0, oracle.TENSOR_V, 64)
+    p.append(X, tb)
+    codes, n16 = oracle.split_encode(X[45], tb, 3)
+    blk = p.codes[1280:2560]
+    for k in range(2):
+        assert (_word(blk, 98 + k) >> 22) & 1 == (codes[83] >> k) & 1
+    for k in range(3):
+        assert (_word(blk, 105 + k) >> 26) & 1 == (codes[37] >> k) & 1
+    m = p.meta[45 * 4:45 * 4 + 4].view(np.uint16)
+    assert (int(m[0]), int(m[1])) == n16
+    # 2.5 and 3.5 bits per channel: 40 and 56 code bytes per token, and 4 meta bytes
+    for bo, per_tok in ((3, 40), (4, 56)):
+        q = oracle.Plane(oracle.TURBO_SPLIT, bo, True, False, 0, oracle.TENSOR_V, 128)
+        assert q.codes.size == 128 * per_tok and per_tok * 8 / 128 == bo - 0.5
+        assert q.meta.size == 128 * 4
+
+
+@pytest.mark.parametrize("bits_o", [3, 4])
+def test_split_round_trip_disjoint_and_distortion(bits_o):
+    # every token reads back its own codes and norms (writing t never disturbs another token),
+    # unwritten tokens stay zero, and the per-subset relative error of the dequantized value sits
+    # at the textbook distortion of its codebook (sqrt(0.0345) = 0.186 at 3 bits, sqrt(0.1175) =
+    # 0.343 at 2 bits, sqrt(0.0095) = 0.097 at 4 bits): a wrong inverse rotation, sign set or
+    # permutation would give errors near 1.4
+    rng = np.random.default_rng(350 + bits_o)
+    perm = rng.permutation(128).astype(np.int32)
+    tb = _split_tables(bits_o, 351, perm)
+    n = 150
+    X = rng.standard_normal((n, 128)).astype(np.float32)
+    p = oracle.Plane(oracle.TURBO_SPLIT, bits_o, True, False, 0, oracle.TENSOR_V, 200)
+    p.append(X, tb)
+    err = np.zeros((n, 2))
+    for t in range(n):
+        code, meta8, _ = p.read(t)
+        c, n16 = oracle.split_encode(X[t], tb, bits_o)
+        assert np.array_equal(code, c) and (int(meta8[0]), int(meta8[1])) == n16
+        y = p.dequant(t, tb)
+        for h in range(2):
+            ch = perm[64 * h:64 * h + 64]
+            err[t, h] = np.linalg.norm(y[ch] - X[t, ch]) / np.linalg.norm(X[t, ch])
+    code, meta8, _ = p.read(n + 3)
+    assert not code.any() and not meta8.any()
+    expect = {4: 0.097, 3: 0.186, 2: 0.343}
+    for h, b in ((0, bits_o), (1, bits_o - 1)):
+        assert abs(np.mean(err[:, h]) - expect[b]) < 0.15 * expect[b]
+    # a token with energy only in the outlier channels: the rest subset has norm 0 and dequantizes
+    # to exact zeros
+    x = np.zeros(128, np.float32)
+    x[perm[:64]] = rng.standard_normal(64)
+    q = oracle.Plane(oracle.TURBO_SPLIT, bits_o, True, False, 0, oracle.TENSOR_V, 64)
+    q.append(x[None], tb)
+    _, meta8, _ = q.read(0)
+    assert meta8[1] == 0 and not q.dequant(0, tb)[perm[64:]].any()
+
+
+def test_attention_split_v_close_to_exact():
+    rng = np.random.default_rng(360)
+    n = 300
+    K = rng.standard_normal((n, 128)).astype(np.float32)
+    V = rng.standard_normal((n, 128)).astype(np.float32)
+    V[:, :16] *= 6.0  # outlier channels
+    q = rng.standard_normal((2, 128)).astype(np.float32)
+    perm = oracle.select_outliers(V[:64])
+    assert set(range(16)) <= set(perm[:64].tolist())
+    tk = oracle.TableSet()
+    pk = oracle.Plane(oracle.UNIFORM, 8, False, False, 0, oracle.TENSOR_K, n)
+    pk.append(K, tk)
+    outs = {}
+    for bo in (3, 4):
+        tv = _split_tables(bo, 361, perm)
+        pv = oracle.Plane(oracle.TURBO_SPLIT, bo, True, False, 0, oracle.TENSOR_V, n)
+        pv.append(V, tv)
+        outs[bo] = oracle.attention(pk, pv, tk, tv, q)
+    ref = _textbook(q, K, V)
+    r3 = np.linalg.norm(outs[3] - ref) / np.linalg.norm(ref)
+    r4 = np.linalg.norm(outs[4] - ref) / np.linalg.norm(ref)
+    assert r4 < r3 < 0.35
