@@ -37,6 +37,8 @@ def token_head_bytes(scheme, bits):
         return 16 * bits + 16
     if scheme == W.TURBO_QJL:
         return 48 + 4 + 16
+    if scheme == W.TURBO_SPLIT:
+        return 8 * (2 * bits - 1) + 4  # bits + (bits - 1) planes of 8 B + two fp16 norms
     return 16 * bits + 2  # TurboQuant-MSE: b bit planes + fp16 norm
 
 
@@ -116,7 +118,8 @@ def prefill_report(wl: W.Workload, prefill_s):
 
 def split_kernel_name(wl: W.Workload) -> str:
     """The split-K decode kernel the library launches for this cache (matrix-core path)."""
-    kind = lambda scheme, bits: ("Tb4" if bits == 4 else "Tb") if W.is_turbo(scheme) else f"U{bits}"  # noqa: E731
+    kind = lambda scheme, bits: (f"Ts{bits}" if scheme == W.TURBO_SPLIT else  # noqa: E731
+                                 ("Tb4" if bits == 4 else "Tb") if W.is_turbo(scheme) else f"U{bits}")
     return (f"decode_mfma_kernel (K {kind(wl.k_scheme, wl.k_bits)}, V {kind(wl.v_scheme, wl.v_bits)}, "
             f"{wl.group} query heads per kv head)")
 
@@ -132,7 +135,7 @@ def build_cache(wl: W.Workload, extra: int, log):
     stream = torch.cuda.current_stream()
     pre = []  # (start, end) events around each layer's bulk prefill on the launch stream
     for layer in range(wl.n_layers):
-        if wl.sinkhorn_iters > 0:
+        if wl.sinkhorn_iters > 0 or wl.v_scheme == W.TURBO_SPLIT:
             cache.calibrate(layer, W.gen_calib(wl, layer, 0, device="cuda"),
                             W.gen_calib(wl, layer, 1, device="cuda"))
         k = W.gen_kv(wl, layer, 0, device="cuda")
@@ -174,6 +177,10 @@ def cpu_baseline(wl: W.Workload, kv0, budget_s: float):
             if sink:
                 cal = W.gen_calib(wl, 0, tensor)[:, h].float().numpy()
                 kw["c"], kw["inv_c"] = oracle.sinkhorn(cal, kw.get("signs"), wl.sinkhorn_iters)
+            if scheme == W.TURBO_SPLIT:
+                kw["perm"] = oracle.select_outliers(W.gen_calib(wl, 0, 1)[:, h].float().numpy())
+                _, kw["mu"], kw["theta"], _ = oracle.lloyd_max(oracle.LLOYD_ITERS, 1 << bits, 64)
+                _, kw["mu2"], kw["theta2"], _ = oracle.lloyd_max(oracle.LLOYD_ITERS, 1 << (bits - 1), 64)
             tb = oracle.TableSet(**kw)
             p = oracle.Plane(scheme, bits, rot, sink, wl.window, tensor, X.shape[0])
             p.append(X[:, h], tb)

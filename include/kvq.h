@@ -54,10 +54,19 @@ typedef enum {
     KVQ_TURBO_QJL = 1, /* K only: rotation + 3-bit Lloyd-Max code + 1-bit QJL residual [P3]  */
     KVQ_TURBO_MSE = 2, /* rotation + 3-bit (or, for V, 4-bit) Lloyd-Max code, no residual
                           sketch [P3]                                                      */
-    KVQ_Q8_0 = 3       /* symmetric 8-bit groups of 32, one fp16 scale d ("q8_0", [P2]'s
+    KVQ_Q8_0 = 3,      /* symmetric 8-bit groups of 32, one fp16 scale d ("q8_0", [P2]'s
                           baseline; K = Q8 of [P3]'s application rules): q = rint(y / d) in
                           [-127, 127] with d = fp16(max|y| / 127); stored in the UNIFORM 8-bit
                           layout as code q + 128 with zero = -128 d, so y = d q exactly       */
+    KVQ_TURBO_SPLIT = 4 /* V only: TurboQuant-MSE with the outlier-channel split that gives the
+                          fractional bit widths of [P3] (2.5 and 3.5 bits, method table and
+                          verification notes).  kvq_calibrate picks per (layer, kv head) the 64
+                          channels of largest energy (sum of squares over the calibration
+                          tokens, binary64 in token order; ties to the smaller index); each
+                          64-channel subset gets its own 64-point random-sign Walsh-Hadamard
+                          rotation (signs 0..63 / 64..127 of the tensor's sign vector, scale
+                          1/8), fp16 norm and Lloyd-Max code for N(0, 1/64): v_bits (3 or 4)
+                          bits on the outliers, v_bits - 1 on the rest                     */
 } kvq_scheme;
 
 typedef struct {
@@ -67,13 +76,15 @@ typedef struct {
                                             ("context_length" of [P1])                       */
     int k_scheme, v_scheme;              /* kvq_scheme, chosen separately for K and V [P2]   */
     int k_bits, v_bits;                  /* UNIFORM: 4 or 8; TURBO_QJL: 3; TURBO_MSE: 3, or 4
-                                            for V ("Turbo4", [P3] rules); Q8_0: 8           */
+                                            for V ("Turbo4", [P3] rules); Q8_0: 8;
+                                            TURBO_SPLIT: 3 (2.5 bits) or 4 (3.5 bits)        */
     int group_size;                      /* must be 32                                       */
     int fp32_window;                     /* 0 = flat, 128 = progressive [P1]                 */
     int rotate_k, rotate_v;              /* random-sign Walsh-Hadamard before coding [P2];
                                             implied by the TURBO schemes                      */
     int sinkhorn_iters, calib_tokens;    /* Sinkhorn balancing of UNIFORM planes [P2]; 0 = off;
-                                            calib_tokens bounds kvq_calibrate's n_tokens     */
+                                            calib_tokens bounds kvq_calibrate's n_tokens (also
+                                            needed, 2..65536, by a TURBO_SPLIT V)             */
 } kvq_config;
 
 typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
@@ -101,6 +112,11 @@ typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
  *      (tau = t%32, o = tau/8, i = tau%8), channel d (n = d%16, N = d/16): bit k of its code is
  *      in u32 word 2b*(16o + n) + 2k + N/4 of block t/32, at bit 16*(i%2) + 4*(N%4) + i/2.
  *      Meta: u16 fp16 norm per token.  4-bit codes index the 16-level Lloyd-Max codebook.
+ *  TURBO_SPLIT V (bo = v_bits, W = 2 bo - 1): blocks of 32 tokens, 256 W B each; position j
+ *      (channel perm[j], n = j%16, N = j/16): bit k of its code is in u32 word
+ *      W*(16o + n) + k (j < 64, k < bo) or W*(16o + n) + bo + k (j >= 64, k < bo - 1) of block
+ *      t/32, at bit 16*(i%2) + 4*(N%4) + i/2.  Meta: u16 fp16 outlier norm, u16 fp16 rest norm
+ *      per token.
  *  Window ring: [fp32_window][128] fp32, token t at slot t % fp32_window.               */
 typedef struct {
     void *codes, *meta, *qjl, *window;
@@ -118,13 +134,17 @@ typedef struct {
     const float* theta;  /* [7] Lloyd-Max decision thresholds                            */
     const float* mu16;   /* [16] 16-level centroids (4-bit TurboQuant-MSE V), if present */
     const float* theta16; /* [15] their thresholds                                       */
+    const int* perm;     /* [n_layers][n_kv_heads][128] TURBO_SPLIT position -> channel    */
+    const float* mu64;   /* [28] TURBO_SPLIT codebooks of N(0, 1/64): 4, 8, 16 levels at 0,
+                            4, 12                                                       */
+    const float* theta64; /* [28] their thresholds, same offsets (levels - 1 used)       */
 } kvq_tables;
 
 enum {
     KVQ_OPT_SPLIT_TOKENS = 1, /* tokens per decode split (multiple of 64); 0 = automatic     */
     KVQ_OPT_DECODE_PATH = 2   /* 0 = automatic, 1 = vector-ALU kernel, 2 = matrix-core kernel;
-                                 4-bit TurboQuant V has the matrix-core kernel only (1 gives
-                                 KVQ_ERR_UNSUPPORTED at decode time)                      */
+                                 4-bit and split TurboQuant V have the matrix-core kernel
+                                 only (1 gives KVQ_ERR_UNSUPPORTED at decode time)        */
 };
 
 /* Bytes of device memory a cache with this configuration needs (planes for every layer,
@@ -154,7 +174,8 @@ kvq_status kvq_set_random_tables(kvq_cache* cache, const float* signs, const flo
  * [128] of dtype for K and V; a tensor's pointer may be NULL when it is not balanced), then
  * alternately divide rows and columns by their population standard deviation sinkhorn_iters
  * times in fp64 on the device, and store c = product of the column divisors and fp32(1/c).
- * 2 <= n_tokens <= calib_tokens.  Required once per layer before appending to it. */
+ * 2 <= n_tokens <= calib_tokens.  A TURBO_SPLIT V takes its 64 outlier channels per kv head
+ * from Vc (required then) in the same call.  Required once per layer before appending to it. */
 kvq_status kvq_calibrate(kvq_cache* cache, int layer, const void* Kc, const void* Vc, int dtype,
                          int n_tokens, void* stream);
 

@@ -97,6 +97,7 @@ class KvCache:
         return codes, meta, qjl, win
 
     def table(self, name, count):
-        """fp32 device view of one table (signs, c, inv_c, qjl_S, mu, theta, mu16, theta16)."""
+        """Device view of one table: fp32 for signs, c, inv_c, qjl_S, mu, theta, mu16, theta16, mu64,
+        theta64; int32 for perm (the split V's position -> channel map)."""
         t = _kvq.kvq_get_tables(self.handle)
-        return self._slice(getattr(t, name), 4 * count).view(torch.float32)
+        return self._slice(getattr(t, name), 4 * count).view(torch.int32 if name == "perm" else torch.float32)

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
 KVQ_F32, KVQ_BF16 = 0, 1
-KVQ_UNIFORM, KVQ_TURBO_QJL, KVQ_TURBO_MSE = 0, 1, 2
+KVQ_UNIFORM, KVQ_TURBO_QJL, KVQ_TURBO_MSE, KVQ_Q8_0, KVQ_TURBO_SPLIT = 0, 1, 2, 3, 4
 KVQ_OPT_SPLIT_TOKENS, KVQ_OPT_DECODE_PATH = 1, 2
 STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_INVALID_ARG", 2: "KVQ_ERR_UNSUPPORTED", 3: "KVQ_ERR_CAPACITY",
           4: "KVQ_ERR_NOT_READY", 5: "KVQ_ERR_BUFFER_TOO_SMALL", 6: "KVQ_ERR_MISALIGNED",
@@ -49,7 +49,7 @@ class kvq_layout(ctypes.Structure):
 
 class kvq_tables(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("signs", "c", "inv_c", "qjl_S", "mu", "theta", "mu16",
-                                              "theta16")]
+                                              "theta16", "perm", "mu64", "theta64")]
 
 
 _lib = None

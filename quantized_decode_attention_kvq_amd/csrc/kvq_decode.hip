@@ -376,6 +376,7 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     __shared__ float s_m[8], s_l[8];
     __shared__ float4 s_q[8][32], s_w[8][32];
+    __shared__ float s_x[kDim]; // split V: the un-rotated positions, scattered to their channels
     const int hq = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
     const int c4 = t & 31, part = t >> 5;
     const int kvh = hq / p.G;
@@ -446,7 +447,39 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     const size_t tab = (size_t)(kvh * 2 + 1) * kDim + 4 * c4;
     if (VG.sinkhorn)
         for (int j = 0; j < 4; ++j) q[j] *= p.cs[tab + j];
-    if (VG.rotate) {
+    if (VG.scheme == kTurboSplit) {
+        // each 64-position half: (1/8) d .* H64 y (strides 1, 2 in the thread, 4..32 across
+        // lanes), then position j goes to channel perm[j]
+        for (int h = 1; h < 4; h <<= 1)
+            for (int j = 0; j < 4; ++j)
+                if (!(j & h)) {
+                    const float x = q[j], y = q[j + h];
+                    q[j] = x + y;
+                    q[j + h] = x - y;
+                }
+        auto stage = [&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            const bool upper = (c4 & h) != 0;
+            for (int j = 0; j < 4; ++j) {
+                const float o = xor_lane<h>(q[j]);
+                q[j] = upper ? o - q[j] : q[j] + o;
+            }
+        };
+        stage(std::integral_constant<int, 1>{});
+        stage(std::integral_constant<int, 2>{});
+        stage(std::integral_constant<int, 4>{});
+        stage(std::integral_constant<int, 8>{});
+        const int4 pm = reinterpret_cast<const int4*>(p.perm + (size_t)kvh * kDim)[c4];
+        const int pj[4] = {pm.x, pm.y, pm.z, pm.w};
+        for (int j = 0; j < 4; ++j) {
+            float v = q[j] * 0.125f;
+            if (p.signs[tab + j] < 0.0f) v = -v;
+            s_x[pj[j]] = v;
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        for (int j = 0; j < 4; ++j) q[j] = s_x[4 * c4 + j];
+    } else if (VG.rotate) {
         // Walsh-Hadamard butterflies over the 128 channels: strides 1 and 2 inside a thread,
         // strides 4..64 between the 32 lanes (channel 4*lane + j) by xor shuffles.
         for (int h = 1; h < 4; h <<= 1)

@@ -48,8 +48,9 @@ constexpr int kPRow = 72;                 // halves per staged P row: 64 tokens 
 constexpr int kPWave = 4 * 16 * kPRow;    // halves per wave: [group | plane][16 rows][token]
 constexpr float kKappa = 0.0097915166977774f; // sqrt(pi/2) / 128
 // cache kinds (template parameters)
-// uniform 4-bit, uniform 8-bit, TurboQuant 3-bit, TurboQuant-MSE 4-bit (V only)
-constexpr int kU4 = 0, kU8 = 1, kTb = 2, kTb4 = 3;
+// uniform 4-bit, uniform 8-bit, TurboQuant 3-bit, TurboQuant-MSE 4-bit (V only), and the split
+// TurboQuant-MSE V with 3 / 4 bits on the outlier half (2.5 / 3.5 bits per channel)
+constexpr int kU4 = 0, kU8 = 1, kTb = 2, kTb4 = 3, kTs3 = 4, kTs4 = 5;
 
 // Eight one-bit operands from a half-interleaved word: quarter q (0..3) of each half, i.e. bits
 // 4q + v and 16 + 4q + v (v = 0..3).  Operand 2v + h is that bit times 2^(4(q%2) + v - 24).
@@ -114,13 +115,85 @@ struct VRegs<kTb4> {
     uint2 w[2][4];
     uint2 nm;
 };
+// split V: the lane's W = 2 bo - 1 words (outlier planes, then the rest's) of each 32-token
+// block, and the (outlier, rest) norm pairs of tokens 4 (lane % 16) + 0..3
+template <>
+struct VRegs<kTs3> {
+    uint32_t w[2][5];
+    u4 nm;
+};
+template <>
+struct VRegs<kTs4> {
+    uint32_t w[2][7];
+    u4 nm;
+};
+
+// Coefficients of a b-bit odd-symmetric codebook as a sum over the odd monomials of the code's
+// +-1 bits (b = 2: b0, b1; b = 3: b0, b1, b2, b0b1b2; b = 4: b0, b1, b2, b3, b0b1b2, b0b1b3,
+// b0b2b3, b1b2b3): a_S = mean over the upper half of mu[c] prod_S b (the top bit is 1 there).
+template <int B>
+__device__ __forceinline__ void odd_coeffs(const float* mu, float* a) {
+    constexpr int H = 1 << (B - 1);
+#pragma unroll
+    for (int s = 0; s < H; ++s) a[s] = 0.0f;
+#pragma unroll
+    for (int c = H; c < 2 * H; ++c) {
+        const float m = mu[c];
+        const float b0 = (c & 1) ? 1.0f : -1.0f, b1 = (c & 2) ? 1.0f : -1.0f, b2 = (c & 4) ? 1.0f : -1.0f;
+        if constexpr (B == 2) {
+            a[0] += m * b0;
+            a[1] += m;
+        } else if constexpr (B == 3) {
+            a[0] += m * b0;
+            a[1] += m * b1;
+            a[2] += m;
+            a[3] += m * (b0 * b1);
+        } else {
+            a[0] += m * b0;
+            a[1] += m * b1;
+            a[2] += m * b2;
+            a[3] += m;
+            a[4] += m * (b0 * b1 * b2);
+            a[5] += m * (b0 * b1);
+            a[6] += m * (b0 * b2);
+            a[7] += m * (b1 * b2);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < H; ++s) a[s] *= 1.0f / (float)H;
+}
+
+// PV products of one 16-channel tile with a b-bit plane set: w[k] = plane k's word, the
+// monomials in odd_coeffs order as -+1 operands (an odd product of +-1 bits is 2 parity - 1).
+template <int B>
+__device__ __forceinline__ f4 pv_planes(const h8* Pg, const uint32_t* w, int q, f4 acc) {
+    acc = mfma16(Pg[0], as_h8(pm1x8(w[0], q)), acc);
+    acc = mfma16(Pg[1], as_h8(pm1x8(w[1], q)), acc);
+    if constexpr (B == 3) {
+        acc = mfma16(Pg[2], as_h8(pm1x8(w[2], q)), acc);
+        acc = mfma16(Pg[3], as_h8(pm1x8(w[0] ^ w[1] ^ w[2], q)), acc);
+    } else if constexpr (B == 4) {
+        const uint32_t x01 = w[0] ^ w[1];
+        acc = mfma16(Pg[2], as_h8(pm1x8(w[2], q)), acc);
+        acc = mfma16(Pg[3], as_h8(pm1x8(w[3], q)), acc);
+        acc = mfma16(Pg[4], as_h8(pm1x8(x01 ^ w[2], q)), acc);
+        acc = mfma16(Pg[5], as_h8(pm1x8(x01 ^ w[3], q)), acc);
+        acc = mfma16(Pg[6], as_h8(pm1x8(w[0] ^ w[2] ^ w[3], q)), acc);
+        acc = mfma16(Pg[7], as_h8(pm1x8(w[1] ^ w[2] ^ w[3], q)), acc);
+    }
+    return acc;
+}
 
 template <int KT, int VT, int MB, int kNW>
 __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     constexpr bool KU = KT != kTb, VU = VT == kU4 || VT == kU8, VT4 = VT == kTb4;
+    constexpr bool VS = VT == kTs3 || VT == kTs4;
     constexpr int KB = KT == kU4 ? 4 : 8, VB = VT == kU4 ? 4 : 8;
-    // P staging slots per wave: 4 (uniform groups, or the 3-bit planes), 8 (the 4-bit monomials)
-    constexpr int kSlots = VT4 ? 8 : 4, kPW = kSlots * 16 * kPRow;
+    // split V: bo bits on the outlier half (kSo monomials), bo - 1 on the rest (kSr), W words
+    constexpr int kBo = VT == kTs4 ? 4 : 3, kSo = 1 << (kBo - 1), kSr = kSo / 2, kWv = 2 * kBo - 1;
+    // P staging slots per wave: 4 (uniform groups, or the 3-bit planes), 8 (the 4-bit
+    // monomials), kSo + kSr (split V)
+    constexpr int kSlots = VT4 ? 8 : (VS ? kSo + kSr : 4), kPW = kSlots * 16 * kPRow;
     __shared__ float s_q[kMaxGroupHeads][kDim];   // q' in the rotated/balanced domain, scaled
     __shared__ float s_qw[kMaxGroupHeads][kDim];  // plain q * scale * log2e (FP32 window)
     __shared__ float s_sp[KU ? 1 : kMaxGroupHeads][kDim]; // S q' (TurboQuant K)
@@ -242,6 +315,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                     vr.vc[k][u] = *reinterpret_cast<const u4*>(c + k * 512 * VB + 16 * u);
 #pragma unroll
             for (int j = 0; j < 4; ++j) vr.vm[j] = *reinterpret_cast<const u4*>(vmeta + (t0 + 4 * lr + j) * 16);
+        } else if constexpr (VS) {
+            const uint32_t* c = reinterpret_cast<const uint32_t*>(vcodes + (t0 / 32) * (256 * kWv)) + kWv * l;
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int u = 0; u < kWv; ++u) vr.w[k][u] = c[k * 64 * kWv + u];
+            vr.nm = *reinterpret_cast<const u4*>(vmeta + (t0 + 4 * lr) * 4);
         } else if constexpr (VT4) {
             const uint8_t* c = vcodes + (t0 / 32) * 2048 + 32 * l;
 #pragma unroll
@@ -361,7 +441,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int g = 0; g < 8; ++g) a16[g] *= 0.125f;
     }
-    if constexpr (!KU || !(VU || VT4)) {
+    // split V: the outlier and rest codebooks of N(0, 1/64) (tables at levels - 4)
+    float aO[kSo], aR[kSr];
+    if constexpr (VS) {
+        odd_coeffs<kBo>(p.mu64 + ((1 << kBo) - 4), aO);
+        odd_coeffs<kBo - 1>(p.mu64 + ((1 << (kBo - 1)) - 4), aR);
+    }
+    if constexpr (!KU || !(VU || VT4 || VS)) {
         const float m4 = mu4[0], m5 = mu4[1], m6 = mu4[2], m7 = mu4[3];
         al[0] = 0.25f * ((m5 - m4) + (m7 - m6));
         al[1] = 0.25f * ((m6 - m4) + (m7 - m5));
@@ -589,6 +675,17 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                         P[2][j] = pw * lo_h(vm[j].y);
                         P[3][j] = pw * hi_h(vm[j].y);
                     }
+                } else if constexpr (VS) {
+                    // outlier slots -p n_O a_S, then the rest's -p n_R a_S
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t nw = (j == 0) ? vr.nm.x : (j == 1) ? vr.nm.y : (j == 2) ? vr.nm.z : vr.nm.w;
+                        const float po = pj[mb][j] * lo_h(nw), pr = pj[mb][j] * hi_h(nw);
+#pragma unroll
+                        for (int g = 0; g < kSo; ++g) P[g][j] = -po * aO[g];
+#pragma unroll
+                        for (int g = 0; g < kSr; ++g) P[kSo + g][j] = -pr * aR[g];
+                    }
                 } else {
                     // weight of plane p = -p n a_p: the bit operands are -b = -(2 bit - 1)
 #pragma unroll
@@ -633,6 +730,15 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                         else
                             Bv = as_h8(centred8(vc[k][N >> 1][2 * (N & 1)], vc[k][N >> 1][2 * (N & 1) + 1]));
                         acc[N] = mfma16(Pg[N >> 1], Bv, acc[N]);
+                    }
+                } else if constexpr (VS) {
+                    // channels 0..63 (N < 4) are the outlier subset's positions, 64..127 the rest's
+#pragma unroll
+                    for (int N = 0; N < 8; ++N) {
+                        if (N < 4)
+                            acc[N] = pv_planes<kBo>(Pg, vr.w[k], N & 3, acc[N]);
+                        else
+                            acc[N] = pv_planes<kBo - 1>(Pg + kSo, vr.w[k] + kBo, N & 3, acc[N]);
                     }
                 } else if constexpr (VT4) {
                     // four planes; the cubic monomials are XORs of three (b_i b_j b_k = 2 (c_i ^
@@ -802,7 +908,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 template <int KT, int VT, int MB>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     // 8 waves where registers allow; the 4-bit TurboQuant V stages twice the P slots in LDS
-    constexpr int NW = (MB == 1 && !(KT == kU8 && VT == kU8) && VT != kTb4) ? 8 : 4;
+    constexpr int NW = (MB == 1 && !(KT == kU8 && VT == kU8) && VT != kTb4 && VT != kTs3 && VT != kTs4) ? 8 : 4;
     dim3 grid(p.n_splits_total, p.Hkv, p.batch);
     hipExtLaunchKernelGGL((decode_mfma_kernel<KT, VT, MB, NW>), grid, dim3(NW * 64), 0, s, ev0, ev1, 0, p);
     return hipGetLastError();
@@ -816,6 +922,8 @@ hipError_t launch_mb(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEv
 template <int KT>
 hipError_t launch_v(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const PlaneGeom& V = p.geom[1];
+    if (V.scheme == kTurboSplit)
+        return V.bits == 4 ? launch_mb<KT, kTs4>(p, s, ev0, ev1) : launch_mb<KT, kTs3>(p, s, ev0, ev1);
     if (V.scheme != kUniform) return V.bits == 4 ? launch_mb<KT, kTb4>(p, s, ev0, ev1) : launch_mb<KT, kTb>(p, s, ev0, ev1);
     return V.bits == 4 ? launch_mb<KT, kU4>(p, s, ev0, ev1) : launch_mb<KT, kU8>(p, s, ev0, ev1);
 }
@@ -826,7 +934,8 @@ bool mfma_path_supported(const DecodeParams& p) {
     const PlaneGeom& K = p.geom[0];
     const PlaneGeom& V = p.geom[1];
     const bool k_ok = (K.scheme == kUniform && (K.bits == 4 || K.bits == 8)) || K.scheme == kTurboQjl;
-    const bool v_ok = (V.scheme == kUniform && (V.bits == 4 || V.bits == 8)) || V.scheme == kTurboMse;
+    const bool v_ok = (V.scheme == kUniform && (V.bits == 4 || V.bits == 8)) || V.scheme == kTurboMse ||
+                      (V.scheme == kTurboSplit && (V.bits == 3 || V.bits == 4));
     return k_ok && v_ok && p.G <= kMaxGroupHeads;
 }
 

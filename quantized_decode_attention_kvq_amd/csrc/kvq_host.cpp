@@ -28,6 +28,7 @@ struct Plan {
     size_t plane_bytes[2];
     size_t slot_bytes;
     size_t off_signs, off_c, off_inv_c, off_S, off_ST, off_mu, off_theta, off_mu16, off_theta16;
+    size_t off_perm, off_mu64, off_theta64;
     size_t off_work, work_bytes;
     size_t off_planes, total;
 };
@@ -46,7 +47,8 @@ kvq_status check_config(const kvq_config* c) {
     if (c->fp32_window != 0 && c->fp32_window != kWindowMax) return KVQ_ERR_UNSUPPORTED;
     if (c->k_scheme != KVQ_UNIFORM && c->k_scheme != KVQ_TURBO_QJL && c->k_scheme != KVQ_Q8_0)
         return KVQ_ERR_UNSUPPORTED;
-    if (c->v_scheme != KVQ_UNIFORM && c->v_scheme != KVQ_TURBO_MSE && c->v_scheme != KVQ_Q8_0)
+    if (c->v_scheme != KVQ_UNIFORM && c->v_scheme != KVQ_TURBO_MSE && c->v_scheme != KVQ_Q8_0 &&
+        c->v_scheme != KVQ_TURBO_SPLIT)
         return KVQ_ERR_UNSUPPORTED;
     for (int t = 0; t < 2; ++t) {
         const int scheme = t == 0 ? c->k_scheme : c->v_scheme, bits = t == 0 ? c->k_bits : c->v_bits;
@@ -55,11 +57,14 @@ kvq_status check_config(const kvq_config* c) {
         if (scheme == KVQ_TURBO_QJL && bits != 3) return KVQ_ERR_UNSUPPORTED;
         // TurboQuant-MSE: 3-bit codes, or 4-bit codes for V ("Turbo4")
         if (scheme == KVQ_TURBO_MSE && bits != 3 && !(bits == 4 && t == 1)) return KVQ_ERR_UNSUPPORTED;
+        // outlier split (V only): 3 or 4 bits on the outlier half, one fewer on the rest
+        if (scheme == KVQ_TURBO_SPLIT && bits != 3 && bits != 4) return KVQ_ERR_UNSUPPORTED;
     }
     if ((c->rotate_k != 0 && c->rotate_k != 1) || (c->rotate_v != 0 && c->rotate_v != 1))
         return KVQ_ERR_INVALID_ARG;
     if (c->sinkhorn_iters > 1000) return KVQ_ERR_UNSUPPORTED;
-    if (c->sinkhorn_iters > 0 && (c->calib_tokens < 2 || c->calib_tokens > 65536))
+    if ((c->sinkhorn_iters > 0 || c->v_scheme == KVQ_TURBO_SPLIT) &&
+        (c->calib_tokens < 2 || c->calib_tokens > 65536))
         return KVQ_ERR_UNSUPPORTED;
     return KVQ_OK;
 }
@@ -80,6 +85,10 @@ PlaneGeom make_geom(const kvq_config* c, int tensor) {
     if (scheme == KVQ_UNIFORM) {
         g.codes_bytes = rows * 16 * (size_t)g.bits;
         g.meta_bytes = rows * 16;
+        g.qjl_bytes = 0;
+    } else if (scheme == KVQ_TURBO_SPLIT) {
+        g.codes_bytes = rows * 8 * (size_t)(2 * g.bits - 1); // bits + (bits - 1) planes of 8 B
+        g.meta_bytes = rows * 4;                             // two fp16 norms per token
         g.qjl_bytes = 0;
     } else {
         g.codes_bytes = rows * 16 * (size_t)g.bits; // b bit planes of 16 B per token-head
@@ -125,6 +134,12 @@ Plan make_plan(const kvq_config* c) {
     off = align_up(off + 16 * sizeof(float));
     p.off_theta16 = off;
     off = align_up(off + 16 * sizeof(float));
+    p.off_perm = off;
+    off = align_up(off + (size_t)c->n_layers * c->n_kv_heads * kDim * sizeof(int));
+    p.off_mu64 = off;
+    off = align_up(off + kSplitTable * sizeof(float));
+    p.off_theta64 = off;
+    off = align_up(off + kSplitTable * sizeof(float));
     const size_t partial = (size_t)c->max_batch * c->n_q_heads * kMaxSplits * kPartialFloats *
                            sizeof(float);
     // Sinkhorn work: the calibration block [2][Hkv][n][128], then two [2][Hkv][128] scale rows
@@ -167,13 +182,19 @@ struct kvq_cache {
     float* mu16() const { return reinterpret_cast<float*>(base + plan.off_mu16); }
     float* theta16() const { return reinterpret_cast<float*>(base + plan.off_theta16); }
     bool turbo4() const { return cfg.v_scheme == KVQ_TURBO_MSE && cfg.v_bits == 4; }
+    bool split() const { return cfg.v_scheme == KVQ_TURBO_SPLIT; }
+    int* perm() const { return reinterpret_cast<int*>(base + plan.off_perm); }
+    float* mu64() const { return reinterpret_cast<float*>(base + plan.off_mu64); }
+    float* theta64() const { return reinterpret_cast<float*>(base + plan.off_theta64); }
+    size_t perm_off(int layer) const { return (size_t)layer * cfg.n_kv_heads * kDim; }
     char* layer_base(int layer) const {
         return base + plan.off_planes + (size_t)layer * cfg.max_batch * cfg.n_kv_heads * plan.slot_bytes;
     }
     size_t table_off(int layer) const { return (size_t)layer * cfg.n_kv_heads * 2 * kDim; }
     bool needs_signs() const { return plan.geom[0].rotate || plan.geom[1].rotate; }
     bool needs_S() const { return cfg.k_scheme == KVQ_TURBO_QJL; }
-    bool needs_calib() const { return plan.geom[0].sinkhorn || plan.geom[1].sinkhorn; }
+    bool needs_sinkhorn() const { return plan.geom[0].sinkhorn || plan.geom[1].sinkhorn; }
+    bool needs_calib() const { return needs_sinkhorn() || split(); }
     bool turbo() const { return cfg.k_scheme == KVQ_TURBO_QJL || cfg.v_scheme == KVQ_TURBO_MSE; }
 };
 
@@ -248,8 +269,11 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, 
         if (e == hipSuccess) e = launch_fill(c->inv_c(), n, 1.0f, s);
         if (e == hipSuccess) e = launch_fill(c->signs(), n, 1.0f, s);
     }
-    if (e == hipSuccess && c->turbo()) e = launch_codebook(c->mu(), c->theta(), kLloydIters, 8, s);
-    if (e == hipSuccess && c->turbo4()) e = launch_codebook(c->mu16(), c->theta16(), kLloydIters, 16, s);
+    if (e == hipSuccess && c->turbo()) e = launch_codebook(c->mu(), c->theta(), kLloydIters, 8, 128, s);
+    if (e == hipSuccess && c->turbo4()) e = launch_codebook(c->mu16(), c->theta16(), kLloydIters, 16, 128, s);
+    // split V: the 4-, 8- and 16-level codebooks of N(0, 1/64), table offset levels - 4
+    for (int levels = 4; levels <= 16 && e == hipSuccess && c->split(); levels *= 2)
+        e = launch_codebook(c->mu64() + (levels - 4), c->theta64() + (levels - 4), kLloydIters, levels, 64, s);
     if (e != hipSuccess) {
         delete c;
         return KVQ_ERR_DEVICE;
@@ -300,6 +324,7 @@ kvq_status kvq_calibrate(kvq_cache* c, int layer, const void* Kc, const void* Vc
         if (src[t] && !aligned16(src[t])) return KVQ_ERR_MISALIGNED;
         p.src[t] = src[t];
     }
+    if (c->split() && !Vc) return KVQ_ERR_INVALID_ARG;
     if (c->needs_signs() && !c->tables_set) return KVQ_ERR_NOT_READY;
     p.work = reinterpret_cast<double*>(c->base + c->plan.off_work);
     p.signs = c->signs() + c->table_off(layer);
@@ -309,7 +334,17 @@ kvq_status kvq_calibrate(kvq_cache* c, int layer, const void* Kc, const void* Vc
     p.n = n_tokens;
     p.Hkv = c->cfg.n_kv_heads;
     p.iters = c->cfg.sinkhorn_iters;
-    const hipError_t e = launch_calibrate(p, static_cast<hipStream_t>(stream));
+    hipError_t e = hipSuccess;
+    if (c->needs_sinkhorn()) e = launch_calibrate(p, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess && c->split()) {
+        OutlierParams op{};
+        op.src = Vc;
+        op.perm = c->perm() + c->perm_off(layer);
+        op.dtype = dtype;
+        op.n = n_tokens;
+        op.Hkv = c->cfg.n_kv_heads;
+        e = launch_select_outliers(op, static_cast<hipStream_t>(stream));
+    }
     if (e != hipSuccess) return dev_fail(c, e);
     c->calibrated[(size_t)layer] = 1;
     return KVQ_OK;
@@ -346,6 +381,9 @@ kvq_status make_quant(kvq_cache* c, int layer, const void* K, const void* V, int
     p.theta = c->theta();
     p.mu16 = c->mu16();
     p.theta16 = c->theta16();
+    p.perm = c->perm() + c->perm_off(layer);
+    p.mu64 = c->mu64();
+    p.theta64 = c->theta64();
     p.dtype = dtype;
     p.T = n_tokens;
     p.batch = batch;
@@ -386,6 +424,8 @@ kvq_status make_decode(const kvq_cache* c, int layer, const void* q, int dtype, 
     p.qjl_st = c->ST();
     p.mu = c->mu();
     p.mu16 = c->mu16();
+    p.perm = c->perm() + c->perm_off(layer);
+    p.mu64 = c->mu64();
     p.partials = reinterpret_cast<float*>(c->base + c->plan.off_work);
     p.dtype = dtype;
     p.batch = batch;
@@ -404,7 +444,8 @@ kvq_status make_decode(const kvq_cache* c, int layer, const void* q, int dtype, 
     }
     matrix = c->decode_path != 1 && mfma_path_supported(p);
     if (c->decode_path == 2 && !matrix) return KVQ_ERR_UNSUPPORTED;
-    if (!matrix && c->turbo4()) return KVQ_ERR_UNSUPPORTED; // 4-bit TurboQuant V: matrix path only
+    // 4-bit and split TurboQuant V: matrix path only
+    if (!matrix && (c->turbo4() || c->split())) return KVQ_ERR_UNSUPPORTED;
     int st;
     if (c->split_tokens_opt > 0) {
         st = c->split_tokens_opt;
@@ -633,6 +674,9 @@ kvq_status kvq_get_tables(const kvq_cache* c, kvq_tables* out) {
     out->theta = c->theta();
     out->mu16 = c->mu16();
     out->theta16 = c->theta16();
+    out->perm = c->perm();
+    out->mu64 = c->mu64();
+    out->theta64 = c->theta64();
     return KVQ_OK;
 }
 

@@ -17,7 +17,12 @@ constexpr int kPartialFloats = 132; // m, l, pad, pad, acc[128] per (sequence, q
 constexpr int kWindowMax = 128;
 constexpr int kWinSplitsMatrix = 1; // FP32-window workgroups per (sequence, kv head), matrix path
 
-enum Scheme { kUniform = 0, kTurboQjl = 1, kTurboMse = 2 };
+// kTurboSplit: TurboQuant-MSE V with the outlier-channel split (the public KVQ_TURBO_SPLIT);
+// bits = the outlier subset's code bits (3 or 4), the other 64 channels take one bit fewer
+enum Scheme { kUniform = 0, kTurboQjl = 1, kTurboMse = 2, kTurboSplit = 4 };
+// Split-coder codebooks for N(0, 1/64) with L = 4, 8, 16 levels start at float L - 4 of the
+// 28-float tables (centroids; thresholds likewise, L - 1 of L used)
+constexpr int kSplitTable = 28;
 
 // Geometry of one tensor's plane inside a (layer, seq, head) slot.
 struct PlaneGeom {
@@ -42,6 +47,9 @@ struct QuantParams {
     const float* theta;       // [8], 7 used
     const float* mu16;        // [16]: 4-bit TurboQuant-MSE V codebook
     const float* theta16;     // [16], 15 used
+    const int* perm;          // layer base [Hkv][128]: channel at each position (split V)
+    const float* mu64;        // [kSplitTable] split codebooks
+    const float* theta64;     // [kSplitTable]
     int dtype, T, batch, Hkv, window;
     int groups8;              // 8-token groups per (sequence) unit range (max over sequences)
     int start[kMaxBatch];     // length before this append, per sequence
@@ -60,6 +68,8 @@ struct DecodeParams {
     const float* qjl_st;      // [128 j][128 i]
     const float* mu;
     const float* mu16;        // [16]: 4-bit TurboQuant-MSE V codebook
+    const int* perm;          // layer base [Hkv][128] (split V)
+    const float* mu64;        // [kSplitTable] split codebooks
     float* partials;          // [batch][Hq][n_splits_total][kPartialFloats]
     int dtype, batch, Hq, Hkv, G, window;
     float qscale;             // softmax scale * log2(e)
@@ -101,6 +111,14 @@ struct CalibParams {
     int dtype, n, Hkv, iters;
 };
 
+// Outlier selection of a split V plane: per kv head, the 64 channels of largest energy over the
+// n calibration tokens ([n][Hkv][128] of dtype), written as perm [Hkv][128].
+struct OutlierParams {
+    const void* src;
+    int* perm;                // layer base
+    int dtype, n, Hkv;
+};
+
 // Launchers (defined in the .hip files); return the launch's hipError_t.
 hipError_t launch_quantize(const QuantParams& p, hipStream_t s);
 // Lane-dense quantizer for many tokens per call (same bytes as launch_quantize).
@@ -112,7 +130,9 @@ constexpr int kQuantBulkQjlBlocks = 256;
 // Smallest append the bulk quantizer takes.
 constexpr int kQuantBulkMinTokens = 16;
 hipError_t launch_calibrate(const CalibParams& p, hipStream_t s);
-hipError_t launch_codebook(float* mu, float* theta, int iters, int levels, hipStream_t s);
+hipError_t launch_select_outliers(const OutlierParams& p, hipStream_t s);
+// Lloyd-Max codebook with `levels` levels for coordinates of unit vectors in `dim` dimensions.
+hipError_t launch_codebook(float* mu, float* theta, int iters, int levels, int dim, hipStream_t s);
 hipError_t launch_transpose128(const float* in, float* out, hipStream_t s);
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t s);
 // The split-K launchers take optional events bound to the kernel's dispatch (measurement).

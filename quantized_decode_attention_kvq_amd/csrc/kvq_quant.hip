@@ -37,6 +37,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
     qdev::quantize_wave(p, blockIdx.z & 1, blockIdx.z >> 1, blockIdx.y, blockIdx.x * 4 + wave, rbuf[wave]);
 }
 
+// The same quantizer for one tensor only (blockIdx.z = sequence): the bulk path of the split V
+// coder, whose channel gather goes through the wave's LDS row.
+__global__ __launch_bounds__(256) void quantize_one_kernel(QuantParams p, int tensor) {
+    __shared__ float rbuf[4][kDim];
+    const int wave = threadIdx.x >> 6;
+    qdev::quantize_wave(p, tensor, blockIdx.z, blockIdx.y, blockIdx.x * 4 + wave, rbuf[wave]);
+}
+
 // Bulk quantizer of one TurboQuant tensor (QJL: TurboQuant-QJL K, else TurboQuant-MSE).  Wave
 // w of workgroup x takes octets 4x + w, then every 4 * gridDim.x-th after it, of one (sequence,
 // kv head), requesting the next octet's source before quantizing the current one.  QJL
@@ -287,7 +295,7 @@ __device__ double mass_d(double a, double b, bool b_inf) {
     return 0.5 * (erfc(a / sqrt(2.0)) - eb);
 }
 
-__global__ void codebook_kernel(float* mu, float* theta, int iters, int levels) {
+__global__ void codebook_kernel(float* mu, float* theta, int iters, int levels, int dim) {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
     const int h = levels / 2;
     double m[8];
@@ -304,7 +312,7 @@ __global__ void codebook_kernel(float* mu, float* theta, int iters, int levels) 
         }
         for (int k = 0; k < h; ++k) m[k] = nm[k];
     }
-    const double r = sqrt(128.0);
+    const double r = sqrt((double)dim);
     for (int k = 0; k < h; ++k) {
         const float f = (float)(m[k] / r);
         mu[h + k] = f;
@@ -318,6 +326,36 @@ __global__ void codebook_kernel(float* mu, float* theta, int iters, int levels) 
         theta[h - 1 - k] = -f;
     }
     theta[levels - 1] = 0.0f;
+}
+
+// Outlier channels of one kv head's calibration tokens (TurboQuant split): thread d sums
+// x[t][d]^2 in binary64 in token order (each square is exact), then ranks its channel against
+// the others (larger energy first, ties to the smaller index); the top 64 go to positions
+// 0..63 in ascending channel order, the rest to 64..127.
+__global__ __launch_bounds__(128) void select_outliers_kernel(OutlierParams p) {
+    __shared__ double s_e[kDim];
+    __shared__ int s_out[kDim];
+    const int head = blockIdx.x, d = threadIdx.x;
+    double acc = 0.0;
+    for (int t = 0; t < p.n; ++t) {
+        const size_t i = ((size_t)t * p.Hkv + head) * kDim + d;
+        const double v = p.dtype == 0 ? (double)static_cast<const float*>(p.src)[i]
+                                      : (double)qdev::bf16_to_f32(static_cast<const uint16_t*>(p.src)[i]);
+        acc = acc + v * v;
+    }
+    s_e[d] = acc;
+    __syncthreads();
+    int rank = 0;
+    for (int i = 0; i < kDim; ++i) {
+        const double e = s_e[i];
+        rank += (e > acc || (e == acc && i < d)) ? 1 : 0;
+    }
+    const int out = rank < kDim / 2 ? 1 : 0;
+    s_out[d] = out;
+    __syncthreads();
+    int pos = out ? 0 : kDim / 2;
+    for (int i = 0; i < d; ++i) pos += (s_out[i] == out) ? 1 : 0;
+    p.perm[(size_t)head * kDim + pos] = d;
 }
 
 __global__ void fill_kernel(float* p, size_t n, float v) {
@@ -393,6 +431,10 @@ hipError_t launch_bulk_scheme(int scheme, const QuantParams& p, hipStream_t s, i
     switch (scheme) {
     case kUniform: return launch_uniform_bulk_for(p.geom[tensor0], p, s, tensor0, n_tensors);
     case kTurboQjl: return launch_turbo_bulk<true>(p, s, tensor0);
+    case kTurboSplit:
+        hipLaunchKernelGGL(quantize_one_kernel, dim3((p.groups8 + 3) / 4, p.Hkv, p.batch), dim3(256), 0, s, p,
+                           tensor0);
+        return hipGetLastError();
     default:
         if (p.geom[tensor0].bits == 4) return launch_turbo4v_bulk(p, s); // V only
         return launch_turbo_bulk<false>(p, s, tensor0);
@@ -425,8 +467,13 @@ hipError_t launch_calibrate(const CalibParams& p, hipStream_t s) {
     return e;
 }
 
-hipError_t launch_codebook(float* mu, float* theta, int iters, int levels, hipStream_t s) {
-    hipLaunchKernelGGL(codebook_kernel, dim3(1), dim3(64), 0, s, mu, theta, iters, levels);
+hipError_t launch_codebook(float* mu, float* theta, int iters, int levels, int dim, hipStream_t s) {
+    hipLaunchKernelGGL(codebook_kernel, dim3(1), dim3(64), 0, s, mu, theta, iters, levels, dim);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_outliers(const OutlierParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(select_outliers_kernel, dim3(p.Hkv), dim3(kDim), 0, s, p);
     return hipGetLastError();
 }
 

@@ -105,6 +105,24 @@ __device__ __forceinline__ void rotate_signed(float& a, float& b, float s0, floa
     b = b * c0f();
 }
 
+// 64-point R64(x) = (1/8) H64 (d .* x) on each half of the wave (lanes 0-31: positions 0..63,
+// lanes 32-63: positions 64..127): the butterflies of hadamard_wave without the last span.
+__device__ __forceinline__ void rotate64_signed(float& a, float& b, float s0, float s1) {
+    const int l = lane_id();
+    if (s0 < 0.0f) a = -a;
+    if (s1 < 0.0f) b = -b;
+    const float s = a + b, d = a - b;
+    a = s;
+    b = d;
+    hadamard_step<1>(a, b, l);
+    hadamard_step<2>(a, b, l);
+    hadamard_step<4>(a, b, l);
+    hadamard_step<8>(a, b, l);
+    hadamard_step<16>(a, b, l);
+    a = a * 0.125f;
+    b = b * 0.125f;
+}
+
 // Index-order pairwise sum of v^2 over the 128 elements (level 1 inside the lane, then lane
 // pairs at distance 1, 2, ..., 32); every lane returns the total.
 __device__ __forceinline__ float tree_sum_sq(float a, float b) {
@@ -221,6 +239,13 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
         ic0 = ic_l[0];
         ic1 = ic_l[1];
     }
+    // split V: this lane codes positions 2l, 2l+1, i.e. channels perm[2l], perm[2l+1]
+    int pm0 = 0, pm1 = 0;
+    if (G.scheme == kTurboSplit) {
+        const int2 pm = reinterpret_cast<const int2*>(p.perm + (size_t)head * kDim)[l];
+        pm0 = pm.x;
+        pm1 = pm.y;
+    }
 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -274,6 +299,44 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
                     m[4 + g] = z16;
                 }
             }
+        } else if (G.scheme == kTurboSplit) {
+            // outlier split: gather the lane's two positions through the wave's LDS row, then
+            // per half of the wave rho = R64(x_h), n_h = fp16(|rho|), codes = #thresholds of the
+            // half's codebook (outliers G.bits bits, the rest one fewer) below rho / n_h
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            rbuf[2 * l] = a;
+            rbuf[2 * l + 1] = c;
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            a = rbuf[pm0];
+            c = rbuf[pm1];
+            rotate64_signed(a, c, sg0, sg1);
+            const float nsq = xor_reduce<32>(a * a + c * c, [](float x, float y) { return x + y; });
+            const uint16_t n16 = f16_rn(sqrtf(nsq));
+            const float n = f16_val(n16);
+            const float inv = (n > 0.0f) ? 1.0f / n : 0.0f;
+            const float ua = a * inv, uc = c * inv;
+            const int levels = (l < 32) ? (1 << G.bits) : (1 << (G.bits - 1));
+            const float* th = p.theta64 + (levels - 4);
+            uint32_t qa = 0, qc = 0;
+#pragma unroll
+            for (int k = 0; k < 15; ++k) {
+                if (k < levels - 1) {
+                    const float thk = th[k];
+                    qa += (ua > thk) ? 1u : 0u;
+                    qc += (uc > thk) ? 1u : 0u;
+                }
+            }
+            const int i = t % 8, N = l >> 3;
+            const uint32_t pos = 1u << (16 * (i & 1) + 4 * (N & 3) + (i >> 1));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                tv_a[k] |= ((qa >> k) & 1u) ? pos : 0u;
+                tv_c[k] |= ((qc >> k) & 1u) ? pos : 0u;
+            }
+            tv_mask |= pos;
+            if ((l & 31) == 0) reinterpret_cast<uint16_t*>(meta)[2 * t + (l >> 5)] = n16;
         } else {
             // TurboQuant code: rho = R(x); n = fp16(|rho|); codes = #thresholds below rho/n;
             // residual r = rho - n mu[code]; QJL bits = sign(S r) with a sequential fma chain.
@@ -375,7 +438,20 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
             tv_c[k] |= xor_lane<8>(tv_c[k]);
             tv_c[k] |= xor_lane<16>(tv_c[k]);
         }
-        if (((l >> 3) & 3) == 0) {
+        if (((l >> 3) & 3) == 0 && G.scheme == kTurboSplit) {
+            // W = 2 bits - 1 words per (octet, lane column): the outlier planes, then the rest's
+            const int W = 2 * G.bits - 1, o = (t_lo % 32) / 8, n0 = 2 * (l & 7);
+            const int first = (l < 32) ? 0 : G.bits, nb = (l < 32) ? G.bits : G.bits - 1;
+            uint32_t* blk = reinterpret_cast<uint32_t*>(codes + (size_t)(t_lo / 32) * (256 * W));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (k >= nb) break;
+                uint32_t* wa = blk + W * (16 * o + n0) + first + k;
+                uint32_t* wc = wa + W;
+                *wa = (*wa & ~m) | tv_a[k];
+                *wc = (*wc & ~m) | tv_c[k];
+            }
+        } else if (((l >> 3) & 3) == 0) {
             const int b = G.bits; // bit planes
             const int o = (t_lo % 32) / 8, n0 = 2 * (l & 7), N = l >> 3;
             uint32_t* blk = reinterpret_cast<uint32_t*>(codes + (size_t)(t_lo / 32) * (512 * b));

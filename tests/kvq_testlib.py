@@ -50,7 +50,7 @@ class Case:
                 torch.from_numpy(np.ascontiguousarray(self.signs)).to(device),
                 torch.from_numpy(self.S).to(device))
         self.calib = {}
-        if wl.sinkhorn_iters > 0:
+        if wl.sinkhorn_iters > 0 or wl.v_scheme == W.TURBO_SPLIT:
             for li, layer in enumerate(self.layers):
                 kc = W.gen_calib(wl, layer, 0, device=self.gen_device).to(device)
                 vc = W.gen_calib(wl, layer, 1, device=self.gen_device).to(device)
@@ -97,7 +97,13 @@ class Case:
             X = self.calib[layer][tensor][:, head, :]
             c, inv_c = oracle.sinkhorn(X, kw.get("signs"), wl.sinkhorn_iters)
             kw["c"], kw["inv_c"] = c, inv_c
-        if W.is_turbo(scheme):
+        if scheme == W.TURBO_SPLIT:
+            # outlier split: channels from the calibration block, codebooks of N(0, 1/64)
+            bo = wl.v_bits
+            kw["perm"] = oracle.select_outliers(self.calib[layer][1][:, head, :])
+            _, kw["mu"], kw["theta"], _ = _codebook64(1 << bo)
+            _, kw["mu2"], kw["theta2"], _ = _codebook64(1 << (bo - 1))
+        elif W.is_turbo(scheme):
             bits = wl.k_bits if tensor == 0 else wl.v_bits
             if bits == 4:  # 4-bit TurboQuant-MSE V: the 16-level codebook
                 _, mu, theta, _ = _codebook16()
@@ -137,6 +143,13 @@ def compare_plane(dev, orc: oracle.Plane, label=""):
 
 
 _CB16 = None
+_CB64 = {}
+
+
+def _codebook64(levels):
+    if levels not in _CB64:
+        _CB64[levels] = oracle.lloyd_max(oracle.LLOYD_ITERS, levels, 64)
+    return _CB64[levels]
 
 
 def _codebook16():

@@ -56,6 +56,11 @@ def test_required_bytes_match_format():
     npg = K.kvq_cache_required_bytes(_cfg(wlp))
     pp = 28 * 8 * (131072 * 160 + 2 * 128 * 512)
     assert pp <= npg <= pp + 16 * 2 ** 20
+    # split V (2.5 / 3.5 bits): 40 / 56 B codes + 4 B norms per token-head, K q8_0 at 144 B
+    for wls, vb in ((W.LLAMA8B_32K_Q8_0_TURBO25_V, 44), (W.LLAMA8B_32K_Q8_0_TURBO35_V, 60)):
+        ns = K.kvq_cache_required_bytes(_cfg(wls))
+        ps = 32 * 8 * 32768 * (144 + vb)
+        assert ps <= ns <= ps + 16 * 2 ** 20
 
 
 @pytest.mark.parametrize("over,status", [
@@ -63,6 +68,9 @@ def test_required_bytes_match_format():
     (dict(fp32_window=64), 2), (dict(n_q_heads=25), 1), (dict(n_q_heads=8 * 9), 2),
     (dict(max_batch=65), 2), (dict(max_batch=0), 1), (dict(k_scheme=2), 2), (dict(v_scheme=1), 2),
     (dict(rotate_k=2), 1), (dict(n_layers=0), 1), (dict(sinkhorn_iters=5, calib_tokens=1), 2),
+    # the outlier split is a V coder with 3 or 4 outlier bits, and needs a calibration block
+    (dict(k_scheme=4, k_bits=3), 2), (dict(v_scheme=4, v_bits=2, calib_tokens=512), 2),
+    (dict(v_scheme=4, v_bits=5, calib_tokens=512), 2), (dict(v_scheme=4, v_bits=3, calib_tokens=0), 2),
 ])
 def test_invalid_configs_rejected(over, status):
     with pytest.raises(K.KvqError) as e:

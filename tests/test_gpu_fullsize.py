@@ -93,3 +93,9 @@ def test_fullsize_llama3b_128k_progressive_b8():
 @pytest.mark.parametrize("wl", [W.DENSE27B_120K_KVARN, W.DENSE27B_120K_U8], ids=lambda w: w.name)
 def test_fullsize_dense27b_120k_b4(wl):
     _run(wl, layers=[0, 63], seqs=[0, 3], plane_heads=[0, 7], attn_heads=[0, 7])
+
+
+@pytest.mark.parametrize("wl", [W.LLAMA8B_32K_Q8_0_TURBO25_V, W.LLAMA8B_32K_Q8_0_TURBO35_V],
+                         ids=lambda w: w.name)
+def test_fullsize_llama8b_32k_turbo_split_v(wl):
+    _run(wl, layers=[0, 31], seqs=[0], plane_heads=[0, 4, 7], attn_heads=[0, 4, 7])

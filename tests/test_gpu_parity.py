@@ -36,8 +36,8 @@ def _check_all_planes(case, li, heads=None, seqs=None):
 
 
 def _paths(wl):
-    if wl.v_scheme == W.TURBO_MSE and wl.v_bits == 4:
-        return (2,)  # 4-bit TurboQuant V: matrix-core kernel only
+    if (wl.v_scheme == W.TURBO_MSE and wl.v_bits == 4) or wl.v_scheme == W.TURBO_SPLIT:
+        return (2,)  # 4-bit and split TurboQuant V: matrix-core kernel only
     return (1, 2)  # vector-ALU kernel, matrix-core kernel
 
 
@@ -82,7 +82,8 @@ def test_progressive_3970_full():
 
 
 @pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_TURBO, W.LLAMA3B_32K_TURBO_ASYM,
-                                W.LLAMA3B_32K_Q8_0_TURBO_V, W.DENSE27B_120K_Q8_0, W.LLAMA3B_32K_Q8_0_TURBO4_V],
+                                W.LLAMA3B_32K_Q8_0_TURBO_V, W.DENSE27B_120K_Q8_0, W.LLAMA3B_32K_Q8_0_TURBO4_V,
+                                W.LLAMA8B_32K_Q8_0_TURBO25_V, W.LLAMA8B_32K_Q8_0_TURBO35_V],
                          ids=lambda w: w.name)
 def test_prefill_equals_appends_bytewise(wl):
     _say("case: prefill == appends,", wl.name, "n=300")
@@ -107,7 +108,8 @@ RAGGED_CALLS = [(3, 21), (1, 5), (2, 3), (3, 37), (1, 16), (3, 130)]
 
 @pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_KVARN, W.LLAMA3B_32K_TURBO,
                                 W.LLAMA3B_32K_TURBO_ASYM, W.DENSE27B_120K_U8, W.DENSE27B_120K_Q8_0,
-                                W.LLAMA3B_32K_Q8_0_TURBO_V, W.LLAMA3B_32K_Q8_0_TURBO4_V],
+                                W.LLAMA3B_32K_Q8_0_TURBO_V, W.LLAMA3B_32K_Q8_0_TURBO4_V,
+                                W.LLAMA8B_32K_Q8_0_TURBO25_V, W.LLAMA8B_32K_Q8_0_TURBO35_V],
                          ids=lambda w: w.name)
 def test_prefill_ragged_batch_bytewise(wl):
     """Prefill calls over a batch whose sequences start at different lengths leave exactly the
@@ -211,6 +213,62 @@ def test_q8_0_k_turbo4_mse_v_small():
         case.cache.attn_decode(0, q, out)
     assert e.value.name == "KVQ_ERR_UNSUPPORTED"
     case.cache.set_option(2, 0)
+
+
+@pytest.mark.parametrize("wl", [W.LLAMA8B_32K_Q8_0_TURBO25_V, W.LLAMA8B_32K_Q8_0_TURBO35_V],
+                         ids=lambda w: w.name)
+def test_turbo_split_v_small(wl):
+    # TurboQuant's fractional bit widths (outlier-channel split): the device's outlier choice per
+    # kv head equals the oracle's from the same calibration block, its N(0, 1/64) codebooks equal
+    # the oracle's bit for bit, the planes byte for byte (bulk prefill and appends), and attention
+    _say("case:", wl.name, "2 layers, 300 prefill + 45 appends")
+    case = Case(wl, 345, layers=[0, 7])
+    for li, layer in enumerate(case.layers):
+        k, v = case.kv(layer)
+        case.cache.prefill_quantize(li, k[:, :300].contiguous(), v[:, :300].contiguous())
+        for t in range(300, 345):
+            case.cache.append(li, k[:, t].contiguous(), v[:, t].contiguous())
+    torch.cuda.synchronize()
+    perm = case.cache.table("perm", 2 * 8 * 128).cpu().numpy().reshape(2, 8, 128)
+    for li, layer in enumerate(case.layers):
+        for h in range(8):
+            ref = oracle.select_outliers(case.calib[layer][1][:, h, :])
+            assert np.array_equal(perm[li, h], ref), (li, h)
+    mu64 = case.cache.table("mu64", 28).cpu().numpy()
+    th64 = case.cache.table("theta64", 28).cpu().numpy()
+    for levels in (4, 8, 16):
+        _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS, levels, 64)
+        o = levels - 4
+        assert np.array_equal(mu64[o:o + levels].view(np.uint32), mu.view(np.uint32)), levels
+        assert np.array_equal(th64[o:o + levels - 1].view(np.uint32), theta.view(np.uint32)), levels
+    for li in range(2):
+        planes = _check_all_planes(case, li)
+        _decode_and_compare(case, li, planes)
+    case.cache.set_option(2, 1)
+    q = W.gen_q(wl, 0, 0).to("cuda")
+    out = torch.zeros((1, wl.n_q_heads, 128), device="cuda")
+    with pytest.raises(case.K.KvqError) as e:
+        case.cache.attn_decode(0, q, out)
+    assert e.value.name == "KVQ_ERR_UNSUPPORTED"
+    case.cache.set_option(2, 0)
+
+
+def test_turbo_split_v_requires_calibration():
+    # appending to a split V before kvq_calibrate has chosen its outlier channels is refused
+    wl = W.LLAMA8B_32K_Q8_0_TURBO25_V
+    import quantized_decode_attention_kvq_amd as K
+    cache = K.KvCache(device="cuda", **wl.kvq_config(max_context=128))
+    cache.set_random_tables(torch.from_numpy(np.ascontiguousarray(W.rotation_signs(wl))).cuda(),
+                            torch.from_numpy(W.qjl_projection(wl)).cuda())
+    k = W.gen_kv(wl, 0, 0, 4).cuda()
+    v = W.gen_kv(wl, 0, 1, 4).cuda()
+    with pytest.raises(K.KvqError) as e:
+        cache.prefill_quantize(0, k, v)
+    assert e.value.name == "KVQ_ERR_NOT_READY"
+    with pytest.raises(K.KvqError) as e:  # the split takes its outliers from V's block
+        cache.calibrate(0, W.gen_calib(wl, 0, 0, device="cuda"), None)
+    assert e.value.name == "KVQ_ERR_INVALID_ARG"
+    assert cache.length(0, 0) == 0
 
 
 def test_q8_0_k_turbo_mse_v_small():
@@ -411,7 +469,8 @@ def _planes_equal(a, b, li, batch, n_heads):
                                   (W.LLAMA3B_32K_KVARN, 1023), (W.LLAMA3B_32K_TURBO, 700),
                                   (W.LLAMA3B_32K_TURBO_ASYM, 64), (W.DENSE27B_120K_KVARN, 500),
                                   (W.LLAMA3B_32K_Q8_0_TURBO_V, 130), (W.DENSE27B_120K_Q8_0, 65),
-                                  (W.LLAMA3B_32K_Q8_0_TURBO4_V, 200)],
+                                  (W.LLAMA3B_32K_Q8_0_TURBO4_V, 200), (W.LLAMA8B_32K_Q8_0_TURBO25_V, 190),
+                                  (W.LLAMA8B_32K_Q8_0_TURBO35_V, 64)],
                          ids=lambda x: x.name if hasattr(x, "name") else str(x))
 def test_fused_append_decode_equals_separate_calls(wl, n, path):
     # kvq_append_attn_decode == kvq_append + kvq_attn_decode: byte-identical planes and

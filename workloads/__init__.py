@@ -19,13 +19,13 @@ from typing import Optional
 import numpy as np
 import torch
 
-UNIFORM, TURBO_QJL, TURBO_MSE, Q8_0 = 0, 1, 2, 3
+UNIFORM, TURBO_QJL, TURBO_MSE, Q8_0, TURBO_SPLIT = 0, 1, 2, 3, 4
 D = 128
 
 
 def is_turbo(scheme: int) -> bool:
     """TurboQuant planes (rotation implied, Lloyd-Max codes); the others use the uniform layout."""
-    return scheme in (TURBO_QJL, TURBO_MSE)
+    return scheme in (TURBO_QJL, TURBO_MSE, TURBO_SPLIT)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -100,10 +100,21 @@ LLAMA3B_32K_Q8_0_TURBO_V = Workload(
 LLAMA3B_32K_Q8_0_TURBO4_V = Workload(
     "llama3b-28layer-32k-q8_0-k-turbo4mse-v", 28, 24, 8, 1, 32768, Q8_0, TURBO_MSE, 8, 4, 0,
     False, True, 0, 0, "f32", "outliers8x8", 1003)
+# TurboQuant's fractional bit widths on the Llama-3.1-8B attention shape (32 layers, 32 query
+# heads, 8 KV heads): V with the outlier-channel split at 2.5 bits (3 on the 64 outlier channels,
+# 2 on the rest) and 3.5 bits (4 / 3), K kept at Q8; the outlier channels come from a 512-token
+# calibration block of the same per-channel distribution
+LLAMA8B_32K_Q8_0_TURBO25_V = Workload(
+    "llama8b-32layer-32k-q8_0-k-turbo2.5split-v", 32, 32, 8, 1, 32768, Q8_0, TURBO_SPLIT, 8, 3, 0,
+    False, True, 0, 512, "f32", "outliers8x8", 1006)
+LLAMA8B_32K_Q8_0_TURBO35_V = Workload(
+    "llama8b-32layer-32k-q8_0-k-turbo3.5split-v", 32, 32, 8, 1, 32768, Q8_0, TURBO_SPLIT, 8, 4, 0,
+    False, True, 0, 512, "f32", "outliers8x8", 1006)
 
 ALL = [LLAMA3B_3970_PROGRESSIVE, LLAMA3B_32K_KVARN, LLAMA3B_32K_TURBO, LLAMA3B_32K_TURBO_ASYM,
        LLAMA3B_128K_PROGRESSIVE, DENSE27B_120K_KVARN, DENSE27B_120K_U8, DENSE27B_120K_Q8_0,
-       LLAMA3B_32K_Q8_0_TURBO_V, LLAMA3B_32K_Q8_0_TURBO4_V]
+       LLAMA3B_32K_Q8_0_TURBO_V, LLAMA3B_32K_Q8_0_TURBO4_V, LLAMA8B_32K_Q8_0_TURBO25_V,
+       LLAMA8B_32K_Q8_0_TURBO35_V]
 BY_NAME = {w.name: w for w in ALL}
 
 TAGS = {"kv": 1, "calib": 2, "q": 3, "signs": 4, "qjl": 5, "chan": 6, "step": 7}
