@@ -907,8 +907,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 
 template <int KT, int VT, int MB>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    // 8 waves where registers allow; the 4-bit TurboQuant V stages twice the P slots in LDS
-    constexpr int NW = (MB == 1 && !(KT == kU8 && VT == kU8) && VT != kTb4 && VT != kTs3 && VT != kTs4) ? 8 : 4;
+    // 8 waves where registers allow; the 4-bit TurboQuant V stages twice the P slots in LDS and
+    // the 3.5-bit split V three times (12 slots: 8 waves would need 221 KiB)
+    constexpr int NW = (MB == 1 && !(KT == kU8 && VT == kU8) && VT != kTb4 && VT != kTs4) ? 8 : 4;
     dim3 grid(p.n_splits_total, p.Hkv, p.batch);
     hipExtLaunchKernelGGL((decode_mfma_kernel<KT, VT, MB, NW>), grid, dim3(NW * 64), 0, s, ev0, ev1, 0, p);
     return hipGetLastError();
