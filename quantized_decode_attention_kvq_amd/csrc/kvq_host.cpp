@@ -623,6 +623,8 @@ kvq_status kvq_attn_prefill(kvq_cache* c, int layer, const void* q, int dtype, f
     fill_params_common(c, layer, p.layer_base, p.seq_stride, p.head_stride, p.plane_off, p.geom);
     p.signs = c->signs() + c->table_off(layer);
     p.cs = c->cs() + c->table_off(layer);
+    p.mu = c->mu();
+    p.mu16 = c->mu16();
     p.dtype = dtype;
     p.batch = batch;
     p.n_q = n_q;

@@ -95,6 +95,8 @@ struct PrefillParams {
     PlaneGeom geom[2];
     const float* signs;       // layer base [Hkv][2][128]
     const float* cs;          // layer base [Hkv][2][128] Sinkhorn c
+    const float* mu;          // [8]: TurboQuant-MSE V codebook (3-bit)
+    const float* mu16;        // [16]: 4-bit TurboQuant-MSE V codebook
     int dtype, batch, n_q, Hq, Hkv, G, window;
     int n_splits;             // key splits per row (1: the attention kernel writes out itself)
     float qscale;             // softmax scale * log2(e)

@@ -82,6 +82,10 @@ struct Planes {
     const uint8_t *kcodes, *kmeta, *vcodes, *vmeta;
 };
 
+// Value kinds: VB = 4 or 8 (uniform codes), or -b for TurboQuant-MSE V with b = 3 or 4 bit planes.
+// A TurboQuant value unit is one thread's (block half, octet kb, lane column n, channel quad
+// N / 4, token parity): the b plane words of (kb, n, N / 4), whose nibble 4 (N % 4) of the
+// half-word of that parity holds tokens par, par + 2, par + 4, par + 6 of the octet.
 template <int KB, int VB>
 __device__ __forceinline__ void load_codes(const Planes& P, int ci, int tid, ChunkRegs& R) {
 #pragma unroll
@@ -94,22 +98,42 @@ __device__ __forceinline__ void load_codes(const Planes& P, int ci, int tid, Chu
         R.ks[j] = m[g]; // kept apart until the dequantization: no wait on the load here
         R.kz[j] = m[4 + g];
     }
+    if constexpr (VB < 0) {
+        constexpr int NB = -VB;
+        const int r = tid & 255, kb = r >> 6, n = (r >> 2) & 15, hN = (r >> 1) & 1;
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(P.vcodes + ((size_t)2 * ci + (tid >> 8)) * (512 * NB)) +
+                            2 * NB * (16 * kb + n) + hN;
+        R.vc[0].x = w[0];
+        R.vc[0].y = w[2];
+        R.vc[1].x = w[4];
+        R.vc[1].y = (NB == 4) ? w[6] : 0u;
+    } else {
 #pragma unroll
-    for (int j = 0; j < kUnits; ++j) {
-        const int u = tid + kThreads * j;
-        const size_t blk = (size_t)2 * ci + (u >> 9);
-        if constexpr (VB == 4) R.vc[j].x = reinterpret_cast<const uint32_t*>(P.vcodes + blk * 2048)[u & 511];
-        else R.vc[j] = reinterpret_cast<const uint2*>(P.vcodes + blk * 4096)[u & 511];
+        for (int j = 0; j < kUnits; ++j) {
+            const int u = tid + kThreads * j;
+            const size_t blk = (size_t)2 * ci + (u >> 9);
+            if constexpr (VB == 4) R.vc[j].x = reinterpret_cast<const uint32_t*>(P.vcodes + blk * 2048)[u & 511];
+            else R.vc[j] = reinterpret_cast<const uint2*>(P.vcodes + blk * 4096)[u & 511];
+        }
     }
 }
 
+template <int VB>
 __device__ __forceinline__ void load_vmeta(const Planes& P, int ci, int tid, ChunkRegs& R) {
-    if (tid < 64) R.vm = *reinterpret_cast<const u4*>(P.vmeta + ((size_t)64 * ci + tid) * 16);
+    if constexpr (VB < 0) {
+        if (tid < 64) R.vm.x = reinterpret_cast<const uint16_t*>(P.vmeta)[(size_t)64 * ci + tid]; // fp16 norm
+    } else {
+        if (tid < 64) R.vm = *reinterpret_cast<const u4*>(P.vmeta + ((size_t)64 * ci + tid) * 16);
+    }
 }
 
-// value meta of one chunk -> sm[scale | zero][group][token] (fp16)
+// value meta of one chunk -> sm[scale | zero][group][token] (fp16); TurboQuant: sm[0][0][token]
+// = the token's norm
+template <int VB>
 __device__ __forceinline__ void store_vmeta(_Float16 (*sm)[4][kVmRow], int tid, const ChunkRegs& R) {
-    if (tid < 64) {
+    if constexpr (VB < 0) {
+        if (tid < 64) sm[0][0][tid] = __builtin_bit_cast(_Float16, (uint16_t)R.vm.x);
+    } else if (tid < 64) {
         const uint32_t w[4] = {R.vm.x, R.vm.y, R.vm.z, R.vm.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -158,9 +182,28 @@ __device__ __forceinline__ Pair dequant_pair(h2v s, h2v c, h2v z, float mone) {
 //    d = 16 N + n, tokens 8 kb + i of the block).  Value rows [channel][token] store the 8-token
 //    slot s at slot s ^ (d / 16), which keeps both these writes and the operand reads free of
 //    bank conflicts.
+// Centroid of a b-bit TurboQuant code from the upper half of its odd-symmetric codebook
+// (mg[j] = mu[2^(b-1) + j]): mu[c] = mg[c - h] for c >= h, -mg[h - 1 - c] below.
+template <int NB>
+__device__ __forceinline__ float centroid(uint32_t c, const float* mg) {
+    constexpr uint32_t H = 1u << (NB - 1);
+    const bool up = (c & H) != 0;
+    const uint32_t j = (c & (H - 1)) ^ (up ? 0u : H - 1);
+    float a = (j & 1) ? mg[1] : mg[0];
+    float b = (j & 1) ? mg[3] : mg[2];
+    float m = (j & 2) ? b : a;
+    if constexpr (NB == 4) {
+        const float e = (j & 1) ? mg[5] : mg[4];
+        const float f = (j & 1) ? mg[7] : mg[6];
+        const float g = (j & 2) ? f : e;
+        m = (j & 4) ? g : m;
+    }
+    return up ? m : -m;
+}
+
 template <int KB, int VB>
 __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const _Float16 (*sm)[4][kVmRow], int tid,
-                                              const ChunkRegs& R) {
+                                              const ChunkRegs& R, const float* mg) {
     // -1 in a register the compiler cannot see through: hi * (-1) + y stays one mixed-precision
     // fma (v_fma_mix*) instead of being rewritten as a conversion and a subtraction
     float mone = -1.0f;
@@ -181,6 +224,51 @@ __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const 
         _Float16* dst = sk + key_lds_row(t) * kKS + 8 * w; // channels 32 (w / 4) + 8 (w % 4) + i
         *reinterpret_cast<u4*>(dst) = hi;
         *reinterpret_cast<u4*>(dst + 64 * kKS) = lo;
+    }
+    if constexpr (VB < 0) {
+        // TurboQuant-MSE values n_t mu[code] (fp32 product), then fp16 hi + remainder lo.  The
+        // two parity threads of a unit (adjacent lanes) swap halves so that each ends up with two
+        // whole channels of the octet: channels 4 hN + 2 par + {0, 1}.
+        constexpr int NB = -VB;
+        const int r = tid & 255, half = tid >> 8, kb = r >> 6, n = (r >> 2) & 15, hN = (r >> 1) & 1, par = r & 1;
+        const uint32_t wd[4] = {R.vc[0].x, R.vc[0].y, R.vc[1].x, R.vc[1].y};
+        float v[4][4]; // [channel quad q][token pair m]: token 2m + par
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float nt = (float)sm[0][0][32 * half + 8 * kb + 2 * m + par];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int sh = 16 * par + 4 * q + m;
+                uint32_t c = 0;
+#pragma unroll
+                for (int k = 0; k < NB; ++k) c |= ((wd[k] >> sh) & 1u) << k;
+                v[q][m] = nt * centroid<NB>(c, mg);
+            }
+        }
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            float tok[8];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float keep = par ? v[2 + qq][m] : v[qq][m];  // this thread's channel
+                const float give = par ? v[qq][m] : v[2 + qq][m];  // the partner's channel
+                const float got = xor_lane<1>(give);
+                tok[2 * m] = par ? got : keep;
+                tok[2 * m + 1] = par ? keep : got;
+            }
+            h8 hi, lo;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const _Float16 h = (_Float16)tok[i];
+                hi[i] = h;
+                lo[i] = (_Float16)(tok[i] - (float)h);
+            }
+            const int N = 4 * hN + 2 * par + qq, d = 16 * N + n;
+            _Float16* dst = sv + d * kVS + 8 * ((4 * half + kb) ^ N);
+            *reinterpret_cast<h8*>(dst) = hi;
+            *reinterpret_cast<h8*>(dst + 128 * kVS) = lo;
+        }
+        return;
     }
 #pragma unroll
     for (int j = 0; j < kUnits; ++j) {
@@ -249,6 +337,15 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
     P.kmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.meta_off);
     P.vcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.codes_off);
     P.vmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.meta_off);
+    // TurboQuant-MSE V: the upper half of the codebook (the lower half is its mirror image)
+    float mg[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (VB == -3) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mg[j] = p.mu[4 + j];
+    } else if constexpr (VB == -4) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mg[j] = p.mu16[8 + j];
+    }
 
     // ---------------- q' = R_K(q) .* c_K * scale * log2(e) * 2^e per row (2^e keeps max|q'| in
     // [64, 128)), then the B operands of the score product (column = row lr of the block,
@@ -344,13 +441,13 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
     ChunkRegs R;
     const bool late = wave >= kWaves / 2; // dequantizes before its matrix products
     if (c0 < c1) {
-        load_vmeta(P, c0, tid, R);
-        store_vmeta(s_vm[0], tid, R);
+        load_vmeta<VB>(P, c0, tid, R);
+        store_vmeta<VB>(s_vm[0], tid, R);
         load_codes<KB, VB>(P, c0, tid, R);
-        if (c0 + 1 < c1) load_vmeta(P, c0 + 1, tid, R);
+        if (c0 + 1 < c1) load_vmeta<VB>(P, c0 + 1, tid, R);
         __syncthreads();
-        dequant_chunk<KB, VB>(s_lds, s_lds + 2 * kKBuf, s_vm[0], tid, R);
-        if (c0 + 1 < c1) store_vmeta(s_vm[1], tid, R);
+        dequant_chunk<KB, VB>(s_lds, s_lds + 2 * kKBuf, s_vm[0], tid, R, mg);
+        if (c0 + 1 < c1) store_vmeta<VB>(s_vm[1], tid, R);
         if (late && c0 + 1 < c1) load_codes<KB, VB>(P, c0 + 1, tid, R);
         __syncthreads();
     }
@@ -363,12 +460,12 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
         auto dequant_next = [&]() {
             if (more) {
                 dequant_chunk<KB, VB>(s_lds + (buf ^ 1) * kKBuf, s_lds + 2 * kKBuf + (buf ^ 1) * kVBuf,
-                                      s_vm[buf ^ 1], tid, R);
-                if (ci + 2 < c1) store_vmeta(s_vm[buf], tid, R);
+                                      s_vm[buf ^ 1], tid, R, mg);
+                if (ci + 2 < c1) store_vmeta<VB>(s_vm[buf], tid, R);
             }
         };
         if (!late) {
-            if (ci + 2 < c1) load_vmeta(P, ci + 2, tid, R); // first: it may wait on its register
+            if (ci + 2 < c1) load_vmeta<VB>(P, ci + 2, tid, R); // first: it may wait on its register
             if (more) load_codes<KB, VB>(P, ci + 1, tid, R);
         } else {
             dequant_next();
@@ -564,11 +661,16 @@ bool prefill_attn_supported(const PrefillParams& p) {
     const PlaneGeom& K = p.geom[0];
     const PlaneGeom& V = p.geom[1];
     auto ok = [](const PlaneGeom& g) { return g.scheme == kUniform && (g.bits == 4 || g.bits == 8); };
-    return ok(K) && ok(V) && p.window == 0 && p.G >= 1 && p.G <= kMaxGroupHeads;
+    const bool v_turbo = V.scheme == kTurboMse && (V.bits == 3 || V.bits == 4);
+    return ok(K) && (ok(V) || v_turbo) && p.window == 0 && p.G >= 1 && p.G <= kMaxGroupHeads;
 }
 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
     const int kb = p.geom[0].bits, vb = p.geom[1].bits;
+    if (p.geom[1].scheme == kTurboMse) {
+        if (kb == 4) return vb == 4 ? launch_t<4, -4>(p, s) : launch_t<4, -3>(p, s);
+        return vb == 4 ? launch_t<8, -4>(p, s) : launch_t<8, -3>(p, s);
+    }
     if (kb == 4) return vb == 4 ? launch_t<4, 4>(p, s) : launch_t<4, 8>(p, s);
     return vb == 4 ? launch_t<8, 4>(p, s) : launch_t<8, 8>(p, s);
 }
