@@ -625,6 +625,8 @@ kvq_status kvq_attn_prefill(kvq_cache* c, int layer, const void* q, int dtype, f
     p.cs = c->cs() + c->table_off(layer);
     p.mu = c->mu();
     p.mu16 = c->mu16();
+    p.perm = c->perm() + c->perm_off(layer);
+    p.mu64 = c->mu64();
     p.dtype = dtype;
     p.batch = batch;
     p.n_q = n_q;

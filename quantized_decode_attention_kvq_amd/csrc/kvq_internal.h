@@ -97,6 +97,8 @@ struct PrefillParams {
     const float* cs;          // layer base [Hkv][2][128] Sinkhorn c
     const float* mu;          // [8]: TurboQuant-MSE V codebook (3-bit)
     const float* mu16;        // [16]: 4-bit TurboQuant-MSE V codebook
+    const int* perm;          // layer base [Hkv][128] (split V)
+    const float* mu64;        // [kSplitTable] split codebooks
     int dtype, batch, n_q, Hq, Hkv, G, window;
     int n_splits;             // key splits per row (1: the attention kernel writes out itself)
     float qscale;             // softmax scale * log2(e)

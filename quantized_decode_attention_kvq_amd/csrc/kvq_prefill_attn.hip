@@ -82,10 +82,25 @@ struct Planes {
     const uint8_t *kcodes, *kmeta, *vcodes, *vmeta;
 };
 
-// Value kinds: VB = 4 or 8 (uniform codes), or -b for TurboQuant-MSE V with b = 3 or 4 bit planes.
+// Value kinds: VB = 4 or 8 (uniform codes), -b for TurboQuant-MSE V with b = 3 or 4 bit planes,
+// or kSplitV - bo for the split TurboQuant V with bo = 3 or 4 outlier bits (channel quads
+// N / 4 = 0 are the outlier half's positions, bo planes; N / 4 = 1 the rest's, bo - 1 planes).
 // A TurboQuant value unit is one thread's (block half, octet kb, lane column n, channel quad
 // N / 4, token parity): the b plane words of (kb, n, N / 4), whose nibble 4 (N % 4) of the
 // half-word of that parity holds tokens par, par + 2, par + 4, par + 6 of the octet.
+constexpr int kSplitV = -10;
+__host__ __device__ constexpr bool split_kind(int vb) { return vb <= kSplitV; }
+
+// Thread -> TurboQuant value unit: token parity in lane bit 0 (the swap partner is lane ^ 1),
+// lane column n in bits 1-4, octet kb in bits 5-6, channel quad N / 4 in bit 7 and block half in
+// bit 8, so that the quad (and with it a split V's half and codebook) is uniform per wave.
+struct TUnit {
+    int half, kb, n, hN, par;
+};
+__device__ __forceinline__ TUnit turbo_unit(int tid) {
+    return TUnit{tid >> 8, (tid >> 5) & 3, (tid >> 1) & 15, (tid >> 7) & 1, tid & 1};
+}
+
 template <int KB, int VB>
 __device__ __forceinline__ void load_codes(const Planes& P, int ci, int tid, ChunkRegs& R) {
 #pragma unroll
@@ -98,11 +113,22 @@ __device__ __forceinline__ void load_codes(const Planes& P, int ci, int tid, Chu
         R.ks[j] = m[g]; // kept apart until the dequantization: no wait on the load here
         R.kz[j] = m[4 + g];
     }
-    if constexpr (VB < 0) {
+    if constexpr (split_kind(VB)) {
+        constexpr int BO = kSplitV - VB, W = 2 * BO - 1;
+        const TUnit U = turbo_unit(tid);
+        const int hN = U.hN;
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(P.vcodes + ((size_t)2 * ci + U.half) * (256 * W)) +
+                            W * (16 * U.kb + U.n) + (hN ? BO : 0);
+        const int nb = hN ? BO - 1 : BO;
+        R.vc[0].x = w[0];
+        R.vc[0].y = w[1];
+        R.vc[1].x = (nb > 2) ? w[2] : 0u;
+        R.vc[1].y = (nb > 3) ? w[3] : 0u;
+    } else if constexpr (VB < 0) {
         constexpr int NB = -VB;
-        const int r = tid & 255, kb = r >> 6, n = (r >> 2) & 15, hN = (r >> 1) & 1;
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(P.vcodes + ((size_t)2 * ci + (tid >> 8)) * (512 * NB)) +
-                            2 * NB * (16 * kb + n) + hN;
+        const TUnit U = turbo_unit(tid);
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(P.vcodes + ((size_t)2 * ci + U.half) * (512 * NB)) +
+                            2 * NB * (16 * U.kb + U.n) + U.hN;
         R.vc[0].x = w[0];
         R.vc[0].y = w[2];
         R.vc[1].x = w[4];
@@ -120,7 +146,9 @@ __device__ __forceinline__ void load_codes(const Planes& P, int ci, int tid, Chu
 
 template <int VB>
 __device__ __forceinline__ void load_vmeta(const Planes& P, int ci, int tid, ChunkRegs& R) {
-    if constexpr (VB < 0) {
+    if constexpr (split_kind(VB)) {
+        if (tid < 64) R.vm.x = reinterpret_cast<const uint32_t*>(P.vmeta)[(size_t)64 * ci + tid]; // two fp16 norms
+    } else if constexpr (VB < 0) {
         if (tid < 64) R.vm.x = reinterpret_cast<const uint16_t*>(P.vmeta)[(size_t)64 * ci + tid]; // fp16 norm
     } else {
         if (tid < 64) R.vm = *reinterpret_cast<const u4*>(P.vmeta + ((size_t)64 * ci + tid) * 16);
@@ -128,10 +156,15 @@ __device__ __forceinline__ void load_vmeta(const Planes& P, int ci, int tid, Chu
 }
 
 // value meta of one chunk -> sm[scale | zero][group][token] (fp16); TurboQuant: sm[0][0][token]
-// = the token's norm
+// = the token's norm; split: sm[0][0 | 1][token] = the outlier / rest norm
 template <int VB>
 __device__ __forceinline__ void store_vmeta(_Float16 (*sm)[4][kVmRow], int tid, const ChunkRegs& R) {
-    if constexpr (VB < 0) {
+    if constexpr (split_kind(VB)) {
+        if (tid < 64) {
+            sm[0][0][tid] = __builtin_bit_cast(_Float16, (uint16_t)(R.vm.x & 0xffffu));
+            sm[0][1][tid] = __builtin_bit_cast(_Float16, (uint16_t)(R.vm.x >> 16));
+        }
+    } else if constexpr (VB < 0) {
         if (tid < 64) sm[0][0][tid] = __builtin_bit_cast(_Float16, (uint16_t)R.vm.x);
     } else if (tid < 64) {
         const uint32_t w[4] = {R.vm.x, R.vm.y, R.vm.z, R.vm.w};
@@ -201,6 +234,25 @@ __device__ __forceinline__ float centroid(uint32_t c, const float* mg) {
     return up ? m : -m;
 }
 
+// n_t mu[code] for the 4 channels x 4 tokens of a TurboQuant value unit: v[q][m] = channel quad
+// q, token 2m + par of the octet; NB-bit codes from the plane words wd, norms from nrm[token].
+template <int NB>
+__device__ __forceinline__ void turbo_values(const uint32_t* wd, const _Float16* nrm, const float* mg, int par,
+                                             float (&v)[4][4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float nt = (float)nrm[2 * m + par];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int sh = 16 * par + 4 * q + m;
+            uint32_t c = 0;
+#pragma unroll
+            for (int k = 0; k < NB; ++k) c |= ((wd[k] >> sh) & 1u) << k;
+            v[q][m] = nt * centroid<NB>(c, mg);
+        }
+    }
+}
+
 template <int KB, int VB>
 __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const _Float16 (*sm)[4][kVmRow], int tid,
                                               const ChunkRegs& R, const float* mg) {
@@ -229,22 +281,19 @@ __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const 
         // TurboQuant-MSE values n_t mu[code] (fp32 product), then fp16 hi + remainder lo.  The
         // two parity threads of a unit (adjacent lanes) swap halves so that each ends up with two
         // whole channels of the octet: channels 4 hN + 2 par + {0, 1}.
-        constexpr int NB = -VB;
-        const int r = tid & 255, half = tid >> 8, kb = r >> 6, n = (r >> 2) & 15, hN = (r >> 1) & 1, par = r & 1;
+        // split V: the thread's half (hN) fixes its norm row, code bits and codebook (mg holds
+        // the outlier table in 0..7 and the rest's in 8..11)
+        constexpr bool SPL = split_kind(VB);
+        constexpr int NB = SPL ? kSplitV - VB : -VB;
+        const TUnit U = turbo_unit(tid);
+        const int half = U.half, kb = U.kb, n = U.n, hN = U.hN, par = U.par;
         const uint32_t wd[4] = {R.vc[0].x, R.vc[0].y, R.vc[1].x, R.vc[1].y};
+        const int t0 = 32 * half + 8 * kb;
         float v[4][4]; // [channel quad q][token pair m]: token 2m + par
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float nt = (float)sm[0][0][32 * half + 8 * kb + 2 * m + par];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int sh = 16 * par + 4 * q + m;
-                uint32_t c = 0;
-#pragma unroll
-                for (int k = 0; k < NB; ++k) c |= ((wd[k] >> sh) & 1u) << k;
-                v[q][m] = nt * centroid<NB>(c, mg);
-            }
-        }
+        if (SPL && hN) // the rest half of a split V (uniform per wave): one bit fewer, own table
+            turbo_values<(SPL ? NB - 1 : NB)>(wd, &sm[0][1][t0], mg + 8, par, v);
+        else
+            turbo_values<NB>(wd, &sm[0][0][t0], mg, par, v);
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
             float tok[8];
@@ -295,7 +344,26 @@ __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const 
 
 // out row = R_V^-1(c_V .* x) for a row held as two channels per lane (2l, 2l + 1).
 __device__ __forceinline__ void store_out_row(float a, float c, const PlaneGeom& VG, float2 csv, float2 sgv,
-                                              float* out_row, int l) {
+                                              int2 pm, float* out_row, int l) {
+    if (VG.scheme == kTurboSplit) {
+        // two 64-point inverse rotations (the 128-point butterflies without the last span), then
+        // positions 2l, 2l + 1 go to their channels
+        const float s = a + c, d = a - c;
+        a = s;
+        c = d;
+        qdev::hadamard_step<1>(a, c, l);
+        qdev::hadamard_step<2>(a, c, l);
+        qdev::hadamard_step<4>(a, c, l);
+        qdev::hadamard_step<8>(a, c, l);
+        qdev::hadamard_step<16>(a, c, l);
+        a *= 0.125f;
+        c *= 0.125f;
+        if (sgv.x < 0.0f) a = -a;
+        if (sgv.y < 0.0f) c = -c;
+        out_row[pm.x] = a;
+        out_row[pm.y] = c;
+        return;
+    }
     if (VG.sinkhorn) {
         a *= csv.x;
         c *= csv.y;
@@ -338,8 +406,15 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
     P.vcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.codes_off);
     P.vmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.meta_off);
     // TurboQuant-MSE V: the upper half of the codebook (the lower half is its mirror image)
-    float mg[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (VB == -3) {
+    float mg[12] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (split_kind(VB)) {
+        // upper halves of the N(0, 1/64) codebooks (tables at levels - 4): outliers, then the rest
+        constexpr int BO = kSplitV - VB, LO = 1 << BO, LR = 1 << (BO - 1);
+#pragma unroll
+        for (int j = 0; j < LO / 2; ++j) mg[j] = p.mu64[(LO - 4) + LO / 2 + j];
+#pragma unroll
+        for (int j = 0; j < LR / 2; ++j) mg[8 + j] = p.mu64[(LR - 4) + LR / 2 + j];
+    } else if constexpr (VB == -3) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) mg[j] = p.mu[4 + j];
     } else if constexpr (VB == -4) {
@@ -592,6 +667,8 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
     __syncthreads(); // c0 >= c1 workgroups skipped the loop's barriers
     const float2 csv = reinterpret_cast<const float2*>(p.cs + (size_t)(kvh * 2 + 1) * kDim)[l];
     const float2 sgv = reinterpret_cast<const float2*>(p.signs + (size_t)(kvh * 2 + 1) * kDim)[l];
+    const int2 pmv = VG.scheme == kTurboSplit ? reinterpret_cast<const int2*>(p.perm + (size_t)kvh * kDim)[l]
+                                              : make_int2(2 * l, 2 * l + 1);
     float* s_rows = reinterpret_cast<float*>(s_lds) + wave * 8 * kDim;
 #pragma unroll
     for (int ps = 0; ps < 2 * kQB; ++ps) { // register indexes must stay compile-time: unrolled
@@ -611,7 +688,7 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
             if (gr >= nrows) break;
             const int i = gr / G, hq = kvh * G + (gr - i * G);
             const float2 x = reinterpret_cast<const float2*>(s_rows + rr * kDim)[l];
-            store_out_row(x.x, x.y, VG, csv, sgv, p.out + (((size_t)b * p.n_q + i) * p.Hq + hq) * kDim, l);
+            store_out_row(x.x, x.y, VG, csv, sgv, pmv, p.out + (((size_t)b * p.n_q + i) * p.Hq + hq) * kDim, l);
         }
         wave_lds_sync();
     }
@@ -640,7 +717,9 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillParams p) {
     c = (L > 0.0f) ? c / L : 0.0f;
     const float2 csv = reinterpret_cast<const float2*>(p.cs + (size_t)(kvh * 2 + 1) * kDim)[l];
     const float2 sgv = reinterpret_cast<const float2*>(p.signs + (size_t)(kvh * 2 + 1) * kDim)[l];
-    store_out_row(a, c, p.geom[1], csv, sgv, p.out + (size_t)rr * kDim, l);
+    const int2 pmv = p.geom[1].scheme == kTurboSplit ? reinterpret_cast<const int2*>(p.perm + (size_t)kvh * kDim)[l]
+                                                      : make_int2(2 * l, 2 * l + 1);
+    store_out_row(a, c, p.geom[1], csv, sgv, pmv, p.out + (size_t)rr * kDim, l);
 }
 
 template <int KB, int VB>
@@ -661,12 +740,16 @@ bool prefill_attn_supported(const PrefillParams& p) {
     const PlaneGeom& K = p.geom[0];
     const PlaneGeom& V = p.geom[1];
     auto ok = [](const PlaneGeom& g) { return g.scheme == kUniform && (g.bits == 4 || g.bits == 8); };
-    const bool v_turbo = V.scheme == kTurboMse && (V.bits == 3 || V.bits == 4);
+    const bool v_turbo = (V.scheme == kTurboMse || V.scheme == kTurboSplit) && (V.bits == 3 || V.bits == 4);
     return ok(K) && (ok(V) || v_turbo) && p.window == 0 && p.G >= 1 && p.G <= kMaxGroupHeads;
 }
 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
     const int kb = p.geom[0].bits, vb = p.geom[1].bits;
+    if (p.geom[1].scheme == kTurboSplit) {
+        if (kb == 4) return vb == 4 ? launch_t<4, kSplitV - 4>(p, s) : launch_t<4, kSplitV - 3>(p, s);
+        return vb == 4 ? launch_t<8, kSplitV - 4>(p, s) : launch_t<8, kSplitV - 3>(p, s);
+    }
     if (p.geom[1].scheme == kTurboMse) {
         if (kb == 4) return vb == 4 ? launch_t<4, -4>(p, s) : launch_t<4, -3>(p, s);
         return vb == 4 ? launch_t<8, -4>(p, s) : launch_t<8, -3>(p, s);

@@ -92,18 +92,20 @@ def test_prefill_attention_dense27b_gqa5_bf16(wl):
 
 
 @pytest.mark.parametrize("wl", [W.LLAMA3B_32K_TURBO_ASYM, W.LLAMA3B_32K_Q8_0_TURBO_V, W.LLAMA3B_32K_Q8_0_TURBO4_V,
-                                W.LLAMA3B_32K_TURBO_ASYM.with_(name="llama3b-u4-k-turbomse-v", k_bits=4)],
+                                W.LLAMA3B_32K_TURBO_ASYM.with_(name="llama3b-u4-k-turbomse-v", k_bits=4),
+                                W.LLAMA8B_32K_Q8_0_TURBO25_V, W.LLAMA8B_32K_Q8_0_TURBO35_V],
                          ids=lambda w: w.name)
 def test_prefill_attention_turbo_mse_v(wl):
-    # TurboQuant-MSE values (3- and 4-bit codes, rotated domain, R_V^-1 at the end) under uniform
-    # or q8_0 keys: the cache types of the application rule K = Q8, V = Turbo 3/4
+    # TurboQuant-MSE values (3- and 4-bit codes, and the outlier split at 2.5 / 3.5 bits; rotated
+    # domain, inverse rotation and un-permutation at the end) under uniform or q8_0 keys: the
+    # cache types of the application rule K = Q8, V = Turbo
     _say("case: prefill attention,", wl.name)
     _run(wl, n0=300, B=2, nb=1, ne=37, n_q=90, seed=5)
 
 
-def test_prefill_attention_turbo4_v_key_splits():
+@pytest.mark.parametrize("wl", [W.LLAMA3B_32K_Q8_0_TURBO4_V, W.LLAMA8B_32K_Q8_0_TURBO25_V], ids=lambda w: w.name)
+def test_prefill_attention_turbo_v_key_splits(wl):
     # a long context, so that the keys are split over workgroups and the merge un-rotates V
-    wl = W.LLAMA3B_32K_Q8_0_TURBO4_V
     _say("case: prefill attention with key splits,", wl.name)
     case, _, _ = _run(wl, n0=3000, B=1, nb=0, ne=0, n_q=64, seed=6)
     assert case.cache.attn_prefill_workspace(0, 64, 1) > 0
@@ -139,11 +141,9 @@ def test_prefill_attention_last_token_equals_decode():
 
 def test_prefill_attention_refusals():
     import quantized_decode_attention_kvq_amd as K
-    # FP32 window, TurboQuant-QJL keys and split values are not read by this kernel; n_q beyond
-    # a length
+    # FP32 window and TurboQuant-QJL keys are not read by this kernel; n_q beyond a length
     for wl, n, nq, name in ((W.LLAMA3B_3970_PROGRESSIVE, 200, 10, "KVQ_ERR_UNSUPPORTED"),
                             (W.LLAMA3B_32K_TURBO, 200, 10, "KVQ_ERR_UNSUPPORTED"),
-                            (W.LLAMA8B_32K_Q8_0_TURBO25_V, 200, 10, "KVQ_ERR_UNSUPPORTED"),
                             (W.LLAMA3B_32K_KVARN, 200, 201, "KVQ_ERR_INVALID_ARG")):
         case = Case(wl, n, layers=[0], batch=1)
         case.prefill(0)
