@@ -225,8 +225,10 @@ kvq_status kvq_append_attn_decode(kvq_cache* cache, int layer, const void* k, co
  * Errors (nothing enqueued): KVQ_ERR_INVALID_ARG for a bad handle, layer, pointer, dtype, batch
  * outside 1 .. max_batch, n_q < 1, or n_q above some sequence's length; KVQ_ERR_MISALIGNED;
  * KVQ_ERR_NOT_READY before the layer's tables / calibration are set; KVQ_ERR_UNSUPPORTED for
- * TurboQuant-QJL keys and caches with an FP32 window (the kernel reads UNIFORM / Q8_0 keys and
- * UNIFORM, Q8_0, TURBO_MSE or TURBO_SPLIT values). */
+ * TurboQuant-QJL keys, and for an FP32 window beside rotated or balanced codes (the kernel
+ * reads UNIFORM / Q8_0 keys and UNIFORM, Q8_0, TURBO_MSE or TURBO_SPLIT values; the window's
+ * originals are taken as they are, so with fp32_window > 0 both tensors must be UNIFORM without
+ * rotation or Sinkhorn balancing). */
 kvq_status kvq_attn_prefill(kvq_cache* cache, int layer, const void* q, int dtype, float* out,
                             int n_q, int batch, float softmax_scale, void* workspace,
                             size_t workspace_bytes, void* stream);

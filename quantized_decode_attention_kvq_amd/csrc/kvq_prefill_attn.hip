@@ -342,6 +342,58 @@ __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const 
     }
 }
 
+// FP32 window (progressive caches, plain domain): tokens nqd .. len - 1 of the chunk take their
+// original values from the rings instead of the codes.  Each thread rewrites exactly the LDS
+// units it dequantized (same unit mapping, so program order makes the ring values final); a
+// value unit straddling nqd keeps its dequantized tokens below it.
+template <int VB>
+__device__ __forceinline__ void window_overwrite(_Float16* sk, _Float16* sv, int chunk, int nqd, int len, int W,
+                                                 const float* kring, const float* vring, int tid) {
+    if (W == 0 || 64 * chunk + 63 < nqd || 64 * chunk >= len) return;
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j) {
+        const int u = tid + kThreads * j, pr = u >> 4, w = u & 15;
+        const int t = 4 * (pr & 15) + (pr >> 4), tok = 64 * chunk + t;
+        if (tok < nqd || tok >= len) continue;
+        const float4* r = reinterpret_cast<const float4*>(kring + (size_t)(tok % W) * kDim + 8 * w);
+        const float4 a = r[0], c = r[1];
+        const float y[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        h8 hi, lo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const _Float16 h = (_Float16)y[i];
+            hi[i] = h;
+            lo[i] = (_Float16)(y[i] - (float)h);
+        }
+        _Float16* dst = sk + key_lds_row(t) * kKS + 8 * w;
+        *reinterpret_cast<h8*>(dst) = hi;
+        *reinterpret_cast<h8*>(dst + 64 * kKS) = lo;
+    }
+    if constexpr (VB > 0) {
+#pragma unroll
+        for (int j = 0; j < kUnits; ++j) {
+            const int u = tid + kThreads * j, half = u >> 9, w = u & 511;
+            const int kb = w >> 7, n = (w >> 3) & 15, N = w & 7, d = 16 * N + n;
+            const int tok0 = 64 * chunk + 32 * half + 8 * kb;
+            if (tok0 + 7 < nqd || tok0 >= len) continue;
+            _Float16* dst = sv + d * kVS + 8 * ((4 * half + kb) ^ N);
+            h8 hi = *reinterpret_cast<const h8*>(dst), lo = *reinterpret_cast<const h8*>(dst + 128 * kVS);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int tok = tok0 + i;
+                if (tok >= nqd && tok < len) {
+                    const float y = vring[(size_t)(tok % W) * kDim + d];
+                    const _Float16 h = (_Float16)y;
+                    hi[i] = h;
+                    lo[i] = (_Float16)(y - (float)h);
+                }
+            }
+            *reinterpret_cast<h8*>(dst) = hi;
+            *reinterpret_cast<h8*>(dst + 128 * kVS) = lo;
+        }
+    }
+}
+
 // out row = R_V^-1(c_V .* x) for a row held as two channels per lane (2l, 2l + 1).
 __device__ __forceinline__ void store_out_row(float a, float c, const PlaneGeom& VG, float2 csv, float2 sgv,
                                               int2 pm, float* out_row, int l) {
@@ -405,6 +457,10 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
     P.kmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.meta_off);
     P.vcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.codes_off);
     P.vmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.meta_off);
+    // FP32 window: the newest min(len, W) tokens are read from the rings
+    const int Wn = p.window, nqd = (Wn > 0) ? max(0, N - Wn) : N;
+    const float* kring = reinterpret_cast<const float*>(slot + p.plane_off[0] + KG.ring_off);
+    const float* vring = reinterpret_cast<const float*>(slot + p.plane_off[1] + VG.ring_off);
     // TurboQuant-MSE V: the upper half of the codebook (the lower half is its mirror image)
     float mg[12] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (split_kind(VB)) {
@@ -522,6 +578,7 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
         if (c0 + 1 < c1) load_vmeta<VB>(P, c0 + 1, tid, R);
         __syncthreads();
         dequant_chunk<KB, VB>(s_lds, s_lds + 2 * kKBuf, s_vm[0], tid, R, mg);
+        window_overwrite<VB>(s_lds, s_lds + 2 * kKBuf, c0, nqd, N, Wn, kring, vring, tid);
         if (c0 + 1 < c1) store_vmeta<VB>(s_vm[1], tid, R);
         if (late && c0 + 1 < c1) load_codes<KB, VB>(P, c0 + 1, tid, R);
         __syncthreads();
@@ -536,6 +593,8 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
             if (more) {
                 dequant_chunk<KB, VB>(s_lds + (buf ^ 1) * kKBuf, s_lds + 2 * kKBuf + (buf ^ 1) * kVBuf,
                                       s_vm[buf ^ 1], tid, R, mg);
+                window_overwrite<VB>(s_lds + (buf ^ 1) * kKBuf, s_lds + 2 * kKBuf + (buf ^ 1) * kVBuf, ci + 1,
+                                     nqd, N, Wn, kring, vring, tid);
                 if (ci + 2 < c1) store_vmeta<VB>(s_vm[buf], tid, R);
             }
         };
@@ -741,7 +800,10 @@ bool prefill_attn_supported(const PrefillParams& p) {
     const PlaneGeom& V = p.geom[1];
     auto ok = [](const PlaneGeom& g) { return g.scheme == kUniform && (g.bits == 4 || g.bits == 8); };
     const bool v_turbo = (V.scheme == kTurboMse || V.scheme == kTurboSplit) && (V.bits == 3 || V.bits == 4);
-    return ok(K) && (ok(V) || v_turbo) && p.window == 0 && p.G >= 1 && p.G <= kMaxGroupHeads;
+    // an FP32 window is read in the plain domain: no rotation or balancing on either tensor
+    const bool plain = !K.rotate && !K.sinkhorn && !V.rotate && !V.sinkhorn;
+    const bool win_ok = p.window == 0 || (p.window == kWindowMax && plain && ok(V));
+    return ok(K) && (ok(V) || v_turbo) && win_ok && p.G >= 1 && p.G <= kMaxGroupHeads;
 }
 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {

@@ -111,6 +111,24 @@ def test_prefill_attention_turbo_v_key_splits(wl):
     assert case.cache.attn_prefill_workspace(0, 64, 1) > 0
 
 
+@pytest.mark.parametrize("n0,nb,ne,n_q", [(500, 1, 37, 150), (90, 0, 0, 40), (64, 1, 100, 60)])
+def test_prefill_attention_progressive_window(n0, nb, ne, n_q):
+    # quantcpp's progressive cache (4-bit codes, newest 128 tokens in FP32): a query sees the
+    # window tokens of the cache as it stands with their original values, older ones from the
+    # codes; queries on both sides of the window start, whole caches inside the window, and a
+    # ragged batch whose sequences have different window starts
+    wl = W.LLAMA3B_3970_PROGRESSIVE
+    _say("case: prefill attention, progressive window, n0", n0, "n_q", n_q)
+    _run(wl, n0=n0, B=2, nb=nb, ne=ne, n_q=n_q, seed=7)
+
+
+def test_prefill_attention_progressive_128k_shape_key_splits():
+    wl = W.LLAMA3B_128K_PROGRESSIVE
+    _say("case: prefill attention,", wl.name, "3000 tokens, key splits")
+    case, _, _ = _run(wl, n0=3000, B=1, nb=0, ne=0, n_q=64, seed=8)
+    assert case.cache.attn_prefill_workspace(0, 64, 1) > 0
+
+
 def test_prefill_attention_asym_bits_and_long_chunk():
     # 8-bit K with 4-bit V (uniform, no rotation), a chunk longer than the two-tile boundary
     wl = W.LLAMA3B_3970_PROGRESSIVE.with_(window=0, k_bits=8)
@@ -141,8 +159,9 @@ def test_prefill_attention_last_token_equals_decode():
 
 def test_prefill_attention_refusals():
     import quantized_decode_attention_kvq_amd as K
-    # FP32 window and TurboQuant-QJL keys are not read by this kernel; n_q beyond a length
-    for wl, n, nq, name in ((W.LLAMA3B_3970_PROGRESSIVE, 200, 10, "KVQ_ERR_UNSUPPORTED"),
+    # an FP32 window beside rotated codes and TurboQuant-QJL keys are not read by this kernel;
+    # n_q beyond a length
+    for wl, n, nq, name in ((W.LLAMA3B_3970_PROGRESSIVE.with_(rotate_k=True), 200, 10, "KVQ_ERR_UNSUPPORTED"),
                             (W.LLAMA3B_32K_TURBO, 200, 10, "KVQ_ERR_UNSUPPORTED"),
                             (W.LLAMA3B_32K_KVARN, 200, 201, "KVQ_ERR_INVALID_ARG")):
         case = Case(wl, n, layers=[0], batch=1)
