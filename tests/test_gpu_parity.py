@@ -253,6 +253,21 @@ def test_turbo_split_v_small(wl):
     case.cache.set_option(2, 0)
 
 
+def test_turbo_split_v_bf16_window_batch():
+    # bf16 sources (calibration included), two sequences, and the progressive FP32 window beside a
+    # split V: planes and rings byte-exact, decode (window tokens in FP32) against the oracle
+    wl = W.LLAMA8B_32K_Q8_0_TURBO35_V.with_(name="llama8b-split3.5-bf16-window", dtype="bf16", window=128)
+    _say("case:", wl.name, "1 layer, 2 seqs, 250 prefill + 50 appends")
+    case = Case(wl, 300, layers=[3], batch=2)
+    k, v = case.kv(3)
+    case.cache.prefill_quantize(0, k[:, :250].contiguous(), v[:, :250].contiguous())
+    for t in range(250, 300):
+        case.cache.append(0, k[:, t].contiguous(), v[:, t].contiguous())
+    torch.cuda.synchronize()
+    planes = _check_all_planes(case, 0, heads=[0, 3, 7])
+    _decode_and_compare(case, 0, None)
+
+
 def test_turbo_split_v_requires_calibration():
     # appending to a split V before kvq_calibrate has chosen its outlier channels is refused
     wl = W.LLAMA8B_32K_Q8_0_TURBO25_V
