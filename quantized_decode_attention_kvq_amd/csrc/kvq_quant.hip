@@ -37,12 +37,49 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
     qdev::quantize_wave(p, blockIdx.z & 1, blockIdx.z >> 1, blockIdx.y, blockIdx.x * 4 + wave, rbuf[wave]);
 }
 
-// The same quantizer for one tensor only (blockIdx.z = sequence): the bulk path of the split V
-// coder, whose channel gather goes through the wave's LDS row.
-__global__ __launch_bounds__(256) void quantize_one_kernel(QuantParams p, int tensor) {
-    __shared__ float rbuf[4][kDim];
-    const int wave = threadIdx.x >> 6;
-    qdev::quantize_wave(p, tensor, blockIdx.z, blockIdx.y, blockIdx.x * 4 + wave, rbuf[wave]);
+// Bulk quantizer of a split TurboQuant V plane (BO outlier bits): waves 2u and 2u + 1 of a
+// workgroup take the outlier and the rest half (NB = BO or BO - 1 code bits) of the same octets
+// (2x + u, then every 2 * gridDim.x-th after it), requesting the next octet's source before
+// coding the current one.
+template <int BO, int NB>
+__device__ __forceinline__ void splitv_loop(const QuantParams& p, const qbulk::WavePlane& w, int hv, const int* pm,
+                                            const uint32_t* sgm, float* wl) {
+    constexpr int levels = 1 << NB;
+    const float* t = p.theta64 + (levels - 4); // levels - 1 ascending thresholds
+    auto at = [&](int k) { return k < levels - 1 ? t[k] : 0.0f; };
+    const qbulk::TurboTabs4 th{at(0), at(1), at(2), at(3), at(4), at(5), at(6), at(7),
+                               at(8), at(9), at(10), at(11), at(12), at(13), at(14)};
+    const int g_first = w.start / 8, step = gridDim.x * 2;
+    int u = blockIdx.x * 2 + ((threadIdx.x >> 6) >> 1);
+    qbulk::SplitIn cur;
+    qbulk::load_split(w, g_first + u, pm, cur);
+    for (; u < p.groups8; u += step) {
+        qbulk::SplitIn nxt;
+        qbulk::load_split(w, g_first + u + step, pm, nxt);
+        qbulk::split_v_octet<BO, NB>(w, g_first + u, hv, cur, pm, sgm, th, wl);
+        cur = nxt;
+    }
+}
+
+template <int BO>
+__global__ __launch_bounds__(256) void quantize_splitv_bulk_kernel(QuantParams p) {
+    constexpr int kW = 4, tensor = 1;
+    __shared__ __align__(16) float wl[kW][128]; // 8 tokens x 64 positions of code bytes per wave
+    const int b = blockIdx.z, head = blockIdx.y, wave = threadIdx.x >> 6, L = threadIdx.x & 63;
+    const int hv = wave & 1;
+    const qbulk::WavePlane w = qbulk::wave_plane(p, tensor, b, head);
+    // the lane's 8 positions 64 hv + 8 (L % 8) + i: their channels and sign bits
+    const int pos0 = 64 * hv + 8 * (L & 7);
+    int pm[8];
+    uint32_t sgm[8];
+    const float* sg = p.signs[tensor] + (size_t)(head * 2 + tensor) * kDim + pos0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        pm[i] = p.perm[(size_t)head * kDim + pos0 + i];
+        sgm[i] = sg[i] < 0.0f ? 0x80000000u : 0u;
+    }
+    if (hv) splitv_loop<BO, BO - 1>(p, w, 1, pm, sgm, wl[wave]);
+    else splitv_loop<BO, BO>(p, w, 0, pm, sgm, wl[wave]);
 }
 
 // Bulk quantizer of one TurboQuant tensor (QJL: TurboQuant-QJL K, else TurboQuant-MSE).  Wave
@@ -431,10 +468,15 @@ hipError_t launch_bulk_scheme(int scheme, const QuantParams& p, hipStream_t s, i
     switch (scheme) {
     case kUniform: return launch_uniform_bulk_for(p.geom[tensor0], p, s, tensor0, n_tensors);
     case kTurboQjl: return launch_turbo_bulk<true>(p, s, tensor0);
-    case kTurboSplit:
-        hipLaunchKernelGGL(quantize_one_kernel, dim3((p.groups8 + 3) / 4, p.Hkv, p.batch), dim3(256), 0, s, p,
-                           tensor0);
+    case kTurboSplit: {
+        const int planes = p.Hkv * p.batch;
+        const int gx = std::max(1, std::min((p.groups8 + 1) / 2, (kQuantBulkBlocks + planes - 1) / planes));
+        if (p.geom[tensor0].bits == 4)
+            hipLaunchKernelGGL(quantize_splitv_bulk_kernel<4>, dim3(gx, p.Hkv, p.batch), dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL(quantize_splitv_bulk_kernel<3>, dim3(gx, p.Hkv, p.batch), dim3(256), 0, s, p);
         return hipGetLastError();
+    }
     default:
         if (p.geom[tensor0].bits == 4) return launch_turbo4v_bulk(p, s); // V only
         return launch_turbo_bulk<false>(p, s, tensor0);

@@ -646,5 +646,142 @@ __device__ __forceinline__ void turbo4_v_octet(const WavePlane& w, int g, const 
     __builtin_amdgcn_wave_barrier();
 }
 
+// ---------------------------------------------------------------------------------------------
+// Split TurboQuant V (outlier split): one wave per (octet, half).  Lane L takes token L / 8 of
+// the octet and positions 8 (L % 8) .. + 7 of the wave's half (channels perm[.] of the source row,
+// gathered); the 64-point rotation runs inside the lane (spans 1, 2, 4) and across lanes L ^ 1,
+// 2, 4 (spans 8, 16, 32); the norm is the index-order tree over the half; the half's codebook
+// is uniform per wave.  Codes are staged as [token][position] bytes in the wave's LDS and formed
+// into the half's plane words: word W (16 o + n) + k (outliers) or + bo + k (the rest).
+// ---------------------------------------------------------------------------------------------
+struct SplitIn {
+    float v[8];
+};
+
+__device__ __forceinline__ void load_split(const WavePlane& w, int g, const int* pm, SplitIn& in) {
+    const int t = 8 * g + (lane_id() >> 3);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) in.v[i] = 0.0f;
+    if (t >= w.start && t < w.end) {
+        // w.src points at channel 8 (lane % 16) of the row; step back to channel 0
+        const int j16 = lane_id() & 15;
+        const char* row = w.src + (size_t)(t - w.start) * w.tok_bytes - (size_t)8 * j16 * (w.dtype == 0 ? 4 : 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (w.dtype == 0) in.v[i] = reinterpret_cast<const float*>(row)[pm[i]];
+            else in.v[i] = bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[pm[i]]);
+        }
+    }
+}
+
+// Code of u with NB bits: the number of thresholds below u, by binary search over the ascending
+// thresholds t0 .. t(2^NB - 2) (named values: a select over an array would index scratch).
+template <int NB>
+__device__ __forceinline__ uint32_t split_code(float u, const TurboTabs4& T) {
+    if constexpr (NB == 2) {
+        const bool b1 = u > T.t1;
+        const bool b0 = u > (b1 ? T.t2 : T.t0);
+        return (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+    } else if constexpr (NB == 3) {
+        const bool b2 = u > T.t3;
+        const bool b1 = u > (b2 ? T.t5 : T.t1);
+        const bool b0 = u > (b2 ? (b1 ? T.t6 : T.t4) : (b1 ? T.t2 : T.t0));
+        return (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+    } else {
+        return turbo_code4(u, T);
+    }
+}
+
+// NB = the half's code bits (bo for the outliers, bo - 1 for the rest), hv = the half.
+template <int BO, int NB>
+__device__ __forceinline__ void split_v_octet(const WavePlane& w, int g, int hv, const SplitIn& in, const int* pm,
+                                              const uint32_t* sgm, const TurboTabs4& th, float* wl) {
+    constexpr int W = 2 * BO - 1;
+    const int L = lane_id(), tk = L >> 3, j = L & 7;
+    const int t_lo = max(w.start, 8 * g), t_hi = min(w.end, 8 * g + 8);
+    if (t_lo >= t_hi) return;
+    uint8_t* wv = reinterpret_cast<uint8_t*>(wl);
+    const int t = 8 * g + tk;
+    const bool valid = t >= t_lo && t < t_hi;
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = in.v[i];
+    if (w.window > 0 && valid && t >= w.end - w.window) {
+        float* ring = w.ring + (size_t)(t % w.window) * kDim;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ring[pm[i]] = e[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = __uint_as_float(__float_as_uint(e[i]) ^ sgm[i]);
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (!(i & h)) {
+                const float x = e[i], y = e[i + h];
+                e[i] = x + y;
+                e[i + h] = x - y;
+            }
+    cross8<1>(e, j);
+    cross8<2>(e, j);
+    cross8<4>(e, j);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = e[i] * 0.125f;
+    const float l0 = e[0] * e[0] + e[1] * e[1], l1 = e[2] * e[2] + e[3] * e[3];
+    const float l2 = e[4] * e[4] + e[5] * e[5], l3 = e[6] * e[6] + e[7] * e[7];
+    const float nsq = xor_reduce<8>((l0 + l1) + (l2 + l3), [](float x, float y) { return x + y; });
+    const uint16_t n16 = f16_rn(sqrtf(nsq));
+    const float n = f16_val(n16);
+    const float inv = (n > 0.0f) ? 1.0f / n : 0.0f;
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t q = split_code<NB>(e[i] * inv, th);
+        if (i < 4) lo |= q << (8 * i);
+        else hi |= q << (8 * (i - 4));
+    }
+    *reinterpret_cast<uint2*>(wv + (size_t)tk * 64 + 8 * j) = make_uint2(lo, hi);
+    if (valid && j == 0) reinterpret_cast<uint16_t*>(w.meta)[2 * t + hv] = n16;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // lane L < 32: column n = L % 16, quads Nq = 2 (L / 16) + {0, 1} of the half's positions
+    // 16 Nq + n; lanes L and L + 16 then hold complementary nibbles of the same words
+    const int n_ = L & 15, cp = (L >> 4) & 1;
+    uint32_t wk[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int Nq = 2 * cp + c, d = 16 * Nq + n_;
+        uint32_t lo4 = 0u, hi4 = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo4 |= (uint32_t)wv[i * 64 + d] << (8 * i);
+            hi4 |= (uint32_t)wv[(i + 4) * 64 + d] << (8 * i);
+        }
+        const uint32_t ev = __builtin_amdgcn_perm(hi4, lo4, 0x06040200u); // tokens 0, 2, 4, 6
+        const uint32_t od = __builtin_amdgcn_perm(hi4, lo4, 0x07050301u); // tokens 1, 3, 5, 7
+#pragma unroll
+        for (int k = 0; k < NB; ++k) wk[k] |= (byte_bits(ev, k) | (byte_bits(od, k) << 16)) << (4 * Nq);
+    }
+#pragma unroll
+    for (int k = 0; k < NB; ++k) wk[k] |= xor_lane<16>(wk[k]);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (L < 16) {
+        const int o = g & 3;
+        uint32_t* blk = reinterpret_cast<uint32_t*>(w.codes + (size_t)(g >> 2) * (256 * W)) + W * (16 * o + n_) +
+                        (hv ? BO : 0);
+        if (t_hi - t_lo == 8) {
+#pragma unroll
+            for (int k = 0; k < NB; ++k) blk[k] = wk[k];
+        } else {
+            uint32_t m = 0u;
+            for (int i = t_lo - 8 * g; i < t_hi - 8 * g; ++i) m |= 0x1111u << (16 * (i & 1) + (i >> 1));
+#pragma unroll
+            for (int k = 0; k < NB; ++k) blk[k] = (blk[k] & ~m) | (wk[k] & m);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
 } // namespace qbulk
 } // namespace kvq
