@@ -7,17 +7,20 @@
 //    stands, up to its own position: out_i = softmax(q_i k_t^T * scale | t <= pos_i) v.
 //  * quantcpp article, progressive table and "how it works" (4-bit codes with fp16 scale and
 //    zero per 32 channels), and the KVarN post, TL;DR (Walsh-Hadamard + Sinkhorn-balanced
-//    cache): keys and values are the dequantized uniform codes; scores are taken in the
-//    rotated / balanced domain with q' = R(q) .* c, and the output is mapped back with c_V and
-//    R_V^-1.
+//    cache): keys and values are the dequantized uniform codes (the newest 128 tokens from the
+//    FP32 window in progressive mode); scores are taken in the rotated / balanced domain with
+//    q' = R(q) .* c, and the output is mapped back with c_V and R_V^-1.
+//  * "LLM memory saving ... 2026", TurboQuant row and application rules (K = Q8, V = TurboQuant),
+//    with the outlier split of its 2.5 / 3.5-bit figures: values may be TurboQuant-MSE codes,
+//    n mu[code] in the rotated domain (two 64-channel halves for the split).
 //
 // How.  The (query, head) pairs of one (sequence, kv head) are rows r = G * i + h (query i,
-// query head h of the kv head's group).  A workgroup of 8 waves owns 256 consecutive rows (32 per
-// wave, two 16-row MFMA column blocks) and one share of the key chunks up to its last row's
-// position ("split"; the host picks the number of splits that fills the chip).  Per 64-token
+// query head h of the kv head's group).  A workgroup of 8 waves owns 128 consecutive rows (16 per
+// wave, one 16-row MFMA column block) and one share of the key chunks up to its last row's
+// position ("split"; the host picks the number of splits from a cost model).  Per 64-token
 // chunk:
 //  * the workgroup dequantizes the chunk's keys and values (z + s * code in fp32) into LDS as
-//    fp16 pairs (hi = the value rounded, lo = the remainder rounded), once for its 256 rows,
+//    fp16 pairs (hi = the value rounded, lo = the remainder rounded), once for its 128 rows,
 //    while the waves work on the previous chunk (two LDS buffers, global loads one chunk ahead);
 //  * each wave forms the transposed scores S^T = K q'^T on v_mfma_f32_16x16x32_f16 with three
 //    products per slice (K_hi q_hi, K_hi q_lo, K_lo q_hi: close to fp32 accuracy);
@@ -27,8 +30,8 @@
 //    then O^T += V_hi^T P^T + V_lo^T P^T (values as the A operand, fp16 probabilities as B).
 // With one split, each row's output is divided by its softmax sum and mapped back with c_V and
 // R_V^-1 in the same kernel; with several, each split writes (m, l, acc) and a merge kernel
-// combines them in a fixed order.  Planes with an FP32 window, or TurboQuant planes, are refused
-// by the host (not supported by this kernel).
+// combines them in a fixed order.  TurboQuant-QJL keys, and an FP32 window beside rotated or
+// balanced codes, are refused by the host (not supported by this kernel).
 #include <hip/hip_runtime.h>
 
 #include "kvq_internal.h"
