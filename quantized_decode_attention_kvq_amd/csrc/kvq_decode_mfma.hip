@@ -193,7 +193,11 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     constexpr int kBo = VT == kTs4 ? 4 : 3, kSo = 1 << (kBo - 1), kSr = kSo / 2, kWv = 2 * kBo - 1;
     // P staging slots per wave: 4 (uniform groups, or the 3-bit planes), 8 (the 4-bit
     // monomials), kSo + kSr (split V)
-    constexpr int kSlots = VT4 ? 8 : (VS ? kSo + kSr : 4), kPW = kSlots * 16 * kPRow;
+    // Split V with one head block (G <= 4) stages 8 rows per slot (heads' hi in rows 0-3, lo in
+    // 4-7; lanes of rows 8-15 take zeros), which halves the LDS so that 8 waves fit
+    constexpr bool kCmp = VS && MB == 1;
+    constexpr int kRows = kCmp ? 8 : 16;
+    constexpr int kSlots = VT4 ? 8 : (VS ? kSo + kSr : 4), kPW = kSlots * kRows * kPRow;
     __shared__ float s_q[kMaxGroupHeads][kDim];   // q' in the rotated/balanced domain, scaled
     __shared__ float s_qw[kMaxGroupHeads][kDim];  // plain q * scale * log2e (FP32 window)
     __shared__ float s_sp[KU ? 1 : kMaxGroupHeads][kDim]; // S q' (TurboQuant K)
@@ -645,7 +649,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                     const float a0 = readlane_f(alpha[0], 16 * v);
                     float a1 = 1.0f;
                     if (MB == 2) a1 = readlane_f(alpha[MB - 1], 16 * v);
-                    av[v] = (lq & 1) ? a1 : a0;
+                    av[v] = (kCmp || !(lq & 1)) ? a0 : a1; // compact: rows 4-7 are lo of heads 0-3
                 }
 #pragma unroll
                 for (int N = 0; N < 8; ++N)
@@ -706,8 +710,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                         hv[j] = ph;
                         lv[j] = (_Float16)((P[g][j] - (float)ph) * kLoScale);
                     }
-                    *reinterpret_cast<h4*>(my_p + (g * 16 + row) * kPRow + 4 * lr) = hv;
-                    *reinterpret_cast<h4*>(my_p + (g * 16 + 8 + row) * kPRow + 4 * lr) = lv;
+                    *reinterpret_cast<h4*>(my_p + (g * kRows + row) * kPRow + 4 * lr) = hv;
+                    *reinterpret_cast<h4*>(my_p + (g * kRows + kRows / 2 + row) * kPRow + 4 * lr) = lv;
                 }
             }
             __builtin_amdgcn_wave_barrier();
@@ -719,7 +723,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                 h8 Pg[kSlots];
 #pragma unroll
                 for (int g = 0; g < kSlots; ++g)
-                    Pg[g] = *reinterpret_cast<const h8*>(my_p + (g * 16 + lr) * kPRow + 32 * k + 8 * lq);
+                    Pg[g] = (kCmp && lr >= 8) ? h8{0, 0, 0, 0, 0, 0, 0, 0}
+                                              : *reinterpret_cast<const h8*>(my_p + (g * kRows + lr) * kPRow + 32 * k + 8 * lq);
                 if constexpr (VU) {
                     const auto& vc = vr.vc;
 #pragma unroll
@@ -863,9 +868,12 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             const float u = VU ? UV : 1.0f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int h = 4 * (lq & 1) + v;
-                if (h < G) {
-                    if (lq < 2)
+                // rows 4 lq + v: head 4 (lq % 2) + v, hi part for lq < 2 (compact: head v, hi for
+                // lq = 0, lo for lq = 1, nothing in rows 8-15)
+                const int h = kCmp ? v : 4 * (lq & 1) + v;
+                const bool lo_part = kCmp ? (lq == 1) : (lq >= 2);
+                if (h < G && (!kCmp || lq < 2)) {
+                    if (!lo_part)
                         s_acc[(wave * 8 + h) * kDim + 16 * N + lr] = acc[N][v] * u;
                     else
                         s_acc2[(wave * 8 + h) * kDim + 16 * N + lr] = acc[N][v] * (u * kLoInv);
@@ -907,9 +915,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 
 template <int KT, int VT, int MB>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    // 8 waves where registers allow; the 4-bit TurboQuant V stages twice the P slots in LDS and
-    // the 3.5-bit split V three times (12 slots: 8 waves would need 221 KiB)
-    constexpr int NW = (MB == 1 && !(KT == kU8 && VT == kU8) && VT != kTb4 && VT != kTs4) ? 8 : 4;
+    // 8 waves where registers allow; the 4-bit TurboQuant V stages twice the P slots in LDS (the
+    // split V stages up to 12, in the compact 8-row form)
+    constexpr int NW = (MB == 1 && !(KT == kU8 && VT == kU8) && VT != kTb4) ? 8 : 4;
     dim3 grid(p.n_splits_total, p.Hkv, p.batch);
     hipExtLaunchKernelGGL((decode_mfma_kernel<KT, VT, MB, NW>), grid, dim3(NW * 64), 0, s, ev0, ev1, 0, p);
     return hipGetLastError();
