@@ -193,9 +193,10 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     constexpr int kBo = VT == kTs4 ? 4 : 3, kSo = 1 << (kBo - 1), kSr = kSo / 2, kWv = 2 * kBo - 1;
     // P staging slots per wave: 4 (uniform groups, or the 3-bit planes), 8 (the 4-bit
     // monomials), kSo + kSr (split V)
-    // Split V with one head block (G <= 4) stages 8 rows per slot (heads' hi in rows 0-3, lo in
-    // 4-7; lanes of rows 8-15 take zeros), which halves the LDS so that 8 waves fit
-    constexpr bool kCmp = VS && MB == 1;
+    // 4-bit and split TurboQuant V with one head block (G <= 4) stage 8 rows per slot (heads' hi
+    // in rows 0-3, lo in 4-7; lanes of rows 8-15 take zeros), which halves the LDS so that 8
+    // waves fit
+    constexpr bool kCmp = (VS || VT4) && MB == 1;
     constexpr int kRows = kCmp ? 8 : 16;
     constexpr int kSlots = VT4 ? 8 : (VS ? kSo + kSr : 4), kPW = kSlots * kRows * kPRow;
     __shared__ float s_q[kMaxGroupHeads][kDim];   // q' in the rotated/balanced domain, scaled
@@ -915,9 +916,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 
 template <int KT, int VT, int MB>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    // 8 waves where registers allow; the 4-bit TurboQuant V stages twice the P slots in LDS (the
-    // split V stages up to 12, in the compact 8-row form)
-    constexpr int NW = (MB == 1 && !(KT == kU8 && VT == kU8) && VT != kTb4) ? 8 : 4;
+    // 8 waves where registers allow (the 4-bit and split TurboQuant V stage 8 or 12 P slots, in
+    // the compact 8-row form with one head block)
+    constexpr int NW = (MB == 1 && !(KT == kU8 && VT == kU8)) ? 8 : 4;
     dim3 grid(p.n_splits_total, p.Hkv, p.batch);
     hipExtLaunchKernelGGL((decode_mfma_kernel<KT, VT, MB, NW>), grid, dim3(NW * 64), 0, s, ev0, ev1, 0, p);
     return hipGetLastError();
