@@ -198,7 +198,11 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     // waves fit
     constexpr bool kCmp = (VS || VT4) && MB == 1;
     constexpr int kRows = kCmp ? 8 : 16;
-    constexpr int kSlots = VT4 ? 8 : (VS ? kSo + kSr : 4), kPW = kSlots * kRows * kPRow;
+    // halves per wave: the staged P slots, and at least the 2 x 8 x 128 fp32 accumulator rows the
+    // epilogue stores in the same memory
+    constexpr int kSlots = VT4 ? 8 : (VS ? kSo + kSr : 4);
+    constexpr int kPW = (kSlots * kRows * kPRow > 2 * 8 * kDim * 2) ? kSlots * kRows * kPRow : 2 * 8 * kDim * 2;
+    static_assert(kPW * 2 >= 2 * 8 * kDim * 4, "the epilogue's accumulator rows fit in the staging area");
     __shared__ float s_q[kMaxGroupHeads][kDim];   // q' in the rotated/balanced domain, scaled
     __shared__ float s_qw[kMaxGroupHeads][kDim];  // plain q * scale * log2e (FP32 window)
     __shared__ float s_sp[KU ? 1 : kMaxGroupHeads][kDim]; // S q' (TurboQuant K)
