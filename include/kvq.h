@@ -142,9 +142,8 @@ typedef struct {
 
 enum {
     KVQ_OPT_SPLIT_TOKENS = 1, /* tokens per decode split (multiple of 64); 0 = automatic     */
-    KVQ_OPT_DECODE_PATH = 2   /* 0 = automatic, 1 = vector-ALU kernel, 2 = matrix-core kernel;
-                                 4-bit and split TurboQuant V have the matrix-core kernel
-                                 only (1 gives KVQ_ERR_UNSUPPORTED at decode time)        */
+    KVQ_OPT_DECODE_PATH = 2   /* 0 = automatic, 1 = vector-ALU kernel, 2 = matrix-core kernel
+                                 (every scheme has both)                                  */
 };
 
 /* Bytes of device memory a cache with this configuration needs (planes for every layer,

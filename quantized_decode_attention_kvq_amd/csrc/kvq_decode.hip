@@ -79,13 +79,29 @@ __device__ __forceinline__ uint32_t turbo_k_code(const uint8_t* row, int j) {
     return ((w[0] >> b) & 1u) | (((w[1] >> b) & 1u) << 1) | (((w[2] >> b) & 1u) << 2);
 }
 
-// 3-bit TurboQuant code of (token t, channel d) from the V plane's 32-token blocks.
-__device__ __forceinline__ uint32_t turbo_v_code(const uint8_t* codes, int t, int d) {
+// nb-bit TurboQuant code of (token t, channel d) from the V plane's 32-token blocks (nb = 3 or
+// 4 planes; word 2 nb (16 o + n) + 2 k + N / 4 of block t / 32).
+__device__ __forceinline__ uint32_t turbo_v_code(const uint8_t* codes, int t, int d, int nb) {
     const int o = (t & 31) >> 3, i = t & 7, n = d & 15, N = d >> 4;
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(codes + (size_t)(t >> 5) * 1536) +
-                        6 * (16 * o + n) + (N >> 2);
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(codes + (size_t)(t >> 5) * (512 * nb)) +
+                        2 * nb * (16 * o + n) + (N >> 2);
     const int b = 16 * (i & 1) + 4 * (N & 3) + (i >> 1);
-    return ((w[0] >> b) & 1u) | (((w[2] >> b) & 1u) << 1) | (((w[4] >> b) & 1u) << 2);
+    uint32_t c = 0;
+    for (int k = 0; k < nb; ++k) c |= ((w[2 * k] >> b) & 1u) << k;
+    return c;
+}
+
+// Split V (bo outlier bits, W = 2 bo - 1 words per (octet, column)): code of position d of token
+// t; the outlier half (d < 64) has bo planes at words W (16 o + n) + k, the rest bo - 1 at + bo + k.
+__device__ __forceinline__ uint32_t split_v_code(const uint8_t* codes, int t, int d, int bo) {
+    const int W = 2 * bo - 1, o = (t & 31) >> 3, i = t & 7, n = d & 15, N = d >> 4;
+    const int rest = d >= 64, nb = rest ? bo - 1 : bo;
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(codes + (size_t)(t >> 5) * (256 * W)) +
+                        W * (16 * o + n) + (rest ? bo : 0);
+    const int b = 16 * (i & 1) + 4 * (N & 3) + (i >> 1);
+    uint32_t c = 0;
+    for (int k = 0; k < nb; ++k) c |= ((w[k] >> b) & 1u) << k;
+    return c;
 }
 
 __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
@@ -318,10 +334,17 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
                 }
                 v0 = zc + sc * (float)q0;
                 v1 = zc + sc * (float)q1;
-            } else { // TurboQuant-MSE value (rotated domain)
+            } else if (VG.scheme == kTurboSplit) { // split: positions 2l, 2l + 1 of one half
+                const int rest = d0 >= 64, levels = rest ? (1 << (VG.bits - 1)) : (1 << VG.bits);
+                const float* mu = p.mu64 + (levels - 4);
+                const float nrm = h2f(reinterpret_cast<const uint16_t*>(vmeta)[2 * tok + rest]);
+                v0 = nrm * mu[split_v_code(vcodes, tok, d0, VG.bits)];
+                v1 = nrm * mu[split_v_code(vcodes, tok, d0 + 1, VG.bits)];
+            } else { // TurboQuant-MSE value (rotated domain), 3- or 4-bit codes
+                const float* mu = VG.bits == 4 ? p.mu16 : p.mu;
                 const float nrm = h2f(reinterpret_cast<const uint16_t*>(vmeta)[tok]);
-                v0 = nrm * p.mu[turbo_v_code(vcodes, tok, d0)];
-                v1 = nrm * p.mu[turbo_v_code(vcodes, tok, d0 + 1)];
+                v0 = nrm * mu[turbo_v_code(vcodes, tok, d0, VG.bits)];
+                v1 = nrm * mu[turbo_v_code(vcodes, tok, d0 + 1, VG.bits)];
             }
 #pragma unroll
             for (int h = 0; h < kMaxGroupHeads; ++h)

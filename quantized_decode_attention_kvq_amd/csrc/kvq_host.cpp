@@ -444,8 +444,6 @@ kvq_status make_decode(const kvq_cache* c, int layer, const void* q, int dtype, 
     }
     matrix = c->decode_path != 1 && mfma_path_supported(p);
     if (c->decode_path == 2 && !matrix) return KVQ_ERR_UNSUPPORTED;
-    // 4-bit and split TurboQuant V: matrix path only
-    if (!matrix && (c->turbo4() || c->split())) return KVQ_ERR_UNSUPPORTED;
     int st;
     if (c->split_tokens_opt > 0) {
         st = c->split_tokens_opt;

@@ -36,8 +36,6 @@ def _check_all_planes(case, li, heads=None, seqs=None):
 
 
 def _paths(wl):
-    if (wl.v_scheme == W.TURBO_MSE and wl.v_bits == 4) or wl.v_scheme == W.TURBO_SPLIT:
-        return (2,)  # 4-bit and split TurboQuant V: matrix-core kernel only
     return (1, 2)  # vector-ALU kernel, matrix-core kernel
 
 
@@ -205,14 +203,7 @@ def test_q8_0_k_turbo4_mse_v_small():
     assert np.array_equal(case.cache.table("mu16", 16).cpu().numpy().view(np.uint32), mu.view(np.uint32))
     assert np.array_equal(case.cache.table("theta16", 15).cpu().numpy().view(np.uint32), theta.view(np.uint32))
     planes = _check_all_planes(case, 0)
-    _decode_and_compare(case, 0, planes)
-    case.cache.set_option(2, 1)
-    q = W.gen_q(wl, 1, 0).to("cuda")
-    out = torch.zeros((1, wl.n_q_heads, 128), device="cuda")
-    with pytest.raises(case.K.KvqError) as e:
-        case.cache.attn_decode(0, q, out)
-    assert e.value.name == "KVQ_ERR_UNSUPPORTED"
-    case.cache.set_option(2, 0)
+    _decode_and_compare(case, 0, planes)  # both decode paths
 
 
 @pytest.mark.parametrize("wl", [W.LLAMA8B_32K_Q8_0_TURBO25_V, W.LLAMA8B_32K_Q8_0_TURBO35_V],
@@ -243,14 +234,7 @@ def test_turbo_split_v_small(wl):
         assert np.array_equal(th64[o:o + levels - 1].view(np.uint32), theta.view(np.uint32)), levels
     for li in range(2):
         planes = _check_all_planes(case, li)
-        _decode_and_compare(case, li, planes)
-    case.cache.set_option(2, 1)
-    q = W.gen_q(wl, 0, 0).to("cuda")
-    out = torch.zeros((1, wl.n_q_heads, 128), device="cuda")
-    with pytest.raises(case.K.KvqError) as e:
-        case.cache.attn_decode(0, q, out)
-    assert e.value.name == "KVQ_ERR_UNSUPPORTED"
-    case.cache.set_option(2, 0)
+        _decode_and_compare(case, li, planes)  # both decode paths
 
 
 def test_turbo_split_v_bf16_window_batch():
@@ -490,8 +474,6 @@ def _planes_equal(a, b, li, batch, n_heads):
 def test_fused_append_decode_equals_separate_calls(wl, n, path):
     # kvq_append_attn_decode == kvq_append + kvq_attn_decode: byte-identical planes and
     # bit-identical outputs over consecutive steps, with ragged lengths in the batch
-    if path not in _paths(wl):
-        pytest.skip("this cache has the matrix-core decode kernel only")
     _say("case: fused append+decode", wl.name, "n", n, "path", path)
     B = 2
     a = Case(wl, max(n, 1), layers=[0], batch=B, extra_tokens=8)
