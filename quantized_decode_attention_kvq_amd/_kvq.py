@@ -121,6 +121,60 @@ def _dtype(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+# Shapes each handle was created with: the C ABI takes raw pointers and no sizes, so the binding
+# checks every tensor against them before a pointer crosses into C (a wrong shape or dtype would
+# otherwise make a kernel read or write past the tensor).
+_SHAPES = {}
+
+
+def _dims(h):
+    key = h.value if isinstance(h, ctypes.c_void_p) else h
+    d = _SHAPES.get(key)
+    if d is None:
+        raise ValueError("unknown kvq handle (not created through this binding, or destroyed)")
+    return d
+
+
+def _tensor(t, name, shape, dtypes):
+    """Checks one tensor argument's shape (None = any extent) and dtype."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dim() != len(shape) or any(e is not None and t.shape[i] != e for i, e in enumerate(shape)):
+        want = "[" + ", ".join("*" if e is None else str(e) for e in shape) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    return t
+
+
+def _resident(**named):
+    """Every given tensor lives in device memory and is contiguous (the last check before C)."""
+    for name, t in named.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise TypeError(f"{name} must be a device (cuda) tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _inputs():
+    import torch
+    return (torch.float32, torch.bfloat16)
+
+
+def _same_dtype(*ts):
+    ts = [t for t in ts if t is not None]
+    if any(t.dtype != ts[0].dtype for t in ts):
+        raise TypeError("all inputs of one call must share one dtype: " + ", ".join(str(t.dtype) for t in ts))
+
+
+def _batch(h, B):
+    if not 1 <= B <= _dims(h)["max_batch"]:
+        raise ValueError(f"batch {B} outside 1 .. max_batch = {_dims(h)['max_batch']}")
+
+
 def make_config(**kw) -> kvq_config:
     c = kvq_config()
     for k, v in kw.items():
@@ -138,40 +192,85 @@ def kvq_cache_required_bytes(cfg: kvq_config) -> int:
 def kvq_cache_create(cfg: kvq_config, buf, stream=None):
     h = ctypes.c_void_p()
     nbytes = buf.numel() * buf.element_size()
+    _resident(buf=buf)
     _check(load().kvq_cache_create(ctypes.byref(cfg), _ptr(buf), nbytes, _stream(stream),
                                    ctypes.byref(h)), "kvq_cache_create")
+    _SHAPES[h.value] = {"n_layers": cfg.n_layers, "n_q_heads": cfg.n_q_heads,
+                        "n_kv_heads": cfg.n_kv_heads, "max_batch": cfg.max_batch}
     return h
 
 
 def kvq_cache_destroy(h):
     _check(load().kvq_cache_destroy(h), "kvq_cache_destroy")
+    _SHAPES.pop(h.value if isinstance(h, ctypes.c_void_p) else h, None)
 
 
 def kvq_set_random_tables(h, signs=None, qjl_S=None, stream=None):
+    """signs: [n_layers][n_kv_heads][2][128] fp32; qjl_S: [128][128] fp32 (either may be None)."""
+    import torch
+    d = _dims(h)
+    if signs is not None:
+        _tensor(signs, "signs", (d["n_layers"], d["n_kv_heads"], 2, 128), (torch.float32,))
+    if qjl_S is not None:
+        _tensor(qjl_S, "qjl_S", (128, 128), (torch.float32,))
+    _resident(signs=signs, qjl_S=qjl_S)
     _check(load().kvq_set_random_tables(h, _ptr(signs), _ptr(qjl_S), _stream(stream)),
            "kvq_set_random_tables")
 
 
 def kvq_calibrate(h, layer, Kc=None, Vc=None, stream=None):
+    """Kc, Vc: [n_tokens][n_kv_heads][128] calibration tokens of one dtype (either may be None)."""
+    d = _dims(h)
+    if Kc is None and Vc is None:
+        raise ValueError("kvq_calibrate needs Kc or Vc")
+    for name, t in (("Kc", Kc), ("Vc", Vc)):
+        if t is not None:
+            _tensor(t, name, (None, d["n_kv_heads"], 128), _inputs())
+    _same_dtype(Kc, Vc)
+    if Kc is not None and Vc is not None and Kc.shape[0] != Vc.shape[0]:
+        raise ValueError("Kc and Vc must hold the same number of tokens")
+    _resident(Kc=Kc, Vc=Vc)
     t = Kc if Kc is not None else Vc
     _check(load().kvq_calibrate(h, layer, _ptr(Kc), _ptr(Vc), _dtype(t), t.shape[0],
                                 _stream(stream)), "kvq_calibrate")
 
 
 def kvq_prefill_quantize(h, layer, K, V, stream=None):
-    """K, V: [batch][n_tokens][n_kv_heads][128]."""
+    """K, V: [batch][n_tokens][n_kv_heads][128], one dtype."""
+    d = _dims(h)
+    _tensor(K, "K", (None, None, d["n_kv_heads"], 128), _inputs())
+    _tensor(V, "V", tuple(K.shape), _inputs())
+    _same_dtype(K, V)
+    _batch(h, K.shape[0])
+    _resident(K=K, V=V)
     _check(load().kvq_prefill_quantize(h, layer, _ptr(K), _ptr(V), _dtype(K), K.shape[1],
                                        K.shape[0], _stream(stream)), "kvq_prefill_quantize")
 
 
 def kvq_append(h, layer, k, v, stream=None):
-    """k, v: [batch][n_kv_heads][128]."""
+    """k, v: [batch][n_kv_heads][128], one dtype."""
+    d = _dims(h)
+    _tensor(k, "k", (None, d["n_kv_heads"], 128), _inputs())
+    _tensor(v, "v", tuple(k.shape), _inputs())
+    _same_dtype(k, v)
+    _batch(h, k.shape[0])
+    _resident(k=k, v=v)
     _check(load().kvq_append(h, layer, _ptr(k), _ptr(v), _dtype(k), k.shape[0],
                              _stream(stream)), "kvq_append")
 
 
+def _check_q_out(h, q, out, lead):
+    import torch
+    d = _dims(h)
+    _tensor(q, "q", (*lead, d["n_q_heads"], 128), _inputs())
+    _tensor(out, "out", tuple(q.shape), (torch.float32,))
+    _batch(h, q.shape[0])
+
+
 def kvq_attn_decode(h, layer, q, out, softmax_scale=0.0, stream=None):
     """q: [batch][n_q_heads][128]; out: [batch][n_q_heads][128] fp32."""
+    _check_q_out(h, q, out, (None,))
+    _resident(q=q, out=out)
     _check(load().kvq_attn_decode(h, layer, _ptr(q), _dtype(q), _ptr(out), q.shape[0],
                                   float(softmax_scale), _stream(stream)), "kvq_attn_decode")
 
@@ -179,6 +278,8 @@ def kvq_attn_decode(h, layer, q, out, softmax_scale=0.0, stream=None):
 def kvq_attn_prefill(h, layer, q, out, softmax_scale=0.0, workspace=None, stream=None):
     """q: [batch][n_q][Hq][128] (f32 or bf16), out: [batch][n_q][Hq][128] f32; workspace: a
     device tensor (any dtype, contiguous) or None for the cache's own."""
+    _check_q_out(h, q, out, (None, None))
+    _resident(q=q, out=out, workspace=workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().kvq_attn_prefill(h, layer, _ptr(q), _dtype(q), _ptr(out), q.shape[1], q.shape[0],
                                    float(softmax_scale), _ptr(workspace), ws_bytes, _stream(stream)),
@@ -194,6 +295,12 @@ def kvq_attn_prefill_workspace(h, layer, n_q, batch) -> int:
 
 def kvq_append_attn_decode(h, layer, k, v, q, out, softmax_scale=0.0, stream=None):
     """k, v: [batch][n_kv_heads][128]; q: [batch][n_q_heads][128]; out: fp32 like q."""
+    d = _dims(h)
+    _check_q_out(h, q, out, (None,))
+    _tensor(k, "k", (q.shape[0], d["n_kv_heads"], 128), _inputs())
+    _tensor(v, "v", tuple(k.shape), _inputs())
+    _same_dtype(k, v, q)
+    _resident(k=k, v=v, q=q, out=out)
     _check(load().kvq_append_attn_decode(h, layer, _ptr(k), _ptr(v), _ptr(q), _dtype(q), _ptr(out),
                                          q.shape[0], float(softmax_scale), _stream(stream)),
            "kvq_append_attn_decode")

@@ -543,7 +543,11 @@ kvq_status kvq_append_attn_decode(kvq_cache* c, int layer, const void* k, const 
         e = launch_decode_merge(p, s);
     } else {
         e = launch_quantize(qp, s);
-        if (e == hipSuccess) e = launch_decode(c, p, false, s);
+        if (e != hipSuccess) { // nothing was enqueued: the append did not happen
+            for (int b = 0; b < batch; ++b) len[b] -= 1;
+            return dev_fail(c, e);
+        }
+        e = launch_decode(c, p, false, s);
     }
     if (e != hipSuccess) return dev_fail(c, e);
     return KVQ_OK;

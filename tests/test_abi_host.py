@@ -102,3 +102,45 @@ def test_null_handle_calls_rejected():
     assert lib.kvq_set_timing_events(None, None, None) == 1
     assert lib.kvq_set_option(None, 1, 0) == 1
     assert K.kvq_status_str(0) == "ok" and K.kvq_status_str(3) == "context capacity exceeded"
+
+
+def test_binding_refuses_bad_tensors_before_c():
+    """The binding checks every tensor against the handle's shapes, the call's dtype rules and
+    device residency before a pointer reaches C (which takes no sizes).  A fake handle is
+    registered with the binding only: no call below may reach the library."""
+    import torch
+    h = ctypes.c_void_p(0x5000)
+    K._SHAPES[h.value] = {"n_layers": 2, "n_q_heads": 24, "n_kv_heads": 8, "max_batch": 2}
+    try:
+        q, out = torch.zeros(1, 24, 128), torch.zeros(1, 24, 128)
+        with pytest.raises(TypeError, match="device"):
+            K.kvq_attn_decode(h, 0, q, out)  # host tensors
+        with pytest.raises(ValueError, match="shape"):
+            K.kvq_attn_decode(h, 0, torch.zeros(1, 23, 128), out)  # head count
+        with pytest.raises(ValueError, match="shape"):
+            K.kvq_attn_decode(h, 0, q, torch.zeros(1, 24, 64))  # undersized out
+        with pytest.raises(TypeError, match="dtype"):
+            K.kvq_attn_decode(h, 0, q, torch.zeros(1, 24, 128, dtype=torch.bfloat16))  # out not fp32
+        with pytest.raises(TypeError, match="dtype"):
+            K.kvq_attn_decode(h, 0, q.double(), out)  # unsupported input dtype
+        with pytest.raises(ValueError, match="batch"):
+            K.kvq_attn_decode(h, 0, torch.zeros(3, 24, 128), torch.zeros(3, 24, 128))  # > max_batch
+        k32, v32 = torch.zeros(1, 8, 128), torch.zeros(1, 8, 128)
+        with pytest.raises(TypeError, match="one dtype"):
+            K.kvq_append_attn_decode(h, 0, k32, v32, q.bfloat16(), out)  # mixed input dtypes
+        with pytest.raises(ValueError, match="shape"):
+            K.kvq_append_attn_decode(h, 0, torch.zeros(2, 8, 128), torch.zeros(2, 8, 128), q, out)
+        with pytest.raises(ValueError, match="shape"):
+            K.kvq_prefill_quantize(h, 0, torch.zeros(1, 5, 8, 128), torch.zeros(1, 4, 8, 128))
+        with pytest.raises(ValueError, match="shape"):
+            K.kvq_append(h, 0, torch.zeros(1, 7, 128), torch.zeros(1, 7, 128))  # kv head count
+        with pytest.raises(ValueError, match="shape"):
+            K.kvq_set_random_tables(h, torch.zeros(3, 8, 2, 128))  # layer count
+        with pytest.raises(ValueError, match="shape"):
+            K.kvq_attn_prefill(h, 0, torch.zeros(1, 4, 24, 128), torch.zeros(1, 4, 24, 127))
+        with pytest.raises(TypeError, match="dtype"):
+            K.kvq_calibrate(h, 0, torch.zeros(512, 8, 128), torch.zeros(512, 8, 128).bfloat16())
+        with pytest.raises(ValueError, match="unknown kvq handle"):
+            K.kvq_attn_decode(ctypes.c_void_p(0x6000), 0, q, out)
+    finally:
+        K._SHAPES.pop(h.value)

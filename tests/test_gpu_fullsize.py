@@ -99,3 +99,74 @@ def test_fullsize_dense27b_120k_b4(wl):
                          ids=lambda w: w.name)
 def test_fullsize_llama8b_32k_turbo_split_v(wl):
     _run(wl, layers=[0, 31], seqs=[0], plane_heads=[0, 4, 7], attn_heads=[0, 4, 7])
+
+
+def _fused_steps(wl, layers, seqs, heads, batch=None):
+    """kvq_append_attn_decode, the call bench.py times, at the workload's full context: one step
+    on the matrix-core path (the automatic choice, with the automatic split plan) and one on the
+    vector-ALU path, each checked against the oracle: the planes (the appended token's codes,
+    scales and window slot included) bit-exact and the output of every query head of the sampled
+    kv heads within tolerance."""
+    B = wl.batch if batch is None else batch
+    _say(f"case: fused append+decode, {wl.name} full context {wl.context}, batch {B}, layers {layers}")
+    case = Case(wl, wl.context, layers=layers, batch=B, gen_device="cuda", extra_tokens=2)
+    _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS)
+    G = wl.group
+    cap = case.cache.cfg.max_context
+    for li, layer in enumerate(layers):
+        case.prefill(li)
+        src = case.kv(layer)
+        orc = {}  # (b, h, tensor) -> (plane, tables), grown by one token per step
+        for b in seqs:
+            for h in heads:
+                for tensor in (0, 1):
+                    tb = case.oracle_tables(li, h, tensor, mu, theta)
+                    scheme = wl.k_scheme if tensor == 0 else wl.v_scheme
+                    bits = wl.k_bits if tensor == 0 else wl.v_bits
+                    rot = (wl.rotate_k if tensor == 0 else wl.rotate_v) or W.is_turbo(scheme)
+                    sink = wl.sinkhorn_iters > 0 and not W.is_turbo(scheme)
+                    p = oracle.Plane(scheme, bits, rot, sink, wl.window, tensor, cap)
+                    p.append(src[tensor][b, :, h].float().cpu().numpy(), tb)
+                    orc[(b, h, tensor)] = (p, tb)
+        case.inputs.clear()
+        del src
+        for s, path in enumerate((0, 1)):  # 0: automatic (matrix cores), 1: vector ALU
+            case.cache.set_option(2, path)
+            k, v = W.gen_step_kv(wl, layer, s, device="cuda", batch=B)
+            q = W.gen_q(wl, layer, 1 + s, device="cuda", batch=B)
+            out = torch.full((B, wl.n_q_heads, 128), float("nan"), device="cuda")
+            case.cache.append_attn_decode(li, k, v, q, out)
+            torch.cuda.synchronize()
+            assert case.cache.length(li, 0) == wl.context + 1 + s
+            got = out.cpu().numpy()
+            assert np.isfinite(got).all()
+            kn, vn, qn = k.float().cpu().numpy(), v.float().cpu().numpy(), q.float().cpu().numpy()
+            worst = (0.0, 0.0)
+            for b in seqs:
+                for h in heads:
+                    for tensor, x in ((0, kn), (1, vn)):
+                        p, tb = orc[(b, h, tensor)]
+                        p.append(x[b, h], tb)
+                        compare_plane(case.device_plane(li, b, h, tensor), p,
+                                      f"layer {layer} seq {b} head {h} tensor {tensor} path {path}")
+                    pk, tk = orc[(b, h, 0)]
+                    pv, tv = orc[(b, h, 1)]
+                    ref = oracle.attention(pk, pv, tk, tv, qn[b, h * G:(h + 1) * G])
+                    blk = got[b, h * G:(h + 1) * G]
+                    r, m = rel_l2(blk, ref), max_abs(blk, ref)
+                    worst = (max(worst[0], r), max(worst[1], m))
+                    assert r <= REL_L2_TOL and m <= MAX_ABS_TOL, (layer, path, b, h, r, m)
+            _say(f"  layer {layer} path {path} n={wl.context + 1 + s}: planes bit-exact, attention "
+                 f"rel_l2<={worst[0]:.2e} max_abs<={worst[1]:.2e}")
+        case.cache.set_option(2, 0)
+        torch.cuda.empty_cache()
+
+
+def test_fullsize_fused_llama3b_32k_kvarn():
+    # the benchmarked workload and call: 32K WHT + Sinkhorn U4, first and last layer
+    _fused_steps(W.LLAMA3B_32K_KVARN, layers=[0, 27], seqs=[0], heads=ALL8)
+
+
+def test_fullsize_fused_llama3b_128k_progressive_b1():
+    # 128K progressive: the new token lands in the FP32 window, owned by the window workgroup
+    _fused_steps(W.LLAMA3B_128K_PROGRESSIVE, layers=[0, 27], seqs=[0], heads=[0, 3, 7])

@@ -388,13 +388,16 @@ def test_capacity_and_batch_limits_leave_state_unchanged():
     assert e.value.name == "KVQ_ERR_CAPACITY"
     k3 = W.gen_kv(wl, 7, 0, 1, batch=3).to("cuda")
     v3 = W.gen_kv(wl, 7, 1, 1, batch=3).to("cuda")
-    with pytest.raises(K.KvqError) as e:
-        case.cache.prefill_quantize(0, k3, v3)  # batch 3 > max_batch 2
-    assert e.value.name == "KVQ_ERR_INVALID_ARG"
+    with pytest.raises(ValueError):  # the binding refuses batch 3 > max_batch 2 ...
+        case.cache.prefill_quantize(0, k3, v3)
+    lib = K._kvq.load()  # ... and so does the library itself, called directly
+    st = lib.kvq_prefill_quantize(case.cache.handle, 0, k3.data_ptr(), v3.data_ptr(), 0, 1, 3, None)
+    assert st == 1  # KVQ_ERR_INVALID_ARG
     q3 = W.gen_q(wl, 0, 0, batch=3).to("cuda")
     out3 = torch.full((3, 24, 128), 3.0, device="cuda")
-    with pytest.raises(K.KvqError):
+    with pytest.raises(ValueError):
         case.cache.attn_decode(0, q3, out3)
+    assert lib.kvq_attn_decode(case.cache.handle, 0, q3.data_ptr(), 0, out3.data_ptr(), 3, 0.0, None) == 1
     torch.cuda.synchronize()
     assert case.cache.length(0, 0) == 90 and case.cache.length(0, 1) == 90
     assert bool((out3 == 3.0).all())
@@ -516,3 +519,88 @@ def test_fused_append_decode_matches_oracle():
                                 planes={h: planes[(0, h)] for h in range(wl.n_kv_heads)})
     got = out.cpu().numpy()[0]
     assert rel_l2(got, ref) <= REL_L2_TOL and max_abs(got, ref) <= MAX_ABS_TOL
+
+
+# Progressive caches at the edges of the FP32 window: every token in the ring (n <= 128), the
+# first token read from the codes (n = 129), and a few beyond.  Plain, rotated + balanced, and
+# TurboQuant-QJL keys beside the window.
+WINDOW_EDGE_NS = [1, 2, 64, 127, 128, 129, 130, 192, 257]
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE,
+                                W.LLAMA3B_32K_KVARN.with_(name="llama3b-kvarn-u4-window", window=128),
+                                W.LLAMA3B_32K_TURBO.with_(name="llama3b-turboqjl-k-window", window=128)],
+                         ids=lambda w: w.name)
+def test_window_edges_decode_and_fused(wl, path):
+    """At each n the cache holds tokens 0 .. n - 2 (bulk prefill and appends), token n - 1 comes
+    through kvq_append_attn_decode, then kvq_attn_decode runs on the same cache: planes and ring
+    bit-exact, both outputs against the oracle."""
+    _say("case: window edges,", wl.name, "path", path, WINDOW_EDGE_NS)
+    n_max = max(WINDOW_EDGE_NS)
+    case = Case(wl, n_max, layers=[0])
+    case.cache.set_option(2, path)
+    k_all, v_all = case.kv(0)
+    done = 0
+    for n in WINDOW_EDGE_NS:
+        if n - 1 > done:
+            case.cache.prefill_quantize(0, k_all[:, done:n - 1].contiguous(), v_all[:, done:n - 1].contiguous())
+            done = n - 1
+        q = W.gen_q(wl, 0, n).to("cuda")
+        o_fused = torch.full((1, wl.n_q_heads, 128), float("nan"), device="cuda")
+        case.cache.append_attn_decode(0, k_all[:, n - 1].contiguous(), v_all[:, n - 1].contiguous(), q, o_fused)
+        done = n
+        o_dec = torch.full_like(o_fused, float("nan"))
+        case.cache.attn_decode(0, q, o_dec)
+        torch.cuda.synchronize()
+        assert case.cache.length(0, 0) == n
+        _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS)
+        planes = {}
+        for h in range(wl.n_kv_heads):
+            row = []
+            for tensor in (0, 1):
+                tb = case.oracle_tables(0, h, tensor, mu, theta)
+                p, _ = case.oracle_plane(0, 0, h, tensor, tb, n=n)
+                if h in (0, 7):
+                    compare_plane(case.device_plane(0, 0, h, tensor), p, f"n {n} head {h} tensor {tensor}")
+                row += [p, tb]
+            planes[h] = row
+        ref = oracle_attention_case(case, 0, 0, q.float().cpu().numpy()[0], planes=planes)
+        for label, o in (("fused", o_fused), ("decode", o_dec)):
+            got = o.cpu().numpy()[0]
+            r, m = rel_l2(got, ref), max_abs(got, ref)
+            assert r <= REL_L2_TOL and m <= MAX_ABS_TOL, (n, label, r, m)
+        _say(f"  n={n}: planes bit-exact, fused and decode within tolerance")
+
+
+# Five query heads per kv head (the 27B shape) with the value coders whose matrix-core kernels
+# take the two-head-block form: 4-bit TurboQuant-MSE V and the split V at 2.5 / 3.5 bits.
+G5_TURBO_V = [
+    W.DENSE27B_120K_Q8_0.with_(name="dense27b-q8_0-k-turbo4mse-v", v_scheme=W.TURBO_MSE, v_bits=4,
+                               rotate_v=True),
+    W.DENSE27B_120K_Q8_0.with_(name="dense27b-q8_0-k-turbo2.5split-v", v_scheme=W.TURBO_SPLIT, v_bits=3,
+                               rotate_v=True, calib_tokens=512),
+    W.DENSE27B_120K_Q8_0.with_(name="dense27b-q8_0-k-turbo3.5split-v", v_scheme=W.TURBO_SPLIT, v_bits=4,
+                               rotate_v=True, calib_tokens=512),
+]
+
+
+@pytest.mark.parametrize("wl", G5_TURBO_V, ids=lambda w: w.name)
+def test_gqa5_turbo_values_both_paths(wl):
+    _say("case:", wl.name, "2 seqs, 300 prefill + 44 appends + 1 fused step")
+    case = Case(wl, 345, layers=[0], batch=2)
+    k, v = case.kv(0)
+    case.cache.prefill_quantize(0, k[:, :300].contiguous(), v[:, :300].contiguous())
+    for t in range(300, 344):
+        case.cache.append(0, k[:, t].contiguous(), v[:, t].contiguous())
+    q = W.gen_q(wl, 0, 9, batch=2).to("cuda")
+    out = torch.full((2, wl.n_q_heads, 128), float("nan"), device="cuda")
+    case.cache.append_attn_decode(0, k[:, 344].contiguous(), v[:, 344].contiguous(), q, out)
+    torch.cuda.synchronize()
+    planes = _check_all_planes(case, 0, heads=[0, 7])
+    qn = q.float().cpu().numpy()
+    for b in (0, 1):
+        ref = oracle_attention_case(case, 0, b, qn[b])
+        r, m = rel_l2(out.cpu().numpy()[b], ref), max_abs(out.cpu().numpy()[b], ref)
+        assert r <= REL_L2_TOL and m <= MAX_ABS_TOL, (b, r, m)
+    _decode_and_compare(case, 0, None)  # both decode paths
