@@ -8,7 +8,10 @@ Parity notes: every function here is pinned by ``tests/test_oracle_pins.py`` exc
 Sinkhorn calibration's agreement with KVarN itself (the pages give no values), which is
 "parity unpinned" beyond the invariants tested there.  The outlier split (TURBO_SPLIT) is pinned
 by the 64-point Sylvester matrix, brute-force outlier ranking with ties, nearest-centroid codes,
-the textbook 4-level codebook and distortions, and hand-derived layout words.
+the textbook 4-level codebook and distortions, and hand-derived layout words.  Uniform 3-bit
+planes (three bit planes in the TurboQuant 3-bit byte layout, uniform fp16 scale/zero meta) are
+pinned by the quantizer's error bound, brute-force nearest level and grid-point recovery at
+L = 7, hand-derived K and V words, round trips, and lossless-grid attention against the textbook.
 """
 from __future__ import annotations
 

@@ -526,6 +526,11 @@ void orc_split_encode(const float* x, const orc_tables* tb, int bits_o, uint8_t*
  *
  * Uniform planes of either tensor hold a whole number of 64-token blocks.
  *
+ * Uniform 3-bit codes (reading of "3-bit group packing"; the pages print no layout) are kept as
+ * three bit planes in exactly the byte layout of the TurboQuant 3-bit planes below (K: 48-byte
+ * rows in the uniform K row order; V: 1536-byte blocks of 32 tokens), with the uniform meta
+ * (16 B per token, K in row order, V in token order): 48 + 16 = 64 B per token-head.
+ *
  * Uniform V (blocks of 32 tokens, head dimension outermost within 8-token lanes).  Token t:
  * block b = t/32, tau = t%32, kb = tau/8, i = tau%8; element d: n = d%16, N = d/16.
  * 4-bit block (2048 B): u32 word 8*(16*kb + n) + N, token i at bit 16*(i%2) + 4*(i/2).
@@ -629,6 +634,29 @@ static void pack_token(const orc_plane_cfg* pc, int t, const uint8_t* code, cons
                        const uint16_t* z16, uint16_t n16, uint16_t g16, const uint8_t* bits,
                        uint8_t* codes, uint8_t* meta, uint8_t* qjl)
 {
+    if (uniform_layout(pc) && pc->bits == 3) {
+        /* 3-bit codes: the three bit planes of the TurboQuant 3-bit layout, uniform meta */
+        if (pc->tensor == ORC_TENSOR_K) {
+            size_t row = k_row(t);
+            uint8_t* r = codes + row * 48;
+            for (int j = 0; j < D; j++)
+                for (int k = 0; k < 3; k++) put_bit(r + 12 * (j / 32) + 4 * k, ibit(j % 32), code[j] >> k);
+            uint8_t* m = meta + row * 16;
+            for (int g = 0; g < NG; g++) {
+                put_u16(m + 2 * g, s16[g]);
+                put_u16(m + 8 + 2 * g, z16[g]);
+            }
+        } else {
+            for (int d = 0; d < D; d++)
+                for (int k = 0; k < 3; k++) put_bit(codes + tv_word(t, d, k, 3), tv_bit(t, d), code[d] >> k);
+            uint8_t* m = meta + (size_t)t * 16;
+            for (int g = 0; g < NG; g++) {
+                put_u16(m + 2 * g, s16[g]);
+                put_u16(m + 8 + 2 * g, z16[g]);
+            }
+        }
+        return;
+    }
     if (uniform_layout(pc)) {
         if (pc->tensor == ORC_TENSOR_K) {
             size_t row = k_row(t);
@@ -699,6 +727,28 @@ static void pack_token(const orc_plane_cfg* pc, int t, const uint8_t* code, cons
 void orc_plane_read(const orc_plane_cfg* pc, const uint8_t* codes, const uint8_t* meta,
                     const uint8_t* qjl, int t, uint8_t* code, uint16_t* meta8, uint8_t* bits)
 {
+    if (uniform_layout(pc) && pc->bits == 3) {
+        const uint8_t* m;
+        if (pc->tensor == ORC_TENSOR_K) {
+            size_t row = k_row(t);
+            const uint8_t* r = codes + row * 48;
+            for (int j = 0; j < D; j++) {
+                int c = 0;
+                for (int k = 0; k < 3; k++) c |= get_bit(r + 12 * (j / 32) + 4 * k, ibit(j % 32)) << k;
+                code[j] = (uint8_t)c;
+            }
+            m = meta + row * 16;
+        } else {
+            for (int d = 0; d < D; d++) {
+                int c = 0;
+                for (int k = 0; k < 3; k++) c |= get_bit(codes + tv_word(t, d, k, 3), tv_bit(t, d)) << k;
+                code[d] = (uint8_t)c;
+            }
+            m = meta + (size_t)t * 16;
+        }
+        for (int k = 0; k < 8; k++) meta8[k] = get_u16(m + 2 * k);
+        return;
+    }
     if (uniform_layout(pc)) {
         const uint8_t* m;
         if (pc->tensor == ORC_TENSOR_K) {

@@ -43,7 +43,7 @@ enum { ORC_TENSOR_K = 0, ORC_TENSOR_V = 1 };
 /* One (layer, sequence, kv head, tensor) plane description. */
 typedef struct {
     int scheme;    /* ORC_UNIFORM / ORC_TURBO_QJL / ORC_TURBO_MSE / ORC_Q8_0 / ORC_TURBO_SPLIT */
-    int bits;      /* uniform: 4 or 8; turbo: 3 (MSE V also 4); split: outlier bits 3 or 4 */
+    int bits;      /* uniform: 3, 4 or 8; turbo: 3 (MSE V also 4); split: outlier bits 3 or 4 */
     int rotate;    /* random-sign WHT before coding (always on for turbo) */
     int sinkhorn;  /* fold 1/c before uniform coding */
     int window;    /* FP32 window W: 0 (flat) or 128 (progressive) */

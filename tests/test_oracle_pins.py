@@ -132,7 +132,7 @@ def _deq(codes, s16, z16):
     return z + s * codes.astype(np.float64), s, z
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [3, 4, 8])
 def test_quant_group_error_bound_and_range(bits):
     L = (1 << bits) - 1
     rng = np.random.default_rng(10 + bits)
@@ -153,7 +153,7 @@ def test_quant_group_error_bound_and_range(bits):
             assert np.all(err <= s / 2 + L * s * 2.0 ** -12 + slack + 1e-12)
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [3, 4, 8])
 def test_quant_group_brute_force_nearest_level(bits):
     # code = argmin_c |y - (z + s c)| over all L+1 levels, except inputs within float rounding
     # of a tie between two levels.
@@ -173,7 +173,7 @@ def test_quant_group_brute_force_nearest_level(bits):
         assert ok.all()
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [3, 4, 8])
 def test_quant_group_grid_points_recovered(bits):
     # y = z + s*c with fp16 z, s and the extreme codes 0 and L present: lossless.
     L = (1 << bits) - 1
@@ -331,6 +331,38 @@ def test_layout_golden_words():
     assert (_word(pv.codes, w) >> bit) & 0xF == 7
 
 
+def test_layout_golden_words_uniform3():
+    # 3-bit uniform codes: bit planes in the TurboQuant 3-bit layout, uniform meta; the words were
+    # worked out by hand from the layout definition
+    g = _golden("layout_words.txt")
+    tb = oracle.TableSet()
+    x = (np.arange(128) % 8).astype(np.float32)
+    pk = oracle.Plane(oracle.UNIFORM, 3, False, False, 0, oracle.TENSOR_K, 128)
+    pk.append(np.zeros((5, 128), np.float32), tb)
+    pk.append(x, tb)  # token 5
+    row = int(g["k_row_of_t5"])
+    rb = pk.codes[48 * row:48 * row + 48]
+    for w in range(4):
+        assert _word(rb, w) == int(g[f"u3k_t5_word{w}"], 16), w
+    assert [hex(v) for v in np.frombuffer(pk.meta[16 * row:16 * row + 8].tobytes(), np.uint16)] == \
+        [g["u3k_t5_meta_scale"]] * 4
+    assert not pk.meta[16 * row + 8:16 * row + 16].any()
+    code, _, _ = pk.read(5)
+    assert np.array_equal(code, np.arange(128) % 8)
+    pv = oracle.Plane(oracle.UNIFORM, 3, False, False, 0, oracle.TENSOR_V, 64)
+    X = np.zeros((16, 128), np.float32)
+    X[:, 1] = 7.0
+    X[:8, 0] = np.arange(8)
+    X[9, 17] = 5.0
+    pv.append(X, tb)
+    for w in (0, 2, 4, 6):
+        assert _word(pv.codes, w) == int(g[f"u3v_word{w}"], 16), w
+    w0, bit = int(g["u3v_t9_d17_word0"]), int(g["u3v_t9_d17_bit"])
+    assert [(_word(pv.codes, w0 + 2 * k) >> bit) & 1 for k in range(3)] == [1, 0, 1]
+    # 48 B of codes + 16 B of meta per token-head
+    assert (pk.codes.size + pk.meta.size) / 128 == 64
+
+
 def test_layout_golden_turbo_bits():
     # Bit positions of turbo codes and QJL signs against hand-derived word/bit numbers; the codes
     # themselves come from turbo_encode, which is pinned separately.
@@ -362,6 +394,7 @@ def test_layout_golden_turbo_bits():
 
 
 @pytest.mark.parametrize("scheme,bits,tensor", [
+    (oracle.UNIFORM, 3, oracle.TENSOR_K), (oracle.UNIFORM, 3, oracle.TENSOR_V),
     (oracle.UNIFORM, 4, oracle.TENSOR_K), (oracle.UNIFORM, 4, oracle.TENSOR_V),
     (oracle.UNIFORM, 8, oracle.TENSOR_K), (oracle.UNIFORM, 8, oracle.TENSOR_V),
     (oracle.TURBO_QJL, 3, oracle.TENSOR_K), (oracle.TURBO_MSE, 3, oracle.TENSOR_V),
@@ -691,7 +724,7 @@ def _grid_tokens(rng, n, bits):
     return X
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [3, 4, 8])
 def test_attention_lossless_grid_equals_textbook(bits):
     rng = np.random.default_rng(100 + bits)
     n, G = 37, 3
