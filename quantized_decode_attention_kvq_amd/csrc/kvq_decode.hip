@@ -217,7 +217,15 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
                 for (int h = 0; h < kMaxGroupHeads; ++h)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) dot[h][g] = 0.0f;
-                if (KG.bits == 4) {
+                if (KG.bits == 3) { // three bit planes per group in a 48-byte row
+                    const uint8_t* r = kcodes + (size_t)row * 48;
+                    for (int j = 0; j < kDim; ++j) {
+                        const float cv = (float)turbo_k_code(r, j);
+#pragma unroll
+                        for (int h = 0; h < kMaxGroupHeads; ++h)
+                            if (h < G) dot[h][j >> 5] += cv * qp[h][j];
+                    }
+                } else if (KG.bits == 4) {
                     const uint32_t* r = reinterpret_cast<const uint32_t*>(kcodes + (size_t)row * 64);
 #pragma unroll
                     for (int w = 0; w < 16; ++w) {
@@ -322,7 +330,10 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
                 const int g = d0 >> 5;
                 const float sc = h2f(mt[g]), zc = h2f(mt[4 + g]);
                 uint32_t q0, q1;
-                if (VG.bits == 4) {
+                if (VG.bits == 3) { // bit planes in the TurboQuant-MSE V layout
+                    q0 = turbo_v_code(vcodes, tok, d0, 3);
+                    q1 = turbo_v_code(vcodes, tok, d0 + 1, 3);
+                } else if (VG.bits == 4) {
                     const uint32_t* bp = reinterpret_cast<const uint32_t*>(vcodes + (size_t)blk * 2048);
                     const int sh = 16 * (i & 1) + 4 * (i >> 1);
                     q0 = (bp[w0] >> sh) & 15u;

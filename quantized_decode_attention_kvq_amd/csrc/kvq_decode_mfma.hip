@@ -48,9 +48,10 @@ constexpr int kPRow = 72;                 // halves per staged P row: 64 tokens 
 constexpr int kPWave = 4 * 16 * kPRow;    // halves per wave: [group | plane][16 rows][token]
 constexpr float kKappa = 0.0097915166977774f; // sqrt(pi/2) / 128
 // cache kinds (template parameters)
-// uniform 4-bit, uniform 8-bit, TurboQuant 3-bit, TurboQuant-MSE 4-bit (V only), and the split
-// TurboQuant-MSE V with 3 / 4 bits on the outlier half (2.5 / 3.5 bits per channel)
-constexpr int kU4 = 0, kU8 = 1, kTb = 2, kTb4 = 3, kTs3 = 4, kTs4 = 5;
+// uniform 4-bit, uniform 8-bit, TurboQuant 3-bit, TurboQuant-MSE 4-bit (V only), the split
+// TurboQuant-MSE V with 3 / 4 bits on the outlier half (2.5 / 3.5 bits per channel), and uniform
+// 3-bit (bit planes in the TurboQuant 3-bit layout, uniform scale / zero)
+constexpr int kU4 = 0, kU8 = 1, kTb = 2, kTb4 = 3, kTs3 = 4, kTs4 = 5, kU3 = 6;
 
 // Eight one-bit operands from a half-interleaved word: quarter q (0..3) of each half, i.e. bits
 // 4q + v and 16 + 4q + v (v = 0..3).  Operand 2v + h is that bit times 2^(4(q%2) + v - 24).
@@ -62,6 +63,46 @@ __device__ __forceinline__ u4 bits8(uint32_t w, int q) {
     r.y = x & (m << 1);
     r.z = x & (m << 2);
     r.w = x & (m << 3);
+    return r;
+}
+
+// Eight 3-bit codes from the three bit-plane words of a half-interleaved group, quarter q of each
+// half: operand 2v + h is the code whose bits sit at 16h + 4q + v of the three words, as the fp16
+// subnormal code * 2^(4(q%2) + v - 24) (the three bits land on consecutive mantissa bits).
+__device__ __forceinline__ u4 codes3x8(uint32_t p0, uint32_t p1, uint32_t p2, int q) {
+    const uint32_t x0 = (q & 2) ? (p0 >> 8) : p0, x1 = (q & 2) ? (p1 >> 8) : p1, x2 = (q & 2) ? (p2 >> 8) : p2;
+    const uint32_t m = 0x00010001u << (4 * (q & 1));
+    u4 r;
+    r.x = (x0 & m) | ((x1 & m) << 1) | ((x2 & m) << 2);
+    r.y = (x0 & (m << 1)) | ((x1 & (m << 1)) << 1) | ((x2 & (m << 1)) << 2);
+    r.z = (x0 & (m << 2)) | ((x1 & (m << 2)) << 1) | ((x2 & (m << 2)) << 2);
+    r.w = (x0 & (m << 3)) | ((x1 & (m << 3)) << 1) | ((x2 & (m << 3)) << 2);
+    return r;
+}
+
+// The same eight codes centred, as exact fp16 (code - 4) * 2^(4(q%2) + v): the code bits are
+// placed in the mantissa of 1024 (0x6400) and 1024 + 4 * 2^(4(q%2) + v) is subtracted with one
+// packed fp16 add per operand pair.
+__device__ __forceinline__ h8 centred3x8(uint32_t p0, uint32_t p1, uint32_t p2, int q) {
+    const u4 c = codes3x8(p0, p1, p2, q);
+    const _Float16 b = (_Float16)(q & 1 ? 16.0f : 1.0f);
+    const h2v k0 = {(_Float16)1024.0f + (_Float16)4.0f * b, (_Float16)1024.0f + (_Float16)4.0f * b};
+    const h2v k1 = {(_Float16)1024.0f + (_Float16)8.0f * b, (_Float16)1024.0f + (_Float16)8.0f * b};
+    const h2v k2 = {(_Float16)1024.0f + (_Float16)16.0f * b, (_Float16)1024.0f + (_Float16)16.0f * b};
+    const h2v k3 = {(_Float16)1024.0f + (_Float16)32.0f * b, (_Float16)1024.0f + (_Float16)32.0f * b};
+    const h2v a0 = __builtin_bit_cast(h2v, c.x | 0x64006400u) - k0;
+    const h2v a1 = __builtin_bit_cast(h2v, c.y | 0x64006400u) - k1;
+    const h2v a2 = __builtin_bit_cast(h2v, c.z | 0x64006400u) - k2;
+    const h2v a3 = __builtin_bit_cast(h2v, c.w | 0x64006400u) - k3;
+    h8 r;
+    r[0] = a0[0];
+    r[1] = a0[1];
+    r[2] = a1[0];
+    r[3] = a1[1];
+    r[4] = a2[0];
+    r[5] = a2[1];
+    r[6] = a3[0];
+    r[7] = a3[1];
     return r;
 }
 
@@ -100,6 +141,12 @@ template <>
 struct KRegs<kTb> {
     uint32_t pw[4][3], qw[4], nm[4];
 };
+// uniform 3-bit K: the three plane words of group lane / 16 and the 16-byte meta row
+template <>
+struct KRegs<kU3> {
+    uint32_t pw[4][3];
+    u4 km[4];
+};
 template <int VT>
 struct VRegs {
     static constexpr int VB = VT == kU4 ? 4 : 8;
@@ -109,6 +156,13 @@ template <>
 struct VRegs<kTb> {
     uint2 w[2][3];
     uint2 nm;
+};
+// uniform 3-bit V: the lane's six plane words of each 32-token block (TurboQuant-MSE V layout) and
+// the 16-byte meta of tokens 4 (lane % 16) + 0..3
+template <>
+struct VRegs<kU3> {
+    uint2 w[2][3];
+    u4 vm[4];
 };
 template <>
 struct VRegs<kTb4> {
@@ -186,9 +240,10 @@ __device__ __forceinline__ f4 pv_planes(const h8* Pg, const uint32_t* w, int q, 
 
 template <int KT, int VT, int MB, int kNW>
 __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
-    constexpr bool KU = KT != kTb, VU = VT == kU4 || VT == kU8, VT4 = VT == kTb4;
+    constexpr bool KU = KT != kTb, VU = VT == kU4 || VT == kU8 || VT == kU3, VT4 = VT == kTb4;
     constexpr bool VS = VT == kTs3 || VT == kTs4;
-    constexpr int KB = KT == kU4 ? 4 : 8, VB = VT == kU4 ? 4 : 8;
+    constexpr bool K3 = KT == kU3, V3 = VT == kU3; // uniform 3-bit planes
+    constexpr int KB = KT == kU4 ? 4 : 8, VB = VT == kU4 ? 4 : (V3 ? 3 : 8);
     // split V: bo bits on the outlier half (kSo monomials), bo - 1 on the rest (kSr), W words
     constexpr int kBo = VT == kTs4 ? 4 : 3, kSo = 1 << (kBo - 1), kSr = kSo / 2, kWv = 2 * kBo - 1;
     // P staging slots per wave: 4 (uniform groups, or the 3-bit planes), 8 (the 4-bit
@@ -240,7 +295,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             __syncthreads();
         }
     }
-    const float UK = (KB == 4) ? 1048576.0f : 16777216.0f; // 2^20 / 2^24: unit of a code product
+    const float UK = (KB == 4 && !K3) ? 1048576.0f : 16777216.0f; // 2^20 / 2^24: unit of a code product
     const float UV = (VB == 4) ? 0.0625f : 1.0f; // 4-bit: half the weights carry x16
 
     // ---------------- the query-side loads go out first (they are small and the preparation
@@ -293,7 +348,16 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     VRegs<VT> vrs[kBuf];
     auto load_k = [&](KRegs<KT>& kr, int ci) {
         const size_t r0 = (size_t)tok_begin + 64 * ci + lr; // row of sub-tile 0
-        if constexpr (KU) {
+        if constexpr (K3) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t* c = reinterpret_cast<const uint32_t*>(kcodes + (r0 + 16 * j) * 48 + 12 * lq);
+                kr.pw[j][0] = c[0];
+                kr.pw[j][1] = c[1];
+                kr.pw[j][2] = c[2];
+                kr.km[j] = *reinterpret_cast<const u4*>(kmeta + (r0 + 16 * j) * 16);
+            }
+        } else if constexpr (KU) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint8_t* c = kcodes + (r0 + 16 * j) * (16 * KB) + (16 * KB / 4) * lq;
@@ -315,7 +379,15 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     };
     auto load_v = [&](VRegs<VT>& vr, int ci) {
         const size_t t0 = (size_t)tok_begin + 64 * ci;
-        if constexpr (VU) {
+        if constexpr (V3) {
+            const uint8_t* c = vcodes + (t0 / 32) * 1536 + 24 * l;
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int u = 0; u < 3; ++u) vr.w[k][u] = *reinterpret_cast<const uint2*>(c + k * 1536 + 8 * u);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vr.vm[j] = *reinterpret_cast<const u4*>(vmeta + (t0 + 4 * lr + j) * 16);
+        } else if constexpr (VU) {
             const uint8_t* c = vcodes + (t0 / 32) * (512 * VB) + (size_t)(32 * VB / 4) * l;
 #pragma unroll
             for (int k = 0; k < 2; ++k)
@@ -501,7 +573,30 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int hs = min(4 * mb + lq, G - 1); // score-layout head of this lane
-            if constexpr (KU) {
+            if constexpr (K3) {
+                // uniform 3-bit K: the product over k-slice s takes channels 32 lq + 8 s + i from
+                // quarter lq, i.e. group lq; row (head, group gq) keeps only the quarter gq, and
+                // each value is pre-scaled by 2^-(4(s%2) + i/2) for the code operand's position
+                const int h = 4 * mb + (lr >> 2), gq = lr & 3;
+                const int hc = min(h, G - 1);
+#pragma unroll
+                for (int sl = 0; sl < 4; ++sl) {
+                    h8 hi, lo;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float sc = __uint_as_float((uint32_t)(127 - 4 * (sl & 1) - (i >> 1)) << 23);
+                        const float x = (h < G && lq == gq) ? s_q[hc][32 * lq + 8 * sl + i] * sc : 0.0f;
+                        const _Float16 xh = (_Float16)x;
+                        hi[i] = xh;
+                        lo[i] = (_Float16)((x - (float)xh) * kLoScale);
+                    }
+                    Ahi[mb][sl] = hi;
+                    Alo[mb][sl] = lo;
+                }
+#pragma unroll
+                for (int g = 0; g < 4; ++g) qs_l[mb][g] = s_qsum[hs][g] * (1.0f / UK);
+                F[mb] = UK * s_qfac[hs];
+            } else if constexpr (KU) {
                 const int h = 4 * mb + (lr >> 2), gq = lr & 3;
                 const int hc = min(h, G - 1);
                 h8 hi, lo;
@@ -556,15 +651,16 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
             for (int j = 0; j < 4; ++j) {
                 const bool valid = (c0 + 4 * lr + j) < tok_end;
                 if constexpr (KU) {
-                    const auto& kc = kr.kc;
                     const auto& km = kr.km;
-                    h8 B[4];
+                    h8 B[4]; // uniform 4 / 8-bit: B[g] = 8 codes of group g; 3-bit: B[s] = slice s
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        if (KB == 4)
-                            B[g] = as_h8(unpack4(kc[j][0][g]));
+                        if constexpr (K3)
+                            B[g] = as_h8(codes3x8(kr.pw[j][0], kr.pw[j][1], kr.pw[j][2], g));
+                        else if constexpr (KB == 4)
+                            B[g] = as_h8(unpack4(kr.kc[j][0][g]));
                         else
-                            B[g] = as_h8(unpack8(kc[j][g >> 1][2 * (g & 1)], kc[j][g >> 1][2 * (g & 1) + 1]));
+                            B[g] = as_h8(unpack8(kr.kc[j][g >> 1][2 * (g & 1)], kr.kc[j][g >> 1][2 * (g & 1) + 1]));
                     }
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) {
@@ -670,14 +766,17 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                 float P[kSlots][4]; // [g][j]
                 if constexpr (VU) {
                     const auto& vm = vr.vm;
-                    constexpr float mid = (VB == 4) ? 8.0f : 128.0f; // codes enter as c - mid
+                    constexpr float mid = (VB == 4) ? 8.0f : (V3 ? 4.0f : 128.0f); // codes enter as c - mid
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         z_run[mb][0] = fmaf(pj[mb][j], fmaf(mid, lo_h(vm[j].x), lo_h(vm[j].z)), z_run[mb][0]);
                         z_run[mb][1] = fmaf(pj[mb][j], fmaf(mid, hi_h(vm[j].x), hi_h(vm[j].z)), z_run[mb][1]);
                         z_run[mb][2] = fmaf(pj[mb][j], fmaf(mid, lo_h(vm[j].y), lo_h(vm[j].w)), z_run[mb][2]);
                         z_run[mb][3] = fmaf(pj[mb][j], fmaf(mid, hi_h(vm[j].y), hi_h(vm[j].w)), z_run[mb][3]);
-                        const float w = (VB == 4 && j < 2) ? 16.0f : 1.0f;
+                        // 4-bit: half the operands carry x16; 3-bit: token 4 lr + j enters its
+                        // operand at 2^((4 lr + j) % 8 / 2), undone here
+                        const float w = V3 ? __uint_as_float((uint32_t)(127 - 2 * (lr & 1) - (j >> 1)) << 23)
+                                           : ((VB == 4 && j < 2) ? 16.0f : 1.0f);
                         const float pw = pj[mb][j] * w;
                         P[0][j] = pw * lo_h(vm[j].x);
                         P[1][j] = pw * hi_h(vm[j].x);
@@ -730,7 +829,18 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                 for (int g = 0; g < kSlots; ++g)
                     Pg[g] = (kCmp && lr >= 8) ? h8{0, 0, 0, 0, 0, 0, 0, 0}
                                               : *reinterpret_cast<const h8*>(my_p + (g * kRows + lr) * kPRow + 32 * k + 8 * lq);
-                if constexpr (VU) {
+                if constexpr (V3) {
+                    // centred 3-bit codes from the three plane words of the tile's half; tiles
+                    // with odd N carry x16 (their quarter's position), undone in the epilogue
+#pragma unroll
+                    for (int N = 0; N < 8; ++N) {
+                        const int hN = N >> 2;
+                        const uint32_t p0 = hN ? vr.w[k][0].y : vr.w[k][0].x;
+                        const uint32_t p1 = hN ? vr.w[k][1].y : vr.w[k][1].x;
+                        const uint32_t p2 = hN ? vr.w[k][2].y : vr.w[k][2].x;
+                        acc[N] = mfma16(Pg[N >> 1], centred3x8(p0, p1, p2, N & 3), acc[N]);
+                    }
+                } else if constexpr (VU) {
                     const auto& vc = vr.vc;
 #pragma unroll
                     for (int N = 0; N < 8; ++N) {
@@ -870,7 +980,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     if (!wsplit) {
 #pragma unroll
         for (int N = 0; N < 8; ++N) {
-            const float u = VU ? UV : 1.0f;
+            const float u = V3 ? ((N & 1) ? 0.0625f : 1.0f) : (VU ? UV : 1.0f);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 // rows 4 lq + v: head 4 (lq % 2) + v, hi part for lq < 2 (compact: head v, hi for
@@ -939,6 +1049,7 @@ hipError_t launch_v(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEve
     if (V.scheme == kTurboSplit)
         return V.bits == 4 ? launch_mb<KT, kTs4>(p, s, ev0, ev1) : launch_mb<KT, kTs3>(p, s, ev0, ev1);
     if (V.scheme != kUniform) return V.bits == 4 ? launch_mb<KT, kTb4>(p, s, ev0, ev1) : launch_mb<KT, kTb>(p, s, ev0, ev1);
+    if (V.bits == 3) return launch_mb<KT, kU3>(p, s, ev0, ev1);
     return V.bits == 4 ? launch_mb<KT, kU4>(p, s, ev0, ev1) : launch_mb<KT, kU8>(p, s, ev0, ev1);
 }
 
@@ -947,8 +1058,8 @@ hipError_t launch_v(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEve
 bool mfma_path_supported(const DecodeParams& p) {
     const PlaneGeom& K = p.geom[0];
     const PlaneGeom& V = p.geom[1];
-    const bool k_ok = (K.scheme == kUniform && (K.bits == 4 || K.bits == 8)) || K.scheme == kTurboQjl;
-    const bool v_ok = (V.scheme == kUniform && (V.bits == 4 || V.bits == 8)) || V.scheme == kTurboMse ||
+    const bool k_ok = (K.scheme == kUniform && (K.bits == 3 || K.bits == 4 || K.bits == 8)) || K.scheme == kTurboQjl;
+    const bool v_ok = (V.scheme == kUniform && (V.bits == 3 || V.bits == 4 || V.bits == 8)) || V.scheme == kTurboMse ||
                       (V.scheme == kTurboSplit && (V.bits == 3 || V.bits == 4));
     return k_ok && v_ok && p.G <= kMaxGroupHeads;
 }
@@ -956,6 +1067,7 @@ bool mfma_path_supported(const DecodeParams& p) {
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const PlaneGeom& K = p.geom[0];
     if (K.scheme != kUniform) return launch_v<kTb>(p, s, ev0, ev1);
+    if (K.bits == 3) return launch_v<kU3>(p, s, ev0, ev1);
     return K.bits == 4 ? launch_v<kU4>(p, s, ev0, ev1) : launch_v<kU8>(p, s, ev0, ev1);
 }
 

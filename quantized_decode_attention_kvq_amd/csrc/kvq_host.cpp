@@ -52,7 +52,7 @@ kvq_status check_config(const kvq_config* c) {
         return KVQ_ERR_UNSUPPORTED;
     for (int t = 0; t < 2; ++t) {
         const int scheme = t == 0 ? c->k_scheme : c->v_scheme, bits = t == 0 ? c->k_bits : c->v_bits;
-        if (scheme == KVQ_UNIFORM && bits != 4 && bits != 8) return KVQ_ERR_UNSUPPORTED;
+        if (scheme == KVQ_UNIFORM && bits != 3 && bits != 4 && bits != 8) return KVQ_ERR_UNSUPPORTED;
         if (scheme == KVQ_Q8_0 && bits != 8) return KVQ_ERR_UNSUPPORTED;
         if (scheme == KVQ_TURBO_QJL && bits != 3) return KVQ_ERR_UNSUPPORTED;
         // TurboQuant-MSE: 3-bit codes, or 4-bit codes for V ("Turbo4")

@@ -437,6 +437,14 @@ hipError_t launch_uniform_bulk(const QuantParams& p, hipStream_t s, int tensor0,
 
 hipError_t launch_uniform_bulk_for(const PlaneGeom& G, const QuantParams& p, hipStream_t s,
                                    int tensor0, int n_tensors) {
+    if (G.bits == 3) {
+        switch ((G.rotate ? 2 : 0) | (G.sinkhorn ? 1 : 0)) {
+        case 0: return launch_uniform_bulk<3, false, false>(p, s, tensor0, n_tensors);
+        case 1: return launch_uniform_bulk<3, false, true>(p, s, tensor0, n_tensors);
+        case 2: return launch_uniform_bulk<3, true, false>(p, s, tensor0, n_tensors);
+        default: return launch_uniform_bulk<3, true, true>(p, s, tensor0, n_tensors);
+        }
+    }
     const int key = (G.symmetric ? 8 : 0) | (G.bits == 8 ? 4 : 0) | (G.rotate ? 2 : 0) | (G.sinkhorn ? 1 : 0);
     switch (key) {
     case 12: return launch_uniform_bulk<8, false, false, true>(p, s, tensor0, n_tensors);

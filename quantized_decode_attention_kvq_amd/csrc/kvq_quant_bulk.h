@@ -222,6 +222,63 @@ __device__ __forceinline__ uint64_t v_token_mask(int lo, int hi) {
     return m;
 }
 
+// Byte of bit k of the four bytes of x (byte 0 -> bit 0), as a nibble.
+__device__ __forceinline__ uint32_t byte_bits(uint32_t x, int k) {
+    x = (x >> k) & 0x01010101u;
+    x = x | (x >> 7);
+    x = x | (x >> 14);
+    return x & 0xFu;
+}
+
+// Block words of an octet of 3-bit codes in the TurboQuant-MSE V layout (TurboQuant V, and the
+// 3-bit uniform V planes, which share it): bit k of channel d -> word 6 (16 o + d % 16) + 2k +
+// (d / 16) / 4, token i at bit 16 (i % 2) + 4 ((d / 16) % 4) + i / 2.  wv: the octet's codes as
+// [token][channel] bytes in the wave's LDS.  Lane L (< 32) forms the three words of n = L % 16,
+// h = L / 16 (channels 16 N + n, N = 4h .. 4h + 3); lanes 32 + L take channels N = 4h + 2, 4h + 3
+// of the same words, merged by the lane 32 apart.  Tokens of the octet outside [t_lo, t_hi) keep
+// their bits.
+__device__ __forceinline__ void v3_plane_words(const WavePlane& w, int g, int t_lo, int t_hi, const uint8_t* wv) {
+    const int L = lane_id();
+    const int n = L & 15, h = (L >> 4) & 1, half = L >> 5;
+    uint32_t wk0 = 0u, wk1 = 0u, wk2 = 0u;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int Nl = 2 * half + c; // N % 4
+        const int d = 16 * (4 * h + Nl) + n;
+        uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo |= (uint32_t)wv[i * kDim + d] << (8 * i);
+            hi |= (uint32_t)wv[(i + 4) * kDim + d] << (8 * i);
+        }
+        const uint32_t ev = __builtin_amdgcn_perm(hi, lo, 0x06040200u); // tokens 0, 2, 4, 6
+        const uint32_t od = __builtin_amdgcn_perm(hi, lo, 0x07050301u); // tokens 1, 3, 5, 7
+        wk0 |= (byte_bits(ev, 0) | (byte_bits(od, 0) << 16)) << (4 * Nl);
+        wk1 |= (byte_bits(ev, 1) | (byte_bits(od, 1) << 16)) << (4 * Nl);
+        wk2 |= (byte_bits(ev, 2) | (byte_bits(od, 2) << 16)) << (4 * Nl);
+    }
+    wk0 |= xor_lane<32>(wk0);
+    wk1 |= xor_lane<32>(wk1);
+    wk2 |= xor_lane<32>(wk2);
+    __builtin_amdgcn_wave_barrier();
+    if (half == 0) {
+        const int o = g & 3;
+        uint32_t* blk = reinterpret_cast<uint32_t*>(w.codes + (size_t)(g >> 2) * 1536) + 6 * (16 * o + n) + h;
+        if (t_hi - t_lo == 8) {
+            blk[0] = wk0;
+            blk[2] = wk1;
+            blk[4] = wk2;
+        } else {
+            // token bits of the octet present in this append
+            uint32_t m = 0u;
+            for (int i = t_lo - 8 * g; i < t_hi - 8 * g; ++i) m |= 0x1111u << (16 * (i & 1) + (i >> 1));
+            blk[0] = (blk[0] & ~m) | (wk0 & m);
+            blk[2] = (blk[2] & ~m) | (wk1 & m);
+            blk[4] = (blk[4] & ~m) | (wk2 & m);
+        }
+    }
+}
+
 // One octet g of a uniform plane.  wv: 1 KiB of the wave's LDS (V planes: codes staged as
 // [channel][token] bytes).
 template <int BITS, bool ROT, bool SINK, bool SYM = false>
@@ -256,7 +313,33 @@ __device__ __forceinline__ void uniform_octet(const WavePlane& w, bool IS_V, int
             group_codes<BITS>(e, c, s16, z16);
         const int g4 = j >> 2, kb = j & 3;
         const int row = IS_V ? t : k_row(t);
-        if (!IS_V && valid) {
+        if constexpr (BITS == 3) {
+            // bit planes in the TurboQuant 3-bit layout: K rows hold three words per group
+            // (channel 8j + i = value 8 (j % 4) + i of group j / 4, at bit 16 (v % 2) + v / 2);
+            // V codes are staged as [token][channel] bytes for the block words
+            if (IS_V) {
+                *reinterpret_cast<uint2*>(wv + (size_t)i_tok * kDim + 8 * j) = make_uint2(pack_bytes(c), pack_bytes(c + 4));
+            } else {
+                uint32_t pw0 = 0u, pw1 = 0u, pw2 = 0u;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int v = 8 * (j & 3) + i;
+                    const uint32_t bit = 1u << (16 * (v & 1) + (v >> 1));
+                    pw0 |= (c[i] & 1u) ? bit : 0u;
+                    pw1 |= (c[i] & 2u) ? bit : 0u;
+                    pw2 |= (c[i] & 4u) ? bit : 0u;
+                }
+                pw0 = qdev::or_reduce<4>(pw0);
+                pw1 = qdev::or_reduce<4>(pw1);
+                pw2 = qdev::or_reduce<4>(pw2);
+                if (valid && kb == 0) {
+                    uint32_t* kw = reinterpret_cast<uint32_t*>(w.codes + (size_t)row * 48 + 12 * g4);
+                    kw[0] = pw0;
+                    kw[1] = pw1;
+                    kw[2] = pw2;
+                }
+            }
+        } else if (!IS_V && valid) {
             uint8_t* rp = w.codes + (size_t)row * (16 * BITS);
             if (BITS == 4) {
                 reinterpret_cast<uint32_t*>(rp)[4 * kb + g4] = pack_k4(c);
@@ -264,7 +347,7 @@ __device__ __forceinline__ void uniform_octet(const WavePlane& w, bool IS_V, int
                 *reinterpret_cast<uint2*>(rp + 8 * (4 * kb + g4)) = make_uint2(pack_bytes(c), pack_bytes(c + 4));
             }
         }
-        if (IS_V) {
+        if (IS_V && BITS != 3) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) wv[(8 * j + i) * 8 + i_tok] = (uint8_t)c[i];
         }
@@ -274,7 +357,11 @@ __device__ __forceinline__ void uniform_octet(const WavePlane& w, bool IS_V, int
             m[4 + g4] = z16;
         }
     }
-    if (IS_V) {
+    if (IS_V && BITS == 3) {
+        __builtin_amdgcn_wave_barrier();
+        v3_plane_words(w, g, t_lo, t_hi, wv);
+        __builtin_amdgcn_wave_barrier();
+    } else if (IS_V) {
         // lane L forms V words w = 2L and 2L + 1 of the octet's 128 (word w holds channel
         // 16 (w % 8) + w / 8): channels 32 (L % 4) + L / 4 and that + 16
         __builtin_amdgcn_wave_barrier();
@@ -350,13 +437,6 @@ __device__ __forceinline__ float turbo_level(bool b0, bool b1, bool b2, const Tu
     return b2 ? hi : lo;
 }
 
-// Nibble of bit k of the four bytes of x (byte 0 -> bit 0).
-__device__ __forceinline__ uint32_t byte_bits(uint32_t x, int k) {
-    x = (x >> k) & 0x01010101u;
-    x = x | (x >> 7);
-    x = x | (x >> 14);
-    return x & 0xFu;
-}
 
 // acc = (r of lane LN of this 16-lane row) * s + acc with one rounding: v_fmac_f32 with a
 // row_newbcast DPP source, the same binary32 result as fmaf(s, r_LN, acc).
@@ -496,50 +576,7 @@ __device__ __forceinline__ void turbo_octet(const WavePlane& w, bool IS_V, int g
         }
     }
     __builtin_amdgcn_wave_barrier();
-    if (IS_V) {
-        // TurboQuant-MSE V block words: bit k of channel d -> word 6 (16 o + d % 16) + 2k + (d / 16) / 4,
-        // token i at bit 16 (i % 2) + 4 ((d / 16) % 4) + i / 2.  Lane L (< 32) forms the three words of
-        // n = L % 16, h = L / 16 (channels 16 N + n, N = 4h .. 4h + 3); lanes 32 + L take channels
-        // N = 4h + 2, 4h + 3 of the same words, merged by the lane 32 apart.
-        const int n = L & 15, h = (L >> 4) & 1, half = L >> 5;
-        uint32_t wk0 = 0u, wk1 = 0u, wk2 = 0u;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int Nl = 2 * half + c; // N % 4
-            const int d = 16 * (4 * h + Nl) + n;
-            uint32_t lo = 0u, hi = 0u;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                lo |= (uint32_t)wv[i * kDim + d] << (8 * i);
-                hi |= (uint32_t)wv[(i + 4) * kDim + d] << (8 * i);
-            }
-            const uint32_t ev = __builtin_amdgcn_perm(hi, lo, 0x06040200u); // tokens 0, 2, 4, 6
-            const uint32_t od = __builtin_amdgcn_perm(hi, lo, 0x07050301u); // tokens 1, 3, 5, 7
-            wk0 |= (byte_bits(ev, 0) | (byte_bits(od, 0) << 16)) << (4 * Nl);
-            wk1 |= (byte_bits(ev, 1) | (byte_bits(od, 1) << 16)) << (4 * Nl);
-            wk2 |= (byte_bits(ev, 2) | (byte_bits(od, 2) << 16)) << (4 * Nl);
-        }
-        wk0 |= xor_lane<32>(wk0);
-        wk1 |= xor_lane<32>(wk1);
-        wk2 |= xor_lane<32>(wk2);
-        __builtin_amdgcn_wave_barrier();
-        if (half == 0) {
-            const int o = g & 3;
-            uint32_t* blk = reinterpret_cast<uint32_t*>(w.codes + (size_t)(g >> 2) * 1536) + 6 * (16 * o + n) + h;
-            if (t_hi - t_lo == 8) {
-                blk[0] = wk0;
-                blk[2] = wk1;
-                blk[4] = wk2;
-            } else {
-                // token bits of the octet present in this append
-                uint32_t m = 0u;
-                for (int i = t_lo - 8 * g; i < t_hi - 8 * g; ++i) m |= 0x1111u << (16 * (i & 1) + (i >> 1));
-                blk[0] = (blk[0] & ~m) | (wk0 & m);
-                blk[2] = (blk[2] & ~m) | (wk1 & m);
-                blk[4] = (blk[4] & ~m) | (wk2 & m);
-            }
-        }
-    }
+    if (IS_V) v3_plane_words(w, g, t_lo, t_hi, wv);
     __builtin_amdgcn_wave_barrier();
 }
 

@@ -271,7 +271,39 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
             else
                 quant_uniform(a, c, G.bits, q0, q1, s16, z16);
             const int g = l >> 4;
-            if (tensor == 0) {
+            if (G.bits == 3) {
+                // 3-bit codes go to bit planes laid out as the TurboQuant 3-bit planes (K: three
+                // words per group in the 48-byte row, channels 2 lg, 2 lg + 1 at bits lg, 16 + lg;
+                // V: the block words written after the octet), the meta as for any uniform plane
+                const int lg = l & 15;
+                const int row = tensor == 0 ? k_row(t) : t;
+                if (tensor == 0) {
+                    uint32_t pw[3];
+#pragma unroll
+                    for (int k = 0; k < 3; ++k)
+                        pw[k] = or_reduce<16>((((q0 >> k) & 1u) << lg) | (((q1 >> k) & 1u) << (16 + lg)));
+                    if (lg == 0) {
+                        uint32_t* w = reinterpret_cast<uint32_t*>(codes + (size_t)row * 48 + 12 * g);
+                        w[0] = pw[0];
+                        w[1] = pw[1];
+                        w[2] = pw[2];
+                    }
+                } else {
+                    const int i = t % 8, N = l >> 3;
+                    const uint32_t pos = 1u << (16 * (i & 1) + 4 * (N & 3) + (i >> 1));
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) {
+                        tv_a[k] |= ((q0 >> k) & 1u) ? pos : 0u;
+                        tv_c[k] |= ((q1 >> k) & 1u) ? pos : 0u;
+                    }
+                    tv_mask |= pos;
+                }
+                if (lg == 0) {
+                    uint16_t* m = reinterpret_cast<uint16_t*>(meta + (size_t)row * 16);
+                    m[g] = s16;
+                    m[4 + g] = z16;
+                }
+            } else if (tensor == 0) {
                 const int row = k_row(t);
                 uint8_t* r = codes + (size_t)row * (16 * G.bits);
                 const int kb = (l & 15) >> 2, i = 2 * (l & 3);
@@ -425,9 +457,10 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
         }
     }
 
-    if (tensor == 1 && G.scheme != kUniform) {
+    if (tensor == 1 && (G.scheme != kUniform || G.bits == 3)) {
         // merge the four lanes (l ^ 8, l ^ 16) whose channels share each word, then
-        // read-modify-write this octet's words
+        // read-modify-write this octet's words (TurboQuant planes, and 3-bit uniform planes in
+        // the same layout)
         uint32_t m = tv_mask;
         m |= xor_lane<8>(m);
         m |= xor_lane<16>(m);
@@ -466,7 +499,7 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
         }
     }
 
-    if (tensor == 1 && G.scheme == kUniform) {
+    if (tensor == 1 && G.scheme == kUniform && G.bits != 3) {
         // read-modify-write the packed words of channels 2l, 2l+1 for this 8-token group
         const int blk = t_lo / 32, kb = (t_lo % 32) / 8;
         const int d0 = 2 * l, n0 = d0 % 16, N = d0 / 16;

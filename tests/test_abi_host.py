@@ -56,6 +56,14 @@ def test_required_bytes_match_format():
     npg = K.kvq_cache_required_bytes(_cfg(wlp))
     pp = 28 * 8 * (131072 * 160 + 2 * 128 * 512)
     assert pp <= npg <= pp + 16 * 2 ** 20
+    # 3-bit uniform: 48 B of bit planes + 16 B meta = 64 B per token-head (K 8-bit: 144 B)
+    wl3 = W.LLAMA3B_32K_U8_K_U3_V
+    n3 = K.kvq_cache_required_bytes(_cfg(wl3))
+    p3 = 28 * 8 * 32768 * (144 + 64)
+    assert p3 <= n3 <= p3 + 16 * 2 ** 20
+    n33 = K.kvq_cache_required_bytes(_cfg(W.LLAMA3B_32K_KVARN_U3))
+    p33 = 28 * 8 * 32768 * (64 + 64)
+    assert p33 <= n33 <= p33 + 16 * 2 ** 20
     # split V (2.5 / 3.5 bits): 40 / 56 B codes + 4 B norms per token-head, K q8_0 at 144 B
     for wls, vb in ((W.LLAMA8B_32K_Q8_0_TURBO25_V, 44), (W.LLAMA8B_32K_Q8_0_TURBO35_V, 60)):
         ns = K.kvq_cache_required_bytes(_cfg(wls))
@@ -64,7 +72,7 @@ def test_required_bytes_match_format():
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(head_dim=64), 2), (dict(group_size=64), 2), (dict(k_bits=3), 2), (dict(v_bits=2), 2),
+    (dict(head_dim=64), 2), (dict(group_size=64), 2), (dict(k_bits=5), 2), (dict(v_bits=2), 2),
     (dict(fp32_window=64), 2), (dict(n_q_heads=25), 1), (dict(n_q_heads=8 * 9), 2),
     (dict(max_batch=65), 2), (dict(max_batch=0), 1), (dict(k_scheme=2), 2), (dict(v_scheme=1), 2),
     (dict(rotate_k=2), 1), (dict(n_layers=0), 1), (dict(sinkhorn_iters=5, calib_tokens=1), 2),

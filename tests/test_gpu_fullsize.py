@@ -170,3 +170,9 @@ def test_fullsize_fused_llama3b_32k_kvarn():
 def test_fullsize_fused_llama3b_128k_progressive_b1():
     # 128K progressive: the new token lands in the FP32 window, owned by the window workgroup
     _fused_steps(W.LLAMA3B_128K_PROGRESSIVE, layers=[0, 27], seqs=[0], heads=[0, 3, 7])
+
+
+@pytest.mark.parametrize("wl", [W.LLAMA3B_32K_U8_K_U3_V, W.LLAMA3B_32K_KVARN_U3], ids=lambda w: w.name)
+def test_fullsize_llama3b_32k_uniform3(wl):
+    # 3-bit uniform group packing at full size: V only (K 8-bit), and K and V behind WHT + Sinkhorn
+    _run(wl, layers=[0, 27], seqs=[0], plane_heads=[0, 4, 7], attn_heads=[0, 4, 7])

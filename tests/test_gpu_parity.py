@@ -81,7 +81,8 @@ def test_progressive_3970_full():
 
 @pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_TURBO, W.LLAMA3B_32K_TURBO_ASYM,
                                 W.LLAMA3B_32K_Q8_0_TURBO_V, W.DENSE27B_120K_Q8_0, W.LLAMA3B_32K_Q8_0_TURBO4_V,
-                                W.LLAMA8B_32K_Q8_0_TURBO25_V, W.LLAMA8B_32K_Q8_0_TURBO35_V],
+                                W.LLAMA8B_32K_Q8_0_TURBO25_V, W.LLAMA8B_32K_Q8_0_TURBO35_V,
+                                W.LLAMA3B_32K_U8_K_U3_V, W.LLAMA3B_32K_KVARN_U3],
                          ids=lambda w: w.name)
 def test_prefill_equals_appends_bytewise(wl):
     _say("case: prefill == appends,", wl.name, "n=300")
@@ -107,7 +108,8 @@ RAGGED_CALLS = [(3, 21), (1, 5), (2, 3), (3, 37), (1, 16), (3, 130)]
 @pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_KVARN, W.LLAMA3B_32K_TURBO,
                                 W.LLAMA3B_32K_TURBO_ASYM, W.DENSE27B_120K_U8, W.DENSE27B_120K_Q8_0,
                                 W.LLAMA3B_32K_Q8_0_TURBO_V, W.LLAMA3B_32K_Q8_0_TURBO4_V,
-                                W.LLAMA8B_32K_Q8_0_TURBO25_V, W.LLAMA8B_32K_Q8_0_TURBO35_V],
+                                W.LLAMA8B_32K_Q8_0_TURBO25_V, W.LLAMA8B_32K_Q8_0_TURBO35_V,
+                                W.LLAMA3B_32K_U8_K_U3_V, W.LLAMA3B_32K_KVARN_U3],
                          ids=lambda w: w.name)
 def test_prefill_ragged_batch_bytewise(wl):
     """Prefill calls over a batch whose sequences start at different lengths leave exactly the
@@ -472,7 +474,8 @@ def _planes_equal(a, b, li, batch, n_heads):
                                   (W.LLAMA3B_32K_TURBO_ASYM, 64), (W.DENSE27B_120K_KVARN, 500),
                                   (W.LLAMA3B_32K_Q8_0_TURBO_V, 130), (W.DENSE27B_120K_Q8_0, 65),
                                   (W.LLAMA3B_32K_Q8_0_TURBO4_V, 200), (W.LLAMA8B_32K_Q8_0_TURBO25_V, 190),
-                                  (W.LLAMA8B_32K_Q8_0_TURBO35_V, 64)],
+                                  (W.LLAMA8B_32K_Q8_0_TURBO35_V, 64), (W.LLAMA3B_32K_U8_K_U3_V, 257),
+                                  (W.LLAMA3B_32K_KVARN_U3, 100)],
                          ids=lambda x: x.name if hasattr(x, "name") else str(x))
 def test_fused_append_decode_equals_separate_calls(wl, n, path):
     # kvq_append_attn_decode == kvq_append + kvq_attn_decode: byte-identical planes and
@@ -604,3 +607,37 @@ def test_gqa5_turbo_values_both_paths(wl):
         r, m = rel_l2(out.cpu().numpy()[b], ref), max_abs(out.cpu().numpy()[b], ref)
         assert r <= REL_L2_TOL and m <= MAX_ABS_TOL, (b, r, m)
     _decode_and_compare(case, 0, None)  # both decode paths
+
+
+# Uniform 3-bit group packing (codes as three bit planes, fp16 scale and zero per 32 channels):
+# K 8-bit / V 3-bit, WHT + Sinkhorn 3-bit K and V, the same with five query heads per kv head and
+# bf16 sources, and a progressive 3-bit cache with the FP32 window.
+U3_CASES = [
+    W.LLAMA3B_32K_U8_K_U3_V,
+    W.LLAMA3B_32K_KVARN_U3,
+    W.DENSE27B_120K_KVARN.with_(name="dense27b-wht-sinkhorn-u3", k_bits=3, v_bits=3),
+    W.LLAMA3B_128K_PROGRESSIVE.with_(name="llama3b-u3-progressive", k_bits=3, v_bits=3),
+]
+
+
+@pytest.mark.parametrize("wl", U3_CASES, ids=lambda w: w.name)
+def test_uniform3_planes_and_decode(wl):
+    _say("case:", wl.name, "2 seqs, 300 prefill + 44 appends + 1 fused step")
+    case = Case(wl, 345, layers=[0], batch=2)
+    k, v = case.kv(0)
+    case.cache.prefill_quantize(0, k[:, :300].contiguous(), v[:, :300].contiguous())
+    for t in range(300, 344):
+        case.cache.append(0, k[:, t].contiguous(), v[:, t].contiguous())
+    q = W.gen_q(wl, 0, 9, batch=2).to("cuda")
+    out = torch.full((2, wl.n_q_heads, 128), float("nan"), device="cuda")
+    case.cache.append_attn_decode(0, k[:, 344].contiguous(), v[:, 344].contiguous(), q, out)
+    torch.cuda.synchronize()
+    planes = _check_all_planes(case, 0)
+    qn = q.float().cpu().numpy()
+    for b in (0, 1):
+        pl = {h: planes[(b, h)] for h in range(wl.n_kv_heads)}
+        ref = oracle_attention_case(case, 0, b, qn[b], planes=pl)
+        r, m = rel_l2(out.cpu().numpy()[b], ref), max_abs(out.cpu().numpy()[b], ref)
+        _say(f"  fused step seq {b}: rel_l2={r:.2e} max_abs={m:.2e}")
+        assert r <= REL_L2_TOL and m <= MAX_ABS_TOL, (b, r, m)
+    _decode_and_compare(case, 0, planes)  # both decode paths

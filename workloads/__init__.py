@@ -111,10 +111,19 @@ LLAMA8B_32K_Q8_0_TURBO35_V = Workload(
     "llama8b-32layer-32k-q8_0-k-turbo3.5split-v", 32, 32, 8, 1, 32768, Q8_0, TURBO_SPLIT, 8, 4, 0,
     False, True, 0, 512, "f32", "outliers8x8", 1006)
 
+# 3-bit uniform group packing: the asymmetric variant with V cut to 3 bits (K kept at 8-bit
+# groups), and the KVarN rotation + balancing in front of 3-bit K and V
+LLAMA3B_32K_U8_K_U3_V = Workload(
+    "llama3b-28layer-32k-u8-k-u3-v", 28, 24, 8, 1, 32768, UNIFORM, UNIFORM, 8, 3, 0,
+    False, False, 0, 0, "f32", "outliers8x8", 1003)
+LLAMA3B_32K_KVARN_U3 = Workload(
+    "llama3b-28layer-32k-wht-sinkhorn-u3", 28, 24, 8, 1, 32768, UNIFORM, UNIFORM, 3, 3, 0,
+    True, True, 5, 512, "f32", "loguniform_std", 1002)
+
 ALL = [LLAMA3B_3970_PROGRESSIVE, LLAMA3B_32K_KVARN, LLAMA3B_32K_TURBO, LLAMA3B_32K_TURBO_ASYM,
        LLAMA3B_128K_PROGRESSIVE, DENSE27B_120K_KVARN, DENSE27B_120K_U8, DENSE27B_120K_Q8_0,
        LLAMA3B_32K_Q8_0_TURBO_V, LLAMA3B_32K_Q8_0_TURBO4_V, LLAMA8B_32K_Q8_0_TURBO25_V,
-       LLAMA8B_32K_Q8_0_TURBO35_V]
+       LLAMA8B_32K_Q8_0_TURBO35_V, LLAMA3B_32K_U8_K_U3_V, LLAMA3B_32K_KVARN_U3]
 BY_NAME = {w.name: w for w in ALL}
 
 TAGS = {"kv": 1, "calib": 2, "q": 3, "signs": 4, "qjl": 5, "chan": 6, "step": 7}
