@@ -77,6 +77,7 @@ __device__ __forceinline__ int key_lds_row(int t) {
 // zero), kUnits value units (8 codes), and one token's value meta (threads 0..63).
 struct ChunkRegs {
     uint2 kc[kUnits], vc[kUnits];
+    uint32_t kc3[kUnits]; // 3-bit keys: the third plane word of the unit's group
     uint32_t ks[kUnits], kz[kUnits]; // fp16 bits of the key unit's scale and zero
     u4 vm;
 };
@@ -85,7 +86,11 @@ struct Planes {
     const uint8_t *kcodes, *kmeta, *vcodes, *vmeta;
 };
 
-// Value kinds: VB = 4 or 8 (uniform codes), -b for TurboQuant-MSE V with b = 3 or 4 bit planes,
+// Key kinds: KB = 4 or 8 (uniform codes), or 3 (uniform 3-bit codes as three bit planes in the
+// TurboQuant 3-bit K row layout).
+// Value kinds: VB = 4 or 8 (uniform codes), 3 (uniform 3-bit codes as three bit planes in the
+// TurboQuant-MSE V layout, read by TurboQuant value units), -b for TurboQuant-MSE V with b = 3 or
+// 4 bit planes,
 // or kSplitV - bo for the split TurboQuant V with bo = 3 or 4 outlier bits (channel quads
 // N / 4 = 0 are the outlier half's positions, bo planes; N / 4 = 1 the rest's, bo - 1 planes).
 // A TurboQuant value unit is one thread's (block half, octet kb, lane column n, channel quad
@@ -110,7 +115,13 @@ __device__ __forceinline__ void load_codes(const Planes& P, int ci, int tid, Chu
     for (int j = 0; j < kUnits; ++j) {
         const int u = tid + kThreads * j, g = (u >> 2) & 3, word = 4 * (u & 3) + g;
         const size_t row = (size_t)64 * ci + (u >> 4);
-        if constexpr (KB == 4) R.kc[j].x = reinterpret_cast<const uint32_t*>(P.kcodes + row * 64)[word];
+        if constexpr (KB == 3) {
+            // the three plane words of group g (the unit's codes are their nibble u % 4)
+            const uint32_t* pw = reinterpret_cast<const uint32_t*>(P.kcodes + row * 48 + 12 * g);
+            R.kc[j].x = pw[0];
+            R.kc[j].y = pw[1];
+            R.kc3[j] = pw[2];
+        } else if constexpr (KB == 4) R.kc[j].x = reinterpret_cast<const uint32_t*>(P.kcodes + row * 64)[word];
         else R.kc[j] = reinterpret_cast<const uint2*>(P.kcodes + row * 128)[word];
         const uint16_t* m = reinterpret_cast<const uint16_t*>(P.kmeta + row * 16);
         R.ks[j] = m[g]; // kept apart until the dequantization: no wait on the load here
@@ -127,8 +138,8 @@ __device__ __forceinline__ void load_codes(const Planes& P, int ci, int tid, Chu
         R.vc[0].y = w[1];
         R.vc[1].x = (nb > 2) ? w[2] : 0u;
         R.vc[1].y = (nb > 3) ? w[3] : 0u;
-    } else if constexpr (VB < 0) {
-        constexpr int NB = -VB;
+    } else if constexpr (VB < 0 || VB == 3) {
+        constexpr int NB = VB == 3 ? 3 : -VB;
         const TUnit U = turbo_unit(tid);
         const uint32_t* w = reinterpret_cast<const uint32_t*>(P.vcodes + ((size_t)2 * ci + U.half) * (512 * NB)) +
                             2 * NB * (16 * U.kb + U.n) + U.hN;
@@ -194,6 +205,15 @@ __device__ __forceinline__ h2v code_pair(uint2 w, int k) {
     return __builtin_bit_cast(h2v, b) - h2v{(_Float16)1024.0f, (_Float16)1024.0f};
 }
 
+// Codes 2k and 2k + 1 of nibble kb of three half-interleaved plane words (bits 4 kb + k and
+// 16 + 4 kb + k) as exact fp16 integers, the same way.
+__device__ __forceinline__ h2v code_pair3(uint32_t p0, uint32_t p1, uint32_t p2, int kb, int k) {
+    const int sh = 4 * kb + k;
+    const uint32_t b = ((p0 >> sh) & 0x00010001u) | (((p1 >> sh) & 0x00010001u) << 1) |
+                       (((p2 >> sh) & 0x00010001u) << 2) | 0x64006400u;
+    return __builtin_bit_cast(h2v, b) - h2v{(_Float16)1024.0f, (_Float16)1024.0f};
+}
+
 // y = s c + z for a pair: hi = fp16 of y in one rounding (packed fp16 fma), lo = fp16(y - hi)
 // with y - hi formed in fp32.
 struct Pair {
@@ -237,6 +257,23 @@ __device__ __forceinline__ float centroid(uint32_t c, const float* mg) {
     return up ? m : -m;
 }
 
+// z + s code for the 4 channels x 4 tokens of a 3-bit uniform value unit (the TurboQuant value
+// unit mapping): v[q][m] = channel 16 (4 hN + q) + n, token t0 + 2m + par, with the fp16 scale
+// and zero of the channel's group from sm[scale | zero][group][token].
+__device__ __forceinline__ void uniform3_values(const uint32_t* wd, const _Float16 (*sm)[4][kVmRow], int t0, int hN,
+                                                int par, float (&v)[4][4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int t = t0 + 2 * m + par;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int g = 2 * hN + (q >> 1), sh = 16 * par + 4 * q + m;
+            const uint32_t c = ((wd[0] >> sh) & 1u) | (((wd[1] >> sh) & 1u) << 1) | (((wd[2] >> sh) & 1u) << 2);
+            v[q][m] = fmaf((float)sm[0][g][t], (float)c, (float)sm[1][g][t]);
+        }
+    }
+}
+
 // n_t mu[code] for the 4 channels x 4 tokens of a TurboQuant value unit: v[q][m] = channel quad
 // q, token 2m + par of the octet; NB-bit codes from the plane words wd, norms from nrm[token].
 template <int NB>
@@ -272,7 +309,10 @@ __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const 
         u4 hi, lo;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const Pair q = dequant_pair(h2v{sc, sc}, code_pair<KB>(R.kc[j], k), h2v{zr, zr}, mone);
+            h2v c;
+            if constexpr (KB == 3) c = code_pair3(R.kc[j].x, R.kc[j].y, R.kc3[j], u & 3, k);
+            else c = code_pair<KB>(R.kc[j], k);
+            const Pair q = dequant_pair(h2v{sc, sc}, c, h2v{zr, zr}, mone);
             hi[k] = q.hi;
             lo[k] = q.lo;
         }
@@ -280,20 +320,23 @@ __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const 
         *reinterpret_cast<u4*>(dst) = hi;
         *reinterpret_cast<u4*>(dst + 64 * kKS) = lo;
     }
-    if constexpr (VB < 0) {
-        // TurboQuant-MSE values n_t mu[code] (fp32 product), then fp16 hi + remainder lo.  The
+    if constexpr (VB < 0 || VB == 3) {
+        // TurboQuant-MSE values n_t mu[code] (fp32 product), or 3-bit uniform values z + s c
+        // (one fp32 fma), then fp16 hi + remainder lo.  The
         // two parity threads of a unit (adjacent lanes) swap halves so that each ends up with two
         // whole channels of the octet: channels 4 hN + 2 par + {0, 1}.
         // split V: the thread's half (hN) fixes its norm row, code bits and codebook (mg holds
         // the outlier table in 0..7 and the rest's in 8..11)
         constexpr bool SPL = split_kind(VB);
-        constexpr int NB = SPL ? kSplitV - VB : -VB;
+        constexpr int NB = SPL ? kSplitV - VB : (VB == 3 ? 3 : -VB);
         const TUnit U = turbo_unit(tid);
         const int half = U.half, kb = U.kb, n = U.n, hN = U.hN, par = U.par;
         const uint32_t wd[4] = {R.vc[0].x, R.vc[0].y, R.vc[1].x, R.vc[1].y};
         const int t0 = 32 * half + 8 * kb;
         float v[4][4]; // [channel quad q][token pair m]: token 2m + par
-        if (SPL && hN) // the rest half of a split V (uniform per wave): one bit fewer, own table
+        if constexpr (VB == 3)
+            uniform3_values(wd, sm, t0, hN, par, v);
+        else if (SPL && hN) // the rest half of a split V (uniform per wave): one bit fewer, own table
             turbo_values<(SPL ? NB - 1 : NB)>(wd, &sm[0][1][t0], mg + 8, par, v);
         else
             turbo_values<NB>(wd, &sm[0][0][t0], mg, par, v);
@@ -372,7 +415,32 @@ __device__ __forceinline__ void window_overwrite(_Float16* sk, _Float16* sv, int
         *reinterpret_cast<h8*>(dst) = hi;
         *reinterpret_cast<h8*>(dst + 64 * kKS) = lo;
     }
-    if constexpr (VB > 0) {
+    if constexpr (VB == 3) {
+        // 3-bit values were dequantized by TurboQuant value units: the thread rewrites its own
+        // two channel slots (channels 16 (4 hN + 2 par + qq) + n, tokens t0 .. t0 + 7)
+        const TUnit U = turbo_unit(tid);
+        const int tok0 = 64 * chunk + 32 * U.half + 8 * U.kb;
+        if (tok0 + 7 >= nqd && tok0 < len) {
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+                const int N = 4 * U.hN + 2 * U.par + qq, d = 16 * N + U.n;
+                _Float16* dst = sv + d * kVS + 8 * ((4 * U.half + U.kb) ^ N);
+                h8 hi = *reinterpret_cast<const h8*>(dst), lo = *reinterpret_cast<const h8*>(dst + 128 * kVS);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int tok = tok0 + i;
+                    if (tok >= nqd && tok < len) {
+                        const float y = vring[(size_t)(tok % W) * kDim + d];
+                        const _Float16 h = (_Float16)y;
+                        hi[i] = h;
+                        lo[i] = (_Float16)(y - (float)h);
+                    }
+                }
+                *reinterpret_cast<h8*>(dst) = hi;
+                *reinterpret_cast<h8*>(dst + 128 * kVS) = lo;
+            }
+        }
+    } else if constexpr (VB > 0) {
 #pragma unroll
         for (int j = 0; j < kUnits; ++j) {
             const int u = tid + kThreads * j, half = u >> 9, w = u & 511;
@@ -801,7 +869,7 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t s) {
 bool prefill_attn_supported(const PrefillParams& p) {
     const PlaneGeom& K = p.geom[0];
     const PlaneGeom& V = p.geom[1];
-    auto ok = [](const PlaneGeom& g) { return g.scheme == kUniform && (g.bits == 4 || g.bits == 8); };
+    auto ok = [](const PlaneGeom& g) { return g.scheme == kUniform && (g.bits == 3 || g.bits == 4 || g.bits == 8); };
     const bool v_turbo = (V.scheme == kTurboMse || V.scheme == kTurboSplit) && (V.bits == 3 || V.bits == 4);
     // an FP32 window is read in the plain domain: no rotation or balancing on either tensor
     const bool plain = !K.rotate && !K.sinkhorn && !V.rotate && !V.sinkhorn;
@@ -809,18 +877,20 @@ bool prefill_attn_supported(const PrefillParams& p) {
     return ok(K) && (ok(V) || v_turbo) && win_ok && p.G >= 1 && p.G <= kMaxGroupHeads;
 }
 
+template <int KB>
+hipError_t launch_k(const PrefillParams& p, hipStream_t s) {
+    const int vb = p.geom[1].bits;
+    if (p.geom[1].scheme == kTurboSplit)
+        return vb == 4 ? launch_t<KB, kSplitV - 4>(p, s) : launch_t<KB, kSplitV - 3>(p, s);
+    if (p.geom[1].scheme == kTurboMse) return vb == 4 ? launch_t<KB, -4>(p, s) : launch_t<KB, -3>(p, s);
+    if (vb == 3) return launch_t<KB, 3>(p, s);
+    return vb == 4 ? launch_t<KB, 4>(p, s) : launch_t<KB, 8>(p, s);
+}
+
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
-    const int kb = p.geom[0].bits, vb = p.geom[1].bits;
-    if (p.geom[1].scheme == kTurboSplit) {
-        if (kb == 4) return vb == 4 ? launch_t<4, kSplitV - 4>(p, s) : launch_t<4, kSplitV - 3>(p, s);
-        return vb == 4 ? launch_t<8, kSplitV - 4>(p, s) : launch_t<8, kSplitV - 3>(p, s);
-    }
-    if (p.geom[1].scheme == kTurboMse) {
-        if (kb == 4) return vb == 4 ? launch_t<4, -4>(p, s) : launch_t<4, -3>(p, s);
-        return vb == 4 ? launch_t<8, -4>(p, s) : launch_t<8, -3>(p, s);
-    }
-    if (kb == 4) return vb == 4 ? launch_t<4, 4>(p, s) : launch_t<4, 8>(p, s);
-    return vb == 4 ? launch_t<8, 4>(p, s) : launch_t<8, 8>(p, s);
+    const int kb = p.geom[0].bits;
+    if (kb == 3) return launch_k<3>(p, s);
+    return kb == 4 ? launch_k<4>(p, s) : launch_k<8>(p, s);
 }
 
 } // namespace kvq

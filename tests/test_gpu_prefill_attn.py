@@ -173,3 +173,24 @@ def test_prefill_attention_refusals():
         assert e.value.name == name
         torch.cuda.synchronize()
         assert bool((out == 5.0).all())
+
+
+@pytest.mark.parametrize("wl", [W.LLAMA3B_32K_U8_K_U3_V, W.LLAMA3B_32K_KVARN_U3,
+                                W.DENSE27B_120K_KVARN.with_(name="dense27b-wht-sinkhorn-u3", k_bits=3, v_bits=3),
+                                W.LLAMA3B_32K_KVARN_U3.with_(name="llama3b-kvarn-u3-k-u4-v", v_bits=4),
+                                W.LLAMA3B_32K_TURBO_ASYM.with_(name="llama3b-u3-k-turbomse-v", k_bits=3)],
+                         ids=lambda w: w.name)
+def test_prefill_attention_uniform3(wl):
+    # 3-bit uniform keys and / or values (bit planes, fp16 scale and zero per 32 channels)
+    _say("case: prefill attention,", wl.name)
+    _run(wl, n0=300, B=2, nb=1, ne=37, n_q=90, seed=9)
+
+
+def test_prefill_attention_uniform3_window_and_key_splits():
+    # a progressive 3-bit cache (window tokens overwrite 3-bit values dequantized by the value
+    # units), and a long 3-bit KVarN cache whose keys are split over workgroups
+    wl = W.LLAMA3B_3970_PROGRESSIVE.with_(name="llama3b-u3-progressive", k_bits=3, v_bits=3)
+    _say("case: prefill attention,", wl.name)
+    _run(wl, n0=500, B=2, nb=1, ne=37, n_q=150, seed=10)
+    case, _, _ = _run(W.LLAMA3B_32K_KVARN_U3, n0=3000, B=1, nb=0, ne=0, n_q=64, seed=11)
+    assert case.cache.attn_prefill_workspace(0, 64, 1) > 0
