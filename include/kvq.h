@@ -50,7 +50,7 @@ typedef enum {
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 
 typedef enum {
-    KVQ_UNIFORM = 0,   /* b-bit asymmetric groups of 32, fp16 scale + fp16 zero [P1], b = 4|8 */
+    KVQ_UNIFORM = 0,   /* b-bit asymmetric groups of 32, fp16 scale + fp16 zero [P1], b = 3|4|8 */
     KVQ_TURBO_QJL = 1, /* K only: rotation + 3-bit Lloyd-Max code + 1-bit QJL residual [P3]  */
     KVQ_TURBO_MSE = 2, /* rotation + 3-bit (or, for V, 4-bit) Lloyd-Max code, no residual
                           sketch [P3]                                                      */
@@ -75,7 +75,7 @@ typedef struct {
     int max_batch, max_context;          /* sequences per call (<= 64); tokens per sequence
                                             ("context_length" of [P1])                       */
     int k_scheme, v_scheme;              /* kvq_scheme, chosen separately for K and V [P2]   */
-    int k_bits, v_bits;                  /* UNIFORM: 4 or 8; TURBO_QJL: 3; TURBO_MSE: 3, or 4
+    int k_bits, v_bits;                  /* UNIFORM: 3, 4 or 8; TURBO_QJL: 3; TURBO_MSE: 3, or 4
                                             for V ("Turbo4", [P3] rules); Q8_0: 8;
                                             TURBO_SPLIT: 3 (2.5 bits) or 4 (3.5 bits)        */
     int group_size;                      /* must be 32                                       */
@@ -101,6 +101,9 @@ typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
  *      16*(i%2) + 4*(i/2) (4-bit) or byte i (8-bit).
  *  UNIFORM meta: 16 B per token: u16 fp16 scale[4], then u16 fp16 zero[4] (K: row order,
  *      V: token order).
+ *  UNIFORM 3-bit codes: three bit planes laid out exactly as the TURBO 3-bit planes below (K:
+ *      48-byte rows in the UNIFORM K row order; V: 1536-byte blocks of 32 tokens), with the
+ *      UNIFORM meta: 64 B per token-head.
  *  TURBO planes keep the three bits of each 3-bit code in three bit planes of "half-interleaved"
  *      u32 words: value e (0..31) of a word at bit 16*(e%2) + e/2.  Every plane holds whole
  *      64-token blocks.
