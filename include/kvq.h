@@ -44,8 +44,13 @@ typedef enum {
     KVQ_ERR_BUFFER_TOO_SMALL = 5, /* dev_buf smaller than kvq_cache_required_bytes()        */
     KVQ_ERR_MISALIGNED = 6,       /* a pointer is not 16-byte (dev_buf: 256-byte) aligned   */
     KVQ_ERR_HOST_ALLOC = 7,       /* host memory for the handle could not be allocated      */
-    KVQ_ERR_DEVICE = 8            /* a HIP call failed; kvq_last_hip_error() has its code   */
+    KVQ_ERR_DEVICE = 8,           /* a HIP call failed; kvq_last_hip_error() has its code   */
+    KVQ_ERR_SCRATCH = 9           /* kvq_attn_decode_static: the call's split partials need
+                                     more than KVQ_STATIC_SCRATCH_BYTES                     */
 } kvq_status;
+
+/* Bytes of the library-held device scratch that kvq_attn_decode_static uses (one per GPU). */
+#define KVQ_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
 
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 
@@ -201,6 +206,19 @@ kvq_status kvq_append(kvq_cache* cache, int layer, const void* k, const void* v,
  * with no tokens gets zeros. */
 kvq_status kvq_attn_decode(kvq_cache* cache, int layer, const void* q, int dtype, float* out,
                            int batch, float softmax_scale, void* stream);
+
+/* kvq_attn_decode for callers that cannot allocate device memory or touch the cache's own work
+ * area per call (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, checks, kernels and split plan as kvq_attn_decode, hence the same
+ * output bit for bit; the split partials (batch x n_q_heads x splits x 528 B) go to a static
+ * device array of KVQ_STATIC_SCRATCH_BYTES that the library holds on each GPU until the process
+ * ends (its address is taken once per device by kvq_cache_create).  Nothing is allocated: no
+ * hipMalloc, hipFree or allocating library routine.  KVQ_ERR_SCRATCH (nothing enqueued) when the
+ * partials would exceed the scratch.  Every call on one GPU shares that GPU's array, which keeps
+ * the last call's contents (every partial is written before it is read, so nothing needs to start
+ * at zero): calls that overlap on one GPU (other streams, other threads) race. */
+kvq_status kvq_attn_decode_static(kvq_cache* cache, int layer, const void* q, int dtype, float* out,
+                                  int batch, float softmax_scale, void* stream);
 
 /* One decode step of one layer: kvq_append(k, v) followed by kvq_attn_decode(q) over the cache
  * that now includes the new token, in one call ([P1], [P2], [P3] as for those two calls).  Same

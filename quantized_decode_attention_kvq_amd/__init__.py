@@ -53,6 +53,9 @@ class KvCache:
     def attn_decode(self, layer, q, out, softmax_scale=0.0, stream=None):
         _kvq.kvq_attn_decode(self.handle, layer, q, out, softmax_scale, stream)
 
+    def attn_decode_static(self, layer, q, out, softmax_scale=0.0, stream=None):
+        _kvq.kvq_attn_decode_static(self.handle, layer, q, out, softmax_scale, stream)
+
     def append_attn_decode(self, layer, k, v, q, out, softmax_scale=0.0, stream=None):
         _kvq.kvq_append_attn_decode(self.handle, layer, k, v, q, out, softmax_scale, stream)
 

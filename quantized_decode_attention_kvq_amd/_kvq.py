@@ -17,12 +17,13 @@ KVQ_UNIFORM, KVQ_TURBO_QJL, KVQ_TURBO_MSE, KVQ_Q8_0, KVQ_TURBO_SPLIT = 0, 1, 2, 
 KVQ_OPT_SPLIT_TOKENS, KVQ_OPT_DECODE_PATH = 1, 2
 STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_INVALID_ARG", 2: "KVQ_ERR_UNSUPPORTED", 3: "KVQ_ERR_CAPACITY",
           4: "KVQ_ERR_NOT_READY", 5: "KVQ_ERR_BUFFER_TOO_SMALL", 6: "KVQ_ERR_MISALIGNED",
-          7: "KVQ_ERR_HOST_ALLOC", 8: "KVQ_ERR_DEVICE"}
+          7: "KVQ_ERR_HOST_ALLOC", 8: "KVQ_ERR_DEVICE", 9: "KVQ_ERR_SCRATCH"}
+KVQ_STATIC_SCRATCH_BYTES = 32 << 20
 EXPORTS = ["kvq_cache_required_bytes", "kvq_cache_create", "kvq_cache_destroy",
            "kvq_set_random_tables", "kvq_calibrate", "kvq_prefill_quantize", "kvq_append",
            "kvq_attn_decode", "kvq_get_layout", "kvq_get_tables", "kvq_set_option",
            "kvq_set_timing_events", "kvq_append_attn_decode", "kvq_attn_prefill",
-           "kvq_attn_prefill_workspace",
+           "kvq_attn_prefill_workspace", "kvq_attn_decode_static",
            "kvq_get_length", "kvq_status_str", "kvq_last_hip_error"]
 
 
@@ -75,6 +76,7 @@ def load():
         "kvq_prefill_quantize": [vp, i, vp, vp, i, i, i, vp],
         "kvq_append": [vp, i, vp, vp, i, i, vp],
         "kvq_attn_decode": [vp, i, vp, i, vp, i, f, vp],
+        "kvq_attn_decode_static": [vp, i, vp, i, vp, i, f, vp],
         "kvq_append_attn_decode": [vp, i, vp, vp, vp, i, vp, i, f, vp],
         "kvq_attn_prefill": [vp, i, vp, i, vp, i, i, f, vp, ctypes.c_size_t, vp],
         "kvq_attn_prefill_workspace": [vp, i, i, i, ctypes.POINTER(ctypes.c_size_t)],
@@ -273,6 +275,14 @@ def kvq_attn_decode(h, layer, q, out, softmax_scale=0.0, stream=None):
     _resident(q=q, out=out)
     _check(load().kvq_attn_decode(h, layer, _ptr(q), _dtype(q), _ptr(out), q.shape[0],
                                   float(softmax_scale), _stream(stream)), "kvq_attn_decode")
+
+
+def kvq_attn_decode_static(h, layer, q, out, softmax_scale=0.0, stream=None):
+    """kvq_attn_decode with the split partials in the library's static device scratch."""
+    _check_q_out(h, q, out, (None,))
+    _resident(q=q, out=out)
+    _check(load().kvq_attn_decode_static(h, layer, _ptr(q), _dtype(q), _ptr(out), q.shape[0],
+                                         float(softmax_scale), _stream(stream)), "kvq_attn_decode_static")
 
 
 def kvq_attn_prefill(h, layer, q, out, softmax_scale=0.0, workspace=None, stream=None):

@@ -14,6 +14,8 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kvq_internal.h"
 #include "kvq_lanes.h"
 
@@ -545,6 +547,38 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
 }
 
 } // namespace
+
+// Library-held scratch for the split partials of kvq_attn_decode_static (callers that cannot
+// allocate).  Each GPU the library runs on holds one copy until the process ends; in host code the
+// name is only a stand-in, so kernels receive the per-device address taken below.
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices] = {};
+} // namespace
+
+hipError_t static_scratch_setup(int device) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[device]) return hipSuccess;
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device) return hipErrorInvalidDevice; // the device must be current
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = static_cast<float*>(ptr);
+    return hipSuccess;
+}
+
+float* static_scratch(int device) {
+    if (device < 0 || device >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    return g_scratch_ptr[device];
+}
 
 hipError_t launch_decode_vec(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     dim3 grid(p.n_splits_total, p.Hkv, p.batch);

@@ -269,6 +269,8 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, 
         if (e == hipSuccess) e = launch_fill(c->inv_c(), n, 1.0f, s);
         if (e == hipSuccess) e = launch_fill(c->signs(), n, 1.0f, s);
     }
+    // the static scratch of kvq_attn_decode_static: its address on this device, once per device
+    if (e == hipSuccess) e = static_scratch_setup(c->device);
     if (e == hipSuccess && c->turbo()) e = launch_codebook(c->mu(), c->theta(), kLloydIters, 8, 128, s);
     if (e == hipSuccess && c->turbo4()) e = launch_codebook(c->mu16(), c->theta16(), kLloydIters, 16, 128, s);
     // split V: the 4-, 8- and 16-level codebooks of N(0, 1/64), table offset levels - 4
@@ -513,6 +515,24 @@ kvq_status kvq_attn_decode(kvq_cache* c, int layer, const void* q, int dtype, fl
     return KVQ_OK;
 }
 
+kvq_status kvq_attn_decode_static(kvq_cache* c, int layer, const void* q, int dtype, float* out, int batch,
+                                  float softmax_scale, void* stream) {
+    kvq_status st = check_decode(c, layer, q, dtype, out, batch, softmax_scale);
+    if (st != KVQ_OK) return st;
+    DecodeParams p;
+    bool matrix = false;
+    st = make_decode(c, layer, q, dtype, out, batch, softmax_scale, p, matrix);
+    if (st != KVQ_OK) return st;
+    const size_t need = (size_t)batch * p.Hq * p.n_splits_total * kPartialFloats * sizeof(float);
+    if (need > kStaticScratchBytes) return KVQ_ERR_SCRATCH;
+    float* ptr = static_scratch(c->device);
+    if (!ptr) return dev_fail(c, hipErrorNotInitialized);
+    p.partials = ptr; // every split writes its partial before the merge reads it: nothing to clear
+    const hipError_t e = launch_decode(c, p, matrix, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return dev_fail(c, e);
+    return KVQ_OK;
+}
+
 kvq_status kvq_append_attn_decode(kvq_cache* c, int layer, const void* k, const void* v, const void* q,
                                   int dtype, float* out, int batch, float softmax_scale, void* stream) {
     QuantParams qp;
@@ -725,6 +745,7 @@ const char* kvq_status_str(kvq_status s) {
     case KVQ_ERR_MISALIGNED: return "misaligned pointer";
     case KVQ_ERR_HOST_ALLOC: return "host allocation failed";
     case KVQ_ERR_DEVICE: return "HIP error";
+    case KVQ_ERR_SCRATCH: return "decode partials exceed the library's static scratch";
     }
     return "unknown status";
 }

@@ -144,6 +144,11 @@ hipError_t launch_decode_vec(const DecodeParams& p, hipStream_t s, hipEvent_t ev
 hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t s);
 bool mfma_path_supported(const DecodeParams& p);
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+// Static scratch of kvq_attn_decode_static: its size, the one-time per-device address lookup
+// (hipGetSymbolAddress, with that device current) and the address it found (null before).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch_setup(int device);
+float* static_scratch(int device);
 bool prefill_attn_supported(const PrefillParams& p);
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s);
 
