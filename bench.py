@@ -98,7 +98,8 @@ def traffic_record(wl: W.Workload):
         for line in open(path):
             if line.startswith("traffic_record "):
                 rec = json.loads(line[len("traffic_record "):])
-                if rec["workload"] == wl.name and rec["kernel_sha256"] == sha:
+                if rec["workload"] == wl.name and rec.get("batch", 1) == wl.batch and \
+                        rec["kernel_sha256"] == sha:
                     return rec
     return None
 
@@ -124,7 +125,7 @@ def split_kernel_name(wl: W.Workload) -> str:
             f"{wl.group} query heads per kv head)")
 
 
-def build_cache(wl: W.Workload, extra: int, log):
+def build_cache(wl: W.Workload, extra: int, log, keep_first: bool = True):
     import quantized_decode_attention_kvq_amd as K
     cfg = wl.kvq_config(max_context=wl.context + extra)
     cache = K.KvCache(device="cuda", **cfg)
@@ -145,7 +146,7 @@ def build_cache(wl: W.Workload, extra: int, log):
         cache.prefill_quantize(layer, k, v)
         ev[1].record(stream)
         pre.append(ev)
-        if layer == 0:
+        if layer == 0 and keep_first:
             keep = (k[:1].cpu(), v[:1].cpu())
         del k, v
         if layer % 8 == 7:
@@ -155,53 +156,111 @@ def build_cache(wl: W.Workload, extra: int, log):
     return cache, keep, prefill_s
 
 
+def _cpu_share():
+    """Host threads this process may use: its CPU affinity, capped at the 16 cores a one-GPU machine
+    grants a job."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(wl: W.Workload, kv0, budget_s: float):
-    """The oracle (single-threaded C) on a bounded sample: layer 0 / sequence 0 of the same
-    workload, planes built once, then full decode queries timed until the budget is spent."""
+    """The oracle (plain C, fp64 attention) on a bounded sample of the same workload: layer 0 /
+    sequence 0, every kv head at the full context.
+
+    - quantize: building the oracle's planes (rotation, balancing, group codes, packing) of the
+      sample, on one thread for two token-head streams and on all host threads for all of them;
+      source fp32 bytes per second;
+    - decode: full decode queries (all kv heads) on one thread, then on all host threads (one kv
+      head of one query per task; ctypes releases the interpreter lock inside the C calls)."""
+    import concurrent.futures as cf
+
     import oracle
     k0, v0 = (t[0].float().numpy() for t in kv0)  # [n][Hkv][128]
+    n = k0.shape[0]
     signs = W.rotation_signs(wl)[0]
     S = W.qjl_projection(wl)
     _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS)
-    planes = []
-    for h in range(wl.n_kv_heads):
-        row = []
-        for tensor, X in ((0, k0), (1, v0)):
-            scheme = wl.k_scheme if tensor == 0 else wl.v_scheme
-            bits = wl.k_bits if tensor == 0 else wl.v_bits
-            rot = (wl.rotate_k if tensor == 0 else wl.rotate_v) or W.is_turbo(scheme)
-            sink = wl.sinkhorn_iters > 0 and not W.is_turbo(scheme)
-            kw = dict(mu=mu, theta=theta, S=S)
-            if rot:
-                kw["signs"] = signs[h, tensor]
-            if sink:
-                cal = W.gen_calib(wl, 0, tensor)[:, h].float().numpy()
-                kw["c"], kw["inv_c"] = oracle.sinkhorn(cal, kw.get("signs"), wl.sinkhorn_iters)
-            if scheme == W.TURBO_SPLIT:
-                kw["perm"] = oracle.select_outliers(W.gen_calib(wl, 0, 1)[:, h].float().numpy())
-                _, kw["mu"], kw["theta"], _ = oracle.lloyd_max(oracle.LLOYD_ITERS, 1 << bits, 64)
-                _, kw["mu2"], kw["theta2"], _ = oracle.lloyd_max(oracle.LLOYD_ITERS, 1 << (bits - 1), 64)
-            tb = oracle.TableSet(**kw)
-            p = oracle.Plane(scheme, bits, rot, sink, wl.window, tensor, X.shape[0])
-            p.append(X[:, h], tb)
-            row += [p, tb]
-        planes.append(row)
+    threads = _cpu_share()
+
+    def tables(h, tensor):
+        scheme = wl.k_scheme if tensor == 0 else wl.v_scheme
+        bits = wl.k_bits if tensor == 0 else wl.v_bits
+        rot = (wl.rotate_k if tensor == 0 else wl.rotate_v) or W.is_turbo(scheme)
+        sink = wl.sinkhorn_iters > 0 and not W.is_turbo(scheme)
+        kw = dict(mu=mu, theta=theta, S=S)
+        if rot:
+            kw["signs"] = signs[h, tensor]
+        if sink:
+            cal = W.gen_calib(wl, 0, tensor)[:, h].float().numpy()
+            kw["c"], kw["inv_c"] = oracle.sinkhorn(cal, kw.get("signs"), wl.sinkhorn_iters)
+        if scheme == W.TURBO_SPLIT:
+            kw["perm"] = oracle.select_outliers(W.gen_calib(wl, 0, 1)[:, h].float().numpy())
+            _, kw["mu"], kw["theta"], _ = oracle.lloyd_max(oracle.LLOYD_ITERS, 1 << bits, 64)
+            _, kw["mu2"], kw["theta2"], _ = oracle.lloyd_max(oracle.LLOYD_ITERS, 1 << (bits - 1), 64)
+        return oracle.TableSet(**kw), scheme, bits, rot, sink
+
+    units = [(h, tensor) for h in range(wl.n_kv_heads) for tensor in (0, 1)]
+    tabs = {u: tables(*u) for u in units}
+
+    def build(u):
+        h, tensor = u
+        tb, scheme, bits, rot, sink = tabs[u]
+        p = oracle.Plane(scheme, bits, rot, sink, wl.window, tensor, n)
+        p.append((k0 if tensor == 0 else v0)[:, h], tb)
+        return p
+
+    src_bytes = n * 128 * 4  # one token-head stream of fp32 source
+    t0 = time.perf_counter()
+    for u in units[:2]:
+        build(u)
+    q1 = 2 * src_bytes / (time.perf_counter() - t0)
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        built = dict(zip(units, ex.map(build, units)))
+    qall = len(units) * src_bytes / (time.perf_counter() - t0)
+    planes = [(built[(h, 0)], tabs[(h, 0)][0], built[(h, 1)], tabs[(h, 1)][0]) for h in range(wl.n_kv_heads)]
+
     q = W.gen_q(wl, 0, 0)[0].float().numpy()
     G = wl.group
-    n_q = 0
+
+    def head(h):
+        pk, tk, pv, tv = planes[h]
+        oracle.attention(pk, pv, tk, tv, q[h * G:(h + 1) * G])
+
+    half = budget_s / 2
+    n1 = 0
     t0 = time.perf_counter()
     while True:
         for h in range(wl.n_kv_heads):
-            pk, tk, pv, tv = planes[h]
-            oracle.attention(pk, pv, tk, tv, q[h * G:(h + 1) * G])
-        n_q += 1
-        if time.perf_counter() - t0 > budget_s:
+            head(h)
+        n1 += 1
+        if time.perf_counter() - t0 > half:
             break
-    dt = time.perf_counter() - t0
-    return {"value": n_q / dt, "unit": "queries/s", "cores": 1, "kind": "oracle",
-            "sample": f"layer 0, sequence 0, {k0.shape[0]} tokens, all {wl.n_kv_heads} kv heads "
-                      f"x {G} query heads; {n_q} full decode queries in {dt:.1f} s "
-                      f"(fp64 attention over the oracle's own planes; plane building not timed)"}
+    dt1 = time.perf_counter() - t0
+    nall = 0
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        while time.perf_counter() - t0 <= half:
+            list(ex.map(head, [h for _ in range(threads) for h in range(wl.n_kv_heads)]))
+            nall += threads
+    dtall = time.perf_counter() - t0
+    qb = query_bytes(wl, n)
+    return {"value": n1 / dt1, "unit": "queries/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0, sequence 0, {n} tokens, all {wl.n_kv_heads} kv heads x {G} query "
+                      f"heads; {n1} full decode queries in {dt1:.1f} s on one thread (fp64 attention "
+                      f"over the oracle's own planes; plane building timed separately)",
+            "compressed_GBps": n1 / dt1 * qb / 1e9,
+            "all_cores": {"value": nall / dtall, "unit": "queries/s", "cores": threads,
+                          "nproc": os.cpu_count(), "compressed_GBps": nall / dtall * qb / 1e9,
+                          "sample": f"{nall} queries in {dtall:.1f} s, one kv head per task"},
+            "quantize": {"GBps_1_core": q1 / 1e9, "GBps_all_cores": qall / 1e9, "cores": threads,
+                         "unit": "GB/s of fp32 source",
+                         "sample": f"oracle planes of layer 0 / sequence 0: 2 of the {len(units)} "
+                                   f"token-head streams ({n} tokens each) on one thread, all "
+                                   f"{len(units)} on {threads} threads"}}
 
 
 def copy_probe():
@@ -277,6 +336,86 @@ def prefill_attention_report(cache, wl: W.Workload, n_q: int = 512, reps: int = 
                          "flops_per_call": flops}}
 
 
+def measure(wl: W.Workload, cache, prefill_s, steps: int, warmup: int, fused: bool = True):
+    """Decode steps over a built cache: `warmup` untimed steps, then `steps` timed steps (events
+    on the launch stream around them, nothing else inside), then the same steps again with
+    events bound to each split-K dispatch for the kernel's own duration."""
+    L, B = wl.n_layers, wl.batch
+    pool = 4
+    step_in = [[W.gen_step_kv(wl, layer, s, device="cuda") for layer in range(L)] for s in range(pool)]
+    qs = [[W.gen_q(wl, layer, s, device="cuda") for layer in range(L)] for s in range(pool)]
+    out = torch.empty((L, B, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    run = step_driver(cache, wl, step_in, qs, out, stream, fused=fused)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    n_start = cache.length(0)
+    # timed region: `steps` decode steps, nothing but the library's own launches inside
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t0.record(stream)
+    run(steps)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    elapsed = t0.elapsed_time(t1) / 1e3
+    # kernel pass: the same steps again with start / stop events bound by the library to each
+    # split-K kernel's own dispatch on the launch stream (each recorded once here so it exists)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps * L)]
+    for pair in evs:
+        for e in pair:
+            e.record(stream)
+    torch.cuda.synchronize()
+    run(steps, evs)
+    torch.cuda.synchronize()
+    split = np.array([pair[0].elapsed_time(pair[1]) for pair in evs]) / 1e3
+    assert torch.isfinite(out).all()
+
+    queries = L * B * steps
+    qps = queries / elapsed
+    n_mean = 0.5 * (n_start + 1 + cache.length(0))  # mean context over both passes
+    bytes_per_launch = B * query_bytes(wl, int(round(n_mean)))
+    split_mean = float(split.mean())
+    achieved = bytes_per_launch / split_mean / 1e9
+    rec = traffic_record(wl)
+    traffic = None if rec is None else rec["fetch_bytes"] + rec["write_bytes"]
+    return {
+        "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": 1e3 * elapsed / steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "batch": B, "context": wl.context,
+                   "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads,
+                   "k_cache": [wl.k_scheme, wl.k_bits, bool(wl.rotate_k)],
+                   "v_cache": [wl.v_scheme, wl.v_bits, bool(wl.rotate_v)],
+                   "fp32_window": wl.window, "sinkhorn_iters": wl.sinkhorn_iters,
+                   "source_dtype": wl.dtype,
+                   "step": ("kvq_append_attn_decode" if fused
+                            else "kvq_append + kvq_attn_decode") + " per layer"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_unit": "bytes/launch",
+                     "traffic_vs_algorithmic": None if traffic is None else traffic / bytes_per_launch,
+                     "kernel": split_kernel_name(wl),
+                     "bytes_per_launch": bytes_per_launch, "avg_launch_us": 1e6 * split_mean,
+                     "p10_us": 1e6 * float(np.percentile(split, 10)),
+                     "p90_us": 1e6 * float(np.percentile(split, 90)),
+                     "layer_step_us": 1e6 * elapsed / (steps * L),
+                     "step_GBps": B * query_bytes(wl, int(round(n_mean))) * L * steps / elapsed / 1e9},
+        "wall_s": wall,
+        "prefill": prefill_report(wl, prefill_s),
+    }
+
+
+# The other half of the metric: the long-context workloads, each measured on its own cache (built,
+# measured, freed) after the headline, in the same JSON line.
+LONG_CONTEXT = [W.LLAMA3B_128K_PROGRESSIVE, W.LLAMA3B_128K_PROGRESSIVE.with_(batch=8),
+                W.DENSE27B_120K_KVARN, W.DENSE27B_120K_U8]
+
+
 def gpu_info():
     p = torch.cuda.get_device_properties(0)
     info = {"name": p.name, "compute_units": p.multi_processor_count,
@@ -296,6 +435,8 @@ def main():
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="only the headline workload (skip the 128K / 120K lines)")
     ap.add_argument("--separate", action="store_true",
                     help="kvq_append + kvq_attn_decode per layer instead of kvq_append_attn_decode")
     ap.add_argument("--copy-probe", action="store_true",
@@ -320,78 +461,29 @@ def main():
     cache, kv0, prefill_s = build_cache(wl, args.warmup + 2 * args.steps, log)
     log(f"cache built in {time.perf_counter() - t_build:.1f} s")
 
-    L, B = wl.n_layers, wl.batch
-    pool = 4
-    step_in = [[W.gen_step_kv(wl, layer, s, device="cuda") for layer in range(L)] for s in range(pool)]
-    qs = [[W.gen_q(wl, layer, s, device="cuda") for layer in range(L)] for s in range(pool)]
-    out = torch.empty((L, B, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-    run = step_driver(cache, wl, step_in, qs, out, stream, fused=not args.separate)
-
-    run(args.warmup)
-    torch.cuda.synchronize()
-    n_start = cache.length(0)
-    # timed region: `steps` decode steps, nothing but the library's own launches inside
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    t0.record(stream)
-    run(args.steps)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    elapsed = t0.elapsed_time(t1) / 1e3
-    # kernel pass: the same steps again with start / stop events bound by the library to each
-    # split-K kernel's own dispatch on the launch stream (each recorded once here so it exists)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps * L)]
-    for pair in evs:
-        for e in pair:
-            e.record(stream)
-    torch.cuda.synchronize()
-    run(args.steps, evs)
-    torch.cuda.synchronize()
-    split = np.array([pair[0].elapsed_time(pair[1]) for pair in evs]) / 1e3
-    assert torch.isfinite(out).all()
-
-    queries = L * B * args.steps
-    qps = queries / elapsed
-    n_mean = 0.5 * (n_start + 1 + cache.length(0))  # mean context over both passes
-    bytes_per_launch = B * query_bytes(wl, int(round(n_mean)))
-    split_mean = float(split.mean())
-    achieved = bytes_per_launch / split_mean / 1e9
-    rec = traffic_record(wl)
-    traffic = None if rec is None else rec["fetch_bytes"] + rec["write_bytes"]
-    res = {
-        "metric": METRIC, "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": 1e3 * elapsed / args.steps,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": wl.name, "layers": L, "batch": B, "context": wl.context,
-                   "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads,
-                   "k_cache": [wl.k_scheme, wl.k_bits, bool(wl.rotate_k)],
-                   "v_cache": [wl.v_scheme, wl.v_bits, bool(wl.rotate_v)],
-                   "fp32_window": wl.window, "sinkhorn_iters": wl.sinkhorn_iters,
-                   "step": ("kvq_append + kvq_attn_decode" if args.separate
-                            else "kvq_append_attn_decode") + " per layer"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "traffic_unit": "bytes/launch",
-                     "traffic_vs_algorithmic": None if traffic is None else traffic / bytes_per_launch,
-                     "kernel": split_kernel_name(wl),
-                     "bytes_per_launch": bytes_per_launch, "avg_launch_us": 1e6 * split_mean,
-                     "p10_us": 1e6 * float(np.percentile(split, 10)),
-                     "p90_us": 1e6 * float(np.percentile(split, 90)),
-                     "layer_step_us": 1e6 * elapsed / (args.steps * L)},
-        "wall_s": wall,
-        "prefill": prefill_report(wl, prefill_s),
-    }
+    res = measure(wl, cache, prefill_s, args.steps, args.warmup, not args.separate)
     res["prefill_attention"] = prefill_attention_report(cache, wl)
     res["gpu"] = gpu_info()
     res["gpu"]["copy_GBps"] = copy_bandwidth()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(wl, kv0, args.cpu_budget)
+    if not args.no_long_context and args.workload == W.LLAMA3B_32K_KVARN.name and not args.batch:
+        del cache, kv0
+        torch.cuda.empty_cache()
+        res["long_context"] = []
+        for lwl in LONG_CONTEXT:
+            st, wu = min(args.steps, 20), min(args.warmup, 3)
+            log(f"long-context workload {lwl.name} batch {lwl.batch}: building cache")
+            lcache, _, lpre = build_cache(lwl, wu + 2 * st, log, keep_first=False)
+            r = measure(lwl, lcache, lpre, st, wu, not args.separate)
+            for k in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data"):
+                r.pop(k)
+            res["long_context"].append(r)
+            log(f"  {lwl.name} B{lwl.batch}: {r['value']:.0f} queries/s, {r['ms_per_step']:.3f} ms/step, "
+                f"split-K {r['roofline']['avg_launch_us']:.1f} us = {r['roofline']['frac']:.3f} of peak")
+            del lcache
+            torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 
 
