@@ -237,24 +237,28 @@ kvq_status kvq_append_attn_decode(kvq_cache* cache, int layer, const void* k, co
  * the cache as it stands: out[b][i][h] = sum_{t <= pos} softmax_t(scale <q[b][i][h], k_t>) v_t.
  * q: device [batch][n_q][n_q_heads][128] of dtype; out: device [batch][n_q][n_q_heads][128]
  * fp32 (row-major, 16-byte aligned).  softmax_scale <= 0 means 1/sqrt(128).
- * workspace: optional caller-owned device memory (16-byte aligned, workspace_bytes long) for the
+ * Every key and value scheme of kvq_config is read, with or without the FP32 window; TurboQuant-
+ * QJL keys score as in kvq_attn_decode ([P3] method table, TurboQuant row: n <R q, mu[code]>
+ * plus the 1-bit QJL estimate of the residual's inner product).
+ * workspace: optional caller-owned device memory (16-byte aligned, workspace_bytes long).  It
+ * holds, first, when fp32_window > 0 beside rotated, balanced or TurboQuant codes, the window's
+ * originals mapped into the code domain (batch x n_kv_heads x 2 x 128 x 128 fp32), then the
  * partial results when the keys of each query are split over several workgroups; NULL uses the
  * cache's own workspace.  kvq_attn_prefill_workspace() gives the bytes the fastest split plan
- * needs; with less, the call uses fewer splits (the result agrees to rounding).  Like the cache's
- * own workspace, it must not be in use by another call at the same time.
+ * needs; with less, the call uses fewer splits (the result agrees to rounding), and with less
+ * than the window copy it fails with KVQ_ERR_BUFFER_TOO_SMALL.  Like the cache's own workspace,
+ * it must not be in use by another call at the same time.
  * Errors (nothing enqueued): KVQ_ERR_INVALID_ARG for a bad handle, layer, pointer, dtype, batch
  * outside 1 .. max_batch, n_q < 1, or n_q above some sequence's length; KVQ_ERR_MISALIGNED;
- * KVQ_ERR_NOT_READY before the layer's tables / calibration are set; KVQ_ERR_UNSUPPORTED for
- * TurboQuant-QJL keys, and for an FP32 window beside rotated or balanced codes (the kernel
- * reads UNIFORM / Q8_0 keys and UNIFORM, Q8_0, TURBO_MSE or TURBO_SPLIT values; the window's
- * originals are taken as they are, so with fp32_window > 0 both tensors must be UNIFORM without
- * rotation or Sinkhorn balancing). */
+ * KVQ_ERR_NOT_READY before the layer's tables / calibration are set; KVQ_ERR_BUFFER_TOO_SMALL as
+ * above. */
 kvq_status kvq_attn_prefill(kvq_cache* cache, int layer, const void* q, int dtype, float* out,
                             int n_q, int batch, float softmax_scale, void* workspace,
                             size_t workspace_bytes, void* stream);
 
 /* Device workspace bytes for kvq_attn_prefill(cache, layer, ..., n_q, batch, ...) with the
- * layer's current lengths: 0 when one split per query fills the GPU.  Pure host computation;
+ * layer's current lengths: the mapped window copy (if the cache needs one) plus the partials of
+ * the fastest split plan (none when one split per query fills the GPU).  Pure host computation;
  * KVQ_ERR_INVALID_ARG as for kvq_attn_prefill. */
 kvq_status kvq_attn_prefill_workspace(const kvq_cache* cache, int layer, int n_q, int batch,
                                       size_t* bytes);

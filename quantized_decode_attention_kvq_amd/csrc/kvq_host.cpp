@@ -146,7 +146,11 @@ Plan make_plan(const kvq_config* c) {
     const size_t calib = c->sinkhorn_iters > 0
                              ? (size_t)2 * c->n_kv_heads * (c->calib_tokens + 2) * kDim * sizeof(double)
                              : 0;
-    p.work_bytes = align_up(std::max(partial, calib));
+    // prefill attention beside rotated or balanced codes also keeps the mapped window there
+    const size_t win = window_in_code_domain(p.geom[0], p.geom[1], c->fp32_window)
+                           ? align_up(prefill_window_bytes(c->max_batch, c->n_kv_heads))
+                           : 0;
+    p.work_bytes = align_up(std::max(partial + win, calib));
     p.off_work = off;
     off += p.work_bytes;
     p.off_planes = off;
@@ -605,6 +609,14 @@ int prefill_splits(const kvq_cache* c, int n_q, int batch, int max_len, size_t c
     return best;
 }
 
+// Workspace bytes ahead of the partials: the window mapped into the code domain, if the planes
+// need it (256-byte aligned, so the partials stay aligned).
+size_t prefill_window_area(const kvq_cache* c, int batch) {
+    return window_in_code_domain(c->plan.geom[0], c->plan.geom[1], c->cfg.fp32_window)
+               ? align_up(prefill_window_bytes(batch, c->cfg.n_kv_heads))
+               : 0;
+}
+
 kvq_status check_prefill(const kvq_cache* c, int layer, int n_q, int batch, int* max_len) {
     if (!c || layer < 0 || layer >= c->cfg.n_layers || batch < 1 || batch > c->cfg.max_batch || n_q < 1)
         return KVQ_ERR_INVALID_ARG;
@@ -626,7 +638,8 @@ kvq_status kvq_attn_prefill_workspace(const kvq_cache* c, int layer, int n_q, in
     if (st != KVQ_OK) return st;
     if (!bytes) return KVQ_ERR_INVALID_ARG;
     const int S = prefill_splits(c, n_q, batch, max_len, static_cast<size_t>(-1));
-    *bytes = S > 1 ? (size_t)batch * n_q * c->cfg.n_q_heads * S * kPartialFloats * sizeof(float) : 0;
+    *bytes = prefill_window_area(c, batch) +
+             (S > 1 ? (size_t)batch * n_q * c->cfg.n_q_heads * S * kPartialFloats * sizeof(float) : 0);
     return KVQ_OK;
 }
 
@@ -645,6 +658,8 @@ kvq_status kvq_attn_prefill(kvq_cache* c, int layer, const void* q, int dtype, f
     fill_params_common(c, layer, p.layer_base, p.seq_stride, p.head_stride, p.plane_off, p.geom);
     p.signs = c->signs() + c->table_off(layer);
     p.cs = c->cs() + c->table_off(layer);
+    p.inv_c = c->inv_c() + c->table_off(layer);
+    p.qjl_st = c->ST();
     p.mu = c->mu();
     p.mu16 = c->mu16();
     p.perm = c->perm() + c->perm_off(layer);
@@ -661,9 +676,14 @@ kvq_status kvq_attn_prefill(kvq_cache* c, int layer, const void* q, int dtype, f
     const int* len = &c->len[(size_t)layer * c->cfg.max_batch];
     for (int b = 0; b < batch; ++b) p.len[b] = len[b];
     if (!prefill_attn_supported(p)) return KVQ_ERR_UNSUPPORTED;
-    const size_t cap = workspace ? workspace_bytes : c->plan.work_bytes;
-    p.partials = workspace ? static_cast<float*>(workspace) : reinterpret_cast<float*>(c->base + c->plan.off_work);
-    p.n_splits = prefill_splits(c, n_q, batch, max_len, cap);
+    // workspace: [mapped window (if any)][partials]
+    char* ws = workspace ? static_cast<char*>(workspace) : c->base + c->plan.off_work;
+    const size_t ws_bytes = workspace ? workspace_bytes : c->plan.work_bytes;
+    const size_t win = prefill_window_area(c, batch);
+    if (ws_bytes < win) return KVQ_ERR_BUFFER_TOO_SMALL;
+    p.wring = win ? reinterpret_cast<float*>(ws) : nullptr;
+    p.partials = reinterpret_cast<float*>(ws + win);
+    p.n_splits = prefill_splits(c, n_q, batch, max_len, ws_bytes - win);
     const hipError_t e = launch_prefill_attn(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return dev_fail(c, e);
     return KVQ_OK;

@@ -89,13 +89,17 @@ struct PrefillParams {
     const void* q;            // [batch][n_q][Hq][128] of dtype
     float* out;               // [batch][n_q][Hq][128]
     float* partials;          // [batch][n_q][Hq][n_splits][kPartialFloats] when n_splits > 1
+    float* wring;             // [batch][Hkv][2][kWindowMax][128]: the window mapped into the code
+                              // domain (window_in_code_domain), else null
     char* layer_base;
     size_t seq_stride, head_stride;
     size_t plane_off[2];
     PlaneGeom geom[2];
     const float* signs;       // layer base [Hkv][2][128]
     const float* cs;          // layer base [Hkv][2][128] Sinkhorn c
-    const float* mu;          // [8]: TurboQuant-MSE V codebook (3-bit)
+    const float* inv_c;       // layer base [Hkv][2][128] 1 / c (window originals into the code domain)
+    const float* qjl_st;      // [128 j][128 i] = S[i][j] (TurboQuant-QJL keys)
+    const float* mu;          // [8]: 3-bit TurboQuant codebook (QJL K, MSE V)
     const float* mu16;        // [16]: 4-bit TurboQuant-MSE V codebook
     const int* perm;          // layer base [Hkv][128] (split V)
     const float* mu64;        // [kSplitTable] split codebooks
@@ -104,6 +108,15 @@ struct PrefillParams {
     float qscale;             // softmax scale * log2(e)
     int len[kMaxBatch];
 };
+
+// An FP32 window beside rotated or balanced codes (TurboQuant planes are rotated): prefill
+// attention reads the window's originals from a copy mapped into the code domain.
+inline bool window_in_code_domain(const PlaneGeom& K, const PlaneGeom& V, int window) {
+    return window > 0 && (K.rotate || K.sinkhorn || V.rotate || V.sinkhorn || V.scheme == kTurboSplit);
+}
+inline size_t prefill_window_bytes(int batch, int Hkv) {
+    return (size_t)batch * Hkv * 2 * kWindowMax * kDim * sizeof(float);
+}
 
 struct CalibParams {
     const void* src[2];       // [n][Hkv][128] of dtype

@@ -12,7 +12,10 @@
 //    q' = R(q) .* c, and the output is mapped back with c_V and R_V^-1.
 //  * "LLM memory saving ... 2026", TurboQuant row and application rules (K = Q8, V = TurboQuant),
 //    with the outlier split of its 2.5 / 3.5-bit figures: values may be TurboQuant-MSE codes,
-//    n mu[code] in the rotated domain (two 64-channel halves for the split).
+//    n mu[code] in the rotated domain (two 64-channel halves for the split).  Keys may be
+//    TurboQuant-QJL codes (same row, 1-bit QJL for an unbiased inner product): the score of key t
+//    is n_t <rho_q, mu[code_t]> + gamma_t sqrt(pi/2) / 128 sum_i (2 b_ti - 1) (S rho_q)_i with
+//    rho_q = R(q), i.e. a 256-long contraction of [n mu[code], f_t signs] with [rho_q, S rho_q].
 //
 // How.  The (query, head) pairs of one (sequence, kv head) are rows r = G * i + h (query i,
 // query head h of the kv head's group).  A workgroup of 8 waves owns 128 consecutive rows (16 per
@@ -27,11 +30,20 @@
 //    key rows are ordered in LDS so that each lane's score values are exactly the P^T operand
 //    of the PV product, which therefore never leaves the registers;
 //  * an online softmax per row in the log2 domain (tokens after the row's position are masked),
-//    then O^T += V_hi^T P^T + V_lo^T P^T (values as the A operand, fp16 probabilities as B).
+//    then O^T += V_hi^T P^T + V_lo^T P^T (values as the A operand, fp16 weights as B; the
+//    softmax sum adds the same fp16 weights).
 // With one split, each row's output is divided by its softmax sum and mapped back with c_V and
 // R_V^-1 in the same kernel; with several, each split writes (m, l, acc) and a merge kernel
-// combines them in a fixed order.  TurboQuant-QJL keys, and an FP32 window beside rotated or
-// balanced codes, are refused by the host (not supported by this kernel).
+// combines them in a fixed order.
+// TurboQuant-QJL keys: the key rows hold n mu[code] (hi, lo) like any dequantized key; the QJL
+// signs stay in LDS as their 16-byte words, and each lane expands its eight signs of a k-slice
+// into the A operands +-f_t hi and lo (f_t = gamma_t sqrt(pi/2) / 128 per key row) against
+// S q' as fp16 hi and lo, three more products per slice accumulated with the others.
+// FP32 window: in the plain domain the window tokens' original values overwrite their LDS units
+// in the dequantizer's own thread mapping; beside rotated or balanced codes, a chunk holding
+// window tokens gets one more barrier after which each wave maps whole window tokens into the
+// code domain (R(x) .* 1/c for uniform planes, R(x) for TurboQuant, the two 64-point rotations
+// of the permuted channels for a split V) before writing them, and their QJL scale f_t is zero.
 #include <hip/hip_runtime.h>
 
 #include "kvq_internal.h"
@@ -63,7 +75,7 @@ constexpr int kVmRow = 80;                        // value meta row, fp16 (64 to
 constexpr int kUnits = 64 * 16 / kThreads;        // 8-code units of a chunk per thread (K; V alike)
 static_assert(kWaves == 8, "two waves per SIMD");
 static_assert(kUnits * kThreads == 1024, "a chunk is 1024 key units and 1024 value units");
-static_assert(kLdsHalves * 2 >= kWaves * 16 * kDim * 4, "the q' rows fit in the chunk buffers");
+static_assert(kLdsHalves * 2 >= 2 * kWaves * 16 * kDim * 4, "the q' rows and the S q' rows fit in the chunk buffers");
 
 // LDS row of chunk token t (0..63) in the key buffer.  Score tile b (16 key rows) holds at row
 // 4u + v the token 32 (b / 2) + 8u + 4 (b % 2) + v, so that a lane's four score values of tile
@@ -78,16 +90,20 @@ __device__ __forceinline__ int key_lds_row(int t) {
 struct ChunkRegs {
     uint2 kc[kUnits], vc[kUnits];
     uint32_t kc3[kUnits]; // 3-bit keys: the third plane word of the unit's group
-    uint32_t ks[kUnits], kz[kUnits]; // fp16 bits of the key unit's scale and zero
+    uint32_t ks[kUnits], kz[kUnits]; // fp16 bits of the key unit's scale and zero (QJL: n, gamma)
+    uint32_t kq;          // QJL keys: one sign word of the chunk (threads 0..255)
     u4 vm;
 };
 
 struct Planes {
-    const uint8_t *kcodes, *kmeta, *vcodes, *vmeta;
+    const uint8_t *kcodes, *kmeta, *kqjl, *vcodes, *vmeta;
 };
 
-// Key kinds: KB = 4 or 8 (uniform codes), or 3 (uniform 3-bit codes as three bit planes in the
-// TurboQuant 3-bit K row layout).
+// Key kinds: KB = 4 or 8 (uniform codes), 3 (uniform 3-bit codes as three bit planes in the
+// TurboQuant 3-bit K row layout), or kQjlK (TurboQuant-QJL: 3-bit Lloyd-Max codes in that row
+// layout, fp16 n and gamma per row, 16 bytes of QJL signs per row).
+constexpr int kQjlK = -3;
+constexpr float kKappa = 0.0097915166977774f; // sqrt(pi/2) / 128
 // Value kinds: VB = 4 or 8 (uniform codes), 3 (uniform 3-bit codes as three bit planes in the
 // TurboQuant-MSE V layout, read by TurboQuant value units), -b for TurboQuant-MSE V with b = 3 or
 // 4 bit planes,
@@ -115,7 +131,7 @@ __device__ __forceinline__ void load_codes(const Planes& P, int ci, int tid, Chu
     for (int j = 0; j < kUnits; ++j) {
         const int u = tid + kThreads * j, g = (u >> 2) & 3, word = 4 * (u & 3) + g;
         const size_t row = (size_t)64 * ci + (u >> 4);
-        if constexpr (KB == 3) {
+        if constexpr (KB == 3 || KB == kQjlK) {
             // the three plane words of group g (the unit's codes are their nibble u % 4)
             const uint32_t* pw = reinterpret_cast<const uint32_t*>(P.kcodes + row * 48 + 12 * g);
             R.kc[j].x = pw[0];
@@ -123,9 +139,19 @@ __device__ __forceinline__ void load_codes(const Planes& P, int ci, int tid, Chu
             R.kc3[j] = pw[2];
         } else if constexpr (KB == 4) R.kc[j].x = reinterpret_cast<const uint32_t*>(P.kcodes + row * 64)[word];
         else R.kc[j] = reinterpret_cast<const uint2*>(P.kcodes + row * 128)[word];
-        const uint16_t* m = reinterpret_cast<const uint16_t*>(P.kmeta + row * 16);
-        R.ks[j] = m[g]; // kept apart until the dequantization: no wait on the load here
-        R.kz[j] = m[4 + g];
+        if constexpr (KB == kQjlK) {
+            const uint16_t* m = reinterpret_cast<const uint16_t*>(P.kmeta + row * 4);
+            R.ks[j] = m[0]; // n
+            R.kz[j] = m[1]; // gamma
+        } else {
+            const uint16_t* m = reinterpret_cast<const uint16_t*>(P.kmeta + row * 16);
+            R.ks[j] = m[g]; // kept apart until the dequantization: no wait on the load here
+            R.kz[j] = m[4 + g];
+        }
+    }
+    if constexpr (KB == kQjlK) {
+        // sign word tid % 4 of physical row tid / 4
+        if (tid < 256) R.kq = reinterpret_cast<const uint32_t*>(P.kqjl + ((size_t)64 * ci + (tid >> 2)) * 16)[tid & 3];
     }
     if constexpr (split_kind(VB)) {
         constexpr int BO = kSplitV - VB, W = 2 * BO - 1;
@@ -293,9 +319,16 @@ __device__ __forceinline__ void turbo_values(const uint32_t* wd, const _Float16*
     }
 }
 
+// QJL keys: the 3-bit code of each of a key unit's elements 2k, 2k + 1 (bits 4 kb + k and
+// 16 + 4 kb + k of the three plane words)
+__device__ __forceinline__ uint32_t code3_at(uint32_t p0, uint32_t p1, uint32_t p2, int sh) {
+    return ((p0 >> sh) & 1u) | (((p1 >> sh) & 1u) << 1) | (((p2 >> sh) & 1u) << 2);
+}
+
 template <int KB, int VB>
 __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const _Float16 (*sm)[4][kVmRow], int tid,
-                                              const ChunkRegs& R, const float* mg) {
+                                              const ChunkRegs& R, const float* mg, const float* mgk, uint32_t* ssg,
+                                              uint32_t* sf) {
     // -1 in a register the compiler cannot see through: hi * (-1) + y stays one mixed-precision
     // fma (v_fma_mix*) instead of being rewritten as a conversion and a subtraction
     float mone = -1.0f;
@@ -307,18 +340,49 @@ __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const 
         const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)R.ks[j]);
         const _Float16 zr = __builtin_bit_cast(_Float16, (uint16_t)R.kz[j]);
         u4 hi, lo;
+        if constexpr (KB == kQjlK) {
+            // n mu[code] in fp32, then fp16 hi + remainder lo; the row's first unit writes f_t
+            const float n = (float)sc;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            h2v c;
-            if constexpr (KB == 3) c = code_pair3(R.kc[j].x, R.kc[j].y, R.kc3[j], u & 3, k);
-            else c = code_pair<KB>(R.kc[j], k);
-            const Pair q = dequant_pair(h2v{sc, sc}, c, h2v{zr, zr}, mone);
-            hi[k] = q.hi;
-            lo[k] = q.lo;
+            for (int k = 0; k < 4; ++k) {
+                const int sh = 4 * (u & 3) + k;
+                float ye = n * centroid<3>(code3_at(R.kc[j].x, R.kc[j].y, R.kc3[j], sh), mgk);
+                float yo = n * centroid<3>(code3_at(R.kc[j].x, R.kc[j].y, R.kc3[j], sh + 16), mgk);
+                // the products are rounded to fp32 once, here: with contraction the compiler may
+                // otherwise take hi from the fp32 product and lo from the exact one, which differ
+                // by one fp16 ulp where the fp32 product is an fp16 tie
+                asm volatile("" : "+v"(ye), "+v"(yo));
+                const h2v h = h2v{(_Float16)ye, (_Float16)yo};
+                const h2v r = h2v{(_Float16)(ye - (float)h[0]), (_Float16)(yo - (float)h[1])};
+                hi[k] = __builtin_bit_cast(uint32_t, h);
+                lo[k] = __builtin_bit_cast(uint32_t, r);
+            }
+            if (w == 0) {
+                const float f = (float)zr * kKappa;
+                const _Float16 fh = (_Float16)f, fl = (_Float16)(f - (float)fh);
+                sf[key_lds_row(t)] = (uint32_t)__builtin_bit_cast(uint16_t, fh) |
+                                     ((uint32_t)__builtin_bit_cast(uint16_t, fl) << 16);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                h2v c;
+                if constexpr (KB == 3) c = code_pair3(R.kc[j].x, R.kc[j].y, R.kc3[j], u & 3, k);
+                else c = code_pair<KB>(R.kc[j], k);
+                const Pair q = dequant_pair(h2v{sc, sc}, c, h2v{zr, zr}, mone);
+                hi[k] = q.hi;
+                lo[k] = q.lo;
+            }
         }
         _Float16* dst = sk + key_lds_row(t) * kKS + 8 * w; // channels 32 (w / 4) + 8 (w % 4) + i
         *reinterpret_cast<u4*>(dst) = hi;
         *reinterpret_cast<u4*>(dst + 64 * kKS) = lo;
+    }
+    if constexpr (KB == kQjlK) {
+        if (tid < 256) {
+            const int p = tid >> 2, t = 4 * (p & 15) + (p >> 4);
+            ssg[4 * key_lds_row(t) + (tid & 3)] = R.kq;
+        }
     }
     if constexpr (VB < 0 || VB == 3) {
         // TurboQuant-MSE values n_t mu[code] (fp32 product), or 3-bit uniform values z + s c
@@ -354,9 +418,11 @@ __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const 
             h8 hi, lo;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const _Float16 h = (_Float16)tok[i];
+                float y = tok[i];
+                asm volatile("" : "+v"(y)); // one fp32 value for hi and lo (see the QJL keys)
+                const _Float16 h = (_Float16)y;
                 hi[i] = h;
-                lo[i] = (_Float16)(tok[i] - (float)h);
+                lo[i] = (_Float16)(y - (float)h);
             }
             const int N = 4 * hN + 2 * par + qq, d = 16 * N + n;
             _Float16* dst = sv + d * kVS + 8 * ((4 * half + kb) ^ N);
@@ -388,13 +454,14 @@ __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const 
     }
 }
 
-// FP32 window (progressive caches, plain domain): tokens nqd .. len - 1 of the chunk take their
-// original values from the rings instead of the codes.  Each thread rewrites exactly the LDS
-// units it dequantized (same unit mapping, so program order makes the ring values final); a
-// value unit straddling nqd keeps its dequantized tokens below it.
-template <int VB>
-__device__ __forceinline__ void window_overwrite(_Float16* sk, _Float16* sv, int chunk, int nqd, int len, int W,
-                                                 const float* kring, const float* vring, int tid) {
+// FP32 window (progressive caches): tokens nqd .. len - 1 of the chunk take their original
+// values (in the code domain: the rings themselves, or their mapped copies) instead of the codes.
+// Each thread rewrites exactly the LDS units it dequantized (same unit mapping, so program order
+// makes the ring values final); a value unit straddling nqd keeps its dequantized tokens below
+// it.  A QJL key's scale f_t becomes 0: its signs carry no estimate for a window token.
+template <int KB, int VB>
+__device__ __forceinline__ void window_overwrite(_Float16* sk, _Float16* sv, uint32_t* sf, int chunk, int nqd,
+                                                 int len, int W, const float* kring, const float* vring, int tid) {
     if (W == 0 || 64 * chunk + 63 < nqd || 64 * chunk >= len) return;
 #pragma unroll
     for (int j = 0; j < kUnits; ++j) {
@@ -414,10 +481,14 @@ __device__ __forceinline__ void window_overwrite(_Float16* sk, _Float16* sv, int
         _Float16* dst = sk + key_lds_row(t) * kKS + 8 * w;
         *reinterpret_cast<h8*>(dst) = hi;
         *reinterpret_cast<h8*>(dst + 64 * kKS) = lo;
+        if constexpr (KB == kQjlK) {
+            if (w == 0) sf[key_lds_row(t)] = 0u;
+        }
     }
-    if constexpr (VB == 3) {
-        // 3-bit values were dequantized by TurboQuant value units: the thread rewrites its own
-        // two channel slots (channels 16 (4 hN + 2 par + qq) + n, tokens t0 .. t0 + 7)
+    if constexpr (VB == 3 || VB < 0) {
+        // 3-bit uniform, TurboQuant and split values were dequantized by TurboQuant value units:
+        // the thread rewrites its own two channel (split: position) slots, 16 (4 hN + 2 par + qq)
+        // + n, tokens t0 .. t0 + 7
         const TUnit U = turbo_unit(tid);
         const int tok0 = 64 * chunk + 32 * U.half + 8 * U.kb;
         if (tok0 + 7 >= nqd && tok0 < len) {
@@ -465,6 +536,56 @@ __device__ __forceinline__ void window_overwrite(_Float16* sk, _Float16* sv, int
     }
 }
 
+// FP32 window beside rotated or balanced codes: the window tokens' originals mapped into the
+// domain their tensor's codes live in, the one the scores and the value accumulator use (uniform
+// planes: R(x) when rotated, then .* 1/c when balanced; TurboQuant planes: R(x); a split V: the
+// two 64-point rotations of the permuted channels, position j holding channel perm[j]).  One
+// workgroup per (kv head, sequence), one wave per token at a time (lane l: channels or positions
+// 2l, 2l + 1); the copy keeps the ring layout, wring[b][kv head][tensor][t % 128][128].
+__global__ __launch_bounds__(256) void prefill_window_kernel(PrefillParams p) {
+    const int kvh = blockIdx.x, b = blockIdx.y, wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const PlaneGeom& KG = p.geom[0];
+    const PlaneGeom& VG = p.geom[1];
+    const char* slot = p.layer_base + (size_t)b * p.seq_stride + (size_t)kvh * p.head_stride;
+    const float* kring = reinterpret_cast<const float*>(slot + p.plane_off[0] + KG.ring_off);
+    const float* vring = reinterpret_cast<const float*>(slot + p.plane_off[1] + VG.ring_off);
+    float* kdst = p.wring + ((size_t)b * p.Hkv + kvh) * 2 * kWindowMax * kDim;
+    float* vdst = kdst + kWindowMax * kDim;
+    const size_t tk = (size_t)(kvh * 2 + 0) * kDim, tv = (size_t)(kvh * 2 + 1) * kDim;
+    const float2 ksg = reinterpret_cast<const float2*>(p.signs + tk)[l];
+    const float2 vsg = reinterpret_cast<const float2*>(p.signs + tv)[l];
+    const float2 kic = KG.sinkhorn ? reinterpret_cast<const float2*>(p.inv_c + tk)[l] : make_float2(1.0f, 1.0f);
+    const float2 vic = VG.sinkhorn ? reinterpret_cast<const float2*>(p.inv_c + tv)[l] : make_float2(1.0f, 1.0f);
+    const bool vsplit = VG.scheme == kTurboSplit;
+    const int2 pm = vsplit ? reinterpret_cast<const int2*>(p.perm + (size_t)kvh * kDim)[l] : make_int2(0, 0);
+    const int N = p.len[b];
+    for (int tok = max(0, N - kWindowMax) + wave; tok < N; tok += 4) { // wave-uniform: shuffles are safe
+        const size_t r = (size_t)(tok % kWindowMax) * kDim;
+        float2 k = reinterpret_cast<const float2*>(kring + r)[l];
+        float2 v = reinterpret_cast<const float2*>(vring + r)[l];
+        if (KG.rotate) qdev::rotate_signed(k.x, k.y, ksg.x, ksg.y);
+        if (KG.sinkhorn) {
+            k.x *= kic.x;
+            k.y *= kic.y;
+        }
+        if (vsplit) {
+            // channel pm.x sits in lane pm.x / 2, component pm.x % 2 (pm.y alike)
+            const float ax = __shfl(v.x, pm.x >> 1), ay = __shfl(v.y, pm.x >> 1);
+            const float bx = __shfl(v.x, pm.y >> 1), by = __shfl(v.y, pm.y >> 1);
+            v = make_float2((pm.x & 1) ? ay : ax, (pm.y & 1) ? by : bx);
+            qdev::rotate64_signed(v.x, v.y, vsg.x, vsg.y);
+        } else {
+            if (VG.rotate) qdev::rotate_signed(v.x, v.y, vsg.x, vsg.y);
+            if (VG.sinkhorn) {
+                v.x *= vic.x;
+                v.y *= vic.y;
+            }
+        }
+        reinterpret_cast<float2*>(kdst + r)[l] = k;
+        reinterpret_cast<float2*>(vdst + r)[l] = v;
+    }
+}
+
 // out row = R_V^-1(c_V .* x) for a row held as two channels per lane (2l, 2l + 1).
 __device__ __forceinline__ void store_out_row(float a, float c, const PlaneGeom& VG, float2 csv, float2 sgv,
                                               int2 pm, float* out_row, int l) {
@@ -509,9 +630,14 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 template <int KB, int VB>
 __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p) {
+    constexpr bool KQ = KB == kQjlK;
     __shared__ __align__(16) _Float16 s_lds[kLdsHalves];
     __shared__ __align__(16) _Float16 s_vm[2][2][4][kVmRow]; // [buffer][scale | zero][group][token]
     __shared__ float s_qf[kWaves][kWaveRows];          // 2^-e of each row's q' scaling
+    // QJL keys, per buffer: the sign words [key row][4] and the scale f_t per key row as fp16
+    // hi | lo << 16
+    __shared__ __align__(16) uint32_t s_sg[2][KQ ? 256 : 1];
+    __shared__ __align__(16) uint32_t s_f[2][KQ ? 64 : 1];
 
     const int S = p.n_splits;
     const int kvh = blockIdx.x % p.Hkv, rest = blockIdx.x / p.Hkv;
@@ -526,12 +652,24 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
     Planes P;
     P.kcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.codes_off);
     P.kmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.meta_off);
+    P.kqjl = reinterpret_cast<const uint8_t*>(slot + p.plane_off[0] + KG.qjl_off);
     P.vcodes = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.codes_off);
     P.vmeta = reinterpret_cast<const uint8_t*>(slot + p.plane_off[1] + VG.meta_off);
-    // FP32 window: the newest min(len, W) tokens are read from the rings
+    // FP32 window: the newest min(len, W) tokens are read from the rings, or beside rotated or
+    // balanced codes from their copies mapped into the code domain by prefill_window_kernel
     const int Wn = p.window, nqd = (Wn > 0) ? max(0, N - Wn) : N;
     const float* kring = reinterpret_cast<const float*>(slot + p.plane_off[0] + KG.ring_off);
     const float* vring = reinterpret_cast<const float*>(slot + p.plane_off[1] + VG.ring_off);
+    if (p.wring) {
+        kring = p.wring + ((size_t)b * p.Hkv + kvh) * 2 * kWindowMax * kDim;
+        vring = kring + kWindowMax * kDim;
+    }
+    // QJL keys: the upper half of the 3-bit codebook
+    float mgk[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (KQ) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mgk[j] = p.mu[4 + j];
+    }
     // TurboQuant-MSE V: the upper half of the codebook (the lower half is its mirror image)
     float mg[12] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (split_kind(VB)) {
@@ -553,6 +691,8 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
     // [64, 128)), then the B operands of the score product (column = row lr of the block,
     // k = channel 32 ks + 8 lq + i): hi = fp16(q'), lo = fp16(q' - hi)
     h8 Bh[4][kQB], Bl[4][kQB];
+    h8 Ph[KQ ? 4 : 1][kQB], Pl[KQ ? 4 : 1][kQB]; // QJL keys: p = S q' per row as fp16 hi + lo (the
+                                                 // operand layout of q')
     {
         const float2 sgn = reinterpret_cast<const float2*>(p.signs + (size_t)(kvh * 2 + 0) * kDim)[l];
         const float2 csk = reinterpret_cast<const float2*>(p.cs + (size_t)(kvh * 2 + 0) * kDim)[l];
@@ -608,6 +748,41 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
                     Bl[ks][qb][i] = (_Float16)(xs[i] - (float)h);
                 }
             }
+            if constexpr (KQ) {
+                // p_r = S q'_r for the wave's 16 rows (lane: projections 2l, 2l + 1; S^T rows from
+                // global memory, q' broadcast from LDS), then through LDS into the operand layout
+                float pa[16], pc[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pa[r] = pc[r] = 0.0f;
+                for (int j = 0; j < kDim; j += 4) {
+                    float2 s4[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        s4[jj] = reinterpret_cast<const float2*>(p.qjl_st + (size_t)(j + jj) * kDim)[l];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float4 x = *reinterpret_cast<const float4*>(s_rows + r * kDim + j);
+                        pa[r] = fmaf(s4[0].x, x.x, fmaf(s4[1].x, x.y, fmaf(s4[2].x, x.z, fmaf(s4[3].x, x.w, pa[r]))));
+                        pc[r] = fmaf(s4[0].y, x.x, fmaf(s4[1].y, x.y, fmaf(s4[2].y, x.z, fmaf(s4[3].y, x.w, pc[r]))));
+                    }
+                }
+                float* s_prows = reinterpret_cast<float*>(s_lds) + (kWaves + wave) * 16 * kDim;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) reinterpret_cast<float2*>(s_prows + r * kDim)[l] = make_float2(pa[r], pc[r]);
+                wave_lds_sync();
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const float4 x0 = *reinterpret_cast<const float4*>(s_prows + lr * kDim + 32 * ks + 8 * lq);
+                    const float4 x1 = *reinterpret_cast<const float4*>(s_prows + lr * kDim + 32 * ks + 8 * lq + 4);
+                    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const _Float16 h = (_Float16)xs[i];
+                        Ph[ks][qb][i] = h;
+                        Pl[ks][qb][i] = (_Float16)(xs[i] - (float)h);
+                    }
+                }
+            }
             wave_lds_sync();
         }
     }
@@ -648,8 +823,8 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
         load_codes<KB, VB>(P, c0, tid, R);
         if (c0 + 1 < c1) load_vmeta<VB>(P, c0 + 1, tid, R);
         __syncthreads();
-        dequant_chunk<KB, VB>(s_lds, s_lds + 2 * kKBuf, s_vm[0], tid, R, mg);
-        window_overwrite<VB>(s_lds, s_lds + 2 * kKBuf, c0, nqd, N, Wn, kring, vring, tid);
+        dequant_chunk<KB, VB>(s_lds, s_lds + 2 * kKBuf, s_vm[0], tid, R, mg, mgk, s_sg[0], s_f[0]);
+        window_overwrite<KB, VB>(s_lds, s_lds + 2 * kKBuf, s_f[0], c0, nqd, N, Wn, kring, vring, tid);
         if (c0 + 1 < c1) store_vmeta<VB>(s_vm[1], tid, R);
         if (late && c0 + 1 < c1) load_codes<KB, VB>(P, c0 + 1, tid, R);
         __syncthreads();
@@ -663,9 +838,9 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
         auto dequant_next = [&]() {
             if (more) {
                 dequant_chunk<KB, VB>(s_lds + (buf ^ 1) * kKBuf, s_lds + 2 * kKBuf + (buf ^ 1) * kVBuf,
-                                      s_vm[buf ^ 1], tid, R, mg);
-                window_overwrite<VB>(s_lds + (buf ^ 1) * kKBuf, s_lds + 2 * kKBuf + (buf ^ 1) * kVBuf, ci + 1,
-                                     nqd, N, Wn, kring, vring, tid);
+                                      s_vm[buf ^ 1], tid, R, mg, mgk, s_sg[buf ^ 1], s_f[buf ^ 1]);
+                window_overwrite<KB, VB>(s_lds + (buf ^ 1) * kKBuf, s_lds + 2 * kKBuf + (buf ^ 1) * kVBuf,
+                                         s_f[buf ^ 1], ci + 1, nqd, N, Wn, kring, vring, tid);
                 if (ci + 2 < c1) store_vmeta<VB>(s_vm[buf], tid, R);
             }
         };
@@ -678,6 +853,8 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
         }
         const _Float16* sk = s_lds + buf * kKBuf;
         const _Float16* sv = s_lds + 2 * kKBuf + buf * kVBuf;
+        const uint32_t* sg = s_sg[buf];
+        const uint32_t* sfb = s_f[buf];
         const bool masked = 64 * ci + 63 > (int)pos_min;
         // ---- S^T for the chunk's four 16-token tiles (tile b, row 4 lq + v = token
         // 32 (b / 2) + 8 lq + 4 (b % 2) + v); three accumulators per tile (K_hi q_hi, K_hi q_lo,
@@ -698,7 +875,30 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
                 for (int qb = 0; qb < kQB; ++qb) {
                     Sa[b][qb] = mfma16(Ah, Bh[ks][qb], Sa[b][qb]);
                     Sb[b][qb] = mfma16(Ah, Bl[ks][qb], Sb[b][qb]);
-                    Sd[b][qb] = mfma16(Al, Bh[ks][qb], Sd[b][qb]);
+                    // QJL keys keep two chains per tile (registers: S q' is one more operand set)
+                    if constexpr (KQ) Sb[b][qb] = mfma16(Al, Bh[ks][qb], Sb[b][qb]);
+                    else Sd[b][qb] = mfma16(Al, Bh[ks][qb], Sd[b][qb]);
+                }
+                if constexpr (KQ) {
+                    // QJL: A = +-f_t (hi, then lo) of the row's eight signs of this slice
+                    // (projections 32 ks + 8 lq + i at bits 16 (i % 2) + 4 lq + i / 2 of word ks; a
+                    // clear bit is -1: the sign bit of f flipped)
+                    const uint32_t nw = ~sg[4 * (16 * b + lr) + ks] >> (4 * lq);
+                    const uint32_t fw = sfb[16 * b + lr];
+                    const uint32_t fh = (fw & 0xffffu) * 0x00010001u, fl = (fw >> 16) * 0x00010001u;
+                    u4 a2h, a2l;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t m = ((nw >> k) & 0x00010001u) << 15;
+                        a2h[k] = m ^ fh;
+                        a2l[k] = m ^ fl;
+                    }
+#pragma unroll
+                    for (int qb = 0; qb < kQB; ++qb) {
+                        Sa[b][qb] = mfma16(__builtin_bit_cast(h8, a2h), Ph[ks][qb], Sa[b][qb]);
+                        Sb[b][qb] = mfma16(__builtin_bit_cast(h8, a2h), Pl[ks][qb], Sb[b][qb]);
+                        Sa[b][qb] = mfma16(__builtin_bit_cast(h8, a2l), Ph[ks][qb], Sa[b][qb]);
+                    }
                 }
             }
         }
@@ -735,9 +935,12 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
             float sum = 0.0f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
+                // the sum takes the fp16 weights the PV product uses: the output stays a convex
+                // combination of the values (exactly so when one weight dominates)
                 const float pv = (m == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(fmaf(raw[i], F[qb], -m));
-                sum += pv;
-                Pb[i >> 3][qb][i & 7] = (_Float16)pv;
+                const _Float16 ph = (_Float16)pv;
+                sum += (float)ph;
+                Pb[i >> 3][qb][i & 7] = ph;
             }
             l_run[qb] = fmaf(l_run[qb], al[qb], sum);
         }
@@ -870,11 +1073,10 @@ bool prefill_attn_supported(const PrefillParams& p) {
     const PlaneGeom& K = p.geom[0];
     const PlaneGeom& V = p.geom[1];
     auto ok = [](const PlaneGeom& g) { return g.scheme == kUniform && (g.bits == 3 || g.bits == 4 || g.bits == 8); };
+    const bool k_qjl = K.scheme == kTurboQjl && K.bits == 3;
     const bool v_turbo = (V.scheme == kTurboMse || V.scheme == kTurboSplit) && (V.bits == 3 || V.bits == 4);
-    // an FP32 window is read in the plain domain: no rotation or balancing on either tensor
-    const bool plain = !K.rotate && !K.sinkhorn && !V.rotate && !V.sinkhorn;
-    const bool win_ok = p.window == 0 || (p.window == kWindowMax && plain && ok(V));
-    return ok(K) && (ok(V) || v_turbo) && win_ok && p.G >= 1 && p.G <= kMaxGroupHeads;
+    const bool win_ok = p.window == 0 || p.window == kWindowMax;
+    return (ok(K) || k_qjl) && (ok(V) || v_turbo) && win_ok && p.G >= 1 && p.G <= kMaxGroupHeads;
 }
 
 template <int KB>
@@ -888,7 +1090,13 @@ hipError_t launch_k(const PrefillParams& p, hipStream_t s) {
 }
 
 hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
+    if (p.wring) {
+        hipLaunchKernelGGL(prefill_window_kernel, dim3(p.Hkv, p.batch), dim3(256), 0, s, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int kb = p.geom[0].bits;
+    if (p.geom[0].scheme == kTurboQjl) return launch_k<kQjlK>(p, s);
     if (kb == 3) return launch_k<3>(p, s);
     return kb == 4 ? launch_k<4>(p, s) : launch_k<8>(p, s);
 }

@@ -159,20 +159,82 @@ def test_prefill_attention_last_token_equals_decode():
 
 def test_prefill_attention_refusals():
     import quantized_decode_attention_kvq_amd as K
-    # an FP32 window beside rotated codes and TurboQuant-QJL keys are not read by this kernel;
-    # n_q beyond a length
-    for wl, n, nq, name in ((W.LLAMA3B_3970_PROGRESSIVE.with_(rotate_k=True), 200, 10, "KVQ_ERR_UNSUPPORTED"),
-                            (W.LLAMA3B_32K_TURBO, 200, 10, "KVQ_ERR_UNSUPPORTED"),
-                            (W.LLAMA3B_32K_KVARN, 200, 201, "KVQ_ERR_INVALID_ARG")):
+    # n_q beyond a length; a caller workspace smaller than the window copy that a progressive
+    # cache beside rotated and balanced codes needs (nothing is written in either case)
+    for wl, n, nq, ws, name in ((W.LLAMA3B_32K_KVARN, 200, 201, None, "KVQ_ERR_INVALID_ARG"),
+                                (W.LLAMA3B_32K_KVARN.with_(window=128), 200, 10, 16, "KVQ_ERR_BUFFER_TOO_SMALL")):
         case = Case(wl, n, layers=[0], batch=1)
         case.prefill(0)
         q = torch.zeros((1, nq, wl.n_q_heads, 128), device="cuda")
         out = torch.full((1, nq, wl.n_q_heads, 128), 5.0, device="cuda")
+        wst = None if ws is None else torch.empty(ws, dtype=torch.uint8, device="cuda")
         with pytest.raises(K.KvqError) as e:
-            case.cache.attn_prefill(0, q, out)
+            case.cache.attn_prefill(0, q, out, workspace=wst)
         assert e.value.name == name
         torch.cuda.synchronize()
         assert bool((out == 5.0).all())
+
+
+QJL = W.LLAMA3B_32K_TURBO
+
+
+@pytest.mark.parametrize("wl", [QJL, QJL.with_(name="llama3b-turboqjl-k-u8-v", v_bits=8),
+                                QJL.with_(name="llama3b-turboqjl-k-u3-v", v_bits=3),
+                                QJL.with_(name="llama3b-turboqjl-k-turbomse-v", v_scheme=W.TURBO_MSE, v_bits=3,
+                                          rotate_v=True),
+                                QJL.with_(name="llama3b-turboqjl-k-turbo4mse-v", v_scheme=W.TURBO_MSE, v_bits=4,
+                                          rotate_v=True),
+                                W.LLAMA8B_32K_Q8_0_TURBO25_V.with_(name="llama8b-turboqjl-k-turbo2.5split-v",
+                                                                   k_scheme=W.TURBO_QJL, k_bits=3)],
+                         ids=lambda w: w.name)
+def test_prefill_attention_turbo_qjl_keys(wl):
+    # TurboQuant-QJL keys (3-bit Lloyd-Max codes + 1-bit QJL of the residual): the score is the
+    # oracle's n <R q, mu[code]> + gamma sqrt(pi/2) / 128 sum_i sign_i (S R q)_i, beside every
+    # value kind (uniform 4 / 8 / 3 bits, TurboQuant-MSE 3 / 4 bits, the 2.5-bit split)
+    _say("case: prefill attention,", wl.name)
+    _run(wl, n0=300, B=2, nb=1, ne=37, n_q=90, seed=12)
+
+
+def test_prefill_attention_turbo_qjl_keys_splits():
+    _say("case: prefill attention,", QJL.name, "3000 tokens, key splits")
+    case, _, _ = _run(QJL, n0=3000, B=1, nb=0, ne=0, n_q=64, seed=13)
+    assert case.cache.attn_prefill_workspace(0, 64, 1) > 0
+
+
+PROG = 128  # the quantcpp progressive window
+
+
+@pytest.mark.parametrize("wl", [
+    W.LLAMA3B_32K_KVARN.with_(name="llama3b-wht-sinkhorn-u4-progressive", window=PROG),
+    W.LLAMA3B_3970_PROGRESSIVE.with_(name="llama3b-wht-k-u4-progressive", rotate_k=True),
+    QJL.with_(name="llama3b-turboqjl-k-u4-v-progressive", window=PROG),
+    W.LLAMA3B_32K_Q8_0_TURBO_V.with_(name="llama3b-q8_0-k-turbomse-v-progressive", window=PROG),
+    W.LLAMA3B_32K_Q8_0_TURBO4_V.with_(name="llama3b-q8_0-k-turbo4mse-v-progressive", window=PROG),
+    W.LLAMA8B_32K_Q8_0_TURBO35_V.with_(name="llama8b-q8_0-k-turbo3.5split-v-progressive", window=PROG),
+    W.LLAMA3B_32K_KVARN_U3.with_(name="llama3b-wht-sinkhorn-u3-progressive", window=PROG),
+    QJL.with_(name="llama3b-turboqjl-k-turbomse-v-progressive", v_scheme=W.TURBO_MSE, v_bits=3, rotate_v=True,
+              window=PROG),
+    W.DENSE27B_120K_KVARN.with_(name="dense27b-wht-sinkhorn-u4-progressive", window=PROG)],
+    ids=lambda w: w.name)
+def test_prefill_attention_window_in_code_domain(wl):
+    # an FP32 window beside rotated, balanced or TurboQuant codes: the window tokens' originals
+    # are mapped into their codes' domain (R(x) ./ c, R(x), the split's permuted 64-point
+    # rotations) and meet the oracle, which reads them as they are; queries on both sides of the
+    # window start, a ragged batch with different window starts
+    _say("case: prefill attention, window in the code domain,", wl.name)
+    _run(wl, n0=500, B=2, nb=1, ne=37, n_q=150, seed=14)
+
+
+@pytest.mark.parametrize("n0,nb,ne,n_q,ws", [(90, 0, 0, 40, "auto"), (64, 1, 100, 60, None),
+                                              (3000, 0, 0, 64, "auto"), (3000, 0, 0, 64, None)],
+                         ids=["inside-window", "ragged-cache-workspace", "key-splits", "key-splits-cache-workspace"])
+def test_prefill_attention_window_in_code_domain_edges(n0, nb, ne, n_q, ws):
+    # whole caches inside the window, a ragged batch on the cache's own workspace (window copy
+    # ahead of the partials there), and long caches whose keys are split over workgroups
+    wl = W.LLAMA3B_32K_KVARN.with_(name="llama3b-wht-sinkhorn-u4-progressive", window=PROG)
+    _say("case: prefill attention, KVarN progressive, n0", n0, "n_q", n_q, "workspace", ws)
+    case, _, _ = _run(wl, n0=n0, B=2 if nb else 1, nb=nb, ne=ne, n_q=n_q, seed=15, workspace=ws)
+    assert case.cache.attn_prefill_workspace(0, n_q, 1) >= 8 * 2 * 128 * 128 * 4
 
 
 @pytest.mark.parametrize("wl", [W.LLAMA3B_32K_U8_K_U3_V, W.LLAMA3B_32K_KVARN_U3,
