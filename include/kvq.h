@@ -52,7 +52,9 @@ typedef enum {
 /* Bytes of the library-held device scratch that kvq_attn_decode_static uses (one per GPU). */
 #define KVQ_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
 
-typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
+/* Element type of the inputs (K, V, q, calibration blocks).  16-bit inputs are widened to fp32
+ * exactly on load; every computation is the same as for fp32 inputs of those values. */
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1, KVQ_F16 = 2 } kvq_dtype;
 
 typedef enum {
     KVQ_UNIFORM = 0,   /* b-bit asymmetric groups of 32, fp16 scale + fp16 zero [P1], b = 3|4|8 */

@@ -12,7 +12,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq.so")
 
-KVQ_F32, KVQ_BF16 = 0, 1
+KVQ_F32, KVQ_BF16, KVQ_F16 = 0, 1, 2
 KVQ_UNIFORM, KVQ_TURBO_QJL, KVQ_TURBO_MSE, KVQ_Q8_0, KVQ_TURBO_SPLIT = 0, 1, 2, 3, 4
 KVQ_OPT_SPLIT_TOKENS, KVQ_OPT_DECODE_PATH = 1, 2
 STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_INVALID_ARG", 2: "KVQ_ERR_UNSUPPORTED", 3: "KVQ_ERR_CAPACITY",
@@ -120,6 +120,8 @@ def _dtype(t):
         return KVQ_F32
     if t.dtype == torch.bfloat16:
         return KVQ_BF16
+    if t.dtype == torch.float16:
+        return KVQ_F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -163,7 +165,7 @@ def _resident(**named):
 
 def _inputs():
     import torch
-    return (torch.float32, torch.bfloat16)
+    return (torch.float32, torch.bfloat16, torch.float16)
 
 
 def _same_dtype(*ts):

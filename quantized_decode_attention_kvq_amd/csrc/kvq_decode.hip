@@ -27,7 +27,6 @@ constexpr float kNegInf = -__builtin_huge_valf();
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ float c0f() { return __uint_as_float(0x3DB504F3u); }
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
-__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ float wave_max(float v) {
     return xor_reduce<64>(v, [](float x, float y) { return fmaxf(x, y); });
@@ -67,8 +66,8 @@ __device__ __forceinline__ void load_q_pair(const DecodeParams& p, int b, int hq
         c = v.y;
     } else {
         const uint32_t v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.q) + off)[l];
-        a = bf2f((uint16_t)(v & 0xffff));
-        c = bf2f((uint16_t)(v >> 16));
+        a = in16_to_f32(v & 0xffff, p.dtype);
+        c = in16_to_f32(v >> 16, p.dtype);
     }
 }
 

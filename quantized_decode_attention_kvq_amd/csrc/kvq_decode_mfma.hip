@@ -314,8 +314,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                 qc[i] = v.y;
             } else {
                 const uint32_t v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.q) + off)[l];
-                qa[i] = bf2f((uint16_t)(v & 0xffff));
-                qc[i] = bf2f((uint16_t)(v >> 16));
+                qa[i] = in16_to_f32(v & 0xffff, p.dtype);
+                qc[i] = in16_to_f32(v >> 16, p.dtype);
             }
         }
     }

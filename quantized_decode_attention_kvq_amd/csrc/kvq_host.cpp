@@ -318,7 +318,7 @@ kvq_status kvq_calibrate(kvq_cache* c, int layer, const void* Kc, const void* Vc
                          int n_tokens, void* stream) {
     if (!c) return KVQ_ERR_INVALID_ARG;
     if (layer < 0 || layer >= c->cfg.n_layers) return KVQ_ERR_INVALID_ARG;
-    if (dtype != KVQ_F32 && dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
+    if (dtype != KVQ_F32 && dtype != KVQ_BF16 && dtype != KVQ_F16) return KVQ_ERR_INVALID_ARG;
     if (!c->needs_calib()) return KVQ_ERR_INVALID_ARG;
     if (n_tokens < 2 || n_tokens > c->cfg.calib_tokens) return KVQ_ERR_INVALID_ARG;
     CalibParams p{};
@@ -365,7 +365,7 @@ kvq_status make_quant(kvq_cache* c, int layer, const void* K, const void* V, int
     if (!c) return KVQ_ERR_INVALID_ARG;
     if (layer < 0 || layer >= c->cfg.n_layers) return KVQ_ERR_INVALID_ARG;
     if (batch < 1 || batch > c->cfg.max_batch || n_tokens < 0) return KVQ_ERR_INVALID_ARG;
-    if (dtype != KVQ_F32 && dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
+    if (dtype != KVQ_F32 && dtype != KVQ_BF16 && dtype != KVQ_F16) return KVQ_ERR_INVALID_ARG;
     if (!K || !V) return KVQ_ERR_INVALID_ARG;
     if (!aligned16(K) || !aligned16(V)) return KVQ_ERR_MISALIGNED;
     const int* len = &c->len[(size_t)layer * c->cfg.max_batch];
@@ -410,7 +410,7 @@ kvq_status check_decode(const kvq_cache* c, int layer, const void* q, int dtype,
     if (!c) return KVQ_ERR_INVALID_ARG;
     if (layer < 0 || layer >= c->cfg.n_layers) return KVQ_ERR_INVALID_ARG;
     if (batch < 1 || batch > c->cfg.max_batch) return KVQ_ERR_INVALID_ARG;
-    if (dtype != KVQ_F32 && dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
+    if (dtype != KVQ_F32 && dtype != KVQ_BF16 && dtype != KVQ_F16) return KVQ_ERR_INVALID_ARG;
     if (!q || !out) return KVQ_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_MISALIGNED;
     if (!std::isfinite(softmax_scale)) return KVQ_ERR_INVALID_ARG;

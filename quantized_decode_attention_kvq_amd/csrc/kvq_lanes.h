@@ -8,6 +8,12 @@
 
 namespace kvq {
 
+// A 16-bit input element as fp32, exactly: bf16 (dtype 1) by widening its bits, fp16 (dtype 2) by
+// conversion.
+__device__ __forceinline__ float in16_to_f32(uint32_t b16, int dtype) {
+    return dtype == 2 ? (float)__builtin_bit_cast(_Float16, (uint16_t)b16) : __uint_as_float(b16 << 16);
+}
+
 template <int M>
 __device__ __forceinline__ int xor_lane_i(int x) {
     static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "xor distance");

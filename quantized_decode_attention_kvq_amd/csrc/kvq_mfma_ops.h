@@ -26,7 +26,6 @@ __device__ __forceinline__ h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
 __device__ __forceinline__ float c0f() { return __uint_as_float(0x3DB504F3u); }
 __device__ __forceinline__ float lo_h(uint32_t w) { return (float)__builtin_bit_cast(h2v, w)[0]; }
 __device__ __forceinline__ float hi_h(uint32_t w) { return (float)__builtin_bit_cast(h2v, w)[1]; }
-__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // 4-bit word (channel/token i at bit 16*(i%2) + 4*(i/2)) -> 8 fp16 subnormal operands in
 // natural order, slots 2,3,6,7 carry an extra factor 16.

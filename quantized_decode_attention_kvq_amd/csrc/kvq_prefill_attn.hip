@@ -710,8 +710,8 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
                         c = v.y;
                     } else {
                         const uint32_t v = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.q) + off)[l];
-                        a = bf2f((uint16_t)(v & 0xffff));
-                        c = bf2f((uint16_t)(v >> 16));
+                        a = in16_to_f32(v & 0xffff, p.dtype);
+                        c = in16_to_f32(v >> 16, p.dtype);
                     }
                 }
                 if (KG.rotate) {

@@ -26,7 +26,6 @@ namespace {
 using qdev::lane_id;
 using qdev::f16_rn;
 using qdev::f16_val;
-using qdev::bf16_to_f32;
 using qdev::rotate_wave;
 using qdev::c0f;
 
@@ -223,7 +222,7 @@ __global__ __launch_bounds__(64) void calib_init_kernel(CalibParams p) {
 #pragma unroll
     for (int j = 0; j < kDim; ++j) {
         float v = (p.dtype == 0) ? static_cast<const float*>(p.src[tensor])[off + j]
-                                 : bf16_to_f32(static_cast<const uint16_t*>(p.src[tensor])[off + j]);
+                                 : in16_to_f32(static_cast<const uint16_t*>(p.src[tensor])[off + j], p.dtype);
         if (p.rotate[tensor] && signs[j] < 0.0f) v = -v;
         y[j] = v;
     }
@@ -377,7 +376,7 @@ __global__ __launch_bounds__(128) void select_outliers_kernel(OutlierParams p) {
     for (int t = 0; t < p.n; ++t) {
         const size_t i = ((size_t)t * p.Hkv + head) * kDim + d;
         const double v = p.dtype == 0 ? (double)static_cast<const float*>(p.src)[i]
-                                      : (double)qdev::bf16_to_f32(static_cast<const uint16_t*>(p.src)[i]);
+                                      : (double)in16_to_f32(static_cast<const uint16_t*>(p.src)[i], p.dtype);
         acc = acc + v * v;
     }
     s_e[d] = acc;

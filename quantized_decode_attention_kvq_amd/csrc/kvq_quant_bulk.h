@@ -23,7 +23,6 @@
 namespace kvq {
 namespace qbulk {
 
-using qdev::bf16_to_f32;
 using qdev::c0f;
 using qdev::f16_rd;
 using qdev::f16_rn;
@@ -90,8 +89,8 @@ __device__ __forceinline__ void load_octet(const WavePlane& w, int g, OctetIn& i
                 const uint32_t x[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    in.v[r][2 * i] = bf16_to_f32((uint16_t)(x[i] & 0xffff));
-                    in.v[r][2 * i + 1] = bf16_to_f32((uint16_t)(x[i] >> 16));
+                    in.v[r][2 * i] = in16_to_f32(x[i] & 0xffff, w.dtype);
+                    in.v[r][2 * i + 1] = in16_to_f32(x[i] >> 16, w.dtype);
                 }
             }
         }
@@ -706,7 +705,7 @@ __device__ __forceinline__ void load_split(const WavePlane& w, int g, const int*
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             if (w.dtype == 0) in.v[i] = reinterpret_cast<const float*>(row)[pm[i]];
-            else in.v[i] = bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[pm[i]]);
+            else in.v[i] = in16_to_f32(reinterpret_cast<const uint16_t*>(row)[pm[i]], w.dtype);
         }
     }
 }

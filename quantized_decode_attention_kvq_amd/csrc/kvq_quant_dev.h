@@ -43,7 +43,6 @@ __device__ __forceinline__ uint16_t f16_rd(float x) {
     return h;
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // Lane l loads channels 2l and 2l+1 of one 128-vector.
 __device__ __forceinline__ void load_pair(const void* base, size_t elem_off, int dtype, float& a,
@@ -57,8 +56,8 @@ __device__ __forceinline__ void load_pair(const void* base, size_t elem_off, int
     } else {
         const uint32_t v = reinterpret_cast<const uint32_t*>(
             static_cast<const uint16_t*>(base) + elem_off)[l];
-        a = bf16_to_f32((uint16_t)(v & 0xffff));
-        b = bf16_to_f32((uint16_t)(v >> 16));
+        a = in16_to_f32(v & 0xffff, dtype);
+        b = in16_to_f32(v >> 16, dtype);
     }
 }
 

@@ -152,3 +152,27 @@ def test_binding_refuses_bad_tensors_before_c():
             K.kvq_attn_decode(ctypes.c_void_p(0x6000), 0, q, out)
     finally:
         K._SHAPES.pop(h.value)
+
+
+def test_f16_inputs_are_kvq_f16():
+    # KVQ_F16 = 2 in the header and the binding; fp16 tensors pass the dtype rules (the fake
+    # handle's call then stops at the residency check), fp64 does not
+    import torch
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    assert re.search(r"KVQ_F16\s*=\s*2", text)
+    assert K.KVQ_F16 == 2 and K._dtype(torch.zeros(1, dtype=torch.float16)) == 2
+    with pytest.raises(TypeError, match="unsupported dtype"):
+        K._dtype(torch.zeros(1, dtype=torch.float64))
+    h = ctypes.c_void_p(0x5100)
+    K._SHAPES[h.value] = {"n_layers": 2, "n_q_heads": 24, "n_kv_heads": 8, "max_batch": 2}
+    try:
+        q16, out = torch.zeros(1, 24, 128, dtype=torch.float16), torch.zeros(1, 24, 128)
+        with pytest.raises(TypeError, match="device"):
+            K.kvq_attn_decode(h, 0, q16, out)
+        k16 = torch.zeros(1, 8, 128, dtype=torch.float16)
+        with pytest.raises(TypeError, match="device"):
+            K.kvq_append_attn_decode(h, 0, k16, k16, q16, out)
+        with pytest.raises(TypeError, match="one dtype"):
+            K.kvq_append_attn_decode(h, 0, k16, k16, q16.float(), out)
+    finally:
+        K._SHAPES.pop(h.value)

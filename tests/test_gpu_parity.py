@@ -641,3 +641,39 @@ def test_uniform3_planes_and_decode(wl):
         _say(f"  fused step seq {b}: rel_l2={r:.2e} max_abs={m:.2e}")
         assert r <= REL_L2_TOL and m <= MAX_ABS_TOL, (b, r, m)
     _decode_and_compare(case, 0, planes)  # both decode paths
+
+
+F16_CASES = [
+    W.LLAMA3B_32K_KVARN.with_(name="llama3b-wht-sinkhorn-u4-f16", dtype="f16"),
+    W.LLAMA3B_32K_TURBO.with_(name="llama3b-turboqjl-k-u4-v-f16", dtype="f16"),
+    W.LLAMA8B_32K_Q8_0_TURBO25_V.with_(name="llama8b-q8_0-k-turbo2.5split-v-f16", dtype="f16"),
+    W.LLAMA3B_3970_PROGRESSIVE.with_(name="llama3b-u4-progressive-f16", dtype="f16"),
+    W.DENSE27B_120K_KVARN.with_(name="dense27b-wht-sinkhorn-u4-f16", dtype="f16"),
+]
+
+
+@pytest.mark.parametrize("wl", F16_CASES, ids=lambda w: w.name)
+def test_f16_inputs_planes_and_decode(wl):
+    # KVQ_F16 inputs (K, V, q and the calibration block rounded to fp16): the library widens them
+    # exactly, so planes, tables and attention meet the oracle fed the same values in fp32 --
+    # bulk prefill, per-token appends, a fused step and both decode paths
+    _say("case:", wl.name, "2 seqs, 300 prefill + 20 appends + 1 fused step")
+    case = Case(wl, 321, layers=[0], batch=2)
+    k, v = case.kv(0)
+    assert k.dtype == torch.float16
+    case.cache.prefill_quantize(0, k[:, :300].contiguous(), v[:, :300].contiguous())
+    for t in range(300, 320):
+        case.cache.append(0, k[:, t].contiguous(), v[:, t].contiguous())
+    q = W.gen_q(wl, 0, 5, batch=2).to("cuda")
+    out = torch.full((2, wl.n_q_heads, 128), float("nan"), device="cuda")
+    case.cache.append_attn_decode(0, k[:, 320].contiguous(), v[:, 320].contiguous(), q, out)
+    torch.cuda.synchronize()
+    planes = _check_all_planes(case, 0)
+    qn = q.float().cpu().numpy()
+    for b in (0, 1):
+        pl = {h: planes[(b, h)] for h in range(wl.n_kv_heads)}
+        ref = oracle_attention_case(case, 0, b, qn[b], planes=pl)
+        r, m = rel_l2(out.cpu().numpy()[b], ref), max_abs(out.cpu().numpy()[b], ref)
+        _say(f"  fused step seq {b}: rel_l2={r:.2e} max_abs={m:.2e}")
+        assert r <= REL_L2_TOL and m <= MAX_ABS_TOL, (b, r, m)
+    _decode_and_compare(case, 0, planes)

@@ -256,3 +256,12 @@ def test_prefill_attention_uniform3_window_and_key_splits():
     _run(wl, n0=500, B=2, nb=1, ne=37, n_q=150, seed=10)
     case, _, _ = _run(W.LLAMA3B_32K_KVARN_U3, n0=3000, B=1, nb=0, ne=0, n_q=64, seed=11)
     assert case.cache.attn_prefill_workspace(0, 64, 1) > 0
+
+
+@pytest.mark.parametrize("wl", [W.LLAMA3B_32K_KVARN.with_(name="llama3b-wht-sinkhorn-u4-f16", dtype="f16"),
+                                QJL.with_(name="llama3b-turboqjl-k-u4-v-progressive-f16", dtype="f16", window=PROG)],
+                         ids=lambda w: w.name)
+def test_prefill_attention_f16_inputs(wl):
+    # KVQ_F16 queries (and cache sources): widened exactly on load
+    _say("case: prefill attention,", wl.name)
+    _run(wl, n0=300, B=2, nb=1, ne=37, n_q=90, seed=16)

@@ -45,7 +45,7 @@ class Workload:
     rotate_v: bool
     sinkhorn_iters: int
     calib_tokens: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16" (values rounded to the 16-bit type, RN)
     data: str  # value recipe, see gen_kv
     seed: int
 
@@ -141,7 +141,7 @@ def _gen(device, seed):
 
 
 def _dtype(wl):
-    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    return {"bf16": torch.bfloat16, "f16": torch.float16}.get(wl.dtype, torch.float32)
 
 
 # ----------------------------------------------------------------------------------------------
