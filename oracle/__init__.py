@@ -93,6 +93,11 @@ def lib():
         L.orc_tree_sum_sq64.argtypes = [_F]
         L.orc_select_outliers.argtypes = [_F, ctypes.c_int, _I32]
         L.orc_split_encode.argtypes = [_F, ctypes.POINTER(Tables), ctypes.c_int, _U8, _U16]
+        L.orc_split_qjl_encode.argtypes = [_F, ctypes.POINTER(Tables), ctypes.c_int, _U8, _U16, _U16, _U8]
+        L.orc_split_rotate_f64.argtypes = [_Dp, ctypes.POINTER(Tables), _Dp]
+        L.orc_split_score.restype = ctypes.c_double
+        L.orc_split_score.argtypes = [ctypes.POINTER(PlaneCfg), ctypes.POINTER(Tables), _U8, _U8, _U8,
+                                      ctypes.c_int, _Dp, _Dp]
         for f in ("orc_codes_bytes", "orc_meta_bytes", "orc_qjl_bytes", "orc_ring_floats"):
             getattr(L, f).restype = ctypes.c_size_t
             getattr(L, f).argtypes = [ctypes.POINTER(PlaneCfg)]
@@ -242,6 +247,35 @@ def split_encode(x, tables: "TableSet", bits_o):
     n16 = np.zeros(2, np.uint16)
     lib().orc_split_encode(_p(x, _F), tables.ref, int(bits_o), _p(codes, _U8), _p(n16, _U16))
     return codes, (int(n16[0]), int(n16[1]))
+
+
+def split_qjl_encode(x, tables: "TableSet", b):
+    """Split key code at b = 3 / 4: codes by position, (n_outlier, n_rest), gamma (fp16 bits) and
+    the 128 QJL bits of the residual."""
+    x = _f32(x)
+    codes = np.empty(D, np.uint8)
+    n16 = np.zeros(2, np.uint16)
+    g16 = np.zeros(1, np.uint16)
+    bits = np.zeros(D, np.uint8)
+    lib().orc_split_qjl_encode(_p(x, _F), tables.ref, int(b), _p(codes, _U8), _p(n16, _U16),
+                               _p(g16, _U16), _p(bits, _U8))
+    return dict(codes=codes, n16=(int(n16[0]), int(n16[1])), g16=int(g16[0]), bits=bits)
+
+
+def split_rotate_f64(q, tables: "TableSet"):
+    """The split domain of q in binary64 (position 64h + j = R64(q[perm[64h + .]])_j)."""
+    q = np.ascontiguousarray(q, np.float64)
+    y = np.empty(D, np.float64)
+    lib().orc_split_rotate_f64(_p(q, _Dp), tables.ref, _p(y, _Dp))
+    return y
+
+
+def split_score(plane: "Plane", tables: "TableSet", t, rho_q, s_rho_q):
+    """Split-key score estimate of token t of a split K plane (unscaled, fp64)."""
+    rq = np.ascontiguousarray(rho_q, np.float64)
+    sq = np.ascontiguousarray(s_rho_q, np.float64)
+    return float(lib().orc_split_score(plane.ref, tables.ref, _p(plane.codes, _U8), _p(plane.meta, _U8),
+                                       _p(plane.qjl, _U8), int(t), _p(rq, _Dp), _p(sq, _Dp)))
 
 
 LLOYD_ITERS = 2000  # fixed iteration count of the codebook (same count on the device side)

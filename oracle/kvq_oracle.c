@@ -294,7 +294,7 @@ static double mass(double a, double b)
 /* Lloyd's two conditions, iterated on the positive half line (the density is even, so the
  * optimal quantizer with an even number of levels is odd-symmetric with a threshold at 0):
  * thresholds are midpoints of neighbouring centroids, centroids are conditional means
- * (phi(a) - phi(b)) / mass(a, b).  `levels` = 4, 8 or 16 (2-, 3-, 4-bit codes); the start is
+ * (phi(a) - phi(b)) / mass(a, b).  `levels` = 2, 4, 8 or 16 (1- to 4-bit codes); the start is
  * the evenly spaced half line 2 (k + 1) / (levels / 2), k = 0 .. levels/2 - 1.  A coordinate of a
  * random rotation of a unit vector in `dim` dimensions is close to N(0, 1/dim), so the stored
  * centroids and thresholds are the N(0,1) ones divided by sqrt(dim). */
@@ -490,8 +490,10 @@ void orc_select_outliers(const float* X, int n, int* perm)
 
 /* Each subset h (positions 64h .. 64h+63, channels perm[.]): rho = R64(x_h) with signs
  * 64h .. 64h+63 of the tensor's sign vector; n_h = fp16(|rho|); code = number of thresholds of
- * the subset's codebook below rho / n_h (outliers: bits_o bits, the rest bits_o - 1). */
-void orc_split_encode(const float* x, const orc_tables* tb, int bits_o, uint8_t* codes, uint16_t* n16)
+ * the subset's codebook below rho / n_h (outliers: bits_o bits, the rest bits_o - 1).  rho (in
+ * position order) goes to rho_out when that is not NULL. */
+static void split_halves(const float* x, const orc_tables* tb, int bits_o, uint8_t* codes, uint16_t* n16,
+                         float* rho_out)
 {
     for (int h = 0; h < 2; h++) {
         float z[64], rho[64];
@@ -510,6 +512,57 @@ void orc_split_encode(const float* x, const orc_tables* tb, int bits_o, uint8_t*
             codes[64 * h + j] = (uint8_t)c;
         }
         n16[h] = nh;
+        if (rho_out) memcpy(rho_out + 64 * h, rho, sizeof rho);
+    }
+}
+
+void orc_split_encode(const float* x, const orc_tables* tb, int bits_o, uint8_t* codes, uint16_t* n16)
+{
+    split_halves(x, tb, bits_o, codes, n16, NULL);
+}
+
+/* Split TurboQuant key at b = 3 or 4 (reading R23): the MSE stage of the TurboQuant key code run
+ * on the outlier split (outliers b - 1 bits, the rest b - 2, each half its own 64-point rotation,
+ * norm and N(0, 1/64) codebook), then the 1-bit QJL sketch of the whole residual as for a
+ * TurboQuant key: r = rho - n_h mu_h[code] in position order, gamma = fp16(|r|) (index-order tree
+ * over the 128 positions), bit i = (sum_j S_ij r_j >= 0) with a sequential fma chain.  Budget:
+ * (b - 1 + b - 2) / 2 + 1 = b - 0.5 bits per channel (2.5 or 3.5), plus three fp16 norms. */
+void orc_split_qjl_encode(const float* x, const orc_tables* tb, int b, uint8_t* codes, uint16_t* n16,
+                          uint16_t* g16o, uint8_t* bits)
+{
+    float rho[D], r[D];
+    split_halves(x, tb, b - 1, codes, n16, rho);
+    for (int j = 0; j < D; j++) {
+        const int h = j >= 64;
+        float n = orc_f16_to_f32(n16[h]);
+        float p = n * (h ? tb->mu2 : tb->mu)[codes[j]];
+        r[j] = rho[j] - p;
+    }
+    *g16o = orc_f32_to_f16_rn(sqrtf(orc_tree_sum_sq(r)));
+    for (int i = 0; i < D; i++) {
+        float acc = 0.0f;
+        for (int j = 0; j < D; j++) acc = fmaf(tb->S[i * D + j], r[j], acc);
+        bits[i] = (acc >= 0.0f) ? 1 : 0;
+    }
+}
+
+/* The split domain of a query in binary64: position 64h + j = R64(q[perm[64h + .]])_j. */
+void orc_split_rotate_f64(const double* q, const orc_tables* tb, double* y)
+{
+    for (int h = 0; h < 2; h++) {
+        double t[64];
+        for (int j = 0; j < 64; j++) {
+            double v = q[tb->perm[64 * h + j]];
+            t[j] = (tb->signs[64 * h + j] < 0.0f) ? -v : v;
+        }
+        for (int s = 1; s < 64; s <<= 1)
+            for (int i = 0; i < 64; i++)
+                if (!(i & s)) {
+                    double a = t[i], c = t[i + s];
+                    t[i] = a + c;
+                    t[i + s] = a - c;
+                }
+        for (int j = 0; j < 64; j++) y[64 * h + j] = t[j] / 8.0;
     }
 }
 
@@ -553,6 +606,13 @@ void orc_split_encode(const float* x, const orc_tables* tb, int bits_o, uint8_t*
  * of 32 tokens, 256 W B each; position j (channel perm[j]): n = j%16, N = j/16.  Bit k of the
  * code of (t, j) is in u32 word W*(16*o + n) + k (j < 64) or W*(16*o + n) + bo + k (j >= 64) of
  * block t/32, at bit 16*(i%2) + 4*(N%4) + i/2.  Meta: u16 n_outlier, u16 n_rest per token.
+ * Split K (TURBO_SPLIT on the K tensor, b = 3 or 4, reading R23): rows in the uniform-K block
+ * order; position group g (positions 32g .. 32g+31; groups 0, 1 the outliers with b - 1 planes,
+ * groups 2, 3 the rest with b - 2) holds its planes as consecutive half-interleaved words, value
+ * e of plane k at bit 16*(e%2) + e/2 of word k; group g starts at word g (b-1) for g < 2 and at
+ * 2 (b-1) + (g-2) (b-2) otherwise: 4 (4b - 6) B per row (24 B at b = 3, 40 B at b = 4).  QJL
+ * plane: 16 B per row as for TURBO_QJL.  Meta per row (8 B): u16 n_outlier, u16 n_rest,
+ * u16 gamma, u16 0.
  * Every turbo plane holds a whole number of 64-token blocks.
  * Window ring: [W][128] fp32, token t at slot t % W.
  */
@@ -564,8 +624,11 @@ static size_t k_row(int t) { return (size_t)(64 * (t / 64) + 16 * ((t % 64) % 4)
 /* q8_0 planes use the 8-bit uniform byte layout */
 static int uniform_layout(const orc_plane_cfg* pc) { return pc->scheme == ORC_UNIFORM || pc->scheme == ORC_Q8_0; }
 
+static int split_k(const orc_plane_cfg* pc) { return pc->scheme == ORC_TURBO_SPLIT && pc->tensor == ORC_TENSOR_K; }
+
 size_t orc_codes_bytes(const orc_plane_cfg* pc)
 {
+    if (split_k(pc)) return (size_t)ceil_to(pc->capacity, 64) * 4 * (4 * pc->bits - 6);
     if (pc->scheme == ORC_TURBO_SPLIT) return (size_t)ceil_to(pc->capacity, 64) * 8 * (2 * pc->bits - 1);
     if (!uniform_layout(pc)) return (size_t)ceil_to(pc->capacity, 64) * 16 * pc->bits; /* b bit planes */
     return (size_t)ceil_to(pc->capacity, 64) * 16 * pc->bits;
@@ -573,6 +636,7 @@ size_t orc_codes_bytes(const orc_plane_cfg* pc)
 
 size_t orc_meta_bytes(const orc_plane_cfg* pc)
 {
+    if (split_k(pc)) return (size_t)ceil_to(pc->capacity, 64) * 8;
     if (pc->scheme == ORC_TURBO_QJL) return (size_t)ceil_to(pc->capacity, 64) * 4;
     if (pc->scheme == ORC_TURBO_MSE) return (size_t)ceil_to(pc->capacity, 64) * 2;
     if (pc->scheme == ORC_TURBO_SPLIT) return (size_t)ceil_to(pc->capacity, 64) * 4;
@@ -581,7 +645,7 @@ size_t orc_meta_bytes(const orc_plane_cfg* pc)
 
 size_t orc_qjl_bytes(const orc_plane_cfg* pc)
 {
-    return pc->scheme == ORC_TURBO_QJL ? (size_t)ceil_to(pc->capacity, 64) * 16 : 0;
+    return (pc->scheme == ORC_TURBO_QJL || split_k(pc)) ? (size_t)ceil_to(pc->capacity, 64) * 16 : 0;
 }
 
 size_t orc_ring_floats(const orc_plane_cfg* pc) { return (size_t)pc->window * D; }
@@ -628,6 +692,12 @@ static int tv_bit(int t, int d)
 {
     int i = t % 8, N = d / 16;
     return 16 * (i % 2) + 4 * (N % 4) + i / 2;
+}
+/* Split K: byte offset (in the row) of plane k of position group g, and the planes of group g. */
+static int sk_planes(int g, int b) { return g < 2 ? b - 1 : b - 2; }
+static size_t sk_word(int g, int k, int b)
+{
+    return 4 * (size_t)((g < 2 ? g * (b - 1) : 2 * (b - 1) + (g - 2) * (b - 2)) + k);
 }
 
 static void pack_token(const orc_plane_cfg* pc, int t, const uint8_t* code, const uint16_t* s16,
@@ -690,6 +760,22 @@ static void pack_token(const orc_plane_cfg* pc, int t, const uint8_t* code, cons
                 put_u16(m + 8 + 2 * g, z16[g]);
             }
         }
+        return;
+    }
+    if (split_k(pc)) {
+        size_t row = k_row(t);
+        uint8_t* r = codes + row * (size_t)(4 * (4 * pc->bits - 6));
+        for (int j = 0; j < D; j++) {
+            int g = j / 32, e = j % 32;
+            for (int k = 0; k < sk_planes(g, pc->bits); k++) put_bit(r + sk_word(g, k, pc->bits), ibit(e), code[j] >> k);
+        }
+        uint8_t* m = meta + row * 8;
+        put_u16(m, s16[0]);
+        put_u16(m + 2, s16[1]);
+        put_u16(m + 4, g16);
+        put_u16(m + 6, 0);
+        uint8_t* q = qjl + row * 16;
+        for (int i = 0; i < D; i++) put_bit(q + 4 * (i / 32), ibit(i % 32), bits[i]);
         return;
     }
     if (pc->scheme == ORC_TURBO_SPLIT) {
@@ -778,6 +864,19 @@ void orc_plane_read(const orc_plane_cfg* pc, const uint8_t* codes, const uint8_t
         return;
     }
     for (int k = 0; k < 8; k++) meta8[k] = 0;
+    if (split_k(pc)) {
+        size_t row = k_row(t);
+        const uint8_t* r = codes + row * (size_t)(4 * (4 * pc->bits - 6));
+        for (int j = 0; j < D; j++) {
+            int g = j / 32, e = j % 32, c = 0;
+            for (int k = 0; k < sk_planes(g, pc->bits); k++) c |= get_bit(r + sk_word(g, k, pc->bits), ibit(e)) << k;
+            code[j] = (uint8_t)c;
+        }
+        for (int k = 0; k < 3; k++) meta8[k] = get_u16(meta + row * 8 + 2 * k);
+        if (bits)
+            for (int i = 0; i < D; i++) bits[i] = (uint8_t)get_bit(qjl + row * 16 + 4 * (i / 32), ibit(i % 32));
+        return;
+    }
     if (pc->scheme == ORC_TURBO_SPLIT) {
         for (int j = 0; j < D; j++) {
             int nb = (j < 64) ? pc->bits : pc->bits - 1, c = 0;
@@ -839,6 +938,8 @@ void orc_plane_append(const orc_plane_cfg* pc, const orc_tables* tb, const float
                 else
                     orc_quant_group(y + GS * g, pc->bits, code + GS * g, &s16[g], &z16[g]);
             }
+        } else if (split_k(pc)) {
+            orc_split_qjl_encode(x, tb, pc->bits, code, s16, &g16, bits); /* s16[0..1] = n_O, n_R */
         } else if (pc->scheme == ORC_TURBO_SPLIT) {
             uint16_t nn[2];
             orc_split_encode(x, tb, pc->bits, code, nn);
@@ -912,6 +1013,22 @@ double orc_turbo_score(const orc_tables* tb, const uint8_t* codes, const uint8_t
     return n * a + gam * sqrt(ORC_PI / 2.0) / 128.0 * b;
 }
 
+/* Split K (reading R23): <q, k_t> ~= n_O <rho_q, mu_O[code]>_outliers + n_R <rho_q, mu_R[code]>_rest
+ * + gamma sqrt(pi/2)/128 sum_i sign_i (S rho_q)_i, with rho_q the split domain of q
+ * (orc_split_rotate_f64) and mu_O, mu_R = tb->mu, tb->mu2. */
+double orc_split_score(const orc_plane_cfg* pc, const orc_tables* tb, const uint8_t* codes, const uint8_t* meta,
+                       const uint8_t* qjl, int t, const double* rho_q, const double* s_rho_q)
+{
+    uint8_t code[D], bits[D];
+    uint16_t m8[8];
+    orc_plane_read(pc, codes, meta, qjl, t, code, m8, bits);
+    double a[2] = {0.0, 0.0}, b = 0.0;
+    for (int j = 0; j < D; j++) a[j >= 64] += rho_q[j] * (double)(j >= 64 ? tb->mu2 : tb->mu)[code[j]];
+    for (int i = 0; i < D; i++) b += (bits[i] ? 1.0 : -1.0) * s_rho_q[i];
+    return (double)orc_f16_to_f32(m8[0]) * a[0] + (double)orc_f16_to_f32(m8[1]) * a[1] +
+           (double)orc_f16_to_f32(m8[2]) * sqrt(ORC_PI / 2.0) / 128.0 * b;
+}
+
 /* Attention of G query heads over the first n_vis tokens of a cache holding n tokens
  * (1 <= n_vis <= n).  Which tokens are read from the FP32 window depends on n (the cache as it
  * stands), not on n_vis: a query of a prefill chunk at position n_vis - 1 sees the same token
@@ -931,7 +1048,8 @@ void orc_attention_prefix(const orc_plane_cfg* kc, const orc_plane_cfg* vc,
     int nq = (W > 0 && n > W) ? n - W : (W > 0 ? 0 : n); /* tokens read from the codes */
     double* V = (double*)malloc(sizeof(double) * (size_t)n * D);
     double* K = NULL;
-    if (kc->scheme != ORC_TURBO_QJL) K = (double*)malloc(sizeof(double) * (size_t)n * D);
+    const int ksplit = split_k(kc);
+    if (kc->scheme != ORC_TURBO_QJL && !ksplit) K = (double*)malloc(sizeof(double) * (size_t)n * D);
     for (int t = 0; t < n; t++) {
         if (t >= nq) { /* FP32 window token */
             const float* kr = kring + (size_t)(t % W) * D;
@@ -951,7 +1069,10 @@ void orc_attention_prefix(const orc_plane_cfg* kc, const orc_plane_cfg* vc,
         double qd[D], rq[D], srq[D];
         for (int j = 0; j < D; j++) qd[j] = qh[j];
         if (!K) {
-            orc_rotate_f64(qd, ktb->signs, rq);
+            if (ksplit)
+                orc_split_rotate_f64(qd, ktb, rq);
+            else
+                orc_rotate_f64(qd, ktb->signs, rq);
             for (int i = 0; i < D; i++) {
                 double s = 0.0;
                 for (int j = 0; j < D; j++) s += (double)ktb->S[i * D + j] * rq[j];
@@ -969,6 +1090,8 @@ void orc_attention_prefix(const orc_plane_cfg* kc, const orc_plane_cfg* vc,
                 } else {
                     for (int j = 0; j < D; j++) s += qd[j] * K[(size_t)t * D + j];
                 }
+            } else if (ksplit) {
+                s = orc_split_score(kc, ktb, kcodes, kmeta, kqjl, t, rq, srq);
             } else {
                 s = orc_turbo_score(ktb, kcodes, kmeta, kqjl, t, rq, srq);
             }

@@ -16,7 +16,8 @@
  *    1-bit QJL on the residual for an unbiased inner product.
  *  - the same page, method comparison table (the row of re-checked figures: 2.5 and 3.5 bits) and
  *    its verification notes (non-integer bit widths come from splitting off outlier channels;
- *    the printed example is garbled): the outlier-channel split of the value coder.
+ *    the printed example is garbled): the outlier-channel split of the value coder, and of the
+ *    key coder's MSE stage in front of its 1-bit QJL sketch (keys at 2.5 / 3.5 bits).
  * Every step the pages leave open is fixed by a stated reading (see the .c file's comments).
  *
  * Arithmetic conventions: binary32 round-to-nearest-even with no FMA contraction (the library is
@@ -120,6 +121,12 @@ float orc_tree_sum_sq64(const float* v);
 void orc_select_outliers(const float* X, int n, int* perm);
 /* Token code of the split: codes[j] for position j (channel perm[j]), n16[2] = subset norms. */
 void orc_split_encode(const float* x, const orc_tables* tb, int bits_o, uint8_t* codes, uint16_t* n16);
+/* Split key at b = 3 or 4: the split codes with b - 1 / b - 2 bits (tb->mu/theta: outlier
+ * codebook, mu2/theta2: the rest), n16[2], then gamma and the 128 QJL bits of the residual. */
+void orc_split_qjl_encode(const float* x, const orc_tables* tb, int b, uint8_t* codes, uint16_t* n16,
+                          uint16_t* g16, uint8_t* bits);
+/* y[128] = the split domain of q (binary64): position 64h + j = R64(q[perm[64h + .]])_j. */
+void orc_split_rotate_f64(const double* q, const orc_tables* tb, double* y);
 
 /* ---- planes ---- */
 size_t orc_codes_bytes(const orc_plane_cfg* pc);
@@ -142,6 +149,10 @@ void orc_dequant_token(const orc_plane_cfg* pc, const orc_tables* tb, const uint
 /* Turbo-QJL score estimate of <q, k_t> (fp64, unscaled). */
 double orc_turbo_score(const orc_tables* tb, const uint8_t* codes, const uint8_t* meta,
                        const uint8_t* qjl, int t, const double* rho_q, const double* s_rho_q);
+/* Split-key score estimate (rho_q = split domain of q, s_rho_q = S rho_q). */
+double orc_split_score(const orc_plane_cfg* pc, const orc_tables* tb, const uint8_t* codes,
+                       const uint8_t* meta, const uint8_t* qjl, int t, const double* rho_q,
+                       const double* s_rho_q);
 
 /* Attention of one kv head's G query heads over tokens 0 .. n_vis - 1 of a cache of n tokens
  * (window tokens chosen by n), fp64. */
