@@ -65,15 +65,18 @@ typedef enum {
                           baseline; K = Q8 of [P3]'s application rules): q = rint(y / d) in
                           [-127, 127] with d = fp16(max|y| / 127); stored in the UNIFORM 8-bit
                           layout as code q + 128 with zero = -128 d, so y = d q exactly       */
-    KVQ_TURBO_SPLIT = 4 /* V only: TurboQuant-MSE with the outlier-channel split that gives the
-                          fractional bit widths of [P3] (2.5 and 3.5 bits, method table and
-                          verification notes).  kvq_calibrate picks per (layer, kv head) the 64
-                          channels of largest energy (sum of squares over the calibration
-                          tokens, binary64 in token order; ties to the smaller index); each
-                          64-channel subset gets its own 64-point random-sign Walsh-Hadamard
-                          rotation (signs 0..63 / 64..127 of the tensor's sign vector, scale
-                          1/8), fp16 norm and Lloyd-Max code for N(0, 1/64): v_bits (3 or 4)
-                          bits on the outliers, v_bits - 1 on the rest                     */
+    KVQ_TURBO_SPLIT = 4 /* the outlier-channel split that gives the fractional bit widths of
+                          [P3] (2.5 and 3.5 bits, method table and verification notes).
+                          kvq_calibrate picks per (layer, kv head, tensor) the 64 channels of
+                          largest energy (sum of squares over the calibration tokens, binary64
+                          in token order; ties to the smaller index); each 64-channel subset
+                          gets its own 64-point random-sign Walsh-Hadamard rotation (signs
+                          0..63 / 64..127 of the tensor's sign vector, scale 1/8), fp16 norm
+                          and Lloyd-Max code for N(0, 1/64).  V: TurboQuant-MSE, v_bits (3 or
+                          4) bits on the outliers, v_bits - 1 on the rest.  K (k_bits = b = 3
+                          or 4): the TurboQuant key coder at b - 0.5 bits per channel, MSE
+                          codes of b - 1 bits on the outliers and b - 2 on the rest, then the
+                          1-bit QJL sketch of the whole residual with the cache's S          */
 } kvq_scheme;
 
 typedef struct {
@@ -84,7 +87,7 @@ typedef struct {
     int k_scheme, v_scheme;              /* kvq_scheme, chosen separately for K and V [P2]   */
     int k_bits, v_bits;                  /* UNIFORM: 3, 4 or 8; TURBO_QJL: 3; TURBO_MSE: 3, or 4
                                             for V ("Turbo4", [P3] rules); Q8_0: 8;
-                                            TURBO_SPLIT: 3 (2.5 bits) or 4 (3.5 bits)        */
+                                            TURBO_SPLIT: 3 (2.5 bits) or 4 (3.5 bits), K or V */
     int group_size;                      /* must be 32                                       */
     int fp32_window;                     /* 0 = flat, 128 = progressive [P1]                 */
     int rotate_k, rotate_v;              /* random-sign Walsh-Hadamard before coding [P2];
@@ -127,6 +130,12 @@ typedef struct kvq_cache kvq_cache; /* opaque host-side handle */
  *      W*(16o + n) + k (j < 64, k < bo) or W*(16o + n) + bo + k (j >= 64, k < bo - 1) of block
  *      t/32, at bit 16*(i%2) + 4*(N%4) + i/2.  Meta: u16 fp16 outlier norm, u16 fp16 rest norm
  *      per token.
+ *  TURBO_SPLIT K (b = k_bits): rows in the UNIFORM K row order; position group g (positions
+ *      32g .. 32g+31; groups 0, 1 are the outliers with b - 1 code planes, groups 2, 3 the rest
+ *      with b - 2) keeps plane k as the u32 word g(b-1) + k (g < 2) or 2(b-1) + (g-2)(b-2) + k
+ *      (g >= 2) of its row, value e of the group at bit 16*(e%2) + e/2: 4(4b - 6) B per row
+ *      (24 or 40).  QJL plane: 16 B per row as for TURBO_QJL.  Meta: 8 B per row, u16 fp16
+ *      outlier norm, rest norm, residual norm, 0.
  *  Window ring: [fp32_window][128] fp32, token t at slot t % fp32_window.               */
 typedef struct {
     void *codes, *meta, *qjl, *window;
@@ -144,16 +153,18 @@ typedef struct {
     const float* theta;  /* [7] Lloyd-Max decision thresholds                            */
     const float* mu16;   /* [16] 16-level centroids (4-bit TurboQuant-MSE V), if present */
     const float* theta16; /* [15] their thresholds                                       */
-    const int* perm;     /* [n_layers][n_kv_heads][128] TURBO_SPLIT position -> channel    */
-    const float* mu64;   /* [28] TURBO_SPLIT codebooks of N(0, 1/64): 4, 8, 16 levels at 0,
-                            4, 12                                                       */
-    const float* theta64; /* [28] their thresholds, same offsets (levels - 1 used)       */
+    const int* perm;     /* [n_layers][n_kv_heads][128] TURBO_SPLIT V position -> channel  */
+    const float* mu64;   /* [30] TURBO_SPLIT codebooks of N(0, 1/64): 4, 8, 16 levels at 0,
+                            4, 12; 2 levels at 28                                       */
+    const float* theta64; /* [30] their thresholds, same offsets (levels - 1 used)       */
+    const int* perm_k;   /* [n_layers][n_kv_heads][128] TURBO_SPLIT K position -> channel  */
 } kvq_tables;
 
 enum {
     KVQ_OPT_SPLIT_TOKENS = 1, /* tokens per decode split (multiple of 64); 0 = automatic     */
     KVQ_OPT_DECODE_PATH = 2   /* 0 = automatic, 1 = vector-ALU kernel, 2 = matrix-core kernel
-                                 (every scheme has both)                                  */
+                                 (every scheme has both except a TURBO_SPLIT K, which decodes
+                                 on the vector ALU: 2 gives KVQ_ERR_UNSUPPORTED for it)      */
 };
 
 /* Bytes of device memory a cache with this configuration needs (planes for every layer,
@@ -183,8 +194,9 @@ kvq_status kvq_set_random_tables(kvq_cache* cache, const float* signs, const flo
  * [128] of dtype for K and V; a tensor's pointer may be NULL when it is not balanced), then
  * alternately divide rows and columns by their population standard deviation sinkhorn_iters
  * times in fp64 on the device, and store c = product of the column divisors and fp32(1/c).
- * 2 <= n_tokens <= calib_tokens.  A TURBO_SPLIT V takes its 64 outlier channels per kv head
- * from Vc (required then) in the same call.  Required once per layer before appending to it. */
+ * 2 <= n_tokens <= calib_tokens.  A TURBO_SPLIT V (K) takes its 64 outlier channels per kv
+ * head from Vc (Kc), required then, in the same call.  Required once per layer before appending
+ * to it. */
 kvq_status kvq_calibrate(kvq_cache* cache, int layer, const void* Kc, const void* Vc, int dtype,
                          int n_tokens, void* stream);
 

@@ -101,6 +101,6 @@ class KvCache:
 
     def table(self, name, count):
         """Device view of one table: fp32 for signs, c, inv_c, qjl_S, mu, theta, mu16, theta16, mu64,
-        theta64; int32 for perm (the split V's position -> channel map)."""
+        theta64; int32 for perm and perm_k (the split V's / K's position -> channel maps)."""
         t = _kvq.kvq_get_tables(self.handle)
-        return self._slice(getattr(t, name), 4 * count).view(torch.int32 if name == "perm" else torch.float32)
+        return self._slice(getattr(t, name), 4 * count).view(torch.int32 if name in ("perm", "perm_k") else torch.float32)

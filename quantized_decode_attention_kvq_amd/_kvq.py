@@ -50,7 +50,7 @@ class kvq_layout(ctypes.Structure):
 
 class kvq_tables(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("signs", "c", "inv_c", "qjl_S", "mu", "theta", "mu16",
-                                              "theta16", "perm", "mu64", "theta64")]
+                                              "theta16", "perm", "mu64", "theta64", "perm_k")]
 
 
 _lib = None

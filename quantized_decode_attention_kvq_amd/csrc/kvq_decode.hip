@@ -55,6 +55,29 @@ __device__ __forceinline__ void hadamard_wave(float& a, float& b) {
     hadamard_step<32>(a, b, l);
 }
 
+// The split domain of a vector held as channel pairs (lane l: 2l, 2l+1): positions 2l, 2l+1 take
+// channels pm.x, pm.y (lane pm / 2, component pm % 2), then the signs by position and the two
+// 64-point Walsh-Hadamard transforms (the butterflies without the last span), scale 1/8.
+__device__ __forceinline__ void split_rotate(float& a, float& c, int2 pm, float2 sg) {
+    const int l = lane_id();
+    const float ax = __shfl(a, pm.x >> 1), ay = __shfl(c, pm.x >> 1);
+    const float bx = __shfl(a, pm.y >> 1), by = __shfl(c, pm.y >> 1);
+    a = (pm.x & 1) ? ay : ax;
+    c = (pm.y & 1) ? by : bx;
+    if (sg.x < 0.0f) a = -a;
+    if (sg.y < 0.0f) c = -c;
+    const float s = a + c, d = a - c;
+    a = s;
+    c = d;
+    hadamard_step<1>(a, c, l);
+    hadamard_step<2>(a, c, l);
+    hadamard_step<4>(a, c, l);
+    hadamard_step<8>(a, c, l);
+    hadamard_step<16>(a, c, l);
+    a *= 0.125f;
+    c *= 0.125f;
+}
+
 __device__ __forceinline__ int k_row(int t) { return 64 * (t / 64) + 16 * ((t % 64) % 4) + (t % 64) / 4; }
 
 __device__ __forceinline__ void load_q_pair(const DecodeParams& p, int b, int hq, float& a, float& c) {
@@ -89,6 +112,17 @@ __device__ __forceinline__ uint32_t turbo_v_code(const uint8_t* codes, int t, in
     const int b = 16 * (i & 1) + 4 * (N & 3) + (i >> 1);
     uint32_t c = 0;
     for (int k = 0; k < nb; ++k) c |= ((w[2 * k] >> b) & 1u) << k;
+    return c;
+}
+
+// Split key (b = 3 or 4): code of position j from a row of per-group plane words (group
+// g = j / 32 has b - 1 planes if g < 2, else b - 2, from word split_k_group_word(g, b)).
+__device__ __forceinline__ uint32_t split_k_code(const uint8_t* row, int j, int b) {
+    const int g = j >> 5, e = j & 31, nb = g < 2 ? b - 1 : b - 2;
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(row) + split_k_group_word(g, b);
+    const int bit = 16 * (e & 1) + (e >> 1);
+    uint32_t c = 0;
+    for (int k = 0; k < nb; ++k) c |= ((w[k] >> bit) & 1u) << k;
     return c;
 }
 
@@ -143,7 +177,11 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
     for (int h = wave; h < G; h += 4) {
         float a, c;
         load_q_pair(p, b, kvh * G + h, a, c);
-        if (!wsplit && KG.rotate) {
+        if (!wsplit && KG.scheme == kTurboSplit) {
+            const int2 pm = reinterpret_cast<const int2*>(p.perm_k + (size_t)kvh * kDim)[l];
+            const float2 sg = reinterpret_cast<const float2*>(p.signs + (size_t)(kvh * 2 + 0) * kDim)[l];
+            split_rotate(a, c, pm, sg);
+        } else if (!wsplit && KG.rotate) {
             const float* sg = p.signs + (size_t)(kvh * 2 + 0) * kDim;
             if (sg[2 * l] < 0.0f) a = -a;
             if (sg[2 * l + 1] < 0.0f) c = -c;
@@ -160,7 +198,7 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
         qp[h][2 * l + 1] = c * p.qscale;
     }
     __syncthreads();
-    const bool turbo_k = !wsplit && KG.scheme == kTurboQjl;
+    const bool turbo_k = !wsplit && (KG.scheme == kTurboQjl || KG.scheme == kTurboSplit);
     if (turbo_k) {
         for (int idx = threadIdx.x; idx < G * kDim; idx += 256) {
             const int h = idx / kDim, i = idx % kDim;
@@ -263,6 +301,42 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
                     for (int h = 0; h < kMaxGroupHeads; ++h)
                         if (h < G) s[h] += sc * dot[h][g] + zc * qsum[h][g];
                 }
+            } else if (KG.scheme == kTurboSplit) { // split key: two halves, then the QJL term
+                const int krow = k_row(t), kb = KG.bits;
+                const uint8_t* row = kcodes + (size_t)krow * split_k_row_bytes(kb);
+                const uint16_t* mt = reinterpret_cast<const uint16_t*>(kmeta + (size_t)krow * 8);
+                const float nO = h2f(mt[0]), nR = h2f(mt[1]), gam = h2f(mt[2]);
+                const float* muO = p.mu64 + split_table_off(1 << (kb - 1));
+                const float* muR = p.mu64 + split_table_off(1 << (kb - 2));
+                float aO[kMaxGroupHeads], aR[kMaxGroupHeads], a2[kMaxGroupHeads];
+#pragma unroll
+                for (int h = 0; h < kMaxGroupHeads; ++h) aO[h] = aR[h] = a2[h] = 0.0f;
+                for (int j = 0; j < 64; ++j) {
+                    const float mv = muO[split_k_code(row, j, kb)];
+#pragma unroll
+                    for (int h = 0; h < kMaxGroupHeads; ++h)
+                        if (h < G) aO[h] += mv * qp[h][j];
+                }
+                for (int j = 64; j < kDim; ++j) {
+                    const float mv = muR[split_k_code(row, j, kb)];
+#pragma unroll
+                    for (int h = 0; h < kMaxGroupHeads; ++h)
+                        if (h < G) aR[h] += mv * qp[h][j];
+                }
+                const uint32_t* qb = reinterpret_cast<const uint32_t*>(kqjl + (size_t)krow * 16);
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t bits = qb[w];
+                    for (int i = 0; i < 32; ++i)
+                        if ((bits >> i) & 1u) {
+                            const int idx = 32 * w + 2 * (i & 15) + (i >> 4);
+#pragma unroll
+                            for (int h = 0; h < kMaxGroupHeads; ++h)
+                                if (h < G) a2[h] += sp[h][idx];
+                        }
+                }
+#pragma unroll
+                for (int h = 0; h < kMaxGroupHeads; ++h)
+                    if (h < G) s[h] = nO * aO[h] + nR * aR[h] + gam * kappa * (2.0f * a2[h] - spsum[h]);
             } else { // TurboQuant key
                 const int krow = k_row(t);
                 const uint8_t* row = kcodes + (size_t)krow * 48;

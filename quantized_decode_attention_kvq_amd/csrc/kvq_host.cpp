@@ -28,7 +28,7 @@ struct Plan {
     size_t plane_bytes[2];
     size_t slot_bytes;
     size_t off_signs, off_c, off_inv_c, off_S, off_ST, off_mu, off_theta, off_mu16, off_theta16;
-    size_t off_perm, off_mu64, off_theta64;
+    size_t off_perm, off_perm_k, off_mu64, off_theta64;
     size_t off_work, work_bytes;
     size_t off_planes, total;
 };
@@ -45,7 +45,8 @@ kvq_status check_config(const kvq_config* c) {
     if (c->max_batch > kMaxBatch) return KVQ_ERR_UNSUPPORTED;
     if (c->max_context > (1 << 26)) return KVQ_ERR_UNSUPPORTED;
     if (c->fp32_window != 0 && c->fp32_window != kWindowMax) return KVQ_ERR_UNSUPPORTED;
-    if (c->k_scheme != KVQ_UNIFORM && c->k_scheme != KVQ_TURBO_QJL && c->k_scheme != KVQ_Q8_0)
+    if (c->k_scheme != KVQ_UNIFORM && c->k_scheme != KVQ_TURBO_QJL && c->k_scheme != KVQ_Q8_0 &&
+        c->k_scheme != KVQ_TURBO_SPLIT)
         return KVQ_ERR_UNSUPPORTED;
     if (c->v_scheme != KVQ_UNIFORM && c->v_scheme != KVQ_TURBO_MSE && c->v_scheme != KVQ_Q8_0 &&
         c->v_scheme != KVQ_TURBO_SPLIT)
@@ -57,13 +58,14 @@ kvq_status check_config(const kvq_config* c) {
         if (scheme == KVQ_TURBO_QJL && bits != 3) return KVQ_ERR_UNSUPPORTED;
         // TurboQuant-MSE: 3-bit codes, or 4-bit codes for V ("Turbo4")
         if (scheme == KVQ_TURBO_MSE && bits != 3 && !(bits == 4 && t == 1)) return KVQ_ERR_UNSUPPORTED;
-        // outlier split (V only): 3 or 4 bits on the outlier half, one fewer on the rest
+        // outlier split: V with 3 or 4 bits on the outlier half and one fewer on the rest; K at
+        // b = 3 or 4 (b - 1 / b - 2 MSE bits plus the QJL bit: 2.5 or 3.5 bits per channel)
         if (scheme == KVQ_TURBO_SPLIT && bits != 3 && bits != 4) return KVQ_ERR_UNSUPPORTED;
     }
     if ((c->rotate_k != 0 && c->rotate_k != 1) || (c->rotate_v != 0 && c->rotate_v != 1))
         return KVQ_ERR_INVALID_ARG;
     if (c->sinkhorn_iters > 1000) return KVQ_ERR_UNSUPPORTED;
-    if ((c->sinkhorn_iters > 0 || c->v_scheme == KVQ_TURBO_SPLIT) &&
+    if ((c->sinkhorn_iters > 0 || c->v_scheme == KVQ_TURBO_SPLIT || c->k_scheme == KVQ_TURBO_SPLIT) &&
         (c->calib_tokens < 2 || c->calib_tokens > 65536))
         return KVQ_ERR_UNSUPPORTED;
     return KVQ_OK;
@@ -86,6 +88,10 @@ PlaneGeom make_geom(const kvq_config* c, int tensor) {
         g.codes_bytes = rows * 16 * (size_t)g.bits;
         g.meta_bytes = rows * 16;
         g.qjl_bytes = 0;
+    } else if (scheme == KVQ_TURBO_SPLIT && tensor == 0) {
+        g.codes_bytes = rows * (size_t)split_k_row_bytes(g.bits); // per-group plane words per row
+        g.meta_bytes = rows * 8;                                  // fp16 n_outlier, n_rest, gamma, 0
+        g.qjl_bytes = rows * 16;
     } else if (scheme == KVQ_TURBO_SPLIT) {
         g.codes_bytes = rows * 8 * (size_t)(2 * g.bits - 1); // bits + (bits - 1) planes of 8 B
         g.meta_bytes = rows * 4;                             // two fp16 norms per token
@@ -135,6 +141,8 @@ Plan make_plan(const kvq_config* c) {
     p.off_theta16 = off;
     off = align_up(off + 16 * sizeof(float));
     p.off_perm = off;
+    off = align_up(off + (size_t)c->n_layers * c->n_kv_heads * kDim * sizeof(int));
+    p.off_perm_k = off;
     off = align_up(off + (size_t)c->n_layers * c->n_kv_heads * kDim * sizeof(int));
     p.off_mu64 = off;
     off = align_up(off + kSplitTable * sizeof(float));
@@ -187,7 +195,9 @@ struct kvq_cache {
     float* theta16() const { return reinterpret_cast<float*>(base + plan.off_theta16); }
     bool turbo4() const { return cfg.v_scheme == KVQ_TURBO_MSE && cfg.v_bits == 4; }
     bool split() const { return cfg.v_scheme == KVQ_TURBO_SPLIT; }
+    bool split_k() const { return cfg.k_scheme == KVQ_TURBO_SPLIT; }
     int* perm() const { return reinterpret_cast<int*>(base + plan.off_perm); }
+    int* perm_k() const { return reinterpret_cast<int*>(base + plan.off_perm_k); }
     float* mu64() const { return reinterpret_cast<float*>(base + plan.off_mu64); }
     float* theta64() const { return reinterpret_cast<float*>(base + plan.off_theta64); }
     size_t perm_off(int layer) const { return (size_t)layer * cfg.n_kv_heads * kDim; }
@@ -196,9 +206,9 @@ struct kvq_cache {
     }
     size_t table_off(int layer) const { return (size_t)layer * cfg.n_kv_heads * 2 * kDim; }
     bool needs_signs() const { return plan.geom[0].rotate || plan.geom[1].rotate; }
-    bool needs_S() const { return cfg.k_scheme == KVQ_TURBO_QJL; }
+    bool needs_S() const { return cfg.k_scheme == KVQ_TURBO_QJL || cfg.k_scheme == KVQ_TURBO_SPLIT; }
     bool needs_sinkhorn() const { return plan.geom[0].sinkhorn || plan.geom[1].sinkhorn; }
-    bool needs_calib() const { return needs_sinkhorn() || split(); }
+    bool needs_calib() const { return needs_sinkhorn() || split() || split_k(); }
     bool turbo() const { return cfg.k_scheme == KVQ_TURBO_QJL || cfg.v_scheme == KVQ_TURBO_MSE; }
 };
 
@@ -277,9 +287,10 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, 
     if (e == hipSuccess) e = static_scratch_setup(c->device);
     if (e == hipSuccess && c->turbo()) e = launch_codebook(c->mu(), c->theta(), kLloydIters, 8, 128, s);
     if (e == hipSuccess && c->turbo4()) e = launch_codebook(c->mu16(), c->theta16(), kLloydIters, 16, 128, s);
-    // split V: the 4-, 8- and 16-level codebooks of N(0, 1/64), table offset levels - 4
-    for (int levels = 4; levels <= 16 && e == hipSuccess && c->split(); levels *= 2)
-        e = launch_codebook(c->mu64() + (levels - 4), c->theta64() + (levels - 4), kLloydIters, levels, 64, s);
+    // split V / K: the 2-, 4-, 8- and 16-level codebooks of N(0, 1/64) (split_table_off)
+    for (int levels = 2; levels <= 16 && e == hipSuccess && (c->split() || c->split_k()); levels *= 2)
+        e = launch_codebook(c->mu64() + split_table_off(levels), c->theta64() + split_table_off(levels), kLloydIters,
+                            levels, 64, s);
     if (e != hipSuccess) {
         delete c;
         return KVQ_ERR_DEVICE;
@@ -330,7 +341,7 @@ kvq_status kvq_calibrate(kvq_cache* c, int layer, const void* Kc, const void* Vc
         if (src[t] && !aligned16(src[t])) return KVQ_ERR_MISALIGNED;
         p.src[t] = src[t];
     }
-    if (c->split() && !Vc) return KVQ_ERR_INVALID_ARG;
+    if ((c->split() && !Vc) || (c->split_k() && !Kc)) return KVQ_ERR_INVALID_ARG;
     if (c->needs_signs() && !c->tables_set) return KVQ_ERR_NOT_READY;
     p.work = reinterpret_cast<double*>(c->base + c->plan.off_work);
     p.signs = c->signs() + c->table_off(layer);
@@ -342,10 +353,11 @@ kvq_status kvq_calibrate(kvq_cache* c, int layer, const void* Kc, const void* Vc
     p.iters = c->cfg.sinkhorn_iters;
     hipError_t e = hipSuccess;
     if (c->needs_sinkhorn()) e = launch_calibrate(p, static_cast<hipStream_t>(stream));
-    if (e == hipSuccess && c->split()) {
+    for (int t = 0; t < 2 && e == hipSuccess; ++t) {
+        if (!(t == 0 ? c->split_k() : c->split())) continue;
         OutlierParams op{};
-        op.src = Vc;
-        op.perm = c->perm() + c->perm_off(layer);
+        op.src = t == 0 ? Kc : Vc;
+        op.perm = (t == 0 ? c->perm_k() : c->perm()) + c->perm_off(layer);
         op.dtype = dtype;
         op.n = n_tokens;
         op.Hkv = c->cfg.n_kv_heads;
@@ -388,6 +400,7 @@ kvq_status make_quant(kvq_cache* c, int layer, const void* K, const void* V, int
     p.mu16 = c->mu16();
     p.theta16 = c->theta16();
     p.perm = c->perm() + c->perm_off(layer);
+    p.perm_k = c->perm_k() + c->perm_off(layer);
     p.mu64 = c->mu64();
     p.theta64 = c->theta64();
     p.dtype = dtype;
@@ -431,6 +444,7 @@ kvq_status make_decode(const kvq_cache* c, int layer, const void* q, int dtype, 
     p.mu = c->mu();
     p.mu16 = c->mu16();
     p.perm = c->perm() + c->perm_off(layer);
+    p.perm_k = c->perm_k() + c->perm_off(layer);
     p.mu64 = c->mu64();
     p.partials = reinterpret_cast<float*>(c->base + c->plan.off_work);
     p.dtype = dtype;
@@ -663,6 +677,7 @@ kvq_status kvq_attn_prefill(kvq_cache* c, int layer, const void* q, int dtype, f
     p.mu = c->mu();
     p.mu16 = c->mu16();
     p.perm = c->perm() + c->perm_off(layer);
+    p.perm_k = c->perm_k() + c->perm_off(layer);
     p.mu64 = c->mu64();
     p.dtype = dtype;
     p.batch = batch;
@@ -721,6 +736,7 @@ kvq_status kvq_get_tables(const kvq_cache* c, kvq_tables* out) {
     out->mu16 = c->mu16();
     out->theta16 = c->theta16();
     out->perm = c->perm();
+    out->perm_k = c->perm_k();
     out->mu64 = c->mu64();
     out->theta64 = c->theta64();
     return KVQ_OK;

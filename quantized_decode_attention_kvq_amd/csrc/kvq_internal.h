@@ -17,12 +17,21 @@ constexpr int kPartialFloats = 132; // m, l, pad, pad, acc[128] per (sequence, q
 constexpr int kWindowMax = 128;
 constexpr int kWinSplitsMatrix = 1; // FP32-window workgroups per (sequence, kv head), matrix path
 
-// kTurboSplit: TurboQuant-MSE V with the outlier-channel split (the public KVQ_TURBO_SPLIT);
-// bits = the outlier subset's code bits (3 or 4), the other 64 channels take one bit fewer
+// kTurboSplit: the outlier-channel split (the public KVQ_TURBO_SPLIT).  V: TurboQuant-MSE codes,
+// bits = the outlier subset's code bits (3 or 4), the other 64 channels take one bit fewer.
+// K: bits = b (3 or 4), the TurboQuant key coder at b - 0.5 bits per channel -- MSE codes of
+// b - 1 bits on the outliers and b - 2 on the rest, plus the 1-bit QJL sketch of the residual.
 enum Scheme { kUniform = 0, kTurboQjl = 1, kTurboMse = 2, kTurboSplit = 4 };
 // Split-coder codebooks for N(0, 1/64) with L = 4, 8, 16 levels start at float L - 4 of the
-// 28-float tables (centroids; thresholds likewise, L - 1 of L used)
-constexpr int kSplitTable = 28;
+// 30-float tables, the 2-level one at float 28 (centroids; thresholds likewise, L - 1 of L used)
+constexpr int kSplitTable = 30;
+__host__ __device__ constexpr int split_table_off(int levels) { return levels == 2 ? 28 : levels - 4; }
+// Bytes of a split key row's code planes (b - 1 planes on each outlier group, b - 2 on each
+// other group, 4 bytes per plane word) and the word at which position group g's planes start.
+__host__ __device__ constexpr int split_k_row_bytes(int b) { return 4 * (4 * b - 6); }
+__host__ __device__ constexpr int split_k_group_word(int g, int b) {
+    return g < 2 ? g * (b - 1) : 2 * (b - 1) + (g - 2) * (b - 2);
+}
 
 // Geometry of one tensor's plane inside a (layer, seq, head) slot.
 struct PlaneGeom {
@@ -48,6 +57,7 @@ struct QuantParams {
     const float* mu16;        // [16]: 4-bit TurboQuant-MSE V codebook
     const float* theta16;     // [16], 15 used
     const int* perm;          // layer base [Hkv][128]: channel at each position (split V)
+    const int* perm_k;        // layer base [Hkv][128]: the same for a split K
     const float* mu64;        // [kSplitTable] split codebooks
     const float* theta64;     // [kSplitTable]
     int dtype, T, batch, Hkv, window;
@@ -69,6 +79,7 @@ struct DecodeParams {
     const float* mu;
     const float* mu16;        // [16]: 4-bit TurboQuant-MSE V codebook
     const int* perm;          // layer base [Hkv][128] (split V)
+    const int* perm_k;        // layer base [Hkv][128] (split K)
     const float* mu64;        // [kSplitTable] split codebooks
     float* partials;          // [batch][Hq][n_splits_total][kPartialFloats]
     int dtype, batch, Hq, Hkv, G, window;
@@ -102,6 +113,7 @@ struct PrefillParams {
     const float* mu;          // [8]: 3-bit TurboQuant codebook (QJL K, MSE V)
     const float* mu16;        // [16]: 4-bit TurboQuant-MSE V codebook
     const int* perm;          // layer base [Hkv][128] (split V)
+    const int* perm_k;        // layer base [Hkv][128] (split K)
     const float* mu64;        // [kSplitTable] split codebooks
     int dtype, batch, n_q, Hq, Hkv, G, window;
     int n_splits;             // key splits per row (1: the attention kernel writes out itself)

@@ -103,6 +103,12 @@ struct Planes {
 // TurboQuant 3-bit K row layout), or kQjlK (TurboQuant-QJL: 3-bit Lloyd-Max codes in that row
 // layout, fp16 n and gamma per row, 16 bytes of QJL signs per row).
 constexpr int kQjlK = -3;
+// Split keys at b = 3 or 4 (kSplitK - b): per-group plane words (b - 1 planes on groups 0, 1,
+// b - 2 on groups 2, 3) in a split_k_row_bytes(b) row, fp16 n_outlier, n_rest, gamma per row,
+// and the QJL signs of a TurboQuant key.
+constexpr int kSplitK = -20;
+__host__ __device__ constexpr bool split_k_kind(int kb) { return kb <= kSplitK - 3 && kb >= kSplitK - 4; }
+__host__ __device__ constexpr int split_k_bits(int kb) { return kSplitK - kb; }
 constexpr float kKappa = 0.0097915166977774f; // sqrt(pi/2) / 128
 // Value kinds: VB = 4 or 8 (uniform codes), 3 (uniform 3-bit codes as three bit planes in the
 // TurboQuant-MSE V layout, read by TurboQuant value units), -b for TurboQuant-MSE V with b = 3 or
@@ -131,7 +137,16 @@ __device__ __forceinline__ void load_codes(const Planes& P, int ci, int tid, Chu
     for (int j = 0; j < kUnits; ++j) {
         const int u = tid + kThreads * j, g = (u >> 2) & 3, word = 4 * (u & 3) + g;
         const size_t row = (size_t)64 * ci + (u >> 4);
-        if constexpr (KB == 3 || KB == kQjlK) {
+        if constexpr (split_k_kind(KB)) {
+            // the plane words of position group g (planes beyond the group's count read as 0)
+            constexpr int B = split_k_bits(KB);
+            const uint32_t* pw = reinterpret_cast<const uint32_t*>(P.kcodes + row * split_k_row_bytes(B)) +
+                                 split_k_group_word(g, B);
+            const int nb = g < 2 ? B - 1 : B - 2;
+            R.kc[j].x = pw[0];
+            R.kc[j].y = nb > 1 ? pw[1] : 0u;
+            R.kc3[j] = nb > 2 ? pw[2] : 0u;
+        } else if constexpr (KB == 3 || KB == kQjlK) {
             // the three plane words of group g (the unit's codes are their nibble u % 4)
             const uint32_t* pw = reinterpret_cast<const uint32_t*>(P.kcodes + row * 48 + 12 * g);
             R.kc[j].x = pw[0];
@@ -143,13 +158,17 @@ __device__ __forceinline__ void load_codes(const Planes& P, int ci, int tid, Chu
             const uint16_t* m = reinterpret_cast<const uint16_t*>(P.kmeta + row * 4);
             R.ks[j] = m[0]; // n
             R.kz[j] = m[1]; // gamma
+        } else if constexpr (split_k_kind(KB)) {
+            const uint16_t* m = reinterpret_cast<const uint16_t*>(P.kmeta + row * 8);
+            R.ks[j] = m[g < 2 ? 0 : 1]; // the half's norm
+            R.kz[j] = m[2];             // gamma
         } else {
             const uint16_t* m = reinterpret_cast<const uint16_t*>(P.kmeta + row * 16);
             R.ks[j] = m[g]; // kept apart until the dequantization: no wait on the load here
             R.kz[j] = m[4 + g];
         }
     }
-    if constexpr (KB == kQjlK) {
+    if constexpr (KB == kQjlK || split_k_kind(KB)) {
         // sign word tid % 4 of physical row tid / 4
         if (tid < 256) R.kq = reinterpret_cast<const uint32_t*>(P.kqjl + ((size_t)64 * ci + (tid >> 2)) * 16)[tid & 3];
     }
@@ -319,10 +338,22 @@ __device__ __forceinline__ void turbo_values(const uint32_t* wd, const _Float16*
     }
 }
 
-// QJL keys: the 3-bit code of each of a key unit's elements 2k, 2k + 1 (bits 4 kb + k and
-// 16 + 4 kb + k of the three plane words)
+// QJL and split keys: the (up to) 3-bit code of each of a key unit's elements 2k, 2k + 1 (bits
+// 4 kb + k and 16 + 4 kb + k of the plane words; missing planes are 0)
 __device__ __forceinline__ uint32_t code3_at(uint32_t p0, uint32_t p1, uint32_t p2, int sh) {
     return ((p0 >> sh) & 1u) | (((p1 >> sh) & 1u) << 1) | (((p2 >> sh) & 1u) << 2);
+}
+
+// Centroid of an nb-bit code (nb = 1, 2 or 3, known at run time) from the upper half of its
+// odd-symmetric codebook (mg[j] = mu[2^(nb-1) + j], unused entries ignored).
+__device__ __forceinline__ float centroid_rt(uint32_t c, int nb, const float* mg) {
+    const uint32_t H = 1u << (nb - 1);
+    const bool up = (c & H) != 0;
+    const uint32_t j = (c & (H - 1)) ^ (up ? 0u : H - 1);
+    const float a = (j & 1) ? mg[1] : mg[0];
+    const float b = (j & 1) ? mg[3] : mg[2];
+    const float m = (j & 2) ? b : a;
+    return up ? m : -m;
 }
 
 template <int KB, int VB>
@@ -340,14 +371,25 @@ __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const 
         const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)R.ks[j]);
         const _Float16 zr = __builtin_bit_cast(_Float16, (uint16_t)R.kz[j]);
         u4 hi, lo;
-        if constexpr (KB == kQjlK) {
-            // n mu[code] in fp32, then fp16 hi + remainder lo; the row's first unit writes f_t
+        if constexpr (KB == kQjlK || split_k_kind(KB)) {
+            // n mu[code] in fp32, then fp16 hi + remainder lo; the row's first unit writes f_t.
+            // Split keys: the unit's position group g picks the half (norm loaded per unit), its
+            // code width and its codebook (mgk[0..3] outliers, mgk[4..7] the rest)
             const float n = (float)sc;
+            int nb = 3;
+            float mgu[4] = {mgk[0], mgk[1], mgk[2], mgk[3]};
+            if constexpr (split_k_kind(KB)) {
+                constexpr int B = split_k_bits(KB);
+                const bool out = ((u >> 2) & 3) < 2;
+                nb = out ? B - 1 : B - 2;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mgu[i] = out ? mgk[i] : mgk[4 + i];
+            }
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int sh = 4 * (u & 3) + k;
-                float ye = n * centroid<3>(code3_at(R.kc[j].x, R.kc[j].y, R.kc3[j], sh), mgk);
-                float yo = n * centroid<3>(code3_at(R.kc[j].x, R.kc[j].y, R.kc3[j], sh + 16), mgk);
+                float ye = n * centroid_rt(code3_at(R.kc[j].x, R.kc[j].y, R.kc3[j], sh), nb, mgu);
+                float yo = n * centroid_rt(code3_at(R.kc[j].x, R.kc[j].y, R.kc3[j], sh + 16), nb, mgu);
                 // the products are rounded to fp32 once, here: with contraction the compiler may
                 // otherwise take hi from the fp32 product and lo from the exact one, which differ
                 // by one fp16 ulp where the fp32 product is an fp16 tie
@@ -378,7 +420,7 @@ __device__ __forceinline__ void dequant_chunk(_Float16* sk, _Float16* sv, const 
         *reinterpret_cast<u4*>(dst) = hi;
         *reinterpret_cast<u4*>(dst + 64 * kKS) = lo;
     }
-    if constexpr (KB == kQjlK) {
+    if constexpr (KB == kQjlK || split_k_kind(KB)) {
         if (tid < 256) {
             const int p = tid >> 2, t = 4 * (p & 15) + (p >> 4);
             ssg[4 * key_lds_row(t) + (tid & 3)] = R.kq;
@@ -481,7 +523,7 @@ __device__ __forceinline__ void window_overwrite(_Float16* sk, _Float16* sv, uin
         _Float16* dst = sk + key_lds_row(t) * kKS + 8 * w;
         *reinterpret_cast<h8*>(dst) = hi;
         *reinterpret_cast<h8*>(dst + 64 * kKS) = lo;
-        if constexpr (KB == kQjlK) {
+        if constexpr (KB == kQjlK || split_k_kind(KB)) {
             if (w == 0) sf[key_lds_row(t)] = 0u;
         }
     }
@@ -556,14 +598,22 @@ __global__ __launch_bounds__(256) void prefill_window_kernel(PrefillParams p) {
     const float2 vsg = reinterpret_cast<const float2*>(p.signs + tv)[l];
     const float2 kic = KG.sinkhorn ? reinterpret_cast<const float2*>(p.inv_c + tk)[l] : make_float2(1.0f, 1.0f);
     const float2 vic = VG.sinkhorn ? reinterpret_cast<const float2*>(p.inv_c + tv)[l] : make_float2(1.0f, 1.0f);
-    const bool vsplit = VG.scheme == kTurboSplit;
+    const bool vsplit = VG.scheme == kTurboSplit, ksplit = KG.scheme == kTurboSplit;
     const int2 pm = vsplit ? reinterpret_cast<const int2*>(p.perm + (size_t)kvh * kDim)[l] : make_int2(0, 0);
+    const int2 pmk = ksplit ? reinterpret_cast<const int2*>(p.perm_k + (size_t)kvh * kDim)[l] : make_int2(0, 0);
     const int N = p.len[b];
     for (int tok = max(0, N - kWindowMax) + wave; tok < N; tok += 4) { // wave-uniform: shuffles are safe
         const size_t r = (size_t)(tok % kWindowMax) * kDim;
         float2 k = reinterpret_cast<const float2*>(kring + r)[l];
         float2 v = reinterpret_cast<const float2*>(vring + r)[l];
-        if (KG.rotate) qdev::rotate_signed(k.x, k.y, ksg.x, ksg.y);
+        if (ksplit) {
+            const float ax = __shfl(k.x, pmk.x >> 1), ay = __shfl(k.y, pmk.x >> 1);
+            const float bx = __shfl(k.x, pmk.y >> 1), by = __shfl(k.y, pmk.y >> 1);
+            k = make_float2((pmk.x & 1) ? ay : ax, (pmk.y & 1) ? by : bx);
+            qdev::rotate64_signed(k.x, k.y, ksg.x, ksg.y);
+        } else if (KG.rotate) {
+            qdev::rotate_signed(k.x, k.y, ksg.x, ksg.y);
+        }
         if (KG.sinkhorn) {
             k.x *= kic.x;
             k.y *= kic.y;
@@ -630,7 +680,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 template <int KB, int VB>
 __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p) {
-    constexpr bool KQ = KB == kQjlK;
+    constexpr bool KQ = KB == kQjlK || split_k_kind(KB); // keys with the QJL sketch
     __shared__ __align__(16) _Float16 s_lds[kLdsHalves];
     __shared__ __align__(16) _Float16 s_vm[2][2][4][kVmRow]; // [buffer][scale | zero][group][token]
     __shared__ float s_qf[kWaves][kWaveRows];          // 2^-e of each row's q' scaling
@@ -664,11 +714,18 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
         kring = p.wring + ((size_t)b * p.Hkv + kvh) * 2 * kWindowMax * kDim;
         vring = kring + kWindowMax * kDim;
     }
-    // QJL keys: the upper half of the 3-bit codebook
-    float mgk[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (KQ) {
+    // QJL keys: the upper half of the 3-bit codebook; split keys: the upper halves of the outlier
+    // (0..3) and the rest (4..7) codebooks of N(0, 1/64)
+    float mgk[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (KB == kQjlK) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) mgk[j] = p.mu[4 + j];
+    } else if constexpr (split_k_kind(KB)) {
+        constexpr int B = split_k_bits(KB), LO = 1 << (B - 1), LR = 1 << (B - 2);
+#pragma unroll
+        for (int j = 0; j < LO / 2; ++j) mgk[j] = p.mu64[split_table_off(LO) + LO / 2 + j];
+#pragma unroll
+        for (int j = 0; j < LR / 2; ++j) mgk[4 + j] = p.mu64[split_table_off(LR) + LR / 2 + j];
     }
     // TurboQuant-MSE V: the upper half of the codebook (the lower half is its mirror image)
     float mg[12] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -696,6 +753,8 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
     {
         const float2 sgn = reinterpret_cast<const float2*>(p.signs + (size_t)(kvh * 2 + 0) * kDim)[l];
         const float2 csk = reinterpret_cast<const float2*>(p.cs + (size_t)(kvh * 2 + 0) * kDim)[l];
+        const int2 pmk = split_k_kind(KB) ? reinterpret_cast<const int2*>(p.perm_k + (size_t)kvh * kDim)[l]
+                                          : make_int2(0, 0);
         float* s_rows = reinterpret_cast<float*>(s_lds) + wave * 16 * kDim;
         for (int qb = 0; qb < kQB; ++qb) {
             for (int rr = 0; rr < 16; ++rr) {
@@ -714,7 +773,15 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
                         c = in16_to_f32(v >> 16, p.dtype);
                     }
                 }
-                if (KG.rotate) {
+                if constexpr (split_k_kind(KB)) {
+                    // the split domain: positions 2l, 2l + 1 take channels pmk (lane pmk / 2,
+                    // component pmk % 2), then the two 64-point rotations
+                    const float ax = __shfl(a, pmk.x >> 1), ay = __shfl(c, pmk.x >> 1);
+                    const float bx = __shfl(a, pmk.y >> 1), by = __shfl(c, pmk.y >> 1);
+                    a = (pmk.x & 1) ? ay : ax;
+                    c = (pmk.y & 1) ? by : bx;
+                    qdev::rotate64_signed(a, c, sgn.x, sgn.y);
+                } else if (KG.rotate) {
                     if (sgn.x < 0.0f) a = -a;
                     if (sgn.y < 0.0f) c = -c;
                     qdev::hadamard_wave(a, c);
@@ -1073,7 +1140,7 @@ bool prefill_attn_supported(const PrefillParams& p) {
     const PlaneGeom& K = p.geom[0];
     const PlaneGeom& V = p.geom[1];
     auto ok = [](const PlaneGeom& g) { return g.scheme == kUniform && (g.bits == 3 || g.bits == 4 || g.bits == 8); };
-    const bool k_qjl = K.scheme == kTurboQjl && K.bits == 3;
+    const bool k_qjl = (K.scheme == kTurboQjl && K.bits == 3) || (K.scheme == kTurboSplit && (K.bits == 3 || K.bits == 4));
     const bool v_turbo = (V.scheme == kTurboMse || V.scheme == kTurboSplit) && (V.bits == 3 || V.bits == 4);
     const bool win_ok = p.window == 0 || p.window == kWindowMax;
     return (ok(K) || k_qjl) && (ok(V) || v_turbo) && win_ok && p.G >= 1 && p.G <= kMaxGroupHeads;
@@ -1097,6 +1164,7 @@ hipError_t launch_prefill_attn(const PrefillParams& p, hipStream_t s) {
     }
     const int kb = p.geom[0].bits;
     if (p.geom[0].scheme == kTurboQjl) return launch_k<kQjlK>(p, s);
+    if (p.geom[0].scheme == kTurboSplit) return kb == 4 ? launch_k<kSplitK - 4>(p, s) : launch_k<kSplitK - 3>(p, s);
     if (kb == 3) return launch_k<3>(p, s);
     return kb == 4 ? launch_k<4>(p, s) : launch_k<8>(p, s);
 }

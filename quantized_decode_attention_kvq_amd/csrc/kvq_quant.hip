@@ -36,6 +36,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantParams p) {
     qdev::quantize_wave(p, blockIdx.z & 1, blockIdx.z >> 1, blockIdx.y, blockIdx.x * 4 + wave, rbuf[wave]);
 }
 
+// The same for one tensor only: bulk prefill of planes that have no lane-dense quantizer (the
+// split key).
+__global__ __launch_bounds__(256) void quantize_tensor_kernel(QuantParams p, int tensor) {
+    __shared__ float rbuf[4][kDim];
+    const int wave = threadIdx.x >> 6;
+    qdev::quantize_wave(p, tensor, blockIdx.z, blockIdx.y, blockIdx.x * 4 + wave, rbuf[wave]);
+}
+
 // Bulk quantizer of a split TurboQuant V plane (BO outlier bits): waves 2u and 2u + 1 of a
 // workgroup take the outlier and the rest half (NB = BO or BO - 1 code bits) of the same octets
 // (2x + u, then every 2 * gridDim.x-th after it), requesting the next octet's source before
@@ -476,6 +484,11 @@ hipError_t launch_bulk_scheme(int scheme, const QuantParams& p, hipStream_t s, i
     case kUniform: return launch_uniform_bulk_for(p.geom[tensor0], p, s, tensor0, n_tensors);
     case kTurboQjl: return launch_turbo_bulk<true>(p, s, tensor0);
     case kTurboSplit: {
+        if (tensor0 == 0) { // split key: the per-token quantizer, one wave per octet
+            hipLaunchKernelGGL(quantize_tensor_kernel, dim3((p.groups8 + 3) / 4, p.Hkv, p.batch), dim3(256), 0, s, p,
+                               0);
+            return hipGetLastError();
+        }
         const int planes = p.Hkv * p.batch;
         const int gx = std::max(1, std::min((p.groups8 + 1) / 2, (kQuantBulkBlocks + planes - 1) / planes));
         if (p.geom[tensor0].bits == 4)

@@ -238,10 +238,10 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
         ic0 = ic_l[0];
         ic1 = ic_l[1];
     }
-    // split V: this lane codes positions 2l, 2l+1, i.e. channels perm[2l], perm[2l+1]
+    // split V / K: this lane codes positions 2l, 2l+1, i.e. channels perm[2l], perm[2l+1]
     int pm0 = 0, pm1 = 0;
     if (G.scheme == kTurboSplit) {
-        const int2 pm = reinterpret_cast<const int2*>(p.perm + (size_t)head * kDim)[l];
+        const int2 pm = reinterpret_cast<const int2*>((tensor == 0 ? p.perm_k : p.perm) + (size_t)head * kDim)[l];
         pm0 = pm.x;
         pm1 = pm.y;
     }
@@ -330,6 +330,82 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
                     m[4 + g] = z16;
                 }
             }
+        } else if (G.scheme == kTurboSplit && tensor == 0) {
+            // split key (b = G.bits): the split's MSE codes -- outliers (lanes 0-31) b - 1 bits,
+            // the rest b - 2, each half its own rotation, norm and codebook -- in the K row
+            // layout, then gamma and the QJL bits of the whole residual as for a TurboQuant key
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            rbuf[2 * l] = a;
+            rbuf[2 * l + 1] = c;
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            a = rbuf[pm0];
+            c = rbuf[pm1];
+            rotate64_signed(a, c, sg0, sg1);
+            const float nsq = xor_reduce<32>(a * a + c * c, [](float x, float y) { return x + y; });
+            const uint16_t n16 = f16_rn(sqrtf(nsq));
+            const float n = f16_val(n16);
+            const float inv = (n > 0.0f) ? 1.0f / n : 0.0f;
+            const float ua = a * inv, uc = c * inv;
+            const int nb = (l < 32) ? G.bits - 1 : G.bits - 2, levels = 1 << nb;
+            const float* th = p.theta64 + split_table_off(levels);
+            uint32_t qa = 0, qc = 0;
+#pragma unroll
+            for (int k = 0; k < 7; ++k) {
+                if (k < levels - 1) {
+                    const float thk = th[k];
+                    qa += (ua > thk) ? 1u : 0u;
+                    qc += (uc > thk) ? 1u : 0u;
+                }
+            }
+            const float* mu = p.mu64 + split_table_off(levels);
+            const float pa_ = n * mu[qa], pc_ = n * mu[qc];
+            const float ra = a - pa_, rc = c - pc_;
+            // K row: group g = l / 16 (positions 32g .. 32g+31) keeps its nb planes as words
+            // starting at split_k_group_word(g, b); lane lg holds half-interleaved values lg and
+            // 16 + lg of its group
+            const int lg = l & 15, g = l >> 4;
+            const int row = k_row(t);
+            uint32_t pw[3];
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                pw[k] = or_reduce<16>((((qa >> k) & 1u) << lg) | (((qc >> k) & 1u) << (16 + lg)));
+            if (lg == 0) {
+                uint32_t* w = reinterpret_cast<uint32_t*>(codes + (size_t)row * split_k_row_bytes(G.bits)) +
+                              split_k_group_word(g, G.bits);
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    if (k < nb) w[k] = pw[k];
+            }
+            const uint16_t g16 = f16_rn(sqrtf(tree_sum_sq(ra, rc)));
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            rbuf[2 * l] = ra;
+            rbuf[2 * l + 1] = rc;
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            float acc0 = 0.0f, acc1 = 0.0f;
+            for (int j = 0; j < kDim; ++j) {
+                const float rj = rbuf[j];
+                acc0 = fmaf(p.qjl_st[j * kDim + l], rj, acc0);
+                acc1 = fmaf(p.qjl_st[j * kDim + 64 + l], rj, acc1);
+            }
+            __builtin_amdgcn_wave_barrier();
+            const uint64_t b0 = __ballot(acc0 >= 0.0f);
+            const uint64_t b1 = __ballot(acc1 >= 0.0f);
+            uint16_t* m = reinterpret_cast<uint16_t*>(meta + (size_t)row * 8);
+            if (l == 0) {
+                uint32_t* qj = reinterpret_cast<uint32_t*>(slot + G.qjl_off + (size_t)row * 16);
+                qj[0] = unshuffle32((uint32_t)b0);
+                qj[1] = unshuffle32((uint32_t)(b0 >> 32));
+                qj[2] = unshuffle32((uint32_t)b1);
+                qj[3] = unshuffle32((uint32_t)(b1 >> 32));
+                m[0] = n16;
+                m[2] = g16;
+                m[3] = 0;
+            }
+            if (l == 32) m[1] = n16;
         } else if (G.scheme == kTurboSplit) {
             // outlier split: gather the lane's two positions through the wave's LDS row, then
             // per half of the wave rho = R64(x_h), n_h = fp16(|rho|), codes = #thresholds of the

@@ -50,7 +50,7 @@ class Case:
                 torch.from_numpy(np.ascontiguousarray(self.signs)).to(device),
                 torch.from_numpy(self.S).to(device))
         self.calib = {}
-        if wl.sinkhorn_iters > 0 or wl.v_scheme == W.TURBO_SPLIT:
+        if wl.sinkhorn_iters > 0 or wl.v_scheme == W.TURBO_SPLIT or wl.k_scheme == W.TURBO_SPLIT:
             for li, layer in enumerate(self.layers):
                 kc = W.gen_calib(wl, layer, 0, device=self.gen_device).to(device)
                 vc = W.gen_calib(wl, layer, 1, device=self.gen_device).to(device)
@@ -98,11 +98,14 @@ class Case:
             c, inv_c = oracle.sinkhorn(X, kw.get("signs"), wl.sinkhorn_iters)
             kw["c"], kw["inv_c"] = c, inv_c
         if scheme == W.TURBO_SPLIT:
-            # outlier split: channels from the calibration block, codebooks of N(0, 1/64)
-            bo = wl.v_bits
-            kw["perm"] = oracle.select_outliers(self.calib[layer][1][:, head, :])
+            # outlier split: channels from the tensor's calibration block, codebooks of
+            # N(0, 1/64) -- V: bo / bo - 1 bits; K (b): b - 1 / b - 2 bits and the QJL projection
+            bo = wl.v_bits if tensor == 1 else wl.k_bits - 1
+            kw["perm"] = oracle.select_outliers(self.calib[layer][tensor][:, head, :])
             _, kw["mu"], kw["theta"], _ = _codebook64(1 << bo)
             _, kw["mu2"], kw["theta2"], _ = _codebook64(1 << (bo - 1))
+            if tensor == 0:
+                kw["S"] = self.S
         elif W.is_turbo(scheme):
             bits = wl.k_bits if tensor == 0 else wl.v_bits
             if bits == 4:  # 4-bit TurboQuant-MSE V: the 16-level codebook

@@ -69,6 +69,12 @@ def test_required_bytes_match_format():
         ns = K.kvq_cache_required_bytes(_cfg(wls))
         ps = 32 * 8 * 32768 * (144 + vb)
         assert ps <= ns <= ps + 16 * 2 ** 20
+    # split K (2.5 / 3.5 bits): 24 / 40 B split codes + 16 B QJL signs + 8 B norms and gamma,
+    # beside split V at 44 / 60 B
+    for wls, kb, vb in ((W.LLAMA8B_32K_TURBO25_KV, 48, 44), (W.LLAMA8B_32K_TURBO35_KV, 64, 60)):
+        ns = K.kvq_cache_required_bytes(_cfg(wls))
+        ps = 32 * 8 * 32768 * (kb + vb)
+        assert ps <= ns <= ps + 16 * 2 ** 20
 
 
 @pytest.mark.parametrize("over,status", [
@@ -76,8 +82,9 @@ def test_required_bytes_match_format():
     (dict(fp32_window=64), 2), (dict(n_q_heads=25), 1), (dict(n_q_heads=8 * 9), 2),
     (dict(max_batch=65), 2), (dict(max_batch=0), 1), (dict(k_scheme=2), 2), (dict(v_scheme=1), 2),
     (dict(rotate_k=2), 1), (dict(n_layers=0), 1), (dict(sinkhorn_iters=5, calib_tokens=1), 2),
-    # the outlier split is a V coder with 3 or 4 outlier bits, and needs a calibration block
-    (dict(k_scheme=4, k_bits=3), 2), (dict(v_scheme=4, v_bits=2, calib_tokens=512), 2),
+    # the outlier split takes 3 or 4 outlier bits and needs a calibration block, on either tensor
+    (dict(k_scheme=4, k_bits=3), 2), (dict(k_scheme=4, k_bits=5, calib_tokens=512), 2),
+    (dict(k_scheme=4, k_bits=2, calib_tokens=512), 2), (dict(v_scheme=4, v_bits=2, calib_tokens=512), 2),
     (dict(v_scheme=4, v_bits=5, calib_tokens=512), 2), (dict(v_scheme=4, v_bits=3, calib_tokens=0), 2),
 ])
 def test_invalid_configs_rejected(over, status):

@@ -265,3 +265,15 @@ def test_prefill_attention_f16_inputs(wl):
     # KVQ_F16 queries (and cache sources): widened exactly on load
     _say("case: prefill attention,", wl.name)
     _run(wl, n0=300, B=2, nb=1, ne=37, n_q=90, seed=16)
+
+
+@pytest.mark.parametrize("wl", [W.LLAMA8B_32K_TURBO25_KV, W.LLAMA8B_32K_TURBO35_KV,
+                                W.LLAMA8B_32K_TURBO25_KV.with_(name="llama8b-turbo2.5split-k-u4-v", v_scheme=W.UNIFORM,
+                                                               v_bits=4, rotate_v=False),
+                                W.LLAMA8B_32K_TURBO35_KV.with_(name="llama8b-turbo3.5split-kv-progressive", window=PROG)],
+                         ids=lambda w: w.name)
+def test_prefill_attention_split_keys(wl):
+    # keys at 2.5 / 3.5 bits: the unit's half picks its norm, code width and codebook, the QJL
+    # term as for TurboQuant keys; q' is the split domain of q; window tokens mapped the same way
+    _say("case: prefill attention,", wl.name)
+    _run(wl, n0=300, B=2, nb=1, ne=37, n_q=90, seed=17)

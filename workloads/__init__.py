@@ -120,10 +120,20 @@ LLAMA3B_32K_KVARN_U3 = Workload(
     "llama3b-28layer-32k-wht-sinkhorn-u3", 28, 24, 8, 1, 32768, UNIFORM, UNIFORM, 3, 3, 0,
     True, True, 5, 512, "f32", "loguniform_std", 1002)
 
+# TurboQuant's 2.5 / 3.5-bit figures are for the whole KV cache: the outlier split on both
+# tensors (K: split MSE codes + 1-bit QJL; V: split MSE codes), Llama-3.1-8B attention shape
+LLAMA8B_32K_TURBO25_KV = Workload(
+    "llama8b-32layer-32k-turbo2.5split-kv", 32, 32, 8, 1, 32768, TURBO_SPLIT, TURBO_SPLIT, 3, 3, 0,
+    True, True, 0, 512, "f32", "outliers8x8", 1006)
+LLAMA8B_32K_TURBO35_KV = Workload(
+    "llama8b-32layer-32k-turbo3.5split-kv", 32, 32, 8, 1, 32768, TURBO_SPLIT, TURBO_SPLIT, 4, 4, 0,
+    True, True, 0, 512, "f32", "outliers8x8", 1006)
+
 ALL = [LLAMA3B_3970_PROGRESSIVE, LLAMA3B_32K_KVARN, LLAMA3B_32K_TURBO, LLAMA3B_32K_TURBO_ASYM,
        LLAMA3B_128K_PROGRESSIVE, DENSE27B_120K_KVARN, DENSE27B_120K_U8, DENSE27B_120K_Q8_0,
        LLAMA3B_32K_Q8_0_TURBO_V, LLAMA3B_32K_Q8_0_TURBO4_V, LLAMA8B_32K_Q8_0_TURBO25_V,
-       LLAMA8B_32K_Q8_0_TURBO35_V, LLAMA3B_32K_U8_K_U3_V, LLAMA3B_32K_KVARN_U3]
+       LLAMA8B_32K_Q8_0_TURBO35_V, LLAMA3B_32K_U8_K_U3_V, LLAMA3B_32K_KVARN_U3, LLAMA8B_32K_TURBO25_KV,
+       LLAMA8B_32K_TURBO35_KV]
 BY_NAME = {w.name: w for w in ALL}
 
 TAGS = {"kv": 1, "calib": 2, "q": 3, "signs": 4, "qjl": 5, "chan": 6, "step": 7}
