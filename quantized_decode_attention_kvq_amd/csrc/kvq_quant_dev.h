@@ -146,6 +146,33 @@ __device__ __forceinline__ uint32_t unshuffle32(uint32_t x) {
 
 __device__ __forceinline__ int k_row(int t) { return 64 * (t / 64) + 16 * ((t % 64) % 4) + (t % 64) / 4; }
 
+// QJL projections of the residual held in the wave's LDS row r[0..127]: lane l forms
+// (S r)_l and (S r)_{64+l} as sequential fma chains over j = 0..127 (S^T stored [j][i]).  The
+// sixteen S^T loads of each 8-j step are issued together and pinned to registers before the
+// chain consumes them: left to itself, the scheduler of a register-heavy caller (the fused
+// append inside the decode kernel) waited on every load in turn.
+__device__ __forceinline__ void qjl_project(const float* __restrict__ st, const float* r, int l, float& acc0,
+                                            float& acc1) {
+    acc0 = 0.0f;
+    acc1 = 0.0f;
+    for (int j0 = 0; j0 < kDim; j0 += 8) {
+        float x[8], y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            x[u] = st[(j0 + u) * kDim + l];
+            y[u] = st[(j0 + u) * kDim + 64 + l];
+        }
+        asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]),
+                     "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3]), "v"(y[4]), "v"(y[5]), "v"(y[6]), "v"(y[7]));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float rj = r[j0 + u];
+            acc0 = fmaf(x[u], rj, acc0);
+            acc1 = fmaf(y[u], rj, acc1);
+        }
+    }
+}
+
 // Symmetric 8-bit (q8_0-style) quantizer of the two elements a lane holds: d = fp16(max|y| / 127),
 // q = rint(y * fp32(1/d)) clamped to [-127, 127], code q + 128, zero field fp16(-128 d).
 __device__ __forceinline__ void quant_sym8(float a, float b, uint32_t& c0, uint32_t& c1, uint16_t& s16,
@@ -385,12 +412,8 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
             rbuf[2 * l + 1] = rc;
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            float acc0 = 0.0f, acc1 = 0.0f;
-            for (int j = 0; j < kDim; ++j) {
-                const float rj = rbuf[j];
-                acc0 = fmaf(p.qjl_st[j * kDim + l], rj, acc0);
-                acc1 = fmaf(p.qjl_st[j * kDim + 64 + l], rj, acc1);
-            }
+            float acc0, acc1;
+            qjl_project(p.qjl_st, rbuf, l, acc0, acc1);
             __builtin_amdgcn_wave_barrier();
             const uint64_t b0 = __ballot(acc0 >= 0.0f);
             const uint64_t b1 = __ballot(acc1 >= 0.0f);
@@ -493,12 +516,8 @@ __device__ __forceinline__ void quantize_wave(const QuantParams& p, int tensor, 
                     rbuf[2 * l] = ra;
                     rbuf[2 * l + 1] = rc;
                     __builtin_amdgcn_wave_barrier();
-                    float acc0 = 0.0f, acc1 = 0.0f;
-                    for (int j = 0; j < kDim; ++j) {
-                        const float rj = rbuf[j];
-                        acc0 = fmaf(p.qjl_st[j * kDim + l], rj, acc0);
-                        acc1 = fmaf(p.qjl_st[j * kDim + 64 + l], rj, acc1);
-                    }
+                    float acc0, acc1;
+                    qjl_project(p.qjl_st, rbuf, l, acc0, acc1);
                     __builtin_amdgcn_wave_barrier();
                     const uint64_t b0 = __ballot(acc0 >= 0.0f);
                     const uint64_t b1 = __ballot(acc1 >= 0.0f);
