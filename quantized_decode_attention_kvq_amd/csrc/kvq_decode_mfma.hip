@@ -20,6 +20,11 @@
 //    <q', mu[code]> is then four dot products of q' with 0/1 bit planes (plus a constant), and
 //    the QJL term a fifth.  A bit plane enters B as a masked word (bit * 2^(k-24) for a bit at
 //    position k < 10, compensated in A); A rows are (head; q' hi, q' lo, Sq' hi, Sq' lo).
+//  * Split K (the outlier split on keys): q' is taken into the split domain (its channels gathered
+//    by the key permutation, then the two 64-point transforms); the A rows carry the outlier
+//    half's q' and the rest's separately (each zero on the other half's channels), so one product
+//    with a bit plane yields both halves' sums, which take their own norms; the outliers' top
+//    plane (and at 3.5 bits their parity monomial) and the QJL term are the remaining products.
 //  * Online softmax in the log2 domain (q' carries softmax_scale * log2(e) and a per-head power
 //    of two that keeps 16 q' inside fp16 range).
 //  * PV: A = p * (scale_g | -n * a_p) as fp16 hi (rows 0-7) + scaled lo (rows 8-15), staged
@@ -49,9 +54,10 @@ constexpr int kPWave = 4 * 16 * kPRow;    // halves per wave: [group | plane][16
 constexpr float kKappa = 0.0097915166977774f; // sqrt(pi/2) / 128
 // cache kinds (template parameters)
 // uniform 4-bit, uniform 8-bit, TurboQuant 3-bit, TurboQuant-MSE 4-bit (V only), the split
-// TurboQuant-MSE V with 3 / 4 bits on the outlier half (2.5 / 3.5 bits per channel), and uniform
-// 3-bit (bit planes in the TurboQuant 3-bit layout, uniform scale / zero)
-constexpr int kU4 = 0, kU8 = 1, kTb = 2, kTb4 = 3, kTs3 = 4, kTs4 = 5, kU3 = 6;
+// TurboQuant-MSE V with 3 / 4 bits on the outlier half (2.5 / 3.5 bits per channel), uniform
+// 3-bit (bit planes in the TurboQuant 3-bit layout, uniform scale / zero), and the split key
+// at b = 3 / 4 (b - 1 bits on the outliers, b - 2 on the rest, plus the QJL sketch; K only)
+constexpr int kU4 = 0, kU8 = 1, kTb = 2, kTb4 = 3, kTs3 = 4, kTs4 = 5, kU3 = 6, kSk3 = 7, kSk4 = 8;
 
 // Eight one-bit operands from a half-interleaved word: quarter q (0..3) of each half, i.e. bits
 // 4q + v and 16 + 4q + v (v = 0..3).  Operand 2v + h is that bit times 2^(4(q%2) + v - 24).
@@ -141,6 +147,18 @@ template <>
 struct KRegs<kTb> {
     uint32_t pw[4][3], qw[4], nm[4];
 };
+// split K: the plane words of group lane / 16 (b - 1 on the outlier groups 0, 1, b - 2 on the
+// others, unused words zero), QJL word lane / 16, and the row's (n_outlier | n_rest, gamma | 0)
+template <>
+struct KRegs<kSk3> {
+    uint32_t pw[4][3], qw[4];
+    uint2 nm[4];
+};
+template <>
+struct KRegs<kSk4> {
+    uint32_t pw[4][3], qw[4];
+    uint2 nm[4];
+};
 // uniform 3-bit K: the three plane words of group lane / 16 and the 16-byte meta row
 template <>
 struct KRegs<kU3> {
@@ -183,7 +201,7 @@ struct VRegs<kTs4> {
 };
 
 // Coefficients of a b-bit odd-symmetric codebook as a sum over the odd monomials of the code's
-// +-1 bits (b = 2: b0, b1; b = 3: b0, b1, b2, b0b1b2; b = 4: b0, b1, b2, b3, b0b1b2, b0b1b3,
+// +-1 bits (b = 1: b0; b = 2: b0, b1; b = 3: b0, b1, b2, b0b1b2; b = 4: b0, b1, b2, b3, b0b1b2, b0b1b3,
 // b0b2b3, b1b2b3): a_S = mean over the upper half of mu[c] prod_S b (the top bit is 1 there).
 template <int B>
 __device__ __forceinline__ void odd_coeffs(const float* mu, float* a) {
@@ -194,7 +212,9 @@ __device__ __forceinline__ void odd_coeffs(const float* mu, float* a) {
     for (int c = H; c < 2 * H; ++c) {
         const float m = mu[c];
         const float b0 = (c & 1) ? 1.0f : -1.0f, b1 = (c & 2) ? 1.0f : -1.0f, b2 = (c & 4) ? 1.0f : -1.0f;
-        if constexpr (B == 2) {
+        if constexpr (B == 1) {
+            a[0] += m;
+        } else if constexpr (B == 2) {
             a[0] += m * b0;
             a[1] += m;
         } else if constexpr (B == 3) {
@@ -240,7 +260,10 @@ __device__ __forceinline__ f4 pv_planes(const h8* Pg, const uint32_t* w, int q, 
 
 template <int KT, int VT, int MB, int kNW>
 __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
-    constexpr bool KU = KT != kTb, VU = VT == kU4 || VT == kU8 || VT == kU3, VT4 = VT == kTb4;
+    // K kinds: uniform (4 / 8 / 3-bit codes), TurboQuant-QJL, split (outlier / rest codes + QJL)
+    constexpr bool KQ = KT == kTb, KS = KT == kSk3 || KT == kSk4, KU = !KQ && !KS;
+    constexpr int kKb = KT == kSk4 ? 4 : 3; // split K: b (outliers b - 1 bits, the rest b - 2)
+    constexpr bool VU = VT == kU4 || VT == kU8 || VT == kU3, VT4 = VT == kTb4;
     constexpr bool VS = VT == kTs3 || VT == kTs4;
     constexpr bool K3 = KT == kU3, V3 = VT == kU3; // uniform 3-bit planes
     constexpr int KB = KT == kU4 ? 4 : 8, VB = VT == kU4 ? 4 : (V3 ? 3 : 8);
@@ -321,11 +344,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     }
     const float2 sgn = reinterpret_cast<const float2*>(p.signs + (size_t)(kvh * 2 + 0) * kDim)[l];
     const float2 csk = reinterpret_cast<const float2*>(p.cs + (size_t)(kvh * 2 + 0) * kDim)[l];
+    int2 pmk = make_int2(0, 0);
+    if constexpr (KS) pmk = reinterpret_cast<const int2*>(p.perm_k + (size_t)kvh * kDim)[l];
     // TurboQuant tables: centroids 4..7, and this thread's slice of S^T (stored [j][i]) for S q'
     constexpr int kParts = kNW * 64 / kDim, kJ = kDim / kParts;
     float mu4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float st[KU ? 1 : kJ];
-    if constexpr (!KU || VT == kTb) {
+    if constexpr (KQ || VT == kTb) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) mu4[c] = p.mu[4 + c];
     }
@@ -364,6 +389,18 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
                 for (int u = 0; u < KB / 4; ++u) kr.kc[j][u] = *reinterpret_cast<const u4*>(c + 16 * u);
                 kr.km[j] = *reinterpret_cast<const u4*>(kmeta + (r0 + 16 * j) * 16);
+            }
+        } else if constexpr (KS) {
+            // group lq's planes start at word split_k_group_word(lq, b) of the row
+            const int nbk = lq < 2 ? kKb - 1 : kKb - 2;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t* c = reinterpret_cast<const uint32_t*>(kcodes + (r0 + 16 * j) * split_k_row_bytes(kKb)) +
+                                    split_k_group_word(lq, kKb);
+#pragma unroll
+                for (int k = 0; k < 3; ++k) kr.pw[j][k] = (k < nbk) ? c[k] : 0u;
+                kr.qw[j] = *reinterpret_cast<const uint32_t*>(kqjl + (r0 + 16 * j) * 16 + 4 * lq);
+                kr.nm[j] = *reinterpret_cast<const uint2*>(kmeta + (r0 + 16 * j) * 8);
             }
         } else {
 #pragma unroll
@@ -438,7 +475,15 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
         float a = qa[i], c = qc[i];
         s_qw[h][2 * l] = a * p.qscale;
         s_qw[h][2 * l + 1] = c * p.qscale;
-        if (KG.rotate) {
+        if constexpr (KS) {
+            // the split domain: positions 2l, 2l+1 take channels perm_k[2l], perm_k[2l+1] (lane
+            // pm / 2, component pm % 2), then signs by position and the two 64-point transforms
+            const float ax = __shfl(a, pmk.x >> 1), ay = __shfl(c, pmk.x >> 1);
+            const float bx = __shfl(a, pmk.y >> 1), by = __shfl(c, pmk.y >> 1);
+            a = (pmk.x & 1) ? ay : ax;
+            c = (pmk.y & 1) ? by : bx;
+            qdev::rotate64_signed(a, c, sgn.x, sgn.y);
+        } else if (KG.rotate) {
             if (sgn.x < 0.0f) a = -a;
             if (sgn.y < 0.0f) c = -c;
             hadamard_wave(a, c, l);
@@ -528,7 +573,17 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
         odd_coeffs<kBo>(p.mu64 + ((1 << kBo) - 4), aO);
         odd_coeffs<kBo - 1>(p.mu64 + ((1 << (kBo - 1)) - 4), aR);
     }
-    if constexpr (!KU || !(VU || VT4 || VS)) {
+    // split K: the outlier (b - 1 bits) and rest (b - 2 bits) codebooks of N(0, 1/64)
+    float aKO[KS ? (1 << (kKb - 2)) : 1], aKR[KS ? (1 << (kKb - 3)) : 1], aKOs = 0.0f, aKRs = 0.0f;
+    if constexpr (KS) {
+        odd_coeffs<kKb - 1>(p.mu64 + split_table_off(1 << (kKb - 1)), aKO);
+        odd_coeffs<kKb - 2>(p.mu64 + split_table_off(1 << (kKb - 2)), aKR);
+#pragma unroll
+        for (int k = 0; k < (1 << (kKb - 2)); ++k) aKOs += aKO[k];
+#pragma unroll
+        for (int k = 0; k < (1 << (kKb - 3)); ++k) aKRs += aKR[k];
+    }
+    if constexpr (KQ || VT == kTb) {
         const float m4 = mu4[0], m5 = mu4[1], m6 = mu4[2], m7 = mu4[3];
         al[0] = 0.25f * ((m5 - m4) + (m7 - m6));
         al[1] = 0.25f * ((m6 - m4) + (m7 - m5));
@@ -567,9 +622,12 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
         // uniform K: Ahi/Alo[mb][g] = (head, group) rows of q' (fp16 hi / lo), zero outside g.
         // TurboQuant K: At[mb][s] rows (head 4mb + lr/4; q' hi, q' lo, Sq' hi, Sq' lo), k-slice s
         // = channels 32*lq + 8s + 0..7, pre-scaled by 2^-(4(s%2) + i/2) for the bit operands.
+        // split K: At rows (head 4mb + lr/4; q'_O hi, q'_O lo, q'_R hi, q'_R lo) -- each half's
+        // rows zero on the other half's channels, so one bit-plane product yields both halves'
+        // sums -- and AtS rows (Sq' hi, Sq' lo, 0, 0) for the QJL term, with the same pre-scaling.
         constexpr int NA = KU ? 4 : 1;
-        h8 Ahi[MB][NA], Alo[MB][NA], At[MB][KU ? 1 : 4];
-        float qs_l[MB][4], F[MB], cQ[MB], cS[MB];
+        h8 Ahi[MB][NA], Alo[MB][NA], At[MB][KU ? 1 : 4], AtS[MB][KS ? 4 : 1];
+        float qs_l[MB][4], F[MB], cQ[MB], cS[MB], cQR[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int hs = min(4 * mb + lq, G - 1); // score-layout head of this lane
@@ -617,6 +675,31 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) qs_l[mb][g] = s_qsum[hs][g] * (1.0f / UK);
                 F[mb] = UK * s_qfac[hs];
+            } else if constexpr (KS) {
+                const int h = 4 * mb + (lr >> 2), v = lr & 3;
+                const int hc = min(h, G - 1);
+                const bool mine = (v < 2) == (lq < 2); // outlier rows on channels < 64, rest rows above
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    h8 a, as;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int c = 32 * lq + 8 * s + i;
+                        const float sc = __uint_as_float((uint32_t)(127 - 4 * (s & 1) - (i >> 1)) << 23);
+                        const float x = (h < G && mine) ? s_q[hc][c] * sc : 0.0f;
+                        const _Float16 xh = (_Float16)x;
+                        a[i] = (v & 1) ? (_Float16)((x - (float)xh) * kLoScale) : xh;
+                        const float y = (h < G && v < 2) ? s_sp[hc][c] * sc : 0.0f;
+                        const _Float16 yh = (_Float16)y;
+                        as[i] = (v & 1) ? (_Float16)((y - (float)yh) * kLoScale) : yh;
+                    }
+                    At[mb][s] = a;
+                    AtS[mb][s] = as;
+                }
+                cQ[mb] = aKOs * (s_qsum[hs][0] + s_qsum[hs][1]) * 5.9604644775390625e-8f; // 2^-24
+                cQR[mb] = aKRs * (s_qsum[hs][2] + s_qsum[hs][3]) * 5.9604644775390625e-8f;
+                cS[mb] = s_spsum[hs] * 5.9604644775390625e-8f;
+                F[mb] = 16777216.0f * s_qfac[hs];
             } else {
                 const int h = 4 * mb + (lr >> 2), v = lr & 3;
                 const int hc = min(h, G - 1);
@@ -680,6 +763,48 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                         r = fmaf(hi_h(km[j].z), qs_l[mb][1], r);
                         r = fmaf(lo_h(km[j].w), qs_l[mb][2], r);
                         r = fmaf(hi_h(km[j].w), qs_l[mb][3], r);
+                        raw[mb][j] = valid ? r : kNegInf;
+                    }
+                } else if constexpr (KS) {
+                    // planes 0 .. b - 3 exist in both halves (one product gives the outlier sum in
+                    // rows 0, 1 and the rest's in rows 2, 3); the outliers' top plane (and at b = 4
+                    // their parity monomial b0 b1 b2) only in lanes of groups 0, 1
+                    constexpr int NP = kKb == 3 ? 2 : 4;
+                    const uint32_t P0 = kr.pw[j][0], P1 = kr.pw[j][1], P2 = kr.pw[j][2];
+                    const uint32_t W[4] = {P0, P1, P2, lq < 2 ? (P0 ^ P1 ^ P2) : 0u};
+                    f4 D[MB][NP + 1];
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int k = 0; k <= NP; ++k) D[mb][k] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        h8 B[NP];
+#pragma unroll
+                        for (int k = 0; k < NP; ++k) B[k] = as_h8(bits8(W[k], s));
+                        const h8 BQ = as_h8(bits8(kr.qw[j], s));
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+                            for (int k = 0; k < NP; ++k) D[mb][k] = mfma16(At[mb][s], B[k], D[mb][k]);
+                            D[mb][NP] = mfma16(AtS[mb][s], BQ, D[mb][NP]);
+                        }
+                    }
+                    const float nO = lo_h(kr.nm[j].x), nR = hi_h(kr.nm[j].x), gam = lo_h(kr.nm[j].y);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        // outlier monomials: b0, b1 (b = 3); b0, b1, b2, b0 b1 b2 (b = 4); the rest:
+                        // b0 (b = 3); b0, b1 (b = 4)
+                        float mo = 0.0f, mr = 0.0f;
+#pragma unroll
+                        for (int k = 0; k < (1 << (kKb - 2)); ++k)
+                            mo = fmaf(aKO[k], fmaf(D[mb][k][1], kLoInv, D[mb][k][0]), mo);
+#pragma unroll
+                        for (int k = 0; k < (1 << (kKb - 3)); ++k)
+                            mr = fmaf(aKR[k], fmaf(D[mb][k][3], kLoInv, D[mb][k][2]), mr);
+                        const float qj = fmaf(D[mb][NP][1], kLoInv, D[mb][NP][0]);
+                        float r = fmaf(nO, fmaf(2.0f, mo, -cQ[mb]), nR * fmaf(2.0f, mr, -cQR[mb]));
+                        r = fmaf(gam * kKappa, fmaf(2.0f, qj, -cS[mb]), r);
                         raw[mb][j] = valid ? r : kNegInf;
                     }
                 } else {
@@ -1058,7 +1183,8 @@ hipError_t launch_v(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEve
 bool mfma_path_supported(const DecodeParams& p) {
     const PlaneGeom& K = p.geom[0];
     const PlaneGeom& V = p.geom[1];
-    const bool k_ok = (K.scheme == kUniform && (K.bits == 3 || K.bits == 4 || K.bits == 8)) || K.scheme == kTurboQjl;
+    const bool k_ok = (K.scheme == kUniform && (K.bits == 3 || K.bits == 4 || K.bits == 8)) || K.scheme == kTurboQjl ||
+                      (K.scheme == kTurboSplit && (K.bits == 3 || K.bits == 4));
     const bool v_ok = (V.scheme == kUniform && (V.bits == 3 || V.bits == 4 || V.bits == 8)) || V.scheme == kTurboMse ||
                       (V.scheme == kTurboSplit && (V.bits == 3 || V.bits == 4));
     return k_ok && v_ok && p.G <= kMaxGroupHeads;
@@ -1066,6 +1192,7 @@ bool mfma_path_supported(const DecodeParams& p) {
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const PlaneGeom& K = p.geom[0];
+    if (K.scheme == kTurboSplit) return K.bits == 4 ? launch_v<kSk4>(p, s, ev0, ev1) : launch_v<kSk3>(p, s, ev0, ev1);
     if (K.scheme != kUniform) return launch_v<kTb>(p, s, ev0, ev1);
     if (K.bits == 3) return launch_v<kU3>(p, s, ev0, ev1);
     return K.bits == 4 ? launch_v<kU4>(p, s, ev0, ev1) : launch_v<kU8>(p, s, ev0, ev1);

@@ -101,6 +101,11 @@ def test_fullsize_llama8b_32k_turbo_split_v(wl):
     _run(wl, layers=[0, 31], seqs=[0], plane_heads=[0, 4, 7], attn_heads=[0, 4, 7])
 
 
+@pytest.mark.parametrize("wl", [W.LLAMA8B_32K_TURBO25_KV, W.LLAMA8B_32K_TURBO35_KV], ids=lambda w: w.name)
+def test_fullsize_llama8b_32k_turbo_split_kv(wl):
+    _run(wl, layers=[0, 31], seqs=[0], plane_heads=[0, 4, 7], attn_heads=[0, 4, 7])
+
+
 def _fused_steps(wl, layers, seqs, heads, batch=None):
     """kvq_append_attn_decode, the call bench.py times, at the workload's full context: one step
     on the matrix-core path (the automatic choice, with the automatic split plan) and one on the

@@ -36,8 +36,6 @@ def _check_all_planes(case, li, heads=None, seqs=None):
 
 
 def _paths(wl):
-    if wl.k_scheme == W.TURBO_SPLIT:
-        return (1,)  # split keys decode on the vector ALU only
     return (1, 2)  # vector-ALU kernel, matrix-core kernel
 
 
@@ -684,15 +682,17 @@ def test_f16_inputs_planes_and_decode(wl):
 SPLIT_KV = [W.LLAMA8B_32K_TURBO25_KV, W.LLAMA8B_32K_TURBO35_KV,
             W.LLAMA8B_32K_TURBO25_KV.with_(name="llama8b-turbo2.5split-k-u4-v", v_scheme=W.UNIFORM, v_bits=4,
                                            rotate_v=False),
-            W.LLAMA8B_32K_TURBO35_KV.with_(name="llama8b-turbo3.5split-k-progressive", window=128)]
+            W.LLAMA8B_32K_TURBO35_KV.with_(name="llama8b-turbo3.5split-k-progressive", window=128),
+            W.LLAMA8B_32K_TURBO25_KV.with_(name="llama8b-turbo2.5split-kv-g5", n_q_heads=40),
+            W.LLAMA8B_32K_TURBO35_KV.with_(name="llama8b-turbo3.5split-k-turbomse-v-bf16", v_scheme=W.TURBO_MSE,
+                                           v_bits=3, dtype="bf16")]
 
 
 @pytest.mark.parametrize("wl", SPLIT_KV, ids=lambda w: w.name)
 def test_split_keys_planes_and_decode(wl):
     # keys at 2.5 / 3.5 bits (split MSE codes + QJL): bulk prefill (the per-token quantizer for the
-    # key plane), appends and a fused step leave the oracle's bytes, and decode (vector ALU) meets
-    # the oracle's split-key score; the matrix-core path refuses these keys
-    import quantized_decode_attention_kvq_amd as K
+    # key plane), appends and a fused step (matrix-core path) leave the oracle's bytes, and both
+    # decode paths meet the oracle's split-key score
     _say("case:", wl.name, "2 seqs, 300 prefill + 20 appends + 1 fused step")
     case = Case(wl, 321, layers=[0], batch=2)
     k, v = case.kv(0)
@@ -714,9 +714,4 @@ def test_split_keys_planes_and_decode(wl):
         r, m = rel_l2(out.cpu().numpy()[b], ref), max_abs(out.cpu().numpy()[b], ref)
         _say(f"  fused step seq {b}: rel_l2={r:.2e} max_abs={m:.2e}")
         assert r <= REL_L2_TOL and m <= MAX_ABS_TOL, (b, r, m)
-    _decode_and_compare(case, 0, planes)
-    case.cache.set_option(2, 2)
-    with pytest.raises(K.KvqError) as e:
-        case.cache.attn_decode(0, q, out)
-    assert e.value.name == "KVQ_ERR_UNSUPPORTED"
-    case.cache.set_option(2, 0)
+    _decode_and_compare(case, 0, planes)  # both decode paths
