@@ -116,10 +116,10 @@ __device__ __forceinline__ h8 centred3x8(uint32_t p0, uint32_t p1, uint32_t p2, 
 // word: operand 2v + h comes from bit 16h + 4q + v.
 __device__ __forceinline__ u4 pm1x8(uint32_t w, int q) {
     u4 r;
-    r.x = ((w << (15 - 4 * q)) & 0x80008000u) | 0x3C003C00u;
-    r.y = ((w << (14 - 4 * q)) & 0x80008000u) | 0x3C003C00u;
-    r.z = ((w << (13 - 4 * q)) & 0x80008000u) | 0x3C003C00u;
-    r.w = ((w << (12 - 4 * q)) & 0x80008000u) | 0x3C003C00u;
+    r.x = and_or(w << (15 - 4 * q), 0x80008000u, 0x3C003C00u);
+    r.y = and_or(w << (14 - 4 * q), 0x80008000u, 0x3C003C00u);
+    r.z = and_or(w << (13 - 4 * q), 0x80008000u, 0x3C003C00u);
+    r.w = and_or(w << (12 - 4 * q), 0x80008000u, 0x3C003C00u);
     return r;
 }
 

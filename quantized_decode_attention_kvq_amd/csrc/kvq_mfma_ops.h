@@ -27,6 +27,16 @@ __device__ __forceinline__ float c0f() { return __uint_as_float(0x3DB504F3u); }
 __device__ __forceinline__ float lo_h(uint32_t w) { return (float)__builtin_bit_cast(h2v, w)[0]; }
 __device__ __forceinline__ float hi_h(uint32_t w) { return (float)__builtin_bit_cast(h2v, w)[1]; }
 
+// (x & m) | c as one v_and_or_b32.  Written plainly, the compiler emits an AND and an OR, each
+// with its own literal (a three-operand instruction takes no literal on this architecture), so
+// the operand builders below that mask code bits and set an fp16 exponent cost two instructions
+// per word instead of one.  m is a wave-uniform constant (scalar register), c a vector register.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+    return r;
+}
+
 // 4-bit word (channel/token i at bit 16*(i%2) + 4*(i/2)) -> 8 fp16 subnormal operands in
 // natural order, slots 2,3,6,7 carry an extra factor 16.
 __device__ __forceinline__ u4 unpack4(uint32_t x) {
@@ -59,11 +69,11 @@ __device__ __forceinline__ uint32_t h2sub(uint32_t x, _Float16 c) {
 }
 __device__ __forceinline__ u4 centred4(uint32_t x) {
     u4 r;
-    r.x = h2sub((x & 0x000F000Fu) | 0x64006400u, (_Float16)1032.0f);
-    r.y = h2sub((x & 0x00F000F0u) | 0x64006400u, (_Float16)1152.0f);
+    r.x = h2sub(and_or(x, 0x000F000Fu, 0x64006400u), (_Float16)1032.0f);
+    r.y = h2sub(and_or(x, 0x00F000F0u, 0x64006400u), (_Float16)1152.0f);
     const uint32_t y = x >> 8;
-    r.z = h2sub((y & 0x000F000Fu) | 0x64006400u, (_Float16)1032.0f);
-    r.w = h2sub((y & 0x00F000F0u) | 0x64006400u, (_Float16)1152.0f);
+    r.z = h2sub(and_or(y, 0x000F000Fu, 0x64006400u), (_Float16)1032.0f);
+    r.w = h2sub(and_or(y, 0x00F000F0u, 0x64006400u), (_Float16)1152.0f);
     return r;
 }
 __device__ __forceinline__ u4 centred8(uint32_t x0, uint32_t x1) {
