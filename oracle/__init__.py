@@ -86,6 +86,13 @@ def lib():
                                             _F, _U8, _U16, _U16, _U8, _F]
         L.orc_tree_sum_sq.restype = ctypes.c_float
         L.orc_tree_sum_sq.argtypes = [_F]
+        L.orc_stream_key.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.orc_stream_key.restype = ctypes.c_uint64
+        L.orc_stream_draw.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        L.orc_stream_draw.restype = ctypes.c_uint64
+        L.orc_box_muller.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+        L.orc_box_muller.restype = ctypes.c_double
+        L.orc_derive_tables.argtypes = [ctypes.c_uint64, ctypes.c_int, ctypes.c_int, _F, _F]
         L.orc_lloyd_max_dim.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _Dp, _F, _F, _Dp]
         L.orc_rotate64_f32.argtypes = [_F, _F, _F]
         L.orc_unrotate64_f64.argtypes = [_Dp, _F, _Dp]
@@ -406,3 +413,24 @@ def attention_prefix(kplane: Plane, vplane: Plane, ktables: TableSet, vtables: T
                                _p(vplane.ring, _F), kplane.length, int(n_vis), G, _p(q, _F), scale,
                                _p(out, _Dp))
     return out
+
+
+# ---- seeded random tables (counter-based SplitMix64 + Box-Muller; see kvq_oracle.c) ----------
+def stream_key(seed: int, tag: int, layer: int, head: int, tensor: int) -> int:
+    return int(lib().orc_stream_key(seed, tag, layer, head, tensor))
+
+
+def stream_draw(key: int, i: int) -> int:
+    return int(lib().orc_stream_draw(key, i))
+
+
+def box_muller(x1: int, x2: int) -> float:
+    return float(lib().orc_box_muller(x1, x2))
+
+
+def derive_random_tables(seed: int, n_layers: int, n_kv_heads: int):
+    """(signs [n_layers][n_kv_heads][2][128] of +-1, S [128][128]) float32 from a 64-bit seed."""
+    signs = np.zeros((n_layers, n_kv_heads, 2, D), np.float32)
+    S = np.zeros((D, D), np.float32)
+    lib().orc_derive_tables(seed, n_layers, n_kv_heads, _p(signs, _F), _p(S, _F))
+    return signs, S

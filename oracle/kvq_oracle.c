@@ -1123,3 +1123,61 @@ void orc_attention(const orc_plane_cfg* kc, const orc_plane_cfg* vc, const orc_t
     orc_attention_prefix(kc, vc, ktb, vtb, kcodes, kmeta, kqjl, kring, vcodes, vmeta, vring, n, n,
                          G, q, scale, out);
 }
+
+/* ---- Seeded random tables --------------------------------------------------------------------
+ * The pages draw a random-sign Walsh-Hadamard rotation (KVarN post, TL;DR; the TurboQuant row of
+ * "LLM memory saving ... 2026", method comparison table) and a Gaussian projection for the QJL
+ * sketch (same row) without naming a generator.  Reading: SplitMix64 (Steele, Lea and Flood,
+ * "Fast splittable pseudorandom number generators", OOPSLA 2014) used counter-style.  Its
+ * generator adds the odd constant gamma to a 64-bit state and returns the state passed through
+ * a fixed mixing function; so the (i + 1)-th output from state k is mix(k + (i + 1) gamma), and
+ * every draw can be computed on its own.  Stream keys chain mix over the fields. */
+static const uint64_t SM_GAMMA = 0x9E3779B97F4A7C15ull;
+
+static uint64_t sm_mix(uint64_t z)
+{
+    z ^= z >> 30;
+    z *= 0xBF58476D1CE4E5B9ull;
+    z ^= z >> 27;
+    z *= 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z;
+}
+
+uint64_t orc_stream_key(uint64_t seed, int tag, int layer, int head, int tensor)
+{
+    uint64_t k = sm_mix(seed + SM_GAMMA * (uint64_t)(tag + 1));
+    k = sm_mix(k + SM_GAMMA * (uint64_t)(layer + 1));
+    k = sm_mix(k + SM_GAMMA * (uint64_t)(head + 1));
+    return sm_mix(k + SM_GAMMA * (uint64_t)(tensor + 1));
+}
+
+uint64_t orc_stream_draw(uint64_t key, uint64_t i) { return sm_mix(key + SM_GAMMA * (i + 1)); }
+
+double orc_box_muller(uint64_t x1, uint64_t x2)
+{
+    const double two_to_m53 = 1.0 / 9007199254740992.0; /* 2^-53 */
+    double u1 = (double)((x1 >> 11) + 1) * two_to_m53;   /* (0, 1]: log never sees 0 */
+    double u2 = (double)(x2 >> 11) * two_to_m53;         /* [0, 1) */
+    double r = sqrt(-2.0 * log(u1));
+    double c = cos(6.283185307179586 * u2);              /* 2 pi rounded to binary64 */
+    return r * c;
+}
+
+void orc_derive_tables(uint64_t seed, int n_layers, int n_kv_heads, float* signs, float* S)
+{
+    if (signs) {
+        for (int l = 0; l < n_layers; l++)
+            for (int h = 0; h < n_kv_heads; h++)
+                for (int t = 0; t < 2; t++) {
+                    uint64_t key = orc_stream_key(seed, 1, l, h, t);
+                    float* out = signs + (((size_t)l * n_kv_heads + h) * 2 + t) * D;
+                    for (int j = 0; j < D; j++) out[j] = (orc_stream_draw(key, (uint64_t)j) >> 63) ? -1.0f : 1.0f;
+                }
+    }
+    if (S) {
+        uint64_t key = orc_stream_key(seed, 2, 0, 0, 0);
+        for (int k = 0; k < D * D; k++)
+            S[k] = (float)orc_box_muller(orc_stream_draw(key, 2 * (uint64_t)k), orc_stream_draw(key, 2 * (uint64_t)k + 1));
+    }
+}

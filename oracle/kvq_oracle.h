@@ -169,6 +169,19 @@ void orc_attention(const orc_plane_cfg* kc, const orc_plane_cfg* vc, const orc_t
                    const uint8_t* vmeta, const float* vring, int n, int G, const float* q,
                    double scale, double* out);
 
+/* Seeded random tables (the pages draw a random-sign rotation and a Gaussian QJL projection but
+ * name no generator; this is the stated reading).  Counter-based SplitMix64: a stream key chains
+ * the SplitMix64 output function over (seed, tag, layer, head, tensor); draw i of a stream is
+ * the (i + 1)-th output of a SplitMix64 generator started at the key. */
+uint64_t orc_stream_key(uint64_t seed, int tag, int layer, int head, int tensor);
+uint64_t orc_stream_draw(uint64_t key, uint64_t i);
+/* Box-Muller in binary64 from two 64-bit draws: u1 = ((x1 >> 11) + 1) 2^-53 in (0, 1],
+ * u2 = (x2 >> 11) 2^-53 in [0, 1), z = sqrt(-2 ln u1) cos(2 pi u2). */
+double orc_box_muller(uint64_t x1, uint64_t x2);
+/* signs [n_layers][n_kv_heads][2][128] = +-1 (tag 1, bit 63 of draw j set -> -1) and
+ * S [128][128] = fp32 of Box-Muller over draws 2k, 2k + 1 of the tag-2 stream, k = 128 i + j. */
+void orc_derive_tables(uint64_t seed, int n_layers, int n_kv_heads, float* signs, float* S);
+
 #ifdef __cplusplus
 }
 #endif
