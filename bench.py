@@ -86,14 +86,26 @@ def step_driver(cache, wl: W.Workload, step_in, qs, out, stream, fused=True):
     return run
 
 
+# The sources the split-K decode kernel is compiled from (its unit and the headers it includes).
+DECODE_SOURCES = ["kvq_decode_mfma.hip", "kvq_internal.h", "kvq_lanes.h", "kvq_mfma_ops.h", "kvq_quant_dev.h"]
+
+
+def decode_source_sha() -> str:
+    """sha256 over the decode kernel's sources, concatenated in DECODE_SOURCES order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "quantized_decode_attention_kvq_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_record(wl: W.Workload):
     """HBM bytes per launch of the split-K kernel measured with rocprofv3 --pmc (FETCH_SIZE and
     WRITE_SIZE, scaled by the copy-probe factors) and recorded under profiles/, valid only while
-    the kernel source has the recorded sha256; None otherwise."""
+    the kernel's sources have the recorded sha256 (decode_source_sha); None otherwise."""
     import glob
-    import hashlib
-    src = os.path.join(ROOT, "quantized_decode_attention_kvq_amd", "csrc", "kvq_decode_mfma.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = decode_source_sha()
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         for line in open(path):
             if line.startswith("traffic_record "):
@@ -119,9 +131,9 @@ def prefill_report(wl: W.Workload, prefill_s):
 
 def split_kernel_name(wl: W.Workload) -> str:
     """The split-K decode kernel the library launches for this cache (matrix-core path)."""
-    kind = lambda scheme, bits: (f"Ts{bits}" if scheme == W.TURBO_SPLIT else  # noqa: E731
-                                 ("Tb4" if bits == 4 else "Tb") if W.is_turbo(scheme) else f"U{bits}")
-    return (f"decode_mfma_kernel (K {kind(wl.k_scheme, wl.k_bits)}, V {kind(wl.v_scheme, wl.v_bits)}, "
+    kind = lambda scheme, bits, t: ((f"Sk{bits}" if t == 0 else f"Ts{bits}") if scheme == W.TURBO_SPLIT else  # noqa: E731
+                                    ("Tb4" if bits == 4 else "Tb") if W.is_turbo(scheme) else f"U{bits}")
+    return (f"decode_mfma_kernel (K {kind(wl.k_scheme, wl.k_bits, 0)}, V {kind(wl.v_scheme, wl.v_bits, 1)}, "
             f"{wl.group} query heads per kv head)")
 
 
@@ -136,7 +148,7 @@ def build_cache(wl: W.Workload, extra: int, log, keep_first: bool = True):
     stream = torch.cuda.current_stream()
     pre = []  # (start, end) events around each layer's bulk prefill on the launch stream
     for layer in range(wl.n_layers):
-        if wl.sinkhorn_iters > 0 or wl.v_scheme == W.TURBO_SPLIT:
+        if wl.sinkhorn_iters > 0 or wl.v_scheme == W.TURBO_SPLIT or wl.k_scheme == W.TURBO_SPLIT:
             cache.calibrate(layer, W.gen_calib(wl, layer, 0, device="cuda"),
                             W.gen_calib(wl, layer, 1, device="cuda"))
         k = W.gen_kv(wl, layer, 0, device="cuda")
@@ -414,6 +426,11 @@ def measure(wl: W.Workload, cache, prefill_s, steps: int, warmup: int, fused: bo
 # measured, freed) after the headline, in the same JSON line.
 LONG_CONTEXT = [W.LLAMA3B_128K_PROGRESSIVE, W.LLAMA3B_128K_PROGRESSIVE.with_(batch=8),
                 W.DENSE27B_120K_KVARN, W.DENSE27B_120K_U8]
+# The other 32K caches: the TurboQuant cache (QJL keys, 4-bit values) and its asymmetric variants
+# (8-bit keys with TurboQuant-MSE or uniform 3-bit values), and the whole cache at 2.5 / 3.5 bits
+# by the outlier split on both tensors.
+OTHER_32K = [W.LLAMA3B_32K_TURBO, W.LLAMA3B_32K_TURBO_ASYM, W.LLAMA3B_32K_U8_K_U3_V,
+             W.LLAMA8B_32K_TURBO25_KV, W.LLAMA8B_32K_TURBO35_KV]
 
 
 def gpu_info():
@@ -436,7 +453,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-context", action="store_true",
-                    help="only the headline workload (skip the 128K / 120K lines)")
+                    help="only the headline workload (skip the 128K / 120K and other 32K lines)")
     ap.add_argument("--separate", action="store_true",
                     help="kvq_append + kvq_attn_decode per layer instead of kvq_append_attn_decode")
     ap.add_argument("--copy-probe", action="store_true",
@@ -472,14 +489,15 @@ def main():
         del cache, kv0
         torch.cuda.empty_cache()
         res["long_context"] = []
-        for lwl in LONG_CONTEXT:
+        res["other_32k"] = []
+        for lwl in LONG_CONTEXT + OTHER_32K:
             st, wu = min(args.steps, 20), min(args.warmup, 3)
-            log(f"long-context workload {lwl.name} batch {lwl.batch}: building cache")
+            log(f"workload {lwl.name} batch {lwl.batch}: building cache")
             lcache, _, lpre = build_cache(lwl, wu + 2 * st, log, keep_first=False)
             r = measure(lwl, lcache, lpre, st, wu, not args.separate)
             for k in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data"):
                 r.pop(k)
-            res["long_context"].append(r)
+            res["long_context" if lwl in LONG_CONTEXT else "other_32k"].append(r)
             log(f"  {lwl.name} B{lwl.batch}: {r['value']:.0f} queries/s, {r['ms_per_step']:.3f} ms/step, "
                 f"split-K {r['roofline']['avg_launch_us']:.1f} us = {r['roofline']['frac']:.3f} of peak")
             del lcache

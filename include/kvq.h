@@ -189,6 +189,27 @@ kvq_status kvq_cache_destroy(kvq_cache* cache);
 kvq_status kvq_set_random_tables(kvq_cache* cache, const float* signs, const float* qjl_S,
                                  void* stream);
 
+/* Draw those tables from a 64-bit seed, on the host (no device work, no handle): signs
+ * [n_layers][n_kv_heads][2][128] of +-1.0f and S [128][128] of N(0,1) rounded to fp32, into
+ * caller-owned host arrays (either may be NULL).  The pages ask for random signs and a Gaussian
+ * projection ([P2] TL;DR; [P3] method comparison table, TurboQuant row) but name no generator;
+ * this one is counter-based SplitMix64 (Steele, Lea and Flood, 2014): a stream key chains the
+ * SplitMix64 output function over (seed, tag, layer, head, tensor), draw i of a stream is the
+ * (i + 1)-th output of the generator started at the key.  Sign j of (layer, head, tensor) is -1
+ * when bit 63 of draw j of the tag-1 stream is set.  S[i][j] = fp32 of the binary64 Box-Muller
+ * value sqrt(-2 ln u1) cos(2 pi u2) with u1 = ((x1 >> 11) + 1) 2^-53, u2 = (x2 >> 11) 2^-53 from
+ * draws 2k and 2k + 1 (k = 128 i + j) of the tag-2 stream (key fields 0, 0, 0).  The same seed
+ * gives the same tables on every host with the same C math library.  KVQ_ERR_INVALID_ARG when
+ * n_layers or n_kv_heads < 1 and signs is not NULL. */
+kvq_status kvq_derive_random_tables(unsigned long long seed, int n_layers, int n_kv_heads, float* signs,
+                                    float* qjl_S);
+
+/* kvq_set_random_tables with the tables kvq_derive_random_tables draws from `seed` for this
+ * cache's n_layers and n_kv_heads.  Synchronous: the draw is staged in host memory the call
+ * allocates (KVQ_ERR_HOST_ALLOC if it cannot), copied on `stream`, and the call returns after
+ * the copy has completed. */
+kvq_status kvq_set_random_tables_seeded(kvq_cache* cache, unsigned long long seed, void* stream);
+
 /* Sinkhorn variance balancing of one layer ([P2] TL;DR): for every kv head and every UNIFORM
  * tensor with sinkhorn_iters > 0, rotate the calibration tokens (device, [n_tokens][n_kv_heads]
  * [128] of dtype for K and V; a tensor's pointer may be NULL when it is not balanced), then

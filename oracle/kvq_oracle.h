@@ -170,7 +170,9 @@ void orc_attention(const orc_plane_cfg* kc, const orc_plane_cfg* vc, const orc_t
                    double scale, double* out);
 
 /* Seeded random tables (the pages draw a random-sign rotation and a Gaussian QJL projection but
- * name no generator; this is the stated reading).  Counter-based SplitMix64: a stream key chains
+ * name no generator; this is the stated reading).  Parity unpinned in part: no published
+ * SplitMix64 output is at hand to pin the exact bit stream; the counter structure, the
+ * Box-Muller closed forms and the distributions of the draws are pinned.  Counter-based SplitMix64: a stream key chains
  * the SplitMix64 output function over (seed, tag, layer, head, tensor); draw i of a stream is
  * the (i + 1)-th output of a SplitMix64 generator started at the key. */
 uint64_t orc_stream_key(uint64_t seed, int tag, int layer, int head, int tensor);

@@ -41,6 +41,9 @@ class KvCache:
     def set_random_tables(self, signs=None, qjl_S=None, stream=None):
         _kvq.kvq_set_random_tables(self.handle, signs, qjl_S, stream)
 
+    def set_random_tables_seeded(self, seed, stream=None):
+        _kvq.kvq_set_random_tables_seeded(self.handle, seed, stream)
+
     def calibrate(self, layer, Kc=None, Vc=None, stream=None):
         _kvq.kvq_calibrate(self.handle, layer, Kc, Vc, stream)
 

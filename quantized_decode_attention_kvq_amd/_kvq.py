@@ -20,7 +20,8 @@ STATUS = {0: "KVQ_OK", 1: "KVQ_ERR_INVALID_ARG", 2: "KVQ_ERR_UNSUPPORTED", 3: "K
           7: "KVQ_ERR_HOST_ALLOC", 8: "KVQ_ERR_DEVICE", 9: "KVQ_ERR_SCRATCH"}
 KVQ_STATIC_SCRATCH_BYTES = 32 << 20
 EXPORTS = ["kvq_cache_required_bytes", "kvq_cache_create", "kvq_cache_destroy",
-           "kvq_set_random_tables", "kvq_calibrate", "kvq_prefill_quantize", "kvq_append",
+           "kvq_set_random_tables", "kvq_derive_random_tables", "kvq_set_random_tables_seeded",
+           "kvq_calibrate", "kvq_prefill_quantize", "kvq_append",
            "kvq_attn_decode", "kvq_get_layout", "kvq_get_tables", "kvq_set_option",
            "kvq_set_timing_events", "kvq_append_attn_decode", "kvq_attn_prefill",
            "kvq_attn_prefill_workspace", "kvq_attn_decode_static",
@@ -72,6 +73,8 @@ def load():
                              ctypes.POINTER(vp)],
         "kvq_cache_destroy": [vp],
         "kvq_set_random_tables": [vp, vp, vp, vp],
+        "kvq_derive_random_tables": [ctypes.c_ulonglong, i, i, vp, vp],
+        "kvq_set_random_tables_seeded": [vp, ctypes.c_ulonglong, vp],
         "kvq_calibrate": [vp, i, vp, vp, i, i, vp],
         "kvq_prefill_quantize": [vp, i, vp, vp, i, i, i, vp],
         "kvq_append": [vp, i, vp, vp, i, i, vp],
@@ -220,6 +223,21 @@ def kvq_set_random_tables(h, signs=None, qjl_S=None, stream=None):
     _resident(signs=signs, qjl_S=qjl_S)
     _check(load().kvq_set_random_tables(h, _ptr(signs), _ptr(qjl_S), _stream(stream)),
            "kvq_set_random_tables")
+
+
+def kvq_derive_random_tables(seed, n_layers, n_kv_heads):
+    """Host-side draw of (signs [n_layers][n_kv_heads][2][128], S [128][128]) float32 numpy arrays
+    from a 64-bit seed (no device work)."""
+    import numpy as np
+    signs = np.zeros((n_layers, n_kv_heads, 2, 128), np.float32)
+    S = np.zeros((128, 128), np.float32)
+    _check(load().kvq_derive_random_tables(seed, n_layers, n_kv_heads, signs.ctypes.data_as(ctypes.c_void_p),
+                                           S.ctypes.data_as(ctypes.c_void_p)), "kvq_derive_random_tables")
+    return signs, S
+
+
+def kvq_set_random_tables_seeded(h, seed, stream=None):
+    _check(load().kvq_set_random_tables_seeded(h, seed, _stream(stream)), "kvq_set_random_tables_seeded")
 
 
 def kvq_calibrate(h, layer, Kc=None, Vc=None, stream=None):

@@ -167,6 +167,36 @@ Plan make_plan(const kvq_config* c) {
     return p;
 }
 
+// Seeded tables: SplitMix64 (Steele, Lea and Flood, 2014) used counter-style.  Its generator
+// steps a 64-bit state by the odd constant 0x9E3779B97F4A7C15 and outputs the state through a
+// fixed mixing function, so the (i + 1)-th output from a state k is mix(k + (i + 1) * step).
+constexpr uint64_t kSeedStep = 0x9E3779B97F4A7C15ull;
+inline uint64_t splitmix_out(uint64_t x) {
+    x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+    x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+    return x ^ (x >> 31);
+}
+// One stream of draws: key = the output function chained over (seed, tag, layer, head, tensor).
+struct SeedStream {
+    uint64_t key;
+    SeedStream(uint64_t seed, int tag, int layer, int head, int tensor) {
+        const int fields[4] = {tag, layer, head, tensor};
+        key = seed;
+        for (int f : fields) key = splitmix_out(key + kSeedStep * (uint64_t)(f + 1));
+    }
+    uint64_t draw(uint64_t i) const { return splitmix_out(key + kSeedStep * (i + 1)); }
+};
+// Box-Muller: radius from u1 in (0, 1], angle from u2 in [0, 1), binary64, rounded to fp32 once.
+inline float gaussian_from(uint64_t a, uint64_t b) {
+    const double scale = 0x1p-53;
+    const double u1 = static_cast<double>((a >> 11) + 1) * scale;
+    const double u2 = static_cast<double>(b >> 11) * scale;
+    const double radius = std::sqrt(-2.0 * std::log(u1));
+    const double angle = 6.283185307179586 * u2;
+    const double value = radius * std::cos(angle);
+    return static_cast<float>(value);
+}
+
 } // namespace
 
 struct kvq_cache {
@@ -320,6 +350,46 @@ kvq_status kvq_set_random_tables(kvq_cache* c, const float* signs, const float* 
         e = hipMemcpyAsync(c->S(), qjl_S, kDim * kDim * sizeof(float), hipMemcpyDeviceToDevice, s);
         if (e == hipSuccess) e = launch_transpose128(c->S(), c->ST(), s);
     }
+    if (e != hipSuccess) return dev_fail(c, e);
+    c->tables_set = true;
+    return KVQ_OK;
+}
+
+kvq_status kvq_derive_random_tables(unsigned long long seed, int n_layers, int n_kv_heads, float* signs,
+                                    float* qjl_S) {
+    if (signs && (n_layers < 1 || n_kv_heads < 1)) return KVQ_ERR_INVALID_ARG;
+    if (signs) {
+        for (int layer = 0; layer < n_layers; ++layer)
+            for (int head = 0; head < n_kv_heads; ++head)
+                for (int tensor = 0; tensor < 2; ++tensor) {
+                    const SeedStream st(seed, 1, layer, head, tensor);
+                    float* row = signs + (((size_t)layer * n_kv_heads + head) * 2 + tensor) * kDim;
+                    for (int j = 0; j < kDim; ++j) row[j] = (st.draw((uint64_t)j) >> 63) != 0 ? -1.0f : 1.0f;
+                }
+    }
+    if (qjl_S) {
+        const SeedStream st(seed, 2, 0, 0, 0);
+        for (int e = 0; e < kDim * kDim; ++e) qjl_S[e] = gaussian_from(st.draw(2 * (uint64_t)e), st.draw(2 * (uint64_t)e + 1));
+    }
+    return KVQ_OK;
+}
+
+kvq_status kvq_set_random_tables_seeded(kvq_cache* c, unsigned long long seed, void* stream) {
+    if (!c) return KVQ_ERR_INVALID_ARG;
+    const size_t n_signs = (size_t)c->cfg.n_layers * c->cfg.n_kv_heads * 2 * kDim;
+    std::vector<float> staging;
+    try {
+        staging.resize(n_signs + (size_t)kDim * kDim);
+    } catch (const std::bad_alloc&) {
+        return KVQ_ERR_HOST_ALLOC;
+    }
+    kvq_derive_random_tables(seed, c->cfg.n_layers, c->cfg.n_kv_heads, staging.data(), staging.data() + n_signs);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(c->signs(), staging.data(), n_signs * sizeof(float), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(c->S(), staging.data() + n_signs, (size_t)kDim * kDim * sizeof(float), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = launch_transpose128(c->S(), c->ST(), s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s); // the staging vector goes out of scope below
     if (e != hipSuccess) return dev_fail(c, e);
     c->tables_set = true;
     return KVQ_OK;

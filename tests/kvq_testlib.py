@@ -29,7 +29,9 @@ class Case:
     """One workload instance on the device plus everything the oracle needs."""
 
     def __init__(self, wl: W.Workload, n_tokens: int, layers=None, batch=None, max_context=None,
-                 device="cuda", gen_device=None, extra_tokens=0):
+                 device="cuda", gen_device=None, extra_tokens=0, seed=None):
+        """seed: install the random tables with kvq_set_random_tables_seeded (the oracle then
+        uses its own draw from the same seed) instead of passing the workload's tables."""
         import quantized_decode_attention_kvq_amd as K
         self.K = K
         self.wl = wl
@@ -42,10 +44,15 @@ class Case:
                             max_batch=self.batch)
         cfg["n_layers"] = len(self.layers)
         self.cache = K.KvCache(device=device, **cfg)
-        self.signs = W.rotation_signs(wl)[self.layers]  # [L][Hkv][2][128]
-        self.S = W.qjl_projection(wl)
+        if seed is not None:
+            # the cache's layers are 0 .. len(layers) - 1, and so are the seeded tables'
+            self.signs, self.S = oracle.derive_random_tables(seed, len(self.layers), wl.n_kv_heads)
+            self.cache.set_random_tables_seeded(seed)
+        else:
+            self.signs = W.rotation_signs(wl)[self.layers]  # [L][Hkv][2][128]
+            self.S = W.qjl_projection(wl)
         needs_signs = wl.rotate_k or wl.rotate_v or W.is_turbo(wl.k_scheme) or W.is_turbo(wl.v_scheme)
-        if needs_signs or wl.k_scheme == W.TURBO_QJL:
+        if seed is None and (needs_signs or wl.k_scheme == W.TURBO_QJL):
             self.cache.set_random_tables(
                 torch.from_numpy(np.ascontiguousarray(self.signs)).to(device),
                 torch.from_numpy(self.S).to(device))

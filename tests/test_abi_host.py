@@ -183,3 +183,24 @@ def test_f16_inputs_are_kvq_f16():
             K.kvq_append_attn_decode(h, 0, k16, k16, q16.float(), out)
     finally:
         K._SHAPES.pop(h.value)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 123456789, 2**63 + 11, 2**64 - 1])
+def test_seeded_tables_equal_the_oracle_draw(seed):
+    # host-only: the library's SplitMix64 / Box-Muller draw, written separately from the oracle's
+    # from the same definition, gives the same signs and projection bit for bit
+    import numpy as np
+
+    import oracle
+    signs, S = K.kvq_derive_random_tables(seed, 3, 5)
+    osigns, oS = oracle.derive_random_tables(seed, 3, 5)
+    assert np.array_equal(signs.view(np.uint32), osigns.view(np.uint32))
+    assert np.array_equal(S.view(np.uint32), oS.view(np.uint32))
+
+
+def test_seeded_tables_arguments():
+    lib = K.load()
+    assert lib.kvq_derive_random_tables(1, 0, 8, ctypes.c_void_p(0x10000), None) == 1
+    assert lib.kvq_derive_random_tables(1, 2, 0, ctypes.c_void_p(0x10000), None) == 1
+    assert lib.kvq_derive_random_tables(1, 0, 0, None, None) == 0  # nothing asked, nothing drawn
+    assert lib.kvq_set_random_tables_seeded(None, 1, None) == 1

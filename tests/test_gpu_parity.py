@@ -715,3 +715,28 @@ def test_split_keys_planes_and_decode(wl):
         _say(f"  fused step seq {b}: rel_l2={r:.2e} max_abs={m:.2e}")
         assert r <= REL_L2_TOL and m <= MAX_ABS_TOL, (b, r, m)
     _decode_and_compare(case, 0, planes)  # both decode paths
+
+
+@pytest.mark.parametrize("wl", [W.LLAMA3B_32K_TURBO, W.LLAMA3B_32K_KVARN, W.LLAMA8B_32K_TURBO25_KV],
+                         ids=lambda w: w.name)
+def test_seeded_random_tables(wl):
+    # kvq_set_random_tables_seeded: the device holds exactly the oracle's draw from the seed (signs
+    # and S; the transposed copy the kernels read shows in the QJL bits and scores), and the planes
+    # and attention built on them match the oracle's, on both decode paths
+    seed = 20261202
+    _say("case:", wl.name, "seeded tables, 2 layers, 300 prefill + 10 appends")
+    case = Case(wl, 310, layers=[0, 1], seed=seed)
+    L, H = 2, wl.n_kv_heads
+    sg = case.cache.table("signs", L * H * 2 * 128).cpu().numpy().reshape(L, H, 2, 128)
+    S = case.cache.table("qjl_S", 128 * 128).cpu().numpy().reshape(128, 128)
+    assert np.array_equal(sg.view(np.uint32), case.signs.view(np.uint32))
+    assert np.array_equal(S.view(np.uint32), case.S.view(np.uint32))
+    for li in range(2):
+        k, v = case.kv(li)
+        case.cache.prefill_quantize(li, k[:, :300].contiguous(), v[:, :300].contiguous())
+        for t in range(300, 310):
+            case.cache.append(li, k[:, t].contiguous(), v[:, t].contiguous())
+    torch.cuda.synchronize()
+    for li in range(2):
+        planes = _check_all_planes(case, li, heads=[0, 5, 7])
+        _decode_and_compare(case, li, None)
