@@ -82,7 +82,8 @@ def test_progressive_3970_full():
 @pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_TURBO, W.LLAMA3B_32K_TURBO_ASYM,
                                 W.LLAMA3B_32K_Q8_0_TURBO_V, W.DENSE27B_120K_Q8_0, W.LLAMA3B_32K_Q8_0_TURBO4_V,
                                 W.LLAMA8B_32K_Q8_0_TURBO25_V, W.LLAMA8B_32K_Q8_0_TURBO35_V,
-                                W.LLAMA3B_32K_U8_K_U3_V, W.LLAMA3B_32K_KVARN_U3],
+                                W.LLAMA3B_32K_U8_K_U3_V, W.LLAMA3B_32K_KVARN_U3, W.LLAMA8B_32K_TURBO25_KV,
+                                W.LLAMA8B_32K_TURBO35_KV],
                          ids=lambda w: w.name)
 def test_prefill_equals_appends_bytewise(wl):
     _say("case: prefill == appends,", wl.name, "n=300")
@@ -109,7 +110,7 @@ RAGGED_CALLS = [(3, 21), (1, 5), (2, 3), (3, 37), (1, 16), (3, 130)]
                                 W.LLAMA3B_32K_TURBO_ASYM, W.DENSE27B_120K_U8, W.DENSE27B_120K_Q8_0,
                                 W.LLAMA3B_32K_Q8_0_TURBO_V, W.LLAMA3B_32K_Q8_0_TURBO4_V,
                                 W.LLAMA8B_32K_Q8_0_TURBO25_V, W.LLAMA8B_32K_Q8_0_TURBO35_V,
-                                W.LLAMA3B_32K_U8_K_U3_V, W.LLAMA3B_32K_KVARN_U3],
+                                W.LLAMA3B_32K_U8_K_U3_V, W.LLAMA3B_32K_KVARN_U3, W.LLAMA8B_32K_TURBO35_KV],
                          ids=lambda w: w.name)
 def test_prefill_ragged_batch_bytewise(wl):
     """Prefill calls over a batch whose sequences start at different lengths leave exactly the
@@ -330,7 +331,8 @@ def test_progressive_batch_ragged_lengths():
 
 
 @pytest.mark.parametrize("path", [1, 2])
-@pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_TURBO, W.LLAMA3B_32K_TURBO_ASYM],
+@pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE, W.LLAMA3B_32K_TURBO, W.LLAMA3B_32K_TURBO_ASYM,
+                                W.LLAMA8B_32K_TURBO25_KV],
                          ids=lambda w: w.name)
 def test_split_count_invariance_and_determinism(wl, path):
     _say("case: split invariance", wl.name, "path", path)
@@ -341,8 +343,8 @@ def test_split_count_invariance_and_determinism(wl, path):
     outs = {}
     for st in (0, 64, 256, 1024, 4096):
         case.cache.set_option(1, st)
-        o1 = torch.empty((1, 24, 128), device="cuda")
-        o2 = torch.empty((1, 24, 128), device="cuda")
+        o1 = torch.empty((1, wl.n_q_heads, 128), device="cuda")
+        o2 = torch.empty((1, wl.n_q_heads, 128), device="cuda")
         case.cache.attn_decode(0, q, o1)
         case.cache.attn_decode(0, q, o2)
         torch.cuda.synchronize()
@@ -533,7 +535,8 @@ WINDOW_EDGE_NS = [1, 2, 64, 127, 128, 129, 130, 192, 257]
 @pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("wl", [W.LLAMA3B_3970_PROGRESSIVE,
                                 W.LLAMA3B_32K_KVARN.with_(name="llama3b-kvarn-u4-window", window=128),
-                                W.LLAMA3B_32K_TURBO.with_(name="llama3b-turboqjl-k-window", window=128)],
+                                W.LLAMA3B_32K_TURBO.with_(name="llama3b-turboqjl-k-window", window=128),
+                                W.LLAMA8B_32K_TURBO25_KV.with_(name="llama8b-split2.5-kv-window", window=128)],
                          ids=lambda w: w.name)
 def test_window_edges_decode_and_fused(wl, path):
     """At each n the cache holds tokens 0 .. n - 2 (bulk prefill and appends), token n - 1 comes
