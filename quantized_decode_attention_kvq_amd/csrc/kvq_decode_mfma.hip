@@ -854,12 +854,14 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                 t = row_max16(t);
                 const float mnew = fmaxf(m_run[mb], t * F[mb]);
                 const bool inf = (mnew == kNegInf);
-                alpha[mb] = inf ? 1.0f : exp2f(m_run[mb] - mnew);
+                // the hardware exp2 (no denormal-range fix-up: a weight below 2^-126 is zero once it
+                // becomes an fp16 operand, and negligible in the running sum)
+                alpha[mb] = inf ? 1.0f : __builtin_amdgcn_exp2f(m_run[mb] - mnew);
                 grew |= (mnew > m_run[mb]);
                 float s = 0.0f;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    pj[mb][j] = inf ? 0.0f : exp2f(fmaf(raw[mb][j], F[mb], -mnew));
+                    pj[mb][j] = inf ? 0.0f : __builtin_amdgcn_exp2f(fmaf(raw[mb][j], F[mb], -mnew));
                     s += pj[mb][j];
                 }
                 l_run[mb] = l_run[mb] * alpha[mb] + s;
@@ -888,7 +890,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = 4 * mb + lq;
-                float P[kSlots][4]; // [g][j]
+                // operand [g][j] = PA[g][j] * PB[g][j]: the token's weight factor times the slot's
+                // scale or codebook coefficient, split into fp16 hi and scaled lo below
+                float PA[kSlots][4], PB[kSlots][4];
                 if constexpr (VU) {
                     const auto& vm = vr.vm;
                     constexpr float mid = (VB == 4) ? 8.0f : (V3 ? 4.0f : 128.0f); // codes enter as c - mid
@@ -903,10 +907,12 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                         const float w = V3 ? __uint_as_float((uint32_t)(127 - 2 * (lr & 1) - (j >> 1)) << 23)
                                            : ((VB == 4 && j < 2) ? 16.0f : 1.0f);
                         const float pw = pj[mb][j] * w;
-                        P[0][j] = pw * lo_h(vm[j].x);
-                        P[1][j] = pw * hi_h(vm[j].x);
-                        P[2][j] = pw * lo_h(vm[j].y);
-                        P[3][j] = pw * hi_h(vm[j].y);
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) PA[g][j] = pw;
+                        PB[0][j] = lo_h(vm[j].x);
+                        PB[1][j] = hi_h(vm[j].x);
+                        PB[2][j] = lo_h(vm[j].y);
+                        PB[3][j] = hi_h(vm[j].y);
                     }
                 } else if constexpr (VS) {
                     // outlier slots -p n_O a_S, then the rest's -p n_R a_S
@@ -915,9 +921,15 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                         const uint32_t nw = (j == 0) ? vr.nm.x : (j == 1) ? vr.nm.y : (j == 2) ? vr.nm.z : vr.nm.w;
                         const float po = pj[mb][j] * lo_h(nw), pr = pj[mb][j] * hi_h(nw);
 #pragma unroll
-                        for (int g = 0; g < kSo; ++g) P[g][j] = -po * aO[g];
+                        for (int g = 0; g < kSo; ++g) {
+                            PA[g][j] = -po;
+                            PB[g][j] = aO[g];
+                        }
 #pragma unroll
-                        for (int g = 0; g < kSr; ++g) P[kSo + g][j] = -pr * aR[g];
+                        for (int g = 0; g < kSr; ++g) {
+                            PA[kSo + g][j] = -pr;
+                            PB[kSo + g][j] = aR[g];
+                        }
                     }
                 } else {
                     // weight of plane p = -p n a_p: the bit operands are -b = -(2 bit - 1)
@@ -927,7 +939,10 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                         const float nt = (j & 1) ? hi_h(nw) : lo_h(nw);
                         const float pn = pj[mb][j] * nt;
 #pragma unroll
-                        for (int g = 0; g < kSlots; ++g) P[g][j] = -pn * (VT4 ? a16[g] : al[g & 3]);
+                        for (int g = 0; g < kSlots; ++g) {
+                            PA[g][j] = -pn;
+                            PB[g][j] = VT4 ? a16[g] : al[g & 3];
+                        }
                     }
                 }
 #pragma unroll
@@ -935,9 +950,12 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                     h4 hv, lv;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const _Float16 ph = (_Float16)P[g][j];
+                        // hi = fp16(a b); lo = fp16(kLoScale (a b - hi)), a b - hi from one fused
+                        // product (a mixed-precision fma when b is an fp16 scale)
+                        const float a = PA[g][j], b = PB[g][j];
+                        const _Float16 ph = (_Float16)(a * b);
                         hv[j] = ph;
-                        lv[j] = (_Float16)((P[g][j] - (float)ph) * kLoScale);
+                        lv[j] = (_Float16)(fmaf(a, b, -(float)ph) * kLoScale);
                     }
                     *reinterpret_cast<h4*>(my_p + (g * kRows + row) * kPRow + 4 * lr) = hv;
                     *reinterpret_cast<h4*>(my_p + (g * kRows + kRows / 2 + row) * kPRow + 4 * lr) = lv;
