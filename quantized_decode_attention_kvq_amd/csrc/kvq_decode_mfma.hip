@@ -646,7 +646,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                         const float x = (h < G && lq == gq) ? s_q[hc][32 * lq + 8 * sl + i] * sc : 0.0f;
                         const _Float16 xh = (_Float16)x;
                         hi[i] = xh;
-                        lo[i] = (_Float16)((x - (float)xh) * kLoScale);
+                        lo[i] = (_Float16)(x - (float)xh); // unscaled: accumulates with hi
                     }
                     Ahi[mb][sl] = hi;
                     Alo[mb][sl] = lo;
@@ -664,7 +664,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                     const float x = (h < G) ? s_q[hc][32 * gq + 8 * lq + i] * w : 0.0f;
                     const _Float16 xh = (_Float16)x;
                     hi[i] = xh;
-                    lo[i] = (_Float16)((x - (float)xh) * kLoScale);
+                    // the remainder unscaled: it shares the hi product's accumulator (its absolute
+                    // precision, 2^-24 where it is subnormal, is 2^-30 of the largest |q'|)
+                    lo[i] = (_Float16)(x - (float)xh);
                 }
                 const h8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
@@ -747,14 +749,12 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                     }
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) {
-                        f4 D = {0.0f, 0.0f, 0.0f, 0.0f}, E = {0.0f, 0.0f, 0.0f, 0.0f};
+                        f4 D = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
                             D = mfma16(Ahi[mb][g], B[g], D);
-                            E = mfma16(Alo[mb][g], B[g], E);
+                            D = mfma16(Alo[mb][g], B[g], D);
                         }
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) D[v] = fmaf(E[v], kLoInv, D[v]);
                         float r = lo_h(km[j].x) * D[0];
                         r = fmaf(hi_h(km[j].x), D[1], r);
                         r = fmaf(lo_h(km[j].y), D[2], r);
