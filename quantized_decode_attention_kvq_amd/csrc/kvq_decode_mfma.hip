@@ -11,7 +11,8 @@
 //
 // How (one workgroup = NW waves per (sequence, kv head, token split); each wave streams 64-token
 // chunks; all products on v_mfma_f32_16x16x32_f16, every code operand exact):
-//  * Uniform K: A = (head, group) rows of q' as fp16 hi + scaled lo, B = raw codes: 4-bit codes as fp16
+//  * Uniform K: A = (head, group) rows of q' as fp16 hi and remainder lo, both products in one
+//    accumulator chain, B = raw codes: 4-bit codes as fp16
 //    subnormal bit patterns (code * 2^-24, odd nibbles x16 compensated in A), 8-bit codes as
 //    zero-extended bytes.  The fp16 scale and zero fold in afterwards:
 //    s_t = sum_g scale_g,t dot_g + zero_g,t sum_{j in g} q'_j.
@@ -27,7 +28,7 @@
 //    plane (and at 3.5 bits their parity monomial) and the QJL term are the remaining products.
 //  * Online softmax in the log2 domain (q' carries softmax_scale * log2(e) and a per-head power
 //    of two that keeps 16 q' inside fp16 range).
-//  * PV: A = p * (scale_g | -n * a_p) as fp16 hi (rows 0-7) + scaled lo (rows 8-15), staged
+//  * PV: A = p * (scale_g | -n * a_p) as fp16 hi (rows 0-7) + remainder lo (rows 8-15), staged
 //    through LDS in operand order; B = centred V codes c - 8 (c - 128) as exact fp16 integers,
 //    or the TurboQuant-MSE bit planes as -+1, plus a vector-ALU sum of p (zero + 8 scale).
 //    Centring keeps every accumulator of the order of the output itself.
@@ -950,12 +951,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                     h4 hv, lv;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        // hi = fp16(a b); lo = fp16(kLoScale (a b - hi)), a b - hi from one fused
-                        // product (a mixed-precision fma when b is an fp16 scale)
+                        // hi = fp16(a b); lo = fp16(a b - hi) from one fused product (a mixed-
+                        // precision fma when b is an fp16 scale), unscaled: where it is subnormal
+                        // its absolute precision is 2^-25 of operands whose weights are at most 1
                         const float a = PA[g][j], b = PB[g][j];
                         const _Float16 ph = (_Float16)(a * b);
                         hv[j] = ph;
-                        lv[j] = (_Float16)(fmaf(a, b, -(float)ph) * kLoScale);
+                        lv[j] = (_Float16)fmaf(a, b, -(float)ph);
                     }
                     *reinterpret_cast<h4*>(my_p + (g * kRows + row) * kPRow + 4 * lr) = hv;
                     *reinterpret_cast<h4*>(my_p + (g * kRows + kRows / 2 + row) * kPRow + 4 * lr) = lv;
@@ -1134,7 +1136,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
                     if (!lo_part)
                         s_acc[(wave * 8 + h) * kDim + 16 * N + lr] = acc[N][v] * u;
                     else
-                        s_acc2[(wave * 8 + h) * kDim + 16 * N + lr] = acc[N][v] * (u * kLoInv);
+                        s_acc2[(wave * 8 + h) * kDim + 16 * N + lr] = acc[N][v] * u;
                 }
             }
         }
