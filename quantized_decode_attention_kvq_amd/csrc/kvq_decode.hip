@@ -495,6 +495,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
         return;
     }
     const float* base = p.partials + ((size_t)b * p.Hq + hq) * p.n_splits_total * kPartialFloats;
+    // the output transform's tables (c_V, the signs, a split V's position map) do not depend on
+    // the partials: request them now, so their round trip overlaps the partials' one
+    const PlaneGeom& VG = p.geom[1];
+    const size_t tab = (size_t)(kvh * 2 + 1) * kDim + 4 * c4;
+    float4 cs4 = make_float4(1.0f, 1.0f, 1.0f, 1.0f), sg4 = cs4;
+    int4 pm4 = make_int4(0, 0, 0, 0);
+    if (part == 0) {
+        if (VG.sinkhorn) cs4 = *reinterpret_cast<const float4*>(p.cs + tab);
+        if (VG.rotate || VG.scheme == kTurboSplit) sg4 = *reinterpret_cast<const float4*>(p.signs + tab);
+        if (VG.scheme == kTurboSplit) pm4 = reinterpret_cast<const int4*>(p.perm + (size_t)kvh * kDim)[c4];
+    }
     float m = kNegInf, l = 0.0f;
     float4 aq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), aw = aq;
     // eight splits per thread per round (one round up to 64 splits), all loads issued before
@@ -519,7 +530,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
         for (int i = 0; i < 8; ++i) {
             if (ms[i] == kNegInf) continue;
             const float mn = fmaxf(m, ms[i]);
-            const float fo = exp2f(m - mn), fn = exp2f(ms[i] - mn);
+            const float fo = __builtin_amdgcn_exp2f(m - mn), fn = __builtin_amdgcn_exp2f(ms[i] - mn);
             m = mn;
             l = fmaf(ls[i], fn, l * fo);
             aq.x *= fo; aq.y *= fo; aq.z *= fo; aq.w *= fo;
@@ -544,7 +555,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     float L = 0.0f, q[4] = {0.0f, 0.0f, 0.0f, 0.0f}, w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int i = 0; i < 8; ++i) {
         if (s_m[i] == kNegInf) continue;
-        const float f = exp2f(s_m[i] - M);
+        const float f = __builtin_amdgcn_exp2f(s_m[i] - M);
         L = fmaf(s_l[i], f, L);
         const float4 a = s_q[i][c4], c = s_w[i][c4];
         q[0] = fmaf(a.x, f, q[0]); q[1] = fmaf(a.y, f, q[1]);
@@ -552,10 +563,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
         w[0] = fmaf(c.x, f, w[0]); w[1] = fmaf(c.y, f, w[1]);
         w[2] = fmaf(c.z, f, w[2]); w[3] = fmaf(c.w, f, w[3]);
     }
-    const PlaneGeom& VG = p.geom[1];
-    const size_t tab = (size_t)(kvh * 2 + 1) * kDim + 4 * c4;
+    const float csj[4] = {cs4.x, cs4.y, cs4.z, cs4.w}, sgj[4] = {sg4.x, sg4.y, sg4.z, sg4.w};
     if (VG.sinkhorn)
-        for (int j = 0; j < 4; ++j) q[j] *= p.cs[tab + j];
+        for (int j = 0; j < 4; ++j) q[j] *= csj[j];
     if (VG.scheme == kTurboSplit) {
         // each 64-position half: (1/8) d .* H64 y (strides 1, 2 in the thread, 4..32 across
         // lanes), then position j goes to channel perm[j]
@@ -578,11 +588,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
         stage(std::integral_constant<int, 2>{});
         stage(std::integral_constant<int, 4>{});
         stage(std::integral_constant<int, 8>{});
-        const int4 pm = reinterpret_cast<const int4*>(p.perm + (size_t)kvh * kDim)[c4];
-        const int pj[4] = {pm.x, pm.y, pm.z, pm.w};
+        const int pj[4] = {pm4.x, pm4.y, pm4.z, pm4.w};
         for (int j = 0; j < 4; ++j) {
             float v = q[j] * 0.125f;
-            if (p.signs[tab + j] < 0.0f) v = -v;
+            if (sgj[j] < 0.0f) v = -v;
             s_x[pj[j]] = v;
         }
         __builtin_amdgcn_wave_barrier();
@@ -613,7 +622,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
         stage(std::integral_constant<int, 16>{});
         for (int j = 0; j < 4; ++j) {
             q[j] *= c0f();
-            if (p.signs[tab + j] < 0.0f) q[j] = -q[j];
+            if (sgj[j] < 0.0f) q[j] = -q[j];
         }
     }
     *out = make_float4((q[0] + w[0]) / L, (q[1] + w[1]) / L, (q[2] + w[2]) / L, (q[3] + w[3]) / L);
