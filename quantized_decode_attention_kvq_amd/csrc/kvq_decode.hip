@@ -515,16 +515,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
         float4 a[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+            // unconditional loads (a split past the last reads the last one again and is then
+            // ignored), so that all sixteen go out back to back with no branch between them
             const int s = s0 + 8 * i;
-            ms[i] = kNegInf;
-            ls[i] = 0.0f;
-            a[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (s < p.n_splits_total) {
-                const float* ps = base + (size_t)s * kPartialFloats;
-                ms[i] = ps[0];
-                ls[i] = ps[1];
-                a[i] = *reinterpret_cast<const float4*>(ps + 4 + 4 * c4);
-            }
+            const float* ps = base + (size_t)min(s, p.n_splits_total - 1) * kPartialFloats;
+            const float2 ml = *reinterpret_cast<const float2*>(ps);
+            ms[i] = s < p.n_splits_total ? ml.x : kNegInf;
+            ls[i] = ml.y;
+            a[i] = *reinterpret_cast<const float4*>(ps + 4 + 4 * c4);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -625,7 +623,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
             if (sgj[j] < 0.0f) q[j] = -q[j];
         }
     }
-    *out = make_float4((q[0] + w[0]) / L, (q[1] + w[1]) / L, (q[2] + w[2]) / L, (q[3] + w[3]) / L);
+    const float inv_l = 1.0f / L;
+    *out = make_float4((q[0] + w[0]) * inv_l, (q[1] + w[1]) * inv_l, (q[2] + w[2]) * inv_l, (q[3] + w[3]) * inv_l);
 }
 
 } // namespace
