@@ -454,75 +454,74 @@ __global__ __launch_bounds__(256) void decode_vec_kernel(DecodeParams p) {
             wacc[wave][h][2 * l] = acc0[h];
             wacc[wave][h][2 * l + 1] = acc1[h];
         }
+    // the value plane's output map tables for the lane's channel pair
+    const bool vsplit = VG.scheme == kTurboSplit;
+    const size_t vtab = (size_t)(kvh * 2 + 1) * kDim;
+    float2 cs2 = make_float2(1.0f, 1.0f), sg2 = cs2;
+    int2 pm2 = make_int2(2 * l, 2 * l + 1);
+    if (!wsplit) {
+        if (VG.sinkhorn) cs2 = reinterpret_cast<const float2*>(p.cs + vtab)[l];
+        if (VG.rotate || vsplit) sg2 = reinterpret_cast<const float2*>(p.signs + vtab)[l];
+        if (vsplit) pm2 = reinterpret_cast<const int2*>(p.perm + (size_t)kvh * kDim)[l];
+    }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < G * kDim; idx += 256) {
-        const int h = idx / kDim, d = idx % kDim;
+    // partial of this split per query head in the plain channel domain: one wave per head, lane l
+    // the channel pair 2l, 2l + 1, mapped back by the value plane's output map
+    for (int h = wave; h < G; h += 4) {
         float M = kNegInf;
         for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][h]);
-        float A = 0.0f, L = 0.0f;
+        float A0 = 0.0f, A1 = 0.0f, L = 0.0f;
         if (M != kNegInf) {
             for (int w = 0; w < 4; ++w) {
                 if (wm[w][h] == kNegInf) continue;
                 const float f = exp2f(wm[w][h] - M);
-                A += wacc[w][h][d] * f;
+                A0 += wacc[w][h][2 * l] * f;
+                A1 += wacc[w][h][2 * l + 1] * f;
                 L += wl[w][h] * f;
             }
         }
+        if (!wsplit) value_out_map(A0, A1, vsplit, VG.sinkhorn, VG.rotate, cs2, sg2);
         float* part = p.partials +
                       (((size_t)b * p.Hq + kvh * G + h) * p.n_splits_total + split) * kPartialFloats;
-        if (d == 0) {
+        if (l == 0) {
             part[0] = M;
             part[1] = L;
         }
-        part[4 + d] = A;
+        part[4 + pm2.x] = A0;
+        part[4 + pm2.y] = A1;
     }
 }
 
-// Fixed-order merge of the splits of one (sequence, query head), then
-// out = (R_V^-1(c_V .* acc_codes) + acc_window) / l.  256 threads: thread t owns channels
-// 4(t%32)..4(t%32)+3 of splits t/32, t/32 + 8, ...; the 8 split classes are then combined in
-// LDS in ascending order, so the result depends only on the split count.
+// Fixed-order merge of the splits of one (sequence, query head): the partials arrive in the plain
+// channel domain (the split kernels apply the value plane's output map), so
+// out = (sum_s 2^(m_s - M) acc_s) / (sum_s 2^(m_s - M) l_s).  256 threads: thread t owns channels
+// 4 (t / 8) .. 4 (t / 8) + 3 of splits t % 8, t % 8 + 8, ..., combined in ascending order; the
+// eight threads of a channel group (consecutive lanes) then combine over a fixed xor tree, so the
+// result depends only on the split count, with no shared memory and no barrier.
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
-    __shared__ float s_m[8], s_l[8];
-    __shared__ float4 s_q[8][32], s_w[8][32];
-    __shared__ float s_x[kDim]; // split V: the un-rotated positions, scattered to their channels
     const int hq = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-    const int c4 = t & 31, part = t >> 5;
-    const int kvh = hq / p.G;
+    const int c4 = t >> 3, part = t & 7;
     float4* out = reinterpret_cast<float4*>(p.out + ((size_t)b * p.Hq + hq) * kDim) + c4;
     if (p.len[b] == 0) {
         if (part == 0) *out = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         return;
     }
     const float* base = p.partials + ((size_t)b * p.Hq + hq) * p.n_splits_total * kPartialFloats;
-    // the output transform's tables (c_V, the signs, a split V's position map) do not depend on
-    // the partials: request them now, so their round trip overlaps the partials' one
-    const PlaneGeom& VG = p.geom[1];
-    const size_t tab = (size_t)(kvh * 2 + 1) * kDim + 4 * c4;
-    float4 cs4 = make_float4(1.0f, 1.0f, 1.0f, 1.0f), sg4 = cs4;
-    int4 pm4 = make_int4(0, 0, 0, 0);
-    if (part == 0) {
-        if (VG.sinkhorn) cs4 = *reinterpret_cast<const float4*>(p.cs + tab);
-        if (VG.rotate || VG.scheme == kTurboSplit) sg4 = *reinterpret_cast<const float4*>(p.signs + tab);
-        if (VG.scheme == kTurboSplit) pm4 = reinterpret_cast<const int4*>(p.perm + (size_t)kvh * kDim)[c4];
-    }
     float m = kNegInf, l = 0.0f;
-    float4 aq = make_float4(0.0f, 0.0f, 0.0f, 0.0f), aw = aq;
-    // eight splits per thread per round (one round up to 64 splits), all loads issued before
-    // any is used; each thread combines its splits in ascending order
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (int s0 = part; s0 < p.n_splits_total; s0 += 64) {
         float ms[8], ls[8];
-        float4 a[8];
+        float4 as[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            // unconditional loads (a split past the last reads the last one again and is then
-            // ignored), so that all sixteen go out back to back with no branch between them
+            // unconditional loads (a split past the last re-reads the last one and is ignored),
+            // so that all of them go out back to back with no branch between them
             const int s = s0 + 8 * i;
             const float* ps = base + (size_t)min(s, p.n_splits_total - 1) * kPartialFloats;
             const float2 ml = *reinterpret_cast<const float2*>(ps);
             ms[i] = s < p.n_splits_total ? ml.x : kNegInf;
             ls[i] = ml.y;
-            a[i] = *reinterpret_cast<const float4*>(ps + 4 + 4 * c4);
+            as[i] = *reinterpret_cast<const float4*>(ps + 4 + 4 * c4);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -531,100 +530,35 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
             const float fo = __builtin_amdgcn_exp2f(m - mn), fn = __builtin_amdgcn_exp2f(ms[i] - mn);
             m = mn;
             l = fmaf(ls[i], fn, l * fo);
-            aq.x *= fo; aq.y *= fo; aq.z *= fo; aq.w *= fo;
-            aw.x *= fo; aw.y *= fo; aw.z *= fo; aw.w *= fo;
-            float4& dst = s0 + 8 * i >= p.n_splits ? aw : aq;
-            dst.x = fmaf(a[i].x, fn, dst.x);
-            dst.y = fmaf(a[i].y, fn, dst.y);
-            dst.z = fmaf(a[i].z, fn, dst.z);
-            dst.w = fmaf(a[i].w, fn, dst.w);
+            a.x = fmaf(as[i].x, fn, a.x * fo);
+            a.y = fmaf(as[i].y, fn, a.y * fo);
+            a.z = fmaf(as[i].z, fn, a.z * fo);
+            a.w = fmaf(as[i].w, fn, a.w * fo);
         }
     }
-    if (c4 == 0) {
-        s_m[part] = m;
-        s_l[part] = l;
+    // the eight split classes of the channel group: pairs at xor distance 1, 2, 4 (a fixed tree;
+    // lane part == 0 holds the result)
+    auto pair = [&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        const float mo = xor_lane<h>(m), lo = xor_lane<h>(l);
+        const float ax = xor_lane<h>(a.x), ay = xor_lane<h>(a.y), az = xor_lane<h>(a.z), aw = xor_lane<h>(a.w);
+        const float mn = fmaxf(m, mo);
+        const float f = (m == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+        const float g = (mo == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mo - mn);
+        m = mn;
+        l = l * f + lo * g;
+        a.x = a.x * f + ax * g;
+        a.y = a.y * f + ay * g;
+        a.z = a.z * f + az * g;
+        a.w = a.w * f + aw * g;
+    };
+    pair(std::integral_constant<int, 1>{});
+    pair(std::integral_constant<int, 2>{});
+    pair(std::integral_constant<int, 4>{});
+    if (part == 0) {
+        const float inv_l = 1.0f / l;
+        *out = make_float4(a.x * inv_l, a.y * inv_l, a.z * inv_l, a.w * inv_l);
     }
-    s_q[part][c4] = aq;
-    s_w[part][c4] = aw;
-    __syncthreads();
-    if (part != 0) return;
-    float M = kNegInf;
-    for (int i = 0; i < 8; ++i) M = fmaxf(M, s_m[i]);
-    float L = 0.0f, q[4] = {0.0f, 0.0f, 0.0f, 0.0f}, w[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int i = 0; i < 8; ++i) {
-        if (s_m[i] == kNegInf) continue;
-        const float f = __builtin_amdgcn_exp2f(s_m[i] - M);
-        L = fmaf(s_l[i], f, L);
-        const float4 a = s_q[i][c4], c = s_w[i][c4];
-        q[0] = fmaf(a.x, f, q[0]); q[1] = fmaf(a.y, f, q[1]);
-        q[2] = fmaf(a.z, f, q[2]); q[3] = fmaf(a.w, f, q[3]);
-        w[0] = fmaf(c.x, f, w[0]); w[1] = fmaf(c.y, f, w[1]);
-        w[2] = fmaf(c.z, f, w[2]); w[3] = fmaf(c.w, f, w[3]);
-    }
-    const float csj[4] = {cs4.x, cs4.y, cs4.z, cs4.w}, sgj[4] = {sg4.x, sg4.y, sg4.z, sg4.w};
-    if (VG.sinkhorn)
-        for (int j = 0; j < 4; ++j) q[j] *= csj[j];
-    if (VG.scheme == kTurboSplit) {
-        // each 64-position half: (1/8) d .* H64 y (strides 1, 2 in the thread, 4..32 across
-        // lanes), then position j goes to channel perm[j]
-        for (int h = 1; h < 4; h <<= 1)
-            for (int j = 0; j < 4; ++j)
-                if (!(j & h)) {
-                    const float x = q[j], y = q[j + h];
-                    q[j] = x + y;
-                    q[j + h] = x - y;
-                }
-        auto stage = [&](auto hc) {
-            constexpr int h = decltype(hc)::value;
-            const bool upper = (c4 & h) != 0;
-            for (int j = 0; j < 4; ++j) {
-                const float o = xor_lane<h>(q[j]);
-                q[j] = upper ? o - q[j] : q[j] + o;
-            }
-        };
-        stage(std::integral_constant<int, 1>{});
-        stage(std::integral_constant<int, 2>{});
-        stage(std::integral_constant<int, 4>{});
-        stage(std::integral_constant<int, 8>{});
-        const int pj[4] = {pm4.x, pm4.y, pm4.z, pm4.w};
-        for (int j = 0; j < 4; ++j) {
-            float v = q[j] * 0.125f;
-            if (sgj[j] < 0.0f) v = -v;
-            s_x[pj[j]] = v;
-        }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        for (int j = 0; j < 4; ++j) q[j] = s_x[4 * c4 + j];
-    } else if (VG.rotate) {
-        // Walsh-Hadamard butterflies over the 128 channels: strides 1 and 2 inside a thread,
-        // strides 4..64 between the 32 lanes (channel 4*lane + j) by xor shuffles.
-        for (int h = 1; h < 4; h <<= 1)
-            for (int j = 0; j < 4; ++j)
-                if (!(j & h)) {
-                    const float x = q[j], y = q[j + h];
-                    q[j] = x + y;
-                    q[j + h] = x - y;
-                }
-        auto stage = [&](auto hc) {
-            constexpr int h = decltype(hc)::value;
-            const bool upper = (c4 & h) != 0;
-            for (int j = 0; j < 4; ++j) {
-                const float o = xor_lane<h>(q[j]);
-                q[j] = upper ? o - q[j] : q[j] + o;
-            }
-        };
-        stage(std::integral_constant<int, 1>{});
-        stage(std::integral_constant<int, 2>{});
-        stage(std::integral_constant<int, 4>{});
-        stage(std::integral_constant<int, 8>{});
-        stage(std::integral_constant<int, 16>{});
-        for (int j = 0; j < 4; ++j) {
-            q[j] *= c0f();
-            if (sgj[j] < 0.0f) q[j] = -q[j];
-        }
-    }
-    const float inv_l = 1.0f / L;
-    *out = make_float4((q[0] + w[0]) * inv_l, (q[1] + w[1]) * inv_l, (q[2] + w[2]) * inv_l, (q[3] + w[3]) * inv_l);
 }
 
 } // namespace

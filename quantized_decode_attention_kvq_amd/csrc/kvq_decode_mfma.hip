@@ -291,6 +291,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
     __shared__ __align__(16) _Float16 s_p[kNW * kPW];
     __shared__ float s_wm[kNW][kMaxGroupHeads], s_wl[kNW][kMaxGroupHeads];
     __shared__ float s_wz[kNW][kMaxGroupHeads][4];
+    __shared__ float2 s_vmap[2][64]; // value plane's c_V and signs per lane pair (output map)
+    __shared__ int2 s_vperm[64];     // split V: channels of the lane's two positions
 
     const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
@@ -344,6 +346,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
         }
     }
     const float2 sgn = reinterpret_cast<const float2*>(p.signs + (size_t)(kvh * 2 + 0) * kDim)[l];
+    // the value plane's output-map tables, staged once for the epilogue (read after barriers)
+    if (wave == 0 && !wsplit) {
+        const size_t vtab = (size_t)(kvh * 2 + 1) * kDim;
+        s_vmap[0][l] = VG.sinkhorn ? reinterpret_cast<const float2*>(p.cs + vtab)[l] : make_float2(1.0f, 1.0f);
+        s_vmap[1][l] = (VG.rotate || VS) ? reinterpret_cast<const float2*>(p.signs + vtab)[l] : make_float2(1.0f, 1.0f);
+        s_vperm[l] = VS ? reinterpret_cast<const int2*>(p.perm + (size_t)kvh * kDim)[l] : make_int2(2 * l, 2 * l + 1);
+    }
     const float2 csk = reinterpret_cast<const float2*>(p.cs + (size_t)(kvh * 2 + 0) * kDim)[l];
     int2 pmk = make_int2(0, 0);
     if constexpr (KS) pmk = reinterpret_cast<const int2*>(p.perm_k + (size_t)kvh * kDim)[l];
@@ -1149,24 +1158,32 @@ __global__ __launch_bounds__(kNW * 64) void decode_mfma_kernel(DecodeParams p) {
         }
     }
     __syncthreads();
-    // partial of this split for each of its query heads: [b][hq][split][m, l, -, -, acc[128]]
-    for (int idx = tid; idx < G * kDim; idx += kNW * 64) {
-        const int h = idx >> 7, d = idx & 127;
+    const float2 cs2 = wsplit ? make_float2(1.0f, 1.0f) : s_vmap[0][l];
+    const float2 sg2 = wsplit ? make_float2(1.0f, 1.0f) : s_vmap[1][l];
+    const int2 pm2 = wsplit ? make_int2(2 * l, 2 * l + 1) : s_vperm[l];
+    // partial of this split for each of its query heads, [b][hq][split][m, l, -, -, acc[128]], in
+    // the plain channel domain: one wave per head, lane l the channel pair 2l, 2l + 1 (code-domain
+    // positions, mapped back by the value plane's output map; the FP32-window split is plain)
+    for (int h = wave; h < G; h += kNW) {
         float M = kNegInf;
         for (int w = 0; w < kNW; ++w) M = fmaxf(M, s_wm[w][h]);
-        float A = 0.0f, L = 0.0f;
+        float A0 = 0.0f, A1 = 0.0f, L = 0.0f;
         if (M != kNegInf) {
             for (int w = 0; w < kNW; ++w) {
                 if (s_wm[w][h] == kNegInf) continue;
                 const float f = exp2f(s_wm[w][h] - M);
-                const int o = (w * 8 + h) * kDim + d;
-                A = fmaf(f, (s_acc[o] + s_acc2[o]) + s_wz[w][h][d >> 5], A);
+                const int o = (w * 8 + h) * kDim + 2 * l;
+                const float z = s_wz[w][h][l >> 4];
+                A0 = fmaf(f, (s_acc[o] + s_acc2[o]) + z, A0);
+                A1 = fmaf(f, (s_acc[o + 1] + s_acc2[o + 1]) + z, A1);
                 L = fmaf(f, s_wl[w][h], L);
             }
         }
+        if (!wsplit) value_out_map(A0, A1, VS, VG.sinkhorn, VG.rotate, cs2, sg2);
         float* part = p.partials + (((size_t)b * p.Hq + kvh * G + h) * p.n_splits_total + split) * kPartialFloats;
-        part[4 + d] = A;
-        if (d == 0) {
+        part[4 + pm2.x] = A0;
+        part[4 + pm2.y] = A1;
+        if (l == 0) {
             part[0] = M;
             part[1] = L;
         }

@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 namespace kvq {
 
 // A 16-bit input element as fp32, exactly: bf16 (dtype 1) by widening its bits, fp16 (dtype 2) by
@@ -51,6 +53,49 @@ __device__ __forceinline__ T xor_reduce(T v, Op op) {
     if constexpr (W > 16) v = op(v, xor_lane<16>(v));
     if constexpr (W > 32) v = op(v, xor_lane<32>(v));
     return v;
+}
+
+// The value plane's output map on one head's accumulator held as channel pairs (lane l: code-
+// domain positions 2l, 2l + 1), so that split partials leave in the plain channel domain:
+//  - outlier split (split): each 64-position half's inverse rotation (1/8) d .* H64 y (the
+//    butterflies of spans 1 .. 32, then the signs by position); the caller stores position p at
+//    channel perm[p];
+//  - otherwise y .* c (Sinkhorn, when sink) and, for a rotated plane (rot), d .* (c0 H y) with
+//    c0 = fp32(2^-3.5).
+// cs and sg hold the lane's two entries of c_V and of the plane's signs.
+__device__ __forceinline__ void value_out_map(float& a, float& b, bool split, bool sink, bool rot, float2 cs,
+                                              float2 sg) {
+    const int l = threadIdx.x & 63;
+    auto step = [&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        const float pa = xor_lane<h>(a), pb = xor_lane<h>(b);
+        const bool lower = (l & h) == 0;
+        a = lower ? (a + pa) : (pa - a);
+        b = lower ? (b + pb) : (pb - b);
+    };
+    if (split || rot) {
+        if (!split && sink) {
+            a *= cs.x;
+            b *= cs.y;
+        }
+        const float s = a + b, d = a - b;
+        a = s;
+        b = d;
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 4>{});
+        step(std::integral_constant<int, 8>{});
+        step(std::integral_constant<int, 16>{});
+        if (!split) step(std::integral_constant<int, 32>{});
+        const float f = split ? 0.125f : __uint_as_float(0x3DB504F3u);
+        a *= f;
+        b *= f;
+        if (sg.x < 0.0f) a = -a;
+        if (sg.y < 0.0f) b = -b;
+    } else if (sink) {
+        a *= cs.x;
+        b *= cs.y;
+    }
 }
 
 } // namespace kvq
