@@ -339,37 +339,39 @@ __device__ double mass_d(double a, double b, bool b_inf) {
     return 0.5 * (erfc(a / sqrt(2.0)) - eb);
 }
 
-__global__ void codebook_kernel(float* mu, float* theta, int iters, int levels, int dim) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    const int h = levels / 2;
-    double m[8];
-    for (int k = 0; k < h; ++k) m[k] = 2.0 * (double)(k + 1) / (double)h;
+// One lane per centroid k < levels / 2 of the upper half: each iteration, lane k takes its
+// neighbours' centroids by shuffle, forms the cell bounds b_k = (m_{k-1} + m_k) / 2 (b_0 = 0) and
+// b_{k+1}, and moves m_k to the cell's conditional mean (phi(b_k) - phi(b_{k+1})) / P(b_k < x <
+// b_{k+1}); the last cell is open above. Every value is the same binary64 expression, in the same
+// order, as in a one-thread loop over k, so the tables do not depend on the lane count.
+__global__ __launch_bounds__(64) void codebook_kernel(float* mu, float* theta, int iters, int levels, int dim) {
+    const int h = levels / 2, k = threadIdx.x;
+    const bool last = (k == h - 1);
+    double m = 2.0 * (double)(min(k, h - 1) + 1) / (double)h;
     for (int it = 0; it < iters; ++it) {
-        double bnd[8];
-        bnd[0] = 0.0;
-        for (int k = 1; k < h; ++k) bnd[k] = (m[k - 1] + m[k]) * 0.5;
-        double nm[8];
-        for (int k = 0; k < h; ++k) {
-            const bool last = (k == h - 1);
-            const double pb = last ? 0.0 : phi_d(bnd[k + 1]);
-            nm[k] = (phi_d(bnd[k]) - pb) / mass_d(bnd[k], last ? 0.0 : bnd[k + 1], last);
-        }
-        for (int k = 0; k < h; ++k) m[k] = nm[k];
+        const double ml = __shfl(m, max(k - 1, 0)), mr = __shfl(m, min(k + 1, 63));
+        const double b0 = (k == 0) ? 0.0 : (ml + m) * 0.5;
+        const double b1 = last ? 0.0 : (m + mr) * 0.5;
+        const double pb = last ? 0.0 : phi_d(b1);
+        const double nm = (phi_d(b0) - pb) / mass_d(b0, b1, last);
+        m = (k < h) ? nm : m;
     }
     const double r = sqrt((double)dim);
-    for (int k = 0; k < h; ++k) {
-        const float f = (float)(m[k] / r);
+    const double ml = __shfl(m, max(k - 1, 0));
+    if (k < h) {
+        const float f = (float)(m / r);
         mu[h + k] = f;
         mu[h - 1 - k] = -f;
+        if (k == 0) {
+            theta[h - 1] = 0.0f;
+            theta[levels - 1] = 0.0f;
+        } else {
+            const double t = (ml + m) * 0.5;
+            const float ft = (float)(t / r);
+            theta[h - 1 + k] = ft;
+            theta[h - 1 - k] = -ft;
+        }
     }
-    theta[h - 1] = 0.0f;
-    for (int k = 1; k < h; ++k) {
-        const double t = (m[k - 1] + m[k]) * 0.5;
-        const float f = (float)(t / r);
-        theta[h - 1 + k] = f;
-        theta[h - 1 - k] = -f;
-    }
-    theta[levels - 1] = 0.0f;
 }
 
 // Outlier channels of one kv head's calibration tokens (TurboQuant split): thread d sums
