@@ -502,20 +502,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     const int hq = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
     const int c4 = t >> 3, part = t & 7;
     float4* out = reinterpret_cast<float4*>(p.out + ((size_t)b * p.Hq + hq) * kDim) + c4;
-    if (p.len[b] == 0) {
-        if (part == 0) *out = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        return;
-    }
+    // Every split wrote its partial (an empty split: m = -inf, l = 0, acc = 0), so all loads are
+    // issued before anything is tested, and the combine has no branch that the compiler could
+    // turn into a second round trip; an empty sequence (l = 0) is resolved at the store.
     const float* base = p.partials + ((size_t)b * p.Hq + hq) * p.n_splits_total * kPartialFloats;
     float m = kNegInf, l = 0.0f;
     float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int s0 = part; s0 < p.n_splits_total; s0 += 64) {
+    auto round = [&](int s0) __attribute__((always_inline)) {
         float ms[8], ls[8];
         float4 as[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            // unconditional loads (a split past the last re-reads the last one and is ignored),
-            // so that all of them go out back to back with no branch between them
+            // a split past the last re-reads the last one and is given weight 0
             const int s = s0 + 8 * i;
             const float* ps = base + (size_t)min(s, p.n_splits_total - 1) * kPartialFloats;
             const float2 ml = *reinterpret_cast<const float2*>(ps);
@@ -523,11 +521,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
             ls[i] = ml.y;
             as[i] = *reinterpret_cast<const float4*>(ps + 4 + 4 * c4);
         }
+        // all of the round's loads in flight before the first is consumed
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            asm volatile("" ::"v"(ms[i]), "v"(ls[i]), "v"(as[i].x), "v"(as[i].y), "v"(as[i].z), "v"(as[i].w));
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            if (ms[i] == kNegInf) continue;
+            // weights exp2(m - mn) and exp2(ms - mn) are 0 for a -inf side; both sides -inf
+            // leaves the state as it is
             const float mn = fmaxf(m, ms[i]);
-            const float fo = __builtin_amdgcn_exp2f(m - mn), fn = __builtin_amdgcn_exp2f(ms[i] - mn);
+            const bool none = (mn == kNegInf);
+            const float fo = none ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+            const float fn = none ? 0.0f : __builtin_amdgcn_exp2f(ms[i] - mn);
             m = mn;
             l = fmaf(ls[i], fn, l * fo);
             a.x = fmaf(as[i].x, fn, a.x * fo);
@@ -535,7 +540,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
             a.z = fmaf(as[i].z, fn, a.z * fo);
             a.w = fmaf(as[i].w, fn, a.w * fo);
         }
-    }
+    };
+    // the first round of up to 64 splits unconditionally (no branch ahead of its loads)
+    round(part);
+    for (int s0 = part + 64; s0 < p.n_splits_total; s0 += 64) round(s0);
     // the eight split classes of the channel group: pairs at xor distance 1, 2, 4 (a fixed tree;
     // lane part == 0 holds the result)
     auto pair = [&](auto hc) {
@@ -556,8 +564,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     pair(std::integral_constant<int, 2>{});
     pair(std::integral_constant<int, 4>{});
     if (part == 0) {
+        // l = 0 only for an empty sequence (a non-empty one has a weight-1 token in some split)
         const float inv_l = 1.0f / l;
-        *out = make_float4(a.x * inv_l, a.y * inv_l, a.z * inv_l, a.w * inv_l);
+        *out = (l == 0.0f) ? make_float4(0.0f, 0.0f, 0.0f, 0.0f) : make_float4(a.x * inv_l, a.y * inv_l, a.z * inv_l, a.w * inv_l);
     }
 }
 
