@@ -355,6 +355,53 @@ def test_split_count_invariance_and_determinism(wl, path):
 
 
 @pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("wl", [W.LLAMA3B_32K_KVARN, W.LLAMA8B_32K_TURBO25_KV], ids=lambda w: w.name)
+def test_decode_batch_with_an_empty_sequence(wl, path):
+    # one decode call over a batch whose last sequence is empty: the empty sequence's splits all
+    # hold m = -inf, l = 0 and the merge writes zeros for it (l = 0), while the others match the
+    # oracle (lengths 700 and 130, built by a batch-2 and a batch-1 prefill call)
+    _say("case: batch with an empty sequence,", wl.name, "path", path)
+    case = Case(wl, 700, layers=[0], batch=3)
+    case.cache.set_option(2, path)
+    streams = {b: ([], []) for b in range(2)}
+    for ci, (nb, nt) in enumerate([(2, 130), (1, 570)]):
+        k = W.gen_kv(wl, 2000 + ci, 0, nt, batch=nb)
+        v = W.gen_kv(wl, 2000 + ci, 1, nt, batch=nb)
+        case.cache.prefill_quantize(0, k.to("cuda"), v.to("cuda"))
+        for b in range(nb):
+            streams[b][0].append(k[b].float().numpy())
+            streams[b][1].append(v[b].float().numpy())
+    q = W.gen_q(wl, 0, 0, batch=3).to("cuda")
+    out = torch.full((3, wl.n_q_heads, 128), 7.0, device="cuda")
+    case.cache.attn_decode(0, q, out)
+    torch.cuda.synchronize()
+    assert [case.cache.length(0, b) for b in range(3)] == [700, 130, 0]
+    got = out.cpu().numpy()
+    assert np.count_nonzero(got[2]) == 0
+    _, mu, theta, _ = oracle.lloyd_max(oracle.LLOYD_ITERS)
+    cap = case.cache.cfg.max_context
+    qn = q.float().cpu().numpy()
+    G = wl.group
+    for b in range(2):
+        ref = np.zeros((wl.n_q_heads, 128))
+        for h in range(wl.n_kv_heads):
+            pl = []
+            for tensor in (0, 1):
+                scheme = wl.k_scheme if tensor == 0 else wl.v_scheme
+                bits = wl.k_bits if tensor == 0 else wl.v_bits
+                rot = (wl.rotate_k if tensor == 0 else wl.rotate_v) or W.is_turbo(scheme)
+                sink = wl.sinkhorn_iters > 0 and not W.is_turbo(scheme)
+                tb = case.oracle_tables(0, h, tensor, mu, theta)
+                pln = oracle.Plane(scheme, bits, rot, sink, wl.window, tensor, cap)
+                pln.append(np.concatenate(streams[b][tensor])[:, h], tb)
+                pl.append((pln, tb))
+            ref[h * G:(h + 1) * G] = oracle.attention(pl[0][0], pl[1][0], pl[0][1], pl[1][1], qn[b, h * G:(h + 1) * G])
+        e, m = rel_l2(got[b], ref), max_abs(got[b], ref)
+        _say(f"  seq {b}: rel_l2={e:.2e} max_abs={m:.2e}")
+        assert e <= REL_L2_TOL and m <= MAX_ABS_TOL, (b, e, m)
+
+
+@pytest.mark.parametrize("path", [1, 2])
 def test_empty_and_single_token(path):
     wl = W.LLAMA3B_32K_KVARN
     _say("case: empty / single token, path", path)
