@@ -508,7 +508,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     const float* base = p.partials + ((size_t)b * p.Hq + hq) * p.n_splits_total * kPartialFloats;
     float m = kNegInf, l = 0.0f;
     float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    auto round = [&](int s0) __attribute__((always_inline)) {
+    auto merge_round = [&](int s0) __attribute__((always_inline)) {
         float ms[8], ls[8];
         float4 as[8];
 #pragma unroll
@@ -542,8 +542,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
         }
     };
     // the first round of up to 64 splits unconditionally (no branch ahead of its loads)
-    round(part);
-    for (int s0 = part + 64; s0 < p.n_splits_total; s0 += 64) round(s0);
+    merge_round(part);
+    for (int s0 = part + 64; s0 < p.n_splits_total; s0 += 64) merge_round(s0);
     // the eight split classes of the channel group: pairs at xor distance 1, 2, 4 (a fixed tree;
     // lane part == 0 holds the result)
     auto pair = [&](auto hc) {
